@@ -1,0 +1,544 @@
+"""Pins of the CPU oracle against what the pages and plain mathematics fix.
+
+Nothing here compares the oracle with a retyped copy of itself: every check is a
+page figure (tests/golden/page_figures.json), a library routine (numpy's fp16
+cast and quantile), a brute-force search over all codes, a closed form, or an
+invariant of the definition.  CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLD = json.load(open(os.path.join(HERE, "golden", "page_figures.json")))
+
+
+def tiny(**kw):
+    c = dict(batch=1, q_heads=1, kv_heads=1, head_dim=8, tokens=16, k_bits=4, k_mode=0,
+             k_block=8, v_bits=4, v_group=8, clip_quantile=0.0, outlier_pct=0, rope_theta=10000.0)
+    c.update(kw)
+    c.setdefault("capacity", c["tokens"])
+    return c
+
+
+def f16(x):
+    return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def hval(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- fp16
+def test_h2f_exhaustive(orc):
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.h2f(allh)
+    ref = allh.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f2h_rn_matches_numpy_cast(orc):
+    rng = np.random.default_rng(7)
+    e = rng.integers(-30, 17, 200000)
+    x = (rng.random(200000) + 0.5) * np.exp2(e) * rng.choice([-1, 1], 200000)
+    x = x.astype(np.float32)
+    # exact midpoints between neighbouring fp16 values (ties) and boundary values
+    h = rng.integers(0, 0x7bff, 50000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float32)
+    hi = (h + 1).view(np.float16).astype(np.float32)
+    mids = ((lo.astype(np.float64) + hi.astype(np.float64)) / 2).astype(np.float32)
+    special = np.array([0.0, -0.0, 65504, 65519.99, 65520, 1e9, -1e9, 2 ** -24, 2 ** -25,
+                        3 * 2 ** -26, 2 ** -14, 6.1e-5, np.inf, -np.inf], np.float32)
+    x = np.concatenate([x, mids, -mids, special])
+    got = orc.f2h(x, "rn")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_f2h_directed_rounding(orc):
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(100000) * np.exp2(rng.integers(-26, 14, 100000))).astype(np.float32)
+    x = np.concatenate([x, f16([0.5, -3.25, 1024.0]).view(np.float16).astype(np.float32),
+                        np.array([0.0, 1e-9, -1e-9], np.float32)])
+    rd = hval(orc.f2h(x, "rd"))
+    ru = hval(orc.f2h(x, "ru"))
+    rn = hval(orc.f2h(x, "rn"))
+    xd = x.astype(np.float64)
+    assert np.all(rd <= xd) and np.all(ru >= xd)
+    exact = rd == xd
+    assert np.all(ru[exact] == xd[exact])
+    # otherwise rd and ru are neighbours in fp16
+    ne = ~exact
+    nxt = np.nextafter(rd[ne].astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    assert np.all(nxt == ru[ne])
+    assert np.all((rn == rd) | (rn == ru))
+
+
+# --------------------------------------------------------------------------- sizes
+def test_kv_size_worked_example(orc):
+    for key in ("kv_size_example", "kv_size_example_batch4"):
+        g = GOLD[key]
+        v = orc.kv_bytes(g["layers"], g["batch"], g["tokens"], g["hidden"], g["bits"])
+        assert v == 2 * g["layers"] * g["batch"] * g["tokens"] * g["hidden"] * 2
+        assert abs(v - g["page_value_bytes_approx"]) / g["page_value_bytes_approx"] < 0.08
+    assert orc.kv_bytes(32, 1, 2048, 4096, 16) == 2 ** 30
+
+
+def test_int4_is_quarter_of_fp16(orc):
+    g = GOLD["fp16_to_int4_factor"]
+    for kb, frac in ((4, 1 / g["factor"]), (3, 3 / 16), (2, 1 / 8)):
+        c = tiny(head_dim=128, k_block=128, tokens=1024, k_bits=kb, v_group=128)
+        lay = orc.layout(c)
+        fp16 = c["tokens"] * c["head_dim"] * 2
+        assert lay["k_codes"] / fp16 == frac
+    c = tiny(head_dim=128, k_block=128, tokens=1024, v_group=128)
+    assert orc.layout(c)["v_codes"] / (1024 * 128 * 2) == 0.25
+
+
+def test_int4_has_16_states(orc):
+    g = GOLD["int4_states"]
+    c = tiny(head_dim=8, k_block=32, tokens=32)
+    x = np.linspace(-3, 5, 32 * 8).reshape(32, 8)
+    hc = orc.HeadCache(c).build(f16(x), f16(x))
+    codes = _codes_uniform_k(hc, c)
+    assert sorted(set(codes.ravel().tolist())) == list(range(g["states"]))
+
+
+def test_memory_fraction_near_quarter(orc):
+    g = GOLD["int4_memory_target"]
+    import synth
+    c = synth.config("c1")
+    lay = orc.layout(c)
+    tail = lay["k_tail"] + lay["v_tail"]
+    frac = (sum(lay.values()) - tail) / (2 * c["batch"] * c["kv_heads"] * c["tokens"] * c["head_dim"] * 2)
+    assert abs(frac - g["fraction_of_fp16"]) < 0.02        # 26.6 % with fp16 scales and zeros
+    per_token_head = (sum(lay.values()) - tail) / (c["batch"] * c["kv_heads"] * c["tokens"])
+    assert per_token_head == 136                            # 64 + 64 code bytes, 4 + 4 metadata bytes
+
+
+# --------------------------------------------------------------------------- helpers
+def _deq(hc, which):
+    return hc.dequantize(which).astype(np.float64)
+
+
+def _codes_uniform_k(hc, c):
+    """Recover K codes from the dequantized values (fmaf(c, s, z) with s > 0)."""
+    D, Bk = c["head_dim"], c["k_block"]
+    n = hc.length // Bk * Bk
+    x = _deq(hc, 0)[:n]
+    s = np.repeat(hval(hc.k_scale), Bk, axis=0)[:n]
+    z = np.repeat(hval(hc.k_zero), Bk, axis=0)[:n]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        cc = np.where(s > 0, np.rint((x - z) / np.where(s > 0, s, 1)), 0)
+    return cc.astype(np.int64)
+
+
+def _rand_block(rng, T, D, scale=1.0, heavy=False):
+    std = np.exp(rng.normal(0, 0.5, D)) * scale
+    x = rng.standard_normal((T, D)) * std
+    if heavy:
+        m = rng.random((T, D)) < 0.02
+        x[m] = np.clip(10 * rng.standard_t(3, m.sum()), -200, 200)
+    return f16(x)
+
+
+def _outlier_mask(hc, c, which):
+    T = hc.length // c["k_block"] * c["k_block"]
+    m = np.zeros((T, c["head_dim"]), bool)
+    if hc.kout:
+        col = (hc.v_col if which else hc.k_col)[:T * hc.kout].reshape(T, hc.kout)
+        m[np.arange(T)[:, None], col] = True
+    return m
+
+
+# --------------------------------------------------------------------------- uniform quantizer
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("pct", [0, 5])
+def test_uniform_codes_are_nearest_grid_points(orc, bits, pct):
+    """Brute force over every code: the chosen code minimises |x - (c*s + z)| (exact
+    ties excluded), for K per channel and V per token group."""
+    rng = np.random.default_rng(bits * 10 + pct)
+    vb = 4 if bits == 3 else bits
+    c = tiny(head_dim=32, k_block=16, tokens=64, k_bits=bits, v_bits=vb, v_group=16, outlier_pct=pct)
+    k = _rand_block(rng, 64, 32, heavy=pct > 0)
+    v = _rand_block(rng, 64, 32, heavy=pct > 0)
+    hc = orc.HeadCache(c).build(k, v)
+    for which, src, L in ((0, k, (1 << bits) - 1), (1, v, (1 << vb) - 1)):
+        x = hval(src)
+        xh = _deq(hc, which)
+        if which == 0:
+            s = np.repeat(hval(hc.k_scale), 16, axis=0)
+            z = np.repeat(hval(hc.k_zero), 16, axis=0)
+        else:
+            s = np.repeat(hval(hc.v_scale), 16, axis=1)
+            z = np.repeat(hval(hc.v_zero), 16, axis=1)
+        dense = ~_outlier_mask(hc, c, which) & (s > 0)
+        grid = z[..., None] + np.arange(L + 1) * s[..., None]              # fp64 grid
+        best = np.argmin(np.abs(x[..., None] - grid), axis=-1)
+        chosen = np.rint((xh - z) / np.where(s > 0, s, 1))
+        u = (x - z) / np.where(s > 0, s, 1)
+        tie = np.abs(u - np.floor(u) - 0.5) < 1e-5
+        ok = dense & ~tie
+        assert ok.sum() > 0.9 * dense.sum()
+        assert np.array_equal(best[ok], chosen[ok])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_uniform_error_bound_half_scale(orc, bits):
+    """|x - dequant(x)| <= s/2 (+ fp32 evaluation slack) for unclipped dense values."""
+    rng = np.random.default_rng(100 + bits)
+    vb = 4 if bits == 3 else bits
+    c = tiny(head_dim=64, k_block=32, tokens=96, k_bits=bits, v_bits=vb, v_group=32, outlier_pct=2)
+    k = _rand_block(rng, 96, 64, heavy=True)
+    v = _rand_block(rng, 96, 64, heavy=True)
+    hc = orc.HeadCache(c).build(k, v)
+    for which, src in ((0, k), (1, v)):
+        x = hval(src)
+        xh = _deq(hc, which)
+        if which == 0:
+            s = np.repeat(hval(hc.k_scale), 32, axis=0)
+            z = np.repeat(hval(hc.k_zero), 32, axis=0)
+        else:
+            s = np.repeat(hval(hc.v_scale), 32, axis=1)
+            z = np.repeat(hval(hc.v_zero), 32, axis=1)
+        m = _outlier_mask(hc, c, which)
+        ulp = np.spacing(np.maximum(np.abs(x), np.abs(z)).astype(np.float32)).astype(np.float64)
+        err = np.abs(x - xh)
+        assert np.all(err[~m] <= s[~m] / 2 + 4 * ulp[~m])
+        assert np.array_equal(xh[m], x[m])                         # outliers are exact
+
+
+def test_metadata_invariants(orc):
+    """zero = largest fp16 <= group min, scale = smallest fp16 >= (max - zero)/L;
+    the group min codes to 0 and the group max to L; outliers take no part."""
+    rng = np.random.default_rng(5)
+    c = tiny(head_dim=64, k_block=32, tokens=64, v_group=16, outlier_pct=3)
+    k = _rand_block(rng, 64, 64, heavy=True)
+    v = _rand_block(rng, 64, 64, heavy=True)
+    hc = orc.HeadCache(c).build(k, v)
+    L = 15
+    mk = _outlier_mask(hc, c, 0)
+    mv = _outlier_mask(hc, c, 1)
+    x = hval(k)
+    codes = _codes_uniform_k(hc, c)
+    for n in range(2):
+        for ch in range(64):
+            sel = ~mk[n * 32:(n + 1) * 32, ch]
+            vals = x[n * 32:(n + 1) * 32, ch][sel]
+            z = hval(hc.k_zero[n, ch])
+            s = hval(hc.k_scale[n, ch])
+            lo, hi = vals.min(), vals.max()
+            assert z <= lo < np.nextafter(np.float16(z), np.float16(np.inf)).astype(np.float64)
+            r = np.float32(np.float32(hi - z) / np.float32(L))
+            assert s >= r and np.nextafter(np.float16(s), np.float16(-np.inf)) < r
+            cc = codes[n * 32:(n + 1) * 32, ch][sel]
+            assert cc[np.argmin(vals)] == 0 and cc[np.argmax(vals)] == L
+    xv = hval(v)
+    for t in range(64):
+        for g in range(4):
+            sel = ~mv[t, g * 16:(g + 1) * 16]
+            vals = xv[t, g * 16:(g + 1) * 16][sel]
+            z = hval(hc.v_zero[t, g])
+            assert z <= vals.min() < np.nextafter(np.float16(z), np.float16(np.inf)).astype(np.float64)
+
+
+def test_metadata_invariants_after_clipping(orc):
+    """With clipping the group minimum is the fp32 threshold -t, not an fp16 value:
+    the zero-point must still be the largest fp16 not above it."""
+    rng = np.random.default_rng(6)
+    c = tiny(head_dim=64, k_block=32, tokens=64, v_group=64, clip_quantile=0.97)
+    k = _rand_block(rng, 64, 64, heavy=True)
+    hc = orc.HeadCache(c).build(k, k)
+    hits = 0
+    for n in range(2):
+        blk = k[n * 32:(n + 1) * 32]
+        t = np.float32(orc.clip_threshold(blk, np.float32(0.97)))
+        d = np.clip(hval(blk).astype(np.float32), -t, t).astype(np.float64)
+        for ch in range(64):
+            lo = d[:, ch].min()
+            z = hval(hc.k_zero[n, ch])
+            assert z <= lo < np.nextafter(np.float16(z), np.float16(np.inf)).astype(np.float64)
+            hits += lo == -t
+        for t_ in range(32):
+            lo = d[t_].min()
+            z = hval(hc.v_zero[n * 32 + t_, 0])
+            assert z <= lo < np.nextafter(np.float16(z), np.float16(np.inf)).astype(np.float64)
+    assert hits > 0
+
+
+def test_exact_ties_round_half_to_even(orc):
+    """Group with zero 0 and scale 1 (values 0 and 15 present); x = k + 1/2 must take
+    the even neighbour."""
+    c = tiny(head_dim=32, k_block=8, tokens=8, v_group=32)
+    v = np.zeros((8, 32))
+    v[:, 0], v[:, 1] = 0.0, 15.0
+    v[:, 2:17] = np.arange(15) + 0.5
+    hc = orc.HeadCache(c).build(f16(v), f16(v))
+    got = _deq(hc, 1)[:, 2:17]
+    want = np.array([k if k % 2 == 0 else k + 1 for k in range(15)], np.float64)
+    assert np.all(hval(hc.v_scale) == 1.0) and np.all(hval(hc.v_zero) == 0.0)
+    assert np.array_equal(got, np.tile(want, (8, 1)))
+
+
+def test_constant_and_empty_groups(orc):
+    c = tiny(head_dim=8, k_block=8, tokens=8, v_group=4, outlier_pct=13)   # k_out = 2
+    k = np.full((8, 8), 1.25)
+    k[:, 3] = 500.0 + np.arange(8)             # channel 3 is the largest of every token
+    k[:, 6] = 400.0                            # channel 6 is the second largest
+    v = np.full((8, 8), -0.75)
+    v[:, 0] = 9.0
+    v[:, 1] = 8.0                              # group 0 keeps channels 2, 3 only
+    hc = orc.HeadCache(c).build(f16(k), f16(v))
+    assert hc.k_scale[0, 3] == 0 and hc.k_zero[0, 3] == 0          # empty channel
+    assert hc.k_scale[0, 0] == 0 and hval(hc.k_zero[0, 0]) == 1.25  # constant channel
+    assert np.all(hc.v_scale == 0) and np.all(hval(hc.v_zero) == -0.75)
+    assert np.array_equal(_deq(hc, 0), hval(f16(k)))
+    assert np.array_equal(_deq(hc, 1), hval(f16(v)))
+
+
+# --------------------------------------------------------------------------- outliers
+def test_outliers_are_top_k_by_magnitude(orc):
+    rng = np.random.default_rng(11)
+    c = tiny(head_dim=128, k_block=16, tokens=64, v_group=128, outlier_pct=1)
+    assert orc.kout(c) == 2 and orc.kout(tiny(head_dim=64, outlier_pct=1)) == 1
+    k = _rand_block(rng, 64, 128, heavy=True)
+    v = _rand_block(rng, 64, 128, heavy=True)
+    k[5, [10, 90]] = f16([7.0, -7.0])           # exact magnitude tie: both must be taken
+    k[5, 20] = f16(1e3)
+    hc = orc.HeadCache(c).build(k, v)
+    for which, src in ((0, k), (1, v)):
+        col = (hc.v_col if which else hc.k_col).reshape(64, 2)
+        val = (hc.v_val if which else hc.k_val).reshape(64, 2)
+        rp = hc.v_rowptr if which else hc.k_rowptr
+        assert rp[0] == 0 and np.all(np.diff(rp) == 2)
+        mag = (src & 0x7FFF).astype(np.int64)
+        for t in range(64):
+            order = np.lexsort((np.arange(128), -mag[t]))   # |x| descending, then column ascending
+            want = np.sort(order[:2])
+            assert np.array_equal(col[t], want)
+            assert np.all(np.diff(col[t].astype(int)) > 0)
+            assert np.array_equal(val[t], src[t, want])
+    assert set(hc.k_col.reshape(64, 2)[5]) == {20, 10}
+
+
+# --------------------------------------------------------------------------- clip
+@pytest.mark.parametrize("q", [0.99, 0.5, 0.9])
+def test_clip_threshold_equals_numpy_quantile(orc, q):
+    rng = np.random.default_rng(int(q * 100))
+    for trial in range(20):
+        n = int(rng.integers(2, 5000))
+        x = rng.standard_normal(n) * np.exp(rng.normal(0, 2))
+        if trial % 3 == 0:
+            x = np.round(x * 4) / 4                              # many exact duplicates
+        b = f16(x)
+        t = orc.clip_threshold(b, np.float32(q))
+        ref = np.quantile(np.abs(hval(b)), np.float64(np.float32(q)), method="linear")
+        assert abs(t - ref) <= np.spacing(np.float32(ref))
+
+
+def test_clip_bounds_dense_values(orc):
+    rng = np.random.default_rng(3)
+    c = tiny(head_dim=64, k_block=32, tokens=64, v_group=64, clip_quantile=0.99, outlier_pct=1)
+    k = _rand_block(rng, 64, 64, heavy=True)
+    v = _rand_block(rng, 64, 64, heavy=True)
+    hc = orc.HeadCache(c).build(k, v)
+    for which, src in ((0, k), (1, v)):
+        xh = _deq(hc, which)
+        m = _outlier_mask(hc, c, which)
+        for n in range(2):
+            blk = src[n * 32:(n + 1) * 32]
+            t = np.quantile(np.abs(hval(blk)), np.float64(np.float32(0.99)), method="linear")
+            s = hval(hc.k_scale[n]).max() if which == 0 else hval(hc.v_scale[n * 32:(n + 1) * 32]).max()
+            dense = xh[n * 32:(n + 1) * 32][~m[n * 32:(n + 1) * 32]]
+            assert np.abs(dense).max() <= t + s / 2 + 1e-3
+            assert np.abs(hval(blk)).max() > t                     # something was clipped
+
+
+# --------------------------------------------------------------------------- non-uniform codebook
+def _lut_cfg(D=16, kb=3, Bk=16, T=32):
+    return tiny(head_dim=D, k_block=Bk, tokens=T, k_bits=kb, k_mode=1, v_bits=4, v_group=D)
+
+
+def test_codebook_codes_are_nearest_centroid(orc):
+    rng = np.random.default_rng(21)
+    c = _lut_cfg()
+    lut = np.sort(rng.standard_normal((16, 8)) * 1.5, axis=1).astype(np.float16).view(np.uint16)
+    k = _rand_block(rng, 32, 16)
+    v = _rand_block(rng, 32, 16)
+    hc = orc.HeadCache(c, lut).build(k, v)
+    x = hval(k)
+    xh = _deq(hc, 0)
+    C = hval(lut)                                               # [D][8]
+    best = np.argmin(np.abs(x[:, :, None] - C[None]), axis=2)
+    got = np.argmax(xh[:, :, None] == C[None], axis=2)
+    mids = (C[:, :-1] + C[:, 1:]) / 2
+    near = np.min(np.abs(x[:, :, None] - mids[None]), axis=2) < 1e-6 * (1 + np.abs(x))
+    assert np.array_equal(best[~near], got[~near])
+    assert np.all(np.isin(xh, C))
+
+
+def test_evenly_spaced_codebook_is_uniform_rounding(orc):
+    rng = np.random.default_rng(22)
+    c = _lut_cfg(kb=4)
+    z, s = -2.0, 0.25
+    lut = np.tile(f16(z + s * np.arange(16)), (16, 1))
+    k = _rand_block(rng, 32, 16)
+    k[3] = f16(z + s * (np.arange(16) % 15 + 0.5))             # exact midpoints: lower code wins
+    hc = orc.HeadCache(c, lut).build(k, k)
+    u = (hval(k) - z) / s
+    want = np.clip(np.floor(u + 0.5 - 1e-12), 0, 15)           # nearest, ties to lower
+    got = (_deq(hc, 0) - z) / s
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------- packing
+def _identity_lut(D, kb):
+    return np.tile(f16(np.arange(1 << kb)), (D, 1))
+
+
+@pytest.mark.parametrize("kb,row,want", [
+    (4, [1, 2, 3, 4], [0x31, 0x42]),            # bytes hold channel pairs (0, 2) and (1, 3)
+    (3, [1, 2, 3, 4, 5, 6, 7, 0], [0xA9, 0xBC, 0x13]),   # 3-bit codes straddle bytes, LSB first
+    (2, [1, 2, 3, 0], [0x2D]),
+])
+def test_key_row_known_bytes(orc, kb, row, want):
+    D = len(row)
+    c = tiny(head_dim=D, k_block=8, tokens=8, k_bits=kb, k_mode=1, v_group=D)
+    k = np.tile(np.asarray(row, np.float64), (8, 1))
+    hc = orc.HeadCache(c, _identity_lut(D, kb)).build(f16(k), f16(k))
+    rb = D * kb // 8
+    assert list(hc.k_codes[:rb]) == want
+    assert np.array_equal(hc.k_codes.reshape(8, rb), np.tile(np.asarray(want, np.uint8), (8, 1)))
+
+
+def test_value_words_known_bytes(orc):
+    c = tiny(head_dim=2, k_block=8, tokens=8, v_group=2)
+    v = np.array([[0, 15], [15, 0]] * 4, np.float64)             # per-token codes equal the values
+    hc = orc.HeadCache(c).build(f16(v), f16(v))
+    assert list(hc.v_codes) == [0xF0] * 4 + [0x0F] * 4          # word(ch0), word(ch1); token t at bits 4t
+    c2 = tiny(head_dim=2, k_block=16, tokens=16, v_bits=2, v_group=2)
+    v2 = np.array([[0, 3], [3, 0]] * 8, np.float64)
+    hc2 = orc.HeadCache(c2).build(f16(v2), f16(v2))
+    assert list(hc2.v_codes) == [0xCC] * 4 + [0x33] * 4
+
+
+@pytest.mark.parametrize("kb", [2, 3, 4])
+def test_key_pack_roundtrip(orc, kb):
+    rng = np.random.default_rng(kb)
+    c = tiny(head_dim=64, k_block=16, tokens=48, k_bits=kb, k_mode=1, v_group=64)
+    codes = rng.integers(0, 1 << kb, (48, 64))
+    hc = orc.HeadCache(c, _identity_lut(64, kb)).build(f16(codes), f16(codes))
+    assert np.array_equal(_deq(hc, 0), codes.astype(np.float64))
+
+
+# --------------------------------------------------------------------------- attention
+def _softmax_attn(qr, kr, v, D):
+    s = kr @ qr / math.sqrt(D)
+    w = np.exp(s - s.max())
+    return (w[:, None] * v).sum(0) / w.sum()
+
+
+def _rot_matrix(pos, D, theta):
+    """Full D x D rotary matrix built from 2x2 rotations on channel pairs (i, i + D/2)."""
+    R = np.zeros((D, D))
+    h = D // 2
+    for i in range(h):
+        a = pos * theta ** (-2.0 * i / D)
+        R[i, i], R[i, i + h], R[i + h, i], R[i + h, i + h] = np.cos(a), -np.sin(a), np.sin(a), np.cos(a)
+    return R
+
+
+def test_rope_pairing_and_direction_closed_form(orc):
+    """D = 4, tail-only cache (exact values): key e_2 at position 1 against query e_0
+    at position 0 scores -sin(1)/2; key e_3 against e_1 scores -sin(0.01)/2."""
+    c = tiny(head_dim=4, k_block=8, tokens=2, v_group=4)
+    for qch, kch, ang in ((0, 2, 1.0), (1, 3, 0.01)):
+        k = np.zeros((2, 4)); k[0, qch] = 1.0; k[1, kch] = 1.0
+        v = np.zeros((2, 4)); v[0, 0] = 1.0; v[1, 1] = 1.0
+        hc = orc.HeadCache(c).build(f16(k), f16(v))
+        q = np.zeros(4); q[qch] = 1.0
+        out = hc.decode(f16(q), q_pos=0)
+        s0, s1 = 0.5, -math.sin(ang) / 2
+        w0, w1 = math.exp(s0), math.exp(s1)
+        assert abs(out[0] - w0 / (w0 + w1)) < 1e-12 and abs(out[1] - w1 / (w0 + w1)) < 1e-12
+
+
+def test_attention_closed_forms(orc):
+    rng = np.random.default_rng(31)
+    c = tiny(head_dim=32, k_block=16, tokens=72, v_group=16, outlier_pct=4)
+    k = _rand_block(rng, 72, 32, heavy=True)
+    v = _rand_block(rng, 72, 32, heavy=True)
+    hc = orc.HeadCache(c).build(k, v)
+    vh = _deq(hc, 1)
+    out = hc.decode(f16(np.zeros(32)), q_pos=71)                # q = 0: uniform weights
+    assert np.allclose(out, vh.mean(0), rtol=0, atol=1e-12)
+    h1 = orc.HeadCache(tiny(head_dim=32, k_block=16, tokens=1, v_group=16)).build(k[:1], v[:1])
+    assert np.array_equal(h1.decode(f16(rng.standard_normal(32))), hval(v[0]))   # one token
+    vc = np.full((72, 32), 0.8125)
+    hcc = orc.HeadCache(c).build(k, f16(vc))
+    assert np.allclose(hcc.decode(f16(rng.standard_normal(32))), 0.8125, rtol=0, atol=1e-12)
+
+
+def _on_grid(rng, T, D, Bk, L, per_channel):
+    """Values that the uniform quantizer must reproduce exactly: each group holds
+    zero + c * scale with zero a multiple of 1/64, a power-of-two scale and both end
+    codes present, so every value is exact in fp16."""
+    x = np.empty((T, D))
+    for n in range(T // Bk):
+        if per_channel:
+            for ch in range(D):
+                z = float(rng.integers(-192, 1)) / 64
+                s = 2.0 ** rng.integers(-5, -1)
+                cc = rng.integers(0, L + 1, Bk); cc[0], cc[1] = 0, L
+                x[n * Bk:(n + 1) * Bk, ch] = z + cc * s
+        else:
+            for t in range(n * Bk, (n + 1) * Bk):
+                z = float(rng.integers(-192, 1)) / 64
+                s = 2.0 ** rng.integers(-5, -1)
+                cc = rng.integers(0, L + 1, D); cc[0], cc[1] = 0, L
+                x[t] = z + cc * s
+    return x
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantized_attention_equals_textbook_on_grid(orc, bits):
+    """On-grid caches dequantize exactly, so the oracle must equal plain fp64
+    softmax attention with rotary matrices applied to the raw inputs."""
+    rng = np.random.default_rng(40 + bits)
+    D, Bk, T = 16, 16, 48
+    L = (1 << bits) - 1
+    c = tiny(head_dim=D, k_block=Bk, tokens=T + 5, k_bits=bits, v_bits=bits, v_group=D, capacity=64)
+    k = np.concatenate([_on_grid(rng, T, D, Bk, L, True), rng.standard_normal((5, D))])
+    v = np.concatenate([_on_grid(rng, T, D, Bk, L, False), rng.standard_normal((5, D))])
+    kb, vb = f16(k), f16(v)
+    hc = orc.HeadCache(c).build(kb, vb)
+    assert np.array_equal(_deq(hc, 0), hval(kb)) and np.array_equal(_deq(hc, 1), hval(vb))
+    q = f16(rng.standard_normal(D) * 2)
+    for qp in (T + 4, 200, 3):
+        out = hc.decode(q, q_pos=qp)
+        qr = _rot_matrix(qp, D, 10000.0) @ hval(q)
+        kr = np.stack([_rot_matrix(t, D, 10000.0) @ hval(kb[t]) for t in range(T + 5)])
+        ref = _softmax_attn(qr, kr, hval(vb), D)
+        assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_blocks_are_independent_of_later_tokens(orc):
+    rng = np.random.default_rng(50)
+    c = tiny(head_dim=16, k_block=16, tokens=64, v_group=8, outlier_pct=7, clip_quantile=0.9)
+    k = _rand_block(rng, 64, 16, heavy=True)
+    v = _rand_block(rng, 64, 16, heavy=True)
+    a = orc.HeadCache(c).build(k[:37], v[:37])
+    b = orc.HeadCache(c).build(k, v)
+    n = 32
+    assert np.array_equal(a.k_codes[:n * 8], b.k_codes[:n * 8])
+    assert np.array_equal(a.v_codes[:n * 8], b.v_codes[:n * 8])
+    assert np.array_equal(a.k_scale[:2], b.k_scale[:2]) and np.array_equal(a.v_zero[:n], b.v_zero[:n])
+    assert np.array_equal(a.k_tail[:5], k[32:37]) and np.array_equal(a.v_tail[:5], v[32:37])
+    assert np.array_equal(a.dequantize(0, 0, 32), b.dequantize(0, 0, 32))
+    assert np.array_equal(a.dequantize(0, 32, 37), hval(k[32:37]).astype(np.float32))
