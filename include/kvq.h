@@ -1,0 +1,195 @@
+/*
+ * kvq.h -- C ABI of libkvq: 2/3/4-bit KV-cache quantization and single-query decode
+ * attention computed directly over the packed cache, on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, address):
+ *   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
+ *   [TQ]   "TurboQuant：突破大模型推理瓶颈的KVCache量化技术解析", mlqm.cn/news/1002276
+ *   [UQ]   "大模型长上下文推理优化：4-bit KV Cache量化技术解析与部署实践", mlqm.cn/news/1064729
+ *
+ * The three operations follow the problem the pages pose: quantize keys and values
+ * when they enter the cache, keeping per-block scale and zero-point metadata
+ * ([KVC3] "Quanto 的量化原理"; [TQ] section 4.2), accumulating tokens by block
+ * ([UQ] section 4.2); and either dequantize or compute attention directly on the
+ * quantized form when it is read ([KVC3] "Pre-RoPE Key Quantization" and the
+ * custom kernels of "Q-Norm 与其他细节"; [UQ] section 4.2 on fusing dequantization
+ * into attention).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Memory: the caller allocates every device buffer (sizes from kvq_cache_layout)
+ *   and frees it; the library allocates no device memory and keeps no state between
+ *   calls.  Pointers named *device* must be device (or managed) memory of the GPU
+ *   that is current on the calling thread.
+ * - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every call only enqueues work on it and returns; nothing synchronises the device.
+ * - Errors: arguments are checked on the host before anything is enqueued.  On any
+ *   error return nothing has been enqueued and the cache (including `length`) is
+ *   unchanged.  KVQ_EHIP means a launch failed after checking; the cache contents are
+ *   then undefined.  No C++ exception crosses this interface.
+ * - Inputs must be finite; the library does not scan for NaN or Inf.
+ * - Calls on different caches are independent; concurrent calls on one cache are
+ *   undefined.
+ *
+ * fp16 values are IEEE binary16 bit patterns (uint16_t).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvq_status;
+#define KVQ_OK 0
+#define KVQ_EINVAL (-1)        /* malformed arguments or descriptor                 */
+#define KVQ_EUNSUPPORTED (-2)  /* well-formed, but outside what the kernels build   */
+#define KVQ_ECAPACITY (-3)     /* append would exceed capacity; nothing written      */
+#define KVQ_EWORKSPACE (-4)    /* workspace too small                                */
+#define KVQ_EHIP (-5)          /* a HIP launch or query failed                       */
+
+/* Immutable description of one layer's cache.
+ *
+ * Keys: quantized before RoPE ([KVC3] "Pre-RoPE Key Quantization").
+ *   k_mode 0: uniform asymmetric, one fp16 scale and zero-point per channel per
+ *             block of k_block tokens ([KVC3] "Per-Channel Key Quantization").
+ *   k_mode 1: per-channel non-uniform codebook of 2^k_bits sorted fp16 entries,
+ *             supplied by the caller ([KVC3] "Non-Uniform KV Cache Quantization").
+ * Values: uniform asymmetric per token over groups of v_group channels, one fp16
+ *   scale and zero-point per group ([KVC3] "Quanto 的量化原理").
+ * clip_quantile q > 0: before the statistics, every dense value of a block is
+ *   clipped to [-t, t], t = the q-quantile of |x| over that block's k_block x
+ *   head_dim elements of the same tensor (exact order statistics, linear
+ *   interpolation), as the percentile clip of [UQ] section 4.2.  0 disables.
+ * outlier_pct p > 0: in every token vector of K and of V, the ceil(p*head_dim/100)
+ *   elements of largest |x| are kept exactly as fp16 in a per-token CSR and take
+ *   no part in the statistics ([KVC3] "Per-Vector Dense-and-Sparse Quantization").
+ * rope_theta: base of the rotary embedding applied to keys and the query at read
+ *   time (rotate-half pairs (i, i + head_dim/2), angle pos * theta^(-2i/head_dim)).
+ *
+ * Supported by the kernels: head_dim in {64, 128}; k_bits in {2, 3, 4} (k_mode 0 or
+ * 1); v_bits in {2, 4}; v_group in {16, 32, 64, 128} dividing head_dim; k_block in
+ * {64, 128}; capacity a positive multiple of k_block below 2^31; q_heads a multiple of
+ * kv_heads with q_heads/kv_heads <= 8; clip_quantile in [0, 1); outlier_pct in
+ * [0, 100] with ceil(p*head_dim/100) <= 4; rope_theta > 1.
+ */
+typedef struct {
+  int32_t batch, q_heads, kv_heads, head_dim, capacity;
+  int32_t k_bits, k_mode, k_block;
+  int32_t v_bits, v_group;
+  float clip_quantile;
+  int32_t outlier_pct;
+  float rope_theta;
+} kvq_config;
+
+/* Byte size of each buffer of a cache; 0 = buffer not used by this configuration. */
+typedef struct {
+  size_t k_codes, k_scale, k_zero, k_lut, k_tail;
+  size_t v_codes, v_scale, v_zero, v_tail;
+  size_t k_rowptr, k_col, k_val, v_rowptr, v_col, v_val;
+  size_t rope;
+} kvq_layout;
+
+/* A cache: caller-owned device buffers plus the host-side token count.
+ * Shapes, with BH = batch * kv_heads in (b, h) row-major order, T = capacity,
+ * D = head_dim, Bk = k_block, ko = outliers per vector (0 if off):
+ *
+ *  k_codes  u8   [BH][T][D*k_bits/8]  one packed row per token.  Row element e,
+ *                 at bits [e*k_bits, (e+1)*k_bits) of the little-endian row, LSB
+ *                 first (a 3-bit code may straddle two bytes), holds channel
+ *                 (e >> 1) + (e & 1) * D/2: each rotary pair sits side by side.
+ *  k_scale  fp16 [BH][T/Bk][D]        uniform keys: scale per block and channel.
+ *  k_zero   fp16 [BH][T/Bk][D]        uniform keys: zero-point (x = c*scale + zero).
+ *  k_lut    fp16 [kv_heads][D][2^k_bits] codebook keys: input, sorted ascending.
+ *  k_tail   fp16 [BH][Bk][D]          the length % Bk newest keys, unquantized.
+ *  v_codes  u32  [BH][T/(32/v_bits)][D] words: word (t / tpw, d), tpw = 32/v_bits,
+ *                 holds the codes of channel d for tpw consecutive tokens; token t
+ *                 at bits [(t % tpw)*v_bits, ...).
+ *  v_scale  fp16 [BH][T][D/v_group]
+ *  v_zero   fp16 [BH][T][D/v_group]
+ *  v_tail   fp16 [BH][Bk][D]
+ *  k_rowptr i32  [BH][T+1]            CSR row pointers of key outliers; for every
+ *                 quantized token rowptr[t+1] - rowptr[t] == ko and rowptr[0] == 0.
+ *  k_col    u8   [BH][T*ko]           outlier channels, ascending within a token.
+ *  k_val    fp16 [BH][T*ko]           outlier values, exact input bits.
+ *  v_rowptr, v_col, v_val: the same for values.
+ *  rope     f32  [Bk][D/2][2] cos/sin(j * f_i), then [T/Bk][D/2][2] cos/sin(n*Bk*f_i),
+ *                 with f_i = theta^(-2i/D); filled by kvq_cache_init.
+ *
+ * Tokens [0, floor(length/Bk)*Bk) are quantized; the rest live in the tails.
+ * At a quantized position that holds an outlier the stored code is 0; readers
+ * use the CSR value there.
+ */
+typedef struct {
+  kvq_config cfg;
+  int64_t length;
+  void *k_codes;
+  uint16_t *k_scale, *k_zero;
+  const uint16_t *k_lut;
+  uint16_t *k_tail;
+  void *v_codes;
+  uint16_t *v_scale, *v_zero, *v_tail;
+  int32_t *k_rowptr;
+  uint8_t *k_col;
+  uint16_t *k_val;
+  int32_t *v_rowptr;
+  uint8_t *v_col;
+  uint16_t *v_val;
+  float *rope;
+} kvq_cache;
+
+/* Text for a status code (static storage; never NULL). */
+const char *kvq_status_string(kvq_status s);
+
+/* Validate `cfg` and report the byte size of every buffer.  Host only; touches no
+ * GPU.  KVQ_EINVAL for malformed values, KVQ_EUNSUPPORTED for well-formed values the
+ * kernels do not build.  The total follows the cache-size formula of [TQ] section 2.1
+ * with the packed widths of [KVC3] "前言" (4 bits instead of 16). */
+kvq_status kvq_cache_layout(const kvq_config *cfg, kvq_layout *out);
+
+/* Prepare an empty cache: validates the descriptor and its buffer pointers,
+ * fills `rope` (angles evaluated in fp64) and sets length = 0.  Enqueued on `stream`. */
+kvq_status kvq_cache_init(kvq_cache *cache, void *stream);
+
+/* Append n_new tokens for every (b, kv-head): k_new, v_new are *device* fp16
+ * [batch][kv_heads][n_new][head_dim], keys pre-RoPE.  Every token block that
+ * becomes complete (absolute positions [j*Bk, (j+1)*Bk)) is quantized from its
+ * tokens (old tail + new); the remaining newest tokens go to the tails, as in the
+ * block accumulation of [UQ] section 4.2.  `length` grows by n_new on the host at
+ * enqueue time.  n_new == 0 is a no-op.  KVQ_ECAPACITY if length + n_new > capacity. */
+kvq_status kvq_quantize_append(kvq_cache *cache, const void *k_new, const void *v_new,
+                               int64_t n_new, void *stream);
+
+/* Bytes of device workspace kvq_decode_attention needs for `num_splits` splits of
+ * the cache per (b, kv-head) (0 = the library's choice for this cache). */
+size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_splits);
+
+/* Single-query decode attention over the whole cache:
+ *   out[b][hq] = softmax_t( RoPE(q[b][hq], q_pos) . RoPE(k_hat[b][h][t], t) / sqrt(D) ) v_hat[b][h][t]
+ * with h = hq / (q_heads/kv_heads), t in [0, length), k_hat and v_hat the
+ * dequantized keys and values (outliers and tails exact).  RoPE is applied to the
+ * keys after dequantization ([KVC3] "Pre-RoPE Key Quantization").
+ * q: *device* fp16 [batch][q_heads][head_dim], pre-RoPE.  out: *device* fp32
+ * [batch][q_heads][head_dim].  ws: *device* workspace of ws_bytes >=
+ * kvq_decode_workspace_bytes(cache, num_splits).  q_pos >= 0 (usually length-1).
+ * The result does not depend on num_splits beyond fp32 rounding and is bitwise
+ * reproducible for a fixed num_splits.  KVQ_EINVAL if length == 0. */
+kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int64_t q_pos,
+                                float *out, void *ws, size_t ws_bytes, int32_t num_splits,
+                                void *stream);
+
+/* Dequantize tokens [t0, t1) of keys (which = 0) or values (which = 1) into *device*
+ * fp32 out [batch][kv_heads][t1-t0][head_dim], pre-RoPE: x = fmaf(c, scale, zero) or
+ * the codebook entry, outlier positions and tail tokens exact.
+ * 0 <= t0 <= t1 <= length. */
+kvq_status kvq_dequantize(const kvq_cache *cache, int32_t which, int64_t t0, int64_t t1,
+                          float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

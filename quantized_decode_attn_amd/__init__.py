@@ -1,0 +1,217 @@
+"""Python binding of libkvq (2/3/4-bit KV-cache quantization and decode attention over
+the packed cache, HIP kernels for gfx950).
+
+Argument marshalling only: every step of the path runs inside libkvq.so.  PyTorch
+provides device memory and the current stream.  If the library has not been built
+every call raises: there is no fallback.
+
+The functions carry the names of the C ABI in ``include/kvq.h``
+(``kvq_cache_layout``, ``kvq_cache_init``, ``kvq_quantize_append``,
+``kvq_decode_workspace_bytes``, ``kvq_decode_attention``, ``kvq_dequantize``,
+``kvq_status_string``); ``Cache`` bundles the buffers of one cache.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4, -5
+EXPORTED = ["kvq_status_string", "kvq_cache_layout", "kvq_cache_init", "kvq_quantize_append",
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_dequantize"]
+
+
+class KvqConfig(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("q_heads", C.c_int32), ("kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("capacity", C.c_int32), ("k_bits", C.c_int32),
+                ("k_mode", C.c_int32), ("k_block", C.c_int32), ("v_bits", C.c_int32),
+                ("v_group", C.c_int32), ("clip_quantile", C.c_float), ("outlier_pct", C.c_int32),
+                ("rope_theta", C.c_float)]
+
+
+BUFFERS = ["k_codes", "k_scale", "k_zero", "k_lut", "k_tail", "v_codes", "v_scale", "v_zero",
+           "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val", "rope"]
+
+
+class KvqLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in BUFFERS]
+
+
+class KvqCache(C.Structure):
+    _fields_ = [("cfg", KvqConfig), ("length", C.c_int64)] + [(n, C.c_void_p) for n in BUFFERS]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, kvq_status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libkvq.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libkvq.so is not built (run quantized_decode_attn_amd/build.py "
+                              "or __graft_entry__.build()); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+        L.kvq_status_string.restype = C.c_char_p
+        L.kvq_status_string.argtypes = [i32]
+        L.kvq_cache_layout.restype = i32
+        L.kvq_cache_layout.argtypes = [C.POINTER(KvqConfig), C.POINTER(KvqLayout)]
+        L.kvq_cache_init.restype = i32
+        L.kvq_cache_init.argtypes = [C.POINTER(KvqCache), vp]
+        L.kvq_quantize_append.restype = i32
+        L.kvq_quantize_append.argtypes = [C.POINTER(KvqCache), vp, vp, i64, vp]
+        L.kvq_decode_workspace_bytes.restype = C.c_size_t
+        L.kvq_decode_workspace_bytes.argtypes = [C.POINTER(KvqCache), i32]
+        L.kvq_decode_attention.restype = i32
+        L.kvq_decode_attention.argtypes = [C.POINTER(KvqCache), vp, i64, vp, vp, C.c_size_t, i32, vp]
+        L.kvq_dequantize.restype = i32
+        L.kvq_dequantize.argtypes = [C.POINTER(KvqCache), i32, i64, i64, vp, vp]
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ C ABI, same names
+def kvq_status_string(status: int) -> str:
+    return lib().kvq_status_string(status).decode()
+
+
+def kvq_cache_layout(cfg: KvqConfig) -> KvqLayout:
+    out = KvqLayout()
+    st = lib().kvq_cache_layout(C.byref(cfg), C.byref(out))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_cache_layout")
+    return out
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def kvq_cache_init(cache: KvqCache, stream=None) -> None:
+    st = lib().kvq_cache_init(C.byref(cache), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_cache_init")
+
+
+def kvq_quantize_append(cache: KvqCache, k_new, v_new, n_new: int, stream=None) -> None:
+    st = lib().kvq_quantize_append(C.byref(cache), _ptr(k_new), _ptr(v_new), int(n_new), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_quantize_append")
+
+
+def kvq_decode_workspace_bytes(cache: KvqCache, num_splits: int = 0) -> int:
+    return int(lib().kvq_decode_workspace_bytes(C.byref(cache), int(num_splits)))
+
+
+def kvq_decode_attention(cache: KvqCache, q, q_pos: int, out, ws, ws_bytes: int, num_splits: int = 0,
+                         stream=None) -> None:
+    st = lib().kvq_decode_attention(C.byref(cache), _ptr(q), int(q_pos), _ptr(out), _ptr(ws),
+                                    int(ws_bytes), int(num_splits), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention")
+
+
+def kvq_dequantize(cache: KvqCache, which: int, t0: int, t1: int, out, stream=None) -> None:
+    st = lib().kvq_dequantize(C.byref(cache), int(which), int(t0), int(t1), _ptr(out), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_dequantize")
+
+
+# ------------------------------------------------------------------ convenience wrapper
+_CFG_FIELDS = [f[0] for f in KvqConfig._fields_]
+
+
+def make_config(cfg: dict) -> KvqConfig:
+    d = dict(cfg)
+    d.setdefault("capacity", d.get("tokens"))
+    return KvqConfig(**{k: d[k] for k in _CFG_FIELDS})
+
+
+class Cache:
+    """Device buffers of one cache (torch uint8 tensors sized by kvq_cache_layout) and the
+    C descriptor pointing at them.  ``lut`` (codebook keys) is a uint16 tensor
+    ``[kv_heads][D][2**k_bits]`` of fp16 bits, or None."""
+
+    def __init__(self, cfg: dict, device="cuda", lut=None, stream=None):
+        import torch
+        self.cfg = dict(cfg)
+        self.cfg.setdefault("capacity", self.cfg["tokens"])
+        self.c_cfg = make_config(self.cfg)
+        self.layout = kvq_cache_layout(self.c_cfg)
+        self.desc = KvqCache()
+        self.desc.cfg = self.c_cfg
+        self.bufs = {}
+        for name in BUFFERS:
+            size = getattr(self.layout, name)
+            if name == "k_lut":
+                if size:
+                    if lut is None:
+                        raise ValueError("a codebook is required for k_mode 1")
+                    t = lut.to(device=device).contiguous().view(torch.uint8).reshape(-1)
+                    if t.numel() != size:
+                        raise ValueError("codebook has %d bytes, expected %d" % (t.numel(), size))
+                    self.bufs[name] = t
+                    setattr(self.desc, name, t.data_ptr())
+                continue
+            if size:
+                t = torch.zeros(size, dtype=torch.uint8, device=device)
+                self.bufs[name] = t
+                setattr(self.desc, name, t.data_ptr())
+        kvq_cache_init(self.desc, stream)
+        self._ws = None
+
+    @property
+    def length(self) -> int:
+        return int(self.desc.length)
+
+    def append(self, k_new, v_new, stream=None) -> None:
+        """k_new, v_new: fp16 tensors [B][Hkv][N][D] on the device (keys pre-RoPE)."""
+        n = k_new.shape[2]
+        kvq_quantize_append(self.desc, k_new, v_new, n, stream)
+
+    def workspace(self, num_splits: int = 0):
+        import torch
+        need = kvq_decode_workspace_bytes(self.desc, num_splits)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 4), dtype=torch.uint8, device=self.bufs["rope"].device)
+        return self._ws
+
+    def decode(self, q, q_pos: int | None = None, num_splits: int = 0, out=None, stream=None):
+        """q: fp16 [B][Hq][D] on the device (pre-RoPE).  Returns fp32 [B][Hq][D]."""
+        import torch
+        if q_pos is None:
+            q_pos = self.length - 1
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        ws = self.workspace(num_splits)
+        kvq_decode_attention(self.desc, q, q_pos, out, ws, ws.numel(), num_splits, stream)
+        return out
+
+    def dequantize(self, which: int, t0: int = 0, t1: int | None = None, stream=None):
+        import torch
+        if t1 is None:
+            t1 = self.length
+        B, H, D = self.cfg["batch"], self.cfg["kv_heads"], self.cfg["head_dim"]
+        out = torch.empty((B, H, t1 - t0, D), dtype=torch.float32, device=self.bufs["rope"].device)
+        kvq_dequantize(self.desc, which, t0, t1, out, stream)
+        return out
+
+    def buffer(self, name: str):
+        """The raw device buffer (uint8) of one layout entry."""
+        return self.bufs.get(name)

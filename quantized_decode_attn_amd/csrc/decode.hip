@@ -1,0 +1,447 @@
+// decode.hip -- single-query decode attention computed directly on the packed cache.
+//
+// Pages cited (title, address):
+//   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
+//   [UQ]   "大模型长上下文推理优化：4-bit KV Cache量化技术解析与部署实践", mlqm.cn/news/1064729
+//   [TQ]   "TurboQuant：突破大模型推理瓶颈的KVCache量化技术解析", mlqm.cn/news/1002276
+//
+// Keys are stored before RoPE ([KVC3] "Pre-RoPE Key Quantization"), so the rotation
+// is applied at read time.  With channel pairs written as complex numbers
+// (k_i + i*k_{i+D/2}) the score of token t against the query at position p is
+//     s_t = sum_i Re( conj(q_i) e^{-i f_i p} e^{i f_i t} k_i ) / sqrt(D),
+// and t = n*Bk + j factors the rotation into a per-block term and a per-offset term.
+// Per block and pair the query-side weight W = conj(q) e^{-i f p} e^{i f n Bk} is
+// folded with the block's scale and zero-point (uniform keys) so that one token pair
+// costs six fused multiply-adds on its two integer codes plus the cos/sin of j*f
+// from an LDS table shared by every block, head and sequence.  Nothing is
+// dequantized to memory: the dequantize-then-attend fusion the pages ask for
+// ([TQ] sections 5.1 and 6.3; [UQ] section 4.2; the custom kernels of [KVC3]
+// "Q-Norm 与其他细节").
+//
+// Work split (split-K flash decoding): a work item is (b, kv-head, split); a split is
+// a contiguous range of Bk-token blocks (the last split of a sequence also takes the
+// unquantized tail).  Each wave owns whole items and keeps, for every query head of
+// its kv-head, the running max m, the running sum l and the unnormalised output o
+// (online softmax in base 2).  Partials (m, l, o) go to the workspace and a second
+// kernel merges the splits of every (b, q-head) in a fixed order.
+#include <math.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D, int KB, int KMODE, int VB>
+struct Shape {
+  static constexpr int HALF = D / 2;                  // rotary pairs
+  static constexpr int PPL = KB == 3 ? 16 : 8;        // pairs per lane
+  static constexpr int LPT = HALF / PPL;              // lanes per token
+  static constexpr int TPI = kWave / LPT;             // tokens per iteration
+  static constexpr int KW = 2 * PPL * KB / 32;        // code dwords per lane per token
+  static constexpr int TPW = 32 / VB;                 // tokens per value word
+  static constexpr int CPL = D / kWave;               // value channels per lane
+  static constexpr int TPITCH = D + 4;                // floats per rope-table row
+  static constexpr int NW = 12;                       // floats of per-pair weights
+};
+
+struct WaveLds {  // offsets (in floats) of one wave's scratch area
+  int wts, wq, p, ps, vs, vz, state, vc, lut, total;
+};
+
+__host__ __device__ inline WaveLds wave_lds(int D, int Bk, int gq, int ng, int tpi, int kb, int kmode,
+                                             bool ko) {
+  WaveLds w;
+  int o = 0;
+  w.wts = o; o += (D / 2) * 12;
+  w.wq = o; o += gq * D;
+  w.p = o; o += Bk;
+  w.ps = o; o += Bk * ng;
+  w.vs = o; o += Bk * ng;
+  w.vz = o; o += Bk * ng;
+  w.state = o; o += gq * (D + 2 + ng);
+  w.vc = o; o += ko ? tpi * D : 0;
+  w.lut = o; o += kmode == 1 ? D * (1 << kb) : 0;
+  w.total = o;
+  return w;
+}
+
+template <int KB, int KW>
+__device__ __forceinline__ uint32_t get_code(const uint32_t (&w)[KW], int k) {
+  const int p = k * KB;
+  uint32_t v = w[p >> 5] >> (p & 31);
+  if ((p & 31) + KB > 32) v |= w[(p >> 5) + 1] << (32 - (p & 31));
+  return v & ((1u << KB) - 1u);
+}
+
+template <int D, int KB, int KMODE, int VB>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
+                                                                const uint16_t* __restrict__ q,
+                                                                int64_t q_pos, float* __restrict__ ws,
+                                                                int S, int64_t nitems) {
+  using Sh = Shape<D, KB, KMODE, VB>;
+  extern __shared__ float lds[];
+  const int Bk = c.cfg.k_block;
+  const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, GQ = Hq / H;
+  const int G = c.cfg.v_group, ng = D / G;
+  const int ko = kout_of(c.cfg);
+  const int64_t T = c.cfg.capacity;
+  const int64_t nfull = c.length / Bk;
+  const int ntail = (int)(c.length - nfull * Bk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
+
+  // rotary offset table cos/sin(j * f_i), j < Bk, shared by the whole workgroup
+  float* table = lds;
+  for (int idx = threadIdx.x; idx < Bk * Sh::HALF; idx += kThreads) {
+    const int j = idx / Sh::HALF, i = idx % Sh::HALF;
+    table[j * Sh::TPITCH + 2 * i] = c.rope[2 * idx];
+    table[j * Sh::TPITCH + 2 * i + 1] = c.rope[2 * idx + 1];
+  }
+  const WaveLds L = wave_lds(D, Bk, GQ, ng, Sh::TPI, KB, KMODE, ko > 0);
+  float* wl = lds + Bk * Sh::TPITCH + wave * L.total;
+  float* wts = wl + L.wts;
+  float* wq = wl + L.wq;
+  float* Pl = wl + L.p;
+  float* PS = wl + L.ps;
+  float* VS = wl + L.vs;
+  float* VZ = wl + L.vz;
+  float* state = wl + L.state;
+  float* VC = wl + L.vc;
+  float* lutl = wl + L.lut;
+  const float* rope_blk = c.rope + (int64_t)Bk * D;  // [T/Bk][HALF][2]
+  __syncthreads();
+
+  const int64_t total_waves = (int64_t)gridDim.x * kWaves;
+  for (int64_t item = (int64_t)blockIdx.x * kWaves + wave; item < nitems; item += total_waves) {
+    const int split = (int)(item % S);
+    const int64_t bh = item / S;
+    const int h = (int)(bh % H);
+    const int b = (int)(bh / H);
+    const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
+    const bool do_tail = split == S - 1 && ntail > 0;
+
+    // ---- per item: query weights Wq = scale * conj(q) * e^{-i f p} (fp64), state reset
+    for (int g = 0; g < GQ; ++g) {
+      const uint16_t* qv = q + ((int64_t)b * Hq + (int64_t)h * GQ + g) * D;
+      for (int i = lane; i < Sh::HALF; i += kWave) {
+        const double qa = (double)h2f(qv[i]), qb = (double)h2f(qv[i + Sh::HALF]);
+        const double f = pow((double)c.cfg.rope_theta, -(2.0 * i) / (double)D);
+        double sn, cs;
+        sincos((double)q_pos * f, &sn, &cs);
+        const double sc = (double)kLog2e / sqrt((double)D);
+        wq[g * D + 2 * i] = (float)(sc * (qa * cs - qb * sn));
+        wq[g * D + 2 * i + 1] = (float)(-sc * (qa * sn + qb * cs));
+      }
+      float* st = state + g * (D + 2 + ng);
+      for (int k = lane; k < D + 2 + ng; k += kWave) st[k] = k == 0 ? -__builtin_inff() : 0.0f;
+    }
+    if (KMODE == 1) {
+      for (int k = lane; k < D * (1 << KB); k += kWave)
+        lutl[k] = h2f(c.k_lut[(int64_t)h * D * (1 << KB) + k]);
+    }
+    wave_lds_sync();
+
+    const uint8_t* kcodes = static_cast<const uint8_t*>(c.k_codes) + bh * T * (D * KB / 8);
+    const uint32_t* vwords = static_cast<const uint32_t*>(c.v_codes) + bh * (T / Sh::TPW) * D;
+
+    const int64_t nblocks = (n1 - n0) + (do_tail ? 1 : 0);
+    for (int64_t bi = 0; bi < nblocks; ++bi) {
+      const bool tail = bi == n1 - n0;
+      const int64_t n = tail ? nfull : n0 + bi;
+      const int64_t tb = n * Bk;                         // absolute first token
+      const int ntok = tail ? ntail : Bk;
+      const int iters = (ntok + Sh::TPI - 1) / Sh::TPI;
+
+      // value metadata of the block (quantized blocks only)
+      if (!tail) {
+        for (int k = lane; k < Bk * ng; k += kWave) {
+          const int64_t m = (bh * T + tb) * ng + k;
+          VS[k] = h2f(c.v_scale[m]);
+          VZ[k] = h2f(c.v_zero[m]);
+        }
+      }
+
+      for (int g = 0; g < GQ; ++g) {
+        float* st = state + g * (D + 2 + ng);
+        // ---- per block and pair: W = Wq * e^{i f n Bk}, folded with the metadata
+        for (int i = lane; i < Sh::HALF; i += kWave) {
+          const float qr = wq[g * D + 2 * i], qi = wq[g * D + 2 * i + 1];
+          const float cb = rope_blk[(n * Sh::HALF + i) * 2], sb = rope_blk[(n * Sh::HALF + i) * 2 + 1];
+          const float wr = qr * cb - qi * sb, wi = qr * sb + qi * cb;
+          float* o = wts + i * Sh::NW;
+          if (KMODE == 0 && !tail) {
+            const int64_t m = (bh * (T / Bk) + n) * D;
+            const float al = h2f(c.k_scale[m + i]), be = h2f(c.k_scale[m + i + Sh::HALF]);
+            const float za = h2f(c.k_zero[m + i]), zb = h2f(c.k_zero[m + i + Sh::HALF]);
+            o[0] = wr * al;
+            o[1] = -wi * be;
+            o[2] = wr * za - wi * zb;
+            o[3] = -wi * al;
+            o[4] = -wr * be;
+            o[5] = -(wi * za + wr * zb);
+            o[6] = za;
+            o[7] = zb;
+          }
+          o[8] = wr;
+          o[9] = wi;
+        }
+        wave_lds_sync();
+
+        // ---- scores: lane (ts, r) covers pairs [r*PPL, r*PPL+PPL) of token it*TPI+ts
+        float A1[Sh::PPL], B1[Sh::PPL], Z1[Sh::PPL], A2[Sh::PPL], B2[Sh::PPL], Z2[Sh::PPL];
+        float WR[Sh::PPL], WI[Sh::PPL];
+#pragma unroll
+        for (int m = 0; m < Sh::PPL; ++m) {
+          const float* o = wts + (r * Sh::PPL + m) * Sh::NW;
+          A1[m] = o[0]; B1[m] = o[1]; Z1[m] = o[2]; A2[m] = o[3]; B2[m] = o[4]; Z2[m] = o[5];
+          WR[m] = o[8]; WI[m] = o[9];
+        }
+        constexpr int MAXIT = 128 / Sh::TPI;  // k_block <= 128
+        float sc[MAXIT];
+        float mloc = -__builtin_inff();
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+          if (it >= iters) break;
+          const int j = it * Sh::TPI + ts;
+          float s = 0.0f;
+          if (j < ntok) {
+            const float* tab = table + j * Sh::TPITCH + 2 * r * Sh::PPL;
+            if (!tail) {
+              uint32_t w[Sh::KW];
+              const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                  kcodes + (tb + j) * (D * KB / 8) + r * (Sh::KW * 4));
+#pragma unroll
+              for (int k = 0; k < Sh::KW; ++k) w[k] = src[k];
+#pragma unroll
+              for (int m = 0; m < Sh::PPL; ++m) {
+                const float cs = tab[2 * m], sn = tab[2 * m + 1];
+                const uint32_t ca = get_code<KB, Sh::KW>(w, 2 * m), cb = get_code<KB, Sh::KW>(w, 2 * m + 1);
+                float X, Y;
+                if (KMODE == 0) {
+                  X = __builtin_fmaf(B1[m], (float)cb, __builtin_fmaf(A1[m], (float)ca, Z1[m]));
+                  Y = __builtin_fmaf(B2[m], (float)cb, __builtin_fmaf(A2[m], (float)ca, Z2[m]));
+                } else {
+                  const int ch = r * Sh::PPL + m;
+                  const float a = lutl[ch * (1 << KB) + ca];
+                  const float bb = lutl[(ch + Sh::HALF) * (1 << KB) + cb];
+                  X = __builtin_fmaf(WR[m], a, -WI[m] * bb);
+                  Y = -__builtin_fmaf(WI[m], a, WR[m] * bb);
+                }
+                s = __builtin_fmaf(cs, X, __builtin_fmaf(sn, Y, s));
+              }
+              // outlier corrections: code 0 was stored there, the CSR holds the value
+              if (r < ko) {
+                const int64_t e = (bh * T + tb + j) * ko + r;
+                const int col = c.k_col[e];
+                const float xo = h2f(c.k_val[e]);
+                const int i = col % Sh::HALF;
+                const float* o = wts + i * Sh::NW;
+                const float cs = table[j * Sh::TPITCH + 2 * i], sn = table[j * Sh::TPITCH + 2 * i + 1];
+                const float wr = o[8], wi = o[9];
+                float x0;
+                if (KMODE == 0) x0 = col < Sh::HALF ? o[6] : o[7];
+                else x0 = lutl[col * (1 << KB)];
+                const float dlt = xo - x0;
+                s += col < Sh::HALF ? dlt * (wr * cs - wi * sn) : -dlt * (wi * cs + wr * sn);
+              }
+            } else {
+              const uint16_t* kr = c.k_tail + (bh * Bk + j) * D;
+#pragma unroll
+              for (int m = 0; m < Sh::PPL; ++m) {
+                const int i = r * Sh::PPL + m;
+                const float a = h2f(kr[i]), bb = h2f(kr[i + Sh::HALF]);
+                const float cs = tab[2 * m], sn = tab[2 * m + 1];
+                const float X = __builtin_fmaf(WR[m], a, -WI[m] * bb);
+                const float Y = -__builtin_fmaf(WI[m], a, WR[m] * bb);
+                s = __builtin_fmaf(cs, X, __builtin_fmaf(sn, Y, s));
+              }
+            }
+          }
+          s = group_sum<Sh::LPT>(s);
+          if (j >= ntok) s = -__builtin_inff();
+          sc[it] = s;
+          mloc = fmaxf(mloc, s);
+        }
+        // ---- online softmax (base 2)
+        const float mblk = wave_max(mloc);
+        const float mold = st[0];
+        const float mnew = fmaxf(mold, mblk);
+        const float alpha = exp2f(mold - mnew);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+          if (it >= iters) break;
+          const int j = it * Sh::TPI + ts;
+          const float p = j < ntok ? exp2f(sc[it] - mnew) : 0.0f;
+          if (r == 0) {
+            lsum += p;
+            if (j < ntok) Pl[j] = p;
+          }
+        }
+        lsum = wave_sum(lsum);
+        wave_lds_sync();
+
+        // ---- values
+        float acc[Sh::CPL];
+#pragma unroll
+        for (int k = 0; k < Sh::CPL; ++k) acc[k] = st[2 + lane + k * kWave] * alpha;
+        if (!tail) {
+          for (int k = lane; k < Bk * ng; k += kWave) PS[k] = Pl[k / ng] * VS[k];
+          float zp[8];
+          for (int gg = 0; gg < ng; ++gg) zp[gg] = 0.0f;
+          for (int t = lane; t < Bk; t += kWave)
+            for (int gg = 0; gg < ng; ++gg) zp[gg] = __builtin_fmaf(Pl[t], VZ[t * ng + gg], zp[gg]);
+          for (int gg = 0; gg < ng; ++gg) {
+            const float z = wave_sum(zp[gg]);
+            if (lane == 0) st[2 + D + gg] = st[2 + D + gg] * alpha + z;
+          }
+          wave_lds_sync();
+          const int64_t wbase = tb / Sh::TPW;
+          for (int gw = 0; gw < Bk / Sh::TPW; ++gw) {
+#pragma unroll
+            for (int k = 0; k < Sh::CPL; ++k) {
+              const int ch = lane + k * kWave;
+              const uint32_t word = vwords[(wbase + gw) * D + ch];
+              const int grp = ch / G;
+#pragma unroll
+              for (int u = 0; u < Sh::TPW; ++u) {
+                const uint32_t code = (word >> (u * VB)) & ((1u << VB) - 1u);
+                acc[k] = __builtin_fmaf(PS[(gw * Sh::TPW + u) * ng + grp], (float)code, acc[k]);
+              }
+            }
+          }
+          // value outliers: rows of VC are token slots, so one instruction never
+          // updates one address twice
+          if (ko > 0) {
+            for (int k = lane; k < Sh::TPI * D; k += kWave) VC[k] = 0.0f;
+            wave_lds_sync();
+            for (int it = 0; it < iters; ++it) {
+              const int j = it * Sh::TPI + ts;
+              if (r < ko) {
+                const int64_t e = (bh * T + tb + j) * ko + r;
+                const int col = c.v_col[e];
+                const float dlt = h2f(c.v_val[e]) - VZ[j * ng + col / G];
+                VC[ts * D + col] += Pl[j] * dlt;
+              }
+              wave_lds_sync();
+            }
+#pragma unroll
+            for (int k = 0; k < Sh::CPL; ++k)
+              for (int row = 0; row < Sh::TPI; ++row) acc[k] += VC[row * D + lane + k * kWave];
+          }
+        } else {
+          for (int j = 0; j < ntok; ++j) {
+            const float p = Pl[j];
+#pragma unroll
+            for (int k = 0; k < Sh::CPL; ++k)
+              acc[k] = __builtin_fmaf(p, h2f(c.v_tail[(bh * Bk + j) * D + lane + k * kWave]), acc[k]);
+          }
+          if (lane == 0)
+            for (int gg = 0; gg < ng; ++gg) st[2 + D + gg] *= alpha;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < Sh::CPL; ++k) st[2 + lane + k * kWave] = acc[k];
+        if (lane == 0) {
+          st[0] = mnew;
+          st[1] = st[1] * alpha + lsum;
+        }
+        wave_lds_sync();
+      }
+    }
+
+    // ---- write the partial of every query head of this kv head
+    for (int g = 0; g < GQ; ++g) {
+      const float* st = state + g * (D + 2 + ng);
+      float* dst = ws + (((int64_t)b * Hq + (int64_t)h * GQ + g) * S + split) * (D + 2);
+      for (int k = lane; k < D; k += kWave) dst[2 + k] = st[2 + k] + st[2 + D + k / G];
+      if (lane == 0) {
+        dst[0] = st[0];
+        dst[1] = st[1];
+      }
+    }
+    wave_lds_sync();
+  }
+}
+
+// Merge the S partials of one (b, q-head) in split order: out = sum_s o_s 2^(m_s-M) / sum_s l_s 2^(m_s-M).
+__global__ void decode_combine_kernel(const float* __restrict__ ws, float* __restrict__ out, int S, int D) {
+  const int64_t bq = blockIdx.x;
+  const float* base = ws + bq * (int64_t)S * (D + 2);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float M = -__builtin_inff();
+    for (int s = 0; s < S; ++s) M = fmaxf(M, base[(int64_t)s * (D + 2)]);
+    float Lsum = 0.0f, O = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      const float* p = base + (int64_t)s * (D + 2);
+      if (p[0] == -__builtin_inff()) continue;  // empty split
+      const float w = exp2f(p[0] - M);
+      Lsum = __builtin_fmaf(p[1], w, Lsum);
+      O = __builtin_fmaf(p[2 + d], w, O);
+    }
+    out[bq * D + d] = O / Lsum;
+  }
+}
+
+template <int D, int KB, int KMODE, int VB>
+hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
+                        int S, hipStream_t s) {
+  using Sh = Shape<D, KB, KMODE, VB>;
+  const int GQ = c.cfg.q_heads / c.cfg.kv_heads, ng = D / c.cfg.v_group;
+  const WaveLds L = wave_lds(D, c.cfg.k_block, GQ, ng, Sh::TPI, KB, KMODE, host_kout(c.cfg) > 0);
+  const size_t bytes = ((size_t)c.cfg.k_block * Sh::TPITCH + (size_t)kWaves * L.total) * sizeof(float);
+  if (bytes > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<D, KB, KMODE, VB>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
+  int64_t grid = (nitems + kWaves - 1) / kWaves;
+  const int64_t cap = (int64_t)cus * (bytes <= 80 * 1024 ? 2 : 1);
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, KMODE, VB>), dim3((unsigned)grid), dim3(kThreads), bytes, s,
+                     c, q, q_pos, ws, S, nitems);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(D), 0, s, ws,
+                     out, S, D);
+  return hipGetLastError();
+}
+
+template <int D, int KB, int KMODE>
+hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws, int S,
+                     hipStream_t s) {
+  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, q_pos, out, ws, S, s);
+  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, q_pos, out, ws, S, s);
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_d(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws, int S,
+                    hipStream_t s) {
+  const int kb = c.cfg.k_bits, km = c.cfg.k_mode;
+  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, q_pos, out, ws, S, s);
+  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, q_pos, out, ws, S, s);
+  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, q_pos, out, ws, S, s);
+  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, q_pos, out, ws, S, s);
+  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, q_pos, out, ws, S, s);
+  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, q_pos, out, ws, S, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
+                         int splits, hipStream_t s) {
+  if (c.cfg.head_dim == 128) return launch_d<128>(c, q, q_pos, out, ws, splits, s);
+  if (c.cfg.head_dim == 64) return launch_d<64>(c, q, q_pos, out, ws, splits, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,183 @@
+// kvq_api.hip -- the C ABI: argument checking, buffer sizes, launch sequencing.
+// Nothing here allocates device memory; every launch goes on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+kvq_status check_cfg(const kvq_config* c) {
+  if (!c) return KVQ_EINVAL;
+  if (c->batch <= 0 || c->q_heads <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->capacity <= 0)
+    return KVQ_EINVAL;
+  if (c->head_dim % 2 || c->q_heads % c->kv_heads) return KVQ_EINVAL;
+  if (c->k_bits < 1 || c->k_bits > 8 || c->v_bits < 1 || c->v_bits > 8) return KVQ_EINVAL;
+  if (c->k_mode != 0 && c->k_mode != 1) return KVQ_EINVAL;
+  if (c->k_block <= 0 || c->capacity % c->k_block) return KVQ_EINVAL;
+  if (c->v_group <= 0 || c->head_dim % c->v_group) return KVQ_EINVAL;
+  if (!(c->clip_quantile >= 0.0f && c->clip_quantile < 1.0f)) return KVQ_EINVAL;
+  if (c->outlier_pct < 0 || c->outlier_pct > 100) return KVQ_EINVAL;
+  if (!(c->rope_theta > 1.0f) || !isfinite(c->rope_theta)) return KVQ_EINVAL;
+  // what the kernels are built for
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_EUNSUPPORTED;
+  if (c->k_bits < 2 || c->k_bits > 4) return KVQ_EUNSUPPORTED;
+  if (c->v_bits != 2 && c->v_bits != 4) return KVQ_EUNSUPPORTED;
+  if (c->v_group != 16 && c->v_group != 32 && c->v_group != 64 && c->v_group != 128)
+    return KVQ_EUNSUPPORTED;
+  if (c->k_block != 64 && c->k_block != 128) return KVQ_EUNSUPPORTED;
+  if (c->q_heads / c->kv_heads > 8) return KVQ_EUNSUPPORTED;
+  if (kvq::host_kout(*c) > 4) return KVQ_EUNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache* cache) {
+  if (!cache) return KVQ_EINVAL;
+  kvq_status st = check_cfg(&cache->cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = cache->cfg;
+  if (!cache->k_codes || !cache->k_tail || !cache->v_codes || !cache->v_scale || !cache->v_zero ||
+      !cache->v_tail || !cache->rope)
+    return KVQ_EINVAL;
+  if (c.k_mode == 0 && (!cache->k_scale || !cache->k_zero)) return KVQ_EINVAL;
+  if (c.k_mode == 1 && !cache->k_lut) return KVQ_EINVAL;
+  if (kvq::host_kout(c) > 0 && (!cache->k_rowptr || !cache->k_col || !cache->k_val ||
+                                !cache->v_rowptr || !cache->v_col || !cache->v_val))
+    return KVQ_EINVAL;
+  if (cache->length < 0 || cache->length > c.capacity) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+int auto_splits(const kvq_config& c) {
+  // Aim at a few thousand (b, kv-head, split) work items so that every wave of the
+  // chip gets whole items, without splitting a sequence below one block per split.
+  const int64_t units = (int64_t)c.batch * c.kv_heads;
+  int64_t s = (4096 + units - 1) / units;
+  const int64_t nblk = c.capacity / c.k_block;
+  if (s > nblk) s = nblk;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration";
+    case KVQ_ECAPACITY: return "cache capacity exceeded";
+    case KVQ_EWORKSPACE: return "workspace too small";
+    case KVQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout* out) {
+  if (!out) return KVQ_EINVAL;
+  kvq_status st = check_cfg(cfg);
+  if (st != KVQ_OK) return st;
+  const kvq_config& c = *cfg;
+  const size_t BH = (size_t)c.batch * c.kv_heads, D = c.head_dim, T = c.capacity;
+  const size_t nblk = T / c.k_block, ko = kvq::host_kout(c);
+  memset(out, 0, sizeof *out);
+  out->k_codes = BH * T * D * c.k_bits / 8;
+  if (c.k_mode == 0) {
+    out->k_scale = BH * nblk * D * 2;
+    out->k_zero = out->k_scale;
+  } else {
+    out->k_lut = (size_t)c.kv_heads * D * ((size_t)1 << c.k_bits) * 2;
+  }
+  out->k_tail = BH * c.k_block * D * 2;
+  out->v_codes = BH * T * D * c.v_bits / 8;
+  out->v_scale = BH * T * (D / c.v_group) * 2;
+  out->v_zero = out->v_scale;
+  out->v_tail = out->k_tail;
+  if (ko) {
+    out->k_rowptr = BH * (T + 1) * 4;
+    out->k_col = BH * T * ko;
+    out->k_val = BH * T * ko * 2;
+    out->v_rowptr = out->k_rowptr;
+    out->v_col = out->k_col;
+    out->v_val = out->k_val;
+  }
+  out->rope = ((size_t)c.k_block + nblk) * (D / 2) * 2 * 4;
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_init(kvq_cache* cache, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = from_hip(kvq::launch_rope_init(*cache, (hipStream_t)stream));
+  if (st == KVQ_OK) cache->length = 0;
+  return st;
+}
+
+kvq_status kvq_quantize_append(kvq_cache* cache, const void* k_new, const void* v_new,
+                               int64_t n_new, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (n_new < 0) return KVQ_EINVAL;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_EINVAL;
+  const kvq_config& c = cache->cfg;
+  const int64_t L0 = cache->length, L1 = L0 + n_new, Bk = c.k_block;
+  if (L1 > c.capacity) return KVQ_ECAPACITY;
+  const int64_t nf0 = L0 / Bk, nf1 = L1 / Bk;
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* kn = (const uint16_t*)k_new;
+  const uint16_t* vn = (const uint16_t*)v_new;
+  if (nf1 > nf0) {
+    st = from_hip(kvq::launch_quantize(*cache, kn, vn, L0, n_new, nf0, nf1 - nf0, s));
+    if (st != KVQ_OK) return st;
+  }
+  // the newest L1 % Bk tokens stay unquantized in the tails
+  const int64_t rem = L1 - nf1 * Bk;
+  if (rem > 0) {
+    const int64_t src0 = n_new - (nf1 > nf0 ? rem : n_new);
+    const int64_t dst0 = nf1 > nf0 ? 0 : L0 - nf0 * Bk;
+    st = from_hip(kvq::launch_tail_copy(*cache, kn, vn, n_new, src0, dst0, s));
+    if (st != KVQ_OK) return st;
+  }
+  cache->length = L1;
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_splits) {
+  if (check_cache(cache) != KVQ_OK || num_splits < 0) return 0;
+  const kvq_config& c = cache->cfg;
+  const int S = num_splits ? num_splits : auto_splits(c);
+  return (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int64_t q_pos, float* out,
+                                void* ws, size_t ws_bytes, int32_t num_splits, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || q_pos < 0 || num_splits < 0 || cache->length == 0) return KVQ_EINVAL;
+  if (q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
+  const kvq_config& c = cache->cfg;
+  const int S = num_splits ? num_splits : auto_splits(c);
+  if (S > (1 << 20)) return KVQ_EINVAL;
+  const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
+  if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
+  return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, (float*)ws, S,
+                                     (hipStream_t)stream));
+}
+
+kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, int64_t t0, int64_t t1, float* out,
+                          void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if ((which != 0 && which != 1) || t0 < 0 || t1 < t0 || t1 > cache->length) return KVQ_EINVAL;
+  if (t1 == t0) return KVQ_OK;
+  if (!out) return KVQ_EINVAL;
+  return from_hip(kvq::launch_dequantize(*cache, which, t0, t1, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

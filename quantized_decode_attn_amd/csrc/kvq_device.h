@@ -1,0 +1,80 @@
+// kvq_device.h -- device helpers shared by the libkvq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- fp16 helpers
+// Conversions use the hardware v_cvt_f32_f16 / v_cvt_f16_f32 (round to nearest even).
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f2h_rn(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+__device__ __forceinline__ uint16_t h_step_down(uint16_t h) {
+  if ((h & 0x7fff) == 0) return 0x8001;
+  return (h & 0x8000) ? (uint16_t)(h + 1) : (uint16_t)(h - 1);
+}
+__device__ __forceinline__ uint16_t h_step_up(uint16_t h) {
+  if ((h & 0x7fff) == 0) return 0x0001;
+  return (h & 0x8000) ? (uint16_t)(h - 1) : (uint16_t)(h + 1);
+}
+// Largest fp16 not above v, and smallest fp16 not below v (directed rounding done
+// as round-to-nearest followed by a one-step correction of the bit pattern).
+__device__ __forceinline__ uint16_t f2h_rd(float v) {
+  uint16_t h = f2h_rn(v);
+  return h2f(h) > v ? h_step_down(h) : h;
+}
+__device__ __forceinline__ uint16_t f2h_ru(float v) {
+  uint16_t h = f2h_rn(v);
+  return h2f(h) < v ? h_step_up(h) : h;
+}
+
+// ---------------------------------------------------------------- cross-lane
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i <-> 7-i within 8
+constexpr int kDppRowMirror = 0x140;    // row_mirror: lane i <-> 15-i within 16
+
+// Sum over aligned groups of N lanes (N in {1,2,4,8,16}); every lane of the group
+// receives the group sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_f<kDppQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Wave-local ordering point for LDS traffic exchanged between lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int kout_of(const kvq_config& c) {
+  return c.outlier_pct > 0 ? (c.outlier_pct * c.head_dim + 99) / 100 : 0;
+}
+
+}  // namespace kvq

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Quantized caches (codes, scales, zeros, outlier CSR, tails) and dequantized values
+must be bit-identical; decode outputs must be within 2e-3 (max abs) of the oracle's
+fp64 attention over the same quantized cache.  Small cases span several blocks and a
+ragged tail and are compared in full; the five workloads at their full sizes are
+compared on sampled heads, in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import synth
+from _gpu_util import build_gpu_cache, compare_head, inputs, oracle_heads, say, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import quantized_decode_attn_amd as kvq
+    kvq.lib()                                   # raises if the library is not built
+    import oracle
+    oracle.build()
+
+
+SMALL = {
+    "c0": (synth.config("c0"), None),
+    "c0_ragged": (synth.config("c0", tokens=293, capacity=320), [37, 64, 192]),
+    "mha_int4_d128": (synth.config("c1", batch=2, q_heads=4, kv_heads=4, tokens=3 * 128 + 50,
+                                   capacity=512), [100, 30, 304]),
+    "gqa_csr_inject": (synth.config("c2", batch=2, q_heads=8, kv_heads=2, tokens=4 * 128 + 77,
+                                    capacity=640), None),
+    "lut3_v2": (synth.config("c3", batch=1, q_heads=4, kv_heads=4, tokens=5 * 128 + 3,
+                             capacity=768), [640, 3]),
+    "clip_csr_append": (synth.config("c4", batch=2, q_heads=4, kv_heads=4, tokens=5 * 128 + 57,
+                                     capacity=768), [2 * 128 + 17, 3 * 128 + 40]),
+    "k2_v2_g16_gqa_d64": (synth.config("c0", k_bits=2, v_bits=2, v_group=16, tokens=200,
+                                       capacity=256, q_heads=8, kv_heads=2), [5, 195]),
+    "k3_uniform_g32": (synth.config("c1", batch=1, q_heads=2, kv_heads=2, k_bits=3, v_group=32,
+                                    tokens=300, capacity=384), None),
+    "lut4_bk64_csr": (synth.config("c3", batch=1, q_heads=2, kv_heads=2, k_bits=4, k_block=64,
+                                   v_bits=4, v_group=128, tokens=333, capacity=384, outlier_pct=2),
+                      None),
+    "lut2_d64_clip": (synth.config("c0", k_mode=1, k_bits=2, v_group=32, tokens=150, capacity=192,
+                                   clip_quantile=0.9), None),
+}
+
+
+def _lut(cfg):
+    return synth.calib_lut(cfg) if cfg["k_mode"] == 1 else None
+
+
+def _q(cfg):
+    return synth.gen_q(cfg)
+
+
+def _decode_ref(cfg, heads, q, q_pos):
+    """Oracle outputs [B][Hq][D] (fp64) for every (b, q-head)."""
+    import oracle
+    B, Hq, H = cfg["batch"], cfg["q_heads"], cfg["kv_heads"]
+    gq = Hq // H
+    hl, ql = [], []
+    for b in range(B):
+        for hq in range(Hq):
+            hl.append(heads[(b, hq // gq)])
+            ql.append(q[b, hq])
+    out = oracle.decode_many(cfg, hl, np.stack(ql), q_pos)
+    return out.reshape(B, Hq, -1)
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_cases_bitwise_and_decode(case):
+    import torch
+    import oracle
+    cfg, chunks = SMALL[case]
+    say("case", case, cfg)
+    k, v = inputs(cfg)
+    lut = _lut(cfg)
+    cache = build_gpu_cache(cfg, k, v, chunks, lut)
+    heads = oracle_heads(cfg, k, v, lut)
+    ko = oracle.kout(cfg)
+    assert cache.length == cfg["tokens"]
+    for (b, h), hc in heads.items():
+        compare_head(cache, hc, cfg, ko, b, h)
+    for which in (0, 1):
+        g = cache.dequantize(which).cpu().numpy()
+        for (b, h), hc in heads.items():
+            o = hc.dequantize(which)
+            assert np.array_equal(g[b, h].view(np.uint32), o.view(np.uint32)), (which, b, h)
+    q = _q(cfg)
+    qd = upload(q)
+    for q_pos in (cfg["tokens"] - 1, cfg["tokens"] + 1000, 3):
+        out = cache.decode(qd, q_pos=q_pos).cpu().numpy().astype(np.float64)
+        ref = _decode_ref(cfg, heads, q, q_pos)
+        err = np.abs(out - ref).max()
+        say("  q_pos", q_pos, "max abs err", err)
+        assert err <= TOL
+    torch.cuda.synchronize()
+
+
+def test_split_count_invariance_and_determinism():
+    cfg, _ = SMALL["clip_csr_append"]
+    k, v = inputs(cfg)
+    cache = build_gpu_cache(cfg, k, v)
+    qd = upload(_q(cfg))
+    outs = {}
+    for S in (1, 3, 7, 64):
+        a = cache.decode(qd, num_splits=S).cpu().numpy()
+        b = cache.decode(qd, num_splits=S).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), S
+        outs[S] = a
+    for S in (3, 7, 64):
+        assert np.abs(outs[S] - outs[1]).max() <= 4e-6, S
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65])
+def test_short_caches(n):
+    """Tail-only caches, exactly one block, one block plus one token."""
+    import oracle
+    cfg = synth.config("c0", tokens=n, capacity=128)
+    k, v = inputs(cfg)
+    cache = build_gpu_cache(cfg, k, v, [n])
+    heads = oracle_heads(cfg, k, v)
+    for (b, h), hc in heads.items():
+        compare_head(cache, hc, cfg, 0, b, h)
+    q = _q(cfg)
+    out = cache.decode(upload(q)).cpu().numpy()
+    ref = _decode_ref(cfg, heads, q, n - 1)
+    assert np.abs(out - ref).max() <= TOL
+
+
+def test_append_errors_do_not_touch_the_cache():
+    import quantized_decode_attn_amd as kvq
+    cfg = synth.config("c0", tokens=100, capacity=128)
+    k, v = inputs(cfg)
+    cache = build_gpu_cache(cfg, k, v)
+    before = {n: t.clone() for n, t in cache.bufs.items()}
+    with pytest.raises(kvq.KvqError) as e:
+        cache.append(upload(k[:, :, :29]), upload(v[:, :, :29]))
+    assert e.value.status == kvq.KVQ_ECAPACITY and cache.length == 100
+    for n, t in cache.bufs.items():
+        assert bool((t == before[n]).all()), n
+
+
+# --------------------------------------------------------------------------- full sizes
+SAMPLE = {
+    "c1": [(0, 0), (7, 31), (3, 17)],
+    "c2": [(0, 0), (3, 7), (2, 3)],
+    "c3": [(0, 0), (0, 21)],
+    "c4": [(0, 0), (15, 31), (9, 4)],
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_size_sampled(name):
+    """The workload at its full size, appended as the benchmark appends it; sampled
+    heads compared bitwise and sampled decode outputs against the oracle."""
+    import torch
+    import oracle
+    cfg = synth.config(name)
+    say("full-size", name, cfg["workload"])
+    lut = _lut(cfg)
+    T = cfg["tokens"]
+    import quantized_decode_attn_amd as kvq
+    dev = torch.device("cuda:0")
+    lut_t = None if lut is None else torch.from_numpy(lut.view(np.int16)).to(dev)
+    cache = kvq.Cache(cfg, device=dev, lut=lut_t)
+    step = cfg["existing"] if cfg["existing"] else min(T, 131072)
+    t = 0
+    while t < T:
+        n = min(step, T - t)
+        k, v = inputs(cfg, t, t + n)
+        cache.append(upload(k), upload(v))
+        del k, v
+        t += n
+    torch.cuda.synchronize()
+    say("  appended", cache.length)
+    sample = SAMPLE[name]
+    heads = {}
+    for (b, h) in sample:
+        kh = synth.gen_head(cfg, synth.TENSOR_K, b, h)
+        vh = synth.gen_head(cfg, synth.TENSOR_V, b, h)
+        hc = oracle.HeadCache(cfg, None if lut is None else lut[h]).build(kh, vh)
+        compare_head(cache, hc, cfg, oracle.kout(cfg), b, h)
+        heads[(b, h)] = hc
+    say("  sampled heads bitwise equal")
+    q = synth.gen_q(cfg)
+    out = cache.decode(upload(q)).cpu().numpy()
+    gq = cfg["q_heads"] // cfg["kv_heads"]
+    hl, ql, idx = [], [], []
+    for (b, h) in sample:
+        for hq in range(h * gq, (h + 1) * gq):
+            hl.append(heads[(b, h)])
+            ql.append(q[b, hq])
+            idx.append((b, hq))
+    ref = oracle.decode_many(cfg, hl, np.stack(ql), T - 1)
+    err = max(np.abs(out[b, hq] - ref[i]).max() for i, (b, hq) in enumerate(idx))
+    say("  decode max abs err", err)
+    assert err <= TOL
