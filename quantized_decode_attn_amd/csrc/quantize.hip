@@ -152,6 +152,37 @@ __device__ __forceinline__ void meta_from(float lo, float hi, int cnt, int L, ui
   *s16 = f2h_ru(s32);
 }
 
+// Key rows: 32 elements (16 rotary pairs: channels m and m + D/2) per work item,
+// packed LSB first into KB dwords and written with one vector store.
+template <int D, int BK, int KB, typename CodeFn>
+__device__ __forceinline__ void pack_key_rows(uint8_t* out, CodeFn code_of) {
+  constexpr int kChunksPerRow = D / 32;
+  constexpr int kRowBytes = D * KB / 8;
+  for (int idx = threadIdx.x; idx < BK * kChunksPerRow; idx += kThreads) {
+    const int j = idx / kChunksPerRow, cch = idx % kChunksPerRow;
+    uint32_t w[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) w[k] = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int ch = cch * 16 + (e >> 1) + (e & 1) * (D / 2);
+      const uint32_t code = code_of(j, ch);
+      const int pos = e * KB;
+      w[pos >> 5] |= code << (pos & 31);
+      if ((pos & 31) + KB > 32) w[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+    }
+    uint8_t* dst = out + (int64_t)j * kRowBytes + cch * 4 * KB;
+    if constexpr (KB == 4) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (KB == 2) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) reinterpret_cast<uint32_t*>(dst)[k] = w[k];
+    }
+  }
+}
+
 template <int D, int BK>
 __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
     kvq_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -388,40 +419,21 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
 
   // 5. codes and packing
   if (is_key) {
-    const int kb = bits;
-    const int rowbytes = D * kb / 8;
-    const bool lut = c.cfg.k_mode == 1;
+    const int rowbytes = D * bits / 8;
     uint8_t* out = static_cast<uint8_t*>(c.k_codes) + (bh * T + t0) * rowbytes;
-    constexpr int kChunksPerRow = D / 32;  // 32 elements (16 rotary pairs) per chunk
-    for (int idx = tid; idx < BK * kChunksPerRow; idx += kThreads) {
-      const int j = idx / kChunksPerRow, cch = idx % kChunksPerRow;
-      uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll 4
-      for (int e = 0; e < 32; ++e) {
-        const int m = cch * 16 + (e >> 1);
-        const int ch = m + (e & 1) * (D / 2);
-        int code = 0;
-        if (!is_out(j, ch)) {
-          const float d = dense(j, ch);
-          if (lut) {
-            for (int k = 0; k < L; ++k) code += d > sh.mids[ch * 15 + k];
-          } else {
-            code = code_uniform(d, sh.meta_z[ch], sh.meta_s[ch], L);
-          }
-        }
-        const int pos = e * kb;
-        w[pos >> 5] |= (uint32_t)code << (pos & 31);
-        if ((pos & 31) + kb > 32) w[(pos >> 5) + 1] |= (uint32_t)code >> (32 - (pos & 31));
+    auto code_of = [&](int j, int ch) -> uint32_t {
+      if (is_out(j, ch)) return 0u;
+      const float d = dense(j, ch);
+      if (c.cfg.k_mode == 1) {
+        uint32_t cc = 0;
+        for (int k = 0; k < L; ++k) cc += d > sh.mids[ch * 15 + k];
+        return cc;
       }
-      uint32_t* dst = reinterpret_cast<uint32_t*>(out + (int64_t)j * rowbytes + cch * 4 * kb);
-      if (kb == 4) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-      } else if (kb == 2) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-      } else {
-        for (int k = 0; k < kb; ++k) dst[k] = w[k];
-      }
-    }
+      return (uint32_t)code_uniform(d, sh.meta_z[ch], sh.meta_s[ch], L);
+    };
+    if (bits == 4) pack_key_rows<D, BK, 4>(out, code_of);
+    else if (bits == 3) pack_key_rows<D, BK, 3>(out, code_of);
+    else pack_key_rows<D, BK, 2>(out, code_of);
   } else {
     const int vb = bits, tpw = 32 / vb;
     const int G = c.cfg.v_group, ng = D / G;

@@ -64,6 +64,7 @@ def config(name: str, **overrides) -> dict:
     """A copy of a named workload, optionally with fields replaced (for shrunken test cases)."""
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
+    cfg.setdefault("capacity", cfg["tokens"])
     return cfg
 
 
