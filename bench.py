@@ -1,0 +1,265 @@
+"""Benchmark of the low-bit KV-cache hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the
+quantize-append of the batch's keys and values into an empty cache (every block
+quantized, packed, with its metadata) followed by one decode-attention query per
+sequence over the packed cache.  Inputs are resident in HBM before timing starts.
+``value`` is the decode attention's effective bandwidth (algorithmic bytes over the
+decode call's average duration, measured with HIP events on the stream the kernels
+run on); the append throughput is reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload c1] [--gpus 1]
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, published
+METRIC = "int4-KV decode attention GB/s & frac of HBM peak; quantize-append tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kout(cfg):
+    p = cfg["outlier_pct"]
+    return (p * cfg["head_dim"] + 99) // 100 if p > 0 else 0
+
+
+def decode_bytes_per_token_head(cfg) -> float:
+    """Bytes one decode must read per (b, kv-head, token): packed key and value codes,
+    key scale/zero amortised over the block, value scale/zero, outlier columns and
+    values (the fixed per-token count makes the row pointers unnecessary to read)."""
+    D, Bk, ko = cfg["head_dim"], cfg["k_block"], kout(cfg)
+    rk = D * cfg["k_bits"] / 8
+    rv = D * cfg["v_bits"] / 8
+    kmeta = 2 * D * 2 / Bk if cfg["k_mode"] == 0 else 0.0
+    vmeta = (D // cfg["v_group"]) * 2 * 2
+    csr = 2 * ko * 3
+    return rk + rv + kmeta + vmeta + csr
+
+
+def decode_bytes(cfg, T) -> float:
+    B, H, Hq, D = cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
+    lut = H * D * (1 << cfg["k_bits"]) * 2 if cfg["k_mode"] == 1 else 0
+    return B * H * T * decode_bytes_per_token_head(cfg) + B * Hq * D * (2 + 4) + lut
+
+
+def append_bytes_per_token_head(cfg) -> float:
+    """fp16 keys and values read, packed codes, scale/zero and outlier CSR written."""
+    D, ko = cfg["head_dim"], kout(cfg)
+    csr = 2 * (ko * 3 + 4) if ko else 0
+    return 2 * D * 2 + decode_bytes_per_token_head(cfg) - 2 * ko * 3 + csr
+
+
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_decode_attn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, k, v, q, lut, seconds: float):
+    """The oracle as it stands, on a bounded sample of the same workload: quantize the
+    sampled heads, then time fp64 decode over them."""
+    import oracle
+    oracle.build()
+    T, D, Hq, H = cfg["tokens"], cfg["head_dim"], cfg["q_heads"], cfg["kv_heads"]
+    gq = Hq // H
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    hc = oracle.HeadCache(cfg, None if lut is None else lut[0]).build(k[0, 0], v[0, 0])
+    t_build1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.decode_many(cfg, [hc], q[0, :1], T - 1)
+    t_dec1 = time.perf_counter() - t0
+    # heads so that the decode leg costs about `seconds` of wall time on `threads` cores
+    nheads = int(max(1, min(cfg["batch"] * H, seconds * threads / max(t_dec1, 1e-3))))
+    nheads = max(1, min(nheads, cfg["batch"] * H))
+    sample = [(i // H, i % H) for i in range(nheads)]
+    t0 = time.perf_counter()
+    heads = [hc] + [oracle.HeadCache(cfg, None if lut is None else lut[h]).build(k[b, h], v[b, h])
+                    for (b, h) in sample[1:]]
+    t_build = time.perf_counter() - t0 + t_build1
+    hl = [heads[i] for i in range(nheads) for _ in range(gq)]
+    ql = np.stack([q[b, h * gq + g] for (b, h) in sample for g in range(gq)])
+    t0 = time.perf_counter()
+    oracle.decode_many(cfg, hl, ql, T - 1)
+    t_dec = time.perf_counter() - t0
+    dec_bytes = nheads * T * decode_bytes_per_token_head(cfg)
+    return {
+        "value": round(dec_bytes / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "fp64 decode over %d of %d (b, kv-head) heads x %d tokens (%d query heads each), "
+                  "caches quantized by the oracle (%.1f s, %.3g tokens/s append); decode %.1f s"
+                  % (nheads, cfg["batch"] * H, T, gq, t_build, nheads * T / t_build, t_dec),
+        "append_tokens_per_s": round(nheads * T / t_build, 1),
+    }
+
+
+def copy_probe():
+    """A plain 1 GiB device-to-device copy (for scaling HBM byte counters)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy probe: 3 x %d bytes" % n)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c1", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    cfg = synth.config(args.workload)
+    T, B, H, Hq, D = cfg["tokens"], cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
+    existing = cfg["existing"]
+    log("workload", args.workload, cfg["workload"])
+    t0 = time.time()
+    k = synth.gen_tensor(cfg, synth.TENSOR_K)
+    v = synth.gen_tensor(cfg, synth.TENSOR_V)
+    q = synth.gen_q(cfg)
+    lut = synth.calib_lut(cfg) if cfg["k_mode"] == 1 else None
+    log("inputs drawn in %.1f s" % (time.time() - t0))
+
+    import torch
+    import quantized_decode_attn_amd as kvq
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.float16)
+    k_d, v_d, q_d = up(k), up(v), up(q)
+    lut_d = None if lut is None else torch.from_numpy(lut.view(np.int16)).to(dev)
+    cache = kvq.Cache(cfg, device=dev, lut=lut_d)
+    if existing:
+        cache.append(k_d[:, :, :existing].contiguous(), v_d[:, :, :existing].contiguous())
+    k_new = k_d[:, :, existing:].contiguous()
+    v_new = v_d[:, :, existing:].contiguous()
+    n_new = T - existing
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    cache.workspace(args.splits)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        cache.desc.length = existing            # re-append the same tokens into the same slots
+        if e: e[0].record(stream)
+        cache.append(k_new, v_new)
+        if e: e[1].record(stream)
+        cache.decode(q_d, q_pos=T - 1, num_splits=args.splits, out=out)
+        if e: e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    app_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
+    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+
+    dbytes = decode_bytes(cfg, T)
+    abytes = B * H * n_new * append_bytes_per_token_head(cfg)
+    dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
+    app_gbps = abytes / (app_ms.mean() * 1e-3) / 1e9
+    app_tps = B * n_new / (app_ms.mean() * 1e-3)
+    log("decode  %.1f us  %.1f GB/s (%.1f%% of 8 TB/s)" % (dec_ms.mean() * 1e3, dec_gbps, dec_gbps / 80))
+    log("append  %.1f us  %.1f GB/s  %.3g tokens/s" % (app_ms.mean() * 1e3, app_gbps, app_tps))
+
+    dec_hash = source_hash(["decode.hip", "kvq_device.h"])
+    app_hash = source_hash(["quantize.hip", "kvq_device.h"])
+    tr_dec = measured_traffic("decode", dec_hash)
+    tr_app = measured_traffic("append", app_hash)
+    rec = {
+        "metric": METRIC,
+        "value": round(dec_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": cfg["workload"], "batch": B, "q_heads": Hq, "kv_heads": H,
+                   "head_dim": D, "tokens": T, "appended_per_step": n_new, "k_bits": cfg["k_bits"],
+                   "v_bits": cfg["v_bits"], "k_block": cfg["k_block"], "v_group": cfg["v_group"],
+                   "splits": args.splits or "auto"},
+        "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "decode_us": round(float(dec_ms.mean()) * 1e3, 2),
+        "append_us": round(float(app_ms.mean()) * 1e3, 2),
+        "append_tokens_per_s": round(app_tps, 1),
+        "append_GBps": round(app_gbps, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": tr_dec, "kernel": "decode (split + combine launches)",
+                     "algorithmic_bytes": int(dbytes)},
+        "roofline_append": {"bound": "hbm", "achieved": round(app_gbps, 2), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(app_gbps / HBM_PEAK_GBPS, 4),
+                            "traffic": tr_app, "algorithmic_bytes": int(abytes)},
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -389,8 +389,8 @@ __global__ void decode_combine_kernel(const float* __restrict__ ws, float* __res
 }
 
 template <int D, int KB, int KMODE, int VB>
-hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
-                        int S, hipStream_t s) {
+hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                        hipStream_t s, int cus) {
   using Sh = Shape<D, KB, KMODE, VB>;
   const int GQ = c.cfg.q_heads / c.cfg.kv_heads, ng = D / c.cfg.v_group;
   const WaveLds L = wave_lds(D, c.cfg.k_block, GQ, ng, Sh::TPI, KB, KMODE, host_kout(c.cfg) > 0);
@@ -399,49 +399,56 @@ hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, fl
   hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<D, KB, KMODE, VB>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
   int64_t grid = (nitems + kWaves - 1) / kWaves;
   const int64_t cap = (int64_t)cus * (bytes <= 80 * 1024 ? 2 : 1);
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL((decode_split_kernel<D, KB, KMODE, VB>), dim3((unsigned)grid), dim3(kThreads), bytes, s,
                      c, q, q_pos, ws, S, nitems);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(D), 0, s, ws,
-                     out, S, D);
   return hipGetLastError();
 }
 
 template <int D, int KB, int KMODE>
-hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws, int S,
-                     hipStream_t s) {
-  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, q_pos, out, ws, S, s);
-  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, q_pos, out, ws, S, s);
+hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
+                     int cus) {
+  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, q_pos, ws, S, s, cus);
+  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, q_pos, ws, S, s, cus);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws, int S,
-                    hipStream_t s) {
+hipError_t launch_d(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
+                    int cus) {
   const int kb = c.cfg.k_bits, km = c.cfg.k_mode;
-  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, q_pos, out, ws, S, s);
-  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, q_pos, out, ws, S, s);
-  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, q_pos, out, ws, S, s);
-  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, q_pos, out, ws, S, s);
-  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, q_pos, out, ws, S, s);
-  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, q_pos, out, ws, S, s);
+  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, q_pos, ws, S, s, cus);
+  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, q_pos, ws, S, s, cus);
+  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, q_pos, ws, S, s, cus);
+  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, q_pos, ws, S, s, cus);
+  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, q_pos, ws, S, s, cus);
+  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, q_pos, ws, S, s, cus);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                             hipStream_t s, int cus);
+
 hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
                          int splits, hipStream_t s) {
-  if (c.cfg.head_dim == 128) return launch_d<128>(c, q, q_pos, out, ws, splits, s);
-  if (c.cfg.head_dim == 64) return launch_d<64>(c, q, q_pos, out, ws, splits, s);
-  return hipErrorInvalidValue;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  hipError_t e = launch_decode_mha(c, q, q_pos, ws, splits, s, cus);
+  if (e == hipErrorNotSupported) {
+    if (c.cfg.head_dim == 128) e = launch_d<128>(c, q, q_pos, ws, splits, s, cus);
+    else if (c.cfg.head_dim == 64) e = launch_d<64>(c, q, q_pos, ws, splits, s, cus);
+    else e = hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int D = c.cfg.head_dim;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(D), 0, s, ws,
+                     out, splits, D);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -1,0 +1,614 @@
+// decode_mha.hip -- decode attention over uniform 2/4-bit key and value caches with one
+// query head per kv head (multi-head attention), tuned for gfx950.
+//
+// Pages cited (title, address):
+//   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
+//   [TQ]   "TurboQuant：突破大模型推理瓶颈的KVCache量化技术解析", mlqm.cn/news/1002276
+//
+// Same arithmetic as the generic decode kernel (score of token n*Bk+j is
+// sum_i Re(W_n,i e^{i f_i j} k_i) with W folded with the block's per-channel scale and
+// zero-point, [KVC3] "Per-Channel Key Quantization" and "Pre-RoPE Key Quantization"),
+// organised for bandwidth:
+//  * 8-wave workgroups share one LDS copy of the cos/sin(j f_i) table;
+//  * every wave owns whole (b, head, split) items and streams their blocks through
+//    one set of registers: each register slot (codes of one token slot, one 16-byte
+//    value load, the metadata) is refilled with block n+1 right after its last use
+//    in block n, so a whole block of loads stays in flight;
+//  * a key token is covered by 8 lanes (4 for head_dim 64), 8 rotary pairs each,
+//    8-byte coalesced loads; codes become floats two at a time with the packed fp8
+//    conversion (a byte 0..15 is an exact fp8 value proportional to it);
+//  * values are stored as words of consecutive tokens of one channel, so a 16-byte
+//    load gives each lane 4 channels x (32 / v_bits) tokens and the value update is
+//    one FMA per code with the per-token weight p*scale from LDS;
+//  * block weights are computed once per rotary pair and shared through LDS.
+// The pages' fusion advice ([TQ] sections 5.1 and 6.3) is the design: no dequantized
+// value is ever written to memory.
+#include <math.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D, int BK, int KB, int VB>
+struct MShape {
+  static constexpr int HALF = D / 2;
+  static constexpr int PPL = 8;                  // rotary pairs per lane
+  static constexpr int LPT = HALF / PPL;         // lanes per key token
+  static constexpr int TPI = kWave / LPT;        // key tokens per iteration
+  static constexpr int NIT = BK / TPI;           // iterations per block
+  static constexpr int KW = 2 * PPL * KB / 32;   // code dwords per lane per token
+  static constexpr int RK = D * KB / 8;          // key row bytes
+  static constexpr int TPW = 32 / VB;            // tokens per value word
+  static constexpr int WPB = (BK / TPW) * D;     // value words per block
+  static constexpr int NVI = WPB / 256;          // 16-byte value loads per lane per block
+  static constexpr int TPITCH = D + 4;           // floats per rotary-table row
+  static constexpr int CHL = D / 4;              // lanes owning distinct value channels
+};
+
+// Per-wave LDS area, in floats.
+struct MLds {
+  int wts, p, ps, vz, vc, csr, total;
+};
+__host__ __device__ inline MLds mha_lds(int D, int BK, int ko, int tpi) {
+  MLds m;
+  int o = 0;
+  m.wts = o; o += 10 * (D / 2);     // A1 B1 Z1 A2 B2 Z2 WR WI ZA ZB, one array per name
+  m.p = o; o += BK;
+  m.ps = o; o += 2 * BK;            // [group][token], at most two value groups
+  m.vz = o; o += ko ? 2 * BK : 0;
+  m.vc = o; o += ko ? tpi * D : 0;
+  m.csr = o; o += ko ? (BK * ko * 6 + 3) / 4 : 0;   // k cols, v cols (u8), k vals, v vals (u16)
+  m.total = o;
+  return m;
+}
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f2v cvt_lo(uint32_t x) { return __builtin_amdgcn_cvt_pk_f32_fp8(x, false); }
+__device__ __forceinline__ f2v cvt_hi(uint32_t x) { return __builtin_amdgcn_cvt_pk_f32_fp8(x, true); }
+
+// Codes of one lane's 8 rotary pairs as floats (times the fp8 unit).
+template <int KB, int KW>
+__device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[KW], float (&ca)[8], float (&cb)[8]) {
+  if constexpr (KB == 4) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
+      const f2v a01 = cvt_lo(lo), a23 = cvt_hi(lo), b01 = cvt_lo(hi), b23 = cvt_hi(hi);
+      ca[4 * d] = a01.x; ca[4 * d + 1] = a01.y; ca[4 * d + 2] = a23.x; ca[4 * d + 3] = a23.y;
+      cb[4 * d] = b01.x; cb[4 * d + 1] = b01.y; cb[4 * d + 2] = b23.x; cb[4 * d + 3] = b23.y;
+    }
+  } else {
+    const uint32_t x0 = w[0] & 0x03030303u, x1 = (w[0] >> 2) & 0x03030303u;
+    const uint32_t x2 = (w[0] >> 4) & 0x03030303u, x3 = (w[0] >> 6) & 0x03030303u;
+    f2v t;
+    t = cvt_lo(x0); ca[0] = t.x; ca[2] = t.y;
+    t = cvt_hi(x0); ca[4] = t.x; ca[6] = t.y;
+    t = cvt_lo(x2); ca[1] = t.x; ca[3] = t.y;
+    t = cvt_hi(x2); ca[5] = t.x; ca[7] = t.y;
+    t = cvt_lo(x1); cb[0] = t.x; cb[2] = t.y;
+    t = cvt_hi(x1); cb[4] = t.x; cb[6] = t.y;
+    t = cvt_lo(x3); cb[1] = t.x; cb[3] = t.y;
+    t = cvt_hi(x3); cb[5] = t.x; cb[7] = t.y;
+  }
+}
+
+// All global data of one block that a wave needs, held in registers.
+template <int D, int BK, int KB, int VB>
+struct BlockRegs {
+  using Sh = MShape<D, BK, KB, VB>;
+  uint32_t k[Sh::NIT][Sh::KW];
+  uint4 v[Sh::NVI];
+  uint16_t kmeta[4];      // lane i < D/2: scale[i], scale[i+D/2], zero[i], zero[i+D/2]
+  float eb_c, eb_s;       // lane i < D/2: cos/sin(n*Bk*f_i)
+  uint16_t vs[4], vz[4];  // value scale/zero of elements lane + 64*k
+  uint32_t kcol, vcol;    // outlier CSR slice of the block (bytes lane*4..)
+  uint2 kval, vval;       // (bytes lane*8..)
+};
+
+// Loaders of the pieces of block n, each into its own register slot, so that a
+// slot can be refilled with the next block as soon as it has been consumed.
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_k(BlockRegs<D, BK, KB, VB>& R, int it, const kvq_cache& c, int64_t bh,
+                                       int64_t n, int ts, int r) {
+  using Sh = MShape<D, BK, KB, VB>;
+  const int64_t T = c.cfg.capacity;
+  const uint8_t* kc = static_cast<const uint8_t*>(c.k_codes) + (bh * T + n * BK + it * Sh::TPI + ts) * Sh::RK +
+                      r * (Sh::KW * 4);
+  if constexpr (Sh::KW == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(kc);
+    R.k[it][0] = x.x;
+    R.k[it][1] = x.y;
+  } else {
+    R.k[it][0] = *reinterpret_cast<const uint32_t*>(kc);
+  }
+}
+
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_v(BlockRegs<D, BK, KB, VB>& R, int i, const kvq_cache& c, int64_t bh,
+                                       int64_t n, int lane) {
+  using Sh = MShape<D, BK, KB, VB>;
+  const int64_t T = c.cfg.capacity;
+  const uint4* vw = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(c.v_codes) +
+                                                   (bh * (T / Sh::TPW) + n * (BK / Sh::TPW)) * D);
+  R.v[i] = vw[i * 64 + lane];
+}
+
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB>& R, const kvq_cache& c, int64_t bh, int64_t n,
+                                           int lane, int ko) {
+  using Sh = MShape<D, BK, KB, VB>;
+  const int64_t T = c.cfg.capacity;
+  if (lane < Sh::HALF) {
+    const int64_t m = (bh * (T / BK) + n) * D;
+    R.kmeta[0] = c.k_scale[m + lane];
+    R.kmeta[1] = c.k_scale[m + lane + Sh::HALF];
+    R.kmeta[2] = c.k_zero[m + lane];
+    R.kmeta[3] = c.k_zero[m + lane + Sh::HALF];
+    const float* eb = c.rope + (int64_t)BK * D + (n * Sh::HALF + lane) * 2;
+    R.eb_c = eb[0];
+    R.eb_s = eb[1];
+  }
+  if (ko > 0) {
+    const int nb = BK * ko;
+    const int64_t e0 = (bh * T + n * BK) * ko;
+    if (lane * 4 < nb) {
+      R.kcol = *reinterpret_cast<const uint32_t*>(c.k_col + e0 + lane * 4);
+      R.vcol = *reinterpret_cast<const uint32_t*>(c.v_col + e0 + lane * 4);
+      R.kval = *reinterpret_cast<const uint2*>(c.k_val + e0 + lane * 4);
+      R.vval = *reinterpret_cast<const uint2*>(c.v_val + e0 + lane * 4);
+    }
+  }
+}
+
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB>& R, const kvq_cache& c, int64_t bh, int64_t n,
+                                           int lane, int ng) {
+  const int64_t T = c.cfg.capacity;
+  const int ne = BK * ng;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = lane + 64 * k;
+    if (e < ne) {
+      const int grp = e / BK, t = e % BK;
+      const int64_t m = (bh * T + n * BK + t) * ng + grp;
+      R.vs[k] = c.v_scale[m];
+      R.vz[k] = c.v_zero[m];
+    }
+  }
+}
+
+template <int D, int BK, int KB, int VB>
+struct MState {
+  float m, lpart, acc[4], zpart[2];
+};
+
+// Process one quantized block held in registers.
+// Process quantized block n held in R; every register slot is refilled with block
+// n + 1 right after its last use when `more` is set.
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MState<D, BK, KB, VB>& st,
+                                              float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
+                                              float wq_r, float wq_i, float inv_unit, int lane, int ts, int r,
+                                              int G, int ng, int ko, const kvq_cache& c, int64_t bh, int64_t n,
+                                              bool more) {
+  using Sh = MShape<D, BK, KB, VB>;
+  float* wA1 = wl + L.wts;
+  float* wB1 = wA1 + Sh::HALF;
+  float* wZ1 = wB1 + Sh::HALF;
+  float* wA2 = wZ1 + Sh::HALF;
+  float* wB2 = wA2 + Sh::HALF;
+  float* wZ2 = wB2 + Sh::HALF;
+  float* wWR = wZ2 + Sh::HALF;
+  float* wWI = wWR + Sh::HALF;
+  float* wZA = wWI + Sh::HALF;
+  float* wZB = wZA + Sh::HALF;
+  float* Pl = wl + L.p;
+  float* PS = wl + L.ps;
+  float* VZl = wl + L.vz;
+  float* VC = wl + L.vc;
+  uint8_t* CSK = reinterpret_cast<uint8_t*>(wl + L.csr);
+  uint8_t* CSV = CSK + BK * ko;
+  uint16_t* CVK = reinterpret_cast<uint16_t*>(CSK + 2 * BK * ko);
+  uint16_t* CVV = CVK + BK * ko;
+
+  // ---- block weights, one rotary pair per lane
+  if (lane < Sh::HALF) {
+    const float wr = wq_r * R.eb_c - wq_i * R.eb_s;
+    const float wi = wq_r * R.eb_s + wq_i * R.eb_c;
+    const float al = h2f(R.kmeta[0]), be = h2f(R.kmeta[1]);
+    const float za = h2f(R.kmeta[2]), zb = h2f(R.kmeta[3]);
+    wA1[lane] = wr * al * inv_unit;
+    wB1[lane] = -wi * be * inv_unit;
+    wZ1[lane] = wr * za - wi * zb;
+    wA2[lane] = -wi * al * inv_unit;
+    wB2[lane] = -wr * be * inv_unit;
+    wZ2[lane] = -(wi * za + wr * zb);
+    wWR[lane] = wr;
+    wWI[lane] = wi;
+    wZA[lane] = za;
+    wZB[lane] = zb;
+  }
+  if (ko > 0 && lane * 4 < BK * ko) {
+    reinterpret_cast<uint32_t*>(CSK)[lane] = R.kcol;
+    reinterpret_cast<uint32_t*>(CSV)[lane] = R.vcol;
+    reinterpret_cast<uint2*>(CVK)[lane] = R.kval;
+    reinterpret_cast<uint2*>(CVV)[lane] = R.vval;
+  }
+  if (more) load_kmeta(R, c, bh, n + 1, lane, ko);
+  wave_lds_sync();
+  float A1[8], B1[8], Z1[8], A2[8], B2[8], Z2[8];
+  {
+    const int p0 = r * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 a1 = *reinterpret_cast<const float4*>(wA1 + p0 + 4 * h);
+      const float4 b1 = *reinterpret_cast<const float4*>(wB1 + p0 + 4 * h);
+      const float4 z1 = *reinterpret_cast<const float4*>(wZ1 + p0 + 4 * h);
+      const float4 a2 = *reinterpret_cast<const float4*>(wA2 + p0 + 4 * h);
+      const float4 b2 = *reinterpret_cast<const float4*>(wB2 + p0 + 4 * h);
+      const float4 z2 = *reinterpret_cast<const float4*>(wZ2 + p0 + 4 * h);
+      A1[4 * h] = a1.x; A1[4 * h + 1] = a1.y; A1[4 * h + 2] = a1.z; A1[4 * h + 3] = a1.w;
+      B1[4 * h] = b1.x; B1[4 * h + 1] = b1.y; B1[4 * h + 2] = b1.z; B1[4 * h + 3] = b1.w;
+      Z1[4 * h] = z1.x; Z1[4 * h + 1] = z1.y; Z1[4 * h + 2] = z1.z; Z1[4 * h + 3] = z1.w;
+      A2[4 * h] = a2.x; A2[4 * h + 1] = a2.y; A2[4 * h + 2] = a2.z; A2[4 * h + 3] = a2.w;
+      B2[4 * h] = b2.x; B2[4 * h + 1] = b2.y; B2[4 * h + 2] = b2.z; B2[4 * h + 3] = b2.w;
+      Z2[4 * h] = z2.x; Z2[4 * h + 1] = z2.y; Z2[4 * h + 2] = z2.z; Z2[4 * h + 3] = z2.w;
+    }
+  }
+
+  // ---- scores
+  float sc[Sh::NIT];
+  float mloc = -__builtin_inff();
+#pragma unroll
+  for (int it = 0; it < Sh::NIT; ++it) {
+    const int j = it * Sh::TPI + ts;
+    const float* tab = table + j * Sh::TPITCH + 16 * r;
+    float ca[8], cb[8];
+    unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
+    if (more) load_k(R, it, c, bh, n + 1, ts, r);
+    float s = 0.0f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 t = *reinterpret_cast<const float4*>(tab + 4 * q4);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int m = 2 * q4 + u;
+        const float cs = u ? t.z : t.x, sn = u ? t.w : t.y;
+        float X = __builtin_fmaf(A1[m], ca[m], Z1[m]);
+        X = __builtin_fmaf(B1[m], cb[m], X);
+        float Y = __builtin_fmaf(A2[m], ca[m], Z2[m]);
+        Y = __builtin_fmaf(B2[m], cb[m], Y);
+        s = __builtin_fmaf(cs, X, s);
+        s = __builtin_fmaf(sn, Y, s);
+      }
+    }
+    if (ko > 0 && r < ko) {  // outlier: code 0 was stored, the CSR holds the exact value
+      const int e = j * ko + r;
+      const int col = CSK[e];
+      const float dlt0 = h2f(CVK[e]);
+      const int i = col % Sh::HALF;
+      const float cs = table[j * Sh::TPITCH + 2 * i], sn = table[j * Sh::TPITCH + 2 * i + 1];
+      const float wr = wWR[i], wi = wWI[i];
+      const bool a = col < Sh::HALF;
+      const float dlt = dlt0 - (a ? wZA[i] : wZB[i]);
+      s += a ? dlt * (wr * cs - wi * sn) : -dlt * (wi * cs + wr * sn);
+    }
+    s = group_sum<Sh::LPT>(s);
+    sc[it] = s;
+    mloc = fmaxf(mloc, s);
+  }
+
+  // ---- online softmax in base 2
+  const float mblk = wave_max(mloc);
+  const float mnew = fmaxf(st.m, mblk);
+  const float alpha = exp2f(st.m - mnew);
+  st.m = mnew;
+  float psum = 0.0f;
+  if (r == 0) {
+#pragma unroll
+    for (int it = 0; it < Sh::NIT; ++it) {
+      const float p = exp2f(sc[it] - mnew);
+      psum += p;
+      Pl[it * Sh::TPI + ts] = p;
+    }
+  }
+  st.lpart = __builtin_fmaf(st.lpart, alpha, psum);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) st.acc[k] *= alpha;
+  st.zpart[0] *= alpha;
+  st.zpart[1] *= alpha;
+  wave_lds_sync();
+
+  // ---- value weights p * scale (times 1/fp8 unit), zero-point sums, per [group][token]
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = lane + 64 * k;
+    if (e < BK * ng) {
+      const int grp = e / BK, t = e % BK;
+      const float p = Pl[t];
+      PS[grp * BK + t] = p * h2f(R.vs[k]) * inv_unit;
+      const float z = h2f(R.vz[k]);
+      if (grp == 0) st.zpart[0] = __builtin_fmaf(p, z, st.zpart[0]);
+      else st.zpart[1] = __builtin_fmaf(p, z, st.zpart[1]);
+      if (ko > 0) VZl[grp * BK + t] = z;
+    }
+  }
+  if (more) load_vmeta(R, c, bh, n + 1, lane, ng);
+  wave_lds_sync();
+
+  // ---- values: lane owns channels ch0..ch0+3, word group g changes with the load
+  const int ch0 = (4 * lane) % D;
+  const int grp0 = ch0 / G;
+#pragma unroll
+  for (int i = 0; i < Sh::NVI; ++i) {
+    const int g = i * (256 / D) + (4 * lane) / D;
+    const float* ps = PS + grp0 * BK + g * Sh::TPW;
+    float pw[Sh::TPW];
+#pragma unroll
+    for (int u4 = 0; u4 < Sh::TPW / 4; ++u4) {
+      const float4 t = *reinterpret_cast<const float4*>(ps + 4 * u4);
+      pw[4 * u4] = t.x; pw[4 * u4 + 1] = t.y; pw[4 * u4 + 2] = t.z; pw[4 * u4 + 3] = t.w;
+    }
+    const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+    if (more) load_v(R, i, c, bh, n + 1, lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = words[k];
+      float a = st.acc[k];
+      if constexpr (VB == 4) {
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+        const f2v e01 = cvt_lo(lo), e23 = cvt_hi(lo), o01 = cvt_lo(hi), o23 = cvt_hi(hi);
+        a = __builtin_fmaf(pw[0], e01.x, a);
+        a = __builtin_fmaf(pw[2], e01.y, a);
+        a = __builtin_fmaf(pw[4], e23.x, a);
+        a = __builtin_fmaf(pw[6], e23.y, a);
+        a = __builtin_fmaf(pw[1], o01.x, a);
+        a = __builtin_fmaf(pw[3], o01.y, a);
+        a = __builtin_fmaf(pw[5], o23.x, a);
+        a = __builtin_fmaf(pw[7], o23.y, a);
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const uint32_t x = (w >> (2 * s2)) & 0x03030303u;
+          const f2v lo = cvt_lo(x), hi = cvt_hi(x);
+          a = __builtin_fmaf(pw[s2], lo.x, a);
+          a = __builtin_fmaf(pw[s2 + 4], lo.y, a);
+          a = __builtin_fmaf(pw[s2 + 8], hi.x, a);
+          a = __builtin_fmaf(pw[s2 + 12], hi.y, a);
+        }
+      }
+      st.acc[k] = a;
+    }
+  }
+
+  // ---- value outliers: VC rows are token slots, so no instruction updates an address twice
+  if (ko > 0) {
+#pragma unroll
+    for (int it = 0; it < Sh::NIT; ++it) {
+      if (r < ko) {
+        const int t = it * Sh::TPI + ts;
+        const int e = t * ko + r;
+        const int col = CSV[e];
+        const float dlt = h2f(CVV[e]) - VZl[(col / G) * BK + t];
+        VC[ts * D + col] += Pl[t] * dlt;
+      }
+    }
+    wave_lds_sync();
+    if (lane < Sh::CHL) {
+#pragma unroll
+      for (int row = 0; row < Sh::TPI; ++row) {
+        float4* p = reinterpret_cast<float4*>(VC + row * D + ch0);
+        const float4 v = *p;
+        st.acc[0] += v.x; st.acc[1] += v.y; st.acc[2] += v.z; st.acc[3] += v.w;
+        *p = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+  wave_lds_sync();
+}
+
+template <int D, int BK, int KB, int VB>
+__global__ __launch_bounds__(kThreads) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+                                                              int64_t q_pos, float* __restrict__ ws, int S,
+                                                              int64_t nitems) {
+  using Sh = MShape<D, BK, KB, VB>;
+  extern __shared__ float lds[];
+  const int H = c.cfg.kv_heads;
+  const int G = c.cfg.v_group, ng = D / G;
+  const int ko = kout_of(c.cfg);
+  const int64_t nfull = c.length / BK;
+  const int ntail = (int)(c.length - nfull * BK);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
+
+  float* table = lds;
+  for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += kThreads) {
+    const int j = idx / Sh::HALF, i = idx % Sh::HALF;
+    *reinterpret_cast<float2*>(table + j * Sh::TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
+  }
+  const MLds L = mha_lds(D, BK, ko, Sh::TPI);
+  float* wl = lds + BK * Sh::TPITCH + wave * L.total;
+  if (ko > 0)
+    for (int k = lane; k < Sh::TPI * D; k += kWave) wl[L.vc + k] = 0.0f;
+  __syncthreads();
+
+  const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
+  const int64_t total_waves = (int64_t)gridDim.x * kWaves;
+  for (int64_t item = (int64_t)blockIdx.x * kWaves + wave; item < nitems; item += total_waves) {
+    const int split = (int)(item % S);
+    const int64_t bh = item / S;
+    const int h = (int)(bh % H);
+    const int b = (int)(bh / H);
+    const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
+    const bool do_tail = split == S - 1 && ntail > 0;
+
+    // query weight of pair `lane`: scale * conj(q_i) * e^{-i f_i q_pos}, evaluated in fp64
+    float wq_r = 0.0f, wq_i = 0.0f;
+    if (lane < Sh::HALF) {
+      const uint16_t* qv = q + ((int64_t)b * H + h) * D;
+      const double qa = (double)h2f(qv[lane]), qb = (double)h2f(qv[lane + Sh::HALF]);
+      const double f = pow((double)c.cfg.rope_theta, -(2.0 * lane) / (double)D);
+      double sn, cs;
+      sincos((double)q_pos * f, &sn, &cs);
+      const double scl = (double)kLog2e / sqrt((double)D);
+      wq_r = (float)(scl * (qa * cs - qb * sn));
+      wq_i = (float)(-scl * (qa * sn + qb * cs));
+    }
+    MState<D, BK, KB, VB> st;
+    st.m = -__builtin_inff();
+    st.lpart = 0.0f;
+    st.acc[0] = st.acc[1] = st.acc[2] = st.acc[3] = 0.0f;
+    st.zpart[0] = st.zpart[1] = 0.0f;
+
+    BlockRegs<D, BK, KB, VB> R;
+    if (n0 < n1) {
+      load_kmeta(R, c, bh, n0, lane, ko);
+      load_vmeta(R, c, bh, n0, lane, ng);
+#pragma unroll
+      for (int it = 0; it < Sh::NIT; ++it) load_k(R, it, c, bh, n0, ts, r);
+#pragma unroll
+      for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, c, bh, n0, lane);
+    }
+    for (int64_t n = n0; n < n1; ++n)
+      process_block(R, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, ko, c, bh, n, n + 1 < n1);
+
+    if (do_tail) {
+      // unquantized newest tokens: exact fp16 keys and values
+      float* wWR = wl + L.wts + 6 * Sh::HALF;
+      float* wWI = wWR + Sh::HALF;
+      float* Pl = wl + L.p;
+      if (lane < Sh::HALF) {
+        const float* eb = c.rope + (int64_t)BK * D + (nfull * Sh::HALF + lane) * 2;
+        wWR[lane] = wq_r * eb[0] - wq_i * eb[1];
+        wWI[lane] = wq_r * eb[1] + wq_i * eb[0];
+      }
+      wave_lds_sync();
+      const uint16_t* kt = c.k_tail + bh * BK * D;
+      const uint16_t* vt = c.v_tail + bh * BK * D;
+      float mloc = -__builtin_inff();
+      float sc[Sh::NIT];
+#pragma unroll
+      for (int it = 0; it < Sh::NIT; ++it) {
+        const int j = it * Sh::TPI + ts;
+        float s = 0.0f;
+        if (j < ntail) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int i = r * 8 + m;
+            const float a = h2f(kt[j * D + i]), bb = h2f(kt[j * D + i + Sh::HALF]);
+            const float wr = wWR[i], wi = wWI[i];
+            const float X = __builtin_fmaf(wr, a, -wi * bb);
+            const float Y = -__builtin_fmaf(wi, a, wr * bb);
+            s = __builtin_fmaf(table[j * Sh::TPITCH + 2 * i], X, s);
+            s = __builtin_fmaf(table[j * Sh::TPITCH + 2 * i + 1], Y, s);
+          }
+        }
+        s = group_sum<Sh::LPT>(s);
+        if (j >= ntail) s = -__builtin_inff();
+        sc[it] = s;
+        mloc = fmaxf(mloc, s);
+      }
+      const float mnew = fmaxf(st.m, wave_max(mloc));
+      const float alpha = exp2f(st.m - mnew);
+      st.m = mnew;
+      float psum = 0.0f;
+      if (r == 0) {
+#pragma unroll
+        for (int it = 0; it < Sh::NIT; ++it) {
+          const int j = it * Sh::TPI + ts;
+          if (j < ntail) {
+            const float p = exp2f(sc[it] - mnew);
+            psum += p;
+            Pl[j] = p;
+          }
+        }
+      }
+      st.lpart = __builtin_fmaf(st.lpart, alpha, psum);
+      for (int k = 0; k < 4; ++k) st.acc[k] *= alpha;
+      st.zpart[0] *= alpha;
+      st.zpart[1] *= alpha;
+      wave_lds_sync();
+      if (lane < Sh::CHL) {
+        const int ch0 = 4 * lane;
+        for (int j = 0; j < ntail; ++j) {
+          const float p = Pl[j];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) st.acc[k] = __builtin_fmaf(p, h2f(vt[j * D + ch0 + k]), st.acc[k]);
+        }
+      }
+      wave_lds_sync();
+    }
+
+    // ---- finish the item: reduce across lanes and write (m, l, o) of this split
+    const float l = wave_sum(st.lpart);
+    const float z0 = wave_sum(st.zpart[0]);
+    const float z1 = wave_sum(st.zpart[1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      for (int msk = Sh::CHL; msk < kWave; msk <<= 1) st.acc[k] += __shfl_xor(st.acc[k], msk, kWave);
+    float* dst = ws + (bh * S + split) * (D + 2);
+    if (lane < Sh::CHL) {
+      const int ch0 = 4 * lane;
+      const float z = (ch0 / G) == 0 ? z0 : z1;
+      *reinterpret_cast<float4*>(dst + 2 + ch0) =
+          make_float4(st.acc[0] + z, st.acc[1] + z, st.acc[2] + z, st.acc[3] + z);
+    }
+    if (lane == 0) {
+      dst[0] = st.m;
+      dst[1] = l;
+    }
+  }
+}
+
+}  // namespace
+
+// Returns hipErrorNotSupported when the configuration is not one this kernel covers.
+hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                             hipStream_t s, int cus);
+
+template <int D, int BK, int KB, int VB>
+static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                                   hipStream_t s, int cus) {
+  using Sh = MShape<D, BK, KB, VB>;
+  const int ko = host_kout(c.cfg);
+  const MLds L = mha_lds(D, BK, ko, Sh::TPI);
+  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kWaves * L.total) * sizeof(float);
+  if (bytes > 160 * 1024) return hipErrorNotSupported;
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
+  int64_t grid = (nitems + kWaves - 1) / kWaves;
+  if (grid > cus) grid = cus;
+  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB>), dim3((unsigned)grid), dim3(kThreads), bytes, s, c, q,
+                     q_pos, ws, S, nitems);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                             hipStream_t s, int cus) {
+  const kvq_config& g = c.cfg;
+  const int ko = host_kout(g);
+  const int ng = g.head_dim / g.v_group;
+  if (g.q_heads != g.kv_heads || g.k_mode != 0 || (g.k_bits != 4 && g.k_bits != 2) || ko > 2 || ng > 2 ||
+      g.k_block * ng > 256)
+    return hipErrorNotSupported;
+  const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
+#define KVQ_MHA(d, bk, kb, vb) \
+  if (D == d && BK == bk && KB == kb && VB == vb) return launch_mha_typed<d, bk, kb, vb>(c, q, q_pos, ws, S, s, cus);
+  KVQ_MHA(128, 128, 4, 4) KVQ_MHA(128, 128, 4, 2) KVQ_MHA(128, 128, 2, 4) KVQ_MHA(128, 128, 2, 2)
+  KVQ_MHA(128, 64, 4, 4) KVQ_MHA(128, 64, 4, 2) KVQ_MHA(128, 64, 2, 4) KVQ_MHA(128, 64, 2, 2)
+  KVQ_MHA(64, 128, 4, 4) KVQ_MHA(64, 128, 4, 2) KVQ_MHA(64, 128, 2, 4) KVQ_MHA(64, 128, 2, 2)
+  KVQ_MHA(64, 64, 4, 4) KVQ_MHA(64, 64, 4, 2) KVQ_MHA(64, 64, 2, 4) KVQ_MHA(64, 64, 2, 2)
+#undef KVQ_MHA
+  return hipErrorNotSupported;
+}
+
+}  // namespace kvq

@@ -52,10 +52,10 @@ kvq_status check_cache(const kvq_cache* cache) {
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
 
 int auto_splits(const kvq_config& c) {
-  // Aim at a few thousand (b, kv-head, split) work items so that every wave of the
-  // chip gets whole items, without splitting a sequence below one block per split.
+  // About one (b, kv-head, split) work item per resident wave of an MI355X (256 CUs x
+  // 8 waves), without splitting a sequence below one block per split.
   const int64_t units = (int64_t)c.batch * c.kv_heads;
-  int64_t s = (4096 + units - 1) / units;
+  int64_t s = (2048 + units - 1) / units;
   const int64_t nblk = c.capacity / c.k_block;
   if (s > nblk) s = nblk;
   if (s < 1) s = 1;
