@@ -369,20 +369,84 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
   }
 }
 
-// Merge the S partials of one (b, q-head) in split order: out = sum_s o_s 2^(m_s-M) / sum_s l_s 2^(m_s-M).
-__global__ void decode_combine_kernel(const float* __restrict__ ws, float* __restrict__ out, int S, int D) {
+// Finish one (b, q-head): optionally attend over the unquantized tail tokens (exact
+// fp16 keys and values, the newest length % k_block tokens), then merge the S split
+// partials and the tail in a fixed order:
+//   M = max m_s,  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+__global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+                                                          int64_t q_pos, const float* __restrict__ ws,
+                                                          float* __restrict__ out, int S, int with_tail) {
+  const int D = c.cfg.head_dim, half = D / 2, Bk = c.cfg.k_block;
+  const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H;
   const int64_t bq = blockIdx.x;
+  const int b = (int)(bq / Hq), hq = (int)(bq % Hq), h = hq / gq;
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t nfull = c.length / Bk;
+  const int ntail = with_tail ? (int)(c.length - nfull * Bk) : 0;
+  __shared__ float wr_s[128], wi_s[128], p_s[128], red[8];
+  __shared__ float tail_m, tail_l;
+  const int tid = threadIdx.x;
+  if (ntail > 0) {
+    if (tid < half) {
+      const uint16_t* qv = q + bq * D;
+      const double qa = (double)h2f(qv[tid]), qb = (double)h2f(qv[tid + half]);
+      const double f = pow((double)c.cfg.rope_theta, -(2.0 * tid) / (double)D);
+      double sn, cs;
+      sincos((double)q_pos * f, &sn, &cs);
+      const double scl = (double)kLog2e / sqrt((double)D);
+      const float qr = (float)(scl * (qa * cs - qb * sn)), qi = (float)(-scl * (qa * sn + qb * cs));
+      const float* eb = c.rope + (int64_t)Bk * D + (nfull * half + tid) * 2;
+      wr_s[tid] = qr * eb[0] - qi * eb[1];
+      wi_s[tid] = qr * eb[1] + qi * eb[0];
+    }
+    __syncthreads();
+    float s = -__builtin_inff();
+    if (tid < ntail) {
+      const uint16_t* kr = c.k_tail + (bh * Bk + tid) * D;
+      const float* tab = c.rope + (int64_t)tid * half * 2;
+      s = 0.0f;
+      for (int i = 0; i < half; ++i) {
+        const float a = h2f(kr[i]), bb = h2f(kr[i + half]);
+        const float X = __builtin_fmaf(wr_s[i], a, -wi_s[i] * bb);
+        const float Y = -__builtin_fmaf(wi_s[i], a, wr_s[i] * bb);
+        s = __builtin_fmaf(tab[2 * i], X, __builtin_fmaf(tab[2 * i + 1], Y, s));
+      }
+    }
+    float m = wave_max(s);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float p = tid < ntail ? exp2f(s - m) : 0.0f;
+    if (tid < 128) p_s[tid] = p;
+    float l = wave_sum(p);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = l;
+    __syncthreads();
+    if (tid == 0) {
+      tail_m = m;
+      tail_l = (red[4] + red[5]) + (red[6] + red[7]);
+    }
+    __syncthreads();
+  }
   const float* base = ws + bq * (int64_t)S * (D + 2);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float M = -__builtin_inff();
+  for (int d = tid; d < D; d += blockDim.x) {
+    float M = ntail > 0 ? tail_m : -__builtin_inff();
     for (int s = 0; s < S; ++s) M = fmaxf(M, base[(int64_t)s * (D + 2)]);
     float Lsum = 0.0f, O = 0.0f;
     for (int s = 0; s < S; ++s) {
-      const float* p = base + (int64_t)s * (D + 2);
-      if (p[0] == -__builtin_inff()) continue;  // empty split
-      const float w = exp2f(p[0] - M);
-      Lsum = __builtin_fmaf(p[1], w, Lsum);
-      O = __builtin_fmaf(p[2 + d], w, O);
+      const float* pp = base + (int64_t)s * (D + 2);
+      if (pp[0] == -__builtin_inff()) continue;  // empty split
+      const float w = exp2f(pp[0] - M);
+      Lsum = __builtin_fmaf(pp[1], w, Lsum);
+      O = __builtin_fmaf(pp[2 + d], w, O);
+    }
+    if (ntail > 0) {
+      const float w = exp2f(tail_m - M);
+      float ot = 0.0f;
+      const uint16_t* vt = c.v_tail + bh * Bk * D + d;
+      for (int j = 0; j < ntail; ++j) ot = __builtin_fmaf(p_s[j], h2f(vt[(int64_t)j * D]), ot);
+      Lsum = __builtin_fmaf(tail_l, w, Lsum);
+      O = __builtin_fmaf(ot, w, O);
     }
     out[bq * D + d] = O / Lsum;
   }
@@ -439,15 +503,16 @@ hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, f
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   hipError_t e = launch_decode_mha(c, q, q_pos, ws, splits, s, cus);
+  int with_tail = 1;  // the multi-head kernel leaves the unquantized tail to the finish kernel
   if (e == hipErrorNotSupported) {
+    with_tail = 0;
     if (c.cfg.head_dim == 128) e = launch_d<128>(c, q, q_pos, ws, splits, s, cus);
     else if (c.cfg.head_dim == 64) e = launch_d<64>(c, q, q_pos, ws, splits, s, cus);
     else e = hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const int D = c.cfg.head_dim;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(D), 0, s, ws,
-                     out, splits, D);
+  hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(256), 0, s, c,
+                     q, q_pos, ws, out, splits, with_tail);
   return hipGetLastError();
 }
 

@@ -18,8 +18,10 @@
 //    8-byte coalesced loads; codes become floats two at a time with the packed fp8
 //    conversion (a byte 0..15 is an exact fp8 value proportional to it);
 //  * values are stored as words of consecutive tokens of one channel, so a 16-byte
-//    load gives each lane 4 channels x (32 / v_bits) tokens and the value update is
-//    one FMA per code with the per-token weight p*scale from LDS;
+//    load gives each lane 4 channels x (32 / v_bits) tokens; the per-token weights
+//    p*scale are quantized per block to 16-bit fixed point and split into four
+//    nibble planes, and the value update is v_dot8_u32_u4 on the packed codes
+//    (no unpacking, 8 codes per instruction and plane);
 //  * block weights are computed once per rotary pair and shared through LDS.
 // The pages' fusion advice ([TQ] sections 5.1 and 6.3) is the design: no dequantized
 // value is ever written to memory.
@@ -31,8 +33,9 @@
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
+// Waves per workgroup: 8 (two per SIMD) when the kernel fits 256 registers, else 4.
+template <bool OUTL>
+constexpr int waves_for() { return OUTL ? 4 : 8; }
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D, int BK, int KB, int VB>
@@ -60,7 +63,7 @@ __host__ __device__ inline MLds mha_lds(int D, int BK, int ko, int tpi) {
   int o = 0;
   m.wts = o; o += 10 * (D / 2);     // A1 B1 Z1 A2 B2 Z2 WR WI ZA ZB, one array per name
   m.p = o; o += BK;
-  m.ps = o; o += 2 * BK;            // [group][token], at most two value groups
+  m.ps = o; o += 2 * BK + 128;      // quantized weights [2][BK] (u16) + nibble planes [2][64]
   m.vz = o; o += ko ? 2 * BK : 0;
   m.vc = o; o += ko ? tpi * D : 0;
   m.csr = o; o += ko ? (BK * ko * 6 + 3) / 4 : 0;   // k cols, v cols (u8), k vals, v vals (u16)
@@ -326,65 +329,123 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   st.zpart[1] *= alpha;
   wave_lds_sync();
 
-  // ---- value weights p * scale (times 1/fp8 unit), zero-point sums, per [group][token]
+  // ---- value weights w_t = p_t * scale_t per [group][token], quantized per block to
+  // 16-bit fixed point (relative to the block maximum) for the integer dot products;
+  // the zero-point part p_t * zero_t is summed in fp32
+  uint16_t* Wq16 = reinterpret_cast<uint16_t*>(PS);                       // [2][BK]
+  uint32_t* PLN = reinterpret_cast<uint32_t*>(PS) + BK;                     // [2][64] nibble planes
+  float wv[4];
+  float wmax0 = 0.0f, wmax1 = 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
+    wv[k] = 0.0f;
     if (e < BK * ng) {
       const int grp = e / BK, t = e % BK;
       const float p = Pl[t];
-      PS[grp * BK + t] = p * h2f(R.vs[k]) * inv_unit;
+      wv[k] = p * h2f(R.vs[k]);
       const float z = h2f(R.vz[k]);
-      if (grp == 0) st.zpart[0] = __builtin_fmaf(p, z, st.zpart[0]);
-      else st.zpart[1] = __builtin_fmaf(p, z, st.zpart[1]);
+      if (grp == 0) {
+        st.zpart[0] = __builtin_fmaf(p, z, st.zpart[0]);
+        wmax0 = fmaxf(wmax0, wv[k]);
+      } else {
+        st.zpart[1] = __builtin_fmaf(p, z, st.zpart[1]);
+        wmax1 = fmaxf(wmax1, wv[k]);
+      }
       if (ko > 0) VZl[grp * BK + t] = z;
     }
   }
   if (more) load_vmeta(R, c, bh, n + 1, lane, ng);
+  wmax0 = wave_max(wmax0);
+  if (ng > 1) wmax1 = wave_max(wmax1);
+  const float kq0 = wmax0 > 0.0f ? 65535.0f / wmax0 : 0.0f;
+  const float kq1 = wmax1 > 0.0f ? 65535.0f / wmax1 : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = lane + 64 * k;
+    if (e < BK * ng) {
+      const float kq = e < BK ? kq0 : kq1;
+      Wq16[e] = (uint16_t)__builtin_rintf(wv[k] * kq);
+    }
+  }
+  wave_lds_sync();
+  // nibble planes: plane k of a token group holds nibble k of each token's weight,
+  // token u of the group at bits [4u, 4u+4) (the bit position of its code in a word)
+  for (int grp = 0; grp < ng; ++grp) {
+    const uint16_t* wg = Wq16 + grp * BK;
+    uint32_t plane = 0;
+    if constexpr (VB == 4) {
+      const int tg = lane >> 2, kk = lane & 3;           // 16 groups of 8 tokens
+      if (tg < BK / 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(wg + 8 * tg);
+        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          plane |= ((d[u >> 1] >> (16 * (u & 1) + 4 * kk)) & 15u) << (4 * u);
+        PLN[grp * 64 + lane] = plane;
+      }
+    } else {
+      const int tg = lane >> 3, par = (lane >> 2) & 1, kk = lane & 3;   // 8 groups of 16 tokens
+      if (tg < BK / 16) {
+        const uint4 w0 = *reinterpret_cast<const uint4*>(wg + 16 * tg);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(wg + 16 * tg + 8);
+        const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)   // token 2u + par of the group
+          plane |= ((d[u] >> (16 * par + 4 * kk)) & 15u) << (4 * u);
+        PLN[grp * 64 + lane] = plane;
+      }
+    }
+  }
   wave_lds_sync();
 
-  // ---- values: lane owns channels ch0..ch0+3, word group g changes with the load
+  // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
+  // sum_t w_t * code_t by 4-bit integer dot products over the four weight nibbles
   const int ch0 = (4 * lane) % D;
   const int grp0 = ch0 / G;
+  uint32_t ia[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl) ia[k][pl] = 0;
 #pragma unroll
   for (int i = 0; i < Sh::NVI; ++i) {
     const int g = i * (256 / D) + (4 * lane) / D;
-    const float* ps = PS + grp0 * BK + g * Sh::TPW;
-    float pw[Sh::TPW];
-#pragma unroll
-    for (int u4 = 0; u4 < Sh::TPW / 4; ++u4) {
-      const float4 t = *reinterpret_cast<const float4*>(ps + 4 * u4);
-      pw[4 * u4] = t.x; pw[4 * u4 + 1] = t.y; pw[4 * u4 + 2] = t.z; pw[4 * u4 + 3] = t.w;
-    }
     const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
     if (more) load_v(R, i, c, bh, n + 1, lane);
+    if constexpr (VB == 4) {
+      const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 4 * g);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ia[k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[k][0], false);
+        ia[k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[k][1], false);
+        ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
+        ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
+      }
+    } else {
+      const uint4 pe = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 8 * g);
+      const uint4 po = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 8 * g + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
+        ia[k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[k][0], false);
+        ia[k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[k][1], false);
+        ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
+        ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
+        ia[k][0] = __builtin_amdgcn_udot8(po.x, od, ia[k][0], false);
+        ia[k][1] = __builtin_amdgcn_udot8(po.y, od, ia[k][1], false);
+        ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
+        ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
+      }
+    }
+  }
+  {
+    const float inv = grp0 == 0 ? (wmax0 > 0.0f ? wmax0 / 65535.0f : 0.0f)
+                                : (wmax1 > 0.0f ? wmax1 / 65535.0f : 0.0f);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t w = words[k];
-      float a = st.acc[k];
-      if constexpr (VB == 4) {
-        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-        const f2v e01 = cvt_lo(lo), e23 = cvt_hi(lo), o01 = cvt_lo(hi), o23 = cvt_hi(hi);
-        a = __builtin_fmaf(pw[0], e01.x, a);
-        a = __builtin_fmaf(pw[2], e01.y, a);
-        a = __builtin_fmaf(pw[4], e23.x, a);
-        a = __builtin_fmaf(pw[6], e23.y, a);
-        a = __builtin_fmaf(pw[1], o01.x, a);
-        a = __builtin_fmaf(pw[3], o01.y, a);
-        a = __builtin_fmaf(pw[5], o23.x, a);
-        a = __builtin_fmaf(pw[7], o23.y, a);
-      } else {
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const uint32_t x = (w >> (2 * s2)) & 0x03030303u;
-          const f2v lo = cvt_lo(x), hi = cvt_hi(x);
-          a = __builtin_fmaf(pw[s2], lo.x, a);
-          a = __builtin_fmaf(pw[s2 + 4], lo.y, a);
-          a = __builtin_fmaf(pw[s2 + 8], hi.x, a);
-          a = __builtin_fmaf(pw[s2 + 12], hi.y, a);
-        }
-      }
-      st.acc[k] = a;
+      const uint32_t tot = ia[k][0] + (ia[k][1] << 4) + (ia[k][2] << 8) + (ia[k][3] << 12);
+      st.acc[k] = __builtin_fmaf((float)tot, inv, st.acc[k]);
     }
   }
 
@@ -414,22 +475,23 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   wave_lds_sync();
 }
 
-template <int D, int BK, int KB, int VB>
-__global__ __launch_bounds__(kThreads) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+template <int D, int BK, int KB, int VB, bool OUTL>
+__global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                               int64_t q_pos, float* __restrict__ ws, int S,
                                                               int64_t nitems) {
   using Sh = MShape<D, BK, KB, VB>;
+  constexpr int kNW = waves_for<OUTL>(), kNT = kNW * 64;
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads;
   const int G = c.cfg.v_group, ng = D / G;
-  const int ko = kout_of(c.cfg);
+  const int ko = OUTL ? kout_of(c.cfg) : 0;
   const int64_t nfull = c.length / BK;
-  const int ntail = (int)(c.length - nfull * BK);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
 
   float* table = lds;
-  for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += kNT) {
     const int j = idx / Sh::HALF, i = idx % Sh::HALF;
     *reinterpret_cast<float2*>(table + j * Sh::TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
   }
@@ -440,14 +502,13 @@ __global__ __launch_bounds__(kThreads) void decode_mha_kernel(kvq_cache c, const
   __syncthreads();
 
   const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
-  const int64_t total_waves = (int64_t)gridDim.x * kWaves;
-  for (int64_t item = (int64_t)blockIdx.x * kWaves + wave; item < nitems; item += total_waves) {
+  const int64_t total_waves = (int64_t)gridDim.x * kNW;
+  for (int64_t item = (int64_t)blockIdx.x * kNW + wave; item < nitems; item += total_waves) {
     const int split = (int)(item % S);
     const int64_t bh = item / S;
     const int h = (int)(bh % H);
     const int b = (int)(bh / H);
     const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
-    const bool do_tail = split == S - 1 && ntail > 0;
 
     // query weight of pair `lane`: scale * conj(q_i) * e^{-i f_i q_pos}, evaluated in fp64
     float wq_r = 0.0f, wq_i = 0.0f;
@@ -479,73 +540,6 @@ __global__ __launch_bounds__(kThreads) void decode_mha_kernel(kvq_cache c, const
     for (int64_t n = n0; n < n1; ++n)
       process_block(R, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, ko, c, bh, n, n + 1 < n1);
 
-    if (do_tail) {
-      // unquantized newest tokens: exact fp16 keys and values
-      float* wWR = wl + L.wts + 6 * Sh::HALF;
-      float* wWI = wWR + Sh::HALF;
-      float* Pl = wl + L.p;
-      if (lane < Sh::HALF) {
-        const float* eb = c.rope + (int64_t)BK * D + (nfull * Sh::HALF + lane) * 2;
-        wWR[lane] = wq_r * eb[0] - wq_i * eb[1];
-        wWI[lane] = wq_r * eb[1] + wq_i * eb[0];
-      }
-      wave_lds_sync();
-      const uint16_t* kt = c.k_tail + bh * BK * D;
-      const uint16_t* vt = c.v_tail + bh * BK * D;
-      float mloc = -__builtin_inff();
-      float sc[Sh::NIT];
-#pragma unroll
-      for (int it = 0; it < Sh::NIT; ++it) {
-        const int j = it * Sh::TPI + ts;
-        float s = 0.0f;
-        if (j < ntail) {
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const int i = r * 8 + m;
-            const float a = h2f(kt[j * D + i]), bb = h2f(kt[j * D + i + Sh::HALF]);
-            const float wr = wWR[i], wi = wWI[i];
-            const float X = __builtin_fmaf(wr, a, -wi * bb);
-            const float Y = -__builtin_fmaf(wi, a, wr * bb);
-            s = __builtin_fmaf(table[j * Sh::TPITCH + 2 * i], X, s);
-            s = __builtin_fmaf(table[j * Sh::TPITCH + 2 * i + 1], Y, s);
-          }
-        }
-        s = group_sum<Sh::LPT>(s);
-        if (j >= ntail) s = -__builtin_inff();
-        sc[it] = s;
-        mloc = fmaxf(mloc, s);
-      }
-      const float mnew = fmaxf(st.m, wave_max(mloc));
-      const float alpha = exp2f(st.m - mnew);
-      st.m = mnew;
-      float psum = 0.0f;
-      if (r == 0) {
-#pragma unroll
-        for (int it = 0; it < Sh::NIT; ++it) {
-          const int j = it * Sh::TPI + ts;
-          if (j < ntail) {
-            const float p = exp2f(sc[it] - mnew);
-            psum += p;
-            Pl[j] = p;
-          }
-        }
-      }
-      st.lpart = __builtin_fmaf(st.lpart, alpha, psum);
-      for (int k = 0; k < 4; ++k) st.acc[k] *= alpha;
-      st.zpart[0] *= alpha;
-      st.zpart[1] *= alpha;
-      wave_lds_sync();
-      if (lane < Sh::CHL) {
-        const int ch0 = 4 * lane;
-        for (int j = 0; j < ntail; ++j) {
-          const float p = Pl[j];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) st.acc[k] = __builtin_fmaf(p, h2f(vt[j * D + ch0 + k]), st.acc[k]);
-        }
-      }
-      wave_lds_sync();
-    }
-
     // ---- finish the item: reduce across lanes and write (m, l, o) of this split
     const float l = wave_sum(st.lpart);
     const float z0 = wave_sum(st.zpart[0]);
@@ -573,21 +567,22 @@ __global__ __launch_bounds__(kThreads) void decode_mha_kernel(kvq_cache c, const
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus);
 
-template <int D, int BK, int KB, int VB>
+template <int D, int BK, int KB, int VB, bool OUTL>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                    hipStream_t s, int cus) {
   using Sh = MShape<D, BK, KB, VB>;
+  constexpr int kNW = waves_for<OUTL>();
   const int ko = host_kout(c.cfg);
   const MLds L = mha_lds(D, BK, ko, Sh::TPI);
-  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kWaves * L.total) * sizeof(float);
+  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kNW * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, OUTL>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
-  int64_t grid = (nitems + kWaves - 1) / kWaves;
+  int64_t grid = (nitems + kNW - 1) / kNW;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB>), dim3((unsigned)grid), dim3(kThreads), bytes, s, c, q,
+  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, OUTL>), dim3((unsigned)grid), dim3(kNW * 64), bytes, s, c, q,
                      q_pos, ws, S, nitems);
   return hipGetLastError();
 }
@@ -601,8 +596,10 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
       g.k_block * ng > 256)
     return hipErrorNotSupported;
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
-#define KVQ_MHA(d, bk, kb, vb) \
-  if (D == d && BK == bk && KB == kb && VB == vb) return launch_mha_typed<d, bk, kb, vb>(c, q, q_pos, ws, S, s, cus);
+#define KVQ_MHA(d, bk, kb, vb)                                                                  \
+  if (D == d && BK == bk && KB == kb && VB == vb)                                               \
+    return ko ? launch_mha_typed<d, bk, kb, vb, true>(c, q, q_pos, ws, S, s, cus)               \
+              : launch_mha_typed<d, bk, kb, vb, false>(c, q, q_pos, ws, S, s, cus);
   KVQ_MHA(128, 128, 4, 4) KVQ_MHA(128, 128, 4, 2) KVQ_MHA(128, 128, 2, 4) KVQ_MHA(128, 128, 2, 2)
   KVQ_MHA(128, 64, 4, 4) KVQ_MHA(128, 64, 4, 2) KVQ_MHA(128, 64, 2, 4) KVQ_MHA(128, 64, 2, 2)
   KVQ_MHA(64, 128, 4, 4) KVQ_MHA(64, 128, 4, 2) KVQ_MHA(64, 128, 2, 4) KVQ_MHA(64, 128, 2, 2)
