@@ -181,6 +181,7 @@ def test_full_size_sampled(name):
         cache.append(upload(k), upload(v))
         del k, v
         t += n
+        say("  appended tokens", t, "of", T)
     torch.cuda.synchronize()
     say("  appended", cache.length)
     sample = SAMPLE[name]
@@ -191,6 +192,7 @@ def test_full_size_sampled(name):
         hc = oracle.HeadCache(cfg, None if lut is None else lut[h]).build(kh, vh)
         compare_head(cache, hc, cfg, oracle.kout(cfg), b, h)
         heads[(b, h)] = hc
+        say("  head", (b, h), "bitwise equal")
     say("  sampled heads bitwise equal")
     q = synth.gen_q(cfg)
     out = cache.decode(upload(q)).cpu().numpy()
