@@ -219,7 +219,7 @@ def main():
     log("decode  %.1f us  %.1f GB/s (%.1f%% of 8 TB/s)" % (dec_ms.mean() * 1e3, dec_gbps, dec_gbps / 80))
     log("append  %.1f us  %.1f GB/s  %.3g tokens/s" % (app_ms.mean() * 1e3, app_gbps, app_tps))
 
-    dec_hash = source_hash(["decode.hip", "kvq_device.h"])
+    dec_hash = source_hash(["decode_mha.hip", "decode.hip", "kvq_device.h"])
     app_hash = source_hash(["quantize.hip", "kvq_device.h"])
     tr_dec = measured_traffic("decode", dec_hash)
     tr_app = measured_traffic("append", app_hash)
