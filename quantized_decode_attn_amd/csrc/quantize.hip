@@ -122,6 +122,7 @@ struct QShared {
   float meta_z[BK * (D / 16) > D ? BK * (D / 16) : D];
   float meta_s[BK * (D / 16) > D ? BK * (D / 16) : D];
   float mids[D * 15];
+  alignas(16) uint8_t krow[BK * D / 2];  // packed key rows of the block (k_bits <= 4)
   float part_lo[kThreads], part_hi[kThreads];
   int part_n[kThreads];
   uint32_t hist[256];
@@ -181,6 +182,318 @@ __device__ __forceinline__ void pack_key_rows(uint8_t* out, CodeFn code_of) {
       for (int k = 0; k < KB; ++k) reinterpret_cast<uint32_t*>(dst)[k] = w[k];
     }
   }
+}
+
+
+// Uniform code from a dense value with a reciprocal multiply: exact unless the
+// quotient lies within 2^-12 of a rounding boundary, which `tie` reports so that the
+// caller redoes the element with the correctly rounded divide (code_uniform).  The
+// reciprocal and the multiply together are within 2 ulp of the IEEE quotient, far
+// inside that margin for |q| <= L + 1; values beyond are clamped first.
+__device__ __forceinline__ uint32_t code_fast(float d, float z, float r, float Lf, bool& tie) {
+  const float x = d - z;
+  const float qv = x * r;
+  const float qc = __builtin_amdgcn_fmed3f(qv, -0.75f, Lf + 0.75f);
+  const float rr = __builtin_rintf(qc);
+  tie |= fabsf(qc - rr) > 0.49975586f;  // 0.5 - 2^-12
+  return (uint32_t)__builtin_amdgcn_fmed3f(rr, 0.0f, Lf);
+}
+
+__device__ __forceinline__ float recip_or_zero(float s) { return s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s); }
+
+template <int D, int BK, int VB>
+__device__ __forceinline__ void value_cells_t(QShared<D, BK>& sh, const kvq_cache& c, int64_t bh, int64_t n,
+                                              int L, bool clip, float thr, bool outl) {
+  constexpr int P = QShared<D, BK>::kPitch;
+  constexpr int TPW = 32 / VB;          // tokens per word (8 or 16)
+  constexpr int CW = VB == 4 ? 8 : 4;   // channels per cell
+  constexpr int NCC = D / CW;
+  constexpr int NTG = BK / TPW;
+  const int tid = threadIdx.x;
+  const int64_t T = c.cfg.capacity;
+  const int G = c.cfg.v_group, ng = D / G;
+  const int lpg = G / CW;               // lanes per value group
+  const float Lf = (float)L;
+  const bool active = tid < NCC * NTG;
+  const int tg = tid / NCC, cc = tid % NCC;
+  const int ch0 = cc * CW, grp = ch0 / G;
+
+  float x[TPW][CW];
+  uint32_t om[TPW];
+  float lo[TPW], hi[TPW];
+  int cnt[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    lo[u] = __builtin_inff(); hi[u] = -__builtin_inff(); cnt[u] = 0; om[u] = 0;
+    if (active) {
+      const int j = TPW * tg + u;
+      uint32_t hw[CW / 2];
+      if constexpr (CW == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sh.tile[j * P + ch0]);
+        hw[0] = v.x; hw[1] = v.y; hw[2] = v.z; hw[3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(&sh.tile[j * P + ch0]);
+        hw[0] = v.x; hw[1] = v.y;
+      }
+      if (outl) {
+        const uint32_t* mw = &sh.mask[j * (D / 32)];
+        om[u] = (mw[ch0 >> 5] >> (ch0 & 31)) & ((1u << CW) - 1u);
+      }
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        float v = h2f((uint16_t)(hw[q >> 1] >> (16 * (q & 1))));
+        if (clip) v = __builtin_amdgcn_fmed3f(v, -thr, thr);
+        x[u][q] = v;
+        const bool keep = !((om[u] >> q) & 1u);
+        lo[u] = keep ? fminf(lo[u], v) : lo[u];
+        hi[u] = keep ? fmaxf(hi[u], v) : hi[u];
+        cnt[u] += keep;
+      }
+    }
+  }
+  // row statistics of each token over its value group
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+    for (int m = 1; m < lpg; m <<= 1) {
+      lo[u] = fminf(lo[u], __shfl_xor(lo[u], m, kWave));
+      hi[u] = fmaxf(hi[u], __shfl_xor(hi[u], m, kWave));
+      if (outl) cnt[u] += __shfl_xor(cnt[u], m, kWave);
+    }
+  if (active) {
+    const int gi = cc % lpg;
+    for (int u0 = 0; u0 < TPW; u0 += lpg) {
+      const int uu = u0 + gi;
+      float l0 = lo[0], h0 = hi[0];
+      int c0 = cnt[0];
+#pragma unroll
+      for (int u = 1; u < TPW; ++u)
+        if (uu == u) { l0 = lo[u]; h0 = hi[u]; c0 = cnt[u]; }
+      if (uu < TPW) {
+        if (!outl) c0 = G;
+        uint16_t z16, s16;
+        meta_from(l0, h0, c0, L, &z16, &s16);
+        const int j = TPW * tg + uu;
+        c.v_scale[(bh * T + n * BK + j) * ng + grp] = s16;
+        c.v_zero[(bh * T + n * BK + j) * ng + grp] = z16;
+        sh.meta_z[j * ng + grp] = h2f(z16);
+        sh.meta_s[j * ng + grp] = h2f(s16);
+      }
+    }
+  }
+  __syncthreads();
+  if (active) {
+    uint32_t w[CW];
+#pragma unroll
+    for (int q = 0; q < CW; ++q) w[q] = 0;
+    float zu[TPW], su[TPW];
+    bool tie = false;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int j = TPW * tg + u;
+      zu[u] = sh.meta_z[j * ng + grp];
+      su[u] = sh.meta_s[j * ng + grp];
+      const float r = recip_or_zero(su[u]);
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        uint32_t cq = code_fast(x[u][q], zu[u], r, Lf, tie);
+        if (outl && ((om[u] >> q) & 1u)) cq = 0;
+        w[q] |= cq << (u * VB);
+      }
+    }
+    if (tie) {  // rare: redo with the correctly rounded divide
+#pragma unroll
+      for (int q = 0; q < CW; ++q) w[q] = 0;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int q = 0; q < CW; ++q) {
+          uint32_t cq = (uint32_t)code_uniform(x[u][q], zu[u], su[u], L);
+          if (outl && ((om[u] >> q) & 1u)) cq = 0;
+          w[q] |= cq << (u * VB);
+        }
+    }
+    uint32_t* out = static_cast<uint32_t*>(c.v_codes) + (bh * (T / TPW) + n * (BK / TPW) + tg) * D + ch0;
+    if constexpr (CW == 8) {
+      reinterpret_cast<uint4*>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      reinterpret_cast<uint4*>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      reinterpret_cast<uint4*>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Keys: a cell is 8 tokens x 8 channels, the channels being 4 rotary pairs
+// (4a..4a+3 and D/2+4a..D/2+4a+3), so that one cell yields whole packed bytes.
+// Cells of one channel set sit in consecutive lanes for the column reductions.
+template <int D, int BK>
+__device__ __forceinline__ void key_cells(QShared<D, BK>& sh, const kvq_cache& c, int64_t bh, int64_t n, int h,
+                                          int L, int kb, bool clip, float thr, bool outl) {
+  constexpr int P = QShared<D, BK>::kPitch;
+  constexpr int NTG = BK / 8;
+  constexpr int NA = D / 8;
+  const int tid = threadIdx.x;
+  const int64_t T = c.cfg.capacity;
+  const bool lut = c.cfg.k_mode == 1;
+  const float Lf = (float)L;
+  const bool active = tid < NA * NTG;
+  const int a = tid / NTG, tg = tid % NTG;
+  auto slot_ch = [&](int q) { return q < 4 ? 4 * a + q : D / 2 + 4 * a + q - 4; };
+
+  float x[8][8];
+  uint32_t om[8];
+  float lo[8], hi[8];
+  int cnt[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { lo[q] = __builtin_inff(); hi[q] = -__builtin_inff(); cnt[q] = 0; }
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = 8 * tg + u;
+      const uint2 wl = *reinterpret_cast<const uint2*>(&sh.tile[j * P + 4 * a]);
+      const uint2 wh = *reinterpret_cast<const uint2*>(&sh.tile[j * P + D / 2 + 4 * a]);
+      const uint32_t hw[4] = {wl.x, wl.y, wh.x, wh.y};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float v = h2f((uint16_t)(hw[q >> 1] >> (16 * (q & 1))));
+        if (clip) v = __builtin_amdgcn_fmed3f(v, -thr, thr);
+        x[u][q] = v;
+      }
+      om[u] = 0;
+      if (outl) {
+        const uint32_t* mw = &sh.mask[j * (D / 32)];
+        const uint32_t ml = (mw[(4 * a) >> 5] >> ((4 * a) & 31)) & 15u;
+        const uint32_t mh = (mw[(D / 2 + 4 * a) >> 5] >> ((D / 2 + 4 * a) & 31)) & 15u;
+        om[u] = ml | (mh << 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool keep = !((om[u] >> q) & 1u);
+        lo[q] = keep ? fminf(lo[q], x[u][q]) : lo[q];
+        hi[q] = keep ? fmaxf(hi[q], x[u][q]) : hi[q];
+        cnt[q] += keep;
+      }
+    }
+  }
+  // column statistics over the whole block: reduce across the NTG lanes of a set
+  if (!lut) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int m = 1; m < NTG; m <<= 1) {
+        lo[q] = fminf(lo[q], __shfl_xor(lo[q], m, kWave));
+        hi[q] = fmaxf(hi[q], __shfl_xor(hi[q], m, kWave));
+        if (outl) cnt[q] += __shfl_xor(cnt[q], m, kWave);
+      }
+    if (active && tg < 8) {
+      float l0 = lo[0], h0 = hi[0];
+      int c0 = cnt[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if (tg == q) { l0 = lo[q]; h0 = hi[q]; c0 = cnt[q]; }
+      if (!outl) c0 = BK;
+      uint16_t z16, s16;
+      meta_from(l0, h0, c0, L, &z16, &s16);
+      const int ch = slot_ch(tg);
+      c.k_scale[(bh * (T / BK) + n) * D + ch] = s16;
+      c.k_zero[(bh * (T / BK) + n) * D + ch] = z16;
+      sh.meta_z[ch] = h2f(z16);
+      sh.meta_s[ch] = h2f(s16);
+    }
+  } else {
+    for (int ch = tid; ch < D; ch += kThreads) {
+      const uint16_t* lt = c.k_lut + ((int64_t)h * D + ch) * (L + 1);
+      for (int k = 0; k < L; ++k) sh.mids[ch * 15 + k] = (h2f(lt[k]) + h2f(lt[k + 1])) * 0.5f;
+    }
+  }
+  __syncthreads();
+  if (active) {
+    uint32_t w[8];
+    if (!lut) {
+      float zq[8], sq[8], rq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        zq[q] = sh.meta_z[slot_ch(q)];
+        sq[q] = sh.meta_s[slot_ch(q)];
+        rq[q] = recip_or_zero(sq[q]);
+      }
+      bool tie = false;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        uint32_t wu = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          uint32_t cq = code_fast(x[u][q], zq[q], rq[q], Lf, tie);
+          if (outl && ((om[u] >> q) & 1u)) cq = 0;
+          const int e = 2 * (q & 3) + (q >> 2);  // element index inside the cell's row bytes
+          wu |= cq << (e * kb);
+        }
+        w[u] = wu;
+      }
+      if (tie) {  // rare: redo this lane's cell with the correctly rounded divide
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          uint32_t wu = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            uint32_t cq = (uint32_t)code_uniform(x[u][q], zq[q], sq[q], L);
+            if (outl && ((om[u] >> q) & 1u)) cq = 0;
+            wu |= cq << ((2 * (q & 3) + (q >> 2)) * kb);
+          }
+          w[u] = wu;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float* md = &sh.mids[slot_ch(q) * 15];
+        const int e = 2 * (q & 3) + (q >> 2);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          uint32_t cq = 0;
+          for (int k = 0; k < L; ++k) cq += x[u][q] > md[k];
+          if (outl && ((om[u] >> q) & 1u)) cq = 0;
+          w[u] |= cq << (e * kb);
+        }
+      }
+    }
+    // stage the packed bytes of the cell: 8 elements x kb bits = kb bytes per token row
+    const int rk = D * kb / 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uint8_t* dst = &sh.krow[(8 * tg + u) * rk + a * kb];
+      if (kb == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = w[u];
+      } else if (kb == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[u];
+      } else {
+        dst[0] = (uint8_t)w[u];
+        dst[1] = (uint8_t)(w[u] >> 8);
+        dst[2] = (uint8_t)(w[u] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  // coalesced 16-byte stores of the block's rows
+  {
+    const int rk = D * kb / 8;
+    uint8_t* out = static_cast<uint8_t*>(c.k_codes) + (bh * T + n * BK) * rk;
+    for (int idx = tid; idx < BK * rk / 16; idx += kThreads)
+      reinterpret_cast<uint4*>(out)[idx] = reinterpret_cast<const uint4*>(sh.krow)[idx];
+  }
+}
+
+// Values: a cell is (32/v_bits) consecutive tokens x CW channels, so that each of
+// its CW channels yields one packed word; the cells of one value group sit in
+// consecutive lanes for the row reductions.
+template <int D, int BK>
+__device__ __forceinline__ void value_cells(QShared<D, BK>& sh, const kvq_cache& c, int64_t bh, int64_t n,
+                                            int L, int vb, bool clip, float thr, bool outl) {
+  if (vb == 4)
+    value_cells_t<D, BK, 4>(sh, c, bh, n, L, clip, thr, outl);
+  else
+    value_cells_t<D, BK, 2>(sh, c, bh, n, L, clip, thr, outl);
 }
 
 template <int D, int BK>
@@ -339,119 +652,11 @@ __global__ __launch_bounds__(kThreads) void quantize_blocks_kernel(
   __syncthreads();
   const float thr = clip ? sh.thr : 0.0f;
 
-  auto dense = [&](int j, int ch) -> float {
-    const float x = h2f(sh.tile[j * P + ch]);
-    return clip ? fminf(fmaxf(x, -thr), thr) : x;
-  };
-  auto is_out = [&](int j, int ch) -> bool {
-    return (sh.mask[j * (D / 32) + (ch >> 5)] >> (ch & 31)) & 1u;
-  };
-
-  // 4. statistics and metadata
-  if (is_key && c.cfg.k_mode == 1) {
-    for (int ch = tid; ch < D; ch += kThreads) {
-      const uint16_t* lut = c.k_lut + ((int64_t)h * D + ch) * (L + 1);
-      for (int k = 0; k < L; ++k) sh.mids[ch * 15 + k] = (h2f(lut[k]) + h2f(lut[k + 1])) * 0.5f;
-    }
-  } else if (is_key) {
-    constexpr int kParts = kThreads / D;
-    const int ch = tid % D, part = tid / D;
-    float lo = __builtin_inff(), hi = -__builtin_inff();
-    int cnt = 0;
-    for (int j = part; j < BK; j += kParts) {
-      if (is_out(j, ch)) continue;
-      const float d = dense(j, ch);
-      lo = fminf(lo, d);
-      hi = fmaxf(hi, d);
-      ++cnt;
-    }
-    sh.part_lo[tid] = lo;
-    sh.part_hi[tid] = hi;
-    sh.part_n[tid] = cnt;
-    __syncthreads();
-    if (part == 0) {
-      for (int p = 1; p < kParts; ++p) {
-        lo = fminf(lo, sh.part_lo[tid + p * D]);
-        hi = fmaxf(hi, sh.part_hi[tid + p * D]);
-        cnt += sh.part_n[tid + p * D];
-      }
-      uint16_t z16, s16;
-      meta_from(lo, hi, cnt, L, &z16, &s16);
-      c.k_scale[(bh * (T / BK) + n) * D + ch] = s16;
-      c.k_zero[(bh * (T / BK) + n) * D + ch] = z16;
-      sh.meta_z[ch] = h2f(z16);
-      sh.meta_s[ch] = h2f(s16);
-    }
-  } else {
-    const int G = c.cfg.v_group, ng = D / G;
-    const int units = BK * ng;
-    const int per = units >= kThreads ? 1 : kThreads / units;  // threads per unit
-    const int span = G / per;
-    for (int base = 0; base < units * per; base += kThreads) {
-      const int idx = base + tid;
-      const int unit = idx / per, part = idx % per;
-      const int j = unit / ng, g = unit % ng;
-      float lo = __builtin_inff(), hi = -__builtin_inff();
-      int cnt = 0;
-      for (int ch = g * G + part * span; ch < g * G + (part + 1) * span; ++ch) {
-        if (is_out(j, ch)) continue;
-        const float d = dense(j, ch);
-        lo = fminf(lo, d);
-        hi = fmaxf(hi, d);
-        ++cnt;
-      }
-      for (int m = 1; m < per; m <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, m, kWave));
-        hi = fmaxf(hi, __shfl_xor(hi, m, kWave));
-        cnt += __shfl_xor(cnt, m, kWave);
-      }
-      if (part == 0) {
-        uint16_t z16, s16;
-        meta_from(lo, hi, cnt, L, &z16, &s16);
-        c.v_scale[(bh * T + t0 + j) * ng + g] = s16;
-        c.v_zero[(bh * T + t0 + j) * ng + g] = z16;
-        sh.meta_z[j * ng + g] = h2f(z16);
-        sh.meta_s[j * ng + g] = h2f(s16);
-      }
-    }
-  }
-  __syncthreads();
-
-  // 5. codes and packing
-  if (is_key) {
-    const int rowbytes = D * bits / 8;
-    uint8_t* out = static_cast<uint8_t*>(c.k_codes) + (bh * T + t0) * rowbytes;
-    auto code_of = [&](int j, int ch) -> uint32_t {
-      if (is_out(j, ch)) return 0u;
-      const float d = dense(j, ch);
-      if (c.cfg.k_mode == 1) {
-        uint32_t cc = 0;
-        for (int k = 0; k < L; ++k) cc += d > sh.mids[ch * 15 + k];
-        return cc;
-      }
-      return (uint32_t)code_uniform(d, sh.meta_z[ch], sh.meta_s[ch], L);
-    };
-    if (bits == 4) pack_key_rows<D, BK, 4>(out, code_of);
-    else if (bits == 3) pack_key_rows<D, BK, 3>(out, code_of);
-    else pack_key_rows<D, BK, 2>(out, code_of);
-  } else {
-    const int vb = bits, tpw = 32 / vb;
-    const int G = c.cfg.v_group, ng = D / G;
-    uint32_t* out = static_cast<uint32_t*>(c.v_codes) + (bh * (T / tpw) + t0 / tpw) * D;
-    const int words = (BK / tpw) * D;
-    for (int idx = tid; idx < words; idx += kThreads) {
-      const int g = idx / D, ch = idx % D;
-      uint32_t w = 0;
-      for (int u = 0; u < tpw; ++u) {
-        const int j = g * tpw + u;
-        int code = 0;
-        if (!is_out(j, ch))
-          code = code_uniform(dense(j, ch), sh.meta_z[j * ng + ch / G], sh.meta_s[j * ng + ch / G], L);
-        w |= (uint32_t)code << (u * vb);
-      }
-      out[idx] = w;
-    }
-  }
+  // 4-5. statistics, metadata, codes and packing, one register cell per thread
+  if (is_key)
+    key_cells<D, BK>(sh, c, bh, n, h, L, bits, clip, thr, ko > 0);
+  else
+    value_cells<D, BK>(sh, c, bh, n, L, bits, clip, thr, ko > 0);
 }
 
 // ---------------------------------------------------------------- tail copy
