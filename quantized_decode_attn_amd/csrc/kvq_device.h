@@ -55,6 +55,37 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Minimum / maximum over aligned groups of N lanes (N in {1,2,4,8,16}), delivered to
+// every lane of the group.  fminf/fmaxf return the other operand for a quiet NaN.
+template <int N>
+__device__ __forceinline__ float group_min(float v) {
+  if constexpr (N >= 2) v = fminf(v, dpp_f<kDppQuadXor1>(v));
+  if constexpr (N >= 4) v = fminf(v, dpp_f<kDppQuadXor2>(v));
+  if constexpr (N >= 8) v = fminf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = fminf(v, dpp_f<kDppRowMirror>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  return v;
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+// Unsigned maximum over the 16 lanes of a DPP row.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppQuadXor1>(v));
+  v = max(v, dpp_u<kDppQuadXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppRowMirror>(v));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));

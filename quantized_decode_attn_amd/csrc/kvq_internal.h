@@ -22,6 +22,12 @@ hipError_t launch_quantize(const kvq_cache& c, const uint16_t* k_new, const uint
                            int64_t old_len, int64_t n_new, int64_t n_first, int64_t nblocks,
                            hipStream_t s);
 
+// The two halves of launch_quantize: one kernel per tensor.
+hipError_t launch_quantize_keys(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
+                                int64_t n_first, int64_t nblocks, hipStream_t s);
+hipError_t launch_quantize_values(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
+                                  int64_t n_first, int64_t nblocks, hipStream_t s);
+
 // Copy new rows [src0, n_new) into tail slots [dst0, ...).
 hipError_t launch_tail_copy(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
                             int64_t n_new, int64_t src0, int64_t dst0, hipStream_t s);

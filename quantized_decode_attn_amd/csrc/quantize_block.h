@@ -1,0 +1,775 @@
+// quantize_block.h -- the block quantizer shared by the key and value kernels.
+//
+// Pages cited (title, address):
+//   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
+//   [UQ]   "大模型长上下文推理优化：4-bit KV Cache量化技术解析与部署实践", mlqm.cn/news/1064729
+//   [TQ]   "TurboQuant：突破大模型推理瓶颈的KVCache量化技术解析", mlqm.cn/news/1002276
+//
+// One workgroup (256 threads, 4 waves) owns one (b, kv-head, block) of one tensor.
+// The k_block x head_dim fp16 tile is staged once in LDS; the steps, in the order the
+// pages give them:
+//   1. dense-and-sparse split: per token vector, the ko largest |x| (ties to the lower
+//      column) go to the CSR ([KVC3] "Per-Vector Dense-and-Sparse Quantization");
+//      their tile entries are then overwritten with a quiet NaN, which fminf/fmaxf
+//      skip, so the statistics below exclude them at no cost;
+//   2. clip threshold: exact q-quantile of |x| over the tile (outliers included) by
+//      radix selection on the 15-bit fp16 magnitudes, linear interpolation in fp64
+//      ([UQ] section 4.2);
+//   3. statistics: keys per channel over the block ([KVC3] "Per-Channel Key
+//      Quantization", before RoPE per "Pre-RoPE Key Quantization"), values per token
+//      over channel groups ([KVC3] "Quanto 的量化原理"); fp16 zero rounded down and
+//      fp16 scale rounded up.  Clipping is monotone, so the statistics of the clipped
+//      values are the clipped statistics;
+//   4. codes: round-half-even((d - zero) / scale) clamped to [0, 2^bits - 1]
+//      (round(x/scale) of [TQ] section 4.2), or the nearest codebook entry
+//      ([KVC3] "Non-Uniform KV Cache Quantization"); outlier positions get code 0.
+//
+// Each thread holds one register cell of the tile (8 x 8 elements for keys, 8 x 8 or
+// 16 x 4 for values) from step 3 on.  The code is computed as rint((d - z) * rcp(s)),
+// which differs from the correctly rounded quotient by a few ulp only; a lane that
+// meets a quotient within 2^-12 of a rounding boundary redoes its cell with the
+// IEEE divide, so the stored bits are those of the exact definition.  Clipping to
+// [-thr, thr] is applied as a clamp of the quotient to [q(-thr), q(thr)]: the
+// quotient is monotone in d, so this equals the quotient of the clipped value.
+#pragma once
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace qb {
+
+constexpr int kThreads = 256;
+constexpr uint16_t kMarkNaN = 0x7E00;  // fp16 quiet NaN marking an outlier in the tile
+constexpr float kTieMargin = 0.49975586f;  // 0.5 - 2^-12
+
+// ---------------------------------------------------------------- block reductions
+struct Red {
+  uint32_t u[kThreads / kWave];
+  int sh_bin;
+  uint32_t sh_below;
+  float thr;
+};
+
+__device__ inline uint32_t block_sum_u32(uint32_t v, Red& r) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.u[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) s += r.u[w];
+  return s;
+}
+__device__ inline uint32_t block_min_u32(uint32_t v, Red& r) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) r.u[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t s = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) s = min(s, r.u[w]);
+  return s;
+}
+
+// First bin where the running count exceeds `rank`; returns the bin and the count
+// of everything below it.  Wave 0 scans, the result is broadcast through LDS.
+__device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rank, int* out_bin,
+                                uint32_t* out_below, Red& r) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = nbins / kWave;
+    uint32_t local = 0;
+    for (int k = 0; k < per; ++k) local += hist[lane * per + k];
+    uint32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      uint32_t o = (uint32_t)__shfl_up((int)incl, d, kWave);
+      if (lane >= d) incl += o;
+    }
+    const uint64_t over = __ballot(incl > rank);
+    const int first = __ffsll((unsigned long long)over) - 1;
+    if (lane == first) {
+      uint32_t below = incl - local;
+      int b = lane * per;
+      for (int k = 0; k < per; ++k) {
+        const uint32_t h = hist[lane * per + k];
+        if (below + h > rank) { b = lane * per + k; break; }
+        below += h;
+      }
+      r.sh_bin = b;
+      r.sh_below = below;
+    }
+  }
+  __syncthreads();
+  *out_bin = r.sh_bin;
+  *out_below = r.sh_below;
+}
+
+// ---------------------------------------------------------------- scalar pieces
+__device__ __forceinline__ int code_uniform(float d, float z, float s, int L) {
+  if (s == 0.0f) return 0;
+  const float num = d - z;
+  const float q = num / s;  // IEEE-correct fp32 division
+  float r = __builtin_rintf(q);
+  r = fmaxf(r, 0.0f);
+  r = fminf(r, (float)L);
+  return (int)r;
+}
+
+// fp16 zero = min rounded down, fp16 scale = (max - zero) / L rounded up; a group
+// with no dense value (lo > hi) gets zero 0 and scale 0.
+__device__ __forceinline__ void meta_from(float lo, float hi, int L, uint16_t* z16, uint16_t* s16) {
+  if (!(lo <= hi)) { lo = 0.0f; hi = 0.0f; }
+  lo = lo + 0.0f;
+  hi = hi + 0.0f;
+  *z16 = f2h_rd(lo);
+  const float range = hi - h2f(*z16);
+  const float s32 = range / (float)L;
+  *s16 = f2h_ru(s32);
+}
+
+__device__ __forceinline__ float recip_or_zero(float s) {
+  return s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+}
+
+// Quotient clamp bounds for one (zero, reciprocal): [0, L] without clipping, else
+// [q(-thr), q(thr)] clamped to [0, L].
+template <bool CLIP>
+__device__ __forceinline__ void quotient_bounds(float z, float r, float Lf, float thr, float* a, float* b) {
+  if constexpr (CLIP) {
+    *a = __builtin_amdgcn_fmed3f((-thr - z) * r, 0.0f, Lf);
+    *b = __builtin_amdgcn_fmed3f((thr - z) * r, 0.0f, Lf);
+  } else {
+    *a = 0.0f;
+    *b = Lf;
+  }
+}
+
+// Fast code of one element; `tie` collects quotients too close to a rounding boundary.
+template <bool OUTL>
+__device__ __forceinline__ uint32_t code_fast(float d, float z, float r, float a, float b, bool& tie) {
+  const float x = d - z;
+  const float qv = x * r;
+  float qc = __builtin_amdgcn_fmed3f(qv, a, b);
+  if constexpr (OUTL) qc = (d != d) ? 0.0f : qc;
+  const float rr = __builtin_rintf(qc);
+  tie |= fabsf(qc - rr) > kTieMargin;
+  return (uint32_t)rr;
+}
+
+// Exact code of one element (the fallback).
+template <bool OUTL, bool CLIP>
+__device__ __forceinline__ uint32_t code_exact(float d, float z, float s, int L, float thr) {
+  if constexpr (OUTL)
+    if (d != d) return 0u;
+  if constexpr (CLIP) d = fminf(fmaxf(d, -thr), thr);
+  return (uint32_t)code_uniform(d, z, s, L);
+}
+
+// ---------------------------------------------------------------- phase 1: staging
+// Rows from the old tail (tokens below old_len) or from the new input.
+template <int D, int BK>
+__device__ __forceinline__ void stage_tile(uint16_t* tile, const uint16_t* tail, const uint16_t* src_new,
+                                           int64_t bh, int64_t t0, int64_t old_len, int64_t n_new) {
+  constexpr int P = D + 8;
+  constexpr int kPerThread = BK * D / 8 / kThreads;
+  static_assert(kPerThread * kThreads * 8 == BK * D, "tile split");
+  const int64_t tail0 = (old_len / BK) * BK;
+  uint4 v[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    const int j = idx / (D / 8), part = idx % (D / 8);
+    const int64_t t = t0 + j;
+    const uint16_t* row = t < old_len ? tail + (bh * BK + (t - tail0)) * D
+                                      : src_new + (bh * n_new + (t - old_len)) * D;
+    v[i] = *reinterpret_cast<const uint4*>(row + part * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    const int j = idx / (D / 8), part = idx % (D / 8);
+    *reinterpret_cast<uint4*>(&tile[j * P + part * 8]) = v[i];
+  }
+}
+
+// ---------------------------------------------------------------- phase 2: outliers
+// 16 lanes per token row, D/16 columns per lane; the ko largest keys
+// (|x| bits << 8 | 255 - column, unique within a row) are extracted one at a time
+// by row maxima.  Outliers are written to the CSR and either marked in the tile at
+// once (MARK_NOW) or remembered in `ocol` for marking after the clip threshold.
+template <int D, int BK, bool MARK_NOW>
+__device__ __forceinline__ void block_outliers(uint16_t* tile, uint8_t* ocol, int32_t* rowptr, uint8_t* col_out,
+                                               uint16_t* val_out, int64_t bh, int64_t T, int64_t t0, int ko) {
+  constexpr int P = D + 8;
+  constexpr int kPer = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane & 15;
+  for (int pass = 0; pass < BK / 16; ++pass) {
+    const int j = pass * 16 + wave * 4 + (lane >> 4);
+    uint32_t key[kPer];
+    {
+      uint32_t raw[kPer / 2];
+      if constexpr (kPer == 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&tile[j * P + sub * kPer]);
+        raw[0] = w.x; raw[1] = w.y; raw[2] = w.z; raw[3] = w.w;
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(&tile[j * P + sub * kPer]);
+        raw[0] = w.x; raw[1] = w.y;
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const uint32_t hbits = (raw[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+        key[k] = (hbits << 8) | (uint32_t)(255 - (sub * kPer + k));
+      }
+    }
+    uint32_t sel[4] = {0, 0, 0, 0};
+    uint32_t prev = 0xffffffffu;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < ko) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) m = max(m, key[k] < prev ? key[k] : 0u);
+        m = row_max_u32(m);
+        sel[r] = m;
+        prev = m;
+      }
+    }
+    if (sub == 0) {
+      int cols[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cols[r] = 255 - (int)(sel[r] & 0xffu);
+      // ascending column order
+#pragma unroll
+      for (int a = 1; a < 4; ++a)
+#pragma unroll
+        for (int q = a; q > 0; --q)
+          if (q < ko && cols[q - 1] > cols[q]) {
+            const int t = cols[q]; cols[q] = cols[q - 1]; cols[q - 1] = t;
+          }
+      const int64_t t = t0 + j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < ko) {
+          col_out[(bh * T + t) * ko + r] = (uint8_t)cols[r];
+          val_out[(bh * T + t) * ko + r] = tile[j * P + cols[r]];
+          if constexpr (MARK_NOW) tile[j * P + cols[r]] = kMarkNaN;
+          else ocol[j * 4 + r] = (uint8_t)cols[r];
+        }
+      }
+      rowptr[bh * (T + 1) + t + 1] = (int32_t)((t + 1) * ko);
+      if (t == 0) rowptr[bh * (T + 1)] = 0;
+    }
+  }
+}
+
+template <int D, int BK>
+__device__ __forceinline__ void mark_outliers(uint16_t* tile, const uint8_t* ocol, int ko) {
+  constexpr int P = D + 8;
+  for (int idx = threadIdx.x; idx < BK * ko; idx += kThreads) {
+    const int j = idx / ko, r = idx % ko;
+    tile[j * P + ocol[j * 4 + r]] = kMarkNaN;
+  }
+}
+
+// ---------------------------------------------------------------- phase 2b: clip
+// Exact order statistics of |x| (15-bit magnitudes) over the whole tile: radix
+// selection of rank kr = floor(q (n - 1)) and the next order statistic, then
+// t = v_kr + frac * (v_kr+1 - v_kr) in fp64, each operation rounded separately.
+struct ClipSmem {
+  uint32_t hist[256];
+};
+
+template <int D, int BK>
+__device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& cs, Red& red, float quantile) {
+  constexpr int P = D + 8;
+  constexpr int NEL = BK * D;
+  constexpr int kChunks = NEL / 8;
+  const int tid = threadIdx.x;
+  const double pos = (double)quantile * (double)(NEL - 1);
+  const int64_t kr = (int64_t)floor(pos);
+  const double frac = pos - (double)kr;
+  auto chunk = [&](int idx) -> uint4 {
+    const int j = idx / (D / 8), part = idx % (D / 8);
+    return *reinterpret_cast<const uint4*>(&tile[j * P + part * 8]);
+  };
+  // pass 1: top 8 of the 15 magnitude bits
+  for (int i = tid; i < 256; i += kThreads) cs.hist[i] = 0;
+  __syncthreads();
+  for (int idx = tid; idx < kChunks; idx += kThreads) {
+    const uint4 w = chunk(idx);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t key = (ws[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+      atomicAdd(&cs.hist[key >> 7], 1u);
+    }
+  }
+  __syncthreads();
+  int bin1;
+  uint32_t below1;
+  find_bin(cs.hist, 256, (uint32_t)kr, &bin1, &below1, red);
+  __syncthreads();
+  // pass 2: low 7 bits inside the selected bin
+  for (int i = tid; i < 256; i += kThreads) cs.hist[i] = 0;
+  __syncthreads();
+  for (int idx = tid; idx < kChunks; idx += kThreads) {
+    const uint4 w = chunk(idx);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t key = (ws[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+      if ((int)(key >> 7) == bin1) atomicAdd(&cs.hist[key & 127], 1u);
+    }
+  }
+  __syncthreads();
+  int bin2;
+  uint32_t below2;
+  find_bin(cs.hist, 128, (uint32_t)kr - below1, &bin2, &below2, red);
+  const uint32_t vk = ((uint32_t)bin1 << 7) | (uint32_t)bin2;
+  // the next order statistic: vk again if it repeats past rank kr, else the smallest
+  // magnitude above vk
+  uint32_t le = 0, gt_min = 0xffffffffu;
+  for (int idx = tid; idx < kChunks; idx += kThreads) {
+    const uint4 w = chunk(idx);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t key = (ws[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+      le += key <= vk;
+      gt_min = key > vk ? min(gt_min, key) : gt_min;
+    }
+  }
+  le = block_sum_u32(le, red);
+  gt_min = block_min_u32(gt_min, red);
+  if (tid == 0) {
+    float t;
+    const double v0 = (double)h2f((uint16_t)vk);
+    if (kr + 1 >= NEL) {
+      t = (float)v0;
+    } else {
+      const uint32_t vk1 = le >= (uint32_t)(kr + 2) ? vk : gt_min;
+      const double v1 = (double)h2f((uint16_t)vk1);
+      const double diff = v1 - v0;
+      const double prod = frac * diff;
+      const double sum = v0 + prod;
+      t = (float)sum;
+    }
+    red.thr = t;
+  }
+  __syncthreads();
+  return red.thr;
+}
+
+// ---------------------------------------------------------------- shared memory
+template <int D, int BK>
+struct KeyMeta {  // per channel
+  float z[D], r[D], s[D], a[D], b[D];
+};
+template <int D, int BK>
+struct ValueMeta {  // per (group, token), groups of at least 16 channels
+  float z[(D / 16) * BK], r[(D / 16) * BK], s[(D / 16) * BK], a[(D / 16) * BK], b[(D / 16) * BK];
+};
+
+template <int D, int BK>
+struct KeySmem {
+  static constexpr int kRowPitchMax = D / 2 + 16;  // packed key row (<= 4 bits) + padding
+  union {
+    uint16_t tile[BK * (D + 8)];
+    struct {
+      KeyMeta<D, BK> meta;
+      alignas(16) uint8_t krow[BK * kRowPitchMax];
+      float mids[D * 15];
+    } out;
+  } u;
+  uint8_t ocol[BK * 4];
+  ClipSmem clip;
+  Red red;
+};
+
+template <int D, int BK>
+struct ValueSmem {
+  union {
+    uint16_t tile[BK * (D + 8)];
+    ValueMeta<D, BK> meta;
+  } u;
+  uint8_t ocol[BK * 4];
+  ClipSmem clip;
+  Red red;
+};
+
+// Steps 1, 2 and 2b for one tile; returns the clip threshold (0 without clipping).
+template <int D, int BK, bool OUTL, bool CLIP>
+__device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, ClipSmem& cs, Red& red,
+                                              const kvq_cache& c, bool is_key, const uint16_t* src_new,
+                                              int64_t bh, int64_t n, int64_t old_len, int64_t n_new) {
+  const int64_t T = c.cfg.capacity;
+  const int64_t t0 = n * BK;
+  stage_tile<D, BK>(tile, is_key ? c.k_tail : c.v_tail, src_new, bh, t0, old_len, n_new);
+  __syncthreads();
+  const int ko = kout_of(c.cfg);
+  if constexpr (OUTL) {
+    block_outliers<D, BK, !CLIP>(tile, ocol, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
+                                 is_key ? c.k_val : c.v_val, bh, T, t0, ko);
+    __syncthreads();
+  }
+  float thr = 0.0f;
+  if constexpr (CLIP) {
+    thr = clip_threshold<D, BK>(tile, cs, red, c.cfg.clip_quantile);
+    if constexpr (OUTL) {
+      mark_outliers<D, BK>(tile, ocol, ko);
+      __syncthreads();
+    }
+  }
+  return thr;
+}
+
+// ---------------------------------------------------------------- keys
+// Cell: 8 tokens x 8 channels, the channels being the rotary pairs 4a..4a+3 and
+// D/2+4a..D/2+4a+3, i.e. elements 8a..8a+7 of the packed row (element e holds channel
+// e/2 + (e%2) D/2).  Thread tid = a * NTG + tg; the cell's tokens are tg + NTG u, so
+// the NTG lanes sharing a channel set form one DPP row and read distinct LDS banks.
+template <int D, int BK, bool OUTL, bool CLIP>
+__global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
+                                                                 int64_t old_len, int64_t n_new, int64_t n_first) {
+  constexpr int P = D + 8;
+  constexpr int NTG = BK / 8;
+  constexpr int NA = D / 8;
+  __shared__ KeySmem<D, BK> sh;
+  const int tid = threadIdx.x;
+  const int64_t n = n_first + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t T = c.cfg.capacity;
+  const int64_t bh = (int64_t)b * c.cfg.kv_heads + h;
+  const int kb = c.cfg.k_bits;
+  const int L = (1 << kb) - 1;
+  const float Lf = (float)L;
+  const bool lut = c.cfg.k_mode == 1;
+
+  const float thr =
+      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
+  __syncthreads();
+
+  const bool active = tid < NA * NTG;
+  const int a = tid / NTG, tg = tid % NTG;
+  float x[8][8];
+  float lo[8], hi[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { lo[q] = __builtin_inff(); hi[q] = -__builtin_inff(); }
+  if (active) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = tg + NTG * u;
+      const uint2 wl = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + 4 * a]);
+      const uint2 wh = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + D / 2 + 4 * a]);
+      const uint32_t hw[4] = {wl.x, wl.y, wh.x, wh.y};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float v = h2f((uint16_t)(hw[q >> 1] >> (16 * (q & 1))));
+        x[u][q] = v;
+        lo[q] = fminf(lo[q], v);
+        hi[q] = fmaxf(hi[q], v);
+      }
+    }
+  }
+  __syncthreads();  // the tile is dead from here on; its space holds the outputs
+  auto& M = sh.u.out.meta;
+  const int chq[8] = {4 * a, 4 * a + 1, 4 * a + 2, 4 * a + 3, D / 2 + 4 * a, D / 2 + 4 * a + 1,
+                      D / 2 + 4 * a + 2, D / 2 + 4 * a + 3};
+  if (!lut) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      lo[q] = group_min<NTG>(lo[q]);
+      hi[q] = group_max<NTG>(hi[q]);
+    }
+    if (CLIP) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        lo[q] = fminf(fmaxf(lo[q], -thr), thr);  // clipping commutes with min and max
+        hi[q] = fminf(fmaxf(hi[q], -thr), thr);
+      }
+    }
+    if (active && tg < 8) {
+      float l0 = lo[0], h0 = hi[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if (tg == q) { l0 = lo[q]; h0 = hi[q]; }
+      uint16_t z16, s16;
+      meta_from(l0, h0, L, &z16, &s16);
+      const int ch = (tg < 4) ? 4 * a + tg : D / 2 + 4 * a + tg - 4;
+      c.k_scale[(bh * (T / BK) + n) * D + ch] = s16;
+      c.k_zero[(bh * (T / BK) + n) * D + ch] = z16;
+      const float z = h2f(z16), s = h2f(s16), r = recip_or_zero(s);
+      float qa, qb;
+      quotient_bounds<CLIP>(z, r, Lf, thr, &qa, &qb);
+      M.z[ch] = z;
+      M.s[ch] = s;
+      M.r[ch] = r;
+      M.a[ch] = qa;
+      M.b[ch] = qb;
+    }
+  } else {
+    for (int ch = tid; ch < D; ch += kThreads) {
+      const uint16_t* lt = c.k_lut + ((int64_t)h * D + ch) * (L + 1);
+      for (int k = 0; k < L; ++k) sh.u.out.mids[ch * 15 + k] = (h2f(lt[k]) + h2f(lt[k + 1])) * 0.5f;
+    }
+  }
+  __syncthreads();
+
+  const int rk = D * kb / 8;
+  const int rkp = rk + 16;
+  if (active) {
+    uint32_t w[8];
+    if (!lut) {
+      float zq[8], rq[8], aq[8], bq[8];
+      auto ld4 = [&](const float* base, float* dst) {
+        const float4 l4 = *reinterpret_cast<const float4*>(base + 4 * a);
+        const float4 h4 = *reinterpret_cast<const float4*>(base + D / 2 + 4 * a);
+        dst[0] = l4.x; dst[1] = l4.y; dst[2] = l4.z; dst[3] = l4.w;
+        dst[4] = h4.x; dst[5] = h4.y; dst[6] = h4.z; dst[7] = h4.w;
+      };
+      ld4(M.z, zq);
+      ld4(M.r, rq);
+      if constexpr (CLIP) {
+        ld4(M.a, aq);
+        ld4(M.b, bq);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { aq[q] = 0.0f; bq[q] = Lf; }
+      }
+      bool tie = false;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        uint32_t wu = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t cq = code_fast<OUTL>(x[u][q], zq[q], rq[q], aq[q], bq[q], tie);
+          wu |= cq << ((2 * (q & 3) + (q >> 2)) * kb);
+        }
+        w[u] = wu;
+      }
+      if (tie) {  // rare: this lane's cell again with the correctly rounded divide
+        float sq[8];
+        ld4(M.s, sq);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          uint32_t wu = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            wu |= code_exact<OUTL, CLIP>(x[u][q], zq[q], sq[q], L, thr) << ((2 * (q & 3) + (q >> 2)) * kb);
+          w[u] = wu;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float md[15];
+#pragma unroll
+        for (int k = 0; k < 15; ++k) md[k] = sh.u.out.mids[chq[q] * 15 + (k < L ? k : 0)];
+        const int e = 2 * (q & 3) + (q >> 2);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float d = x[u][q];
+          if constexpr (CLIP) d = fminf(fmaxf(d, -thr), thr);
+          uint32_t cq = 0;
+#pragma unroll
+          for (int k = 0; k < 15; ++k)
+            if (k < L) cq += d > md[k];
+          if constexpr (OUTL) cq = (x[u][q] != x[u][q]) ? 0u : cq;
+          w[u] |= cq << (e * kb);
+        }
+      }
+    }
+    // the cell's kb bytes of each token row
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uint8_t* dst = &sh.u.out.krow[(tg + NTG * u) * rkp + a * kb];
+      if (kb == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = w[u];
+      } else if (kb == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[u];
+      } else {
+        dst[0] = (uint8_t)w[u];
+        dst[1] = (uint8_t)(w[u] >> 8);
+        dst[2] = (uint8_t)(w[u] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  uint8_t* out = static_cast<uint8_t*>(c.k_codes) + (bh * T + n * BK) * rk;
+  if (rk % 16 == 0) {
+    const int per_row = rk / 16;
+    for (int idx = tid; idx < BK * per_row; idx += kThreads) {
+      const int j = idx / per_row, p = idx % per_row;
+      reinterpret_cast<uint4*>(out)[idx] = *reinterpret_cast<const uint4*>(&sh.u.out.krow[j * rkp + p * 16]);
+    }
+  } else {
+    const int per_row = rk / 8;
+    for (int idx = tid; idx < BK * per_row; idx += kThreads) {
+      const int j = idx / per_row, p = idx % per_row;
+      reinterpret_cast<uint2*>(out)[idx] = *reinterpret_cast<const uint2*>(&sh.u.out.krow[j * rkp + p * 8]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- values
+// Cell: TPW = 32/VB consecutive tokens x CW channels, so that each of its CW channels
+// yields one packed word.  Thread tid = tg * NCC + cc: the lanes of one value group
+// are consecutive, and the row statistics reduce across them.
+__device__ __forceinline__ float vgroup_min(float v, int lpg) {
+  if (lpg >= 2) v = fminf(v, dpp_f<kDppQuadXor1>(v));
+  if (lpg >= 4) v = fminf(v, dpp_f<kDppQuadXor2>(v));
+  if (lpg >= 8) v = fminf(v, dpp_f<kDppHalfMirror>(v));
+  if (lpg >= 16) v = fminf(v, dpp_f<kDppRowMirror>(v));
+  if (lpg >= 32) v = fminf(v, __shfl_xor(v, 16, kWave));
+  return v;
+}
+__device__ __forceinline__ float vgroup_max(float v, int lpg) {
+  if (lpg >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  if (lpg >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  if (lpg >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if (lpg >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  if (lpg >= 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  return v;
+}
+
+template <int D, int BK, int VB, bool OUTL, bool CLIP>
+__global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
+                                                                   int64_t old_len, int64_t n_new, int64_t n_first) {
+  constexpr int P = D + 8;
+  constexpr int TPW = 32 / VB;
+  constexpr int CW = VB == 4 ? 8 : 4;
+  constexpr int NCC = D / CW;
+  constexpr int NTG = BK / TPW;
+  __shared__ ValueSmem<D, BK> sh;
+  const int tid = threadIdx.x;
+  const int64_t n = n_first + blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t T = c.cfg.capacity;
+  const int64_t bh = (int64_t)b * c.cfg.kv_heads + h;
+  const int L = (1 << VB) - 1;
+  const float Lf = (float)L;
+  const int G = c.cfg.v_group, ng = D / G;
+  const int lpg = G / CW;
+
+  const float thr =
+      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
+  __syncthreads();
+
+  const bool active = tid < NCC * NTG;
+  const int tg = tid / NCC, cc = tid % NCC;
+  const int ch0 = cc * CW, grp = ch0 / G;
+  float x[TPW][CW];
+  float lo[TPW], hi[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    lo[u] = __builtin_inff();
+    hi[u] = -__builtin_inff();
+    if (active) {
+      const int j = TPW * tg + u;
+      uint32_t hw[CW / 2];
+      if constexpr (CW == 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sh.u.tile[j * P + ch0]);
+        hw[0] = v.x; hw[1] = v.y; hw[2] = v.z; hw[3] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + ch0]);
+        hw[0] = v.x; hw[1] = v.y;
+      }
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        const float v = h2f((uint16_t)(hw[q >> 1] >> (16 * (q & 1))));
+        x[u][q] = v;
+        lo[u] = fminf(lo[u], v);
+        hi[u] = fmaxf(hi[u], v);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    lo[u] = vgroup_min(lo[u], lpg);
+    hi[u] = vgroup_max(hi[u], lpg);
+    if (CLIP) {
+      lo[u] = fminf(fmaxf(lo[u], -thr), thr);
+      hi[u] = fminf(fmaxf(hi[u], -thr), thr);
+    }
+  }
+  __syncthreads();  // the tile is dead from here on; its space holds the metadata
+  auto& M = sh.u.meta;
+  if (active) {
+    const int gi = cc % lpg;
+    for (int u0 = 0; u0 < TPW; u0 += lpg) {
+      const int uu = u0 + gi;
+      if (uu < TPW) {
+        float l0 = lo[0], h0 = hi[0];
+#pragma unroll
+        for (int u = 1; u < TPW; ++u)
+          if (uu == u) { l0 = lo[u]; h0 = hi[u]; }
+        uint16_t z16, s16;
+        meta_from(l0, h0, L, &z16, &s16);
+        const int j = TPW * tg + uu;
+        c.v_scale[(bh * T + n * BK + j) * ng + grp] = s16;
+        c.v_zero[(bh * T + n * BK + j) * ng + grp] = z16;
+        const float z = h2f(z16), s = h2f(s16), r = recip_or_zero(s);
+        float qa, qb;
+        quotient_bounds<CLIP>(z, r, Lf, thr, &qa, &qb);
+        const int m = grp * BK + j;
+        M.z[m] = z;
+        M.s[m] = s;
+        M.r[m] = r;
+        M.a[m] = qa;
+        M.b[m] = qb;
+      }
+    }
+  }
+  __syncthreads();
+  if (active) {
+    const int m0 = grp * BK + TPW * tg;
+    float zu[TPW], ru[TPW], au[TPW], bu[TPW];
+    auto ldt = [&](const float* base, float* dst) {
+#pragma unroll
+      for (int u = 0; u < TPW; u += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(base + m0 + u);
+        dst[u] = f.x; dst[u + 1] = f.y; dst[u + 2] = f.z; dst[u + 3] = f.w;
+      }
+    };
+    ldt(M.z, zu);
+    ldt(M.r, ru);
+    if constexpr (CLIP) {
+      ldt(M.a, au);
+      ldt(M.b, bu);
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) { au[u] = 0.0f; bu[u] = Lf; }
+    }
+    uint32_t w[CW];
+#pragma unroll
+    for (int q = 0; q < CW; ++q) w[q] = 0;
+    bool tie = false;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int q = 0; q < CW; ++q)
+        w[q] |= code_fast<OUTL>(x[u][q], zu[u], ru[u], au[u], bu[u], tie) << (u * VB);
+    if (tie) {  // rare: this lane's cell again with the correctly rounded divide
+      float su[TPW];
+      ldt(M.s, su);
+#pragma unroll
+      for (int q = 0; q < CW; ++q) w[q] = 0;
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+#pragma unroll
+        for (int q = 0; q < CW; ++q) w[q] |= code_exact<OUTL, CLIP>(x[u][q], zu[u], su[u], L, thr) << (u * VB);
+    }
+    uint32_t* out = static_cast<uint32_t*>(c.v_codes) + (bh * (T / TPW) + n * (BK / TPW) + tg) * D + ch0;
+    reinterpret_cast<uint4*>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    if constexpr (CW == 8) reinterpret_cast<uint4*>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+}  // namespace qb
+}  // namespace kvq

@@ -1,0 +1,46 @@
+// quantize_values.hip -- the value-block kernels (see quantize_block.h for the steps).
+#include "quantize_block.h"
+
+namespace kvq {
+namespace {
+
+template <int D, int BK, int VB, bool OUTL, bool CLIP>
+hipError_t launch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
+                    int64_t n_first, int64_t nblocks, hipStream_t s) {
+  dim3 grid((unsigned)nblocks, (unsigned)c.cfg.kv_heads, (unsigned)c.cfg.batch);
+  hipLaunchKernelGGL((qb::quantize_values_kernel<D, BK, VB, OUTL, CLIP>), grid, dim3(qb::kThreads), 0, s, c,
+                     v_new, old_len, n_new, n_first);
+  return hipGetLastError();
+}
+
+template <int D, int BK, int VB>
+hipError_t dispatch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
+                      int64_t n_first, int64_t nblocks, hipStream_t s) {
+  const bool outl = kvq::host_kout(c.cfg) > 0, clip = c.cfg.clip_quantile > 0.0f;
+  if (outl && clip) return launch_v<D, BK, VB, true, true>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (outl) return launch_v<D, BK, VB, true, false>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (clip) return launch_v<D, BK, VB, false, true>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  return launch_v<D, BK, VB, false, false>(c, v_new, old_len, n_new, n_first, nblocks, s);
+}
+
+template <int D, int BK>
+hipError_t dispatch_vb(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
+                       int64_t n_first, int64_t nblocks, hipStream_t s) {
+  if (c.cfg.v_bits == 4) return dispatch_v<D, BK, 4>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (c.cfg.v_bits == 2) return dispatch_v<D, BK, 2>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_values(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
+                                  int64_t n_first, int64_t nblocks, hipStream_t s) {
+  const int D = c.cfg.head_dim, Bk = c.cfg.k_block;
+  if (D == 128 && Bk == 128) return dispatch_vb<128, 128>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (D == 128 && Bk == 64) return dispatch_vb<128, 64>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (D == 64 && Bk == 128) return dispatch_vb<64, 128>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (D == 64 && Bk == 64) return dispatch_vb<64, 64>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq
