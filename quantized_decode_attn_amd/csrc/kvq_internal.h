@@ -22,9 +22,11 @@ hipError_t launch_quantize(const kvq_cache& c, const uint16_t* k_new, const uint
                            int64_t old_len, int64_t n_new, int64_t n_first, int64_t nblocks,
                            hipStream_t s);
 
-// The two halves of launch_quantize: one kernel per tensor.
-hipError_t launch_quantize_keys(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
-                                int64_t n_first, int64_t nblocks, hipStream_t s);
+// The parts of launch_quantize: one kernel per tensor (uniform or codebook keys).
+hipError_t launch_quantize_keys_uniform(const kvq_cache& c, const uint16_t* k_new, int64_t old_len,
+                                        int64_t n_new, int64_t n_first, int64_t nblocks, hipStream_t s);
+hipError_t launch_quantize_keys_lut(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
+                                    int64_t n_first, int64_t nblocks, hipStream_t s);
 hipError_t launch_quantize_values(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
                                   int64_t n_first, int64_t nblocks, hipStream_t s);
 

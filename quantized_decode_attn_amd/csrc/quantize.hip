@@ -58,7 +58,8 @@ hipError_t launch_quantize(const kvq_cache& c, const uint16_t* k_new, const uint
                            int64_t old_len, int64_t n_new, int64_t n_first, int64_t nblocks,
                            hipStream_t s) {
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipError_t e = launch_quantize_keys(c, k_new, old_len, n_new, n_first, nblocks, s);
+  hipError_t e = c.cfg.k_mode == 1 ? launch_quantize_keys_lut(c, k_new, old_len, n_new, n_first, nblocks, s)
+                                    : launch_quantize_keys_uniform(c, k_new, old_len, n_new, n_first, nblocks, s);
   if (e != hipSuccess) return e;
   return launch_quantize_values(c, v_new, old_len, n_new, n_first, nblocks, s);
 }

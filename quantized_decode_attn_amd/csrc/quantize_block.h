@@ -27,7 +27,7 @@
 // Each thread holds one register cell of the tile (8 x 8 elements for keys, 8 x 8 or
 // 16 x 4 for values) from step 3 on.  The code is computed as rint((d - z) * rcp(s)),
 // which differs from the correctly rounded quotient by a few ulp only; a lane that
-// meets a quotient within 2^-12 of a rounding boundary redoes its cell with the
+// meets a quotient within 2^-17 of a rounding boundary redoes its cell with the
 // IEEE divide, so the stored bits are those of the exact definition.  Clipping to
 // [-thr, thr] is applied as a clamp of the quotient to [q(-thr), q(thr)]: the
 // quotient is monotone in d, so this equals the quotient of the clipped value.
@@ -41,7 +41,11 @@ namespace qb {
 
 constexpr int kThreads = 256;
 constexpr uint16_t kMarkNaN = 0x7E00;  // fp16 quiet NaN marking an outlier in the tile
-constexpr float kTieMargin = 0.49975586f;  // 0.5 - 2^-12
+// A quotient closer than 2^-17 to a rounding boundary is redone exactly.  The fast
+// quotient (d - z) * rcp(s) is within |q| 2^-22 of the correctly rounded one (rcp is
+// good to 1 ulp, the product and the IEEE quotient to half an ulp each), i.e. within
+// 2^-18 for the clamped |q| <= 16, so every other element rounds the same either way.
+constexpr float kTieMargin = 0.49999237f;  // 0.5 - 2^-17
 
 // ---------------------------------------------------------------- block reductions
 struct Red {
@@ -108,6 +112,46 @@ __device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rank, 
   *out_below = r.sh_below;
 }
 
+// ---------------------------------------------------------------- cross-lane min/max
+// One v_min_f32 / v_max_f32 with a DPP source (the s_nop covers the VALU-write to
+// DPP-read hazard).  Written out because the compiler otherwise brackets every
+// cross-lane operand with NaN-quieting moves; the operands here are never signaling
+// NaNs (converted fp16 values, infinities), and the hardware min/max return the
+// other operand for a quiet NaN.
+#define KVQ_DPP_MINMAX(NAME, OP, CTRL)                                                          \
+  __device__ __forceinline__ float NAME(float v) {                                              \
+    float r;                                                                                    \
+    asm("s_nop 1\n\t" OP " %0, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v)); \
+    return r;                                                                                   \
+  }
+KVQ_DPP_MINMAX(min_x1, "v_min_f32_dpp", "quad_perm:[1,0,3,2]")
+KVQ_DPP_MINMAX(min_x2, "v_min_f32_dpp", "quad_perm:[2,3,0,1]")
+KVQ_DPP_MINMAX(min_hm, "v_min_f32_dpp", "row_half_mirror")
+KVQ_DPP_MINMAX(min_rm, "v_min_f32_dpp", "row_mirror")
+KVQ_DPP_MINMAX(max_x1, "v_max_f32_dpp", "quad_perm:[1,0,3,2]")
+KVQ_DPP_MINMAX(max_x2, "v_max_f32_dpp", "quad_perm:[2,3,0,1]")
+KVQ_DPP_MINMAX(max_hm, "v_max_f32_dpp", "row_half_mirror")
+KVQ_DPP_MINMAX(max_rm, "v_max_f32_dpp", "row_mirror")
+#undef KVQ_DPP_MINMAX
+
+// Minimum / maximum over aligned groups of N lanes (N in {1,2,4,8,16}) for every lane.
+template <int N>
+__device__ __forceinline__ float lanes_min(float v) {
+  if constexpr (N >= 2) v = min_x1(v);
+  if constexpr (N >= 4) v = min_x2(v);
+  if constexpr (N >= 8) v = min_hm(v);
+  if constexpr (N >= 16) v = min_rm(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float lanes_max(float v) {
+  if constexpr (N >= 2) v = max_x1(v);
+  if constexpr (N >= 4) v = max_x2(v);
+  if constexpr (N >= 8) v = max_hm(v);
+  if constexpr (N >= 16) v = max_rm(v);
+  return v;
+}
+
 // ---------------------------------------------------------------- scalar pieces
 __device__ __forceinline__ int code_uniform(float d, float z, float s, int L) {
   if (s == 0.0f) return 0;
@@ -148,16 +192,23 @@ __device__ __forceinline__ void quotient_bounds(float z, float r, float Lf, floa
   }
 }
 
-// Fast code of one element; `tie` collects quotients too close to a rounding boundary.
-template <bool OUTL>
-__device__ __forceinline__ uint32_t code_fast(float d, float z, float r, float a, float b, bool& tie) {
+// Fast code of one element as an integral float; `tie` collects quotients too close
+// to a rounding boundary.  The quotient is clamped to [a, b] = [0, L], or with
+// clipping to the quotients of -thr and thr.
+template <bool OUTL, bool CLIP>
+__device__ __forceinline__ float code_fast(float d, float z, float r, float a, float b, bool& tie) {
   const float x = d - z;
-  const float qv = x * r;
-  float qc = __builtin_amdgcn_fmed3f(qv, a, b);
+  float qc = x * r;
+  qc = __builtin_amdgcn_fmed3f(qc, a, b);
   if constexpr (OUTL) qc = (d != d) ? 0.0f : qc;
   const float rr = __builtin_rintf(qc);
   tie |= fabsf(qc - rr) > kTieMargin;
-  return (uint32_t)rr;
+  return rr;
+}
+
+// Byte k of w replaced by the integral value c (0..255).
+__device__ __forceinline__ uint32_t put_byte(float c, uint32_t k, uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(c, k, w);
 }
 
 // Exact code of one element (the fallback).
@@ -377,7 +428,7 @@ struct ValueMeta {  // per (group, token), groups of at least 16 channels
 template <int D, int BK>
 struct KeySmem {
   static constexpr int kRowPitchMax = D / 2 + 16;  // packed key row (<= 4 bits) + padding
-  union {
+  union alignas(16) {
     uint16_t tile[BK * (D + 8)];
     struct {
       KeyMeta<D, BK> meta;
@@ -392,7 +443,7 @@ struct KeySmem {
 
 template <int D, int BK>
 struct ValueSmem {
-  union {
+  union alignas(16) {
     uint16_t tile[BK * (D + 8)];
     ValueMeta<D, BK> meta;
   } u;
@@ -428,11 +479,40 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, Cli
 }
 
 // ---------------------------------------------------------------- keys
+// Fast codes of a key cell packed into one word per token: element e = 2 (q % 4) + q / 4
+// of the cell sits at bits e KB of the word.
+template <int KB, bool OUTL, bool CLIP>
+__device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* zq, const float* rq, const float* aq,
+                                          const float* bq, uint32_t* w, bool& tie) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float cf[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cf[q] = code_fast<OUTL, CLIP>(x[u][q], zq[q], rq[q], aq[q], bq[q], tie);
+    uint32_t wu = 0;
+    if constexpr (KB == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wu = put_byte(__builtin_fmaf(cf[4 + i], 16.0f, cf[i]), i, wu);
+    } else if constexpr (KB == 2) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float lo2 = __builtin_fmaf(cf[4 + 2 * k], 4.0f, cf[2 * k]);
+        const float hi2 = __builtin_fmaf(cf[5 + 2 * k], 4.0f, cf[2 * k + 1]);
+        wu = put_byte(__builtin_fmaf(hi2, 16.0f, lo2), k, wu);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wu |= (uint32_t)cf[q] << ((2 * (q & 3) + (q >> 2)) * KB);
+    }
+    w[u] = wu;
+  }
+}
+
 // Cell: 8 tokens x 8 channels, the channels being the rotary pairs 4a..4a+3 and
 // D/2+4a..D/2+4a+3, i.e. elements 8a..8a+7 of the packed row (element e holds channel
 // e/2 + (e%2) D/2).  Thread tid = a * NTG + tg; the cell's tokens are tg + NTG u, so
 // the NTG lanes sharing a channel set form one DPP row and read distinct LDS banks.
-template <int D, int BK, bool OUTL, bool CLIP>
+template <int D, int BK, bool LUT, bool OUTL, bool CLIP>
 __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
                                                                  int64_t old_len, int64_t n_new, int64_t n_first) {
   constexpr int P = D + 8;
@@ -447,13 +527,13 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
   const int kb = c.cfg.k_bits;
   const int L = (1 << kb) - 1;
   const float Lf = (float)L;
-  const bool lut = c.cfg.k_mode == 1;
+  constexpr bool lut = LUT;
 
   const float thr =
       prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
   __syncthreads();
 
-  const bool active = tid < NA * NTG;
+  const bool active = NA * NTG == kThreads || tid < NA * NTG;
   const int a = tid / NTG, tg = tid % NTG;
   float x[8][8];
   float lo[8], hi[8];
@@ -479,11 +559,11 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
   auto& M = sh.u.out.meta;
   const int chq[8] = {4 * a, 4 * a + 1, 4 * a + 2, 4 * a + 3, D / 2 + 4 * a, D / 2 + 4 * a + 1,
                       D / 2 + 4 * a + 2, D / 2 + 4 * a + 3};
-  if (!lut) {
+  if constexpr (!lut) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      lo[q] = group_min<NTG>(lo[q]);
-      hi[q] = group_max<NTG>(hi[q]);
+      lo[q] = lanes_min<NTG>(lo[q]);
+      hi[q] = lanes_max<NTG>(hi[q]);
     }
     if (CLIP) {
 #pragma unroll
@@ -523,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
   const int rkp = rk + 16;
   if (active) {
     uint32_t w[8];
-    if (!lut) {
+    if constexpr (!lut) {
       float zq[8], rq[8], aq[8], bq[8];
       auto ld4 = [&](const float* base, float* dst) {
         const float4 l4 = *reinterpret_cast<const float4*>(base + 4 * a);
@@ -541,16 +621,9 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
         for (int q = 0; q < 8; ++q) { aq[q] = 0.0f; bq[q] = Lf; }
       }
       bool tie = false;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        uint32_t wu = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t cq = code_fast<OUTL>(x[u][q], zq[q], rq[q], aq[q], bq[q], tie);
-          wu |= cq << ((2 * (q & 3) + (q >> 2)) * kb);
-        }
-        w[u] = wu;
-      }
+      if (kb == 4) key_codes<4, OUTL, CLIP>(x, zq, rq, aq, bq, w, tie);
+      else if (kb == 2) key_codes<2, OUTL, CLIP>(x, zq, rq, aq, bq, w, tie);
+      else key_codes<3, OUTL, CLIP>(x, zq, rq, aq, bq, w, tie);
       if (tie) {  // rare: this lane's cell again with the correctly rounded divide
         float sq[8];
         ld4(M.s, sq);
@@ -621,21 +694,32 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
 // Cell: TPW = 32/VB consecutive tokens x CW channels, so that each of its CW channels
 // yields one packed word.  Thread tid = tg * NCC + cc: the lanes of one value group
 // are consecutive, and the row statistics reduce across them.
-__device__ __forceinline__ float vgroup_min(float v, int lpg) {
-  if (lpg >= 2) v = fminf(v, dpp_f<kDppQuadXor1>(v));
-  if (lpg >= 4) v = fminf(v, dpp_f<kDppQuadXor2>(v));
-  if (lpg >= 8) v = fminf(v, dpp_f<kDppHalfMirror>(v));
-  if (lpg >= 16) v = fminf(v, dpp_f<kDppRowMirror>(v));
-  if (lpg >= 32) v = fminf(v, __shfl_xor(v, 16, kWave));
-  return v;
-}
-__device__ __forceinline__ float vgroup_max(float v, int lpg) {
-  if (lpg >= 2) v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
-  if (lpg >= 4) v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
-  if (lpg >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  if (lpg >= 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
-  if (lpg >= 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
-  return v;
+// Row statistics over the lpg lanes of a value group, for all TPW tokens of a cell.
+template <int TPW>
+__device__ __forceinline__ void vgroup_minmax(float* lo, float* hi, int lpg) {
+  if (lpg >= 2) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) { lo[u] = min_x1(lo[u]); hi[u] = max_x1(hi[u]); }
+  }
+  if (lpg >= 4) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) { lo[u] = min_x2(lo[u]); hi[u] = max_x2(hi[u]); }
+  }
+  if (lpg >= 8) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) { lo[u] = min_hm(lo[u]); hi[u] = max_hm(hi[u]); }
+  }
+  if (lpg >= 16) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) { lo[u] = min_rm(lo[u]); hi[u] = max_rm(hi[u]); }
+  }
+  if (lpg >= 32) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      lo[u] = fminf(lo[u], __shfl_xor(lo[u], 16, kWave));
+      hi[u] = fmaxf(hi[u], __shfl_xor(hi[u], 16, kWave));
+    }
+  }
 }
 
 template <int D, int BK, int VB, bool OUTL, bool CLIP>
@@ -661,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
       prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
   __syncthreads();
 
-  const bool active = tid < NCC * NTG;
+  const bool active = NCC * NTG == kThreads || tid < NCC * NTG;
   const int tg = tid / NCC, cc = tid % NCC;
   const int ch0 = cc * CW, grp = ch0 / G;
   float x[TPW][CW];
@@ -689,10 +773,9 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
       }
     }
   }
+  vgroup_minmax<TPW>(lo, hi, lpg);
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    lo[u] = vgroup_min(lo[u], lpg);
-    hi[u] = vgroup_max(hi[u], lpg);
     if (CLIP) {
       lo[u] = fminf(fmaxf(lo[u], -thr), thr);
       hi[u] = fminf(fmaxf(hi[u], -thr), thr);
@@ -750,11 +833,27 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
 #pragma unroll
     for (int q = 0; q < CW; ++q) w[q] = 0;
     bool tie = false;
+    // token u of the word sits at bits u VB: 4-bit codes pair into bytes, 2-bit
+    // codes come in fours
+    constexpr int TPB = 8 / VB;  // tokens per byte
 #pragma unroll
-    for (int u = 0; u < TPW; ++u)
+    for (int k = 0; k < TPW / TPB; ++k) {
+      float cf[TPB][CW];
 #pragma unroll
-      for (int q = 0; q < CW; ++q)
-        w[q] |= code_fast<OUTL>(x[u][q], zu[u], ru[u], au[u], bu[u], tie) << (u * VB);
+      for (int t = 0; t < TPB; ++t)
+#pragma unroll
+        for (int q = 0; q < CW; ++q) {
+          const int u = k * TPB + t;
+          cf[t][q] = code_fast<OUTL, CLIP>(x[u][q], zu[u], ru[u], au[u], bu[u], tie);
+        }
+#pragma unroll
+      for (int q = 0; q < CW; ++q) {
+        float byte = cf[TPB - 1][q];
+#pragma unroll
+        for (int t = TPB - 2; t >= 0; --t) byte = __builtin_fmaf(byte, (float)(1 << VB), cf[t][q]);
+        w[q] = put_byte(byte, k, w[q]);
+      }
+    }
     if (tie) {  // rare: this lane's cell again with the correctly rounded divide
       float su[TPW];
       ldt(M.s, su);
