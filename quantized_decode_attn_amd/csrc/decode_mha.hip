@@ -116,14 +116,24 @@ struct BlockRegs {
 };
 
 // Loaders of the pieces of block n, each into its own register slot, so that a
-// slot can be refilled with the next block as soon as it has been consumed.
+// slot can be refilled with the next block as soon as it has been consumed.  Every
+// address is a wave-uniform block base plus a 32-bit lane offset.
 template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void load_k(BlockRegs<D, BK, KB, VB>& R, int it, const kvq_cache& c, int64_t bh,
-                                       int64_t n, int ts, int r) {
+__device__ __forceinline__ const uint8_t* k_block(const kvq_cache& c, int64_t bh, int64_t n) {
   using Sh = MShape<D, BK, KB, VB>;
-  const int64_t T = c.cfg.capacity;
-  const uint8_t* kc = static_cast<const uint8_t*>(c.k_codes) + (bh * T + n * BK + it * Sh::TPI + ts) * Sh::RK +
-                      r * (Sh::KW * 4);
+  return static_cast<const uint8_t*>(c.k_codes) + (bh * c.cfg.capacity + n * BK) * Sh::RK;
+}
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ const uint8_t* v_block(const kvq_cache& c, int64_t bh, int64_t n) {
+  using Sh = MShape<D, BK, KB, VB>;
+  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) +
+                                          (bh * (c.cfg.capacity / Sh::TPW) + n * (BK / Sh::TPW)) * D);
+}
+
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_k(BlockRegs<D, BK, KB, VB>& R, int it, const uint8_t* kblk, uint32_t koff) {
+  using Sh = MShape<D, BK, KB, VB>;
+  const uint8_t* kc = kblk + koff + it * (Sh::TPI * Sh::RK);
   if constexpr (Sh::KW == 2) {
     const uint2 x = *reinterpret_cast<const uint2*>(kc);
     R.k[it][0] = x.x;
@@ -134,13 +144,8 @@ __device__ __forceinline__ void load_k(BlockRegs<D, BK, KB, VB>& R, int it, cons
 }
 
 template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void load_v(BlockRegs<D, BK, KB, VB>& R, int i, const kvq_cache& c, int64_t bh,
-                                       int64_t n, int lane) {
-  using Sh = MShape<D, BK, KB, VB>;
-  const int64_t T = c.cfg.capacity;
-  const uint4* vw = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(c.v_codes) +
-                                                   (bh * (T / Sh::TPW) + n * (BK / Sh::TPW)) * D);
-  R.v[i] = vw[i * 64 + lane];
+__device__ __forceinline__ void load_v(BlockRegs<D, BK, KB, VB>& R, int i, const uint8_t* vblk, int lane) {
+  R.v[i] = *reinterpret_cast<const uint4*>(vblk + (uint32_t)(i * 64 + lane) * 16u);
 }
 
 template <int D, int BK, int KB, int VB>
@@ -150,22 +155,24 @@ __device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB>& R, const kv
   const int64_t T = c.cfg.capacity;
   if (lane < Sh::HALF) {
     const int64_t m = (bh * (T / BK) + n) * D;
-    R.kmeta[0] = c.k_scale[m + lane];
-    R.kmeta[1] = c.k_scale[m + lane + Sh::HALF];
-    R.kmeta[2] = c.k_zero[m + lane];
-    R.kmeta[3] = c.k_zero[m + lane + Sh::HALF];
-    const float* eb = c.rope + (int64_t)BK * D + (n * Sh::HALF + lane) * 2;
-    R.eb_c = eb[0];
-    R.eb_s = eb[1];
+    const uint16_t* ks = c.k_scale + m;
+    const uint16_t* kz = c.k_zero + m;
+    R.kmeta[0] = ks[lane];
+    R.kmeta[1] = ks[lane + Sh::HALF];
+    R.kmeta[2] = kz[lane];
+    R.kmeta[3] = kz[lane + Sh::HALF];
+    const float2 eb = reinterpret_cast<const float2*>(c.rope + (int64_t)BK * D + n * D)[lane];
+    R.eb_c = eb.x;
+    R.eb_s = eb.y;
   }
   if (ko > 0) {
     const int nb = BK * ko;
     const int64_t e0 = (bh * T + n * BK) * ko;
     if (lane * 4 < nb) {
-      R.kcol = *reinterpret_cast<const uint32_t*>(c.k_col + e0 + lane * 4);
-      R.vcol = *reinterpret_cast<const uint32_t*>(c.v_col + e0 + lane * 4);
-      R.kval = *reinterpret_cast<const uint2*>(c.k_val + e0 + lane * 4);
-      R.vval = *reinterpret_cast<const uint2*>(c.v_val + e0 + lane * 4);
+      R.kcol = reinterpret_cast<const uint32_t*>(c.k_col + e0)[lane];
+      R.vcol = reinterpret_cast<const uint32_t*>(c.v_col + e0)[lane];
+      R.kval = reinterpret_cast<const uint2*>(c.k_val + e0)[lane];
+      R.vval = reinterpret_cast<const uint2*>(c.v_val + e0)[lane];
     }
   }
 }
@@ -175,16 +182,32 @@ __device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB>& R, const kv
                                            int lane, int ng) {
   const int64_t T = c.cfg.capacity;
   const int ne = BK * ng;
+  const int64_t m0 = (bh * T + n * BK) * ng;
+  const uint16_t* vs = c.v_scale + m0;
+  const uint16_t* vz = c.v_zero + m0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
     if (e < ne) {
       const int grp = e / BK, t = e % BK;
-      const int64_t m = (bh * T + n * BK + t) * ng + grp;
-      R.vs[k] = c.v_scale[m];
-      R.vz[k] = c.v_zero[m];
+      const uint32_t m = (uint32_t)(t * ng + grp);
+      R.vs[k] = vs[m];
+      R.vz[k] = vz[m];
     }
   }
+}
+
+// Maximum over the wave, returned wave-uniform: row maxima by DPP, then the
+// row_bcast steps carry them to lane 63.  Operands are scores or weights (never
+// signaling NaNs), so no quieting is needed around the cross-lane reads.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 template <int D, int BK, int KB, int VB>
@@ -200,8 +223,10 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               float wq_r, float wq_i, float inv_unit, int lane, int ts, int r,
                                               int G, int ng, int ko, const kvq_cache& c, int64_t bh, int64_t n,
-                                              bool more) {
+                                              bool more, uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
+  const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, n + 1);
+  const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, n + 1);
   float* wA1 = wl + L.wts;
   float* wB1 = wA1 + Sh::HALF;
   float* wZ1 = wB1 + Sh::HALF;
@@ -275,7 +300,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     const float* tab = table + j * Sh::TPITCH + 16 * r;
     float ca[8], cb[8];
     unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
-    if (more) load_k(R, it, c, bh, n + 1, ts, r);
+    if (more) load_k(R, it, knext, koff);
     float s = 0.0f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -309,15 +334,15 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   }
 
   // ---- online softmax in base 2
-  const float mblk = wave_max(mloc);
+  const float mblk = wave_max_uniform(mloc);
   const float mnew = fmaxf(st.m, mblk);
-  const float alpha = exp2f(st.m - mnew);
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
   st.m = mnew;
   float psum = 0.0f;
   if (r == 0) {
 #pragma unroll
     for (int it = 0; it < Sh::NIT; ++it) {
-      const float p = exp2f(sc[it] - mnew);
+      const float p = __builtin_amdgcn_exp2f(sc[it] - mnew);
       psum += p;
       Pl[it * Sh::TPI + ts] = p;
     }
@@ -356,10 +381,11 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     }
   }
   if (more) load_vmeta(R, c, bh, n + 1, lane, ng);
-  wmax0 = wave_max(wmax0);
-  if (ng > 1) wmax1 = wave_max(wmax1);
-  const float kq0 = wmax0 > 0.0f ? 65535.0f / wmax0 : 0.0f;
-  const float kq1 = wmax1 > 0.0f ? 65535.0f / wmax1 : 0.0f;
+  wmax0 = wave_max_uniform(wmax0);
+  if (ng > 1) wmax1 = wave_max_uniform(wmax1);
+  // fixed-point scale and its inverse; they need only agree with each other
+  const float kq0 = wmax0 > 0.0f ? 65535.0f * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
+  const float kq1 = wmax1 > 0.0f ? 65535.0f * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
@@ -412,7 +438,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   for (int i = 0; i < Sh::NVI; ++i) {
     const int g = i * (256 / D) + (4 * lane) / D;
     const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
-    if (more) load_v(R, i, c, bh, n + 1, lane);
+    if (more) load_v(R, i, vnext, lane);
     if constexpr (VB == 4) {
       const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 4 * g);
 #pragma unroll
@@ -440,8 +466,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     }
   }
   {
-    const float inv = grp0 == 0 ? (wmax0 > 0.0f ? wmax0 / 65535.0f : 0.0f)
-                                : (wmax1 > 0.0f ? wmax1 / 65535.0f : 0.0f);
+    const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / 65535.0f);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t tot = ia[k][0] + (ia[k][1] << 4) + (ia[k][2] << 8) + (ia[k][3] << 12);
@@ -489,6 +514,7 @@ __global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
+  const uint32_t koff = (uint32_t)(ts * Sh::RK + r * (Sh::KW * 4));
 
   float* table = lds;
   for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += kNT) {
@@ -532,13 +558,15 @@ __global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_
     if (n0 < n1) {
       load_kmeta(R, c, bh, n0, lane, ko);
       load_vmeta(R, c, bh, n0, lane, ng);
+      const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
+      const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
 #pragma unroll
-      for (int it = 0; it < Sh::NIT; ++it) load_k(R, it, c, bh, n0, ts, r);
+      for (int it = 0; it < Sh::NIT; ++it) load_k(R, it, kb0, koff);
 #pragma unroll
-      for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, c, bh, n0, lane);
+      for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
     }
     for (int64_t n = n0; n < n1; ++n)
-      process_block(R, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, ko, c, bh, n, n + 1 < n1);
+      process_block(R, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, ko, c, bh, n, n + 1 < n1, koff);
 
     // ---- finish the item: reduce across lanes and write (m, l, o) of this split
     const float l = wave_sum(st.lpart);
