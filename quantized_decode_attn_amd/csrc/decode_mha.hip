@@ -197,6 +197,16 @@ __device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB>& R, const kv
   }
 }
 
+// Sum over aligned groups of N lanes (N in {2, 4, 8}), one DPP add per step.
+template <int N>
+__device__ __forceinline__ float lanes_sum(float v) {
+  if constexpr (N >= 2) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(v));
+  if constexpr (N >= 4) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(v));
+  if constexpr (N >= 8) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
+  static_assert(N <= 8, "groups of at most 8 lanes");
+  return v;
+}
+
 // Maximum over the wave, returned wave-uniform: row maxima by DPP, then the
 // row_bcast steps carry them to lane 63.  Operands are scores or weights (never
 // signaling NaNs), so no quieting is needed around the cross-lane reads.
@@ -216,8 +226,9 @@ struct MState {
 };
 
 // Process one quantized block held in registers.
-// Process quantized block n held in R; every register slot is refilled with block
-// n + 1 right after its last use when `more` is set.
+// Process quantized block n held in R; every register slot is refilled right after
+// its last use with block n + 1, or with block n again when `more` is clear (the
+// loads stay unconditional, so no register has to survive them).
 template <int D, int BK, int KB, int VB>
 __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MState<D, BK, KB, VB>& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
@@ -225,8 +236,9 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
                                               int G, int ng, int ko, const kvq_cache& c, int64_t bh, int64_t n,
                                               bool more, uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
-  const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, n + 1);
-  const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, n + 1);
+  const int64_t nn = more ? n + 1 : n;
+  const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
+  const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, nn);
   float* wA1 = wl + L.wts;
   float* wB1 = wA1 + Sh::HALF;
   float* wZ1 = wB1 + Sh::HALF;
@@ -269,7 +281,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     reinterpret_cast<uint2*>(CVK)[lane] = R.kval;
     reinterpret_cast<uint2*>(CVV)[lane] = R.vval;
   }
-  if (more) load_kmeta(R, c, bh, n + 1, lane, ko);
+  load_kmeta(R, c, bh, nn, lane, ko);
   wave_lds_sync();
   float A1[8], B1[8], Z1[8], A2[8], B2[8], Z2[8];
   {
@@ -300,7 +312,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     const float* tab = table + j * Sh::TPITCH + 16 * r;
     float ca[8], cb[8];
     unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
-    if (more) load_k(R, it, knext, koff);
+    load_k(R, it, knext, koff);
     float s = 0.0f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -328,7 +340,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
       const float dlt = dlt0 - (a ? wZA[i] : wZB[i]);
       s += a ? dlt * (wr * cs - wi * sn) : -dlt * (wi * cs + wr * sn);
     }
-    s = group_sum<Sh::LPT>(s);
+    s = lanes_sum<Sh::LPT>(s);
     sc[it] = s;
     mloc = fmaxf(mloc, s);
   }
@@ -380,7 +392,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
       if (ko > 0) VZl[grp * BK + t] = z;
     }
   }
-  if (more) load_vmeta(R, c, bh, n + 1, lane, ng);
+  load_vmeta(R, c, bh, nn, lane, ng);
   wmax0 = wave_max_uniform(wmax0);
   if (ng > 1) wmax1 = wave_max_uniform(wmax1);
   // fixed-point scale and its inverse; they need only agree with each other
@@ -438,7 +450,6 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   for (int i = 0; i < Sh::NVI; ++i) {
     const int g = i * (256 / D) + (4 * lane) / D;
     const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
-    if (more) load_v(R, i, vnext, lane);
     if constexpr (VB == 4) {
       const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 4 * g);
 #pragma unroll
@@ -465,6 +476,8 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vnext, lane);
   {
     const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / 65535.0f);
 #pragma unroll
