@@ -220,7 +220,8 @@ def main():
     log("append  %.1f us  %.1f GB/s  %.3g tokens/s" % (app_ms.mean() * 1e3, app_gbps, app_tps))
 
     dec_hash = source_hash(["decode_mha.hip", "decode.hip", "kvq_device.h"])
-    app_hash = source_hash(["quantize.hip", "kvq_device.h"])
+    app_hash = source_hash(["quantize.hip", "quantize_block.h", "quantize_keys.hip", "quantize_keys_lut.hip",
+                            "quantize_values.hip", "kvq_device.h"])
     tr_dec = measured_traffic("decode", dec_hash)
     tr_app = measured_traffic("append", app_hash)
     rec = {

@@ -495,6 +495,8 @@ hipError_t launch_d(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float*
 
 }  // namespace
 
+hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                             hipStream_t s, int cus);
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus);
 
@@ -503,7 +505,8 @@ hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, f
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   hipError_t e = launch_decode_mha(c, q, q_pos, ws, splits, s, cus);
-  int with_tail = 1;  // the multi-head kernel leaves the unquantized tail to the finish kernel
+  if (e == hipErrorNotSupported) e = launch_decode_gqa(c, q, q_pos, ws, splits, s, cus);
+  int with_tail = 1;  // the tuned kernels leave the unquantized tail to the finish kernel
   if (e == hipErrorNotSupported) {
     with_tail = 0;
     if (c.cfg.head_dim == 128) e = launch_d<128>(c, q, q_pos, ws, splits, s, cus);

@@ -27,32 +27,16 @@
 // value is ever written to memory.
 #include <math.h>
 
-#include "kvq_device.h"
-#include "kvq_internal.h"
+#include "decode_common.h"
 
 namespace kvq {
 namespace {
 
+using namespace dcm;
+
 // Waves per workgroup: 8 (two per SIMD) when the kernel fits 256 registers, else 4.
 template <bool OUTL>
 constexpr int waves_for() { return OUTL ? 4 : 8; }
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <int D, int BK, int KB, int VB>
-struct MShape {
-  static constexpr int HALF = D / 2;
-  static constexpr int PPL = 8;                  // rotary pairs per lane
-  static constexpr int LPT = HALF / PPL;         // lanes per key token
-  static constexpr int TPI = kWave / LPT;        // key tokens per iteration
-  static constexpr int NIT = BK / TPI;           // iterations per block
-  static constexpr int KW = 2 * PPL * KB / 32;   // code dwords per lane per token
-  static constexpr int RK = D * KB / 8;          // key row bytes
-  static constexpr int TPW = 32 / VB;            // tokens per value word
-  static constexpr int WPB = (BK / TPW) * D;     // value words per block
-  static constexpr int NVI = WPB / 256;          // 16-byte value loads per lane per block
-  static constexpr int TPITCH = D + 4;           // floats per rotary-table row
-  static constexpr int CHL = D / 4;              // lanes owning distinct value channels
-};
 
 // Per-wave LDS area, in floats.
 struct MLds {
@@ -69,155 +53,6 @@ __host__ __device__ inline MLds mha_lds(int D, int BK, int ko, int tpi) {
   m.csr = o; o += ko ? (BK * ko * 6 + 3) / 4 : 0;   // k cols, v cols (u8), k vals, v vals (u16)
   m.total = o;
   return m;
-}
-
-typedef float f2v __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f2v cvt_lo(uint32_t x) { return __builtin_amdgcn_cvt_pk_f32_fp8(x, false); }
-__device__ __forceinline__ f2v cvt_hi(uint32_t x) { return __builtin_amdgcn_cvt_pk_f32_fp8(x, true); }
-
-// Codes of one lane's 8 rotary pairs as floats (times the fp8 unit).
-template <int KB, int KW>
-__device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[KW], float (&ca)[8], float (&cb)[8]) {
-  if constexpr (KB == 4) {
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const uint32_t lo = w[d] & 0x0F0F0F0Fu, hi = (w[d] >> 4) & 0x0F0F0F0Fu;
-      const f2v a01 = cvt_lo(lo), a23 = cvt_hi(lo), b01 = cvt_lo(hi), b23 = cvt_hi(hi);
-      ca[4 * d] = a01.x; ca[4 * d + 1] = a01.y; ca[4 * d + 2] = a23.x; ca[4 * d + 3] = a23.y;
-      cb[4 * d] = b01.x; cb[4 * d + 1] = b01.y; cb[4 * d + 2] = b23.x; cb[4 * d + 3] = b23.y;
-    }
-  } else {
-    const uint32_t x0 = w[0] & 0x03030303u, x1 = (w[0] >> 2) & 0x03030303u;
-    const uint32_t x2 = (w[0] >> 4) & 0x03030303u, x3 = (w[0] >> 6) & 0x03030303u;
-    f2v t;
-    t = cvt_lo(x0); ca[0] = t.x; ca[2] = t.y;
-    t = cvt_hi(x0); ca[4] = t.x; ca[6] = t.y;
-    t = cvt_lo(x2); ca[1] = t.x; ca[3] = t.y;
-    t = cvt_hi(x2); ca[5] = t.x; ca[7] = t.y;
-    t = cvt_lo(x1); cb[0] = t.x; cb[2] = t.y;
-    t = cvt_hi(x1); cb[4] = t.x; cb[6] = t.y;
-    t = cvt_lo(x3); cb[1] = t.x; cb[3] = t.y;
-    t = cvt_hi(x3); cb[5] = t.x; cb[7] = t.y;
-  }
-}
-
-// All global data of one block that a wave needs, held in registers.
-template <int D, int BK, int KB, int VB>
-struct BlockRegs {
-  using Sh = MShape<D, BK, KB, VB>;
-  uint32_t k[Sh::NIT][Sh::KW];
-  uint4 v[Sh::NVI];
-  uint16_t kmeta[4];      // lane i < D/2: scale[i], scale[i+D/2], zero[i], zero[i+D/2]
-  float eb_c, eb_s;       // lane i < D/2: cos/sin(n*Bk*f_i)
-  uint16_t vs[4], vz[4];  // value scale/zero of elements lane + 64*k
-  uint32_t kcol, vcol;    // outlier CSR slice of the block (bytes lane*4..)
-  uint2 kval, vval;       // (bytes lane*8..)
-};
-
-// Loaders of the pieces of block n, each into its own register slot, so that a
-// slot can be refilled with the next block as soon as it has been consumed.  Every
-// address is a wave-uniform block base plus a 32-bit lane offset.
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ const uint8_t* k_block(const kvq_cache& c, int64_t bh, int64_t n) {
-  using Sh = MShape<D, BK, KB, VB>;
-  return static_cast<const uint8_t*>(c.k_codes) + (bh * c.cfg.capacity + n * BK) * Sh::RK;
-}
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ const uint8_t* v_block(const kvq_cache& c, int64_t bh, int64_t n) {
-  using Sh = MShape<D, BK, KB, VB>;
-  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) +
-                                          (bh * (c.cfg.capacity / Sh::TPW) + n * (BK / Sh::TPW)) * D);
-}
-
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void load_k(BlockRegs<D, BK, KB, VB>& R, int it, const uint8_t* kblk, uint32_t koff) {
-  using Sh = MShape<D, BK, KB, VB>;
-  const uint8_t* kc = kblk + koff + it * (Sh::TPI * Sh::RK);
-  if constexpr (Sh::KW == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(kc);
-    R.k[it][0] = x.x;
-    R.k[it][1] = x.y;
-  } else {
-    R.k[it][0] = *reinterpret_cast<const uint32_t*>(kc);
-  }
-}
-
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void load_v(BlockRegs<D, BK, KB, VB>& R, int i, const uint8_t* vblk, int lane) {
-  R.v[i] = *reinterpret_cast<const uint4*>(vblk + (uint32_t)(i * 64 + lane) * 16u);
-}
-
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB>& R, const kvq_cache& c, int64_t bh, int64_t n,
-                                           int lane, int ko) {
-  using Sh = MShape<D, BK, KB, VB>;
-  const int64_t T = c.cfg.capacity;
-  if (lane < Sh::HALF) {
-    const int64_t m = (bh * (T / BK) + n) * D;
-    const uint16_t* ks = c.k_scale + m;
-    const uint16_t* kz = c.k_zero + m;
-    R.kmeta[0] = ks[lane];
-    R.kmeta[1] = ks[lane + Sh::HALF];
-    R.kmeta[2] = kz[lane];
-    R.kmeta[3] = kz[lane + Sh::HALF];
-    const float2 eb = reinterpret_cast<const float2*>(c.rope + (int64_t)BK * D + n * D)[lane];
-    R.eb_c = eb.x;
-    R.eb_s = eb.y;
-  }
-  if (ko > 0) {
-    const int nb = BK * ko;
-    const int64_t e0 = (bh * T + n * BK) * ko;
-    if (lane * 4 < nb) {
-      R.kcol = reinterpret_cast<const uint32_t*>(c.k_col + e0)[lane];
-      R.vcol = reinterpret_cast<const uint32_t*>(c.v_col + e0)[lane];
-      R.kval = reinterpret_cast<const uint2*>(c.k_val + e0)[lane];
-      R.vval = reinterpret_cast<const uint2*>(c.v_val + e0)[lane];
-    }
-  }
-}
-
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB>& R, const kvq_cache& c, int64_t bh, int64_t n,
-                                           int lane, int ng) {
-  const int64_t T = c.cfg.capacity;
-  const int ne = BK * ng;
-  const int64_t m0 = (bh * T + n * BK) * ng;
-  const uint16_t* vs = c.v_scale + m0;
-  const uint16_t* vz = c.v_zero + m0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = lane + 64 * k;
-    if (e < ne) {
-      const int grp = e / BK, t = e % BK;
-      const uint32_t m = (uint32_t)(t * ng + grp);
-      R.vs[k] = vs[m];
-      R.vz[k] = vz[m];
-    }
-  }
-}
-
-// Sum over aligned groups of N lanes (N in {2, 4, 8}), one DPP add per step.
-template <int N>
-__device__ __forceinline__ float lanes_sum(float v) {
-  if constexpr (N >= 2) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(v));
-  if constexpr (N >= 4) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(v));
-  if constexpr (N >= 8) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
-  static_assert(N <= 8, "groups of at most 8 lanes");
-  return v;
-}
-
-// Maximum over the wave, returned wave-uniform: row maxima by DPP, then the
-// row_bcast steps carry them to lane 63.  Operands are scores or weights (never
-// signaling NaNs), so no quieting is needed around the cross-lane reads.
-__device__ __forceinline__ float wave_max_uniform(float v) {
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(v));
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(v));
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(v));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 template <int D, int BK, int KB, int VB>
@@ -306,17 +141,26 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   // ---- scores
   float sc[Sh::NIT];
   float mloc = -__builtin_inff();
+  // rotary-table rows in registers one iteration ahead, so the LDS latency of the
+  // next token's cos/sin overlaps this token's arithmetic
+  float4 tq[2][4];
+  auto load_tab = [&](int it, float4(&t)[4]) {
+    const float* tab = table + (it * Sh::TPI + ts) * Sh::TPITCH + 16 * r;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) t[q4] = *reinterpret_cast<const float4*>(tab + 4 * q4);
+  };
+  load_tab(0, tq[0]);
 #pragma unroll
   for (int it = 0; it < Sh::NIT; ++it) {
     const int j = it * Sh::TPI + ts;
-    const float* tab = table + j * Sh::TPITCH + 16 * r;
+    if (it + 1 < Sh::NIT) load_tab(it + 1, tq[(it + 1) & 1]);
     float ca[8], cb[8];
     unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
     load_k(R, it, knext, koff);
     float s = 0.0f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 t = *reinterpret_cast<const float4*>(tab + 4 * q4);
+      const float4 t = tq[it & 1][q4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int m = 2 * q4 + u;
