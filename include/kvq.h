@@ -164,7 +164,8 @@ kvq_status kvq_quantize_append(kvq_cache *cache, const void *k_new, const void *
                                int64_t n_new, void *stream);
 
 /* Bytes of device workspace kvq_decode_attention needs for `num_splits` splits of
- * the cache per (b, kv-head) (0 = the library's choice for this cache). */
+ * the cache per (b, kv-head) (0 = the library's choice for this cache; at most
+ * 4096). */
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_splits);
 
 /* Single-query decode attention over the whole cache:
@@ -176,7 +177,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_splits);
  * [batch][q_heads][head_dim].  ws: *device* workspace of ws_bytes >=
  * kvq_decode_workspace_bytes(cache, num_splits).  q_pos >= 0 (usually length-1).
  * The result does not depend on num_splits beyond fp32 rounding and is bitwise
- * reproducible for a fixed num_splits.  KVQ_EINVAL if length == 0. */
+ * reproducible for a fixed num_splits.  KVQ_EINVAL if length == 0 or num_splits is
+ * negative or above 4096. */
 kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int64_t q_pos,
                                 float *out, void *ws, size_t ws_bytes, int32_t num_splits,
                                 void *stream);

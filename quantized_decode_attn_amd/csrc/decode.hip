@@ -35,6 +35,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kFinishMaxSplits = 4096;  // split weights staged in LDS (fp32)
 
 template <int D, int KB, int KMODE, int VB>
 struct Shape {
@@ -428,25 +429,47 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
     }
     __syncthreads();
   }
+  // Merge of the splits (and the tail) in a fixed order.  Split weights
+  // w_s = 2^(m_s - M) are formed once in LDS; the channels then read their partial
+  // outputs with independent loads, the splits divided between the two thread halves
+  // and the halves added in a fixed order.
+  __shared__ float wsh[kFinishMaxSplits];
+  __shared__ float osh[256];
+  __shared__ float red2[8];
   const float* base = ws + bq * (int64_t)S * (D + 2);
-  for (int d = tid; d < D; d += blockDim.x) {
-    float M = ntail > 0 ? tail_m : -__builtin_inff();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, base[(int64_t)s * (D + 2)]);
-    float Lsum = 0.0f, O = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float* pp = base + (int64_t)s * (D + 2);
-      if (pp[0] == -__builtin_inff()) continue;  // empty split
-      const float w = exp2f(pp[0] - M);
-      Lsum = __builtin_fmaf(pp[1], w, Lsum);
-      O = __builtin_fmaf(pp[2 + d], w, O);
-    }
+  float mloc = ntail > 0 ? tail_m : -__builtin_inff();
+  for (int sp = tid; sp < S; sp += blockDim.x) mloc = fmaxf(mloc, base[(int64_t)sp * (D + 2)]);
+  mloc = wave_max(mloc);
+  if ((tid & 63) == 0) red2[tid >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red2[0], red2[1]), fmaxf(red2[2], red2[3]));
+  float lloc = 0.0f;
+  for (int sp = tid; sp < S; sp += blockDim.x) {
+    const float* pp = base + (int64_t)sp * (D + 2);
+    const float w = pp[0] == -__builtin_inff() ? 0.0f : exp2f(pp[0] - M);  // empty split: 0
+    wsh[sp] = w;
+    lloc = __builtin_fmaf(pp[1], w, lloc);
+  }
+  lloc = wave_sum(lloc);
+  __syncthreads();
+  if ((tid & 63) == 0) red2[4 + (tid >> 6)] = lloc;
+  __syncthreads();
+  float Lsum = (red2[4] + red2[5]) + (red2[6] + red2[7]);
+  const float wt = ntail > 0 ? exp2f(tail_m - M) : 0.0f;
+  if (ntail > 0) Lsum = __builtin_fmaf(tail_l, wt, Lsum);
+  const int d = tid % D, part = tid / D, nparts = blockDim.x / D;
+  const int s0 = S * part / nparts, s1 = S * (part + 1) / nparts;
+  float O = 0.0f;
+  for (int sp = s0; sp < s1; ++sp) O = __builtin_fmaf(base[(int64_t)sp * (D + 2) + 2 + d], wsh[sp], O);
+  osh[tid] = O;
+  __syncthreads();
+  if (part == 0) {
+    for (int pt = 1; pt < nparts; ++pt) O += osh[pt * D + d];
     if (ntail > 0) {
-      const float w = exp2f(tail_m - M);
       float ot = 0.0f;
       const uint16_t* vt = c.v_tail + bh * Bk * D + d;
       for (int j = 0; j < ntail; ++j) ot = __builtin_fmaf(p_s[j], h2f(vt[(int64_t)j * D]), ot);
-      Lsum = __builtin_fmaf(tail_l, w, Lsum);
-      O = __builtin_fmaf(ot, w, O);
+      O = __builtin_fmaf(ot, wt, O);
     }
     out[bq * D + d] = O / Lsum;
   }

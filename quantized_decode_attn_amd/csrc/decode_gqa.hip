@@ -21,9 +21,10 @@
 //  * scores of all heads, reduced across a token's lanes by a DPP reduce-scatter
 //    over the heads, written to LDS;
 //  * outliers ([KVC3] "Per-Vector Dense-and-Sparse Quantization"): code 0 was stored
-//    at an outlier's position; per block, each CSR entry's exact score correction is
-//    added into the score array with LDS atomics, and each value correction
-//    p * (x - zero) is scattered into a per-head channel array the same way;
+//    at an outlier's position; the lanes that own a token in the softmax (two tokens
+//    per lane) add each of its CSR entries' exact score terms in registers, and
+//    scatter its value corrections p * (x - zero) into a per-head channel array with
+//    LDS atomics;
 //  * online softmax per head over the block (lanes own two tokens each), value
 //    weights p*scale quantized per head to 16-bit fixed point, nibble planes, and
 //    v_dot8_u32_u4 on the packed value words as in the one-head kernel.
@@ -42,16 +43,15 @@ typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 // Per-wave LDS area, in floats.
 struct GLds {
-  int wts, s, vz, vcorr, total;
+  int wts, s, vcorr, total;
 };
 __host__ __device__ inline GLds gqa_lds(int D, int BK, int GW, int ng, bool outl) {
   GLds m;
   int o = 0;
-  const int wts = (4 + 2 * GW) * (D / 2);            // ALPHA BETA ZA ZB WR[g] WIN[g]
+  const int wts = (4 + 2 * GW) * (D / 2);            // ALPHA BETA ZA ZB, then per pair WR[g] WIN[g]
   const int vq = GW * ng * BK / 2 + GW * ng * 64;     // u16 weights + nibble planes (reuse)
   m.wts = o; o += wts > vq ? wts : vq;
   m.s = o; o += BK * GW;                              // scores, then probabilities [BK][GW]
-  m.vz = o; o += outl ? ng * BK : 0;                  // value zero per [group][token]
   m.vcorr = o; o += outl ? GW * D : 0;                // value outlier corrections [GW][D]
   m.total = o;
   return m;
@@ -67,6 +67,40 @@ __device__ __forceinline__ float add_dpp_hm(float v, float x) {
   return v;
 }
 
+// Outlier CSR entries (two per token) of the lane's tokens lane and lane + 64 of a
+// block: both columns of a token in one u16, both values in one u32.
+struct CsrTok {
+  uint32_t kc[2], kv[2], vc[2], vv[2];
+};
+template <int BK>
+__device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
+  const int64_t e0 = (bh * c.cfg.capacity + n * BK) * 2;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = lane + 64 * k;
+    C.kc[k] = *reinterpret_cast<const uint16_t*>(c.k_col + e0 + 2 * t);
+    C.vc[k] = *reinterpret_cast<const uint16_t*>(c.v_col + e0 + 2 * t);
+    C.kv[k] = *reinterpret_cast<const uint32_t*>(c.k_val + e0 + 2 * t);
+    C.vv[k] = *reinterpret_cast<const uint32_t*>(c.v_val + e0 + 2 * t);
+  }
+}
+
+// Adds the per-head value-outlier corrections accumulated in LDS to the lane's
+// channels and clears them.
+template <int D, int GW>
+__device__ __forceinline__ void merge_vcorr(float* VCR, float (&acc)[GW][4], int lane) {
+  constexpr int CHL = D / 4;
+  if (lane < CHL) {
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      float4* pc = reinterpret_cast<float4*>(VCR + g * D + 4 * lane);
+      const float4 v = *pc;
+      acc[g][0] += v.x; acc[g][1] += v.y; acc[g][2] += v.z; acc[g][3] += v.w;
+      *pc = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
 template <int GW>
 struct GState {
   float m[GW], lpart[GW], acc[GW][4], zpart[GW][2];
@@ -78,7 +112,7 @@ template <int D, int BK, int KB, int VB>
 using GRegs = BlockRegs<D, BK, KB, VB, GShape<D, BK, KB, VB>::NIT / 2, 4>;
 
 template <int D, int BK, int KB, int VB, int GW, int KO>
-__device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& st, float* __restrict__ wl,
+__device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, CsrTok& C, GState<GW>& st, float* __restrict__ wl,
                                           const GLds& L, const float* __restrict__ table, const float (&wq_r)[GW],
                                           const float (&wq_i)[GW], float unit, float inv_unit, int lane, int ts, int r, int G,
                                           int ng, const kvq_cache& c, int64_t bh, int64_t n, bool more,
@@ -94,10 +128,8 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
   float* wBE = wAL + HALF;
   float* wZA = wBE + HALF;
   float* wZB = wZA + HALF;
-  float* wWR = wZB + HALF;        // [GW][HALF]
-  float* wWI = wWR + GW * HALF;   // [GW][HALF], negated imaginary parts
+  float* wWP = wZB + HALF;        // [HALF][2 GW]: WR[g] then -WI[g] of each pair
   float* Sc = wl + L.s;           // [BK][GW]
-  float* VZl = wl + L.vz;
   float* VCR = wl + L.vcorr;
 
   // ---- per-pair dequantization constants and block-rotated query weights
@@ -110,8 +142,8 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
     wZB[lane] = h2f(R.kmeta[3]) * unit;
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
-      wWR[g * HALF + lane] = (wq_r[g] * R.eb_c - wq_i[g] * R.eb_s) * inv_unit;
-      wWI[g * HALF + lane] = -(wq_r[g] * R.eb_s + wq_i[g] * R.eb_c) * inv_unit;
+      wWP[lane * 2 * GW + g] = (wq_r[g] * R.eb_c - wq_i[g] * R.eb_s) * inv_unit;
+      wWP[lane * 2 * GW + GW + g] = -(wq_r[g] * R.eb_s + wq_i[g] * R.eb_c) * inv_unit;
     }
   }
   load_kmeta(R, c, bh, nn, lane, 0);
@@ -132,9 +164,19 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
   ld4(wZA, ZA);
   ld4(wZB, ZB);
 #pragma unroll
-  for (int g = 0; g < GW; ++g) {
-    ld4(wWR + g * HALF, WR[g]);
-    ld4(wWI + g * HALF, WI[g]);
+  for (int m = 0; m < 4; ++m) {
+    const float* wp = wWP + (4 * r + m) * 2 * GW;
+#pragma unroll
+    for (int g4 = 0; g4 < 2 * GW; g4 += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(wp + g4);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int gg = g4 + u;
+        if (gg < GW) WR[gg][m] = xv[u];
+        else WI[gg - GW][m] = xv[u];
+      }
+    }
   }
 
   // ---- scores of all heads: 16 lanes per token, 4 pairs per lane; the per-head lane
@@ -145,15 +187,18 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
   const bool lowhalf = (r & 8) == 0, lowq = (r & 4) == 0;
   // two halves of KS iterations: slot `sl` holds iteration sl of the half; in the first
   // half it is refilled with iteration KS + sl of this block, in the second with
-  // iteration sl of the next block
-#pragma unroll 1
-  for (int hb = 0; hb < 2; ++hb) {
-  const uint8_t* kref = hb ? knext : kcur + KS * (Sh::TPI * Sh::RK);
+  // iteration sl of the next block (fully unrolled, so that every wait for a slot's
+  // load is an exact count of the loads issued after it)
+  constexpr int LPH = 16 / GW;  // lanes per head after the reduce-scatter
+  // per-lane bases; every iteration adds a compile-time offset (folded into the LDS
+  // instructions' offset field)
+  const float* tab0 = table + ts * Sh::TPITCH + 8 * r;
+  float* sc0 = Sc + ts * GW + r / LPH;
 #pragma unroll
-  for (int sl = 0; sl < KS; ++sl) {
-    const int it = hb * KS + sl;
-    const int j = it * Sh::TPI + ts;
-    const float* tab = table + j * Sh::TPITCH + 8 * r;
+  for (int it = 0; it < Sh::NIT; ++it) {
+    const int hb = it / KS, sl = it % KS;
+    const uint8_t* kref = hb ? knext : kcur + KS * (Sh::TPI * Sh::RK);
+    const float* tab = tab0 + it * (Sh::TPI * Sh::TPITCH);
     const uint32_t w = R.k[sl][0];
     load_k_slot(R, sl, sl, kref, koff);
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
@@ -190,38 +235,10 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
       v = add_dpp_rm(lowhalf ? s[0] : s[1], lowhalf ? s[1] : s[0]);
       v = lanes_sum<8>(v);
     }
-    constexpr int LPH = 16 / GW;  // lanes per head after the reduce-scatter
-    if (r % LPH == 0) Sc[j * GW + r / LPH] = v;
-  }
+    if (r % LPH == 0) sc0[it * (Sh::TPI * GW)] = v;
+    // (iterations are left to the scheduler)
   }
   wave_lds_sync();
-
-  // ---- key outliers: exact correction of each CSR entry's score term (entries
-  // 4*lane .. 4*lane+3 of the block, held in registers)
-  if constexpr (OUTL) {
-    const int ne = BK * ko;
-    const uint32_t vals[2] = {R.kval.x, R.kval.y};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 4 * lane + q;
-      if (e < ne) {
-        const int jt = e / ko;
-        const int col = (int)((R.kcol >> (8 * q)) & 0xffu);
-        const float val = h2f((uint16_t)(vals[q >> 1] >> (16 * (q & 1))));
-        const int i = col % HALF;
-        const bool a = col < HALF;
-        const float dl = val * unit - (a ? wZA[i] : wZB[i]);   // (x - zero) * u
-        const float2 cssn = *reinterpret_cast<const float2*>(table + jt * Sh::TPITCH + 2 * i);
-#pragma unroll
-        for (int g = 0; g < GW; ++g) {
-          const float wr = wWR[g * HALF + i], wi = -wWI[g * HALF + i];   // W / u
-          const float re = wr * cssn.x - wi * cssn.y, im = wr * cssn.y + wi * cssn.x;
-          atomicAdd(Sc + jt * GW + g, a ? dl * re : -dl * im);
-        }
-      }
-    }
-    wave_lds_sync();
-  }
 
   // ---- online softmax per head; lane owns tokens lane and lane + 64
   constexpr int TPL = BK / kWave;  // tokens per lane
@@ -239,9 +256,31 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
       const float2 v = *reinterpret_cast<const float2*>(Sc + t * 2);
       p[k][0] = v.x; p[k][1] = v.y;
     }
+    if constexpr (OUTL) {
+      // key outliers of token t: code 0 (dequantized to the zero-point) was stored; add
+      // the exact term (x - zero) of each CSR entry, rotated, for every head
+      const uint32_t vals = C.kv[k];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int col = (int)((C.kc[k] >> (8 * q)) & 0xffu);
+        const float val = h2f((uint16_t)(vals >> (16 * q)));
+        const int i = col % HALF;
+        const bool a = col < HALF;
+        const float dl = val * unit - (a ? wZA[i] : wZB[i]);   // (x - zero) * u
+        const float2 cssn = *reinterpret_cast<const float2*>(table + t * Sh::TPITCH + 2 * i);
+        const float* wp = wWP + i * 2 * GW;
+#pragma unroll
+        for (int g = 0; g < GW; ++g) {
+          const float wr = wp[g], wi = -wp[GW + g];   // W / u
+          const float re = wr * cssn.x - wi * cssn.y, im = wr * cssn.y + wi * cssn.x;
+          p[k][g] += a ? dl * re : -dl * im;
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < GW; ++g) mloc[g] = fmaxf(mloc[g], p[k][g]);
   }
+  if constexpr (OUTL) merge_vcorr<D, GW>(VCR, st.acc, lane);  // the previous block's
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
     const float mnew = fmaxf(st.m[g], wave_max_uniform(mloc[g]));
@@ -259,18 +298,6 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
     st.zpart[g][0] *= alpha;
     st.zpart[g][1] *= alpha;
   }
-  if constexpr (OUTL) {
-#pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      const int t = lane + kWave * k;
-      if constexpr (GW == 4) {
-        *reinterpret_cast<float4*>(Sc + t * 4) = make_float4(p[k][0], p[k][1], p[k][2], p[k][3]);
-      } else {
-        *reinterpret_cast<float2*>(Sc + t * 2) = make_float2(p[k][0], p[k][1]);
-      }
-    }
-  }
-
   // ---- value weights w = p * scale per [head][group][token], 16-bit fixed point per
   // (head, group); the zero-point part p * zero is summed in fp32
   uint16_t* Wq16 = reinterpret_cast<uint16_t*>(wl + L.wts);                 // [GW][ng][BK]
@@ -280,15 +307,18 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
 #pragma unroll
   for (int g = 0; g < GW; ++g) wmax[g][0] = wmax[g][1] = 0.0f;
   float wv[4][GW];
+  float vzc[4];  // this block's value zero-points of elements lane + 64 k
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
+    vzc[k] = 0.0f;
 #pragma unroll
     for (int g = 0; g < GW; ++g) wv[k][g] = 0.0f;
     if (e < BK * ng) {
       const int grp = e / BK;
       const int kt = (e % BK) / kWave;  // which of the lane's tokens
       const float vs = h2f(R.vs[k]), vz = h2f(R.vz[k]);
+      vzc[k] = vz;
 #pragma unroll
       for (int g = 0; g < GW; ++g) {
         const float pp = p[kt][g];
@@ -301,7 +331,6 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
           wmax[g][1] = fmaxf(wmax[g][1], wv[k][g]);
         }
       }
-      if constexpr (OUTL) VZl[e] = vz;
     }
   }
   load_vmeta(R, c, bh, nn, lane, ng);
@@ -416,30 +445,21 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, GState<GW>& s
   }
   // ---- value outliers: p * (x - zero) scattered into the per-head channel array
   if constexpr (OUTL) {
-    const int ne = BK * ko;
-    const uint32_t vals[2] = {R.vval.x, R.vval.y};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 4 * lane + q;
-      if (e < ne) {
-        const int jt = e / ko;
-        const int col = (int)((R.vcol >> (8 * q)) & 0xffu);
-        const float dl = h2f((uint16_t)(vals[q >> 1] >> (16 * (q & 1)))) - VZl[(col / G) * BK + jt];
+    for (int k = 0; k < TPL; ++k) {
+      const uint32_t vals = C.vv[k];
 #pragma unroll
-        for (int g = 0; g < GW; ++g) atomicAdd(VCR + g * D + col, Sc[jt * GW + g] * dl);
+      for (int q = 0; q < 2; ++q) {
+        const int col = (int)((C.vc[k] >> (8 * q)) & 0xffu);
+        const int grp = col / G;
+        const float dl = h2f((uint16_t)(vals >> (16 * q))) - (grp ? vzc[2 + k] : vzc[k]);
+#pragma unroll
+        for (int g = 0; g < GW; ++g) atomicAdd(VCR + g * D + col, p[k][g] * dl);
       }
     }
-    load_csr(R, c, bh, nn, lane, ko);
-    wave_lds_sync();
-    if (lane < Sh::CHL) {
-#pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        float4* pc = reinterpret_cast<float4*>(VCR + g * D + ch0);
-        const float4 v = *pc;
-        st.acc[g][0] += v.x; st.acc[g][1] += v.y; st.acc[g][2] += v.z; st.acc[g][3] += v.w;
-        *pc = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
+    load_csr_tok<BK>(C, c, bh, nn, lane);
+    // merged into the accumulators at the next block's softmax (or the item's end), so
+    // that the atomics complete in the shadow of the next block's scores
   }
 #pragma unroll
   for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vnext, lane);
@@ -514,10 +534,11 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     }
 
     GRegs<D, BK, KB, VB> R;
+    CsrTok C;
     if (n0 < n1) {
       load_kmeta(R, c, bh, n0, lane, 0);
       load_vmeta(R, c, bh, n0, lane, ng);
-      if (OUTL) load_csr(R, c, bh, n0, lane, KO);
+      if (OUTL) load_csr_tok<BK>(C, c, bh, n0, lane);
       const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
       const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
 #pragma unroll
@@ -526,9 +547,14 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
       for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
     }
     for (int64_t n = n0; n < n1; ++n)
-      gqa_block<D, BK, KB, VB, GW, KO>(R, st, wl, L, table, wq_r, wq_i, unit, inv_unit, lane, ts, r, G, ng, c, bh,
+      gqa_block<D, BK, KB, VB, GW, KO>(R, C, st, wl, L, table, wq_r, wq_i, unit, inv_unit, lane, ts, r, G, ng, c, bh,
                                          n, n + 1 < n1, koff);
 
+    if (OUTL) {
+      wave_lds_sync();
+      merge_vcorr<D, GW>(wl + L.vcorr, st.acc, lane);  // the item's last block
+      wave_lds_sync();
+    }
     // ---- finish the item: reduce across lanes and write (m, l, o) of each head's split
 #pragma unroll
     for (int g = 0; g < GW; ++g) {

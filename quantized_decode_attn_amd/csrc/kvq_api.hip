@@ -163,7 +163,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int64_t q
   if (q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
   const kvq_config& c = cache->cfg;
   const int S = num_splits ? num_splits : auto_splits(c);
-  if (S > (1 << 20)) return KVQ_EINVAL;
+  if (S > 4096) return KVQ_EINVAL;
   const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
   if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
   return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, (float*)ws, S,

@@ -119,6 +119,9 @@ def test_decode_and_dequantize_argument_errors(L):
     assert L.kvq_decode_attention(C.byref(c), 0x1000, -1, 0x1000, 0x1000, ws, 4, None) == kvq.KVQ_EINVAL
     assert L.kvq_decode_attention(C.byref(c), None, 99, 0x1000, 0x1000, ws, 4, None) == kvq.KVQ_EINVAL
     assert L.kvq_decode_attention(C.byref(c), 0x1000, 99, 0x1000, None, ws, 4, None) == kvq.KVQ_EWORKSPACE
+    big = L.kvq_decode_workspace_bytes(C.byref(c), 4097)
+    assert L.kvq_decode_attention(C.byref(c), 0x1000, 99, 0x1000, 0x1000, big, 4097, None) == kvq.KVQ_EINVAL
+    assert L.kvq_decode_attention(C.byref(c), 0x1000, 99, 0x1000, 0x1000, big, -2, None) == kvq.KVQ_EINVAL
     assert L.kvq_dequantize(C.byref(c), 2, 0, 10, 0x1000, None) == kvq.KVQ_EINVAL
     assert L.kvq_dequantize(C.byref(c), 0, 5, 4, 0x1000, None) == kvq.KVQ_EINVAL
     assert L.kvq_dequantize(C.byref(c), 0, 0, 101, 0x1000, None) == kvq.KVQ_EINVAL
