@@ -200,5 +200,45 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+
+// Outlier CSR entries (KO = 1 or 2 per token) of the lane's tokens lane + 64 k
+// (k < BK / 64) of a block: a token's columns in one u8/u16, its values in one u16/u32,
+// entry q at byte q (columns) and half-word q (values).
+struct CsrTok {
+  uint32_t kc[2], kv[2], vc[2], vv[2];
+};
+template <int BK, int KO>
+__device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
+  static_assert(KO == 1 || KO == 2, "one or two outliers per vector");
+  const int64_t e0 = (bh * c.cfg.capacity + n * BK) * KO;
+#pragma unroll
+  for (int k = 0; k < BK / kWave; ++k) {
+    const int t = lane + kWave * k;
+    if constexpr (KO == 2) {
+      C.kc[k] = *reinterpret_cast<const uint16_t*>(c.k_col + e0 + 2 * t);
+      C.vc[k] = *reinterpret_cast<const uint16_t*>(c.v_col + e0 + 2 * t);
+      C.kv[k] = *reinterpret_cast<const uint32_t*>(c.k_val + e0 + 2 * t);
+      C.vv[k] = *reinterpret_cast<const uint32_t*>(c.v_val + e0 + 2 * t);
+    } else {
+      C.kc[k] = c.k_col[e0 + t];
+      C.vc[k] = c.v_col[e0 + t];
+      C.kv[k] = c.k_val[e0 + t];
+      C.vv[k] = c.v_val[e0 + t];
+    }
+  }
+}
+
+// Adds one head's value-outlier corrections accumulated in LDS (D floats) to the lane's
+// channels 4*lane .. 4*lane+3 and clears them.
+template <int D>
+__device__ __forceinline__ void merge_vcorr(float* VCR, float (&acc)[4], int lane) {
+  if (lane < D / 4) {
+    float4* pc = reinterpret_cast<float4*>(VCR + 4 * lane);
+    const float4 v = *pc;
+    acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    *pc = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 }  // namespace dcm
 }  // namespace kvq

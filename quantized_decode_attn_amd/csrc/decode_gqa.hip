@@ -67,40 +67,6 @@ __device__ __forceinline__ float add_dpp_hm(float v, float x) {
   return v;
 }
 
-// Outlier CSR entries (two per token) of the lane's tokens lane and lane + 64 of a
-// block: both columns of a token in one u16, both values in one u32.
-struct CsrTok {
-  uint32_t kc[2], kv[2], vc[2], vv[2];
-};
-template <int BK>
-__device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
-  const int64_t e0 = (bh * c.cfg.capacity + n * BK) * 2;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int t = lane + 64 * k;
-    C.kc[k] = *reinterpret_cast<const uint16_t*>(c.k_col + e0 + 2 * t);
-    C.vc[k] = *reinterpret_cast<const uint16_t*>(c.v_col + e0 + 2 * t);
-    C.kv[k] = *reinterpret_cast<const uint32_t*>(c.k_val + e0 + 2 * t);
-    C.vv[k] = *reinterpret_cast<const uint32_t*>(c.v_val + e0 + 2 * t);
-  }
-}
-
-// Adds the per-head value-outlier corrections accumulated in LDS to the lane's
-// channels and clears them.
-template <int D, int GW>
-__device__ __forceinline__ void merge_vcorr(float* VCR, float (&acc)[GW][4], int lane) {
-  constexpr int CHL = D / 4;
-  if (lane < CHL) {
-#pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      float4* pc = reinterpret_cast<float4*>(VCR + g * D + 4 * lane);
-      const float4 v = *pc;
-      acc[g][0] += v.x; acc[g][1] += v.y; acc[g][2] += v.z; acc[g][3] += v.w;
-      *pc = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-}
-
 template <int GW>
 struct GState {
   float m[GW], lpart[GW], acc[GW][4], zpart[GW][2];
@@ -280,7 +246,9 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, CsrTok& C, GS
 #pragma unroll
     for (int g = 0; g < GW; ++g) mloc[g] = fmaxf(mloc[g], p[k][g]);
   }
-  if constexpr (OUTL) merge_vcorr<D, GW>(VCR, st.acc, lane);  // the previous block's
+  if constexpr (OUTL)  // the previous block's
+#pragma unroll
+    for (int g = 0; g < GW; ++g) merge_vcorr<D>(VCR + g * D, st.acc[g], lane);
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
     const float mnew = fmaxf(st.m[g], wave_max_uniform(mloc[g]));
@@ -457,7 +425,7 @@ __device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, CsrTok& C, GS
         for (int g = 0; g < GW; ++g) atomicAdd(VCR + g * D + col, p[k][g] * dl);
       }
     }
-    load_csr_tok<BK>(C, c, bh, nn, lane);
+    load_csr_tok<BK, KO>(C, c, bh, nn, lane);
     // merged into the accumulators at the next block's softmax (or the item's end), so
     // that the atomics complete in the shadow of the next block's scores
   }
@@ -538,7 +506,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     if (n0 < n1) {
       load_kmeta(R, c, bh, n0, lane, 0);
       load_vmeta(R, c, bh, n0, lane, ng);
-      if (OUTL) load_csr_tok<BK>(C, c, bh, n0, lane);
+      if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n0, lane);
       const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
       const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
 #pragma unroll
@@ -552,7 +520,8 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
 
     if (OUTL) {
       wave_lds_sync();
-      merge_vcorr<D, GW>(wl + L.vcorr, st.acc, lane);  // the item's last block
+#pragma unroll
+      for (int g = 0; g < GW; ++g) merge_vcorr<D>(wl + L.vcorr + g * D, st.acc[g], lane);  // the item's last block
       wave_lds_sync();
     }
     // ---- finish the item: reduce across lanes and write (m, l, o) of each head's split

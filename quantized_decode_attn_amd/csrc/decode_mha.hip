@@ -34,43 +34,39 @@ namespace {
 
 using namespace dcm;
 
-// Waves per workgroup: 8 (two per SIMD) when the kernel fits 256 registers, else 4.
-template <bool OUTL>
-constexpr int waves_for() { return OUTL ? 4 : 8; }
+constexpr int kMhaWaves = 8;  // two waves per SIMD
 
 // Per-wave LDS area, in floats.
 struct MLds {
-  int wts, p, ps, vz, vc, csr, total;
+  int wts, s, ps, vcorr, total;
 };
-__host__ __device__ inline MLds mha_lds(int D, int BK, int ko, int tpi) {
+__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl) {
   MLds m;
   int o = 0;
-  m.wts = o; o += 10 * (D / 2);     // A1 B1 Z1 A2 B2 Z2 WR WI ZA ZB, one array per name
-  m.p = o; o += BK;
-  m.ps = o; o += 2 * BK + 128;      // quantized weights [2][BK] (u16) + nibble planes [2][64]
-  m.vz = o; o += ko ? 2 * BK : 0;
-  m.vc = o; o += ko ? tpi * D : 0;
-  m.csr = o; o += ko ? (BK * ko * 6 + 3) / 4 : 0;   // k cols, v cols (u8), k vals, v vals (u16)
+  m.wts = o; o += (outl ? 10 : 6) * (D / 2);  // A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB], one array per name
+  m.s = o; o += BK;                           // scores of the block's tokens
+  m.ps = o; o += BK + 128;                    // quantized weights [2][BK] (u16) + nibble planes [2][64]
+  m.vcorr = o; o += outl ? D : 0;             // value outlier corrections [D]
   m.total = o;
   return m;
 }
 
-template <int D, int BK, int KB, int VB>
 struct MState {
   float m, lpart, acc[4], zpart[2];
 };
 
-// Process one quantized block held in registers.
 // Process quantized block n held in R; every register slot is refilled right after
 // its last use with block n + 1, or with block n again when `more` is clear (the
 // loads stay unconditional, so no register has to survive them).
-template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MState<D, BK, KB, VB>& st,
+template <int D, int BK, int KB, int VB, int KO>
+__device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTok& C, MState& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               float wq_r, float wq_i, float inv_unit, int lane, int ts, int r,
-                                              int G, int ng, int ko, const kvq_cache& c, int64_t bh, int64_t n,
+                                              int G, int ng, const kvq_cache& c, int64_t bh, int64_t n,
                                               bool more, uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
+  constexpr bool OUTL = KO > 0;
+  constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
   const int64_t nn = more ? n + 1 : n;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
   const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, nn);
@@ -84,14 +80,9 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
   float* wWI = wWR + Sh::HALF;
   float* wZA = wWI + Sh::HALF;
   float* wZB = wZA + Sh::HALF;
-  float* Pl = wl + L.p;
+  float* Sc = wl + L.s;
   float* PS = wl + L.ps;
-  float* VZl = wl + L.vz;
-  float* VC = wl + L.vc;
-  uint8_t* CSK = reinterpret_cast<uint8_t*>(wl + L.csr);
-  uint8_t* CSV = CSK + BK * ko;
-  uint16_t* CVK = reinterpret_cast<uint16_t*>(CSK + 2 * BK * ko);
-  uint16_t* CVV = CVK + BK * ko;
+  float* VCR = wl + L.vcorr;
 
   // ---- block weights, one rotary pair per lane
   if (lane < Sh::HALF) {
@@ -105,18 +96,14 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     wA2[lane] = -wi * al * inv_unit;
     wB2[lane] = -wr * be * inv_unit;
     wZ2[lane] = -(wi * za + wr * zb);
-    wWR[lane] = wr;
-    wWI[lane] = wi;
-    wZA[lane] = za;
-    wZB[lane] = zb;
+    if constexpr (OUTL) {
+      wWR[lane] = wr;
+      wWI[lane] = wi;
+      wZA[lane] = za;
+      wZB[lane] = zb;
+    }
   }
-  if (ko > 0 && lane * 4 < BK * ko) {
-    reinterpret_cast<uint32_t*>(CSK)[lane] = R.kcol;
-    reinterpret_cast<uint32_t*>(CSV)[lane] = R.vcol;
-    reinterpret_cast<uint2*>(CVK)[lane] = R.kval;
-    reinterpret_cast<uint2*>(CVV)[lane] = R.vval;
-  }
-  load_kmeta(R, c, bh, nn, lane, ko);
+  load_kmeta(R, c, bh, nn, lane, 0);
   wave_lds_sync();
   float A1[8], B1[8], Z1[8], A2[8], B2[8], Z2[8];
   {
@@ -138,21 +125,20 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     }
   }
 
-  // ---- scores
-  float sc[Sh::NIT];
-  float mloc = -__builtin_inff();
+  // ---- scores, summed over a token's lanes and written to LDS by its first lane
   // rotary-table rows in registers one iteration ahead, so the LDS latency of the
   // next token's cos/sin overlaps this token's arithmetic
   float4 tq[2][4];
+  const float* tab0 = table + ts * Sh::TPITCH + 16 * r;
   auto load_tab = [&](int it, float4(&t)[4]) {
-    const float* tab = table + (it * Sh::TPI + ts) * Sh::TPITCH + 16 * r;
+    const float* tab = tab0 + it * (Sh::TPI * Sh::TPITCH);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) t[q4] = *reinterpret_cast<const float4*>(tab + 4 * q4);
   };
+  float* sc0 = Sc + ts;
   load_tab(0, tq[0]);
 #pragma unroll
   for (int it = 0; it < Sh::NIT; ++it) {
-    const int j = it * Sh::TPI + ts;
     if (it + 1 < Sh::NIT) load_tab(it + 1, tq[(it + 1) & 1]);
     float ca[8], cb[8];
     unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
@@ -173,67 +159,78 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
         s = __builtin_fmaf(sn, Y, s);
       }
     }
-    if (ko > 0 && r < ko) {  // outlier: code 0 was stored, the CSR holds the exact value
-      const int e = j * ko + r;
-      const int col = CSK[e];
-      const float dlt0 = h2f(CVK[e]);
-      const int i = col % Sh::HALF;
-      const float cs = table[j * Sh::TPITCH + 2 * i], sn = table[j * Sh::TPITCH + 2 * i + 1];
-      const float wr = wWR[i], wi = wWI[i];
-      const bool a = col < Sh::HALF;
-      const float dlt = dlt0 - (a ? wZA[i] : wZB[i]);
-      s += a ? dlt * (wr * cs - wi * sn) : -dlt * (wi * cs + wr * sn);
-    }
     s = lanes_sum<Sh::LPT>(s);
-    sc[it] = s;
-    mloc = fmaxf(mloc, s);
+    if (r == 0) sc0[it * Sh::TPI] = s;
   }
-
-  // ---- online softmax in base 2
-  const float mblk = wave_max_uniform(mloc);
-  const float mnew = fmaxf(st.m, mblk);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
-  st.m = mnew;
-  float psum = 0.0f;
-  if (r == 0) {
-#pragma unroll
-    for (int it = 0; it < Sh::NIT; ++it) {
-      const float p = __builtin_amdgcn_exp2f(sc[it] - mnew);
-      psum += p;
-      Pl[it * Sh::TPI + ts] = p;
-    }
-  }
-  st.lpart = __builtin_fmaf(st.lpart, alpha, psum);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) st.acc[k] *= alpha;
-  st.zpart[0] *= alpha;
-  st.zpart[1] *= alpha;
   wave_lds_sync();
+
+  // ---- online softmax in base 2; lane owns tokens lane + 64 k
+  float p[TPL];
+  float mloc = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < TPL; ++k) {
+    const int t = lane + kWave * k;
+    p[k] = Sc[t];
+    if constexpr (OUTL) {
+      // key outliers of token t: code 0 (dequantized to the zero-point) was stored; add
+      // the exact term (x - zero) of each CSR entry, rotated
+#pragma unroll
+      for (int q = 0; q < KO; ++q) {
+        const int col = (int)((C.kc[k] >> (8 * q)) & 0xffu);
+        const float val = h2f((uint16_t)(C.kv[k] >> (16 * q)));
+        const int i = col % Sh::HALF;
+        const bool a = col < Sh::HALF;
+        const float dl = val - (a ? wZA[i] : wZB[i]);
+        const float2 cssn = *reinterpret_cast<const float2*>(table + t * Sh::TPITCH + 2 * i);
+        const float wr = wWR[i], wi = wWI[i];
+        p[k] += a ? dl * (wr * cssn.x - wi * cssn.y) : -dl * (wi * cssn.x + wr * cssn.y);
+      }
+    }
+    mloc = fmaxf(mloc, p[k]);
+  }
+  if constexpr (OUTL) merge_vcorr<D>(VCR, st.acc, lane);  // the previous block's
+  {
+    const float mnew = fmaxf(st.m, wave_max_uniform(mloc));
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+    st.m = mnew;
+    float psum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      p[k] = __builtin_amdgcn_exp2f(p[k] - mnew);
+      psum += p[k];
+    }
+    st.lpart = __builtin_fmaf(st.lpart, alpha, psum);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st.acc[k] *= alpha;
+    st.zpart[0] *= alpha;
+    st.zpart[1] *= alpha;
+  }
 
   // ---- value weights w_t = p_t * scale_t per [group][token], quantized per block to
   // 16-bit fixed point (relative to the block maximum) for the integer dot products;
-  // the zero-point part p_t * zero_t is summed in fp32
+  // the zero-point part p_t * zero_t is summed in fp32.  Element lane + 64 k is token
+  // (64 k) % BK + lane of group (64 k) / BK, so its probability is p[((64 k) % BK) / 64].
   uint16_t* Wq16 = reinterpret_cast<uint16_t*>(PS);                       // [2][BK]
   uint32_t* PLN = reinterpret_cast<uint32_t*>(PS) + BK;                     // [2][64] nibble planes
-  float wv[4];
+  float wv[4], vzc[4];
   float wmax0 = 0.0f, wmax1 = 0.0f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int e = lane + 64 * k;
+    const int grp = (kWave * k) / BK, kt = ((kWave * k) % BK) / kWave;
     wv[k] = 0.0f;
-    if (e < BK * ng) {
-      const int grp = e / BK, t = e % BK;
-      const float p = Pl[t];
-      wv[k] = p * h2f(R.vs[k]);
+    vzc[k] = 0.0f;
+    if (kWave * k < BK * ng) {
+      const float pp = p[kt];
+      wv[k] = pp * h2f(R.vs[k]);
       const float z = h2f(R.vz[k]);
+      vzc[k] = z;
       if (grp == 0) {
-        st.zpart[0] = __builtin_fmaf(p, z, st.zpart[0]);
+        st.zpart[0] = __builtin_fmaf(pp, z, st.zpart[0]);
         wmax0 = fmaxf(wmax0, wv[k]);
       } else {
-        st.zpart[1] = __builtin_fmaf(p, z, st.zpart[1]);
+        st.zpart[1] = __builtin_fmaf(pp, z, st.zpart[1]);
         wmax1 = fmaxf(wmax1, wv[k]);
       }
-      if (ko > 0) VZl[grp * BK + t] = z;
     }
   }
   load_vmeta(R, c, bh, nn, lane, ng);
@@ -245,8 +242,8 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
-    if (e < BK * ng) {
-      const float kq = e < BK ? kq0 : kq1;
+    if (kWave * k < BK * ng) {
+      const float kq = (kWave * k) / BK == 0 ? kq0 : kq1;
       Wq16[e] = (uint16_t)__builtin_rintf(wv[k] * kq);
     }
   }
@@ -320,8 +317,6 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vnext, lane);
   {
     const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / 65535.0f);
 #pragma unroll
@@ -331,42 +326,36 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, MStat
     }
   }
 
-  // ---- value outliers: VC rows are token slots, so no instruction updates an address twice
-  if (ko > 0) {
+  // ---- value outliers: p * (x - zero) scattered into the channel array, merged into
+  // the accumulators at the next block's softmax (or the item's end), so that the
+  // atomics complete in the shadow of the next block's scores
+  if constexpr (OUTL) {
 #pragma unroll
-    for (int it = 0; it < Sh::NIT; ++it) {
-      if (r < ko) {
-        const int t = it * Sh::TPI + ts;
-        const int e = t * ko + r;
-        const int col = CSV[e];
-        const float dlt = h2f(CVV[e]) - VZl[(col / G) * BK + t];
-        VC[ts * D + col] += Pl[t] * dlt;
+    for (int k = 0; k < TPL; ++k) {
+#pragma unroll
+      for (int q = 0; q < KO; ++q) {
+        const int col = (int)((C.vc[k] >> (8 * q)) & 0xffu);
+        const float dl = h2f((uint16_t)(C.vv[k] >> (16 * q))) - (col >= G ? vzc[TPL + k] : vzc[k]);
+        atomicAdd(VCR + col, p[k] * dl);
       }
     }
-    wave_lds_sync();
-    if (lane < Sh::CHL) {
-#pragma unroll
-      for (int row = 0; row < Sh::TPI; ++row) {
-        float4* p = reinterpret_cast<float4*>(VC + row * D + ch0);
-        const float4 v = *p;
-        st.acc[0] += v.x; st.acc[1] += v.y; st.acc[2] += v.z; st.acc[3] += v.w;
-        *p = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
+    load_csr_tok<BK, KO>(C, c, bh, nn, lane);
   }
+#pragma unroll
+  for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vnext, lane);
   wave_lds_sync();
 }
 
-template <int D, int BK, int KB, int VB, bool OUTL>
-__global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
-                                                              int64_t q_pos, float* __restrict__ ws, int S,
-                                                              int64_t nitems) {
+template <int D, int BK, int KB, int VB, int KO>
+__global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+                                                                   int64_t q_pos, float* __restrict__ ws, int S,
+                                                                   int64_t nitems) {
   using Sh = MShape<D, BK, KB, VB>;
-  constexpr int kNW = waves_for<OUTL>(), kNT = kNW * 64;
+  constexpr int kNT = kMhaWaves * 64;
+  constexpr bool OUTL = KO > 0;
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads;
   const int G = c.cfg.v_group, ng = D / G;
-  const int ko = OUTL ? kout_of(c.cfg) : 0;
   const int64_t nfull = c.length / BK;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -378,15 +367,15 @@ __global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_
     const int j = idx / Sh::HALF, i = idx % Sh::HALF;
     *reinterpret_cast<float2*>(table + j * Sh::TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
   }
-  const MLds L = mha_lds(D, BK, ko, Sh::TPI);
+  const MLds L = mha_lds(D, BK, OUTL);
   float* wl = lds + BK * Sh::TPITCH + wave * L.total;
-  if (ko > 0)
-    for (int k = lane; k < Sh::TPI * D; k += kWave) wl[L.vc + k] = 0.0f;
+  if (OUTL)
+    for (int k = lane; k < D; k += kWave) wl[L.vcorr + k] = 0.0f;
   __syncthreads();
 
   const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
-  const int64_t total_waves = (int64_t)gridDim.x * kNW;
-  for (int64_t item = (int64_t)blockIdx.x * kNW + wave; item < nitems; item += total_waves) {
+  const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
+  for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves) {
     const int split = (int)(item % S);
     const int64_t bh = item / S;
     const int h = (int)(bh % H);
@@ -405,16 +394,18 @@ __global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_
       wq_r = (float)(scl * (qa * cs - qb * sn));
       wq_i = (float)(-scl * (qa * sn + qb * cs));
     }
-    MState<D, BK, KB, VB> st;
+    MState st;
     st.m = -__builtin_inff();
     st.lpart = 0.0f;
     st.acc[0] = st.acc[1] = st.acc[2] = st.acc[3] = 0.0f;
     st.zpart[0] = st.zpart[1] = 0.0f;
 
     BlockRegs<D, BK, KB, VB> R;
+    CsrTok C;
     if (n0 < n1) {
-      load_kmeta(R, c, bh, n0, lane, ko);
+      load_kmeta(R, c, bh, n0, lane, 0);
       load_vmeta(R, c, bh, n0, lane, ng);
+      if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n0, lane);
       const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
       const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
 #pragma unroll
@@ -423,7 +414,13 @@ __global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_
       for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
     }
     for (int64_t n = n0; n < n1; ++n)
-      process_block(R, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, ko, c, bh, n, n + 1 < n1, koff);
+      process_block<D, BK, KB, VB, KO>(R, C, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, c, bh, n,
+                                       n + 1 < n1, koff);
+    if (OUTL) {
+      wave_lds_sync();
+      merge_vcorr<D>(wl + L.vcorr, st.acc, lane);  // the item's last block
+      wave_lds_sync();
+    }
 
     // ---- finish the item: reduce across lanes and write (m, l, o) of this split
     const float l = wave_sum(st.lpart);
@@ -452,23 +449,21 @@ __global__ __launch_bounds__(waves_for<OUTL>() * 64) void decode_mha_kernel(kvq_
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus);
 
-template <int D, int BK, int KB, int VB, bool OUTL>
+template <int D, int BK, int KB, int VB, int KO>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                    hipStream_t s, int cus) {
   using Sh = MShape<D, BK, KB, VB>;
-  constexpr int kNW = waves_for<OUTL>();
-  const int ko = host_kout(c.cfg);
-  const MLds L = mha_lds(D, BK, ko, Sh::TPI);
-  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kNW * L.total) * sizeof(float);
+  const MLds L = mha_lds(D, BK, KO > 0);
+  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, OUTL>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
-  int64_t grid = (nitems + kNW - 1) / kNW;
+  int64_t grid = (nitems + kMhaWaves - 1) / kMhaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, OUTL>), dim3((unsigned)grid), dim3(kNW * 64), bytes, s, c, q,
-                     q_pos, ws, S, nitems);
+  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
+                     q, q_pos, ws, S, nitems);
   return hipGetLastError();
 }
 
@@ -482,9 +477,11 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
     return hipErrorNotSupported;
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
 #define KVQ_MHA(d, bk, kb, vb)                                                                  \
-  if (D == d && BK == bk && KB == kb && VB == vb)                                               \
-    return ko ? launch_mha_typed<d, bk, kb, vb, true>(c, q, q_pos, ws, S, s, cus)               \
-              : launch_mha_typed<d, bk, kb, vb, false>(c, q, q_pos, ws, S, s, cus);
+  if (D == d && BK == bk && KB == kb && VB == vb) {                                             \
+    if (ko == 2) return launch_mha_typed<d, bk, kb, vb, 2>(c, q, q_pos, ws, S, s, cus);         \
+    if (ko == 1) return launch_mha_typed<d, bk, kb, vb, 1>(c, q, q_pos, ws, S, s, cus);         \
+    return launch_mha_typed<d, bk, kb, vb, 0>(c, q, q_pos, ws, S, s, cus);                      \
+  }
   KVQ_MHA(128, 128, 4, 4) KVQ_MHA(128, 128, 4, 2) KVQ_MHA(128, 128, 2, 4) KVQ_MHA(128, 128, 2, 2)
   KVQ_MHA(128, 64, 4, 4) KVQ_MHA(128, 64, 4, 2) KVQ_MHA(128, 64, 2, 4) KVQ_MHA(128, 64, 2, 2)
   KVQ_MHA(64, 128, 4, 4) KVQ_MHA(64, 128, 4, 2) KVQ_MHA(64, 128, 2, 4) KVQ_MHA(64, 128, 2, 2)
