@@ -18,7 +18,7 @@ struct MShape {
   static constexpr int LPT = HALF / PPL;         // lanes per key token
   static constexpr int TPI = kWave / LPT;        // key tokens per iteration
   static constexpr int NIT = BK / TPI;           // iterations per block
-  static constexpr int KW = 2 * PPL * KB / 32;   // code dwords per lane per token
+  static constexpr int KW = (2 * PPL * KB + 31) / 32;  // code dwords per lane per token (3-bit: 48 bits in 2)
   static constexpr int RK = D * KB / 8;          // key row bytes
   static constexpr int TPW = 32 / VB;            // tokens per value word
   static constexpr int WPB = (BK / TPW) * D;     // value words per block

@@ -1,28 +1,35 @@
-// decode_mha.hip -- decode attention over uniform 2/4-bit key and value caches with one
-// query head per kv head (multi-head attention), tuned for gfx950.
+// decode_mha.hip -- decode attention over 2/3/4-bit key and 2/4-bit value caches with
+// one query head per kv head (multi-head attention), tuned for gfx950.
 //
 // Pages cited (title, address):
 //   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
 //   [TQ]   "TurboQuant：突破大模型推理瓶颈的KVCache量化技术解析", mlqm.cn/news/1002276
 //
-// Same arithmetic as the generic decode kernel (score of token n*Bk+j is
-// sum_i Re(W_n,i e^{i f_i j} k_i) with W folded with the block's per-channel scale and
-// zero-point, [KVC3] "Per-Channel Key Quantization" and "Pre-RoPE Key Quantization"),
-// organised for bandwidth:
+// Same arithmetic as the generic decode kernel: the score of token n*Bk+j is
+// sum_i Re(W_n,i e^{i f_i j} (k_a + i k_b)_i) over the rotary pairs i, with W_n,i the
+// query weight rotated by the block's first position ([KVC3] "Pre-RoPE Key
+// Quantization").  Uniform keys ([KVC3] "Per-Channel Key Quantization") fold the
+// block's scale and zero-point into W, six FMAs per pair; codebook keys ([KVC3]
+// "Non-Uniform KV Cache Quantization") read (k_a, k_b) of a pair from an LDS table
+// indexed by the pair's two codes, built once per kv head and shared by the
+// workgroup.  Organised for bandwidth:
 //  * 8-wave workgroups share one LDS copy of the cos/sin(j f_i) table;
 //  * every wave owns whole (b, head, split) items and streams their blocks through
 //    one set of registers: each register slot (codes of one token slot, one 16-byte
 //    value load, the metadata) is refilled with block n+1 right after its last use
 //    in block n, so a whole block of loads stays in flight;
 //  * a key token is covered by 8 lanes (4 for head_dim 64), 8 rotary pairs each,
-//    8-byte coalesced loads; codes become floats two at a time with the packed fp8
-//    conversion (a byte 0..15 is an exact fp8 value proportional to it);
+//    coalesced 4- or 8-byte loads; uniform codes become floats two at a time with the
+//    packed fp8 conversion (a byte 0..15 is an exact fp8 value proportional to it);
+//  * scores go to LDS; each lane then owns two tokens (one for 64-token blocks) for
+//    the softmax, the outlier corrections ([KVC3] "Per-Vector Dense-and-Sparse
+//    Quantization": code 0 is stored at an outlier, the exact value sits in the CSR)
+//    and the value weights;
 //  * values are stored as words of consecutive tokens of one channel, so a 16-byte
 //    load gives each lane 4 channels x (32 / v_bits) tokens; the per-token weights
 //    p*scale are quantized per block to 16-bit fixed point and split into four
 //    nibble planes, and the value update is v_dot8_u32_u4 on the packed codes
-//    (no unpacking, 8 codes per instruction and plane);
-//  * block weights are computed once per rotary pair and shared through LDS.
+//    (no unpacking, 8 codes per instruction and plane).
 // The pages' fusion advice ([TQ] sections 5.1 and 6.3) is the design: no dequantized
 // value is ever written to memory.
 #include <math.h>
@@ -40,10 +47,11 @@ constexpr int kMhaWaves = 8;  // two waves per SIMD
 struct MLds {
   int wts, s, ps, vcorr, total;
 };
-__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl) {
+__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut) {
   MLds m;
   int o = 0;
-  m.wts = o; o += (outl ? 10 : 6) * (D / 2);  // A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB], one array per name
+  // uniform keys: A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB]; codebook keys: WR WI; one array per name
+  m.wts = o; o += (lut ? 2 : outl ? 10 : 6) * (D / 2);
   m.s = o; o += BK;                           // scores of the block's tokens
   m.ps = o; o += BK + 128;                    // quantized weights [2][BK] (u16) + nibble planes [2][64]
   m.vcorr = o; o += outl ? D : 0;             // value outlier corrections [D]
@@ -55,17 +63,57 @@ struct MState {
   float m, lpart, acc[4], zpart[2];
 };
 
+// Codebook keys: the table entry of rotary pair i and pair code pc = c_a | c_b << KB
+// (the two codes as they sit side by side in the row) holds the fp16 codebook values
+// (k_a, k_b) in its low and high halves; rows of NPC + 1 entries spread the banks.
+template <int KB>
+struct PairTab {
+  static constexpr int NPC = 1 << (2 * KB);
+  static constexpr int PITCH = NPC + 1;
+};
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef u32x2 u32x2_a4 __attribute__((aligned(4)));
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
 // Process quantized block n held in R; every register slot is refilled right after
 // its last use with block n + 1, or with block n again when `more` is clear (the
 // loads stay unconditional, so no register has to survive them).
-template <int D, int BK, int KB, int VB, int KO>
+// Key codes of iteration `it` of a block.  3-bit rows give a lane 48 bits at byte
+// 6 r: the 8 bytes from the dword boundary below are loaded (dword alignment suffices
+// for the load) and shifted into place at use.
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_codes(BlockRegs<D, BK, KB, VB>& R, int it, const uint8_t* kblk, uint32_t koff) {
+  using Sh = MShape<D, BK, KB, VB>;
+  if constexpr (KB == 3) {
+    const u32x2 x = *reinterpret_cast<const u32x2_a4*>(kblk + koff + it * (Sh::TPI * Sh::RK));
+    R.k[it][0] = x.x;
+    R.k[it][1] = x.y;
+  } else {
+    load_k(R, it, kblk, koff);
+  }
+}
+
+// Block rotation cos/sin(n Bk f_i) of pair `lane` (codebook keys have no block metadata).
+template <int D, int BK, int KB, int VB>
+__device__ __forceinline__ void load_eb(BlockRegs<D, BK, KB, VB>& R, const kvq_cache& c, int64_t n, int lane) {
+  if (lane < D / 2) {
+    const float2 eb = reinterpret_cast<const float2*>(c.rope + (int64_t)BK * D + n * D)[lane];
+    R.eb_c = eb.x;
+    R.eb_s = eb.y;
+  }
+}
+
+template <int D, int BK, int KB, int VB, int KO, bool LUT>
 __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTok& C, MState& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
-                                              float wq_r, float wq_i, float inv_unit, int lane, int ts, int r,
-                                              int G, int ng, const kvq_cache& c, int64_t bh, int64_t n,
-                                              bool more, uint32_t koff) {
+                                              const uint32_t* __restrict__ ptab, float wq_r, float wq_i,
+                                              float inv_unit, int lane, int ts, int r, uint32_t sh, int G, int ng,
+                                              const kvq_cache& c, int64_t bh, int64_t n, bool more,
+                                              uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
   constexpr bool OUTL = KO > 0;
+  static_assert(!(LUT && OUTL), "codebook keys with outliers take the generic kernel");
   constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
   const int64_t nn = more ? n + 1 : n;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
@@ -85,7 +133,11 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   float* VCR = wl + L.vcorr;
 
   // ---- block weights, one rotary pair per lane
-  if (lane < Sh::HALF) {
+  if (LUT && lane < Sh::HALF) {
+    wA1[lane] = wq_r * R.eb_c - wq_i * R.eb_s;   // WR
+    wB1[lane] = wq_r * R.eb_s + wq_i * R.eb_c;   // WI
+  }
+  if (!LUT && lane < Sh::HALF) {
     const float wr = wq_r * R.eb_c - wq_i * R.eb_s;
     const float wi = wq_r * R.eb_s + wq_i * R.eb_c;
     const float al = h2f(R.kmeta[0]), be = h2f(R.kmeta[1]);
@@ -103,10 +155,20 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
       wZB[lane] = zb;
     }
   }
-  load_kmeta(R, c, bh, nn, lane, 0);
+  if constexpr (LUT) load_eb(R, c, nn, lane);
+  else load_kmeta(R, c, bh, nn, lane, 0);
   wave_lds_sync();
   float A1[8], B1[8], Z1[8], A2[8], B2[8], Z2[8];
-  {
+  if constexpr (LUT) {
+    const int p0 = r * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 a1 = *reinterpret_cast<const float4*>(wA1 + p0 + 4 * h);
+      const float4 b1 = *reinterpret_cast<const float4*>(wB1 + p0 + 4 * h);
+      A1[4 * h] = a1.x; A1[4 * h + 1] = a1.y; A1[4 * h + 2] = a1.z; A1[4 * h + 3] = a1.w;
+      B1[4 * h] = b1.x; B1[4 * h + 1] = b1.y; B1[4 * h + 2] = b1.z; B1[4 * h + 3] = b1.w;
+    }
+  } else {
     const int p0 = r * 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -140,23 +202,69 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 #pragma unroll
   for (int it = 0; it < Sh::NIT; ++it) {
     if (it + 1 < Sh::NIT) load_tab(it + 1, tq[(it + 1) & 1]);
-    float ca[8], cb[8];
-    unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
-    load_k(R, it, knext, koff);
     float s = 0.0f;
+    if constexpr (LUT) {
+      const uint32_t pt_lds = (uint32_t)(uintptr_t)(const lds_u32*)ptab;
+      // pair codes of the lane's 8 pairs, then (k_a, k_b) from the table:
+      // X = Re(W k), Y = -Im(W k), score += cos * X + sin * Y
+      uint32_t pc[8];
+      if constexpr (KB == 3) {
+        const uint32_t lo = __builtin_amdgcn_alignbit(R.k[it][1], R.k[it][0], sh);
+        const uint32_t hi = R.k[it][1] >> sh;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 t = tq[it & 1][q4];
+        for (int m = 0; m < 5; ++m) pc[m] = __builtin_amdgcn_ubfe(lo, 6 * m, 6);
+        pc[5] = __builtin_amdgcn_alignbit(hi, lo, 30) & 63u;
+        pc[6] = __builtin_amdgcn_ubfe(hi, 4, 6);
+        pc[7] = __builtin_amdgcn_ubfe(hi, 10, 6);
+      } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int m = 2 * q4 + u;
-        const float cs = u ? t.z : t.x, sn = u ? t.w : t.y;
-        float X = __builtin_fmaf(A1[m], ca[m], Z1[m]);
-        X = __builtin_fmaf(B1[m], cb[m], X);
-        float Y = __builtin_fmaf(A2[m], ca[m], Z2[m]);
-        Y = __builtin_fmaf(B2[m], cb[m], Y);
-        s = __builtin_fmaf(cs, X, s);
-        s = __builtin_fmaf(sn, Y, s);
+        for (int m = 0; m < 8; ++m) pc[m] = __builtin_amdgcn_ubfe(R.k[it][0], 4 * m, 4);
+      }
+      load_codes(R, it, knext, koff);
+      // entry address = lane base + 4 pc (one shift-add; the pair's row is the
+      // instruction's constant offset); all eight lookups issue before their use
+      uint32_t kab[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t ea;
+        asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(ea) : "v"(pc[m]), "v"(pt_lds));
+        kab[m] = reinterpret_cast<const lds_u32*>(ea)[m * PairTab<KB>::PITCH];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the lookups ahead of the arithmetic
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 t = tq[it & 1][q4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int m = 2 * q4 + u;
+          const float cs = u ? t.z : t.x, sn = u ? t.w : t.y;
+          const h2v kv = __builtin_bit_cast(h2v, kab[m]);
+          const float ka = (float)kv.x, kb = (float)kv.y;
+          // products with a zero addend stay mixed-precision FMAs (fp16 operand read in place)
+          const float X = __builtin_fmaf(A1[m], ka, __builtin_fmaf(-B1[m], kb, 0.0f));
+          const float Y = __builtin_fmaf(B1[m], ka, __builtin_fmaf(A1[m], kb, 0.0f));
+          s = __builtin_fmaf(cs, X, s);
+          s = __builtin_fmaf(-sn, Y, s);
+        }
+      }
+    } else {
+      float ca[8], cb[8];
+      unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
+      load_k(R, it, knext, koff);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 t = tq[it & 1][q4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int m = 2 * q4 + u;
+          const float cs = u ? t.z : t.x, sn = u ? t.w : t.y;
+          float X = __builtin_fmaf(A1[m], ca[m], Z1[m]);
+          X = __builtin_fmaf(B1[m], cb[m], X);
+          float Y = __builtin_fmaf(A2[m], ca[m], Z2[m]);
+          Y = __builtin_fmaf(B2[m], cb[m], Y);
+          s = __builtin_fmaf(cs, X, s);
+          s = __builtin_fmaf(sn, Y, s);
+        }
       }
     }
     s = lanes_sum<Sh::LPT>(s);
@@ -346,6 +454,100 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   wave_lds_sync();
 }
 
+// One (b, head, split) item on one wave: every full block of the split, then the
+// split's (m, l, o) to the workspace.
+template <int D, int BK, int KB, int VB, int KO, bool LUT>
+__device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __restrict__ q, int64_t q_pos,
+                                         float* __restrict__ ws, int S, int64_t bh, int split, float* wl,
+                                         const MLds& L, const float* table, const uint32_t* ptab, int lane) {
+  using Sh = MShape<D, BK, KB, VB>;
+  constexpr bool OUTL = KO > 0;
+  const int H = c.cfg.kv_heads;
+  const int G = c.cfg.v_group, ng = D / G;
+  const int64_t nfull = c.length / BK;
+  const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
+  // 3-bit rows: the lane's 48 bits start at byte 6 r, loaded from the dword below
+  const uint32_t koff = KB == 3 ? (uint32_t)(ts * Sh::RK + ((6 * r) & ~3)) : (uint32_t)(ts * Sh::RK + r * (Sh::KW * 4));
+  const uint32_t sh = KB == 3 ? (uint32_t)(((6 * r) & 3) * 8) : 0u;
+  const uint32_t* pt = LUT ? ptab + r * 8 * PairTab<KB>::PITCH : nullptr;
+  const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
+  const int h = (int)(bh % H);
+  const int b = (int)(bh / H);
+  const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
+
+  // query weight of pair `lane`: scale * conj(q_i) * e^{-i f_i q_pos}, evaluated in fp64
+  float wq_r = 0.0f, wq_i = 0.0f;
+  if (lane < Sh::HALF) {
+    const uint16_t* qv = q + ((int64_t)b * H + h) * D;
+    const double qa = (double)h2f(qv[lane]), qb = (double)h2f(qv[lane + Sh::HALF]);
+    const double f = pow((double)c.cfg.rope_theta, -(2.0 * lane) / (double)D);
+    double sn, cs;
+    sincos((double)q_pos * f, &sn, &cs);
+    const double scl = (double)kLog2e / sqrt((double)D);
+    wq_r = (float)(scl * (qa * cs - qb * sn));
+    wq_i = (float)(-scl * (qa * sn + qb * cs));
+  }
+  MState st;
+  st.m = -__builtin_inff();
+  st.lpart = 0.0f;
+  st.acc[0] = st.acc[1] = st.acc[2] = st.acc[3] = 0.0f;
+  st.zpart[0] = st.zpart[1] = 0.0f;
+
+  BlockRegs<D, BK, KB, VB> R;
+  CsrTok C;
+  if (n0 < n1) {
+    if constexpr (LUT) load_eb(R, c, n0, lane);
+    else load_kmeta(R, c, bh, n0, lane, 0);
+    load_vmeta(R, c, bh, n0, lane, ng);
+    if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n0, lane);
+    const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
+    const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
+#pragma unroll
+    for (int it = 0; it < Sh::NIT; ++it) load_codes(R, it, kb0, koff);
+#pragma unroll
+    for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
+  }
+  for (int64_t n = n0; n < n1; ++n)
+    process_block<D, BK, KB, VB, KO, LUT>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
+                                          c, bh, n, n + 1 < n1, koff);
+  if (OUTL) {
+    wave_lds_sync();
+    merge_vcorr<D>(wl + L.vcorr, st.acc, lane);  // the item's last block
+    wave_lds_sync();
+  }
+
+  // ---- finish the item: reduce across lanes and write (m, l, o) of this split
+  const float l = wave_sum(st.lpart);
+  const float z0 = wave_sum(st.zpart[0]);
+  const float z1 = wave_sum(st.zpart[1]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    for (int msk = Sh::CHL; msk < kWave; msk <<= 1) st.acc[k] += __shfl_xor(st.acc[k], msk, kWave);
+  float* dst = ws + (bh * S + split) * (D + 2);
+  if (lane < Sh::CHL) {
+    const int ch0 = 4 * lane;
+    const float z = (ch0 / G) == 0 ? z0 : z1;
+    *reinterpret_cast<float4*>(dst + 2 + ch0) =
+        make_float4(st.acc[0] + z, st.acc[1] + z, st.acc[2] + z, st.acc[3] + z);
+  }
+  if (lane == 0) {
+    dst[0] = st.m;
+    dst[1] = l;
+  }
+}
+
+// Copies the cos/sin(j f_i) table of a block's offsets into LDS ([Bk][D/2] float2
+// rows at a pitch of D + 4 floats).
+template <int D, int BK, int NT>
+__device__ __forceinline__ void stage_rope(float* table, const kvq_cache& c) {
+  constexpr int HALF = D / 2, TPITCH = D + 4;
+  for (int idx = threadIdx.x; idx < BK * HALF; idx += NT) {
+    const int j = idx / HALF, i = idx % HALF;
+    *reinterpret_cast<float2*>(table + j * TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
+  }
+}
+
+// Uniform keys: every wave takes items on its own.
 template <int D, int BK, int KB, int VB, int KO>
 __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
@@ -354,92 +556,57 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
   constexpr int kNT = kMhaWaves * 64;
   constexpr bool OUTL = KO > 0;
   extern __shared__ float lds[];
-  const int H = c.cfg.kv_heads;
-  const int G = c.cfg.v_group, ng = D / G;
-  const int64_t nfull = c.length / BK;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
-  const uint32_t koff = (uint32_t)(ts * Sh::RK + r * (Sh::KW * 4));
 
   float* table = lds;
-  for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += kNT) {
-    const int j = idx / Sh::HALF, i = idx % Sh::HALF;
-    *reinterpret_cast<float2*>(table + j * Sh::TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
-  }
-  const MLds L = mha_lds(D, BK, OUTL);
+  stage_rope<D, BK, kNT>(table, c);
+  const MLds L = mha_lds(D, BK, OUTL, false);
   float* wl = lds + BK * Sh::TPITCH + wave * L.total;
   if (OUTL)
     for (int k = lane; k < D; k += kWave) wl[L.vcorr + k] = 0.0f;
   __syncthreads();
 
-  const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
-  for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves) {
-    const int split = (int)(item % S);
-    const int64_t bh = item / S;
-    const int h = (int)(bh % H);
-    const int b = (int)(bh / H);
-    const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
+  for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves)
+    mha_item<D, BK, KB, VB, KO, false>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table, nullptr, lane);
+}
 
-    // query weight of pair `lane`: scale * conj(q_i) * e^{-i f_i q_pos}, evaluated in fp64
-    float wq_r = 0.0f, wq_i = 0.0f;
-    if (lane < Sh::HALF) {
-      const uint16_t* qv = q + ((int64_t)b * H + h) * D;
-      const double qa = (double)h2f(qv[lane]), qb = (double)h2f(qv[lane + Sh::HALF]);
-      const double f = pow((double)c.cfg.rope_theta, -(2.0 * lane) / (double)D);
-      double sn, cs;
-      sincos((double)q_pos * f, &sn, &cs);
-      const double scl = (double)kLog2e / sqrt((double)D);
-      wq_r = (float)(scl * (qa * cs - qb * sn));
-      wq_i = (float)(-scl * (qa * sn + qb * cs));
-    }
-    MState st;
-    st.m = -__builtin_inff();
-    st.lpart = 0.0f;
-    st.acc[0] = st.acc[1] = st.acc[2] = st.acc[3] = 0.0f;
-    st.zpart[0] = st.zpart[1] = 0.0f;
+// Codebook keys: the workgroup takes groups of up to 8 splits of one (b, head), so
+// that its waves share the head's pair table, rebuilt at every group.
+template <int D, int BK, int KB, int VB>
+__global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+                                                                       int64_t q_pos, float* __restrict__ ws, int S,
+                                                                       int64_t ngroups) {
+  using Sh = MShape<D, BK, KB, VB>;
+  using PT = PairTab<KB>;
+  constexpr int kNT = kMhaWaves * 64;
+  constexpr int NL = 1 << KB;  // codebook entries per channel
+  extern __shared__ float lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = c.cfg.kv_heads;
 
-    BlockRegs<D, BK, KB, VB> R;
-    CsrTok C;
-    if (n0 < n1) {
-      load_kmeta(R, c, bh, n0, lane, 0);
-      load_vmeta(R, c, bh, n0, lane, ng);
-      if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n0, lane);
-      const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
-      const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
-#pragma unroll
-      for (int it = 0; it < Sh::NIT; ++it) load_k(R, it, kb0, koff);
-#pragma unroll
-      for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
-    }
-    for (int64_t n = n0; n < n1; ++n)
-      process_block<D, BK, KB, VB, KO>(R, C, st, wl, L, table, wq_r, wq_i, inv_unit, lane, ts, r, G, ng, c, bh, n,
-                                       n + 1 < n1, koff);
-    if (OUTL) {
-      wave_lds_sync();
-      merge_vcorr<D>(wl + L.vcorr, st.acc, lane);  // the item's last block
-      wave_lds_sync();
-    }
+  float* table = lds;
+  stage_rope<D, BK, kNT>(table, c);
+  uint32_t* ptab = reinterpret_cast<uint32_t*>(lds + BK * Sh::TPITCH);
+  const MLds L = mha_lds(D, BK, false, true);
+  float* wl = reinterpret_cast<float*>(ptab + Sh::HALF * PT::PITCH) + wave * L.total;
 
-    // ---- finish the item: reduce across lanes and write (m, l, o) of this split
-    const float l = wave_sum(st.lpart);
-    const float z0 = wave_sum(st.zpart[0]);
-    const float z1 = wave_sum(st.zpart[1]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      for (int msk = Sh::CHL; msk < kWave; msk <<= 1) st.acc[k] += __shfl_xor(st.acc[k], msk, kWave);
-    float* dst = ws + (bh * S + split) * (D + 2);
-    if (lane < Sh::CHL) {
-      const int ch0 = 4 * lane;
-      const float z = (ch0 / G) == 0 ? z0 : z1;
-      *reinterpret_cast<float4*>(dst + 2 + ch0) =
-          make_float4(st.acc[0] + z, st.acc[1] + z, st.acc[2] + z, st.acc[3] + z);
+  const int gps = (S + kMhaWaves - 1) / kMhaWaves;  // groups per (b, head)
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const int64_t bh = g / gps;
+    const int split = (int)(g % gps) * kMhaWaves + wave;
+    const uint16_t* lut = c.k_lut + (int64_t)(bh % H) * D * NL;  // [D][NL]
+    __syncthreads();  // the previous group is done with the table
+    for (int idx = threadIdx.x; idx < Sh::HALF * PT::NPC; idx += kNT) {
+      const int i = idx / PT::NPC, pc = idx % PT::NPC;
+      const uint32_t ka = lut[i * NL + (pc & (NL - 1))];
+      const uint32_t kb = lut[(i + Sh::HALF) * NL + (pc >> KB)];
+      ptab[i * PT::PITCH + pc] = ka | (kb << 16);
     }
-    if (lane == 0) {
-      dst[0] = st.m;
-      dst[1] = l;
-    }
+    __syncthreads();
+    if (split < S) mha_item<D, BK, KB, VB, 0, true>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
   }
 }
 
@@ -453,7 +620,7 @@ template <int D, int BK, int KB, int VB, int KO>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                    hipStream_t s, int cus) {
   using Sh = MShape<D, BK, KB, VB>;
-  const MLds L = mha_lds(D, BK, KO > 0);
+  const MLds L = mha_lds(D, BK, KO > 0, false);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
   hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO>,
@@ -467,15 +634,44 @@ static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_
   return hipGetLastError();
 }
 
+template <int D, int BK, int KB, int VB>
+static hipError_t launch_mha_lut_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
+                                       hipStream_t s, int cus) {
+  using Sh = MShape<D, BK, KB, VB>;
+  const MLds L = mha_lds(D, BK, false, true);
+  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)Sh::HALF * PairTab<KB>::PITCH +
+                        (size_t)kMhaWaves * L.total) * sizeof(float);
+  if (bytes > 160 * 1024) return hipErrorNotSupported;
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_lut_kernel<D, BK, KB, VB>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return e;
+  const int64_t ngroups = (int64_t)c.cfg.batch * c.cfg.kv_heads * ((S + kMhaWaves - 1) / kMhaWaves);
+  const int64_t grid = ngroups < cus ? ngroups : cus;
+  hipLaunchKernelGGL((decode_mha_lut_kernel<D, BK, KB, VB>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s,
+                     c, q, q_pos, ws, S, ngroups);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus) {
   const kvq_config& g = c.cfg;
   const int ko = host_kout(g);
   const int ng = g.head_dim / g.v_group;
-  if (g.q_heads != g.kv_heads || g.k_mode != 0 || (g.k_bits != 4 && g.k_bits != 2) || ko > 2 || ng > 2 ||
-      g.k_block * ng > 256)
-    return hipErrorNotSupported;
+  if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
+  if (g.k_mode == 1) {
+    // codebook keys: 2- and 3-bit codes (pair tables of 16 and 64 entries), no outliers
+    if (ko != 0 || (KB != 3 && KB != 2)) return hipErrorNotSupported;
+#define KVQ_MHA_LUT(d, bk, kb, vb) \
+  if (D == d && BK == bk && KB == kb && VB == vb) return launch_mha_lut_typed<d, bk, kb, vb>(c, q, q_pos, ws, S, s, cus);
+    KVQ_MHA_LUT(128, 128, 3, 2) KVQ_MHA_LUT(128, 128, 3, 4) KVQ_MHA_LUT(128, 128, 2, 2) KVQ_MHA_LUT(128, 128, 2, 4)
+    KVQ_MHA_LUT(128, 64, 3, 2) KVQ_MHA_LUT(128, 64, 3, 4) KVQ_MHA_LUT(128, 64, 2, 2) KVQ_MHA_LUT(128, 64, 2, 4)
+    KVQ_MHA_LUT(64, 128, 3, 2) KVQ_MHA_LUT(64, 128, 3, 4) KVQ_MHA_LUT(64, 128, 2, 2) KVQ_MHA_LUT(64, 128, 2, 4)
+    KVQ_MHA_LUT(64, 64, 3, 2) KVQ_MHA_LUT(64, 64, 3, 4) KVQ_MHA_LUT(64, 64, 2, 2) KVQ_MHA_LUT(64, 64, 2, 4)
+#undef KVQ_MHA_LUT
+    return hipErrorNotSupported;
+  }
+  if (g.k_mode != 0 || (KB != 4 && KB != 2)) return hipErrorNotSupported;
 #define KVQ_MHA(d, bk, kb, vb)                                                                  \
   if (D == d && BK == bk && KB == kb && VB == vb) {                                             \
     if (ko == 2) return launch_mha_typed<d, bk, kb, vb, 2>(c, q, q_pos, ws, S, s, cus);         \

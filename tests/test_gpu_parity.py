@@ -48,6 +48,11 @@ SMALL = {
                       None),
     "lut2_d64_clip": (synth.config("c0", k_mode=1, k_bits=2, v_group=32, tokens=150, capacity=192,
                                    clip_quantile=0.9), None),
+    "lut3_v4_d64_bk64": (synth.config("c3", batch=2, q_heads=2, kv_heads=2, head_dim=64, k_block=64,
+                                      v_bits=4, v_group=32, tokens=4 * 64 + 21, capacity=384),
+                         [100, 177]),
+    "lut2_v2_d128": (synth.config("c3", batch=1, q_heads=3, kv_heads=3, k_bits=2,
+                                  tokens=3 * 128 + 9, capacity=512), None),
 }
 
 
@@ -103,10 +108,12 @@ def test_small_cases_bitwise_and_decode(case):
     torch.cuda.synchronize()
 
 
-def test_split_count_invariance_and_determinism():
-    cfg, _ = SMALL["clip_csr_append"]
+@pytest.mark.parametrize("case", ["clip_csr_append", "lut3_v2"])
+def test_split_count_invariance_and_determinism(case):
+    cfg, _ = SMALL[case]
+    say("case", case)
     k, v = inputs(cfg)
-    cache = build_gpu_cache(cfg, k, v)
+    cache = build_gpu_cache(cfg, k, v, None, _lut(cfg))
     qd = upload(_q(cfg))
     outs = {}
     for S in (1, 3, 7, 64):
