@@ -512,7 +512,9 @@ __device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* z
 // D/2+4a..D/2+4a+3, i.e. elements 8a..8a+7 of the packed row (element e holds channel
 // e/2 + (e%2) D/2).  Thread tid = a * NTG + tg; the cell's tokens are tg + NTG u, so
 // the NTG lanes sharing a channel set form one DPP row and read distinct LDS banks.
-template <int D, int BK, bool LUT, bool OUTL, bool CLIP>
+// LUTB: 0 for uniform keys (code width from the configuration), else the code width
+// of codebook keys.
+template <int D, int BK, int LUTB, bool OUTL, bool CLIP>
 __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
                                                                  int64_t old_len, int64_t n_new, int64_t n_first) {
   constexpr int P = D + 8;
@@ -524,10 +526,10 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t T = c.cfg.capacity;
   const int64_t bh = (int64_t)b * c.cfg.kv_heads + h;
-  const int kb = c.cfg.k_bits;
+  constexpr bool lut = LUTB > 0;
+  const int kb = lut ? LUTB : c.cfg.k_bits;
   const int L = (1 << kb) - 1;
   const float Lf = (float)L;
-  constexpr bool lut = LUT;
 
   const float thr =
       prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
@@ -637,24 +639,47 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
         }
       }
     } else {
+      // code = the number of midpoints below the value (ties to the lower entry)
+      constexpr int NM = (1 << (lut ? LUTB : 1)) - 1;
 #pragma unroll
       for (int u = 0; u < 8; ++u) w[u] = 0;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        float md[15];
+        float md[NM];
 #pragma unroll
-        for (int k = 0; k < 15; ++k) md[k] = sh.u.out.mids[chq[q] * 15 + (k < L ? k : 0)];
+        for (int k = 0; k < NM; ++k) md[k] = sh.u.out.mids[chq[q] * 15 + k];
         const int e = 2 * (q & 3) + (q >> 2);
+        if constexpr (!CLIP) {
+          // Unclipped values are fp16 (multiples of 2^-24) and every midpoint is a
+          // multiple of 2^-25, so (x - mid) * 2^25 is an integer computed exactly by
+          // one FMA: clamped to [0, 1] it is the step [x > mid], with no compare.
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float d = x[u][q];
-          if constexpr (CLIP) d = fminf(fmaxf(d, -thr), thr);
-          uint32_t cq = 0;
+          for (int k = 0; k < NM; ++k) md[k] *= -33554432.0f;
 #pragma unroll
-          for (int k = 0; k < 15; ++k)
-            if (k < L) cq += d > md[k];
-          if constexpr (OUTL) cq = (x[u][q] != x[u][q]) ? 0u : cq;
-          w[u] |= cq << (e * kb);
+          for (int u = 0; u < 8; ++u) {
+            const float d = x[u][q];
+            float st[NM];
+#pragma unroll
+            for (int k = 0; k < NM; ++k)
+              st[k] = __builtin_amdgcn_fmed3f(__builtin_fmaf(d, 33554432.0f, md[k]), 0.0f, 1.0f);
+#pragma unroll
+            for (int w2 = 1; w2 < NM; w2 *= 2)  // pairwise sum of the steps
+#pragma unroll
+              for (int k = 0; k + w2 < NM; k += 2 * w2) st[k] += st[k + w2];
+            uint32_t cq = (uint32_t)st[0];
+            if constexpr (OUTL) cq = (d != d) ? 0u : cq;
+            w[u] |= cq << (e * (lut ? LUTB : 1));
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float d = fminf(fmaxf(x[u][q], -thr), thr);
+            uint32_t cq = 0;
+#pragma unroll
+            for (int k = 0; k < NM; ++k) cq += d > md[k] ? 1u : 0u;
+            if constexpr (OUTL) cq = (x[u][q] != x[u][q]) ? 0u : cq;
+            w[u] |= cq << (e * (lut ? LUTB : 1));
+          }
         }
       }
     }
