@@ -1,4 +1,4 @@
-// decode_gqa.hip -- decode attention over uniform 2/4-bit key and value caches when
+// decode_gqa.hip -- decode attention over uniform 4-bit keys and 2/4-bit values when
 // several query heads share one kv head (grouped-query attention), tuned for gfx950.
 //
 // Pages cited (title, address):
@@ -9,26 +9,26 @@
 // khat_ij = (k_a + i k_b) e^{i f_i j} is the dequantized pre-RoPE key pair ([KVC3]
 // "Per-Channel Key Quantization", "Pre-RoPE Key Quantization") rotated by the token's
 // offset in the block, and W_g,i = conj(q_g,i) e^{i f_i (n Bk - p)} carries the query
-// rotation.  khat is computed once per key element and shared by every head of the
-// group (6 operations per rotary pair, then 2 per head), unlike the one-head kernel,
-// which folds the dequantization into per-head weights.
-//
-// Organisation (one wave per (b, kv-head, head set, split) item, blocks streamed
-// through a register prefetch exactly as in the one-head kernel):
-//  * per block, lanes < D/2 build the per-pair dequantization constants and the
-//    block-rotated query weights of the wave's heads in LDS; every lane then holds
-//    those of its 4 pairs in registers (16 lanes per key token);
-//  * scores of all heads, reduced across a token's lanes by a DPP reduce-scatter
-//    over the heads, written to LDS;
+// rotation.  Up to four query heads of a kv head form one wave's item, and both
+// contractions run on the matrix cores as fp32 v_mfma_f32_4x4x1_16b_f32, whose 16
+// blocks of 4 x 4 outer products fit four heads without padding:
+//  * scores: every lane owns one key token (two 64-token halves per block) and
+//    computes khat for its token, pair by pair (6 VALU operations per pair: two
+//    dequantizing FMAs, the rotation); per key channel one MFMA multiplies the four
+//    heads' weights (lane l supplies head l % 4) with the 64 tokens' khat, so after
+//    the 128 channels lane l holds the scores of its token for all four heads --
+//    no cross-lane reduction;
+//  * values: lane l owns channels 4 (l % 32) .. +3 and the token groups of its half
+//    of the wave; per token and channel slot one MFMA multiplies the four heads'
+//    weights p * scale with the codes (converted two at a time with the packed fp8
+//    conversion: a byte 0..15 is an exact fp8 value proportional to it);
 //  * outliers ([KVC3] "Per-Vector Dense-and-Sparse Quantization"): code 0 was stored
-//    at an outlier's position; the lanes that own a token in the softmax (two tokens
-//    per lane) add each of its CSR entries' exact score terms in registers, and
-//    scatter its value corrections p * (x - zero) into a per-head channel array with
-//    LDS atomics;
-//  * online softmax per head over the block (lanes own two tokens each), value
-//    weights p*scale quantized per head to 16-bit fixed point, nibble planes, and
-//    v_dot8_u32_u4 on the packed value words as in the one-head kernel.
-// No dequantized key or value is written to memory ([TQ] sections 5.1 and 6.3).
+//    at an outlier's position; the lane owning a token adds the exact score terms of
+//    its CSR entries for every head, and scatters p * (x - zero) into a per-head
+//    channel array with LDS atomics, merged at the next block's softmax.
+// Blocks stream through registers as in the one-head kernel: every register slot is
+// refilled with block n + 1 right after its last use in block n.  No dequantized key
+// or value is written to memory ([TQ] sections 5.1 and 6.3).
 #include <math.h>
 
 #include "decode_common.h"
@@ -39,431 +39,402 @@ namespace {
 using namespace dcm;
 
 constexpr int kGqaWaves = 8;
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+constexpr int kD = 128, kBK = 128, kHalf = 64;
+constexpr int kTP = kD + 4;  // floats per rotary-table row: 64 (cos, sin) pairs + 4 (banks)
+constexpr int kWVP = kBK + 4;  // floats per value-weight row (one row per group and head)
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
 
 // Per-wave LDS area, in floats.
 struct GLds {
-  int wts, s, vcorr, total;
+  int meta, wa, wv, vcorr, wq, total;
 };
-__host__ __device__ inline GLds gqa_lds(int D, int BK, int GW, int ng, bool outl) {
+__host__ __device__ inline GLds gqa_lds(int ng, bool outl) {
   GLds m;
   int o = 0;
-  const int wts = (4 + 2 * GW) * (D / 2);            // ALPHA BETA ZA ZB, then per pair WR[g] WIN[g]
-  const int vq = GW * ng * BK / 2 + GW * ng * 64;     // u16 weights + nibble planes (reuse)
-  m.wts = o; o += wts > vq ? wts : vq;
-  m.s = o; o += BK * GW;                              // scores, then probabilities [BK][GW]
-  m.vcorr = o; o += outl ? GW * D : 0;                // value outlier corrections [GW][D]
+  m.meta = o; o += 4 * kHalf;        // per pair: scale_a / u, zero_a, scale_b / u, zero_b
+  m.wa = o; o += 4 * kHalf * 2;      // per head and pair: (W_r, -W_i)
+  m.wv = o; o += ng * 4 * kWVP;      // value weights p * scale / u, [group][head][token]
+  m.vcorr = o; o += outl ? 4 * kD + 4 : 0;  // value outlier corrections [head][channel] (int), scale per head
+  m.wq = o; o += kHalf * 8;          // the item's query weights per pair: (re, im) of 4 heads
   m.total = o;
   return m;
 }
 
-// v + x of the DPP partner: row_mirror (lane 15 - i) and row_half_mirror (lane 7 - i).
-__device__ __forceinline__ float add_dpp_rm(float v, float x) {
-  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 row_mirror row_mask:0xf bank_mask:0xf" : "+v"(v) : "v"(x));
-  return v;
-}
-__device__ __forceinline__ float add_dpp_hm(float v, float x) {
-  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v) : "v"(x));
-  return v;
-}
-
-template <int GW>
-struct GState {
-  float m[GW], lpart[GW], acc[GW][4], zpart[GW][2];
+template <int VB>
+struct GRegs {
+  static constexpr int NVI = (kBK / (32 / VB)) * kD / 256;  // 16-byte value loads per lane
+  uint4 k[2][4];     // key rows of tokens lane and 64 + lane (64 bytes each)
+  uint4 v[NVI];      // value words: load s holds channels 4 (l % 32) .. +3 of token group 2 s + l / 32
+  uint16_t kmeta[4]; // lane i: scale[i], scale[i + 64], zero[i], zero[i + 64]
+  float eb_c, eb_s;  // lane i: cos/sin(n Bk f_i)
+  uint16_t vs[4], vz[4];  // value scale/zero of elements lane + 64 k ([group][token])
 };
 
-template <int D, int BK, int KB, int VB>
-using GShape = MShape<D, BK, KB, VB, 4>;
-template <int D, int BK, int KB, int VB>
-using GRegs = BlockRegs<D, BK, KB, VB, GShape<D, BK, KB, VB>::NIT / 2, 4>;
+__device__ __forceinline__ const uint8_t* gk_block(const kvq_cache& c, int64_t bh, int64_t n) {
+  return static_cast<const uint8_t*>(c.k_codes) + (bh * c.cfg.capacity + n * kBK) * (kD / 2);
+}
+template <int VB>
+__device__ __forceinline__ const uint8_t* gv_block(const kvq_cache& c, int64_t bh, int64_t n) {
+  constexpr int TPW = 32 / VB;
+  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) +
+                                          (bh * (c.cfg.capacity / TPW) + n * (kBK / TPW)) * kD);
+}
+// Key row slot q (16 bytes) of half hf: token 64 hf + lane.
+template <int VB>
+__device__ __forceinline__ void gload_k(GRegs<VB>& R, int hf, int q, const uint8_t* kblk, int lane) {
+  R.k[hf][q] = *reinterpret_cast<const uint4*>(kblk + (uint32_t)((kHalf * hf + lane) * (kD / 2) + 16 * q));
+}
+// Value load s: words of token group 2 s + lane / 32 (32 / VB tokens each), channels
+// 4 (lane % 32) .. +3.
+template <int VB>
+__device__ __forceinline__ void gload_v(GRegs<VB>& R, int s, const uint8_t* vblk, int lane) {
+  const uint32_t tg = 2 * s + (lane >> 5);
+  R.v[s] = *reinterpret_cast<const uint4*>(vblk + (tg * kD + 4 * (lane & 31)) * 4u);
+}
+template <int VB>
+__device__ __forceinline__ void gload_kmeta(GRegs<VB>& R, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
+  const int64_t m = (bh * (c.cfg.capacity / kBK) + n) * kD;
+  R.kmeta[0] = c.k_scale[m + lane];
+  R.kmeta[1] = c.k_scale[m + lane + kHalf];
+  R.kmeta[2] = c.k_zero[m + lane];
+  R.kmeta[3] = c.k_zero[m + lane + kHalf];
+  const float2 eb = reinterpret_cast<const float2*>(c.rope + (int64_t)kBK * kD + n * kD)[lane];
+  R.eb_c = eb.x;
+  R.eb_s = eb.y;
+}
+template <int VB>
+__device__ __forceinline__ void gload_vmeta(GRegs<VB>& R, const kvq_cache& c, int64_t bh, int64_t n, int lane,
+                                            int ng) {
+  const int64_t m0 = (bh * c.cfg.capacity + n * kBK) * ng;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (kWave * k < kBK * ng) {
+      const int grp = (kWave * k) / kBK, t = (kWave * k) % kBK + lane;
+      const uint32_t e = (uint32_t)(t * ng + grp);
+      R.vs[k] = c.v_scale[m0 + e];
+      R.vz[k] = c.v_zero[m0 + e];
+    }
+  }
+}
 
-template <int D, int BK, int KB, int VB, int GW, int KO>
-__device__ __forceinline__ void gqa_block(GRegs<D, BK, KB, VB>& R, CsrTok& C, GState<GW>& st, float* __restrict__ wl,
-                                          const GLds& L, const float* __restrict__ table, const float (&wq_r)[GW],
-                                          const float (&wq_i)[GW], float unit, float inv_unit, int lane, int ts, int r, int G,
-                                          int ng, const kvq_cache& c, int64_t bh, int64_t n, bool more,
-                                          uint32_t koff) {
-  using Sh = GShape<D, BK, KB, VB>;
-  constexpr int HALF = Sh::HALF;
+struct GState {
+  float m[4], lpart[4], zpart[4][2];
+  f4 acc[4];  // acc[c][g]: head g, channel 4 (lane % 32) + c, this lane's token groups
+};
+
+// Adds the four heads' value-outlier corrections (fixed point in LDS) to the lane's
+// accumulators (channels 4 lane .. +3, lanes < 32) and clears them.
+__device__ __forceinline__ void merge_vcorr_heads(int* VCI, GState& st, int lane) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float a[4] = {st.acc[0][g], st.acc[1][g], st.acc[2][g], st.acc[3][g]};
+    merge_vcorr<kD>(VCI + g * kD, VCI[4 * kD + g], a, lane);
+    st.acc[0][g] = a[0]; st.acc[1][g] = a[1]; st.acc[2][g] = a[2]; st.acc[3][g] = a[3];
+  }
+}
+
+template <int VB, int KO>
+__device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, float* __restrict__ wl, const GLds& L,
+                                          const float* __restrict__ table, float inv_unit, int lane, int G, int ng,
+                                          const kvq_cache& c, int64_t bh, int64_t n, bool more) {
   constexpr bool OUTL = KO > 0;
-  constexpr int ko = KO;
+  constexpr int TPW = 32 / VB;
   const int64_t nn = more ? n + 1 : n;
-  const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
-  const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, nn);
-  float* wAL = wl + L.wts;
-  float* wBE = wAL + HALF;
-  float* wZA = wBE + HALF;
-  float* wZB = wZA + HALF;
-  float* wWP = wZB + HALF;        // [HALF][2 GW]: WR[g] then -WI[g] of each pair
-  float* Sc = wl + L.s;           // [BK][GW]
-  float* VCR = wl + L.vcorr;
+  const uint8_t* knext = gk_block(c, bh, nn);
+  const uint8_t* vnext = gv_block<VB>(c, bh, nn);
+  float* Meta = wl + L.meta;
+  float* WA = wl + L.wa;
+  float* WV = wl + L.wv;
+  int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
+  const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
 
-  // ---- per-pair dequantization constants and block-rotated query weights
-  // The codes arrive as c * u (u the fp8 unit, a power of two): keys are carried as
-  // k * u = scale * (c u) + zero * u and the weights as W / u, which is exact scaling.
-  if (lane < HALF) {
-    reinterpret_cast<uint16_t*>(wAL)[lane] = R.kmeta[0];
-    reinterpret_cast<uint16_t*>(wBE)[lane] = R.kmeta[1];
-    wZA[lane] = h2f(R.kmeta[2]) * unit;
-    wZB[lane] = h2f(R.kmeta[3]) * unit;
+  // ---- per-pair dequantization constants and block-rotated query weights (pair = lane)
+  {
+    const float sa = h2f(R.kmeta[0]) * inv_unit, sb = h2f(R.kmeta[1]) * inv_unit;
+    *reinterpret_cast<float4*>(Meta + 4 * lane) = make_float4(sa, h2f(R.kmeta[2]), sb, h2f(R.kmeta[3]));
+    const float4 q01 = *reinterpret_cast<const float4*>(wl + L.wq + 8 * lane);
+    const float4 q23 = *reinterpret_cast<const float4*>(wl + L.wq + 8 * lane + 4);
+    const float wq_r[4] = {q01.x, q01.z, q23.x, q23.z}, wq_i[4] = {q01.y, q01.w, q23.y, q23.w};
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      wWP[lane * 2 * GW + g] = (wq_r[g] * R.eb_c - wq_i[g] * R.eb_s) * inv_unit;
-      wWP[lane * 2 * GW + GW + g] = -(wq_r[g] * R.eb_s + wq_i[g] * R.eb_c) * inv_unit;
-    }
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float2*>(WA + g * 2 * kHalf + 2 * lane) =
+          make_float2(wq_r[g] * R.eb_c - wq_i[g] * R.eb_s, -(wq_r[g] * R.eb_s + wq_i[g] * R.eb_c));  // W_r, -W_i
   }
-  load_kmeta(R, c, bh, nn, lane, 0);
-  wave_lds_sync();
-  float ZA[4], ZB[4], WR[GW][4], WI[GW][4];
-  h2v AL[2], BE[2];
-  auto ld4 = [&](const float* base, float(&dst)[4]) {
-    const float4 a = *reinterpret_cast<const float4*>(base + r * 4);
-    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-  };
-  auto ldh4 = [&](const float* base, h2v(&dst)[2]) {
-    const uint2 a = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + r * 4);
-    dst[0] = __builtin_bit_cast(h2v, a.x);
-    dst[1] = __builtin_bit_cast(h2v, a.y);
-  };
-  ldh4(wAL, AL);
-  ldh4(wBE, BE);
-  ld4(wZA, ZA);
-  ld4(wZB, ZB);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float* wp = wWP + (4 * r + m) * 2 * GW;
-#pragma unroll
-    for (int g4 = 0; g4 < 2 * GW; g4 += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(wp + g4);
-      const float xv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int gg = g4 + u;
-        if (gg < GW) WR[gg][m] = xv[u];
-        else WI[gg - GW][m] = xv[u];
-      }
-    }
-  }
-
-  // ---- scores of all heads: 16 lanes per token, 4 pairs per lane; the per-head lane
-  // sums are a reduce-scatter that leaves head h of the token in lanes 4h'..4h'+3
-  // (h' = h for 4 heads, lanes 8h..8h+7 for 2 heads)
-  constexpr int KS = Sh::NIT / 2;
-  const uint8_t* kcur = k_block<D, BK, KB, VB>(c, bh, n);
-  const bool lowhalf = (r & 8) == 0, lowq = (r & 4) == 0;
-  // two halves of KS iterations: slot `sl` holds iteration sl of the half; in the first
-  // half it is refilled with iteration KS + sl of this block, in the second with
-  // iteration sl of the next block (fully unrolled, so that every wait for a slot's
-  // load is an exact count of the loads issued after it)
-  constexpr int LPH = 16 / GW;  // lanes per head after the reduce-scatter
-  // per-lane bases; every iteration adds a compile-time offset (folded into the LDS
-  // instructions' offset field)
-  const float* tab0 = table + ts * Sh::TPITCH + 8 * r;
-  float* sc0 = Sc + ts * GW + r / LPH;
-#pragma unroll
-  for (int it = 0; it < Sh::NIT; ++it) {
-    const int hb = it / KS, sl = it % KS;
-    const uint8_t* kref = hb ? knext : kcur + KS * (Sh::TPI * Sh::RK);
-    const float* tab = tab0 + it * (Sh::TPI * Sh::TPITCH);
-    const uint32_t w = R.k[sl][0];
-    load_k_slot(R, sl, sl, kref, koff);
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    const f2v a01 = cvt_lo(lo), a23 = cvt_hi(lo), b01 = cvt_lo(hi), b23 = cvt_hi(hi);
-    const float ca[4] = {a01.x, a01.y, a23.x, a23.y}, cb[4] = {b01.x, b01.y, b23.x, b23.y};
-    const float4 t01 = *reinterpret_cast<const float4*>(tab);
-    const float4 t23 = *reinterpret_cast<const float4*>(tab + 4);
-    const float cs[4] = {t01.x, t01.z, t23.x, t23.z}, sn[4] = {t01.y, t01.w, t23.y, t23.w};
-    float s[GW];
-#pragma unroll
-    for (int g = 0; g < GW; ++g) s[g] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float ka = __builtin_fmaf((float)AL[m >> 1][m & 1], ca[m], ZA[m]);
-      const float kbv = __builtin_fmaf((float)BE[m >> 1][m & 1], cb[m], ZB[m]);
-      const float tr = __builtin_fmaf(ka, cs[m], -kbv * sn[m]);
-      const float ti = __builtin_fmaf(ka, sn[m], kbv * cs[m]);
-#pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        s[g] = __builtin_fmaf(WR[g][m], tr, s[g]);
-        s[g] = __builtin_fmaf(WI[g][m], ti, s[g]);
-      }
-    }
-    float v;
-    if constexpr (GW == 4) {
-      // lanes r and 15 - r: the low half keeps heads 0, 1, the high half heads 2, 3
-      float k0 = lowhalf ? s[0] : s[2], k1 = lowhalf ? s[1] : s[3];
-      k0 = add_dpp_rm(k0, lowhalf ? s[2] : s[0]);
-      k1 = add_dpp_rm(k1, lowhalf ? s[3] : s[1]);
-      // lanes r and 7 - r within the half: the low quad keeps the first of the two
-      v = add_dpp_hm(lowq ? k0 : k1, lowq ? k1 : k0);
-      v = lanes_sum<4>(v);
-    } else {
-      v = add_dpp_rm(lowhalf ? s[0] : s[1], lowhalf ? s[1] : s[0]);
-      v = lanes_sum<8>(v);
-    }
-    if (r % LPH == 0) sc0[it * (Sh::TPI * GW)] = v;
-    // (iterations are left to the scheduler)
-  }
+  gload_kmeta(R, c, bh, nn, lane);
   wave_lds_sync();
 
-  // ---- online softmax per head; lane owns tokens lane and lane + 64
-  constexpr int TPL = BK / kWave;  // tokens per lane
-  float p[TPL][GW];
-  float mloc[GW];
+  // ---- scores: lane owns tokens lane and 64 + lane; per key channel and token half
+  // one MFMA over the four heads.  Both tokens share each pair's constants and
+  // weights; one 16-byte read covers two pairs of the table or of the weights.  The
+  // loop runs over windows of two pairs and is software-pipelined: the LDS reads of
+  // window w + 1 are issued before the arithmetic of window w.
+  f4 S[2];
+  {
+    const float* trA = table + lane * kTP;
+    const float* trB = table + (kHalf + lane) * kTP;
+    const float* wal = WA + hl * 2 * kHalf;
+    struct Win {
+      float4 tA, tB, wa, M0, M1;  // cos/sin of both tokens, weights, pair constants
+    };
+    auto load_win = [&](int w, Win& L) {
+      const int i = 2 * w;
+      L.tA = *reinterpret_cast<const float4*>(trA + 2 * i);
+      L.tB = *reinterpret_cast<const float4*>(trB + 2 * i);
+      L.wa = *reinterpret_cast<const float4*>(wal + 2 * i);
+      L.M0 = *reinterpret_cast<const float4*>(Meta + 4 * i);
+      L.M1 = *reinterpret_cast<const float4*>(Meta + 4 * i + 4);
+    };
+    // two accumulator chains per half; an MFMA result is ready only about 40 cycles
+    // after issue, so dependent MFMAs are kept four apart
+    f4 sc[2][2];
 #pragma unroll
-  for (int g = 0; g < GW; ++g) mloc[g] = -__builtin_inff();
+    for (int hf = 0; hf < 2; ++hf) sc[hf][0] = sc[hf][1] = f4{0.f, 0.f, 0.f, 0.f};
+    Win L[2];
+    load_win(0, L[0]);
+    uint32_t words[2][4];
+    float ca[2][4], cb[2][4];
 #pragma unroll
-  for (int k = 0; k < TPL; ++k) {
-    const int t = lane + kWave * k;
-    if constexpr (GW == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(Sc + t * 4);
-      p[k][0] = v.x; p[k][1] = v.y; p[k][2] = v.z; p[k][3] = v.w;
-    } else {
-      const float2 v = *reinterpret_cast<const float2*>(Sc + t * 2);
-      p[k][0] = v.x; p[k][1] = v.y;
+    for (int w = 0; w < kHalf / 2; ++w) {
+      if (w % 8 == 0) {  // a new 16-byte slot of both rows; refill it with the next block
+        const int q = w / 8;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          words[hf][0] = R.k[hf][q].x; words[hf][1] = R.k[hf][q].y;
+          words[hf][2] = R.k[hf][q].z; words[hf][3] = R.k[hf][q].w;
+          gload_k(R, hf, q, knext, lane);
+        }
+      }
+      if (w % 2 == 0) {  // a new dword: pairs 4 d .. 4 d + 3, byte = (code_a | code_b << 4)
+        const int d = (w % 8) / 2;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t lo = words[hf][d] & 0x0F0F0F0Fu, hi = (words[hf][d] >> 4) & 0x0F0F0F0Fu;
+          const f2v a01 = cvt_lo(lo), a23 = cvt_hi(lo), b01 = cvt_lo(hi), b23 = cvt_hi(hi);
+          ca[hf][0] = a01.x; ca[hf][1] = a01.y; ca[hf][2] = a23.x; ca[hf][3] = a23.y;
+          cb[hf][0] = b01.x; cb[hf][1] = b01.y; cb[hf][2] = b23.x; cb[hf][3] = b23.y;
+        }
+      }
+      if (w + 1 < kHalf / 2) load_win(w + 1, L[(w + 1) & 1]);
+      const Win& C0 = L[w & 1];
+      const int m2 = 2 * (w % 2);
+      float tr[2][2], ti[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4 M = u ? C0.M1 : C0.M0;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const float4 t = hf ? C0.tB : C0.tA;
+          const float cs = u ? t.z : t.x, sn = u ? t.w : t.y;
+          const float ka = __builtin_fmaf(M.x, ca[hf][m2 + u], M.y);
+          const float kb = __builtin_fmaf(M.z, cb[hf][m2 + u], M.w);
+          tr[hf][u] = __builtin_fmaf(ka, cs, -(kb * sn));
+          ti[hf][u] = __builtin_fmaf(ka, sn, kb * cs);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) sc[hf][u] = mfma4(u ? C0.wa.z : C0.wa.x, tr[hf][u], sc[hf][u]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) sc[hf][u] = mfma4(u ? C0.wa.w : C0.wa.y, ti[hf][u], sc[hf][u]);
+      // one window at a time: hoisting the reads of the whole unrolled block would
+      // exhaust the registers
+      __builtin_amdgcn_sched_barrier(0);
     }
+    S[0] = sc[0][0] + sc[0][1];
+    S[1] = sc[1][0] + sc[1][1];
+  }
+
+  // ---- online softmax per head; lane owns tokens lane and 64 + lane
+  float p[2][4];
+  float mloc[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) mloc[g] = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) p[k][g] = S[k][g];
     if constexpr (OUTL) {
       // key outliers of token t: code 0 (dequantized to the zero-point) was stored; add
       // the exact term (x - zero) of each CSR entry, rotated, for every head
-      const uint32_t vals = C.kv[k];
+      const int t = kHalf * k + lane;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = (int)((C.kc[k] >> (8 * q)) & 0xffu);
-        const float val = h2f((uint16_t)(vals >> (16 * q)));
-        const int i = col % HALF;
-        const bool a = col < HALF;
-        const float dl = val * unit - (a ? wZA[i] : wZB[i]);   // (x - zero) * u
-        const float2 cssn = *reinterpret_cast<const float2*>(table + t * Sh::TPITCH + 2 * i);
-        const float* wp = wWP + i * 2 * GW;
+      for (int qq = 0; qq < KO; ++qq) {
+        const int col = (int)((C.kc[k] >> (8 * qq)) & 0xffu);
+        const float val = h2f((uint16_t)(C.kv[k] >> (16 * qq)));
+        const int i = col % kHalf;
+        const bool a = col < kHalf;
+        const float4 M = *reinterpret_cast<const float4*>(Meta + 4 * i);
+        const float dl = val - (a ? M.y : M.w);
+        const float2 cssn = *reinterpret_cast<const float2*>(table + t * kTP + 2 * i);
 #pragma unroll
-        for (int g = 0; g < GW; ++g) {
-          const float wr = wp[g], wi = -wp[GW + g];   // W / u
+        for (int g = 0; g < 4; ++g) {
+          const float2 w = *reinterpret_cast<const float2*>(WA + g * 2 * kHalf + 2 * i);
+          const float wr = w.x, wi = -w.y;
           const float re = wr * cssn.x - wi * cssn.y, im = wr * cssn.y + wi * cssn.x;
           p[k][g] += a ? dl * re : -dl * im;
         }
       }
     }
 #pragma unroll
-    for (int g = 0; g < GW; ++g) mloc[g] = fmaxf(mloc[g], p[k][g]);
+    for (int g = 0; g < 4; ++g) mloc[g] = fmaxf(mloc[g], p[k][g]);
   }
-  if constexpr (OUTL)  // the previous block's
+  if constexpr (OUTL) merge_vcorr_heads(VCI, st, lane);  // the previous block's, before the rescale
 #pragma unroll
-    for (int g = 0; g < GW; ++g) merge_vcorr<D>(VCR + g * D, st.acc[g], lane);
-#pragma unroll
-  for (int g = 0; g < GW; ++g) {
+  for (int g = 0; g < 4; ++g) {
     const float mnew = fmaxf(st.m[g], wave_max_uniform(mloc[g]));
     const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew);
     st.m[g] = mnew;
-    float psum = 0.0f;
+    p[0][g] = __builtin_amdgcn_exp2f(p[0][g] - mnew);
+    p[1][g] = __builtin_amdgcn_exp2f(p[1][g] - mnew);
+    st.lpart[g] = __builtin_fmaf(st.lpart[g], alpha, p[0][g] + p[1][g]);
 #pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      p[k][g] = __builtin_amdgcn_exp2f(p[k][g] - mnew);
-      psum += p[k][g];
-    }
-    st.lpart[g] = __builtin_fmaf(st.lpart[g], alpha, psum);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st.acc[g][q] *= alpha;
+    for (int cc = 0; cc < 4; ++cc) st.acc[cc][g] *= alpha;
     st.zpart[g][0] *= alpha;
     st.zpart[g][1] *= alpha;
   }
-  // ---- value weights w = p * scale per [head][group][token], 16-bit fixed point per
-  // (head, group); the zero-point part p * zero is summed in fp32
-  uint16_t* Wq16 = reinterpret_cast<uint16_t*>(wl + L.wts);                 // [GW][ng][BK]
-  uint32_t* PLN = reinterpret_cast<uint32_t*>(wl + L.wts) + GW * ng * BK / 2;  // [GW][ng][64]
-  float wmax[GW][2];
-  float inv[GW][2];
-#pragma unroll
-  for (int g = 0; g < GW; ++g) wmax[g][0] = wmax[g][1] = 0.0f;
-  float wv[4][GW];
-  float vzc[4];  // this block's value zero-points of elements lane + 64 k
+
+  // ---- value weights p * scale / u per [group][head][token] (the codes enter the
+  // MFMA as c * u); the zero-point part p * zero is summed per lane in fp32.
+  // Element lane + 64 k is token 64 (k % 2) + lane of group k / 2.
+  float vzc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int e = lane + 64 * k;
     vzc[k] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < GW; ++g) wv[k][g] = 0.0f;
-    if (e < BK * ng) {
-      const int grp = e / BK;
-      const int kt = (e % BK) / kWave;  // which of the lane's tokens
-      const float vs = h2f(R.vs[k]), vz = h2f(R.vz[k]);
+    if (kWave * k < kBK * ng) {
+      const int grp = k >> 1, kt = k & 1;
+      const float vs = h2f(R.vs[k]) * inv_unit, vz = h2f(R.vz[k]);
       vzc[k] = vz;
+      float* wvp = WV + grp * 4 * kWVP + kHalf * kt + lane;
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        const float pp = p[kt][g];
-        wv[k][g] = pp * vs;
-        if (grp == 0) {
-          st.zpart[g][0] = __builtin_fmaf(pp, vz, st.zpart[g][0]);
-          wmax[g][0] = fmaxf(wmax[g][0], wv[k][g]);
-        } else {
-          st.zpart[g][1] = __builtin_fmaf(pp, vz, st.zpart[g][1]);
-          wmax[g][1] = fmaxf(wmax[g][1], wv[k][g]);
-        }
+      for (int g = 0; g < 4; ++g) {
+        wvp[g * kWVP] = p[kt][g] * vs;
+        st.zpart[g][grp] = __builtin_fmaf(p[kt][g], vz, st.zpart[g][grp]);
       }
     }
   }
-  load_vmeta(R, c, bh, nn, lane, ng);
-  wave_lds_sync();  // the weight area is reused for the quantized weights below
-#pragma unroll
-  for (int g = 0; g < GW; ++g) {
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      if (grp < ng) {
-        const float w = wave_max_uniform(wmax[g][grp]);
-        inv[g][grp] = w * (1.0f / 65535.0f);
-        wmax[g][grp] = w > 0.0f ? 65535.0f * __builtin_amdgcn_rcpf(w) : 0.0f;  // now the scale
-      } else {
-        inv[g][grp] = 0.0f;
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = lane + 64 * k;
-    if (e < BK * ng) {
-      const int grp = e / BK, t = e % BK;
-#pragma unroll
-      for (int g = 0; g < GW; ++g)
-        Wq16[(g * ng + grp) * BK + t] = (uint16_t)__builtin_rintf(wv[k][g] * (grp ? wmax[g][1] : wmax[g][0]));
-    }
-  }
-  wave_lds_sync();
-  // nibble planes: plane kk of a token group holds nibble kk of each token's weight,
-  // token u of the group at bits [4u, 4u+4) (the bit position of its code in a word)
-  for (int hg = 0; hg < GW * ng; ++hg) {
-    const uint16_t* wg = Wq16 + hg * BK;
-    uint32_t plane = 0;
-    if constexpr (VB == 4) {
-      const int tg = lane >> 2, kk = lane & 3;
-      if (tg < BK / 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(wg + 8 * tg);
-        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) plane |= ((d[u >> 1] >> (16 * (u & 1) + 4 * kk)) & 15u) << (4 * u);
-        PLN[hg * 64 + lane] = plane;
-      }
-    } else {
-      const int tg = lane >> 3, par = (lane >> 2) & 1, kk = lane & 3;
-      if (tg < BK / 16) {
-        const uint4 w0 = *reinterpret_cast<const uint4*>(wg + 16 * tg);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(wg + 16 * tg + 8);
-        const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) plane |= ((d[u] >> (16 * par + 4 * kk)) & 15u) << (4 * u);
-        PLN[hg * 64 + lane] = plane;
-      }
-    }
-  }
+  gload_vmeta(R, c, bh, nn, lane, ng);
   wave_lds_sync();
 
-  // ---- values, two heads at a time over the value words held in registers
-  const int ch0 = (4 * lane) % D;
-  const int grp0 = ch0 / G;
+  // ---- values: per token and channel slot one MFMA over the four heads
+  {
+    f4 va[4];  // even-token chains; the odd tokens accumulate into st.acc directly
 #pragma unroll
-  for (int g0 = 0; g0 < GW; g0 += 2) {
-    uint32_t ia[2][4][4];
+    for (int cc = 0; cc < 4; ++cc) va[cc] = f4{0.f, 0.f, 0.f, 0.f};
+    const int grp_l = (4 * (lane & 31)) / G;
+    const float* wvl = WV + (grp_l * 4 + hl) * kWVP + TPW * (lane >> 5);
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg)
+    for (int s = 0; s < GRegs<VB>::NVI; ++s) {
+      const uint32_t words[4] = {R.v[s].x, R.v[s].y, R.v[s].z, R.v[s].w};
+      gload_v(R, s, vnext, lane);
+      float wt[TPW];  // weights of the group's tokens for head lane % 4
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int u4 = 0; u4 < TPW; u4 += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(wvl + 2 * TPW * s + u4);
+        wt[u4] = x.x; wt[u4 + 1] = x.y; wt[u4 + 2] = x.z; wt[u4 + 3] = x.w;
+      }
+      // two channel slots at a time, each with an even-token and an odd-token chain,
+      // so that four independent MFMA chains alternate
 #pragma unroll
-        for (int pl = 0; pl < 4; ++pl) ia[gg][k][pl] = 0;
+      for (int c2 = 0; c2 < 4; c2 += 2) {
+        float cv[2][TPW];  // codes (times u) of the two words' tokens
 #pragma unroll
-    for (int i = 0; i < Sh::NVI; ++i) {
-      const int tgi = i * (256 / D) + (4 * lane) / D;
-      const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const uint32_t w = words[c2 + h2];
+          if constexpr (VB == 4) {
+            const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+            const f2v e0 = cvt_lo(lo), e1 = cvt_hi(lo), o0 = cvt_lo(hi), o1 = cvt_hi(hi);
+            cv[h2][0] = e0.x; cv[h2][2] = e0.y; cv[h2][4] = e1.x; cv[h2][6] = e1.y;
+            cv[h2][1] = o0.x; cv[h2][3] = o0.y; cv[h2][5] = o1.x; cv[h2][7] = o1.y;
+          } else {
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const uint32_t* pb = PLN + ((g0 + gg) * ng + grp0) * 64;
-        if constexpr (VB == 4) {
-          const uint4 pl = *reinterpret_cast<const uint4*>(pb + 4 * tgi);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            ia[gg][k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[gg][k][0], false);
-            ia[gg][k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[gg][k][1], false);
-            ia[gg][k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[gg][k][2], false);
-            ia[gg][k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[gg][k][3], false);
+            for (int sh = 0; sh < 4; ++sh) {  // tokens sh, sh + 4, sh + 8, sh + 12
+              const uint32_t x = (w >> (2 * sh)) & 0x03030303u;
+              const f2v lo2 = cvt_lo(x), hi2 = cvt_hi(x);
+              cv[h2][sh] = lo2.x; cv[h2][sh + 4] = lo2.y; cv[h2][sh + 8] = hi2.x; cv[h2][sh + 12] = hi2.y;
+            }
           }
-        } else {
-          const uint4 pe = *reinterpret_cast<const uint4*>(pb + 8 * tgi);
-          const uint4 po = *reinterpret_cast<const uint4*>(pb + 8 * tgi + 4);
+        }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
-            ia[gg][k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[gg][k][0], false);
-            ia[gg][k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[gg][k][1], false);
-            ia[gg][k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[gg][k][2], false);
-            ia[gg][k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[gg][k][3], false);
-            ia[gg][k][0] = __builtin_amdgcn_udot8(po.x, od, ia[gg][k][0], false);
-            ia[gg][k][1] = __builtin_amdgcn_udot8(po.y, od, ia[gg][k][1], false);
-            ia[gg][k][2] = __builtin_amdgcn_udot8(po.z, od, ia[gg][k][2], false);
-            ia[gg][k][3] = __builtin_amdgcn_udot8(po.w, od, ia[gg][k][3], false);
-          }
+        for (int u = 0; u < TPW; u += 2) {
+          va[c2] = mfma4(wt[u], cv[0][u], va[c2]);
+          va[c2 + 1] = mfma4(wt[u], cv[1][u], va[c2 + 1]);
+          st.acc[c2] = mfma4(wt[u + 1], cv[0][u + 1], st.acc[c2]);
+          st.acc[c2 + 1] = mfma4(wt[u + 1], cv[1][u + 1], st.acc[c2 + 1]);
         }
       }
     }
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const float sc = grp0 == 0 ? inv[g0 + gg][0] : inv[g0 + gg][1];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t tot = ia[gg][k][0] + (ia[gg][k][1] << 4) + (ia[gg][k][2] << 8) + (ia[gg][k][3] << 12);
-        st.acc[g0 + gg][k] = __builtin_fmaf((float)tot, sc, st.acc[g0 + gg][k]);
-      }
-    }
+    for (int cc = 0; cc < 4; ++cc) st.acc[cc] += va[cc];
   }
-  // ---- value outliers: p * (x - zero) scattered into the per-head channel array
+
+  // ---- value outliers: p * (x - zero) scattered into the per-head channel array in
+  // fixed point; merged at the next block's softmax (or the item's end)
   if constexpr (OUTL) {
+    float cr[2][KO][4];
+    int col[2][KO];
+    float cmax[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < TPL; ++k) {
-      const uint32_t vals = C.vv[k];
+    for (int k = 0; k < 2; ++k) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = (int)((C.vc[k] >> (8 * q)) & 0xffu);
-        const int grp = col / G;
-        const float dl = h2f((uint16_t)(vals >> (16 * q))) - (grp ? vzc[2 + k] : vzc[k]);
+      for (int qq = 0; qq < KO; ++qq) {
+        col[k][qq] = (int)((C.vc[k] >> (8 * qq)) & 0xffu);
+        const float dl = h2f((uint16_t)(C.vv[k] >> (16 * qq))) - (col[k][qq] >= G ? vzc[2 + k] : vzc[k]);
 #pragma unroll
-        for (int g = 0; g < GW; ++g) atomicAdd(VCR + g * D + col, p[k][g] * dl);
+        for (int g = 0; g < 4; ++g) {
+          cr[k][qq][g] = p[k][g] * dl;
+          cmax[g] = fmaxf(cmax[g], fabsf(cr[k][qq][g]));
+        }
       }
     }
-    load_csr_tok<BK, KO>(C, c, bh, nn, lane);
-    // merged into the accumulators at the next block's softmax (or the item's end), so
-    // that the atomics complete in the shadow of the next block's scores
-  }
+    load_csr_tok<kBK, KO>(C, c, bh, nn, lane);
 #pragma unroll
-  for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vnext, lane);
+    for (int g = 0; g < 4; ++g) {
+      const int sh = vcorr_shift(wave_max_uniform(cmax[g]));
+      if (lane == 0) VCI[4 * kD + g] = sh;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int qq = 0; qq < KO; ++qq) atomicAdd(VCI + g * kD + col[k][qq], vcorr_fixed(cr[k][qq][g], sh));
+    }
+  }
   wave_lds_sync();
 }
 
-// Item = (b, kv-head, head set, split): the wave serves GW query heads of the group.
-template <int D, int BK, int KB, int VB, int GW, int KO>
+// Item = (b, kv-head, head set, split): the wave serves GW (4 or 2) query heads of the
+// group; with 2 the MFMA rows of heads 2 and 3 carry zero weights.
+template <int VB, int GW, int KO>
 __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
                                                                    int64_t nitems) {
-  using Sh = GShape<D, BK, KB, VB>;
   constexpr int kNT = kGqaWaves * 64;
+  constexpr bool OUTL = KO > 0;
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H, nsets = gq / GW;
-  const int G = c.cfg.v_group, ng = D / G;
-  constexpr bool OUTL = KO > 0;
-  const int64_t nfull = c.length / BK;
+  const int G = c.cfg.v_group, ng = kD / G;
+  const int64_t nfull = c.length / kBK;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
-  const uint32_t koff = (uint32_t)(ts * Sh::RK + r * (Sh::KW * 4));
 
   float* table = lds;
-  for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += kNT) {
-    const int j = idx / Sh::HALF, i = idx % Sh::HALF;
-    *reinterpret_cast<float2*>(table + j * Sh::TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
+  for (int idx = threadIdx.x; idx < kBK * kHalf; idx += kNT) {
+    const int j = idx / kHalf, i = idx % kHalf;
+    *reinterpret_cast<float2*>(table + j * kTP + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
   }
-  const GLds L = gqa_lds(D, BK, GW, ng, OUTL);
-  float* wl = lds + BK * Sh::TPITCH + wave * L.total;
+  const GLds L = gqa_lds(ng, OUTL);
+  float* wl = lds + kBK * kTP + wave * L.total;
   if (OUTL)
-    for (int k = lane; k < GW * D; k += kWave) wl[L.vcorr + k] = 0.0f;
+    for (int k = lane; k < 4 * kD + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
   __syncthreads();
 
-  const float unit = cvt_lo(1u).x;  // fp8 value of the byte 1, a power of two
-  const float inv_unit = 1.0f / unit;
+  const float inv_unit = 1.0f / cvt_lo(1u).x;  // the fp8 value of the byte 1 is a power of two
   const int64_t total_waves = (int64_t)gridDim.x * kGqaWaves;
   for (int64_t item = (int64_t)blockIdx.x * kGqaWaves + wave; item < nitems; item += total_waves) {
     const int split = (int)(item % S);
@@ -474,72 +445,77 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     const int b = (int)(bh / H);
     const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
 
-    // query weights of pair `lane` for each head: scale * conj(q_i) e^{-i f_i q_pos} (fp64)
-    float wq_r[GW], wq_i[GW];
-#pragma unroll
-    for (int g = 0; g < GW; ++g) { wq_r[g] = 0.0f; wq_i[g] = 0.0f; }
-    if (lane < Sh::HALF) {
-      const double f = pow((double)c.cfg.rope_theta, -(2.0 * lane) / (double)D);
+    // query weights of pair `lane` per head: scale * conj(q_g,i) e^{-i f_i q_pos} (fp64)
+    float wq_r[4], wq_i[4];
+    {
+      const double f = pow((double)c.cfg.rope_theta, -(2.0 * lane) / (double)kD);
       double sn, cs;
       sincos((double)q_pos * f, &sn, &cs);
-      const double scl = (double)kLog2e / sqrt((double)D);
+      const double scl = (double)kLog2e / sqrt((double)kD);
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        const int hq = h * gq + set * GW + g;
-        const uint16_t* qv = q + ((int64_t)b * Hq + hq) * D;
-        const double qa = (double)h2f(qv[lane]), qb = (double)h2f(qv[lane + Sh::HALF]);
-        wq_r[g] = (float)(scl * (qa * cs - qb * sn));
-        wq_i[g] = (float)(-scl * (qa * sn + qb * cs));
+      for (int g = 0; g < 4; ++g) {
+        wq_r[g] = 0.0f;
+        wq_i[g] = 0.0f;
+        if (g < GW) {
+          const int hq = h * gq + set * GW + g;
+          const uint16_t* qv = q + ((int64_t)b * Hq + hq) * kD;
+          const double qa = (double)h2f(qv[lane]), qb = (double)h2f(qv[lane + kHalf]);
+          wq_r[g] = (float)(scl * (qa * cs - qb * sn));
+          wq_i[g] = (float)(-scl * (qa * sn + qb * cs));
+        }
       }
+      *reinterpret_cast<float4*>(wl + L.wq + 8 * lane) = make_float4(wq_r[0], wq_i[0], wq_r[1], wq_i[1]);
+      *reinterpret_cast<float4*>(wl + L.wq + 8 * lane + 4) = make_float4(wq_r[2], wq_i[2], wq_r[3], wq_i[3]);
+      wave_lds_sync();
     }
-    GState<GW> st;
+    GState st;
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
+    for (int g = 0; g < 4; ++g) {
       st.m[g] = -__builtin_inff();
       st.lpart[g] = 0.0f;
-      st.acc[g][0] = st.acc[g][1] = st.acc[g][2] = st.acc[g][3] = 0.0f;
       st.zpart[g][0] = st.zpart[g][1] = 0.0f;
+      st.acc[g] = f4{0.f, 0.f, 0.f, 0.f};
     }
 
-    GRegs<D, BK, KB, VB> R;
+    GRegs<VB> R;
     CsrTok C;
     if (n0 < n1) {
-      load_kmeta(R, c, bh, n0, lane, 0);
-      load_vmeta(R, c, bh, n0, lane, ng);
-      if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n0, lane);
-      const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
-      const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
+      gload_kmeta(R, c, bh, n0, lane);
+      gload_vmeta(R, c, bh, n0, lane, ng);
+      if constexpr (OUTL) load_csr_tok<kBK, KO>(C, c, bh, n0, lane);
+      const uint8_t* kb0 = gk_block(c, bh, n0);
+      const uint8_t* vb0 = gv_block<VB>(c, bh, n0);
 #pragma unroll
-      for (int it = 0; it < Sh::NIT / 2; ++it) load_k_slot(R, it, it, kb0, koff);
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
+        for (int qq = 0; qq < 4; ++qq) gload_k(R, hf, qq, kb0, lane);
+#pragma unroll
+      for (int s = 0; s < GRegs<VB>::NVI; ++s) gload_v(R, s, vb0, lane);
     }
     for (int64_t n = n0; n < n1; ++n)
-      gqa_block<D, BK, KB, VB, GW, KO>(R, C, st, wl, L, table, wq_r, wq_i, unit, inv_unit, lane, ts, r, G, ng, c, bh,
-                                         n, n + 1 < n1, koff);
+      gqa_block<VB, KO>(R, C, st, wl, L, table, inv_unit, lane, G, ng, c, bh, n, n + 1 < n1);
 
-    if (OUTL) {
-      wave_lds_sync();
-#pragma unroll
-      for (int g = 0; g < GW; ++g) merge_vcorr<D>(wl + L.vcorr + g * D, st.acc[g], lane);  // the item's last block
+    if (OUTL) {  // the item's last block of value corrections
+      merge_vcorr_heads(reinterpret_cast<int*>(wl + L.vcorr), st, lane);
       wave_lds_sync();
     }
-    // ---- finish the item: reduce across lanes and write (m, l, o) of each head's split
+    // ---- finish the item: the two token halves of each channel, then (m, l, o) per head
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) st.acc[cc][g] += __shfl_xor(st.acc[cc][g], 32, kWave);
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       const float l = wave_sum(st.lpart[g]);
       const float z0 = wave_sum(st.zpart[g][0]);
       const float z1 = wave_sum(st.zpart[g][1]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        for (int msk = Sh::CHL; msk < kWave; msk <<= 1) st.acc[g][k] += __shfl_xor(st.acc[g][k], msk, kWave);
       const int hq = h * gq + set * GW + g;
-      float* dst = ws + (((int64_t)b * Hq + hq) * S + split) * (D + 2);
-      if (lane < Sh::CHL) {
+      float* dst = ws + (((int64_t)b * Hq + hq) * S + split) * (kD + 2);
+      if (lane < 32) {
         const int ch0 = 4 * lane;
         const float z = (ch0 / G) == 0 ? z0 : z1;
         *reinterpret_cast<float4*>(dst + 2 + ch0) =
-            make_float4(st.acc[g][0] + z, st.acc[g][1] + z, st.acc[g][2] + z, st.acc[g][3] + z);
+            make_float4(st.acc[0][g] + z, st.acc[1][g] + z, st.acc[2][g] + z, st.acc[3][g] + z);
       }
       if (lane == 0) {
         dst[0] = st.m[g];
@@ -549,23 +525,22 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
   }
 }
 
-template <int D, int BK, int KB, int VB, int GW, int KO>
+template <int VB, int GW, int KO>
 hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
                             int cus) {
-  using Sh = GShape<D, BK, KB, VB>;
-  const int ng = c.cfg.head_dim / c.cfg.v_group;
-  const GLds L = gqa_lds(D, BK, GW, ng, KO > 0);
-  const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kGqaWaves * L.total) * sizeof(float);
+  const int ng = kD / c.cfg.v_group;
+  const GLds L = gqa_lds(ng, KO > 0);
+  const size_t bytes = ((size_t)kBK * kTP + (size_t)kGqaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<D, BK, KB, VB, GW, KO>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int gq = c.cfg.q_heads / c.cfg.kv_heads;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * (gq / GW) * S;
   int64_t grid = (nitems + kGqaWaves - 1) / kGqaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_gqa_kernel<D, BK, KB, VB, GW, KO>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes,
-                     s, c, q, q_pos, ws, S, nitems);
+  hipLaunchKernelGGL((decode_gqa_kernel<VB, GW, KO>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes, s, c, q,
+                     q_pos, ws, S, nitems);
   return hipGetLastError();
 }
 
@@ -578,15 +553,17 @@ hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ko = host_kout(g);
   const int gq = g.q_heads / g.kv_heads;
   const int ng = g.head_dim / g.v_group;
-  if (gq < 2 || gq % 2 || g.k_mode != 0 || g.k_bits != 4 || (ko != 0 && ko != 2) || ng > 2 ||
-      g.k_block * ng > 256 || g.head_dim != 128 || g.k_block != 128)
+  if (gq < 2 || gq % 2 || g.k_mode != 0 || g.k_bits != 4 || ko > 2 || ng > 2 || g.head_dim != kD ||
+      g.k_block != kBK || (g.v_bits != 4 && g.v_bits != 2))
     return hipErrorNotSupported;
-  const int KB = g.k_bits, VB = g.v_bits;
-#define KVQ_GQA(kb, vb, gw)                                                                        \
-  if (KB == kb && VB == vb && (gq % 4 == 0) == (gw == 4))                                          \
-    return ko == 2 ? launch_gqa_typed<128, 128, kb, vb, gw, 2>(c, q, q_pos, ws, S, s, cus)         \
-                   : launch_gqa_typed<128, 128, kb, vb, gw, 0>(c, q, q_pos, ws, S, s, cus);
-  KVQ_GQA(4, 4, 4) KVQ_GQA(4, 2, 4) KVQ_GQA(4, 4, 2) KVQ_GQA(4, 2, 2)
+  const bool four = gq % 4 == 0;
+#define KVQ_GQA(vb, gw)                                                                       \
+  if (g.v_bits == vb && four == (gw == 4)) {                                                  \
+    if (ko == 2) return launch_gqa_typed<vb, gw, 2>(c, q, q_pos, ws, S, s, cus);              \
+    if (ko == 1) return launch_gqa_typed<vb, gw, 1>(c, q, q_pos, ws, S, s, cus);              \
+    return launch_gqa_typed<vb, gw, 0>(c, q, q_pos, ws, S, s, cus);                           \
+  }
+  KVQ_GQA(4, 4) KVQ_GQA(2, 4) KVQ_GQA(4, 2) KVQ_GQA(2, 2)
 #undef KVQ_GQA
   return hipErrorNotSupported;
 }

@@ -54,7 +54,7 @@ __host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut) {
   m.wts = o; o += (lut ? 2 : outl ? 10 : 6) * (D / 2);
   m.s = o; o += BK;                           // scores of the block's tokens
   m.ps = o; o += BK + 128;                    // quantized weights [2][BK] (u16) + nibble planes [2][64]
-  m.vcorr = o; o += outl ? D : 0;             // value outlier corrections [D]
+  m.vcorr = o; o += outl ? D + 4 : 0;         // value outlier corrections [D] (int), then the scale shift
   m.total = o;
   return m;
 }
@@ -130,7 +130,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   float* wZB = wZA + Sh::HALF;
   float* Sc = wl + L.s;
   float* PS = wl + L.ps;
-  float* VCR = wl + L.vcorr;
+  int* VCI = reinterpret_cast<int*>(wl + L.vcorr);
 
   // ---- block weights, one rotary pair per lane
   if (LUT && lane < Sh::HALF) {
@@ -296,7 +296,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     }
     mloc = fmaxf(mloc, p[k]);
   }
-  if constexpr (OUTL) merge_vcorr<D>(VCR, st.acc, lane);  // the previous block's
+  if constexpr (OUTL) merge_vcorr<D>(VCI, VCI[D], st.acc, lane);  // the previous block's
   {
     const float mnew = fmaxf(st.m, wave_max_uniform(mloc));
     const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
@@ -438,16 +438,26 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   // the accumulators at the next block's softmax (or the item's end), so that the
   // atomics complete in the shadow of the next block's scores
   if constexpr (OUTL) {
+    float cr[TPL][KO];
+    int col[TPL][KO];
+    float cmax = 0.0f;
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
 #pragma unroll
       for (int q = 0; q < KO; ++q) {
-        const int col = (int)((C.vc[k] >> (8 * q)) & 0xffu);
-        const float dl = h2f((uint16_t)(C.vv[k] >> (16 * q))) - (col >= G ? vzc[TPL + k] : vzc[k]);
-        atomicAdd(VCR + col, p[k] * dl);
+        col[k][q] = (int)((C.vc[k] >> (8 * q)) & 0xffu);
+        const float dl = h2f((uint16_t)(C.vv[k] >> (16 * q))) - (col[k][q] >= G ? vzc[TPL + k] : vzc[k]);
+        cr[k][q] = p[k] * dl;
+        cmax = fmaxf(cmax, fabsf(cr[k][q]));
       }
     }
     load_csr_tok<BK, KO>(C, c, bh, nn, lane);
+    const int vsh = vcorr_shift(wave_max_uniform(cmax));
+    if (lane == 0) VCI[D] = vsh;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k)
+#pragma unroll
+      for (int q = 0; q < KO; ++q) atomicAdd(VCI + col[k][q], vcorr_fixed(cr[k][q], vsh));
   }
 #pragma unroll
   for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vnext, lane);
@@ -512,7 +522,8 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
                                           c, bh, n, n + 1 < n1, koff);
   if (OUTL) {
     wave_lds_sync();
-    merge_vcorr<D>(wl + L.vcorr, st.acc, lane);  // the item's last block
+    int* vci = reinterpret_cast<int*>(wl + L.vcorr);
+    merge_vcorr<D>(vci, vci[D], st.acc, lane);  // the item's last block
     wave_lds_sync();
   }
 
@@ -564,7 +575,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
   const MLds L = mha_lds(D, BK, OUTL, false);
   float* wl = lds + BK * Sh::TPITCH + wave * L.total;
   if (OUTL)
-    for (int k = lane; k < D; k += kWave) wl[L.vcorr + k] = 0.0f;
+    for (int k = lane; k < D + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
   __syncthreads();
 
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
