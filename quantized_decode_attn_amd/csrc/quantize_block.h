@@ -112,6 +112,43 @@ __device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rank, 
   *out_below = r.sh_below;
 }
 
+// The bin holding the element of rank `rank_top` counted from the largest (0-based),
+// scanning from the top bin down; returns the bin and the count of elements in the
+// bins above it.  Bins below the answer need not be counted.  Wave 0 scans, the
+// result is broadcast through LDS.
+__device__ inline void find_bin_top(const uint32_t* hist, int nbins, uint32_t rank_top, int* out_bin,
+                                    uint32_t* out_above, Red& r) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = nbins / kWave;
+    const int hi = nbins - lane * per;  // lane covers bins [hi - per, hi), top lanes first
+    uint32_t local = 0;
+    for (int k = 1; k <= per; ++k) local += hist[hi - k];
+    uint32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      uint32_t o = (uint32_t)__shfl_up((int)incl, d, kWave);
+      if (lane >= d) incl += o;
+    }
+    const uint64_t over = __ballot(incl > rank_top);
+    const int first = __ffsll((unsigned long long)over) - 1;
+    if (lane == first) {
+      uint32_t above = incl - local;
+      int b = hi - 1;
+      for (int k = 1; k <= per; ++k) {
+        const uint32_t h = hist[hi - k];
+        if (above + h > rank_top) { b = hi - k; break; }
+        above += h;
+      }
+      r.sh_bin = b;
+      r.sh_below = above;
+    }
+  }
+  __syncthreads();
+  *out_bin = r.sh_bin;
+  *out_above = r.sh_below;
+}
+
 // ---------------------------------------------------------------- cross-lane min/max
 // One v_min_f32 / v_max_f32 with a DPP source (the s_nop covers the VALU-write to
 // DPP-read hazard).  Written out because the compiler otherwise brackets every
@@ -222,9 +259,11 @@ __device__ __forceinline__ uint32_t code_exact(float d, float z, float s, int L,
 
 // ---------------------------------------------------------------- phase 1: staging
 // Rows from the old tail (tokens below old_len) or from the new input.
+// Returns the largest 15-bit magnitude among the values this thread staged (chunks
+// tid + i * kThreads, the order the clip's histogram pass reads them in).
 template <int D, int BK>
-__device__ __forceinline__ void stage_tile(uint16_t* tile, const uint16_t* tail, const uint16_t* src_new,
-                                           int64_t bh, int64_t t0, int64_t old_len, int64_t n_new) {
+__device__ __forceinline__ uint32_t stage_tile(uint16_t* tile, const uint16_t* tail, const uint16_t* src_new,
+                                               int64_t bh, int64_t t0, int64_t old_len, int64_t n_new) {
   constexpr int P = D + 8;
   constexpr int kPerThread = BK * D / 8 / kThreads;
   static_assert(kPerThread * kThreads * 8 == BK * D, "tile split");
@@ -239,22 +278,30 @@ __device__ __forceinline__ void stage_tile(uint16_t* tile, const uint16_t* tail,
                                       : src_new + (bh * n_new + (t - old_len)) * D;
     v[i] = *reinterpret_cast<const uint4*>(row + part * 8);
   }
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int idx = threadIdx.x + i * kThreads;
     const int j = idx / (D / 8), part = idx % (D / 8);
     *reinterpret_cast<uint4*>(&tile[j * P + part * 8]) = v[i];
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, w[k] & 0x7fff7fffu));
   }
+  return m2.x > m2.y ? m2.x : m2.y;
 }
 
 // ---------------------------------------------------------------- phase 2: outliers
 // 16 lanes per token row, D/16 columns per lane; the ko largest keys
 // (|x| bits << 8 | 255 - column, unique within a row) are extracted one at a time
 // by row maxima.  Outliers are written to the CSR and either marked in the tile at
-// once (MARK_NOW) or remembered in `ocol` for marking after the clip threshold.
+// once (MARK_NOW) or after the clip threshold from `ocol`; the CSR slice is staged in
+// `ocol`/`oval` and written out by consecutive threads.
 template <int D, int BK, bool MARK_NOW>
-__device__ __forceinline__ void block_outliers(uint16_t* tile, uint8_t* ocol, int32_t* rowptr, uint8_t* col_out,
-                                               uint16_t* val_out, int64_t bh, int64_t T, int64_t t0, int ko) {
+__device__ __forceinline__ void block_outliers(uint16_t* tile, uint8_t* ocol, uint16_t* oval, int32_t* rowptr,
+                                               uint8_t* col_out, uint16_t* val_out, int64_t bh, int64_t T, int64_t t0,
+                                               int ko) {
   constexpr int P = D + 8;
   constexpr int kPer = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane & 15;
@@ -301,19 +348,27 @@ __device__ __forceinline__ void block_outliers(uint16_t* tile, uint8_t* ocol, in
           if (q < ko && cols[q - 1] > cols[q]) {
             const int t = cols[q]; cols[q] = cols[q - 1]; cols[q - 1] = t;
           }
-      const int64_t t = t0 + j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (r < ko) {
-          col_out[(bh * T + t) * ko + r] = (uint8_t)cols[r];
-          val_out[(bh * T + t) * ko + r] = tile[j * P + cols[r]];
+          ocol[j * 4 + r] = (uint8_t)cols[r];
+          oval[j * 4 + r] = tile[j * P + cols[r]];
           if constexpr (MARK_NOW) tile[j * P + cols[r]] = kMarkNaN;
-          else ocol[j * 4 + r] = (uint8_t)cols[r];
         }
       }
-      rowptr[bh * (T + 1) + t + 1] = (int32_t)((t + 1) * ko);
-      if (t == 0) rowptr[bh * (T + 1)] = 0;
     }
+  }
+  __syncthreads();
+  // the block's CSR slice, written by consecutive threads
+  for (int idx = threadIdx.x; idx < BK * ko; idx += kThreads) {
+    const int j = idx / ko, r = idx % ko;
+    col_out[(bh * T + t0) * ko + idx] = ocol[j * 4 + r];
+    val_out[(bh * T + t0) * ko + idx] = oval[j * 4 + r];
+  }
+  for (int j = threadIdx.x; j < BK; j += kThreads) {
+    const int64_t t = t0 + j;
+    rowptr[bh * (T + 1) + t + 1] = (int32_t)((t + 1) * ko);
+    if (t == 0) rowptr[bh * (T + 1)] = 0;
   }
 }
 
@@ -335,7 +390,12 @@ struct ClipSmem {
 };
 
 template <int D, int BK>
-__device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& cs, Red& red, float quantile) {
+// `group_max`: the largest magnitude among the values this thread staged.  Every
+// thread's values form a disjoint group, so at least kThreads values are >= the
+// smallest group maximum m; when the target's rank counted from the top is below
+// kThreads, the target is >= m, and the histogram pass skips every bin below m's.
+__device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& cs, Red& red, float quantile,
+                                                uint32_t group_max) {
   constexpr int P = D + 8;
   constexpr int NEL = BK * D;
   constexpr int kChunks = NEL / 8;
@@ -343,26 +403,29 @@ __device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& 
   const double pos = (double)quantile * (double)(NEL - 1);
   const int64_t kr = (int64_t)floor(pos);
   const double frac = pos - (double)kr;
+  const uint32_t rank_top = (uint32_t)(NEL - 1 - kr);
   auto chunk = [&](int idx) -> uint4 {
     const int j = idx / (D / 8), part = idx % (D / 8);
     return *reinterpret_cast<const uint4*>(&tile[j * P + part * 8]);
   };
-  // pass 1: top 8 of the 15 magnitude bits
   for (int i = tid; i < 256; i += kThreads) cs.hist[i] = 0;
+  const uint32_t low_bin = rank_top < (uint32_t)kThreads ? block_min_u32(group_max, red) >> 7 : 0u;
   __syncthreads();
+  // pass 1: top 8 of the 15 magnitude bits, bins >= low_bin only
   for (int idx = tid; idx < kChunks; idx += kThreads) {
     const uint4 w = chunk(idx);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t key = (ws[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
-      atomicAdd(&cs.hist[key >> 7], 1u);
+      if ((key >> 7) >= low_bin) atomicAdd(&cs.hist[key >> 7], 1u);
     }
   }
   __syncthreads();
   int bin1;
-  uint32_t below1;
-  find_bin(cs.hist, 256, (uint32_t)kr, &bin1, &below1, red);
+  uint32_t above1;
+  find_bin_top(cs.hist, 256, rank_top, &bin1, &above1, red);
+  const uint32_t below1 = (uint32_t)NEL - above1 - cs.hist[bin1];
   __syncthreads();
   // pass 2: low 7 bits inside the selected bin
   for (int i = tid; i < 256; i += kThreads) cs.hist[i] = 0;
@@ -382,27 +445,35 @@ __device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& 
   find_bin(cs.hist, 128, (uint32_t)kr - below1, &bin2, &below2, red);
   const uint32_t vk = ((uint32_t)bin1 << 7) | (uint32_t)bin2;
   // the next order statistic: vk again if it repeats past rank kr, else the smallest
-  // magnitude above vk
-  uint32_t le = 0, gt_min = 0xffffffffu;
-  for (int idx = tid; idx < kChunks; idx += kThreads) {
-    const uint4 w = chunk(idx);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // magnitude above vk.  Every sub-bin of bin1 is one magnitude, so that is the next
+  // occupied sub-bin; only when bin1 holds nothing above vk does a pass over the tile
+  // find it.
+  uint32_t vk1 = vk;
+  if (kr + 1 < NEL && below1 + below2 + cs.hist[bin2] < (uint32_t)(kr + 2)) {
+    const uint32_t cand = (tid < 128 && tid > bin2 && cs.hist[tid] != 0u) ? (uint32_t)tid : 0xffffffffu;
+    const uint32_t nb = block_min_u32(cand, red);
+    if (nb != 0xffffffffu) {
+      vk1 = ((uint32_t)bin1 << 7) | nb;
+    } else {
+      uint32_t gt_min = 0xffffffffu;
+      for (int idx = tid; idx < kChunks; idx += kThreads) {
+        const uint4 w = chunk(idx);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t key = (ws[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
-      le += key <= vk;
-      gt_min = key > vk ? min(gt_min, key) : gt_min;
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t key = (ws[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+          gt_min = key > vk ? min(gt_min, key) : gt_min;
+        }
+      }
+      vk1 = block_min_u32(gt_min, red);
     }
   }
-  le = block_sum_u32(le, red);
-  gt_min = block_min_u32(gt_min, red);
   if (tid == 0) {
     float t;
     const double v0 = (double)h2f((uint16_t)vk);
     if (kr + 1 >= NEL) {
       t = (float)v0;
     } else {
-      const uint32_t vk1 = le >= (uint32_t)(kr + 2) ? vk : gt_min;
       const double v1 = (double)h2f((uint16_t)vk1);
       const double diff = v1 - v0;
       const double prod = frac * diff;
@@ -437,6 +508,7 @@ struct KeySmem {
     } out;
   } u;
   uint8_t ocol[BK * 4];
+  uint16_t oval[BK * 4];
   ClipSmem clip;
   Red red;
 };
@@ -448,28 +520,29 @@ struct ValueSmem {
     ValueMeta<D, BK> meta;
   } u;
   uint8_t ocol[BK * 4];
+  uint16_t oval[BK * 4];
   ClipSmem clip;
   Red red;
 };
 
 // Steps 1, 2 and 2b for one tile; returns the clip threshold (0 without clipping).
 template <int D, int BK, bool OUTL, bool CLIP>
-__device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, ClipSmem& cs, Red& red,
+__device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uint16_t* oval, ClipSmem& cs, Red& red,
                                               const kvq_cache& c, bool is_key, const uint16_t* src_new,
                                               int64_t bh, int64_t n, int64_t old_len, int64_t n_new) {
   const int64_t T = c.cfg.capacity;
   const int64_t t0 = n * BK;
-  stage_tile<D, BK>(tile, is_key ? c.k_tail : c.v_tail, src_new, bh, t0, old_len, n_new);
+  const uint32_t group_max = stage_tile<D, BK>(tile, is_key ? c.k_tail : c.v_tail, src_new, bh, t0, old_len, n_new);
   __syncthreads();
   const int ko = kout_of(c.cfg);
   if constexpr (OUTL) {
-    block_outliers<D, BK, !CLIP>(tile, ocol, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
+    block_outliers<D, BK, !CLIP>(tile, ocol, oval, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
                                  is_key ? c.k_val : c.v_val, bh, T, t0, ko);
     __syncthreads();
   }
   float thr = 0.0f;
   if constexpr (CLIP) {
-    thr = clip_threshold<D, BK>(tile, cs, red, c.cfg.clip_quantile);
+    thr = clip_threshold<D, BK>(tile, cs, red, c.cfg.clip_quantile, group_max);
     if constexpr (OUTL) {
       mark_outliers<D, BK>(tile, ocol, ko);
       __syncthreads();
@@ -532,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
   const float Lf = (float)L;
 
   const float thr =
-      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
+      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
   __syncthreads();
 
   const bool active = NA * NTG == kThreads || tid < NA * NTG;
@@ -767,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
   const int lpg = G / CW;
 
   const float thr =
-      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
+      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
   __syncthreads();
 
   const bool active = NCC * NTG == kThreads || tid < NCC * NTG;
