@@ -219,9 +219,9 @@ def main():
     log("decode  %.1f us  %.1f GB/s (%.1f%% of 8 TB/s)" % (dec_ms.mean() * 1e3, dec_gbps, dec_gbps / 80))
     log("append  %.1f us  %.1f GB/s  %.3g tokens/s" % (app_ms.mean() * 1e3, app_gbps, app_tps))
 
-    dec_hash = source_hash(["decode_mha.hip", "decode.hip", "kvq_device.h"])
+    dec_hash = source_hash(["decode_mha.hip", "decode_common.h", "decode.hip", "kvq_device.h", "kvq_internal.h"])
     app_hash = source_hash(["quantize.hip", "quantize_block.h", "quantize_keys.hip", "quantize_keys_lut.hip",
-                            "quantize_values.hip", "kvq_device.h"])
+                            "quantize_values.hip", "kvq_device.h", "kvq_internal.h"])
     tr_dec = measured_traffic("decode", dec_hash)
     tr_app = measured_traffic("append", app_hash)
     rec = {
