@@ -53,6 +53,16 @@ SMALL = {
                          [100, 177]),
     "lut2_v2_d128": (synth.config("c3", batch=1, q_heads=3, kv_heads=3, k_bits=2,
                                   tokens=3 * 128 + 9, capacity=512), None),
+    # grouped-query: two heads per kv head (two of the four matrix rows carry zero weights)
+    "gqa2_csr": (synth.config("c2", batch=1, q_heads=6, kv_heads=3, tokens=3 * 128 + 40,
+                              capacity=512), None),
+    # grouped-query: eight heads per kv head (two head sets), 2-bit values in groups of 64
+    "gqa8_v2_g64": (synth.config("c2", batch=2, q_heads=16, kv_heads=2, v_bits=2, v_group=64,
+                                 outlier_pct=0, inject=False, tokens=4 * 128 + 3, capacity=640),
+                    [200, 315]),
+    # one head per kv head with one outlier per vector (head_dim 64: ceil(0.64) = 1)
+    "mha_csr1_d64": (synth.config("c0", batch=2, outlier_pct=1, inject=True, tokens=5 * 64 + 30,
+                                  capacity=384), [64, 286]),
 }
 
 
@@ -108,7 +118,7 @@ def test_small_cases_bitwise_and_decode(case):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("case", ["clip_csr_append", "lut3_v2"])
+@pytest.mark.parametrize("case", ["clip_csr_append", "lut3_v2", "gqa_csr_inject"])
 def test_split_count_invariance_and_determinism(case):
     cfg, _ = SMALL[case]
     say("case", case)
