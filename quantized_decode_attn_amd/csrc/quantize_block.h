@@ -233,13 +233,13 @@ __device__ __forceinline__ void quotient_bounds(float z, float r, float Lf, floa
 // to a rounding boundary.  The quotient is clamped to [a, b] = [0, L], or with
 // clipping to the quotients of -thr and thr.
 template <bool OUTL, bool CLIP>
-__device__ __forceinline__ float code_fast(float d, float z, float r, float a, float b, bool& tie) {
+__device__ __forceinline__ float code_fast(float d, float z, float r, float a, float b, bool& near, float& qc) {
   const float x = d - z;
-  float qc = x * r;
+  qc = x * r;
   qc = __builtin_amdgcn_fmed3f(qc, a, b);
   if constexpr (OUTL) qc = (d != d) ? 0.0f : qc;
   const float rr = __builtin_rintf(qc);
-  tie |= fabsf(qc - rr) > kTieMargin;
+  near = fabsf(qc - rr) > kTieMargin;
   return rr;
 }
 
@@ -249,6 +249,29 @@ __device__ __forceinline__ uint32_t put_byte(float c, uint32_t k, uint32_t w) {
 }
 
 // Exact code of one element (the fallback).
+// Exact code of an element whose fast quotient qc lies within 2^-17 of the half-integer
+// h = floor(qc) + 1/2, without a divide: the code is rint of the IEEE quotient
+// q = fl(num / s), num = fp32(d - z).  The residual r = num - h s is exact (h s has at
+// most 17 significant bits and cancels with num), and q == h exactly when
+// |r| <= s ulp(h) / 2 (h has few mantissa bits, so ties of the quotient's rounding go to
+// h); otherwise q lies on r's side of h.  A quotient equal to h rounds half to even.
+// (h = 1/2, the one power of two, rounds down on a tie and on the side below, so the
+// narrower lower half-ulp there does not matter.)
+template <bool OUTL, bool CLIP>
+__device__ __forceinline__ float code_near(float d, float z, float s, float qc, float Lf, float thr) {
+  if constexpr (OUTL)
+    if (d != d) return 0.0f;
+  if constexpr (CLIP) d = fminf(fmaxf(d, -thr), thr);
+  if (s == 0.0f) return 0.0f;
+  const float num = d - z;
+  const float k = __builtin_floorf(qc);
+  const float h = k + 0.5f;
+  const float r = __builtin_fmaf(-h, s, num);
+  const float hu = __builtin_amdgcn_ldexpf(s, __builtin_amdgcn_frexp_expf(h) - 25);  // s ulp(h) / 2
+  const float even = k + (float)((int)k & 1);
+  const float code = r > hu ? k + 1.0f : (r < -hu ? k : even);
+  return fminf(fmaxf(code, 0.0f), Lf);
+}
 template <bool OUTL, bool CLIP>
 __device__ __forceinline__ uint32_t code_exact(float d, float z, float s, int L, float thr) {
   if constexpr (OUTL)
@@ -556,12 +579,18 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uin
 // of the cell sits at bits e KB of the word.
 template <int KB, bool OUTL, bool CLIP>
 __device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* zq, const float* rq, const float* aq,
-                                          const float* bq, uint32_t* w, bool& tie) {
+                                          const float* bq, const float* sq, int L, float thr, uint32_t* w) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     float cf[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cf[q] = code_fast<OUTL, CLIP>(x[u][q], zq[q], rq[q], aq[q], bq[q], tie);
+    for (int q = 0; q < 8; ++q) {
+      bool near;
+      float qc;
+      cf[q] = code_fast<OUTL, CLIP>(x[u][q], zq[q], rq[q], aq[q], bq[q], near, qc);
+      // rare: a quotient this close to a rounding boundary is decided exactly
+      if (near) cf[q] = code_near<OUTL, CLIP>(x[u][q], zq[q], sq[q], qc, (float)L, thr);
+    }
     uint32_t wu = 0;
     if constexpr (KB == 4) {
 #pragma unroll
@@ -695,22 +724,11 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
 #pragma unroll
         for (int q = 0; q < 8; ++q) { aq[q] = 0.0f; bq[q] = Lf; }
       }
-      bool tie = false;
-      if (kb == 4) key_codes<4, OUTL, CLIP>(x, zq, rq, aq, bq, w, tie);
-      else if (kb == 2) key_codes<2, OUTL, CLIP>(x, zq, rq, aq, bq, w, tie);
-      else key_codes<3, OUTL, CLIP>(x, zq, rq, aq, bq, w, tie);
-      if (tie) {  // rare: this lane's cell again with the correctly rounded divide
-        float sq[8];
-        ld4(M.s, sq);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          uint32_t wu = 0;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            wu |= code_exact<OUTL, CLIP>(x[u][q], zq[q], sq[q], L, thr) << ((2 * (q & 3) + (q >> 2)) * kb);
-          w[u] = wu;
-        }
-      }
+      float sq[8];
+      ld4(M.s, sq);
+      if (kb == 4) key_codes<4, OUTL, CLIP>(x, zq, rq, aq, bq, sq, L, thr, w);
+      else if (kb == 2) key_codes<2, OUTL, CLIP>(x, zq, rq, aq, bq, sq, L, thr, w);
+      else key_codes<3, OUTL, CLIP>(x, zq, rq, aq, bq, sq, L, thr, w);
     } else {
       // code = the number of midpoints below the value (ties to the lower entry)
       constexpr int NM = (1 << (lut ? LUTB : 1)) - 1;
@@ -930,7 +948,8 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
     uint32_t w[CW];
 #pragma unroll
     for (int q = 0; q < CW; ++q) w[q] = 0;
-    bool tie = false;
+    float su[TPW];
+    ldt(M.s, su);
     // token u of the word sits at bits u VB: 4-bit codes pair into bytes, 2-bit
     // codes come in fours
     constexpr int TPB = 8 / VB;  // tokens per byte
@@ -942,7 +961,11 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
 #pragma unroll
         for (int q = 0; q < CW; ++q) {
           const int u = k * TPB + t;
-          cf[t][q] = code_fast<OUTL, CLIP>(x[u][q], zu[u], ru[u], au[u], bu[u], tie);
+          bool near;
+          float qc;
+          cf[t][q] = code_fast<OUTL, CLIP>(x[u][q], zu[u], ru[u], au[u], bu[u], near, qc);
+          // rare: a quotient this close to a rounding boundary is decided exactly
+          if (near) cf[t][q] = code_near<OUTL, CLIP>(x[u][q], zu[u], su[u], qc, (float)L, thr);
         }
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
@@ -951,16 +974,6 @@ __global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, 
         for (int t = TPB - 2; t >= 0; --t) byte = __builtin_fmaf(byte, (float)(1 << VB), cf[t][q]);
         w[q] = put_byte(byte, k, w[q]);
       }
-    }
-    if (tie) {  // rare: this lane's cell again with the correctly rounded divide
-      float su[TPW];
-      ldt(M.s, su);
-#pragma unroll
-      for (int q = 0; q < CW; ++q) w[q] = 0;
-#pragma unroll
-      for (int u = 0; u < TPW; ++u)
-#pragma unroll
-        for (int q = 0; q < CW; ++q) w[q] |= code_exact<OUTL, CLIP>(x[u][q], zu[u], su[u], L, thr) << (u * VB);
     }
     uint32_t* out = static_cast<uint32_t*>(c.v_codes) + (bh * (T / TPW) + n * (BK / TPW) + tg) * D + ch0;
     reinterpret_cast<uint4*>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
