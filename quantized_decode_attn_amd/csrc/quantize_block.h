@@ -26,9 +26,10 @@
 //
 // Each thread holds one register cell of the tile (8 x 8 elements for keys, 8 x 8 or
 // 16 x 4 for values) from step 3 on.  The code is computed as rint((d - z) * rcp(s)),
-// which differs from the correctly rounded quotient by a few ulp only; a lane that
-// meets a quotient within 2^-17 of a rounding boundary redoes its cell with the
-// IEEE divide, so the stored bits are those of the exact definition.  Clipping to
+// which differs from the correctly rounded quotient by a few ulp only; a quotient
+// within 2^-17 of a rounding boundary is decided exactly from the residual of the
+// nearest half-integer (code_near), so the stored bits are those of the exact
+// definition, rint of the IEEE fp32 quotient.  Clipping to
 // [-thr, thr] is applied as a clamp of the quotient to [q(-thr), q(thr)]: the
 // quotient is monotone in d, so this equals the quotient of the clipped value.
 #pragma once
@@ -41,7 +42,7 @@ namespace qb {
 
 constexpr int kThreads = 256;
 constexpr uint16_t kMarkNaN = 0x7E00;  // fp16 quiet NaN marking an outlier in the tile
-// A quotient closer than 2^-17 to a rounding boundary is redone exactly.  The fast
+// A quotient closer than 2^-17 to a rounding boundary is decided exactly.  The fast
 // quotient (d - z) * rcp(s) is within |q| 2^-22 of the correctly rounded one (rcp is
 // good to 1 ulp, the product and the IEEE quotient to half an ulp each), i.e. within
 // 2^-18 for the clamped |q| <= 16, so every other element rounds the same either way.
@@ -190,15 +191,6 @@ __device__ __forceinline__ float lanes_max(float v) {
 }
 
 // ---------------------------------------------------------------- scalar pieces
-__device__ __forceinline__ int code_uniform(float d, float z, float s, int L) {
-  if (s == 0.0f) return 0;
-  const float num = d - z;
-  const float q = num / s;  // IEEE-correct fp32 division
-  float r = __builtin_rintf(q);
-  r = fmaxf(r, 0.0f);
-  r = fminf(r, (float)L);
-  return (int)r;
-}
 
 // fp16 zero = min rounded down, fp16 scale = (max - zero) / L rounded up; a group
 // with no dense value (lo > hi) gets zero 0 and scale 0.
@@ -271,13 +263,6 @@ __device__ __forceinline__ float code_near(float d, float z, float s, float qc, 
   const float even = k + (float)((int)k & 1);
   const float code = r > hu ? k + 1.0f : (r < -hu ? k : even);
   return fminf(fmaxf(code, 0.0f), Lf);
-}
-template <bool OUTL, bool CLIP>
-__device__ __forceinline__ uint32_t code_exact(float d, float z, float s, int L, float thr) {
-  if constexpr (OUTL)
-    if (d != d) return 0u;
-  if constexpr (CLIP) d = fminf(fmaxf(d, -thr), thr);
-  return (uint32_t)code_uniform(d, z, s, L);
 }
 
 // ---------------------------------------------------------------- phase 1: staging
