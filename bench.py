@@ -75,17 +75,19 @@ def source_hash(names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel source; otherwise None."""
+def measured_traffic(kind: str, workload: str, src_hash: str):
+    """HBM bytes per call from the committed counter summary, if it was taken on this
+    workload and on the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))[kernel]
+        recs = json.load(open(path))["records"]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_hash") != src_hash:
-        return None
-    return rec.get("bytes_per_launch")
+    for rec in recs:
+        if (rec.get("kind") == kind and rec.get("workload") == workload
+                and rec.get("source_hash") == src_hash):
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def cpu_baseline(cfg, k, v, q, lut, seconds: float):
@@ -190,15 +192,22 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Untimed between the timed regions: a 1 GiB read that evicts the 256 MB Infinity
+    # Cache and the L2 (writing back the append's dirty lines), so that neither the append
+    # nor the decode starts with the other's data, or dirty lines, in the caches.
+    scrub = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
 
     def step(e=None):
         cache.desc.length = existing            # re-append the same tokens into the same slots
+        scrub.sum()
         if e: e[0].record(stream)
         cache.append(k_new, v_new)
         if e: e[1].record(stream)
-        cache.decode(q_d, q_pos=T - 1, num_splits=args.splits, out=out)
+        scrub.sum()
         if e: e[2].record(stream)
+        cache.decode(q_d, q_pos=T - 1, num_splits=args.splits, out=out)
+        if e: e[3].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -209,7 +218,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     app_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
-    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+    dec_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(args.steps)])
 
     dbytes = decode_bytes(cfg, T)
     abytes = B * H * n_new * append_bytes_per_token_head(cfg)
@@ -219,11 +228,12 @@ def main():
     log("decode  %.1f us  %.1f GB/s (%.1f%% of 8 TB/s)" % (dec_ms.mean() * 1e3, dec_gbps, dec_gbps / 80))
     log("append  %.1f us  %.1f GB/s  %.3g tokens/s" % (app_ms.mean() * 1e3, app_gbps, app_tps))
 
-    dec_hash = source_hash(["decode_mha.hip", "decode_common.h", "decode.hip", "kvq_device.h", "kvq_internal.h"])
+    dec_hash = source_hash(["decode_mha.hip", "decode_gqa.hip", "decode_common.h", "decode.hip",
+                            "kvq_device.h", "kvq_internal.h"])
     app_hash = source_hash(["quantize.hip", "quantize_block.h", "quantize_keys.hip", "quantize_keys_lut.hip",
                             "quantize_values.hip", "kvq_device.h", "kvq_internal.h"])
-    tr_dec = measured_traffic("decode", dec_hash)
-    tr_app = measured_traffic("append", app_hash)
+    tr_dec = measured_traffic("decode", cfg["workload"], dec_hash)
+    tr_app = measured_traffic("append", cfg["workload"], app_hash)
     rec = {
         "metric": METRIC,
         "value": round(dec_gbps, 2),
