@@ -18,10 +18,12 @@
 //    heads' weights (lane l supplies head l % 4) with the 64 tokens' khat, so after
 //    the 128 channels lane l holds the scores of its token for all four heads --
 //    no cross-lane reduction;
-//  * values: lane l owns channels 4 (l % 32) .. +3 and the token groups of its half
-//    of the wave; per token and channel slot one MFMA multiplies the four heads'
-//    weights p * scale with the codes (converted two at a time with the packed fp8
-//    conversion: a byte 0..15 is an exact fp8 value proportional to it);
+//  * values: the weights p * scale of a block are quantized per head to 16-bit fixed
+//    point (relative to a bound on the block's largest weight) and split into four
+//    nibbles, so that sum_t w_t c_t is an exact integer product: one
+//    v_mfma_i32_16x16x64_i8 takes the 16 rows (head, nibble) against 16 channels and
+//    64 tokens, the codes spread from the packed words into bytes (16 instructions
+//    per block instead of 256 fp32 outer products);
 //  * outliers ([KVC3] "Per-Vector Dense-and-Sparse Quantization"): code 0 was stored
 //    at an outlier's position; the lane owning a token adds the exact score terms of
 //    its CSR entries for every head, and scatters p * (x - zero) into a per-head
@@ -41,7 +43,8 @@ using namespace dcm;
 constexpr int kGqaWaves = 8;
 constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;  // floats per rotary-table row: 64 (cos, sin) pairs + 4 (banks)
-constexpr int kWVP = kBK + 4;  // floats per value-weight row (one row per group and head)
+constexpr int kWAP = 2 * kHalf + 4;  // floats per head of the query weights (distinct banks per head)
+constexpr int kW16P = kHalf + 4;     // dwords per head of the fixed-point value weights
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -49,16 +52,24 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
+typedef int i4 __attribute__((ext_vector_type(4)));
+// D += A B over 64 int8 products: lane l supplies row l % 16 of A and column l % 16 of
+// B, each with 16 entries of the reduction index (the same 16 positions in both), and
+// receives D[4 (l / 16) + r][l % 16] in element r.
+__device__ __forceinline__ i4 mfma_i8(i4 a, i4 b, i4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
 // Per-wave LDS area, in floats.
 struct GLds {
-  int meta, wa, wv, vcorr, wq, total;
+  int meta, wa, w16, vcorr, wq, total;
 };
 __host__ __device__ inline GLds gqa_lds(int ng, bool outl) {
   GLds m;
   int o = 0;
   m.meta = o; o += 4 * kHalf;        // per pair: scale_a / u, zero_a, scale_b / u, zero_b
-  m.wa = o; o += 4 * kHalf * 2;      // per head and pair: (W_r, -W_i)
-  m.wv = o; o += ng * 4 * kWVP;      // value weights p * scale / u, [group][head][token]
+  m.wa = o; o += 4 * kWAP;           // per head and pair: (W_r, -W_i)
+  m.w16 = o; o += ng * 4 * kW16P;    // fixed-point value weights [group][head][lane]: tokens lane, 64 + lane (u16)
   m.vcorr = o; o += outl ? 4 * kD + 4 : 0;  // value outlier corrections [head][channel] (int), scale per head
   m.wq = o; o += kHalf * 8;          // the item's query weights per pair: (re, im) of 4 heads
   m.total = o;
@@ -67,9 +78,11 @@ __host__ __device__ inline GLds gqa_lds(int ng, bool outl) {
 
 template <int VB>
 struct GRegs {
-  static constexpr int NVI = (kBK / (32 / VB)) * kD / 256;  // 16-byte value loads per lane
+  static constexpr int TPW = 32 / VB;   // tokens per value word
+  static constexpr int WPL = 16 / TPW;  // words of one channel per 16 tokens
+  static constexpr int NVI = 4 * WPL;   // 16-byte value loads per lane
   uint4 k[2][4];     // key rows of tokens lane and 64 + lane (64 bytes each)
-  uint4 v[NVI];      // value words: load s holds channels 4 (l % 32) .. +3 of token group 2 s + l / 32
+  uint4 v[NVI];      // value words, see gload_v
   uint16_t kmeta[4]; // lane i: scale[i], scale[i + 64], zero[i], zero[i + 64]
   float eb_c, eb_s;  // lane i: cos/sin(n Bk f_i)
   uint16_t vs[4], vz[4];  // value scale/zero of elements lane + 64 k ([group][token])
@@ -89,12 +102,14 @@ template <int VB>
 __device__ __forceinline__ void gload_k(GRegs<VB>& R, int hf, int q, const uint8_t* kblk, int lane) {
   R.k[hf][q] = *reinterpret_cast<const uint4*>(kblk + (uint32_t)((kHalf * hf + lane) * (kD / 2) + 16 * q));
 }
-// Value load s: words of token group 2 s + lane / 32 (32 / VB tokens each), channels
-// 4 (lane % 32) .. +3.
+// Value load s = (kc WPL + j) 2 + hc: word j of the 16 tokens 64 kc + 16 (lane / 16) ..
+// of channels 64 hc + 4 (lane % 16) .. +3 (one word per channel).
 template <int VB>
 __device__ __forceinline__ void gload_v(GRegs<VB>& R, int s, const uint8_t* vblk, int lane) {
-  const uint32_t tg = 2 * s + (lane >> 5);
-  R.v[s] = *reinterpret_cast<const uint4*>(vblk + (tg * kD + 4 * (lane & 31)) * 4u);
+  constexpr int TPW = GRegs<VB>::TPW, WPL = GRegs<VB>::WPL;
+  const int kc = s / (2 * WPL), j = (s >> 1) % WPL, hc = s & 1;
+  const uint32_t tg = kc * (kHalf / TPW) + (lane >> 4) * WPL + j;
+  R.v[s] = *reinterpret_cast<const uint4*>(vblk + (tg * kD + 64 * hc + 4 * (lane & 15)) * 4u);
 }
 template <int VB>
 __device__ __forceinline__ void gload_kmeta(GRegs<VB>& R, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
@@ -124,21 +139,37 @@ __device__ __forceinline__ void gload_vmeta(GRegs<VB>& R, const kvq_cache& c, in
 
 struct GState {
   float m[4], lpart[4], zpart[4][2];
-  f4 acc[4];  // acc[c][g]: head g, channel 4 (lane % 32) + c, this lane's token groups
+  float acc[8];  // head lane / 16; channels 4 (lane % 16) + c (c < 4) and 64 + 4 (lane % 16) + c - 4
 };
 
-// Adds the four heads' value-outlier corrections (fixed point in LDS) to the lane's
-// accumulators (channels 4 lane .. +3, lanes < 32) and clears them.
+// Adds the value-outlier corrections (fixed point in LDS) of the lane's head and
+// channels to its accumulators and clears them.
 __device__ __forceinline__ void merge_vcorr_heads(int* VCI, GState& st, int lane) {
+  const int hd = lane >> 4, c4 = 4 * (lane & 15);
+  const int sh = VCI[4 * kD + hd];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float a[4] = {st.acc[0][g], st.acc[1][g], st.acc[2][g], st.acc[3][g]};
-    merge_vcorr<kD>(VCI + g * kD, VCI[4 * kD + g], a, lane);
-    st.acc[0][g] = a[0]; st.acc[1][g] = a[1]; st.acc[2][g] = a[2]; st.acc[3][g] = a[3];
+  for (int hc = 0; hc < 2; ++hc) {
+    int4* pc = reinterpret_cast<int4*>(VCI + hd * kD + 64 * hc + c4);
+    const int4 v = *pc;
+    st.acc[4 * hc] += __builtin_amdgcn_ldexpf((float)v.x, -sh);
+    st.acc[4 * hc + 1] += __builtin_amdgcn_ldexpf((float)v.y, -sh);
+    st.acc[4 * hc + 2] += __builtin_amdgcn_ldexpf((float)v.z, -sh);
+    st.acc[4 * hc + 3] += __builtin_amdgcn_ldexpf((float)v.w, -sh);
+    *pc = make_int4(0, 0, 0, 0);
   }
 }
 
-template <int VB, int KO>
+// Positions of the reduction index: the 16 bytes (4 dwords) a lane gives the integer
+// MFMA for its 16 tokens are the code bytes in the order the packed words yield them,
+// dword q byte m = token tau(q, m) of the 16: for 4-bit words (w & 0x0F0F0F0F, then
+// (w >> 4) & ...) the even tokens of a word, then the odd; for 2-bit words
+// ((w >> 2 q) & 0x03030303) tokens q, q + 4, q + 8, q + 12.
+template <int VB>
+__device__ __forceinline__ int tau(int q, int m) {
+  return VB == 4 ? 8 * (q >> 1) + (q & 1) + 2 * m : q + 4 * m;
+}
+
+template <int VB, int KO, int NG>
 __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, float* __restrict__ wl, const GLds& L,
                                           const float* __restrict__ table, float inv_unit, int lane, int G, int ng,
                                           const kvq_cache& c, int64_t bh, int64_t n, bool more) {
@@ -149,7 +180,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   const uint8_t* vnext = gv_block<VB>(c, bh, nn);
   float* Meta = wl + L.meta;
   float* WA = wl + L.wa;
-  float* WV = wl + L.wv;
+  uint32_t* W16 = reinterpret_cast<uint32_t*>(wl + L.w16);  // [group][head][lane]
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
   const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
 
@@ -162,7 +193,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
     const float wq_r[4] = {q01.x, q01.z, q23.x, q23.z}, wq_i[4] = {q01.y, q01.w, q23.y, q23.w};
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<float2*>(WA + g * 2 * kHalf + 2 * lane) =
+      *reinterpret_cast<float2*>(WA + g * kWAP + 2 * lane) =
           make_float2(wq_r[g] * R.eb_c - wq_i[g] * R.eb_s, -(wq_r[g] * R.eb_s + wq_i[g] * R.eb_c));  // W_r, -W_i
   }
   gload_kmeta(R, c, bh, nn, lane);
@@ -177,7 +208,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   {
     const float* trA = table + lane * kTP;
     const float* trB = table + (kHalf + lane) * kTP;
-    const float* wal = WA + hl * 2 * kHalf;
+    const float* wal = WA + hl * kWAP;
     struct Win {
       float4 tA, tB, wa, M0, M1;  // cos/sin of both tokens, weights, pair constants
     };
@@ -276,7 +307,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
         const float2 cssn = *reinterpret_cast<const float2*>(table + t * kTP + 2 * i);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float2 w = *reinterpret_cast<const float2*>(WA + g * 2 * kHalf + 2 * i);
+          const float2 w = *reinterpret_cast<const float2*>(WA + g * kWAP + 2 * i);
           const float wr = w.x, wi = -w.y;
           const float re = wr * cssn.x - wi * cssn.y, im = wr * cssn.y + wi * cssn.x;
           p[k][g] += a ? dl * re : -dl * im;
@@ -287,92 +318,119 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
     for (int g = 0; g < 4; ++g) mloc[g] = fmaxf(mloc[g], p[k][g]);
   }
   if constexpr (OUTL) merge_vcorr_heads(VCI, st, lane);  // the previous block's, before the rescale
+  const int hd = lane >> 4;  // the head of the lane's value accumulators
+  float pmax[4], alpha_hd = 0.0f;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const float mnew = fmaxf(st.m[g], wave_max_uniform(mloc[g]));
+    const float mb = wave_max_uniform(mloc[g]);
+    const float mnew = fmaxf(st.m[g], mb);
     const float alpha = __builtin_amdgcn_exp2f(st.m[g] - mnew);
     st.m[g] = mnew;
+    pmax[g] = __builtin_amdgcn_exp2f(mb - mnew);  // the p of the block's top token
     p[0][g] = __builtin_amdgcn_exp2f(p[0][g] - mnew);
     p[1][g] = __builtin_amdgcn_exp2f(p[1][g] - mnew);
     st.lpart[g] = __builtin_fmaf(st.lpart[g], alpha, p[0][g] + p[1][g]);
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) st.acc[cc][g] *= alpha;
+    alpha_hd = hd == g ? alpha : alpha_hd;
     st.zpart[g][0] *= alpha;
     st.zpart[g][1] *= alpha;
   }
-
-  // ---- value weights p * scale / u per [group][head][token] (the codes enter the
-  // MFMA as c * u); the zero-point part p * zero is summed per lane in fp32.
-  // Element lane + 64 k is token 64 (k % 2) + lane of group k / 2.
-  float vzc[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    vzc[k] = 0.0f;
-    if (kWave * k < kBK * ng) {
-      const int grp = k >> 1, kt = k & 1;
-      const float vs = h2f(R.vs[k]) * inv_unit, vz = h2f(R.vz[k]);
-      vzc[k] = vz;
-      float* wvp = WV + grp * 4 * kWVP + kHalf * kt + lane;
+  for (int t = 0; t < 8; ++t) st.acc[t] *= alpha_hd;
+
+  // ---- value weights w = p * scale of [group][head][token] in 16-bit fixed point: the
+  // weights of head g and group k are at most pmax_g * (the block's largest scale of
+  // group k), so w / bound converts to unorm16 (rounded, clamped at 65535) and the
+  // integer products below are exact; the zero-point part p * zero is summed per lane
+  // in fp32.  Element lane + 64 k is token 64 (k % 2) + lane of group k / 2.
+  float vzc[4] = {0.f, 0.f, 0.f, 0.f}, inv_hd[2] = {0.f, 0.f};
+  {
+    float vsf[4], vmax[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2 * NG; ++k) {
+      vsf[k] = h2f(R.vs[k]);
+      vzc[k] = h2f(R.vz[k]);
+      vmax[k >> 1] = fmaxf(vmax[k >> 1], vsf[k]);
+    }
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp) {
+      vmax[grp] = wave_max_uniform(vmax[grp]);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        wvp[g * kWVP] = p[kt][g] * vs;
-        st.zpart[g][grp] = __builtin_fmaf(p[kt][g], vz, st.zpart[g][grp]);
+        const float bound = pmax[g] * vmax[grp];
+        const float rb = bound > 0x1p-100f ? __builtin_amdgcn_rcpf(bound) : 0.0f;
+        const auto w = __builtin_amdgcn_cvt_pknorm_u16(p[0][g] * vsf[2 * grp] * rb, p[1][g] * vsf[2 * grp + 1] * rb);
+        W16[(grp * 4 + g) * kW16P + lane] = __builtin_bit_cast(uint32_t, w);
+        st.zpart[g][grp] = __builtin_fmaf(p[0][g], vzc[2 * grp], __builtin_fmaf(p[1][g], vzc[2 * grp + 1], st.zpart[g][grp]));
+        inv_hd[grp] = hd == g ? bound * (1.0f / 65535.0f) : inv_hd[grp];
       }
     }
   }
-  gload_vmeta(R, c, bh, nn, lane, ng);
+  gload_vmeta(R, c, bh, nn, lane, NG);
   wave_lds_sync();
 
-  // ---- values: per token and channel slot one MFMA over the four heads
+  // ---- values: D[(head, nibble)][channel] += sum over 64 tokens of nibble * code, per
+  // token half kc and channel tile T (channels 64 (T / 4) + 4 (lane % 16) + T % 4)
   {
-    f4 va[4];  // even-token chains; the odd tokens accumulate into st.acc directly
+    constexpr int WPL = GRegs<VB>::WPL;
+    // A: row lane % 16 = (head h_a, nibble pl), tokens 16 (lane / 16) + tau(q, m) of both
+    // halves; a W16 dword holds a token's weight of half 0 (low) and half 1 (high)
+    const int h_a = (lane >> 2) & 3, pl = lane & 3, lg = lane >> 4;
+    i4 A[2][NG];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) va[cc] = f4{0.f, 0.f, 0.f, 0.f};
-    const int grp_l = (4 * (lane & 31)) / G;
-    const float* wvl = WV + (grp_l * 4 + hl) * kWVP + TPW * (lane >> 5);
+    for (int grp = 0; grp < NG; ++grp) {
+      const uint4* wr = reinterpret_cast<const uint4*>(W16 + (grp * 4 + h_a) * kW16P + 16 * lg);
+      uint32_t x[16];
 #pragma unroll
-    for (int s = 0; s < GRegs<VB>::NVI; ++s) {
-      const uint32_t words[4] = {R.v[s].x, R.v[s].y, R.v[s].z, R.v[s].w};
-      gload_v(R, s, vnext, lane);
-      float wt[TPW];  // weights of the group's tokens for head lane % 4
-#pragma unroll
-      for (int u4 = 0; u4 < TPW; u4 += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(wvl + 2 * TPW * s + u4);
-        wt[u4] = x.x; wt[u4 + 1] = x.y; wt[u4 + 2] = x.z; wt[u4 + 3] = x.w;
+      for (int u = 0; u < 4; ++u) {
+        const uint4 e = wr[u];
+        x[4 * u] = (e.x >> (4 * pl)) & 0x000F000Fu;
+        x[4 * u + 1] = (e.y >> (4 * pl)) & 0x000F000Fu;
+        x[4 * u + 2] = (e.z >> (4 * pl)) & 0x000F000Fu;
+        x[4 * u + 3] = (e.w >> (4 * pl)) & 0x000F000Fu;
       }
-      // two channel slots at a time, each with an even-token and an odd-token chain,
-      // so that four independent MFMA chains alternate
 #pragma unroll
-      for (int c2 = 0; c2 < 4; c2 += 2) {
-        float cv[2][TPW];  // codes (times u) of the two words' tokens
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const uint32_t w = words[c2 + h2];
-          if constexpr (VB == 4) {
-            const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-            const f2v e0 = cvt_lo(lo), e1 = cvt_hi(lo), o0 = cvt_lo(hi), o1 = cvt_hi(hi);
-            cv[h2][0] = e0.x; cv[h2][2] = e0.y; cv[h2][4] = e1.x; cv[h2][6] = e1.y;
-            cv[h2][1] = o0.x; cv[h2][3] = o0.y; cv[h2][5] = o1.x; cv[h2][7] = o1.y;
-          } else {
-#pragma unroll
-            for (int sh = 0; sh < 4; ++sh) {  // tokens sh, sh + 4, sh + 8, sh + 12
-              const uint32_t x = (w >> (2 * sh)) & 0x03030303u;
-              const f2v lo2 = cvt_lo(x), hi2 = cvt_hi(x);
-              cv[h2][sh] = lo2.x; cv[h2][sh + 4] = lo2.y; cv[h2][sh + 8] = hi2.x; cv[h2][sh + 12] = hi2.y;
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < TPW; u += 2) {
-          va[c2] = mfma4(wt[u], cv[0][u], va[c2]);
-          va[c2 + 1] = mfma4(wt[u], cv[1][u], va[c2 + 1]);
-          st.acc[c2] = mfma4(wt[u + 1], cv[0][u + 1], st.acc[c2]);
-          st.acc[c2 + 1] = mfma4(wt[u + 1], cv[1][u + 1], st.acc[c2 + 1]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t ylo = x[tau<VB>(q, 0)] | (x[tau<VB>(q, 1)] << 8);
+        const uint32_t yhi = x[tau<VB>(q, 2)] | (x[tau<VB>(q, 3)] << 8);
+        A[0][grp][q] = (int)__builtin_amdgcn_perm(yhi, ylo, 0x05040100u);
+        A[1][grp][q] = (int)__builtin_amdgcn_perm(yhi, ylo, 0x07060302u);
       }
     }
+    i4 Dt[8];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) st.acc[cc] += va[cc];
+    for (int t = 0; t < 8; ++t) Dt[t] = i4{0, 0, 0, 0};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          i4 B;
+          if constexpr (VB == 4) {
+            const uint4 va = R.v[(kc * WPL) * 2 + hc], vb = R.v[(kc * WPL + 1) * 2 + hc];
+            const uint32_t wa = t4 == 0 ? va.x : t4 == 1 ? va.y : t4 == 2 ? va.z : va.w;
+            const uint32_t wb = t4 == 0 ? vb.x : t4 == 1 ? vb.y : t4 == 2 ? vb.z : vb.w;
+            B = i4{(int)(wa & 0x0F0F0F0Fu), (int)((wa >> 4) & 0x0F0F0F0Fu), (int)(wb & 0x0F0F0F0Fu),
+                   (int)((wb >> 4) & 0x0F0F0F0Fu)};
+          } else {
+            const uint4 va = R.v[kc * 2 + hc];
+            const uint32_t w = t4 == 0 ? va.x : t4 == 1 ? va.y : t4 == 2 ? va.z : va.w;
+            B = i4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                   (int)((w >> 6) & 0x03030303u)};
+          }
+          Dt[4 * hc + t4] = mfma_i8(A[kc][NG == 2 ? hc : 0], B, Dt[4 * hc + t4]);
+        }
+#pragma unroll
+        for (int j = 0; j < WPL; ++j) gload_v(R, (kc * WPL + j) * 2 + hc, vnext, lane);
+      }
+    }
+    // lane holds rows 4 hd + r (nibble r of head hd) of its channel in every tile
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t tot = (uint32_t)Dt[t][0] + ((uint32_t)Dt[t][1] << 4) + ((uint32_t)Dt[t][2] << 8) +
+                           ((uint32_t)Dt[t][3] << 12);
+      st.acc[t] = __builtin_fmaf((float)tot, inv_hd[NG == 2 ? t >> 2 : 0], st.acc[t]);
+    }
   }
 
   // ---- value outliers: p * (x - zero) scattered into the per-head channel array in
@@ -410,7 +468,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 
 // Item = (b, kv-head, head set, split): the wave serves GW (4 or 2) query heads of the
 // group; with 2 the MFMA rows of heads 2 and 3 carry zero weights.
-template <int VB, int GW, int KO>
+template <int VB, int GW, int KO, int NG>
 __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
                                                                    int64_t nitems) {
@@ -418,7 +476,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
   constexpr bool OUTL = KO > 0;
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H, nsets = gq / GW;
-  const int G = c.cfg.v_group, ng = kD / G;
+  const int G = c.cfg.v_group;
   const int64_t nfull = c.length / kBK;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -428,7 +486,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     const int j = idx / kHalf, i = idx % kHalf;
     *reinterpret_cast<float2*>(table + j * kTP + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
   }
-  const GLds L = gqa_lds(ng, OUTL);
+  const GLds L = gqa_lds(NG, OUTL);
   float* wl = lds + kBK * kTP + wave * L.total;
   if (OUTL)
     for (int k = lane; k < 4 * kD + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
@@ -474,14 +532,15 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
       st.m[g] = -__builtin_inff();
       st.lpart[g] = 0.0f;
       st.zpart[g][0] = st.zpart[g][1] = 0.0f;
-      st.acc[g] = f4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.acc[t] = 0.0f;
 
     GRegs<VB> R;
     CsrTok C;
     if (n0 < n1) {
       gload_kmeta(R, c, bh, n0, lane);
-      gload_vmeta(R, c, bh, n0, lane, ng);
+      gload_vmeta(R, c, bh, n0, lane, NG);
       if constexpr (OUTL) load_csr_tok<kBK, KO>(C, c, bh, n0, lane);
       const uint8_t* kb0 = gk_block(c, bh, n0);
       const uint8_t* vb0 = gv_block<VB>(c, bh, n0);
@@ -493,53 +552,55 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
       for (int s = 0; s < GRegs<VB>::NVI; ++s) gload_v(R, s, vb0, lane);
     }
     for (int64_t n = n0; n < n1; ++n)
-      gqa_block<VB, KO>(R, C, st, wl, L, table, inv_unit, lane, G, ng, c, bh, n, n + 1 < n1);
+      gqa_block<VB, KO, NG>(R, C, st, wl, L, table, inv_unit, lane, G, NG, c, bh, n, n + 1 < n1);
 
     if (OUTL) {  // the item's last block of value corrections
       merge_vcorr_heads(reinterpret_cast<int*>(wl + L.vcorr), st, lane);
       wave_lds_sync();
     }
-    // ---- finish the item: the two token halves of each channel, then (m, l, o) per head
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) st.acc[cc][g] += __shfl_xor(st.acc[cc][g], 32, kWave);
+    // ---- finish the item: (m, l) per head from lane 0, o from the 16 lanes of its head
+    float zl[2] = {0.f, 0.f};
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       const float l = wave_sum(st.lpart[g]);
       const float z0 = wave_sum(st.zpart[g][0]);
-      const float z1 = wave_sum(st.zpart[g][1]);
-      const int hq = h * gq + set * GW + g;
-      float* dst = ws + (((int64_t)b * Hq + hq) * S + split) * (kD + 2);
-      if (lane < 32) {
-        const int ch0 = 4 * lane;
-        const float z = (ch0 / G) == 0 ? z0 : z1;
-        *reinterpret_cast<float4*>(dst + 2 + ch0) =
-            make_float4(st.acc[0][g] + z, st.acc[1][g] + z, st.acc[2][g] + z, st.acc[3][g] + z);
-      }
+      const float z1 = NG == 2 ? wave_sum(st.zpart[g][1]) : 0.0f;
+      zl[0] = (lane >> 4) == g ? z0 : zl[0];
+      zl[1] = (lane >> 4) == g ? z1 : zl[1];
       if (lane == 0) {
+        float* dst = ws + (((int64_t)b * Hq + h * gq + set * GW + g) * S + split) * (kD + 2);
         dst[0] = st.m[g];
         dst[1] = l;
+      }
+    }
+    const int hd = lane >> 4;
+    if (hd < GW) {
+      float* dst = ws + (((int64_t)b * Hq + h * gq + set * GW + hd) * S + split) * (kD + 2);
+      const int c4 = 4 * (lane & 15);
+#pragma unroll
+      for (int hc = 0; hc < 2; ++hc) {
+        const float z = NG == 2 && hc == 1 ? zl[1] : zl[0];  // channels 64 hc + c4 .. lie in group hc when G = 64
+        *reinterpret_cast<float4*>(dst + 2 + 64 * hc + c4) =
+            make_float4(st.acc[4 * hc] + z, st.acc[4 * hc + 1] + z, st.acc[4 * hc + 2] + z, st.acc[4 * hc + 3] + z);
       }
     }
   }
 }
 
-template <int VB, int GW, int KO>
+template <int VB, int GW, int KO, int NG>
 hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
                             int cus) {
-  const int ng = kD / c.cfg.v_group;
-  const GLds L = gqa_lds(ng, KO > 0);
+  const GLds L = gqa_lds(NG, KO > 0);
   const size_t bytes = ((size_t)kBK * kTP + (size_t)kGqaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO, NG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int gq = c.cfg.q_heads / c.cfg.kv_heads;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * (gq / GW) * S;
   int64_t grid = (nitems + kGqaWaves - 1) / kGqaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_gqa_kernel<VB, GW, KO>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes, s, c, q,
+  hipLaunchKernelGGL((decode_gqa_kernel<VB, GW, KO, NG>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes, s, c, q,
                      q_pos, ws, S, nitems);
   return hipGetLastError();
 }
@@ -553,18 +614,22 @@ hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ko = host_kout(g);
   const int gq = g.q_heads / g.kv_heads;
   const int ng = g.head_dim / g.v_group;
-  if (gq < 2 || gq % 2 || g.k_mode != 0 || g.k_bits != 4 || ko > 2 || ng > 2 || g.head_dim != kD ||
+  if (gq < 2 || gq % 2 || g.k_mode != 0 || g.k_bits != 4 || ko > 2 || ng < 1 || ng > 2 || g.head_dim != kD ||
       g.k_block != kBK || (g.v_bits != 4 && g.v_bits != 2))
     return hipErrorNotSupported;
   const bool four = gq % 4 == 0;
+#define KVQ_GQA_NG(vb, gw, ko)                                                                \
+  return ng == 2 ? launch_gqa_typed<vb, gw, ko, 2>(c, q, q_pos, ws, S, s, cus)                \
+                 : launch_gqa_typed<vb, gw, ko, 1>(c, q, q_pos, ws, S, s, cus);
 #define KVQ_GQA(vb, gw)                                                                       \
   if (g.v_bits == vb && four == (gw == 4)) {                                                  \
-    if (ko == 2) return launch_gqa_typed<vb, gw, 2>(c, q, q_pos, ws, S, s, cus);              \
-    if (ko == 1) return launch_gqa_typed<vb, gw, 1>(c, q, q_pos, ws, S, s, cus);              \
-    return launch_gqa_typed<vb, gw, 0>(c, q, q_pos, ws, S, s, cus);                           \
+    if (ko == 2) { KVQ_GQA_NG(vb, gw, 2) }                                                    \
+    if (ko == 1) { KVQ_GQA_NG(vb, gw, 1) }                                                    \
+    KVQ_GQA_NG(vb, gw, 0)                                                                     \
   }
   KVQ_GQA(4, 4) KVQ_GQA(2, 4) KVQ_GQA(4, 2) KVQ_GQA(2, 2)
 #undef KVQ_GQA
+#undef KVQ_GQA_NG
   return hipErrorNotSupported;
 }
 

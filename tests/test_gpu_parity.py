@@ -60,6 +60,12 @@ SMALL = {
     "gqa8_v2_g64": (synth.config("c2", batch=2, q_heads=16, kv_heads=2, v_bits=2, v_group=64,
                                  outlier_pct=0, inject=False, tokens=4 * 128 + 3, capacity=640),
                     [200, 315]),
+    # grouped-query: 4-bit values in two groups of 64 channels, two outliers per vector
+    "gqa4_v4_g64": (synth.config("c2", batch=1, q_heads=8, kv_heads=2, v_group=64,
+                                 tokens=3 * 128 + 100, capacity=512), [128, 356]),
+    # grouped-query: 2-bit values in one group of 128 channels, no outliers
+    "gqa4_v2_g128": (synth.config("c2", batch=1, q_heads=4, kv_heads=1, v_bits=2, outlier_pct=0,
+                                  inject=False, tokens=2 * 128 + 64, capacity=384), [100, 220]),
     # one head per kv head with one outlier per vector (head_dim 64: ceil(0.64) = 1)
     "mha_csr1_d64": (synth.config("c0", batch=2, outlier_pct=1, inject=True, tokens=5 * 64 + 30,
                                   capacity=384), [64, 286]),
