@@ -14,7 +14,8 @@
 //      skip, so the statistics below exclude them at no cost;
 //   2. clip threshold: exact q-quantile of |x| over the tile (outliers included) by
 //      radix selection on the 15-bit fp16 magnitudes, linear interpolation in fp64
-//      ([UQ] section 4.2);
+//      ([UQ] section 4.2); for high quantiles the selection runs over a short list of
+//      candidates that provably holds both order statistics;
 //   3. statistics: keys per channel over the block ([KVC3] "Per-Channel Key
 //      Quantization", before RoPE per "Pre-RoPE Key Quantization"), values per token
 //      over channel groups ([KVC3] "Quanto 的量化原理"); fp16 zero rounded down and
@@ -24,8 +25,10 @@
 //      (round(x/scale) of [TQ] section 4.2), or the nearest codebook entry
 //      ([KVC3] "Non-Uniform KV Cache Quantization"); outlier positions get code 0.
 //
-// Each thread holds one register cell of the tile (8 x 8 elements for keys, 8 x 8 or
-// 16 x 4 for values) from step 3 on.  The code is computed as rint((d - z) * rcp(s)),
+// Steps 1 and 2 work on the values each thread staged, still in registers; each
+// thread holds one register cell of the tile (8 x 8 elements for keys, 8 x 8 or
+// 16 x 4 for values) from step 3 on.  Both kernels are compiled for four waves per
+// SIMD (at most 128 registers), which the tile's LDS footprint also allows.  The code is computed as rint((d - z) * rcp(s)),
 // which differs from the correctly rounded quotient by a few ulp only; a quotient
 // within 2^-17 of a rounding boundary is decided exactly from the residual of the
 // nearest half-integer (code_near), so the stored bits are those of the exact
@@ -265,109 +268,127 @@ __device__ __forceinline__ float code_near(float d, float z, float s, float qc, 
   return fminf(fmaxf(code, 0.0f), Lf);
 }
 
-// ---------------------------------------------------------------- phase 1: staging
-// Rows from the old tail (tokens below old_len) or from the new input.
-// Returns the largest 15-bit magnitude among the values this thread staged (chunks
-// tid + i * kThreads, the order the clip's histogram pass reads them in).
+// ---------------------------------------------------------------- phases 1-2b
+// Thread tid stages chunks i < NC of 8 consecutive values: chunk i is token row
+// i * (kThreads / LPR) + tid / LPR, columns 8 (tid % LPR) .. +7, so the LPR = D / 8
+// threads of a row are consecutive lanes.  The outlier search and the clip's
+// candidate collection run on these registers; the tile in LDS is written once.
 template <int D, int BK>
-__device__ __forceinline__ uint32_t stage_tile(uint16_t* tile, const uint16_t* tail, const uint16_t* src_new,
-                                               int64_t bh, int64_t t0, int64_t old_len, int64_t n_new) {
+struct Stage {
+  static constexpr int LPR = D / 8;                     // threads per token row
+  static constexpr int RPS = kThreads / LPR;            // rows per chunk index
+  static constexpr int NC = BK / RPS;                   // chunks per thread
+  static_assert(NC * RPS == BK && NC * kThreads * 8 == BK * D, "tile split");
+};
+
+// Unsigned maximum over aligned groups of N lanes (N = 8 or 16).
+template <int N>
+__device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
+  static_assert(N == 8 || N == 16, "rows of 8 or 16 lanes");
+  v = max(v, dpp_u<kDppQuadXor1>(v));
+  v = max(v, dpp_u<kDppQuadXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  if constexpr (N == 16) v = max(v, dpp_u<kDppRowMirror>(v));
+  return v;
+}
+
+// Loads the thread's chunks (rows from the old tail below old_len, else from the new
+// input) and writes them to the tile.
+template <int D, int BK>
+__device__ __forceinline__ void stage_chunks(uint4 (&v)[BK * D / 8 / kThreads], uint16_t* tile, const uint16_t* tail,
+                                             const uint16_t* src_new, int64_t bh, int64_t t0, int64_t old_len,
+                                             int64_t n_new) {
+  using S = Stage<D, BK>;
   constexpr int P = D + 8;
-  constexpr int kPerThread = BK * D / 8 / kThreads;
-  static_assert(kPerThread * kThreads * 8 == BK * D, "tile split");
   const int64_t tail0 = (old_len / BK) * BK;
-  uint4 v[kPerThread];
+  const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    const int j = idx / (D / 8), part = idx % (D / 8);
+  for (int i = 0; i < S::NC; ++i) {
+    const int j = i * S::RPS + r0;
     const int64_t t = t0 + j;
     const uint16_t* row = t < old_len ? tail + (bh * BK + (t - tail0)) * D
                                       : src_new + (bh * n_new + (t - old_len)) * D;
     v[i] = *reinterpret_cast<const uint4*>(row + part * 8);
   }
-  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-  us2 m2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
-    const int j = idx / (D / 8), part = idx % (D / 8);
-    *reinterpret_cast<uint4*>(&tile[j * P + part * 8]) = v[i];
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, w[k] & 0x7fff7fffu));
-  }
-  return m2.x > m2.y ? m2.x : m2.y;
+  for (int i = 0; i < S::NC; ++i)
+    *reinterpret_cast<uint4*>(&tile[(i * S::RPS + r0) * P + part * 8]) = v[i];
 }
 
-// ---------------------------------------------------------------- phase 2: outliers
-// 16 lanes per token row, D/16 columns per lane; the ko largest keys
-// (|x| bits << 8 | 255 - column, unique within a row) are extracted one at a time
-// by row maxima.  Outliers are written to the CSR and either marked in the tile at
-// once (MARK_NOW) or after the clip threshold from `ocol`; the CSR slice is staged in
-// `ocol`/`oval` and written out by consecutive threads.
-template <int D, int BK, bool MARK_NOW>
-__device__ __forceinline__ void block_outliers(uint16_t* tile, uint8_t* ocol, uint16_t* oval, int32_t* rowptr,
-                                               uint8_t* col_out, uint16_t* val_out, int64_t bh, int64_t T, int64_t t0,
-                                               int ko) {
+// Step 1 from registers: per token row the ko largest keys |x| bits << 8 | 255 - column
+// (unique within a row, so ties go to the lower column), one row maximum per round,
+// the rounds of all the thread's rows interleaved.  The lane owning an outlier's
+// column stages it in ocol/oval (ascending column order within the row, value read
+// back from the tile it wrote itself); the columns are returned packed a byte each
+// for the marking after the clip.
+template <int D, int BK>
+__device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThreads], const uint16_t* tile, int ko,
+                                             uint8_t* ocol, uint16_t* oval, uint32_t (&colpk)[BK * D / 8 / kThreads]) {
+  using S = Stage<D, BK>;
   constexpr int P = D + 8;
-  constexpr int kPer = D / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane & 15;
-  for (int pass = 0; pass < BK / 16; ++pass) {
-    const int j = pass * 16 + wave * 4 + (lane >> 4);
-    uint32_t key[kPer];
-    {
-      uint32_t raw[kPer / 2];
-      if constexpr (kPer == 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&tile[j * P + sub * kPer]);
-        raw[0] = w.x; raw[1] = w.y; raw[2] = w.z; raw[3] = w.w;
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(&tile[j * P + sub * kPer]);
-        raw[0] = w.x; raw[1] = w.y;
-      }
+  constexpr int G = S::NC < 2 ? S::NC : 2;  // rows searched together (register budget)
+  const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const uint32_t hbits = (raw[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
-        key[k] = (hbits << 8) | (uint32_t)(255 - (sub * kPer + k));
-      }
+  for (int i0 = 0; i0 < S::NC; i0 += G) {
+    uint32_t key[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 vi = v[i0 + g];
+      const uint32_t w[4] = {vi.x, vi.y, vi.z, vi.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        key[g][k] = (((w[k >> 1] >> (16 * (k & 1))) & 0x7fffu) << 8) | (uint32_t)(255 - (8 * part + k));
     }
-    uint32_t sel[4] = {0, 0, 0, 0};
-    uint32_t prev = 0xffffffffu;
+    uint32_t sel[G][4], prev[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      prev[g] = 0xffffffffu;
+      sel[g][0] = sel[g][1] = sel[g][2] = sel[g][3] = 0u;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r < ko) {
-        uint32_t m = 0;
 #pragma unroll
-        for (int k = 0; k < kPer; ++k) m = max(m, key[k] < prev ? key[k] : 0u);
-        m = row_max_u32(m);
-        sel[r] = m;
-        prev = m;
+        for (int g = 0; g < G; ++g) {
+          uint32_t m = 0u;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) m = max(m, key[g][k] < prev[g] ? key[g][k] : 0u);
+          m = lanes_max_u32<S::LPR>(m);
+          sel[g][r] = m;
+          prev[g] = m;
+        }
       }
     }
-    if (sub == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = i0 + g;
+      const int j = i * S::RPS + r0;
       int cols[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cols[r] = 255 - (int)(sel[r] & 0xffu);
-      // ascending column order
-#pragma unroll
-      for (int a = 1; a < 4; ++a)
-#pragma unroll
-        for (int q = a; q > 0; --q)
-          if (q < ko && cols[q - 1] > cols[q]) {
-            const int t = cols[q]; cols[q] = cols[q - 1]; cols[q - 1] = t;
-          }
+      colpk[i] = 0u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (r < ko) {
-          ocol[j * 4 + r] = (uint8_t)cols[r];
-          oval[j * 4 + r] = tile[j * P + cols[r]];
-          if constexpr (MARK_NOW) tile[j * P + cols[r]] = kMarkNaN;
+        cols[r] = 255 - (int)(sel[g][r] & 0xffu);
+        colpk[i] |= (uint32_t)(cols[r] & 0xff) << (8 * r);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < ko && (cols[r] >> 3) == part) {
+          int rank = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rank += (q < ko && cols[q] < cols[r]) ? 1 : 0;
+          ocol[j * 4 + rank] = (uint8_t)cols[r];
+          oval[j * 4 + rank] = tile[j * P + cols[r]];
         }
       }
     }
   }
-  __syncthreads();
-  // the block's CSR slice, written by consecutive threads
+}
+
+// Writes the block's CSR slice staged in ocol/oval (consecutive threads) and its
+// row pointers (ko entries per token).
+template <int BK>
+__device__ __forceinline__ void write_csr(const uint8_t* ocol, const uint16_t* oval, int32_t* rowptr, uint8_t* col_out,
+                                          uint16_t* val_out, int64_t bh, int64_t T, int64_t t0, int ko) {
   for (int idx = threadIdx.x; idx < BK * ko; idx += kThreads) {
     const int j = idx / ko, r = idx % ko;
     col_out[(bh * T + t0) * ko + idx] = ocol[j * 4 + r];
@@ -380,38 +401,183 @@ __device__ __forceinline__ void block_outliers(uint16_t* tile, uint8_t* ocol, ui
   }
 }
 
+// The outlier positions get the quiet NaN in the tile (each by the thread that staged
+// the position).
 template <int D, int BK>
-__device__ __forceinline__ void mark_outliers(uint16_t* tile, const uint8_t* ocol, int ko) {
+__device__ __forceinline__ void mark_outliers(uint16_t* tile, const uint32_t (&colpk)[BK * D / 8 / kThreads], int ko) {
+  using S = Stage<D, BK>;
   constexpr int P = D + 8;
-  for (int idx = threadIdx.x; idx < BK * ko; idx += kThreads) {
-    const int j = idx / ko, r = idx % ko;
-    tile[j * P + ocol[j * 4 + r]] = kMarkNaN;
-  }
+  const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
+#pragma unroll
+  for (int i = 0; i < S::NC; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = (int)((colpk[i] >> (8 * r)) & 0xffu);
+      if (r < ko && (col >> 3) == part) tile[(i * S::RPS + r0) * P + col] = kMarkNaN;
+    }
 }
 
 // ---------------------------------------------------------------- phase 2b: clip
-// Exact order statistics of |x| (15-bit magnitudes) over the whole tile: radix
-// selection of rank kr = floor(q (n - 1)) and the next order statistic, then
+// Exact order statistics of |x| (15-bit magnitudes) over the whole tile, outliers
+// included: the element of rank kr = floor(q (n - 1)) and the next one, then
 // t = v_kr + frac * (v_kr+1 - v_kr) in fp64, each operation rounded separately.
+constexpr int kCandCap = 256;  // clip candidates per wave
 struct ClipSmem {
   uint32_t hist[256];
+  uint32_t ncand[kThreads / kWave];
+  uint16_t cand[kThreads / kWave][kCandCap];
 };
 
-template <int D, int BK>
+// The largest 15-bit magnitude among the thread's staged values.
+template <int NC>
+__device__ __forceinline__ uint32_t chunks_max(const uint4 (&v)[NC]) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, w[k] & 0x7fff7fffu));
+  }
+  return m2.x > m2.y ? m2.x : m2.y;
+}
+
+// Candidates, from the staged registers (gmax: the thread's largest magnitude): when the target's rank from the top,
+// rank_top, is below kThreads, each wave takes kk = ceil((rank_top + 1) / 4) and the
+// kk-th largest of its lanes' maxima m_w (a bitwise search on ballot counts); at least
+// kk of the wave's values are >= m_w, so at least rank_top + 1 values of the tile are
+// >= T = min_w m_w, and the target and the next larger value are among the values
+// >= T.  Each wave appends its values >= T to its own list.  Returns false (for every
+// thread) when the bound does not apply or a list overflowed.
+template <int NC>
+__device__ __forceinline__ bool clip_candidates(const uint4 (&v)[NC], uint32_t gmax, uint32_t rank_top, ClipSmem& cs,
+                                                Red& red) {
+  if (rank_top >= (uint32_t)kThreads) return false;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t kk = (rank_top + 4) / 4;
+  uint32_t pre = 0u;
+#pragma unroll
+  for (int bit = 14; bit >= 0; --bit) {
+    const uint32_t cand = pre | (1u << bit);
+    if ((uint32_t)__popcll(__ballot(gmax >= cand)) >= kk) pre = cand;
+  }
+  if (lane == 0) red.u[wave] = pre;
+  __syncthreads();
+  uint32_t T = red.u[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) T = min(T, red.u[w]);
+  uint16_t* lst = cs.cand[wave];
+  uint32_t base = 0u;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t x = (w[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+      const bool take = x >= T;
+      const uint64_t m = __ballot(take);
+      if (m != 0u) {
+        const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (take && pos < (uint32_t)kCandCap) lst[pos] = (uint16_t)x;
+        base += (uint32_t)__popcll(m);
+      }
+    }
+  }
+  if (lane == 0) cs.ncand[wave] = base;
+  __syncthreads();
+  bool ok = true;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) ok = ok && cs.ncand[w] <= (uint32_t)kCandCap;
+  return ok;
+}
+
+// The fp64 interpolation between the two order statistics, by thread 0, broadcast.
+__device__ __forceinline__ float clip_interp(uint32_t vk, uint32_t vk1, bool last, double frac, Red& red) {
+  if (threadIdx.x == 0) {
+    float t;
+    const double v0 = (double)h2f((uint16_t)vk);
+    if (last) {
+      t = (float)v0;
+    } else {
+      const double v1 = (double)h2f((uint16_t)vk1);
+      const double diff = v1 - v0;
+      const double prod = frac * diff;
+      const double sum = v0 + prod;
+      t = (float)sum;
+    }
+    red.thr = t;
+  }
+  __syncthreads();
+  return red.thr;
+}
+
+__device__ __forceinline__ void quantile_rank(float quantile, int nel, int64_t* kr, double* frac, uint32_t* rank_top) {
+  const double pos = (double)quantile * (double)(nel - 1);
+  *kr = (int64_t)floor(pos);
+  *frac = pos - (double)*kr;
+  *rank_top = (uint32_t)(nel - 1 - *kr);
+}
+
+// The two order statistics from the candidate lists: radix selection over the lists
+// only, from the top (8 high bits, then the 7 low bits inside the bin); the next
+// larger value is vk again unless exactly rank_top values exceed vk, then the
+// smallest candidate above vk.
+template <int NEL>
+__device__ __forceinline__ float clip_from_candidates(ClipSmem& cs, Red& red, float quantile) {
+  int64_t kr;
+  double frac;
+  uint32_t rank_top;
+  quantile_rank(quantile, NEL, &kr, &frac, &rank_top);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t nw = cs.ncand[wave];
+  const uint16_t* lst = cs.cand[wave];
+  for (int i = tid; i < 256; i += kThreads) cs.hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t e = lane; e < nw; e += kWave) atomicAdd(&cs.hist[lst[e] >> 7], 1u);
+  __syncthreads();
+  int bin1;
+  uint32_t above1;
+  find_bin_top(cs.hist, 256, rank_top, &bin1, &above1, red);
+  for (int i = tid; i < 128; i += kThreads) cs.hist[i] = 0u;
+  __syncthreads();
+  for (uint32_t e = lane; e < nw; e += kWave) {
+    const uint32_t x = lst[e];
+    if ((int)(x >> 7) == bin1) atomicAdd(&cs.hist[x & 127u], 1u);
+  }
+  __syncthreads();
+  int bin2;
+  uint32_t above2;
+  find_bin_top(cs.hist, 128, rank_top - above1, &bin2, &above2, red);
+  const uint32_t vk = ((uint32_t)bin1 << 7) | (uint32_t)bin2;
+  uint32_t vk1 = vk;
+  if (rank_top >= 1u && above1 + above2 == rank_top) {
+    uint32_t m = 0xffffffffu;
+    for (uint32_t e = lane; e < nw; e += kWave) {
+      const uint32_t x = lst[e];
+      m = x > vk ? min(m, x) : m;
+    }
+    vk1 = block_min_u32(m, red);
+  }
+  return clip_interp(vk, vk1, rank_top == 0u, frac, red);
+}
+
+// The same statistics from the whole tile (when the candidate bound does not
+// apply): radix selection of rank kr over all elements, 8 high bits then 7 low bits.
 // `group_max`: the largest magnitude among the values this thread staged.  Every
 // thread's values form a disjoint group, so at least kThreads values are >= the
 // smallest group maximum m; when the target's rank counted from the top is below
 // kThreads, the target is >= m, and the histogram pass skips every bin below m's.
-__device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& cs, Red& red, float quantile,
+template <int D, int BK>
+__device__ __forceinline__ float clip_from_tile(const uint16_t* tile, ClipSmem& cs, Red& red, float quantile,
                                                 uint32_t group_max) {
   constexpr int P = D + 8;
   constexpr int NEL = BK * D;
   constexpr int kChunks = NEL / 8;
   const int tid = threadIdx.x;
-  const double pos = (double)quantile * (double)(NEL - 1);
-  const int64_t kr = (int64_t)floor(pos);
-  const double frac = pos - (double)kr;
-  const uint32_t rank_top = (uint32_t)(NEL - 1 - kr);
+  int64_t kr;
+  double frac;
+  uint32_t rank_top;
+  quantile_rank(quantile, NEL, &kr, &frac, &rank_top);
   auto chunk = [&](int idx) -> uint4 {
     const int j = idx / (D / 8), part = idx % (D / 8);
     return *reinterpret_cast<const uint4*>(&tile[j * P + part * 8]);
@@ -476,22 +642,7 @@ __device__ __forceinline__ float clip_threshold(const uint16_t* tile, ClipSmem& 
       vk1 = block_min_u32(gt_min, red);
     }
   }
-  if (tid == 0) {
-    float t;
-    const double v0 = (double)h2f((uint16_t)vk);
-    if (kr + 1 >= NEL) {
-      t = (float)v0;
-    } else {
-      const double v1 = (double)h2f((uint16_t)vk1);
-      const double diff = v1 - v0;
-      const double prod = frac * diff;
-      const double sum = v0 + prod;
-      t = (float)sum;
-    }
-    red.thr = t;
-  }
-  __syncthreads();
-  return red.thr;
+  return clip_interp(vk, vk1, kr + 1 >= NEL, frac, red);
 }
 
 // ---------------------------------------------------------------- shared memory
@@ -534,36 +685,53 @@ struct ValueSmem {
 };
 
 // Steps 1, 2 and 2b for one tile; returns the clip threshold (0 without clipping).
+// The tile is written raw; the outliers are marked after the clip (which counts them).
 template <int D, int BK, bool OUTL, bool CLIP>
 __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uint16_t* oval, ClipSmem& cs, Red& red,
                                               const kvq_cache& c, bool is_key, const uint16_t* src_new,
                                               int64_t bh, int64_t n, int64_t old_len, int64_t n_new) {
+  using S = Stage<D, BK>;
   const int64_t T = c.cfg.capacity;
   const int64_t t0 = n * BK;
-  const uint32_t group_max = stage_tile<D, BK>(tile, is_key ? c.k_tail : c.v_tail, src_new, bh, t0, old_len, n_new);
-  __syncthreads();
+  uint4 v[S::NC];
+  stage_chunks<D, BK>(v, tile, is_key ? c.k_tail : c.v_tail, src_new, bh, t0, old_len, n_new);
   const int ko = kout_of(c.cfg);
-  if constexpr (OUTL) {
-    block_outliers<D, BK, !CLIP>(tile, ocol, oval, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
-                                 is_key ? c.k_val : c.v_val, bh, T, t0, ko);
-    __syncthreads();
-  }
-  float thr = 0.0f;
+  uint32_t gmax = 0u;
+  bool fast = false;
   if constexpr (CLIP) {
-    thr = clip_threshold<D, BK>(tile, cs, red, c.cfg.clip_quantile, group_max);
-    if constexpr (OUTL) {
-      mark_outliers<D, BK>(tile, ocol, ko);
-      __syncthreads();
-    }
+    int64_t kr;
+    double frac;
+    uint32_t rank_top;
+    quantile_rank(c.cfg.clip_quantile, BK * D, &kr, &frac, &rank_top);
+    gmax = chunks_max<S::NC>(v);
+    fast = clip_candidates<S::NC>(v, gmax, rank_top, cs, red);
   }
+  uint32_t colpk[S::NC];
+  if constexpr (OUTL) row_outliers<D, BK>(v, tile, ko, ocol, oval, colpk);
+  __syncthreads();  // the tile, the staged CSR slice and the candidate lists are complete
+  if constexpr (OUTL)
+    write_csr<BK>(ocol, oval, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
+                  is_key ? c.k_val : c.v_val, bh, T, t0, ko);
+  float thr = 0.0f;
+  if constexpr (CLIP)
+    thr = fast ? clip_from_candidates<BK * D>(cs, red, c.cfg.clip_quantile)
+               : clip_from_tile<D, BK>(tile, cs, red, c.cfg.clip_quantile, gmax);
+  // the clip's reads of the tile ended at its closing barrier
+  if constexpr (OUTL) mark_outliers<D, BK>(tile, colpk, ko);
   return thr;
 }
 
 // ---------------------------------------------------------------- keys
+// A key cell is held as its fp16 bits, two elements per register (element q of token
+// u in half q % 2 of xw[u][q / 2]), and converted where it is used.
+__device__ __forceinline__ float xel(const uint32_t (&xw)[8][4], int u, int q) {
+  return h2f((uint16_t)(xw[u][q >> 1] >> (16 * (q & 1))));
+}
+
 // Fast codes of a key cell packed into one word per token: element e = 2 (q % 4) + q / 4
 // of the cell sits at bits e KB of the word.
 template <int KB, bool OUTL, bool CLIP>
-__device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* zq, const float* rq, const float* aq,
+__device__ __forceinline__ void key_codes(const uint32_t (&xw)[8][4], const float* zq, const float* rq, const float* aq,
                                           const float* bq, const float* sq, int L, float thr, uint32_t* w) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -572,9 +740,10 @@ __device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* z
     for (int q = 0; q < 8; ++q) {
       bool near;
       float qc;
-      cf[q] = code_fast<OUTL, CLIP>(x[u][q], zq[q], rq[q], aq[q], bq[q], near, qc);
+      const float d = xel(xw, u, q);
+      cf[q] = code_fast<OUTL, CLIP>(d, zq[q], rq[q], aq[q], bq[q], near, qc);
       // rare: a quotient this close to a rounding boundary is decided exactly
-      if (near) cf[q] = code_near<OUTL, CLIP>(x[u][q], zq[q], sq[q], qc, (float)L, thr);
+      if (near) cf[q] = code_near<OUTL, CLIP>(d, zq[q], sq[q], qc, (float)L, thr);
     }
     uint32_t wu = 0;
     if constexpr (KB == 4) {
@@ -592,6 +761,8 @@ __device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* z
       for (int q = 0; q < 8; ++q) wu |= (uint32_t)cf[q] << ((2 * (q & 3) + (q >> 2)) * KB);
     }
     w[u] = wu;
+    // one token at a time: interleaving the tokens' exact-tie paths costs occupancy
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -602,7 +773,7 @@ __device__ __forceinline__ void key_codes(const float (&x)[8][8], const float* z
 // LUTB: 0 for uniform keys (code width from the configuration), else the code width
 // of codebook keys.
 template <int D, int BK, int LUTB, bool OUTL, bool CLIP>
-__global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
                                                                  int64_t old_len, int64_t n_new, int64_t n_first) {
   constexpr int P = D + 8;
   constexpr int NTG = BK / 8;
@@ -624,21 +795,22 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
 
   const bool active = NA * NTG == kThreads || tid < NA * NTG;
   const int a = tid / NTG, tg = tid % NTG;
-  float x[8][8];
+  uint32_t xw[8][4];
   float lo[8], hi[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) { lo[q] = __builtin_inff(); hi[q] = -__builtin_inff(); }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) xw[u][0] = xw[u][1] = xw[u][2] = xw[u][3] = 0u;
   if (active) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = tg + NTG * u;
       const uint2 wl = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + 4 * a]);
       const uint2 wh = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + D / 2 + 4 * a]);
-      const uint32_t hw[4] = {wl.x, wl.y, wh.x, wh.y};
+      xw[u][0] = wl.x; xw[u][1] = wl.y; xw[u][2] = wh.x; xw[u][3] = wh.y;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float v = h2f((uint16_t)(hw[q >> 1] >> (16 * (q & 1))));
-        x[u][q] = v;
+        const float v = xel(xw, u, q);
         lo[q] = fminf(lo[q], v);
         hi[q] = fmaxf(hi[q], v);
       }
@@ -690,6 +862,11 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
 
   const int rk = D * kb / 8;
   const int rkp = rk + 16;
+  // the cell is converted again below rather than kept as 64 floats since the statistics
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(xw[u][i]));
   if (active) {
     uint32_t w[8];
     if constexpr (!lut) {
@@ -711,9 +888,9 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
       }
       float sq[8];
       ld4(M.s, sq);
-      if (kb == 4) key_codes<4, OUTL, CLIP>(x, zq, rq, aq, bq, sq, L, thr, w);
-      else if (kb == 2) key_codes<2, OUTL, CLIP>(x, zq, rq, aq, bq, sq, L, thr, w);
-      else key_codes<3, OUTL, CLIP>(x, zq, rq, aq, bq, sq, L, thr, w);
+      if (kb == 4) key_codes<4, OUTL, CLIP>(xw, zq, rq, aq, bq, sq, L, thr, w);
+      else if (kb == 2) key_codes<2, OUTL, CLIP>(xw, zq, rq, aq, bq, sq, L, thr, w);
+      else key_codes<3, OUTL, CLIP>(xw, zq, rq, aq, bq, sq, L, thr, w);
     } else {
       // code = the number of midpoints below the value (ties to the lower entry)
       constexpr int NM = (1 << (lut ? LUTB : 1)) - 1;
@@ -733,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
           for (int k = 0; k < NM; ++k) md[k] *= -33554432.0f;
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const float d = x[u][q];
+            const float d = xel(xw, u, q);
             float st[NM];
 #pragma unroll
             for (int k = 0; k < NM; ++k)
@@ -749,11 +926,12 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(kvq_cache c, co
         } else {
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const float d = fminf(fmaxf(x[u][q], -thr), thr);
+            const float xv = xel(xw, u, q);
+            const float d = fminf(fmaxf(xv, -thr), thr);
             uint32_t cq = 0;
 #pragma unroll
             for (int k = 0; k < NM; ++k) cq += d > md[k] ? 1u : 0u;
-            if constexpr (OUTL) cq = (x[u][q] != x[u][q]) ? 0u : cq;
+            if constexpr (OUTL) cq = (xv != xv) ? 0u : cq;
             w[u] |= cq << (e * (lut ? LUTB : 1));
           }
         }
@@ -824,7 +1002,7 @@ __device__ __forceinline__ void vgroup_minmax(float* lo, float* hi, int lpg) {
 }
 
 template <int D, int BK, int VB, bool OUTL, bool CLIP>
-__global__ __launch_bounds__(kThreads) void quantize_values_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_values_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
                                                                    int64_t old_len, int64_t n_new, int64_t n_first) {
   constexpr int P = D + 8;
   constexpr int TPW = 32 / VB;

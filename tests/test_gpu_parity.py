@@ -143,6 +143,35 @@ def test_split_count_invariance_and_determinism(case):
         assert d <= 2e-5, S                     # fp32 reassociation only
 
 
+@pytest.mark.parametrize("kind", ["equal_magnitudes", "few_levels"])
+def test_clip_with_ties(kind):
+    """The 99th-percentile clip and the outlier split when magnitudes repeat: every
+    |x| equal (more candidates than the selection's lists hold, so the whole-tile
+    selection runs), and values on a coarse grid (ties at the threshold and between
+    outliers), compared bitwise with the oracle."""
+    import oracle
+    cfg, chunks = SMALL["clip_csr_append"]
+    say("case", kind, cfg)
+    k, v = inputs(cfg)
+    rng = np.random.default_rng(7)
+    f16 = lambda x: np.ascontiguousarray(x.astype(np.float16)).view(np.uint16)   # noqa: E731
+    if kind == "equal_magnitudes":
+        k = f16(np.where(rng.random(k.shape) < 0.5, -1.0, 1.0))
+        v = f16(np.where(rng.random(v.shape) < 0.5, -0.75, 0.75))
+    else:
+        k = f16(np.round(k.view(np.float16).astype(np.float32) * 2.0) / 2.0)
+        v = f16(np.round(v.view(np.float16).astype(np.float32) * 4.0) / 4.0)
+    cache = build_gpu_cache(cfg, k, v, chunks)
+    heads = oracle_heads(cfg, k, v)
+    ko = oracle.kout(cfg)
+    for (b, h), hc in heads.items():
+        compare_head(cache, hc, cfg, ko, b, h)
+    q = _q(cfg)
+    out = cache.decode(upload(q)).cpu().numpy().astype(np.float64)
+    ref = _decode_ref(cfg, heads, q, cfg["tokens"] - 1)
+    assert np.abs(out - ref).max() <= TOL
+
+
 @pytest.mark.parametrize("n", [1, 63, 64, 65])
 def test_short_caches(n):
     """Tail-only caches, exactly one block, one block plus one token."""
