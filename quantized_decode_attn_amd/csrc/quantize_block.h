@@ -339,23 +339,43 @@ __device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThre
       for (int k = 0; k < 8; ++k)
         key[g][k] = (((w[k >> 1] >> (16 * (k & 1))) & 0x7fffu) << 8) | (uint32_t)(255 - (8 * part + k));
     }
-    uint32_t sel[G][4], prev[G];
+    uint32_t sel[G][4];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      prev[g] = 0xffffffffu;
-      sel[g][0] = sel[g][1] = sel[g][2] = sel[g][3] = 0u;
-    }
+    for (int g = 0; g < G; ++g) sel[g][0] = sel[g][1] = sel[g][2] = sel[g][3] = 0u;
+    if (ko <= 2) {
+      // the lane's two largest keys by a merge tree, then the row's largest, then the
+      // row's largest among the other lanes' first and the owner's second
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (r < ko) {
+      for (int g = 0; g < G; ++g) {
+        uint32_t h[4], l[4];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          uint32_t m = 0u;
+        for (int p2 = 0; p2 < 4; ++p2) {
+          h[p2] = max(key[g][2 * p2], key[g][2 * p2 + 1]);
+          l[p2] = min(key[g][2 * p2], key[g][2 * p2 + 1]);
+        }
+        const uint32_t hA = max(h[0], h[1]), lA = max(min(h[0], h[1]), max(l[0], l[1]));
+        const uint32_t hB = max(h[2], h[3]), lB = max(min(h[2], h[3]), max(l[2], l[3]));
+        const uint32_t m1 = max(hA, hB), m2 = max(min(hA, hB), max(lA, lB));
+        const uint32_t M1 = lanes_max_u32<S::LPR>(m1);
+        sel[g][0] = M1;
+        if (ko == 2) sel[g][1] = lanes_max_u32<S::LPR>(m1 == M1 ? m2 : m1);
+      }
+    } else {
+      uint32_t prev[G];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) m = max(m, key[g][k] < prev[g] ? key[g][k] : 0u);
-          m = lanes_max_u32<S::LPR>(m);
-          sel[g][r] = m;
-          prev[g] = m;
+      for (int g = 0; g < G; ++g) prev[g] = 0xffffffffu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r < ko) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) m = max(m, key[g][k] < prev[g] ? key[g][k] : 0u);
+            m = lanes_max_u32<S::LPR>(m);
+            sel[g][r] = m;
+            prev[g] = m;
+          }
         }
       }
     }
@@ -428,32 +448,39 @@ struct ClipSmem {
   uint16_t cand[kThreads / kWave][kCandCap];
 };
 
-// The largest 15-bit magnitude among the thread's staged values.
+// The largest 15-bit magnitude of each of the thread's staged chunks.
 template <int NC>
-__device__ __forceinline__ uint32_t chunks_max(const uint4 (&v)[NC]) {
+__device__ __forceinline__ void chunk_maxima(const uint4 (&v)[NC], uint32_t (&cmax)[NC]) {
   typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-  us2 m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, w[k] & 0x7fff7fffu));
+    const us2 a = __builtin_elementwise_max(__builtin_bit_cast(us2, v[i].x & 0x7fff7fffu),
+                                            __builtin_bit_cast(us2, v[i].y & 0x7fff7fffu));
+    const us2 b = __builtin_elementwise_max(__builtin_bit_cast(us2, v[i].z & 0x7fff7fffu),
+                                            __builtin_bit_cast(us2, v[i].w & 0x7fff7fffu));
+    const us2 m = __builtin_elementwise_max(a, b);
+    cmax[i] = m.x > m.y ? m.x : m.y;
   }
-  return m2.x > m2.y ? m2.x : m2.y;
 }
 
-// Candidates, from the staged registers (gmax: the thread's largest magnitude): when the target's rank from the top,
+// Candidates (cmax: the thread's chunk maxima): when the target's rank from the top,
 // rank_top, is below kThreads, each wave takes kk = ceil((rank_top + 1) / 4) and the
 // kk-th largest of its lanes' maxima m_w (a bitwise search on ballot counts); at least
 // kk of the wave's values are >= m_w, so at least rank_top + 1 values of the tile are
 // >= T = min_w m_w, and the target and the next larger value are among the values
-// >= T.  Each wave appends its values >= T to its own list.  Returns false (for every
-// thread) when the bound does not apply or a list overflowed.
-template <int NC>
-__device__ __forceinline__ bool clip_candidates(const uint4 (&v)[NC], uint32_t gmax, uint32_t rank_top, ClipSmem& cs,
-                                                Red& red) {
+// >= T.  Each wave appends its values >= T to its own list, visiting only the chunks
+// whose maximum reaches T (read back from the tile the thread staged).  Returns false
+// (for every thread) when the bound does not apply or a list overflowed.
+template <int D, int BK>
+__device__ __forceinline__ bool clip_candidates(const uint16_t* tile, const uint32_t (&cmax)[BK * D / 8 / kThreads],
+                                                uint32_t rank_top, ClipSmem& cs, Red& red) {
+  using S = Stage<D, BK>;
+  constexpr int P = D + 8;
   if (rank_top >= (uint32_t)kThreads) return false;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t gmax = 0u;
+#pragma unroll
+  for (int i = 0; i < S::NC; ++i) gmax = max(gmax, cmax[i]);
   const uint32_t kk = (rank_top + 4) / 4;
   uint32_t pre = 0u;
 #pragma unroll
@@ -461,29 +488,39 @@ __device__ __forceinline__ bool clip_candidates(const uint4 (&v)[NC], uint32_t g
     const uint32_t cand = pre | (1u << bit);
     if ((uint32_t)__popcll(__ballot(gmax >= cand)) >= kk) pre = cand;
   }
-  if (lane == 0) red.u[wave] = pre;
+  if (lane == 0) {
+    red.u[wave] = pre;
+    cs.ncand[wave] = 0u;
+  }
   __syncthreads();
   uint32_t T = red.u[0];
 #pragma unroll
   for (int w = 1; w < kThreads / kWave; ++w) T = min(T, red.u[w]);
-  uint16_t* lst = cs.cand[wave];
-  uint32_t base = 0u;
+  uint32_t mask = 0u;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+  for (int i = 0; i < S::NC; ++i) mask |= (cmax[i] >= T ? 1u : 0u) << i;
+  uint16_t* lst = cs.cand[wave];
+  const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
+  while (mask != 0u) {
+    const int i = __builtin_ctz(mask);
+    mask &= mask - 1u;
+    const uint4 c4 = *reinterpret_cast<const uint4*>(&tile[(i * S::RPS + r0) * P + part * 8]);
+    const uint32_t w[4] = {c4.x, c4.y, c4.z, c4.w};
+    uint32_t x[8], n = 0u;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t x = (w[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
-      const bool take = x >= T;
-      const uint64_t m = __ballot(take);
-      if (m != 0u) {
-        const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (take && pos < (uint32_t)kCandCap) lst[pos] = (uint16_t)x;
-        base += (uint32_t)__popcll(m);
+      x[k] = (w[k >> 1] >> (16 * (k & 1))) & 0x7fffu;
+      n += x[k] >= T ? 1u : 0u;
+    }
+    uint32_t pos = atomicAdd(&cs.ncand[wave], n);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (x[k] >= T) {
+        if (pos < (uint32_t)kCandCap) lst[pos] = (uint16_t)x[k];
+        ++pos;
       }
     }
   }
-  if (lane == 0) cs.ncand[wave] = base;
   __syncthreads();
   bool ok = true;
 #pragma unroll
@@ -703,8 +740,11 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uin
     double frac;
     uint32_t rank_top;
     quantile_rank(c.cfg.clip_quantile, BK * D, &kr, &frac, &rank_top);
-    gmax = chunks_max<S::NC>(v);
-    fast = clip_candidates<S::NC>(v, gmax, rank_top, cs, red);
+    uint32_t cmax[S::NC];
+    chunk_maxima<S::NC>(v, cmax);
+#pragma unroll
+    for (int i = 0; i < S::NC; ++i) gmax = max(gmax, cmax[i]);
+    fast = clip_candidates<D, BK>(tile, cmax, rank_top, cs, red);
   }
   uint32_t colpk[S::NC];
   if constexpr (OUTL) row_outliers<D, BK>(v, tile, ko, ocol, oval, colpk);
