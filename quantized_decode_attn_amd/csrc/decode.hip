@@ -459,8 +459,17 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
   if (ntail > 0) Lsum = __builtin_fmaf(tail_l, wt, Lsum);
   const int d = tid % D, part = tid / D, nparts = blockDim.x / D;
   const int s0 = S * part / nparts, s1 = S * (part + 1) / nparts;
+  // eight loads in flight ahead of the fixed-order FMA chain
   float O = 0.0f;
-  for (int sp = s0; sp < s1; ++sp) O = __builtin_fmaf(base[(int64_t)sp * (D + 2) + 2 + d], wsh[sp], O);
+  int sp = s0;
+  for (; sp + 8 <= s1; sp += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = base[(int64_t)(sp + u) * (D + 2) + 2 + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) O = __builtin_fmaf(t[u], wsh[sp + u], O);
+  }
+  for (; sp < s1; ++sp) O = __builtin_fmaf(base[(int64_t)sp * (D + 2) + 2 + d], wsh[sp], O);
   osh[tid] = O;
   __syncthreads();
   if (part == 0) {
@@ -468,7 +477,15 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
     if (ntail > 0) {
       float ot = 0.0f;
       const uint16_t* vt = c.v_tail + bh * Bk * D + d;
-      for (int j = 0; j < ntail; ++j) ot = __builtin_fmaf(p_s[j], h2f(vt[(int64_t)j * D]), ot);
+      int j = 0;
+      for (; j + 8 <= ntail; j += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = h2f(vt[(int64_t)(j + u) * D]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ot = __builtin_fmaf(p_s[j + u], t[u], ot);
+      }
+      for (; j < ntail; ++j) ot = __builtin_fmaf(p_s[j], h2f(vt[(int64_t)j * D]), ot);
       O = __builtin_fmaf(ot, wt, O);
     }
     out[bq * D + d] = O / Lsum;
