@@ -23,8 +23,16 @@ struct MShape {
   static constexpr int TPW = 32 / VB;            // tokens per value word
   static constexpr int WPB = (BK / TPW) * D;     // value words per block
   static constexpr int NVI = WPB / 256;          // 16-byte value loads per lane per block
-  static constexpr int TPITCH = D + 4;           // floats per rotary-table row
+  // LDS copy of the rotary table: a row holds the (cos, sin) of one token offset for
+  // every pair, as 16-byte chunks ordered [chunk q4 of a lane][lane of the token], so
+  // the LPT lanes of a token read consecutive chunks; the pitch D + D/4 puts the
+  // tokens read together by one instruction into distinct bank groups as well
+  static constexpr int TPITCH = D + D / 4;       // floats per rotary-table row
   static constexpr int CHL = D / 4;              // lanes owning distinct value channels
+  // float offset of pair i's (cos, sin) in a row
+  static __host__ __device__ constexpr int tab_off(int i) {
+    return 4 * (LPT * ((i % PPL) / 2) + i / PPL) + 2 * (i % 2);
+  }
 };
 
 typedef float f2v __attribute__((ext_vector_type(2)));
@@ -165,15 +173,17 @@ __device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R,
   const int64_t m0 = (bh * T + n * BK) * ng;
   const uint16_t* vs = c.v_scale + m0;
   const uint16_t* vz = c.v_zero + m0;
+  // every load is issued (an element past the block's ne reads element 0, and its
+  // value goes unused): with no load under a branch, the compiler can keep the next
+  // block's loads in flight across the block loop instead of draining them
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
-    if (e < ne) {
-      const int grp = e / BK, t = e % BK;
-      const uint32_t m = (uint32_t)(t * ng + grp);
-      R.vs[k] = vs[m];
-      R.vz[k] = vz[m];
-    }
+    const bool in = e < ne;
+    const int grp = in ? e / BK : 0, t = in ? e % BK : 0;
+    const uint32_t m = (uint32_t)(t * ng + grp);
+    R.vs[k] = vs[m];
+    R.vz[k] = vz[m];
   }
 }
 
@@ -185,6 +195,27 @@ __device__ __forceinline__ float lanes_sum(float v) {
   if constexpr (N >= 8) asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
   static_assert(N <= 8, "groups of at most 8 lanes");
   return v;
+}
+
+// Four independent sums over aligned groups of N lanes (N in {4, 8}).  The DPP steps
+// of the four values are interleaved, so each DPP read of a register comes at least
+// three instructions after the write that produced it (the hazard needs two wait
+// states); one s_nop covers the writes made before the block.
+template <int N>
+__device__ __forceinline__ void lanes_sum4(float (&v)[4]) {
+  static_assert(N == 4 || N == 8, "groups of 4 or 8 lanes");
+#define KVQ_DPP4(ctl)                                                          \
+  "v_add_f32_dpp %0, %0, %0 " ctl " row_mask:0xf bank_mask:0xf\n\t"           \
+  "v_add_f32_dpp %1, %1, %1 " ctl " row_mask:0xf bank_mask:0xf\n\t"           \
+  "v_add_f32_dpp %2, %2, %2 " ctl " row_mask:0xf bank_mask:0xf\n\t"           \
+  "v_add_f32_dpp %3, %3, %3 " ctl " row_mask:0xf bank_mask:0xf\n\t"
+  if constexpr (N == 8)
+    asm("s_nop 1\n\t" KVQ_DPP4("quad_perm:[1,0,3,2]") KVQ_DPP4("quad_perm:[2,3,0,1]") KVQ_DPP4("row_half_mirror")
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+  else
+    asm("s_nop 1\n\t" KVQ_DPP4("quad_perm:[1,0,3,2]") KVQ_DPP4("quad_perm:[2,3,0,1]")
+        : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
+#undef KVQ_DPP4
 }
 
 // Maximum over the wave, returned wave-uniform: row maxima by DPP, then the

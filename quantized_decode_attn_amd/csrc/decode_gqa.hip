@@ -184,6 +184,13 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
   const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
 
+  // value scale/zero and outlier entries of this block: needed only after the scores,
+  // so they are loaded here rather than a block ahead.  Loads still in flight at the
+  // block's end would be drained there (the counter is in order, so waiting for them
+  // waits for the next block's code loads too).
+  gload_vmeta(R, c, bh, n, lane, NG);
+  if constexpr (OUTL) load_csr_tok<kBK, KO>(C, c, bh, n, lane);
+
   // ---- per-pair dequantization constants and block-rotated query weights (pair = lane)
   {
     const float sa = h2f(R.kmeta[0]) * inv_unit, sb = h2f(R.kmeta[1]) * inv_unit;
@@ -365,7 +372,6 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
       }
     }
   }
-  gload_vmeta(R, c, bh, nn, lane, NG);
   wave_lds_sync();
 
   // ---- values: D[(head, nibble)][channel] += sum over 64 tokens of nibble * code, per
@@ -452,7 +458,6 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
         }
       }
     }
-    load_csr_tok<kBK, KO>(C, c, bh, nn, lane);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int sh = vcorr_shift(wave_max_uniform(cmax[g]));
@@ -540,8 +545,6 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     CsrTok C;
     if (n0 < n1) {
       gload_kmeta(R, c, bh, n0, lane);
-      gload_vmeta(R, c, bh, n0, lane, NG);
-      if constexpr (OUTL) load_csr_tok<kBK, KO>(C, c, bh, n0, lane);
       const uint8_t* kb0 = gk_block(c, bh, n0);
       const uint8_t* vb0 = gv_block<VB>(c, bh, n0);
 #pragma unroll

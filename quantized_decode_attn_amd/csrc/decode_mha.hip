@@ -52,7 +52,7 @@ __host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut) {
   int o = 0;
   // uniform keys: A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB]; codebook keys: WR WI; one array per name
   m.wts = o; o += (lut ? 2 : outl ? 10 : 6) * (D / 2);
-  m.s = o; o += BK;                           // scores of the block's tokens
+  m.s = o; o += BK * (D / 16);                // token scores, as every lane of a token holds it
   m.ps = o; o += BK + 128;                    // quantized weights [2][BK] (u16) + nibble planes [2][64]
   m.vcorr = o; o += outl ? D + 4 : 0;         // value outlier corrections [D] (int), then the scale shift
   m.total = o;
@@ -132,6 +132,13 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   float* PS = wl + L.ps;
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);
 
+  // value scale/zero and outlier entries of this block: needed only after the scores,
+  // so they are loaded here rather than a block ahead (the loads then never stay in
+  // flight across the block loop, which would make the compiler drain every load
+  // before the next block)
+  load_vmeta(R, c, bh, n, lane, ng);
+  if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n, lane);
+
   // ---- block weights, one rotary pair per lane
   if (LUT && lane < Sh::HALF) {
     wA1[lane] = wq_r * R.eb_c - wq_i * R.eb_s;   // WR
@@ -191,14 +198,15 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   // rotary-table rows in registers one iteration ahead, so the LDS latency of the
   // next token's cos/sin overlaps this token's arithmetic
   float4 tq[2][4];
-  const float* tab0 = table + ts * Sh::TPITCH + 16 * r;
+  const float* tab0 = table + ts * Sh::TPITCH + 4 * r;
   auto load_tab = [&](int it, float4(&t)[4]) {
     const float* tab = tab0 + it * (Sh::TPI * Sh::TPITCH);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) t[q4] = *reinterpret_cast<const float4*>(tab + 4 * q4);
+    for (int q4 = 0; q4 < 4; ++q4) t[q4] = *reinterpret_cast<const float4*>(tab + 4 * Sh::LPT * q4);
   };
-  float* sc0 = Sc + ts;
   load_tab(0, tq[0]);
+  static_assert(Sh::NIT % 4 == 0, "token sums are reduced four iterations at a time");
+  float sb[4];
 #pragma unroll
   for (int it = 0; it < Sh::NIT; ++it) {
     if (it + 1 < Sh::NIT) load_tab(it + 1, tq[(it + 1) & 1]);
@@ -250,6 +258,9 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     } else {
       float ca[8], cb[8];
       unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
+      // the refill may not be hoisted above the last read of the slot: the load then
+      // writes the slot's own registers and stays in flight across the block loop
+      __builtin_amdgcn_sched_barrier(0);
       load_k(R, it, knext, koff);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -267,8 +278,12 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
         }
       }
     }
-    s = lanes_sum<Sh::LPT>(s);
-    if (r == 0) sc0[it * Sh::TPI] = s;
+    sb[it & 3] = s;
+    if ((it & 3) == 3) {
+      // every lane stores its four token sums (no branch in the loop)
+      lanes_sum4<Sh::LPT>(sb);
+      *reinterpret_cast<float4*>(Sc + ((it >> 2) * kWave + lane) * 4) = make_float4(sb[0], sb[1], sb[2], sb[3]);
+    }
   }
   wave_lds_sync();
 
@@ -278,7 +293,8 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 #pragma unroll
   for (int k = 0; k < TPL; ++k) {
     const int t = lane + kWave * k;
-    p[k] = Sc[t];
+    // token t = it TPI + ts sits in the copy of lane ts LPT (iteration group it / 4, slot it % 4)
+    p[k] = Sc[((t / Sh::TPI) >> 2) * (4 * kWave) + (t % Sh::TPI) * (4 * Sh::LPT) + ((t / Sh::TPI) & 3)];
     if constexpr (OUTL) {
       // key outliers of token t: code 0 (dequantized to the zero-point) was stored; add
       // the exact term (x - zero) of each CSR entry, rotated
@@ -289,7 +305,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
         const int i = col % Sh::HALF;
         const bool a = col < Sh::HALF;
         const float dl = val - (a ? wZA[i] : wZB[i]);
-        const float2 cssn = *reinterpret_cast<const float2*>(table + t * Sh::TPITCH + 2 * i);
+        const float2 cssn = *reinterpret_cast<const float2*>(table + t * Sh::TPITCH + Sh::tab_off(i));
         const float wr = wWR[i], wi = wWI[i];
         p[k] += a ? dl * (wr * cssn.x - wi * cssn.y) : -dl * (wi * cssn.x + wr * cssn.y);
       }
@@ -341,7 +357,6 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
       }
     }
   }
-  load_vmeta(R, c, bh, nn, lane, ng);
   wmax0 = wave_max_uniform(wmax0);
   if (ng > 1) wmax1 = wave_max_uniform(wmax1);
   // fixed-point scale and its inverse; they need only agree with each other
@@ -451,7 +466,6 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
         cmax = fmaxf(cmax, fabsf(cr[k][q]));
       }
     }
-    load_csr_tok<BK, KO>(C, c, bh, nn, lane);
     const int vsh = vcorr_shift(wave_max_uniform(cmax));
     if (lane == 0) VCI[D] = vsh;
 #pragma unroll
@@ -508,8 +522,6 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   if (n0 < n1) {
     if constexpr (LUT) load_eb(R, c, n0, lane);
     else load_kmeta(R, c, bh, n0, lane, 0);
-    load_vmeta(R, c, bh, n0, lane, ng);
-    if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n0, lane);
     const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
     const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
 #pragma unroll
@@ -547,14 +559,15 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   }
 }
 
-// Copies the cos/sin(j f_i) table of a block's offsets into LDS ([Bk][D/2] float2
-// rows at a pitch of D + 4 floats).
+// Copies the cos/sin(j f_i) table of a block's offsets into LDS (rows of MShape's
+// pitch, pair i at MShape::tab_off(i)).
 template <int D, int BK, int NT>
 __device__ __forceinline__ void stage_rope(float* table, const kvq_cache& c) {
-  constexpr int HALF = D / 2, TPITCH = D + 4;
-  for (int idx = threadIdx.x; idx < BK * HALF; idx += NT) {
-    const int j = idx / HALF, i = idx % HALF;
-    *reinterpret_cast<float2*>(table + j * TPITCH + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
+  using Sh = MShape<D, BK, 4, 4>;
+  for (int idx = threadIdx.x; idx < BK * Sh::HALF; idx += NT) {
+    const int j = idx / Sh::HALF, i = idx % Sh::HALF;
+    *reinterpret_cast<float2*>(table + j * Sh::TPITCH + Sh::tab_off(i)) =
+        *reinterpret_cast<const float2*>(c.rope + 2 * idx);
   }
 }
 
