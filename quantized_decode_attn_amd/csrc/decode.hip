@@ -36,6 +36,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kFinishMaxSplits = 4096;  // split weights staged in LDS (fp32)
+constexpr int kFinishFastSplits = 16;   // merged by one thread per channel with no barrier
 
 template <int D, int KB, int KMODE, int VB>
 struct Shape {
@@ -384,9 +385,41 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
   const int64_t bh = (int64_t)b * H + h;
   const int64_t nfull = c.length / Bk;
   const int ntail = with_tail ? (int)(c.length - nfull * Bk) : 0;
+  const int tid = threadIdx.x;
+  if (ntail == 0 && S <= kFinishFastSplits) {
+    // No tail and few splits: each channel's thread loads every split's (m, l) and its
+    // own partial output at once (one memory round trip, no barriers) and merges them
+    // in split order:  M = max m_s,  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+    if (tid >= D) return;
+    const float* base = ws + bq * (int64_t)S * (D + 2);
+    float mv[kFinishFastSplits], lv[kFinishFastSplits], ov[kFinishFastSplits];
+#pragma unroll
+    for (int sp = 0; sp < kFinishFastSplits; ++sp) {
+      if (sp < S) {
+        const float* pp = base + (int64_t)sp * (D + 2);
+        mv[sp] = pp[0];
+        lv[sp] = pp[1];
+        ov[sp] = pp[2 + tid];
+      }
+    }
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int sp = 0; sp < kFinishFastSplits; ++sp)
+      if (sp < S) M = fmaxf(M, mv[sp]);
+    float Lsum = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < kFinishFastSplits; ++sp) {
+      if (sp < S) {
+        const float w = mv[sp] == -__builtin_inff() ? 0.0f : exp2f(mv[sp] - M);  // empty split: 0
+        Lsum = __builtin_fmaf(lv[sp], w, Lsum);
+        O = __builtin_fmaf(ov[sp], w, O);
+      }
+    }
+    out[bq * D + tid] = O / Lsum;
+    return;
+  }
   __shared__ float wr_s[128], wi_s[128], p_s[128], red[8];
   __shared__ float tail_m, tail_l;
-  const int tid = threadIdx.x;
   if (ntail > 0) {
     if (tid < half) {
       const uint16_t* qv = q + bq * D;
