@@ -66,6 +66,25 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t (&w)[KW], float (&ca
   }
 }
 
+// 4-bit codes of one lane's 8 rotary pairs as exact fp16 subnormals, for FMAs that read
+// them with v_fma_mix_f32 (no conversion instruction): a nibble masked into bits 0-3
+// of a 16-bit half is the fp16 value c * 2^-24, one in bits 4-7 is c * 2^-20.  Byte b
+// of dword d holds pair 4 d + b (code_a low, code_b high); bytes 0 and 2 are read in
+// place, bytes 1 and 3 after one shift, so 8 codes cost 5 bit operations.  The caller
+// scales code_a coefficients by 2^24 and code_b coefficients by 2^20.
+typedef _Float16 h2t __attribute__((ext_vector_type(2)));
+template <int KW>
+__device__ __forceinline__ void unpack4_f16(const uint32_t (&w)[KW], float (&ca)[8], float (&cb)[8]) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const uint32_t t = w[d] >> 8;
+    const h2t a02 = __builtin_bit_cast(h2t, w[d] & 0x000F000Fu), b02 = __builtin_bit_cast(h2t, w[d] & 0x00F000F0u);
+    const h2t a13 = __builtin_bit_cast(h2t, t & 0x000F000Fu), b13 = __builtin_bit_cast(h2t, t & 0x00F000F0u);
+    ca[4 * d] = (float)a02.x; ca[4 * d + 2] = (float)a02.y; ca[4 * d + 1] = (float)a13.x; ca[4 * d + 3] = (float)a13.y;
+    cb[4 * d] = (float)b02.x; cb[4 * d + 2] = (float)b02.y; cb[4 * d + 1] = (float)b13.x; cb[4 * d + 3] = (float)b13.y;
+  }
+}
+
 // All global data of one block that a wave needs, held in registers.
 // KS key slots: a whole block (the default) or half of one, refilled twice per block;
 // PPL rotary pairs per lane.

@@ -171,7 +171,7 @@ __device__ __forceinline__ int tau(int q, int m) {
 
 template <int VB, int KO, int NG>
 __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, float* __restrict__ wl, const GLds& L,
-                                          const float* __restrict__ table, float inv_unit, int lane, int G, int ng,
+                                          const float* __restrict__ table, int lane, int G, int ng,
                                           const kvq_cache& c, int64_t bh, int64_t n, bool more) {
   constexpr bool OUTL = KO > 0;
   constexpr int TPW = 32 / VB;
@@ -193,7 +193,9 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 
   // ---- per-pair dequantization constants and block-rotated query weights (pair = lane)
   {
-    const float sa = h2f(R.kmeta[0]) * inv_unit, sb = h2f(R.kmeta[1]) * inv_unit;
+    // codes are read as fp16 subnormals (code_a * 2^-24, code_b * 2^-20): the scales
+    // carry the inverse powers of two, so the products are exact as before
+    const float sa = h2f(R.kmeta[0]) * 0x1p24f, sb = h2f(R.kmeta[1]) * 0x1p20f;
     *reinterpret_cast<float4*>(Meta + 4 * lane) = make_float4(sa, h2f(R.kmeta[2]), sb, h2f(R.kmeta[3]));
     const float4 q01 = *reinterpret_cast<const float4*>(wl + L.wq + 8 * lane);
     const float4 q23 = *reinterpret_cast<const float4*>(wl + L.wq + 8 * lane + 4);
@@ -251,10 +253,13 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
         const int d = (w % 8) / 2;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const uint32_t lo = words[hf][d] & 0x0F0F0F0Fu, hi = (words[hf][d] >> 4) & 0x0F0F0F0Fu;
-          const f2v a01 = cvt_lo(lo), a23 = cvt_hi(lo), b01 = cvt_lo(hi), b23 = cvt_hi(hi);
-          ca[hf][0] = a01.x; ca[hf][1] = a01.y; ca[hf][2] = a23.x; ca[hf][3] = a23.y;
-          cb[hf][0] = b01.x; cb[hf][1] = b01.y; cb[hf][2] = b23.x; cb[hf][3] = b23.y;
+          // nibbles masked into bits 0-3 / 4-7 of a 16-bit half are exact fp16 subnormals,
+          // read in place by the dequantizing FMAs (v_fma_mix_f32)
+          const uint32_t x = words[hf][d], t = x >> 8;
+          const h2t a02 = __builtin_bit_cast(h2t, x & 0x000F000Fu), b02 = __builtin_bit_cast(h2t, x & 0x00F000F0u);
+          const h2t a13 = __builtin_bit_cast(h2t, t & 0x000F000Fu), b13 = __builtin_bit_cast(h2t, t & 0x00F000F0u);
+          ca[hf][0] = (float)a02.x; ca[hf][1] = (float)a13.x; ca[hf][2] = (float)a02.y; ca[hf][3] = (float)a13.y;
+          cb[hf][0] = (float)b02.x; cb[hf][1] = (float)b13.x; cb[hf][2] = (float)b02.y; cb[hf][3] = (float)b13.y;
         }
       }
       if (w + 1 < kHalf / 2) load_win(w + 1, L[(w + 1) & 1]);
@@ -497,7 +502,6 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     for (int k = lane; k < 4 * kD + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
   __syncthreads();
 
-  const float inv_unit = 1.0f / cvt_lo(1u).x;  // the fp8 value of the byte 1 is a power of two
   const int64_t total_waves = (int64_t)gridDim.x * kGqaWaves;
   for (int64_t item = (int64_t)blockIdx.x * kGqaWaves + wave; item < nitems; item += total_waves) {
     const int split = (int)(item % S);
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
       for (int s = 0; s < GRegs<VB>::NVI; ++s) gload_v(R, s, vb0, lane);
     }
     for (int64_t n = n0; n < n1; ++n)
-      gqa_block<VB, KO, NG>(R, C, st, wl, L, table, inv_unit, lane, G, NG, c, bh, n, n + 1 < n1);
+      gqa_block<VB, KO, NG>(R, C, st, wl, L, table, lane, G, NG, c, bh, n, n + 1 < n1);
 
     if (OUTL) {  // the item's last block of value corrections
       merge_vcorr_heads(reinterpret_cast<int*>(wl + L.vcorr), st, lane);

@@ -19,8 +19,9 @@
 //    value load, the metadata) is refilled with block n+1 right after its last use
 //    in block n, so a whole block of loads stays in flight;
 //  * a key token is covered by 8 lanes (4 for head_dim 64), 8 rotary pairs each,
-//    coalesced 4- or 8-byte loads; uniform codes become floats two at a time with the
-//    packed fp8 conversion (a byte 0..15 is an exact fp8 value proportional to it);
+//    coalesced 4- or 8-byte loads; 4-bit codes masked into 16-bit halves are exact fp16
+//    subnormals that the FMAs read in place (v_fma_mix_f32), 2-bit codes become floats
+//    two at a time with the packed fp8 conversion (a small byte is an exact fp8 value);
 //  * scores go to LDS; each lane then owns two tokens (one for 64-token blocks) for
 //    the softmax, the outlier corrections ([KVC3] "Per-Vector Dense-and-Sparse
 //    Quantization": code 0 is stored at an outlier, the exact value sits in the CSR)
@@ -149,11 +150,14 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     const float wi = wq_r * R.eb_s + wq_i * R.eb_c;
     const float al = h2f(R.kmeta[0]), be = h2f(R.kmeta[1]);
     const float za = h2f(R.kmeta[2]), zb = h2f(R.kmeta[3]);
-    wA1[lane] = wr * al * inv_unit;
-    wB1[lane] = -wi * be * inv_unit;
+    // code units: 4-bit codes are read as fp16 subnormals (code_a * 2^-24, code_b * 2^-20),
+    // 2-bit codes as fp8 values; powers of two, so the products are unchanged
+    const float ua = KB == 4 ? 0x1p24f : inv_unit, ub = KB == 4 ? 0x1p20f : inv_unit;
+    wA1[lane] = wr * al * ua;
+    wB1[lane] = -wi * be * ub;
     wZ1[lane] = wr * za - wi * zb;
-    wA2[lane] = -wi * al * inv_unit;
-    wB2[lane] = -wr * be * inv_unit;
+    wA2[lane] = -wi * al * ua;
+    wB2[lane] = -wr * be * ub;
     wZ2[lane] = -(wi * za + wr * zb);
     if constexpr (OUTL) {
       wWR[lane] = wr;
@@ -257,7 +261,8 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
       }
     } else {
       float ca[8], cb[8];
-      unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
+      if constexpr (KB == 4) unpack4_f16<Sh::KW>(R.k[it], ca, cb);
+      else unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
       // the refill may not be hoisted above the last read of the slot: the load then
       // writes the slot's own registers and stays in flight across the block loop
       __builtin_amdgcn_sched_barrier(0);
