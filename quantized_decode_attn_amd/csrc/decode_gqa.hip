@@ -172,10 +172,10 @@ __device__ __forceinline__ int tau(int q, int m) {
 template <int VB, int KO, int NG>
 __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, float* __restrict__ wl, const GLds& L,
                                           const float* __restrict__ table, int lane, int G, int ng,
-                                          const kvq_cache& c, int64_t bh, int64_t n, bool more) {
+                                          const kvq_cache& c, int64_t bh, int64_t n, int nstep, bool more) {
   constexpr bool OUTL = KO > 0;
   constexpr int TPW = 32 / VB;
-  const int64_t nn = more ? n + 1 : n;
+  const int64_t nn = more ? n + nstep : n;
   const uint8_t* knext = gk_block(c, bh, nn);
   const uint8_t* vnext = gv_block<VB>(c, bh, nn);
   float* Meta = wl + L.meta;
@@ -510,7 +510,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     const int64_t bh = rest / nsets;
     const int h = (int)(bh % H);
     const int b = (int)(bh / H);
-    const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
+    // split `split` takes blocks split, split + S, ...: the waves of a workgroup hold
+    // consecutive splits, so together they stream neighbouring blocks
+    const int64_t n0 = split;
 
     // query weights of pair `lane` per head: scale * conj(q_g,i) e^{-i f_i q_pos} (fp64)
     float wq_r[4], wq_i[4];
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
 
     GRegs<VB> R;
     CsrTok C;
-    if (n0 < n1) {
+    if (n0 < nfull) {
       gload_kmeta(R, c, bh, n0, lane);
       const uint8_t* kb0 = gk_block(c, bh, n0);
       const uint8_t* vb0 = gv_block<VB>(c, bh, n0);
@@ -558,8 +560,8 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
 #pragma unroll
       for (int s = 0; s < GRegs<VB>::NVI; ++s) gload_v(R, s, vb0, lane);
     }
-    for (int64_t n = n0; n < n1; ++n)
-      gqa_block<VB, KO, NG>(R, C, st, wl, L, table, lane, G, NG, c, bh, n, n + 1 < n1);
+    for (int64_t n = n0; n < nfull; n += S)
+      gqa_block<VB, KO, NG>(R, C, st, wl, L, table, lane, G, NG, c, bh, n, S, n + S < nfull);
 
     if (OUTL) {  // the item's last block of value corrections
       merge_vcorr_heads(reinterpret_cast<int*>(wl + L.vcorr), st, lane);

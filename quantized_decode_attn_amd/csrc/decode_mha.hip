@@ -110,13 +110,13 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               const uint32_t* __restrict__ ptab, float wq_r, float wq_i,
                                               float inv_unit, int lane, int ts, int r, uint32_t sh, int G, int ng,
-                                              const kvq_cache& c, int64_t bh, int64_t n, bool more,
+                                              const kvq_cache& c, int64_t bh, int64_t n, int nstep, bool more,
                                               uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
   constexpr bool OUTL = KO > 0;
   static_assert(!(LUT && OUTL), "codebook keys with outliers take the generic kernel");
   constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
-  const int64_t nn = more ? n + 1 : n;
+  const int64_t nn = more ? n + nstep : n;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
   const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, nn);
   float* wA1 = wl + L.wts;
@@ -502,7 +502,10 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
   const int h = (int)(bh % H);
   const int b = (int)(bh / H);
-  const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
+  // split `split` takes blocks split, split + S, split + 2 S, ...: the waves of a
+  // workgroup hold consecutive splits of one head, so at any time they stream
+  // neighbouring blocks (contiguous runs of HBM rather than S scattered streams)
+  const int64_t n0 = split;
 
   // query weight of pair `lane`: scale * conj(q_i) * e^{-i f_i q_pos}, evaluated in fp64
   float wq_r = 0.0f, wq_i = 0.0f;
@@ -524,7 +527,7 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
 
   BlockRegs<D, BK, KB, VB> R;
   CsrTok C;
-  if (n0 < n1) {
+  if (n0 < nfull) {
     if constexpr (LUT) load_eb(R, c, n0, lane);
     else load_kmeta(R, c, bh, n0, lane, 0);
     const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
@@ -534,9 +537,9 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
   }
-  for (int64_t n = n0; n < n1; ++n)
+  for (int64_t n = n0; n < nfull; n += S)
     process_block<D, BK, KB, VB, KO, LUT>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
-                                          c, bh, n, n + 1 < n1, koff);
+                                          c, bh, n, S, n + S < nfull, koff);
   if (OUTL) {
     wave_lds_sync();
     int* vci = reinterpret_cast<int*>(wl + L.vcorr);
