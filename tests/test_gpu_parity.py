@@ -143,6 +143,43 @@ def test_split_count_invariance_and_determinism(case):
         assert d <= 2e-5, S                     # fp32 reassociation only
 
 
+# Caches whose length is a whole number of blocks (no fp16 tail): the split merge then
+# takes its one-round path for at most 16 splits and the LDS path above that.
+NOTAIL = {
+    "mha": synth.config("c1", batch=2, q_heads=4, kv_heads=4, tokens=20 * 128, capacity=20 * 128),
+    "gqa_csr": synth.config("c2", batch=1, q_heads=8, kv_heads=2, tokens=12 * 128, capacity=12 * 128),
+    "clip_csr": synth.config("c4", batch=1, q_heads=2, kv_heads=2, tokens=10 * 128, capacity=10 * 128,
+                             existing=0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(NOTAIL))
+def test_merge_without_tail(case):
+    cfg = NOTAIL[case]
+    say("case", case)
+    k, v = inputs(cfg)
+    lut = _lut(cfg)
+    cache = build_gpu_cache(cfg, k, v, None, lut)
+    heads = oracle_heads(cfg, k, v, lut)
+    q = _q(cfg)
+    qd = upload(q)
+    q_pos = cfg["tokens"] - 1
+    ref = _decode_ref(cfg, heads, q, q_pos)
+    nblk = cfg["tokens"] // cfg["k_block"]
+    outs = {}
+    # 16 and 17 straddle the one-round merge; nblk + 3 leaves some splits without a block
+    for S in (1, 7, 16, 17, nblk + 3):
+        a = cache.decode(qd, q_pos=q_pos, num_splits=S).cpu().numpy()
+        b = cache.decode(qd, q_pos=q_pos, num_splits=S).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), S
+        err = np.abs(a.astype(np.float64) - ref).max()
+        say("  splits", S, "max abs err", err)
+        assert err <= TOL, S
+        outs[S] = a
+    for S in outs:
+        assert np.abs(outs[S] - outs[1]).max() <= 2e-5, S   # fp32 reassociation only
+
+
 @pytest.mark.parametrize("kind", ["equal_magnitudes", "few_levels"])
 def test_clip_with_ties(kind):
     """The 99th-percentile clip and the outlier split when magnitudes repeat: every
