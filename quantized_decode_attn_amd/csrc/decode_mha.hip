@@ -263,9 +263,6 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
       float ca[8], cb[8];
       if constexpr (KB == 4) unpack4_f16<Sh::KW>(R.k[it], ca, cb);
       else unpack_pairs<KB, Sh::KW>(R.k[it], ca, cb);
-      // the refill may not be hoisted above the last read of the slot: the load then
-      // writes the slot's own registers and stays in flight across the block loop
-      __builtin_amdgcn_sched_barrier(0);
       load_k(R, it, knext, koff);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
