@@ -122,12 +122,14 @@ __device__ __forceinline__ void load_k_slot(BlockRegs<D, BK, KB, VB, KS, PPL>& R
   using Sh = MShape<D, BK, KB, VB, PPL>;
   const uint8_t* kc = kblk + koff + it * (Sh::TPI * Sh::RK);
   static_assert(Sh::KW >= 1, "a lane reads at least one dword of codes per token");
+  // codes are read once: non-temporal loads
   if constexpr (Sh::KW == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(kc);
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    const u2v x = __builtin_nontemporal_load(reinterpret_cast<const u2v*>(kc));
     R.k[slot][0] = x.x;
     R.k[slot][1] = x.y;
   } else {
-    R.k[slot][0] = *reinterpret_cast<const uint32_t*>(kc);
+    R.k[slot][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kc));
   }
 }
 template <int D, int BK, int KB, int VB>
@@ -137,7 +139,9 @@ __device__ __forceinline__ void load_k(BlockRegs<D, BK, KB, VB>& R, int it, cons
 
 template <int D, int BK, int KB, int VB, int KS, int PPL>
 __device__ __forceinline__ void load_v(BlockRegs<D, BK, KB, VB, KS, PPL>& R, int i, const uint8_t* vblk, int lane) {
-  R.v[i] = *reinterpret_cast<const uint4*>(vblk + (uint32_t)(i * 64 + lane) * 16u);
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(vblk + (uint32_t)(i * 64 + lane) * 16u));
+  R.v[i] = make_uint4(x.x, x.y, x.z, x.w);
 }
 
 template <int D, int BK, int KB, int VB, int KS, int PPL>
@@ -264,16 +268,17 @@ __device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int6
 #pragma unroll
   for (int k = 0; k < BK / kWave; ++k) {
     const int t = lane + kWave * k;
+    // outlier entries are read once: non-temporal loads
     if constexpr (KO == 2) {
-      C.kc[k] = *reinterpret_cast<const uint16_t*>(c.k_col + e0 + 2 * t);
-      C.vc[k] = *reinterpret_cast<const uint16_t*>(c.v_col + e0 + 2 * t);
-      C.kv[k] = *reinterpret_cast<const uint32_t*>(c.k_val + e0 + 2 * t);
-      C.vv[k] = *reinterpret_cast<const uint32_t*>(c.v_val + e0 + 2 * t);
+      C.kc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(c.k_col + e0 + 2 * t));
+      C.vc[k] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(c.v_col + e0 + 2 * t));
+      C.kv[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c.k_val + e0 + 2 * t));
+      C.vv[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c.v_val + e0 + 2 * t));
     } else {
-      C.kc[k] = c.k_col[e0 + t];
-      C.vc[k] = c.v_col[e0 + t];
-      C.kv[k] = c.k_val[e0 + t];
-      C.vv[k] = c.v_val[e0 + t];
+      C.kc[k] = __builtin_nontemporal_load(c.k_col + e0 + t);
+      C.vc[k] = __builtin_nontemporal_load(c.v_col + e0 + t);
+      C.kv[k] = __builtin_nontemporal_load(c.k_val + e0 + t);
+      C.vv[k] = __builtin_nontemporal_load(c.v_val + e0 + t);
     }
   }
 }

@@ -100,6 +100,8 @@ __device__ __forceinline__ const uint8_t* gv_block(const kvq_cache& c, int64_t b
 // Key row slot q (16 bytes) of half hf: token 64 hf + lane.
 template <int VB>
 __device__ __forceinline__ void gload_k(GRegs<VB>& R, int hf, int q, const uint8_t* kblk, int lane) {
+  // plain loads: non-temporal ones made this kernel slower (c2 decode +3.6%), unlike the
+  // one-head kernels
   R.k[hf][q] = *reinterpret_cast<const uint4*>(kblk + (uint32_t)((kHalf * hf + lane) * (kD / 2) + 16 * q));
 }
 // Value load s = (kc WPL + j) 2 + hc: word j of the 16 tokens 64 kc + 16 (lane / 16) ..

@@ -87,7 +87,7 @@ template <int D, int BK, int KB, int VB>
 __device__ __forceinline__ void load_codes(BlockRegs<D, BK, KB, VB>& R, int it, const uint8_t* kblk, uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
   if constexpr (KB == 3) {
-    const u32x2 x = *reinterpret_cast<const u32x2_a4*>(kblk + koff + it * (Sh::TPI * Sh::RK));
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4*>(kblk + koff + it * (Sh::TPI * Sh::RK)));
     R.k[it][0] = x.x;
     R.k[it][1] = x.y;
   } else {

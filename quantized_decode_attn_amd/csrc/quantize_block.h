@@ -308,7 +308,10 @@ __device__ __forceinline__ void stage_chunks(uint4 (&v)[BK * D / 8 / kThreads], 
     const int64_t t = t0 + j;
     const uint16_t* row = t < old_len ? tail + (bh * BK + (t - tail0)) * D
                                       : src_new + (bh * n_new + (t - old_len)) * D;
-    v[i] = *reinterpret_cast<const uint4*>(row + part * 8);
+    // the new fp16 tokens are read once: non-temporal loads
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(row + part * 8));
+    v[i] = make_uint4(x.x, x.y, x.z, x.w);
   }
 #pragma unroll
   for (int i = 0; i < S::NC; ++i)
