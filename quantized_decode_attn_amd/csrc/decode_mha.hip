@@ -105,6 +105,40 @@ __device__ __forceinline__ void load_eb(BlockRegs<D, BK, KB, VB>& R, const kvq_c
   }
 }
 
+// Block weights of the block whose metadata R holds, one rotary pair per lane, into the
+// wave's LDS area: codebook keys WR WI; uniform keys A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB]
+// (W = query weight rotated by the block's first position, folded with scale and zero).
+template <int D, int BK, int KB, int VB, int KO, bool LUT>
+__device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, VB>& R, float* wb, float wq_r,
+                                                    float wq_i, float inv_unit, int lane) {
+  constexpr int HALF = D / 2;
+  if (lane >= HALF) return;
+  const float wr = wq_r * R.eb_c - wq_i * R.eb_s;
+  const float wi = wq_r * R.eb_s + wq_i * R.eb_c;
+  if constexpr (LUT) {
+    wb[lane] = wr;
+    wb[HALF + lane] = wi;
+  } else {
+    const float al = h2f(R.kmeta[0]), be = h2f(R.kmeta[1]);
+    const float za = h2f(R.kmeta[2]), zb = h2f(R.kmeta[3]);
+    // code units: 4-bit codes are read as fp16 subnormals (code_a * 2^-24, code_b * 2^-20),
+    // 2-bit codes as fp8 values; powers of two, so the products are unchanged
+    const float ua = KB == 4 ? 0x1p24f : inv_unit, ub = KB == 4 ? 0x1p20f : inv_unit;
+    wb[lane] = wr * al * ua;                       // A1
+    wb[HALF + lane] = -wi * be * ub;               // B1
+    wb[2 * HALF + lane] = wr * za - wi * zb;       // Z1
+    wb[3 * HALF + lane] = -wi * al * ua;           // A2
+    wb[4 * HALF + lane] = -wr * be * ub;           // B2
+    wb[5 * HALF + lane] = -(wi * za + wr * zb);    // Z2
+    if constexpr (KO > 0) {
+      wb[6 * HALF + lane] = wr;                    // WR
+      wb[7 * HALF + lane] = wi;                    // WI
+      wb[8 * HALF + lane] = za;                    // ZA
+      wb[9 * HALF + lane] = zb;                    // ZB
+    }
+  }
+}
+
 template <int D, int BK, int KB, int VB, int KO, bool LUT>
 __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTok& C, MState& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
@@ -119,6 +153,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   const int64_t nn = more ? n + nstep : n;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
   const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, nn);
+  // this block's weights were written during the previous block (or at the item's start)
   float* wA1 = wl + L.wts;
   float* wB1 = wA1 + Sh::HALF;
   float* wZ1 = wB1 + Sh::HALF;
@@ -140,32 +175,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   load_vmeta(R, c, bh, n, lane, ng);
   if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n, lane);
 
-  // ---- block weights, one rotary pair per lane
-  if (LUT && lane < Sh::HALF) {
-    wA1[lane] = wq_r * R.eb_c - wq_i * R.eb_s;   // WR
-    wB1[lane] = wq_r * R.eb_s + wq_i * R.eb_c;   // WI
-  }
-  if (!LUT && lane < Sh::HALF) {
-    const float wr = wq_r * R.eb_c - wq_i * R.eb_s;
-    const float wi = wq_r * R.eb_s + wq_i * R.eb_c;
-    const float al = h2f(R.kmeta[0]), be = h2f(R.kmeta[1]);
-    const float za = h2f(R.kmeta[2]), zb = h2f(R.kmeta[3]);
-    // code units: 4-bit codes are read as fp16 subnormals (code_a * 2^-24, code_b * 2^-20),
-    // 2-bit codes as fp8 values; powers of two, so the products are unchanged
-    const float ua = KB == 4 ? 0x1p24f : inv_unit, ub = KB == 4 ? 0x1p20f : inv_unit;
-    wA1[lane] = wr * al * ua;
-    wB1[lane] = -wi * be * ub;
-    wZ1[lane] = wr * za - wi * zb;
-    wA2[lane] = -wi * al * ua;
-    wB2[lane] = -wr * be * ub;
-    wZ2[lane] = -(wi * za + wr * zb);
-    if constexpr (OUTL) {
-      wWR[lane] = wr;
-      wWI[lane] = wi;
-      wZA[lane] = za;
-      wZB[lane] = zb;
-    }
-  }
+  // ---- the next block's metadata (its weights are written during this block's values)
   if constexpr (LUT) load_eb(R, c, nn, lane);
   else load_kmeta(R, c, bh, nn, lane, 0);
   wave_lds_sync();
@@ -403,6 +413,10 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   }
   wave_lds_sync();
 
+  // ---- the next block's weights: this block's were last read by its softmax (key
+  // outliers); writing them here lets their LDS round trip overlap the value dot products
+  write_block_weights<D, BK, KB, VB, KO, LUT>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
+
   // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
   // sum_t w_t * code_t by 4-bit integer dot products over the four weight nibbles
   const int ch0 = (4 * lane) % D;
@@ -527,6 +541,7 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   if (n0 < nfull) {
     if constexpr (LUT) load_eb(R, c, n0, lane);
     else load_kmeta(R, c, bh, n0, lane, 0);
+    write_block_weights<D, BK, KB, VB, KO, LUT>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
     const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
     const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
 #pragma unroll
