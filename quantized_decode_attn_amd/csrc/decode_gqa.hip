@@ -186,6 +186,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
   const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
 
+  __builtin_amdgcn_s_setprio(0);
   // value scale/zero and outlier entries of this block: needed only after the scores,
   // so they are loaded here rather than a block ahead.  Loads still in flight at the
   // block's end would be drained there (the counter is in order, so waiting for them
@@ -296,6 +297,10 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
     S[0] = sc[0][0] + sc[0][1];
     S[1] = sc[1][0] + sc[1][1];
   }
+
+  // the block's serial part (softmax, value weights, value MFMAs, outliers) runs at a
+  // raised wave priority, the score loop at the base one
+  __builtin_amdgcn_s_setprio(1);
 
   // ---- online softmax per head; lane owns tokens lane and 64 + lane
   float p[2][4];
