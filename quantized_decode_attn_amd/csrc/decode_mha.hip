@@ -175,7 +175,6 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   load_vmeta(R, c, bh, n, lane, ng);
   if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n, lane);
 
-  __builtin_amdgcn_s_setprio(0);
   // ---- the next block's metadata (its weights are written during this block's values)
   if constexpr (LUT) load_eb(R, c, nn, lane);
   else load_kmeta(R, c, bh, nn, lane, 0);
@@ -209,6 +208,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- scores, summed over a token's lanes and written to LDS by its first lane
   // rotary-table rows in registers one iteration ahead, so the LDS latency of the
   // next token's cos/sin overlaps this token's arithmetic
@@ -302,7 +302,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 
   // the block's serial part (softmax, value weights, planes, value dot products) runs at
   // a raised wave priority, so that its short dependency chains win issue slots over the
-  // other wave's score loop; the score loop runs at the base priority
+  // other wave's score loop; the priority drops back at the next block's score loop
   __builtin_amdgcn_s_setprio(1);
 
   // ---- online softmax in base 2; lane owns tokens lane + 64 k
