@@ -254,6 +254,18 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Sum over the wave, returned wave-uniform (same DPP pattern as wave_max_uniform: every
+// lane of a row holds the row sum after the mirrors, the row_bcast steps add the rows).
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 
 // Outlier CSR entries (KO = 1 or 2 per token) of the lane's tokens lane + 64 k
 // (k < BK / 64) of a block: a token's columns in one u8/u16, its values in one u16/u32,
@@ -286,11 +298,12 @@ __device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int6
 // Value-outlier corrections p * (x - zero) are scattered into an LDS channel array with
 // integer adds (ds_add_u32 runs several times faster than ds_add_f32): every block's
 // corrections of one head are fixed point with the power-of-two scale 2^sh chosen from
-// the wave's largest |correction| m < 2^e, sh = 22 - e, so each term is below 2^22 in
-// magnitude and up to 256 terms per channel stay below 2^30.  The rounding error is at
-// most m 2^-23 per term.
-__device__ __forceinline__ int vcorr_shift(float max_abs_uniform) {
-  return 22 - __builtin_amdgcn_frexp_expf(max_abs_uniform);
+// the sum A < 2^e of |correction| over the whole wave, sh = 30 - e.  Every channel sum,
+// and every term, then stays below 2^30 in magnitude, and the rounding error is at most
+// 2^-31 2^e <= 2^-30 A per term: at most BK 2^-30 A per channel and block (a channel
+// takes at most one term per token), i.e. fp32-class relative to the corrections' total.
+__device__ __forceinline__ int vcorr_shift(float abs_sum_uniform) {
+  return 30 - __builtin_amdgcn_frexp_expf(abs_sum_uniform);
 }
 __device__ __forceinline__ int vcorr_fixed(float c, int sh) {
   return (int)__builtin_rintf(__builtin_amdgcn_ldexpf(c, sh));

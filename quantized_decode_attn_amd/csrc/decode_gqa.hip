@@ -18,10 +18,10 @@
 //    heads' weights (lane l supplies head l % 4) with the 64 tokens' khat, so after
 //    the 128 channels lane l holds the scores of its token for all four heads --
 //    no cross-lane reduction;
-//  * values: the weights p * scale of a block are quantized per head to 16-bit fixed
-//    point (relative to a bound on the block's largest weight) and split into four
-//    nibbles, so that sum_t w_t c_t is an exact integer product: one
-//    v_mfma_i32_16x16x64_i8 takes the 16 rows (head, nibble) against 16 channels and
+//  * values: the weights p * scale of a block are quantized per head to 30-bit fixed
+//    point (relative to a bound on the block's largest weight) and written as four
+//    signed base-256 digits, so that sum_t w_t c_t is an exact integer product: one
+//    v_mfma_i32_16x16x64_i8 takes the 16 rows (head, digit) against 16 channels and
 //    64 tokens, the codes spread from the packed words into bytes (16 instructions
 //    per block instead of 256 fp32 outer products);
 //  * outliers ([KVC3] "Per-Vector Dense-and-Sparse Quantization"): code 0 was stored
@@ -44,7 +44,7 @@ constexpr int kGqaWaves = 8;
 constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;  // floats per rotary-table row: 64 (cos, sin) pairs + 4 (banks)
 constexpr int kWAP = 2 * kHalf + 4;  // floats per head of the query weights (distinct banks per head)
-constexpr int kW16P = kHalf + 4;     // dwords per head of the fixed-point value weights
+constexpr int kW32P = kHalf + 4;     // dwords per (head, token half) of the fixed-point value weights
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -62,14 +62,14 @@ __device__ __forceinline__ i4 mfma_i8(i4 a, i4 b, i4 c) {
 
 // Per-wave LDS area, in floats.
 struct GLds {
-  int meta, wa, w16, vcorr, wq, total;
+  int meta, wa, w32, vcorr, wq, total;
 };
 __host__ __device__ inline GLds gqa_lds(int ng, bool outl) {
   GLds m;
   int o = 0;
   m.meta = o; o += 4 * kHalf;        // per pair: scale_a / u, zero_a, scale_b / u, zero_b
   m.wa = o; o += 4 * kWAP;           // per head and pair: (W_r, -W_i)
-  m.w16 = o; o += ng * 4 * kW16P;    // fixed-point value weights [group][head][lane]: tokens lane, 64 + lane (u16)
+  m.w32 = o; o += ng * 8 * kW32P;    // value weights as digits [group][head][half][lane]: token 64 half + lane
   m.vcorr = o; o += outl ? 4 * kD + 4 : 0;  // value outlier corrections [head][channel] (int), scale per head
   m.wq = o; o += kHalf * 8;          // the item's query weights per pair: (re, im) of 4 heads
   m.total = o;
@@ -182,7 +182,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   const uint8_t* vnext = gv_block<VB>(c, bh, nn);
   float* Meta = wl + L.meta;
   float* WA = wl + L.wa;
-  uint32_t* W16 = reinterpret_cast<uint32_t*>(wl + L.w16);  // [group][head][lane]
+  uint32_t* W32 = reinterpret_cast<uint32_t*>(wl + L.w32);  // [group][head][half][lane]
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
   const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
 
@@ -356,11 +356,14 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 #pragma unroll
   for (int t = 0; t < 8; ++t) st.acc[t] *= alpha_hd;
 
-  // ---- value weights w = p * scale of [group][head][token] in 16-bit fixed point: the
-  // weights of head g and group k are at most pmax_g * (the block's largest scale of
-  // group k), so w / bound converts to unorm16 (rounded, clamped at 65535) and the
-  // integer products below are exact; the zero-point part p * zero is summed per lane
-  // in fp32.  Element lane + 64 k is token 64 (k % 2) + lane of group k / 2.
+  // ---- value weights w = p * scale of [group][head][token] in 30-bit fixed point: the
+  // weights of head g and group k are at most bound = pmax_g * (the block's largest
+  // scale of group k), so W = rint(w 2^30 / bound) <= 2^30 (1 + 2^-21).  W is stored as
+  // four balanced base-256 digits d_r in [-128, 127], W = sum_r d_r 256^r: the bytes of
+  // (W + 0x80808080) ^ 0x80808080 read as int8 (exact for W < 0x7F7F7F80).  Each weight
+  // is then exact up to half a unit (2^-31 bound) and the fp32 rounding of w 2^30 / bound,
+  // and the integer products below are exact; the zero-point part p * zero is summed
+  // per lane in fp32.  Element lane + 64 k is token 64 (k % 2) + lane of group k / 2.
   float vzc[4] = {0.f, 0.f, 0.f, 0.f}, inv_hd[2] = {0.f, 0.f};
   {
     float vsf[4], vmax[2] = {0.f, 0.f};
@@ -376,42 +379,44 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float bound = pmax[g] * vmax[grp];
-        const float rb = bound > 0x1p-100f ? __builtin_amdgcn_rcpf(bound) : 0.0f;
-        const auto w = __builtin_amdgcn_cvt_pknorm_u16(p[0][g] * vsf[2 * grp] * rb, p[1][g] * vsf[2 * grp + 1] * rb);
-        W16[(grp * 4 + g) * kW16P + lane] = __builtin_bit_cast(uint32_t, w);
+        const float kq = bound > 0x1p-100f ? 0x1p30f * __builtin_amdgcn_rcpf(bound) : 0.0f;
+        const uint32_t w0 = (uint32_t)__builtin_rintf(p[0][g] * vsf[2 * grp] * kq);
+        const uint32_t w1 = (uint32_t)__builtin_rintf(p[1][g] * vsf[2 * grp + 1] * kq);
+        W32[((grp * 4 + g) * 2) * kW32P + lane] = (w0 + 0x80808080u) ^ 0x80808080u;
+        W32[((grp * 4 + g) * 2 + 1) * kW32P + lane] = (w1 + 0x80808080u) ^ 0x80808080u;
         st.zpart[g][grp] = __builtin_fmaf(p[0][g], vzc[2 * grp], __builtin_fmaf(p[1][g], vzc[2 * grp + 1], st.zpart[g][grp]));
-        inv_hd[grp] = hd == g ? bound * (1.0f / 65535.0f) : inv_hd[grp];
+        inv_hd[grp] = hd == g ? bound * 0x1p-30f : inv_hd[grp];
       }
     }
   }
   wave_lds_sync();
 
-  // ---- values: D[(head, nibble)][channel] += sum over 64 tokens of nibble * code, per
+  // ---- values: D[(head, digit)][channel] += sum over 64 tokens of digit * code, per
   // token half kc and channel tile T (channels 64 (T / 4) + 4 (lane % 16) + T % 4)
   {
     constexpr int WPL = GRegs<VB>::WPL;
-    // A: row lane % 16 = (head h_a, nibble pl), tokens 16 (lane / 16) + tau(q, m) of both
-    // halves; a W16 dword holds a token's weight of half 0 (low) and half 1 (high)
+    // A: row lane % 16 = (head h_a, digit pl), tokens 16 (lane / 16) + tau(q, m) of each
+    // half: byte pl of the tokens' digit words, gathered four at a time by v_perm
     const int h_a = (lane >> 2) & 3, pl = lane & 3, lg = lane >> 4;
+    const uint32_t sel = (uint32_t)pl | ((uint32_t)(4 + pl) << 8) | 0x0C0C0000u;  // byte pl of S1, of S0, zeros
     i4 A[2][NG];
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
-      const uint4* wr = reinterpret_cast<const uint4*>(W16 + (grp * 4 + h_a) * kW16P + 16 * lg);
-      uint32_t x[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 e = wr[u];
-        x[4 * u] = (e.x >> (4 * pl)) & 0x000F000Fu;
-        x[4 * u + 1] = (e.y >> (4 * pl)) & 0x000F000Fu;
-        x[4 * u + 2] = (e.z >> (4 * pl)) & 0x000F000Fu;
-        x[4 * u + 3] = (e.w >> (4 * pl)) & 0x000F000Fu;
-      }
+      for (int kc = 0; kc < 2; ++kc) {
+        const uint4* wr = reinterpret_cast<const uint4*>(W32 + ((grp * 4 + h_a) * 2 + kc) * kW32P + 16 * lg);
+        uint32_t x[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t ylo = x[tau<VB>(q, 0)] | (x[tau<VB>(q, 1)] << 8);
-        const uint32_t yhi = x[tau<VB>(q, 2)] | (x[tau<VB>(q, 3)] << 8);
-        A[0][grp][q] = (int)__builtin_amdgcn_perm(yhi, ylo, 0x05040100u);
-        A[1][grp][q] = (int)__builtin_amdgcn_perm(yhi, ylo, 0x07060302u);
+        for (int u = 0; u < 4; ++u) {
+          const uint4 e = wr[u];
+          x[4 * u] = e.x; x[4 * u + 1] = e.y; x[4 * u + 2] = e.z; x[4 * u + 3] = e.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t ab = __builtin_amdgcn_perm(x[tau<VB>(q, 1)], x[tau<VB>(q, 0)], sel);
+          const uint32_t cd = __builtin_amdgcn_perm(x[tau<VB>(q, 3)], x[tau<VB>(q, 2)], sel);
+          A[kc][grp][q] = (int)__builtin_amdgcn_perm(cd, ab, 0x05040100u);
+        }
       }
     }
     i4 Dt[8];
@@ -442,12 +447,14 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
         for (int j = 0; j < WPL; ++j) gload_v(R, (kc * WPL + j) * 2 + hc, vnext, lane);
       }
     }
-    // lane holds rows 4 hd + r (nibble r of head hd) of its channel in every tile
+    // lane holds rows 4 hd + r (digit r of head hd) of its channel in every tile; a row
+    // sum is at most 128 x 128 x 15 in magnitude (the top digit's at most 128 x 64 x 15),
+    // so the digit pairs combine exactly in 32 bits before the fp32 conversion
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint32_t tot = (uint32_t)Dt[t][0] + ((uint32_t)Dt[t][1] << 4) + ((uint32_t)Dt[t][2] << 8) +
-                           ((uint32_t)Dt[t][3] << 12);
-      st.acc[t] = __builtin_fmaf((float)tot, inv_hd[NG == 2 ? t >> 2 : 0], st.acc[t]);
+      const int hi = Dt[t][3] * 256 + Dt[t][2], lo = Dt[t][1] * 256 + Dt[t][0];
+      const float inv = inv_hd[NG == 2 ? t >> 2 : 0];
+      st.acc[t] = __builtin_fmaf((float)hi, inv * 65536.0f, __builtin_fmaf((float)lo, inv, st.acc[t]));
     }
   }
 
@@ -456,7 +463,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   if constexpr (OUTL) {
     float cr[2][KO][4];
     int col[2][KO];
-    float cmax[4] = {0.f, 0.f, 0.f, 0.f};
+    float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -466,13 +473,13 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           cr[k][qq][g] = p[k][g] * dl;
-          cmax[g] = fmaxf(cmax[g], fabsf(cr[k][qq][g]));
+          csum[g] += fabsf(cr[k][qq][g]);
         }
       }
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int sh = vcorr_shift(wave_max_uniform(cmax[g]));
+      const int sh = vcorr_shift(wave_sum_uniform(csum[g]));
       if (lane == 0) VCI[4 * kD + g] = sh;
 #pragma unroll
       for (int k = 0; k < 2; ++k)

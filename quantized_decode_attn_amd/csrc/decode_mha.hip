@@ -28,7 +28,7 @@
 //    and the value weights;
 //  * values are stored as words of consecutive tokens of one channel, so a 16-byte
 //    load gives each lane 4 channels x (32 / v_bits) tokens; the per-token weights
-//    p*scale are quantized per block to 16-bit fixed point and split into four
+//    p*scale are quantized per block to 32-bit fixed point and split into eight
 //    nibble planes, and the value update is v_dot8_u32_u4 on the packed codes
 //    (no unpacking, 8 codes per instruction and plane).
 // The pages' fusion advice ([TQ] sections 5.1 and 6.3) is the design: no dequantized
@@ -43,6 +43,7 @@ namespace {
 using namespace dcm;
 
 constexpr int kMhaWaves = 8;  // two waves per SIMD
+constexpr float kW32Span = 4294901760.0f;  // 2^32 - 2^16: full scale of the fixed-point value weights
 
 // Per-wave LDS area, in floats.
 struct MLds {
@@ -53,8 +54,9 @@ __host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut) {
   int o = 0;
   // uniform keys: A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB]; codebook keys: WR WI; one array per name
   m.wts = o; o += (lut ? 2 : outl ? 10 : 6) * (D / 2);
-  m.s = o; o += BK * (D / 16);                // token scores, as every lane of a token holds it
-  m.ps = o; o += BK + 128;                    // quantized weights [2][BK] (u16) + nibble planes [2][64]
+  m.s = o; o += BK * (D / 16);                // token scores, as every lane of a token holds it;
+                                              // then the fixed-point value weights [2][BK] (u32)
+  m.ps = o; o += 256;                         // nibble planes of the value weights [2][16][8]
   m.vcorr = o; o += outl ? D + 4 : 0;         // value outlier corrections [D] (int), then the scale shift
   m.total = o;
   return m;
@@ -349,11 +351,15 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   }
 
   // ---- value weights w_t = p_t * scale_t per [group][token], quantized per block to
-  // 16-bit fixed point (relative to the block maximum) for the integer dot products;
-  // the zero-point part p_t * zero_t is summed in fp32.  Element lane + 64 k is token
-  // (64 k) % BK + lane of group (64 k) / BK, so its probability is p[((64 k) % BK) / 64].
-  uint16_t* Wq16 = reinterpret_cast<uint16_t*>(PS);                       // [2][BK]
-  uint32_t* PLN = reinterpret_cast<uint32_t*>(PS) + BK;                     // [2][64] nibble planes
+  // 32-bit fixed point for the integer dot products: W = rint(w K) with
+  // K = (2^32 - 2^16) / (the block's largest weight), so W < 2^32 and each weight is
+  // exact up to half a unit (2^-33 of the block maximum) plus the fp32 rounding of w K
+  // (2^-24 of w itself): fp32-class accuracy for every weight, however small next to
+  // the block maximum.  The zero-point part p_t * zero_t is summed in fp32.  Element
+  // lane + 64 k is token (64 k) % BK + lane of group (64 k) / BK, so its probability is
+  // p[((64 k) % BK) / 64].
+  uint32_t* W32 = reinterpret_cast<uint32_t*>(Sc);                        // [2][BK], over the scores
+  uint32_t* PLN = reinterpret_cast<uint32_t*>(PS);                        // [2][16][8] nibble planes
   float wv[4], vzc[4];
   float wmax0 = 0.0f, wmax1 = 0.0f;
 #pragma unroll
@@ -377,43 +383,57 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   }
   wmax0 = wave_max_uniform(wmax0);
   if (ng > 1) wmax1 = wave_max_uniform(wmax1);
-  // fixed-point scale and its inverse; they need only agree with each other
-  const float kq0 = wmax0 > 0.0f ? 65535.0f * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
-  const float kq1 = wmax1 > 0.0f ? 65535.0f * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
+  // fixed-point scale and its inverse; they need only agree with each other (to fp32
+  // rounding).  wmax * K <= (2^32 - 2^16)(1 + 2^-23) stays below 2^32.
+  const float kq0 = wmax0 > 0.0f ? kW32Span * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
+  const float kq1 = wmax1 > 0.0f ? kW32Span * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
+  wave_lds_sync();  // every lane has read its scores before the weights overwrite them
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
     if (kWave * k < BK * ng) {
       const float kq = (kWave * k) / BK == 0 ? kq0 : kq1;
-      Wq16[e] = (uint16_t)__builtin_rintf(wv[k] * kq);
+      W32[e] = (uint32_t)__builtin_rintf(wv[k] * kq);
     }
   }
   wave_lds_sync();
-  // nibble planes: plane k of a token group holds nibble k of each token's weight,
-  // token u of the group at bits [4u, 4u+4) (the bit position of its code in a word)
+  // nibble planes: plane n of a token group holds nibble n of each token's weight,
+  // token u of the group at bits [4u, 4u+4) (the bit position of its code in a word);
+  // a lane builds planes kk and kk + 4 of one token group
   for (int grp = 0; grp < ng; ++grp) {
-    const uint16_t* wg = Wq16 + grp * BK;
-    uint32_t plane = 0;
+    const uint32_t* wg = W32 + grp * BK;
+    uint32_t plo = 0, phi = 0;
     if constexpr (VB == 4) {
       const int tg = lane >> 2, kk = lane & 3;           // 16 groups of 8 tokens
       if (tg < BK / 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(wg + 8 * tg);
-        const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+        const uint4 w0 = *reinterpret_cast<const uint4*>(wg + 8 * tg);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(wg + 8 * tg + 4);
+        const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          plane |= ((d[u >> 1] >> (16 * (u & 1) + 4 * kk)) & 15u) << (4 * u);
-        PLN[grp * 64 + lane] = plane;
+        for (int u = 0; u < 8; ++u) {
+          plo |= __builtin_amdgcn_ubfe(d[u], 4 * kk, 4) << (4 * u);
+          phi |= __builtin_amdgcn_ubfe(d[u], 4 * kk + 16, 4) << (4 * u);
+        }
+        PLN[grp * 128 + 8 * tg + kk] = plo;
+        PLN[grp * 128 + 8 * tg + 4 + kk] = phi;
       }
     } else {
       const int tg = lane >> 3, par = (lane >> 2) & 1, kk = lane & 3;   // 8 groups of 16 tokens
       if (tg < BK / 16) {
-        const uint4 w0 = *reinterpret_cast<const uint4*>(wg + 16 * tg);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(wg + 16 * tg + 8);
-        const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t d[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)   // token 2u + par of the group
-          plane |= ((d[u] >> (16 * par + 4 * kk)) & 15u) << (4 * u);
-        PLN[grp * 64 + lane] = plane;
+        for (int h = 0; h < 4; ++h) {  // tokens 2u + par of the group
+          const uint4 w = *reinterpret_cast<const uint4*>(wg + 16 * tg + 4 * h);
+          d[2 * h] = par ? w.y : w.x;
+          d[2 * h + 1] = par ? w.w : w.z;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          plo |= __builtin_amdgcn_ubfe(d[u], 4 * kk, 4) << (4 * u);
+          phi |= __builtin_amdgcn_ubfe(d[u], 4 * kk + 16, 4) << (4 * u);
+        }
+        PLN[grp * 128 + 16 * tg + 8 * par + kk] = plo;
+        PLN[grp * 128 + 16 * tg + 8 * par + 4 + kk] = phi;
       }
     }
   }
@@ -424,50 +444,55 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   write_block_weights<D, BK, KB, VB, KO, LUT>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
 
   // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
-  // sum_t w_t * code_t by 4-bit integer dot products over the four weight nibbles
+  // sum_t w_t * code_t by 4-bit integer dot products over the eight weight nibbles, in
+  // two passes (bits 16..31, then 0..15) that share the accumulator registers.  A plane
+  // sum is at most BK * 15 * 15 = 28,800, so four planes combine exactly in 32 bits.
   const int ch0 = (4 * lane) % D;
   const int grp0 = ch0 / G;
-  uint32_t ia[4][4];
+  const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / kW32Span);
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int pass = 0; pass < 2; ++pass) {
+    const int poff = pass == 0 ? 4 : 0;  // plane offset within a token group's eight
+    uint32_t ia[4][4];
 #pragma unroll
-    for (int pl = 0; pl < 4; ++pl) ia[k][pl] = 0;
+    for (int k = 0; k < 4; ++k)
 #pragma unroll
-  for (int i = 0; i < Sh::NVI; ++i) {
-    const int g = i * (256 / D) + (4 * lane) / D;
-    const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
-    if constexpr (VB == 4) {
-      const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 4 * g);
+      for (int pl = 0; pl < 4; ++pl) ia[k][pl] = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        ia[k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[k][0], false);
-        ia[k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[k][1], false);
-        ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
-        ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
-      }
-    } else {
-      const uint4 pe = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 8 * g);
-      const uint4 po = *reinterpret_cast<const uint4*>(PLN + grp0 * 64 + 8 * g + 4);
+    for (int i = 0; i < Sh::NVI; ++i) {
+      const int g = i * (256 / D) + (4 * lane) / D;
+      const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+      if constexpr (VB == 4) {
+        const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 8 * g + poff);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
-        ia[k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[k][0], false);
-        ia[k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[k][1], false);
-        ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
-        ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
-        ia[k][0] = __builtin_amdgcn_udot8(po.x, od, ia[k][0], false);
-        ia[k][1] = __builtin_amdgcn_udot8(po.y, od, ia[k][1], false);
-        ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
-        ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
+        for (int k = 0; k < 4; ++k) {
+          ia[k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[k][0], false);
+          ia[k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[k][1], false);
+          ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
+          ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
+        }
+      } else {
+        const uint4 pe = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + poff);
+        const uint4 po = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + 8 + poff);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
+          ia[k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[k][0], false);
+          ia[k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[k][1], false);
+          ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
+          ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
+          ia[k][0] = __builtin_amdgcn_udot8(po.x, od, ia[k][0], false);
+          ia[k][1] = __builtin_amdgcn_udot8(po.y, od, ia[k][1], false);
+          ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
+          ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
+        }
       }
     }
-  }
-  {
-    const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / 65535.0f);
+    const float unit = pass == 0 ? inv * 65536.0f : inv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t tot = ia[k][0] + (ia[k][1] << 4) + (ia[k][2] << 8) + (ia[k][3] << 12);
-      st.acc[k] = __builtin_fmaf((float)tot, inv, st.acc[k]);
+      st.acc[k] = __builtin_fmaf((float)tot, unit, st.acc[k]);
     }
   }
 
@@ -477,7 +502,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   if constexpr (OUTL) {
     float cr[TPL][KO];
     int col[TPL][KO];
-    float cmax = 0.0f;
+    float csum = 0.0f;
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
 #pragma unroll
@@ -485,10 +510,10 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
         col[k][q] = (int)((C.vc[k] >> (8 * q)) & 0xffu);
         const float dl = h2f((uint16_t)(C.vv[k] >> (16 * q))) - (col[k][q] >= G ? vzc[TPL + k] : vzc[k]);
         cr[k][q] = p[k] * dl;
-        cmax = fmaxf(cmax, fabsf(cr[k][q]));
+        csum += fabsf(cr[k][q]);
       }
     }
-    const int vsh = vcorr_shift(wave_max_uniform(cmax));
+    const int vsh = vcorr_shift(wave_sum_uniform(csum));
     if (lane == 0) VCI[D] = vsh;
 #pragma unroll
     for (int k = 0; k < TPL; ++k)

@@ -1,0 +1,206 @@
+"""Error bounds of the decode kernels' fixed-point value arithmetic, checked on the CPU.
+
+The decode kernels form the value contraction sum_t w_t c_t of a block (w_t = p_t *
+scale_t, c_t a packed value code) as integer dot products over fixed-point weights,
+and add the value-outlier corrections p_t (x_t - zero_t) through integer LDS atomics.
+This file emulates that integer arithmetic exactly (numpy, float32 where the kernels
+use fp32) and checks the bounds the kernels rely on:
+
+* one head per kv head: W = rint(w K), K = (2^32 - 2^16) / max w, summed as eight
+  nibble planes in two passes; error <= 2^-33 max(w) sum(c) (+ fp32-relative terms);
+* grouped-query: W = rint(w 2^30 / bound), written as four balanced base-256 digits
+  (the bytes of (W + 0x80808080) ^ 0x80808080 read as int8), summed by int8 products;
+* outlier corrections: fixed point with the shift taken from the sum A of |terms|,
+  error <= 2^-30 A per term.
+
+It also shows that the 16-bit weights used before miss the 2e-3 decode tolerance by
+an order of magnitude on a peaked block, which is why the wider forms exist.  CPU only.
+"""
+import numpy as np
+import pytest
+
+f32 = np.float32
+RNG = np.random.default_rng(11)
+
+
+def peaked_block(bk=128, ratio_log2=17.2, vmax_code=15, seed=0):
+    """One dominant token (p = 1, code 0) and bk - 1 tokens at weight ratio 2^-r at the
+    top code, value scale 16/15 (a row spanning [-8, 8]); returns p, scale, codes [bk][4]."""
+    rng = np.random.default_rng(seed)
+    p = np.full(bk, 2.0 ** -ratio_log2, np.float32)
+    p[0] = 1.0
+    s = np.full(bk, f32(16.0 / 15.0), np.float32)
+    c = np.full((bk, 4), vmax_code, np.int64)
+    c[0] = 0
+    c[1:, rng.integers(0, 4)] = 0
+    return p, s, c
+
+
+def random_block(bk=128, bits=4, spread=12.0, seed=0):
+    rng = np.random.default_rng(seed)
+    p = np.exp2(-rng.random(bk) * spread).astype(np.float32)
+    s = (rng.random(bk) * 2.0 + 0.01).astype(np.float32)
+    c = rng.integers(0, 1 << bits, (bk, 8))
+    return p, s, c
+
+
+# --------------------------------------------------------------- one head per kv head
+SPAN32 = f32(4294901760.0)      # 2^32 - 2^16
+
+
+def mha_weights(w):
+    wmax = f32(w.max())
+    K = f32(SPAN32 * f32(f32(1.0) / wmax))
+    prod = (w * K).astype(np.float32)
+    W = np.rint(prod.astype(np.float64)).astype(np.uint64)
+    assert int(W.max()) < 2 ** 32
+    inv = f32(wmax * f32(f32(1.0) / SPAN32))
+    return W, inv
+
+
+def mha_contract(w, c):
+    """sum_t w_t c_t the way the one-head kernel forms it: nibble planes 4..7 then 0..3,
+    each pass combined exactly in 32 bits, converted to fp32 and added with an FMA."""
+    W, inv = mha_weights(w)
+    acc = np.zeros(c.shape[1], np.float32)
+    for pass_, unit in ((0, f32(inv * f32(65536.0))), (1, inv)):
+        planes = range(4, 8) if pass_ == 0 else range(0, 4)
+        tot = np.zeros(c.shape[1], np.uint64)
+        for j, n in enumerate(planes):
+            nib = (W >> np.uint64(4 * n)) & np.uint64(15)
+            ps = (nib[:, None] * c.astype(np.uint64)).sum(0)          # one plane: udot8 sums
+            assert int(ps.max()) <= w.size * 15 * 15
+            tot += ps << np.uint64(4 * j)
+        assert int(tot.max()) < 2 ** 32                                # combined in a u32
+        acc = (tot.astype(np.float32) * unit + acc).astype(np.float32)  # fp32 FMA (product exact here)
+    return acc, W
+
+
+def mha_bound(w, c):
+    wmax = float(w.max())
+    exact_abs = (w.astype(np.float64)[:, None] * c).sum(0)
+    return 2.0 ** -33 * 1.01 * wmax * c.sum(0) + 2.0 ** -20 * exact_abs
+
+
+def test_nibble_planes_reproduce_the_integer_products():
+    p, s, c = random_block()
+    w = (p * s).astype(np.float32)
+    W, _ = mha_weights(w)
+    direct = (W[:, None] * c.astype(np.uint64)).sum(0)
+    hi = ((W >> np.uint64(16))[:, None] * c.astype(np.uint64)).sum(0)
+    lo = ((W & np.uint64(0xFFFF))[:, None] * c.astype(np.uint64)).sum(0)
+    assert np.array_equal(direct, (hi << np.uint64(16)) + lo)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind", ["random", "peaked17", "peaked20", "wide"])
+def test_one_head_weights_within_bound(kind, seed):
+    if kind == "random":
+        p, s, c = random_block(seed=seed)
+    elif kind == "wide":
+        p, s, c = random_block(seed=seed, spread=60.0)
+    else:
+        p, s, c = peaked_block(ratio_log2=17.2 if kind == "peaked17" else 20.0, seed=seed)
+    w = (p * s).astype(np.float32)
+    got, _ = mha_contract(w, c)
+    exact = (w.astype(np.float64)[:, None] * c).sum(0)
+    assert np.all(np.abs(got - exact) <= mha_bound(w, c))
+
+
+def test_sixteen_bit_weights_miss_the_tolerance_on_a_peaked_block():
+    """The former scheme: rint(w 65535 / max w) as 16-bit weights.  With p = 1 for the
+    dominant token and 127 tokens at 2^-17.2 (rounded to 0), the output error of this
+    one block, divided by l >= 1, exceeds 2e-3 several times over."""
+    p, s, c = peaked_block(ratio_log2=17.2)
+    w = (p * s).astype(np.float32)
+    wmax = f32(w.max())
+    W16 = np.rint((w * f32(f32(65535.0) * f32(f32(1.0) / wmax))).astype(np.float64))
+    old = (W16[:, None] * c).sum(0) * float(wmax) / 65535.0
+    exact = (w.astype(np.float64)[:, None] * c).sum(0)
+    l = float(p.astype(np.float64).sum())
+    assert np.abs(old - exact).max() / l > 5 * 2e-3
+    new, _ = mha_contract(w, c)
+    assert np.abs(new - exact).max() / l < 1e-6
+
+
+# --------------------------------------------------------------------- grouped-query
+def digits(W):
+    V = ((W.astype(np.uint64) + np.uint64(0x80808080)) & np.uint64(0xFFFFFFFF)) ^ np.uint64(0x80808080)
+    b = V.astype(np.uint32).view(np.uint8).reshape(-1, 4).astype(np.int64)
+    return np.where(b >= 128, b - 256, b)          # int8 digits, little endian
+
+
+def test_balanced_digits_are_exact():
+    edge = np.array([0, 1, 127, 128, 255, 256, 0x7F7F, 0x8080, 0xFFFF, 0x7F7F7F7F, 2 ** 30,
+                     2 ** 30 + 4096, 0x40000000 - 1, 0x7F7F7F7F], np.uint64)
+    W = np.concatenate([edge, RNG.integers(0, 2 ** 30 + 2 ** 20, 500000).astype(np.uint64)])
+    d = digits(W)
+    assert d.min() >= -128 and d.max() <= 127
+    back = d[:, 0] + 256 * d[:, 1] + 65536 * d[:, 2] + 16777216 * d[:, 3]
+    assert np.array_equal(back, W.astype(np.int64))
+    small = W <= 2 ** 30 + 2 ** 20                              # the kernel's range: W <= 2^30 (1 + 2^-10)
+    assert d[small, 3].max() <= 64 and d[small, 3].min() >= 0   # so a top-digit row sum stays small
+
+
+def gqa_contract(w, bound, c):
+    kq = f32(f32(2.0 ** 30) * f32(f32(1.0) / f32(bound)))
+    W = np.rint((w * kq).astype(np.float32).astype(np.float64)).astype(np.uint64)
+    assert int(W.max()) < 0x7F7F7F80
+    d = digits(W)
+    D = [(d[:, r][:, None] * c).sum(0) for r in range(4)]       # int8 MFMA rows (exact)
+    assert max(int(np.abs(x).max()) for x in D) <= w.size * 128 * 15
+    hi = D[3] * 256 + D[2]
+    lo = D[1] * 256 + D[0]
+    assert np.abs(hi).max() < 2 ** 31 and np.abs(lo).max() < 2 ** 31
+    assert np.array_equal(hi * 65536 + lo, (W.astype(np.int64)[:, None] * c).sum(0))
+    inv = f32(f32(bound) * f32(2.0 ** -30))
+    acc = (lo.astype(np.float32) * inv).astype(np.float32)
+    acc = (hi.astype(np.float32) * f32(inv * f32(65536.0)) + acc).astype(np.float32)
+    return acc
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind", ["random", "peaked17", "peaked20"])
+def test_grouped_query_digits_within_bound(kind, seed):
+    if kind == "random":
+        p, s, c = random_block(seed=seed)
+    else:
+        p, s, c = peaked_block(ratio_log2=17.2 if kind == "peaked17" else 20.0, seed=seed)
+    w = (p * s).astype(np.float32)
+    bound = float(p.max()) * float(s.max())        # pmax x the block's largest scale
+    got = gqa_contract(w, bound, c)
+    exact = (w.astype(np.float64)[:, None] * c).sum(0)
+    lim = 2.0 ** -31 * 1.01 * bound * c.sum(0) + 2.0 ** -20 * exact
+    assert np.all(np.abs(got - exact) <= lim)
+
+
+# ------------------------------------------------------------- outlier corrections
+def frexp_exp(x):
+    return int(np.frexp(np.float32(x))[1])
+
+
+def corr_fixed(terms, channels, D, shift_from_sum=True):
+    A = float(np.abs(terms).sum()) if shift_from_sum else float(np.abs(terms).max())
+    sh = (30 if shift_from_sum else 22) - frexp_exp(A)
+    acc = np.zeros(D, np.int64)
+    q = np.rint(np.ldexp(terms.astype(np.float32), sh).astype(np.float64)).astype(np.int64)
+    np.add.at(acc, channels, q)
+    assert np.abs(acc).max() < 2 ** 31
+    return np.ldexp(acc.astype(np.float32), -sh), A
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_outlier_corrections_within_bound(seed):
+    rng = np.random.default_rng(seed)
+    bk, D = 128, 128
+    # one dominant token with a large outlier term and 127 tiny ones in the same channel,
+    # each just under half a unit of the former fixed point (2^(e - 22), 400 < 2^e)
+    tiny = 0.49 * 2.0 ** (9 - 22) * (1 - 0.01 * rng.random(bk - 1))
+    terms = np.concatenate([[400.0], tiny]).astype(np.float32)
+    channels = np.zeros(bk, np.int64)
+    got, A = corr_fixed(terms, channels, D)
+    exact = np.zeros(D)
+    np.add.at(exact, channels, terms.astype(np.float64))
+    assert np.abs(got - exact).max() <= bk * 2.0 ** -30 * A
+    old, _ = corr_fixed(terms, channels, D, shift_from_sum=False)
+    assert np.abs(old - exact).max() > 2e-3             # the former shift (from the max term)
