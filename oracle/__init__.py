@@ -246,6 +246,22 @@ def decode_many(cfg: dict, heads: list, qs: np.ndarray, q_pos) -> np.ndarray:
     return out
 
 
+def build_heads(cfg: dict, k_src: np.ndarray, v_src: np.ndarray, luts=None) -> list:
+    """Quantize ``n`` heads at once (fp16 bits ``[n][T][D]`` each), OpenMP across heads;
+    ``luts`` gives each head's codebook (codebook keys only).  Returns the HeadCaches."""
+    k = np.ascontiguousarray(k_src, np.uint16)
+    v = np.ascontiguousarray(v_src, np.uint16)
+    n, T = k.shape[0], k.shape[1]
+    heads = [HeadCache(cfg, None if luts is None else luts[i]) for i in range(n)]
+    arr = (_Head * n)(*[h._struct() for h in heads])
+    c = make_cfg(cfg)
+    if lib().orc_build_heads(C.byref(c), n, C.cast(arr, C.c_void_p), k.ctypes.data, v.ctypes.data, T):
+        raise RuntimeError("oracle build failed")
+    for i, h in enumerate(heads):
+        h.length = int(arr[i].length)
+    return heads
+
+
 def max_threads() -> int:
     return int(lib().orc_max_threads())
 

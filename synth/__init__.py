@@ -138,8 +138,10 @@ def default_workers() -> int:
 
 
 def gen_tensor(cfg: dict, tensor: int, t0: int = 0, t1: int | None = None, seed: int = 0,
-               workers: int | None = None, out: np.ndarray | None = None) -> np.ndarray:
-    """fp16 bits ``uint16 [B][Hkv][t1-t0][D]`` of K or V for every (b, h).
+               workers: int | None = None, out: np.ndarray | None = None,
+               heads: list | None = None) -> np.ndarray:
+    """fp16 bits ``uint16 [B][Hkv][t1-t0][D]`` of K or V for every (b, h), or
+    ``uint16 [n][t1-t0][D]`` for the n (b, h) pairs listed in ``heads``.
 
     Large tensors are drawn by a pool of worker processes, one (b, h) per task;
     the result does not depend on the number of workers.
@@ -147,20 +149,24 @@ def gen_tensor(cfg: dict, tensor: int, t0: int = 0, t1: int | None = None, seed:
     if t1 is None:
         t1 = cfg["tokens"]
     B, H, D = cfg["batch"], cfg["kv_heads"], cfg["head_dim"]
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     if out is None:
-        out = np.empty((B, H, t1 - t0, D), np.uint16)
+        out = np.empty((B, H, t1 - t0, D) if heads is None else (len(pairs), t1 - t0, D), np.uint16)
+    slot = {bh: i for i, bh in enumerate(pairs)}
+    put = (lambda b, h, arr: out.__setitem__((b, h), arr)) if heads is None else \
+        (lambda b, h, arr: out.__setitem__(slot[(b, h)], arr))
     std = chan_std(cfg, seed)
-    tasks = [(cfg, tensor, b, h, t0, t1, seed, std) for b in range(B) for h in range(H)]
+    tasks = [(cfg, tensor, b, h, t0, t1, seed, std) for (b, h) in pairs]
     nw = default_workers() if workers is None else workers
-    if nw <= 1 or B * H * (t1 - t0) * D < (1 << 22):
+    if nw <= 1 or len(pairs) * (t1 - t0) * D < (1 << 22):
         for task in tasks:
             b, h, arr = _gen_task(task)
-            out[b, h] = arr
+            put(b, h, arr)
         return out
     ctx = _mp.get_context("spawn")
     with ProcessPoolExecutor(max_workers=nw, mp_context=ctx) as ex:
         for b, h, arr in ex.map(_gen_task, tasks, chunksize=1):
-            out[b, h] = arr
+            put(b, h, arr)
     return out
 
 

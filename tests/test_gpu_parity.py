@@ -4,7 +4,7 @@ Quantized caches (codes, scales, zeros, outlier CSR, tails) and dequantized valu
 must be bit-identical; decode outputs must be within 2e-3 (max abs) of the oracle's
 fp64 attention over the same quantized cache.  Small cases span several blocks and a
 ragged tail and are compared in full; the five workloads at their full sizes are
-compared on sampled heads, in the launch configuration the benchmark times.
+compared on every head, in the launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -15,6 +15,22 @@ from _gpu_util import build_gpu_cache, compare_head, inputs, oracle_heads, say, 
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+U = 2.0 ** -24
+
+
+def split_tol(vmax, nblk, s1, s2):
+    """Largest difference between two decodes of one cache that differ only in their
+    split counts s1, s2: each is an fp32 evaluation of the same normalised sum with at
+    most nblk + s + 32 roundings (the blocks of a split, the merge, the cross-lane sums,
+    the exponentials), each of relative size u = 2^-24 on terms bounded by max |v|."""
+    return 4.0 * U * vmax * (nblk + s1 + s2 + 32)
+
+
+def _vmax(cfg, k, v):
+    """max |v| over the dequantized values (the oracle's), of every head."""
+    import oracle
+    heads = oracle_heads(cfg, k, v, _lut(cfg))
+    return max(float(np.abs(hc.dequantize(1)).max()) for hc in heads.values())
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -137,10 +153,12 @@ def test_split_count_invariance_and_determinism(case):
         b = cache.decode(qd, num_splits=S).cpu().numpy()
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), S
         outs[S] = a
+    vmax = _vmax(cfg, k, v)
+    nblk = cfg["tokens"] // cfg["k_block"]
     for S in (3, 7, 64):
         d = np.abs(outs[S] - outs[1]).max()
-        say("  splits", S, "max diff vs 1 split", d)
-        assert d <= 2e-5, S                     # fp32 reassociation only
+        say("  splits", S, "max diff vs 1 split", d, "bound", split_tol(vmax, nblk, 1, S))
+        assert d <= split_tol(vmax, nblk, 1, S), S      # fp32 rounding order only
 
 
 # Caches whose length is a whole number of blocks (no fp16 tail): the split merge then
@@ -176,8 +194,9 @@ def test_merge_without_tail(case):
         say("  splits", S, "max abs err", err)
         assert err <= TOL, S
         outs[S] = a
+    vmax = _vmax(cfg, k, v)
     for S in outs:
-        assert np.abs(outs[S] - outs[1]).max() <= 2e-5, S   # fp32 reassociation only
+        assert np.abs(outs[S] - outs[1]).max() <= split_tol(vmax, nblk, 1, S), S   # fp32 rounding order only
 
 
 @pytest.mark.parametrize("kind", ["equal_magnitudes", "few_levels"])
@@ -239,25 +258,40 @@ def test_append_errors_do_not_touch_the_cache():
 
 
 # --------------------------------------------------------------------------- full sizes
-SAMPLE = {
-    "c1": [(0, 0), (7, 31), (3, 17)],
-    "c2": [(0, 0), (3, 7), (2, 3)],
-    "c3": [(0, 0), (0, 21)],
-    "c4": [(0, 0), (15, 31), (9, 4)],
-}
+def _host_buffers(cache, cfg):
+    """Every device buffer of the cache, copied to the host once."""
+    return {n: t.cpu().numpy() for n, t in cache.bufs.items() if n not in ("rope", "k_lut")}
+
+
+def _compare_head_host(bufs, hc, cfg, ko, b, h):
+    from _gpu_util import defined_bytes, oracle_head_bytes, per_head_bytes
+    bh = b * cfg["kv_heads"] + h
+    per = per_head_bytes(cfg, ko)
+    for name, nb in defined_bytes(cfg, ko, hc.length).items():
+        if nb == 0:
+            continue
+        g = bufs[name][bh * per[name]: bh * per[name] + nb]
+        o = oracle_head_bytes(hc, name, nb)
+        if not np.array_equal(g, o):
+            bad = np.nonzero(g != o)[0]
+            raise AssertionError("%s differs at (b=%d, h=%d): %d of %d bytes, first at byte %d"
+                                 % (name, b, h, bad.size, nb, bad[0]))
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
-def test_full_size_sampled(name):
-    """The workload at its full size, appended as the benchmark appends it; sampled
-    heads compared bitwise and sampled decode outputs against the oracle."""
+def test_full_size_all_heads(name):
+    """The workload at its full size, appended as the benchmark appends it (the prefill
+    workload: its cached half, then the appended half), decoded in the launch
+    configuration the benchmark times; every head's cache compared bitwise with the
+    oracle and every (b, q-head) output within 2e-3 of the oracle's fp64 attention."""
     import torch
     import oracle
     cfg = synth.config(name)
     say("full-size", name, cfg["workload"])
     lut = _lut(cfg)
-    T = cfg["tokens"]
+    T, B, H, Hq = cfg["tokens"], cfg["batch"], cfg["kv_heads"], cfg["q_heads"]
+    gq = Hq // H
     import quantized_decode_attn_amd as kvq
     dev = torch.device("cuda:0")
     lut_t = None if lut is None else torch.from_numpy(lut.view(np.int16)).to(dev)
@@ -271,28 +305,28 @@ def test_full_size_sampled(name):
         del k, v
         t += n
         say("  appended tokens", t, "of", T)
-    torch.cuda.synchronize()
-    say("  appended", cache.length)
-    sample = SAMPLE[name]
-    heads = {}
-    for (b, h) in sample:
-        kh = synth.gen_head(cfg, synth.TENSOR_K, b, h)
-        vh = synth.gen_head(cfg, synth.TENSOR_V, b, h)
-        hc = oracle.HeadCache(cfg, None if lut is None else lut[h]).build(kh, vh)
-        compare_head(cache, hc, cfg, oracle.kout(cfg), b, h)
-        heads[(b, h)] = hc
-        say("  head", (b, h), "bitwise equal")
-    say("  sampled heads bitwise equal")
     q = synth.gen_q(cfg)
     out = cache.decode(upload(q)).cpu().numpy()
-    gq = cfg["q_heads"] // cfg["kv_heads"]
-    hl, ql, idx = [], [], []
-    for (b, h) in sample:
-        for hq in range(h * gq, (h + 1) * gq):
-            hl.append(heads[(b, h)])
-            ql.append(q[b, hq])
-            idx.append((b, hq))
-    ref = oracle.decode_many(cfg, hl, np.stack(ql), T - 1)
-    err = max(np.abs(out[b, hq] - ref[i]).max() for i, (b, hq) in enumerate(idx))
-    say("  decode max abs err", err)
-    assert err <= TOL
+    torch.cuda.synchronize()
+    bufs = _host_buffers(cache, cfg)
+    ko = oracle.kout(cfg)
+    # heads in batches of about 2 GiB of fp16 source per tensor
+    per_batch = max(1, (1 << 30) // (T * cfg["head_dim"]))
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    worst = 0.0
+    for i0 in range(0, len(pairs), per_batch):
+        sel = pairs[i0:i0 + per_batch]
+        kh = synth.gen_tensor(cfg, synth.TENSOR_K, heads=sel)
+        vh = synth.gen_tensor(cfg, synth.TENSOR_V, heads=sel)
+        hcs = oracle.build_heads(cfg, kh, vh, None if lut is None else [lut[h] for (_, h) in sel])
+        del kh, vh
+        for (b, h), hc in zip(sel, hcs):
+            _compare_head_host(bufs, hc, cfg, ko, b, h)
+        hl = [hc for hc in hcs for _ in range(gq)]
+        ql = np.stack([q[b, h * gq + g] for (b, h) in sel for g in range(gq)])
+        ref = oracle.decode_many(cfg, hl, ql, T - 1)
+        got = np.stack([out[b, h * gq + g] for (b, h) in sel for g in range(gq)]).astype(np.float64)
+        worst = max(worst, float(np.abs(got - ref).max()))
+        say("  heads", i0 + len(sel), "of", len(pairs), "bitwise equal; decode max abs err so far", worst)
+        del hcs, hl
+    assert worst <= TOL
