@@ -183,6 +183,20 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int64_t q
                                 float *out, void *ws, size_t ws_bytes, int32_t num_splits,
                                 void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same decode as
+ * kvq_decode_attention, with the split partials kept in a library-owned device array
+ * of KVQ_NOALLOC_SCRATCH_BYTES per GPU (B * q_heads * splits * (head_dim + 2) * 4 bytes
+ * must fit: KVQ_EWORKSPACE otherwise) instead of a caller workspace.  The array is
+ * set up on a device at the first call made with that device current and held until
+ * the process ends; this call allocates nothing.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (e.g. on two streams) race and give
+ * undefined results.  Same arguments, results and errors as kvq_decode_attention
+ * otherwise (bitwise the same output for the same num_splits). */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_cache *cache, const void *q, int64_t q_pos,
+                                        float *out, int32_t num_splits, void *stream);
+
 /* Dequantize tokens [t0, t1) of keys (which = 0) or values (which = 1) into *device*
  * fp32 out [batch][kv_heads][t1-t0][head_dim], pre-RoPE: x = fmaf(c, scale, zero) or
  * the codebook entry, outlier positions and tail tokens exact.

@@ -7,7 +7,8 @@ every call raises: there is no fallback.
 
 The functions carry the names of the C ABI in ``include/kvq.h``
 (``kvq_cache_layout``, ``kvq_cache_init``, ``kvq_quantize_append``,
-``kvq_decode_workspace_bytes``, ``kvq_decode_attention``, ``kvq_dequantize``,
+``kvq_decode_workspace_bytes``, ``kvq_decode_attention``, ``kvq_decode_attention_noalloc``,
+``kvq_dequantize``,
 ``kvq_status_string``); ``Cache`` bundles the buffers of one cache.
 """
 from __future__ import annotations
@@ -20,7 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4, -5
 EXPORTED = ["kvq_status_string", "kvq_cache_layout", "kvq_cache_init", "kvq_quantize_append",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_dequantize"]
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
+            "kvq_dequantize"]
+NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
 class KvqConfig(C.Structure):
@@ -73,6 +76,8 @@ def lib() -> C.CDLL:
         L.kvq_decode_workspace_bytes.argtypes = [C.POINTER(KvqCache), i32]
         L.kvq_decode_attention.restype = i32
         L.kvq_decode_attention.argtypes = [C.POINTER(KvqCache), vp, i64, vp, vp, C.c_size_t, i32, vp]
+        L.kvq_decode_attention_noalloc.restype = i32
+        L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(KvqCache), vp, i64, vp, i32, vp]
         L.kvq_dequantize.restype = i32
         L.kvq_dequantize.argtypes = [C.POINTER(KvqCache), i32, i64, i64, vp, vp]
         _lib = L
@@ -125,6 +130,14 @@ def kvq_decode_attention(cache: KvqCache, q, q_pos: int, out, ws, ws_bytes: int,
                                     int(ws_bytes), int(num_splits), _stream(stream))
     if st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(cache: KvqCache, q, q_pos: int, out, num_splits: int = 0,
+                                 stream=None) -> None:
+    st = lib().kvq_decode_attention_noalloc(C.byref(cache), _ptr(q), int(q_pos), _ptr(out),
+                                            int(num_splits), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_attention_noalloc")
 
 
 def kvq_dequantize(cache: KvqCache, which: int, t0: int, t1: int, out, stream=None) -> None:

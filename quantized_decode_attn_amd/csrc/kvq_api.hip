@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq.h"
 #include "kvq_internal.h"
 
@@ -50,6 +52,30 @@ kvq_status check_cache(const kvq_cache* cache) {
 }
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+// Device-side split partials of kvq_decode_attention_noalloc: one array per GPU the
+// library runs on (the code object's copy on that device), held until the process ends.
+constexpr size_t kNoallocScratchBytes = KVQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current GPU's `scratch`, looked up once per device with
+// that device current (the host-side name is only a stand-in for it).
+kvq_status scratch_of_current_device(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVQ_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return KVQ_OK;
+}
 
 int auto_splits(const kvq_config& c) {
   // About one (b, kv-head, split) work item per resident wave of an MI355X (256 CUs x
@@ -168,6 +194,23 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int64_t q
   if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
   return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, (float*)ws, S,
                                      (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int64_t q_pos, float* out,
+                                        int32_t num_splits, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || q_pos < 0 || num_splits < 0 || cache->length == 0) return KVQ_EINVAL;
+  if (q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
+  const kvq_config& c = cache->cfg;
+  const int S = num_splits ? num_splits : auto_splits(c);
+  if (S > 4096) return KVQ_EINVAL;
+  const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
+  if (need > kNoallocScratchBytes) return KVQ_EWORKSPACE;
+  float* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != KVQ_OK) return st;
+  return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, ws, S, (hipStream_t)stream));
 }
 
 kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, int64_t t0, int64_t t1, float* out,
