@@ -1,14 +1,18 @@
 """Benchmark of the low-bit KV-cache hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input: the
-quantize-append of the batch's keys and values into an empty cache (every block
-quantized, packed, with its metadata) followed by one decode-attention query per
-sequence over the packed cache.  Inputs are resident in HBM before timing starts.
+quantize-append of the batch's new keys and values into the cache (every block
+quantized, clipped, split into dense codes and outlier CSR, packed, with its
+metadata) followed by one decode-attention query per sequence over the packed cache.
+The default workload is the prefill-append one: 16 sequences x 32 kv heads, 16384 new
+tokens appended onto 16384 cached ones, 99th-percentile clip, 1% outliers, then a
+decode over all 32768 tokens.  Inputs are resident in HBM before timing starts.
 ``value`` is the decode attention's effective bandwidth (algorithmic bytes over the
 decode call's average duration, measured with HIP events on the stream the kernels
-run on); the append throughput is reported beside it.
+run on); the append's tokens/s is reported beside it, as is a read-streaming probe
+(the achievable bandwidth of a plain 1 GiB read on the same device and stream).
 
-    python bench.py [--steps K] [--warmup W] [--workload c1] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload c4] [--gpus 1]
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -44,7 +48,9 @@ def kout(cfg):
 def decode_bytes_per_token_head(cfg) -> float:
     """Bytes one decode must read per (b, kv-head, token): packed key and value codes,
     key scale/zero amortised over the block, value scale/zero, outlier columns and
-    values (the fixed per-token count makes the row pointers unnecessary to read)."""
+    values.  The CSR row pointers (4 B per token and tensor) are not counted: every
+    quantized token holds exactly ceil(pct * D / 100) entries, so a reader computes
+    the offsets and never loads the pointers."""
     D, Bk, ko = cfg["head_dim"], cfg["k_block"], kout(cfg)
     rk = D * cfg["k_bits"] / 8
     rv = D * cfg["v_bits"] / 8
@@ -90,12 +96,24 @@ def measured_traffic(kind: str, workload: str, src_hash: str):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, k, v, q, lut, seconds: float):
-    """The oracle as it stands, on a bounded sample of the same workload: quantize the
-    sampled heads, then time fp64 decode over them."""
+    """The oracle as it stands, on a bounded sample of the same workload: quantize a
+    sample of heads (OpenMP across heads), then time fp64 decode over them; each leg
+    is sized to about ``seconds`` of wall time."""
     import oracle
     oracle.build()
     T, D, Hq, H = cfg["tokens"], cfg["head_dim"], cfg["q_heads"], cfg["kv_heads"]
+    B = cfg["batch"]
     gq = Hq // H
     threads = oracle.max_threads()
     t0 = time.perf_counter()
@@ -104,14 +122,16 @@ def cpu_baseline(cfg, k, v, q, lut, seconds: float):
     t0 = time.perf_counter()
     oracle.decode_many(cfg, [hc], q[0, :1], T - 1)
     t_dec1 = time.perf_counter() - t0
-    # heads so that the decode leg costs about `seconds` of wall time on `threads` cores
-    nheads = int(max(1, min(cfg["batch"] * H, seconds * threads / max(t_dec1, 1e-3))))
-    nheads = max(1, min(nheads, cfg["batch"] * H))
+    per = max(t_build1, gq * t_dec1, 1e-3)
+    nheads = int(max(1, min(B * H, seconds * threads / per)))
     sample = [(i // H, i % H) for i in range(nheads)]
+    ks = np.stack([k[b, h] for (b, h) in sample])
+    vs = np.stack([v[b, h] for (b, h) in sample])
+    luts = None if lut is None else [lut[h] for (_, h) in sample]
     t0 = time.perf_counter()
-    heads = [hc] + [oracle.HeadCache(cfg, None if lut is None else lut[h]).build(k[b, h], v[b, h])
-                    for (b, h) in sample[1:]]
-    t_build = time.perf_counter() - t0 + t_build1
+    heads = oracle.build_heads(cfg, ks, vs, luts)
+    t_build = time.perf_counter() - t0
+    del ks, vs
     hl = [heads[i] for i in range(nheads) for _ in range(gq)]
     ql = np.stack([q[b, h * gq + g] for (b, h) in sample for g in range(gq)])
     t0 = time.perf_counter()
@@ -122,10 +142,11 @@ def cpu_baseline(cfg, k, v, q, lut, seconds: float):
         "value": round(dec_bytes / t_dec / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": "fp64 decode over %d of %d (b, kv-head) heads x %d tokens (%d query heads each), "
-                  "caches quantized by the oracle (%.1f s, %.3g tokens/s append); decode %.1f s"
-                  % (nheads, cfg["batch"] * H, T, gq, t_build, nheads * T / t_build, t_dec),
+        "sample": "%d of %d (b, kv-head) heads x %d tokens: quantized by the oracle in %.1f s "
+                  "(%.3g tokens/s), then fp64 decode of %d query heads each in %.1f s"
+                  % (nheads, B * H, T, t_build, nheads * T / t_build, gq, t_dec),
         "append_tokens_per_s": round(nheads * T / t_build, 1),
     }
 
@@ -148,7 +169,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c1", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--workload", default="c4", choices=sorted(synth.CONFIGS))
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -221,6 +242,17 @@ def main():
     app_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
     dec_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(args.steps)])
 
+    # read-streaming probe: the same 1 GiB int64 sum that scrubs the caches, timed on
+    # the same stream (achievable read bandwidth of this device, for the fraction below)
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for r in range(5):
+        pe[r].record(stream)
+        scrub_view.sum()
+    pe[5].record(stream)
+    torch.cuda.synchronize()
+    probe_ms = np.array([pe[r].elapsed_time(pe[r + 1]) for r in range(1, 5)])
+    probe_gbps = scrub.numel() / (probe_ms.mean() * 1e-3) / 1e9
+
     dbytes = decode_bytes(cfg, T)
     abytes = B * H * n_new * append_bytes_per_token_head(cfg)
     dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
@@ -228,6 +260,7 @@ def main():
     app_tps = B * n_new / (app_ms.mean() * 1e-3)
     log("decode  %.1f us  %.1f GB/s (%.1f%% of 8 TB/s)" % (dec_ms.mean() * 1e3, dec_gbps, dec_gbps / 80))
     log("append  %.1f us  %.1f GB/s  %.3g tokens/s" % (app_ms.mean() * 1e3, app_gbps, app_tps))
+    log("stream  %.1f GB/s (1 GiB read probe)" % probe_gbps)
 
     dec_hash = source_hash(["decode_mha.hip", "decode_gqa.hip", "decode_common.h", "decode.hip",
                             "kvq_device.h", "kvq_internal.h"])
@@ -246,7 +279,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("f32 scores/softmax; value weights as %s fixed point x u%d codes, exact integer "
+                  "sums; fp32 accumulation" % ("30-bit digit" if Hq > H else "32-bit", cfg["v_bits"])),
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": cfg["workload"], "batch": B, "q_heads": Hq, "kv_heads": H,
                    "head_dim": D, "tokens": T, "appended_per_step": n_new, "k_bits": cfg["k_bits"],
@@ -263,7 +297,12 @@ def main():
                      "algorithmic_bytes": int(dbytes)},
         "roofline_append": {"bound": "hbm", "achieved": round(app_gbps, 2), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(app_gbps / HBM_PEAK_GBPS, 4),
-                            "traffic": tr_app, "algorithmic_bytes": int(abytes)},
+                            "traffic": tr_app, "kernel": "append (key and value quantize launches)",
+                            "algorithmic_bytes": int(abytes)},
+        "stream_probe": {"GBps": round(probe_gbps, 1), "frac_of_peak": round(probe_gbps / HBM_PEAK_GBPS, 4),
+                         "kernel": "1 GiB int64 sum (read-streaming)"},
+        "decode_frac_of_stream": round(dec_gbps / probe_gbps, 4),
+        "append_frac_of_stream": round(app_gbps / probe_gbps, 4),
     }
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
