@@ -141,7 +141,10 @@ typedef struct {
   float *rope;
 } kvq_cache;
 
-/* Text for a status code (static storage; never NULL). */
+/* Text for a status code (static storage; never NULL).  No passage of the pages defines
+ * an error model: the codes are this interface's own, so that a framework that embeds
+ * the cache (the integration [TQ] section 5.3 says the attention and cache management
+ * must undergo) can report why a call was refused. */
 const char *kvq_status_string(kvq_status s);
 
 /* Validate `cfg` and report the byte size of every buffer.  Host only; touches no
@@ -151,7 +154,10 @@ const char *kvq_status_string(kvq_status s);
 kvq_status kvq_cache_layout(const kvq_config *cfg, kvq_layout *out);
 
 /* Prepare an empty cache: validates the descriptor and its buffer pointers,
- * fills `rope` (angles evaluated in fp64) and sets length = 0.  Enqueued on `stream`. */
+ * fills `rope` (angles evaluated in fp64) and sets length = 0.  Enqueued on `stream`.
+ * The pages apply RoPE to the keys after dequantization ([KVC3] "Pre-RoPE Key
+ * Quantization"); `rope` holds the cos/sin of those angles once per cache, in a
+ * caller-owned buffer like every other buffer, so that no decode evaluates them. */
 kvq_status kvq_cache_init(kvq_cache *cache, void *stream);
 
 /* Append n_new tokens for every (b, kv-head): k_new, v_new are *device* fp16
@@ -165,7 +171,11 @@ kvq_status kvq_quantize_append(kvq_cache *cache, const void *k_new, const void *
 
 /* Bytes of device workspace kvq_decode_attention needs for `num_splits` splits of
  * the cache per (b, kv-head) (0 = the library's choice for this cache; at most
- * 4096). */
+ * 4096): one (max, sum, output) partial of head_dim + 2 floats per (b, q-head, split),
+ * B * q_heads * splits * (head_dim + 2) * 4 bytes.  The split-K decode reads the
+ * packed cache once and keeps only these partials as intermediate state, in the
+ * FlashAttention manner [TQ] section 5.2 pairs with the quantized cache.  Host only;
+ * returns 0 for an invalid cache or a negative split count. */
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_splits);
 
 /* Single-query decode attention over the whole cache:
@@ -199,8 +209,11 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache *cache, const void *q, i
 
 /* Dequantize tokens [t0, t1) of keys (which = 0) or values (which = 1) into *device*
  * fp32 out [batch][kv_heads][t1-t0][head_dim], pre-RoPE: x = fmaf(c, scale, zero) or
- * the codebook entry, outlier positions and tail tokens exact.
- * 0 <= t0 <= t1 <= length. */
+ * the codebook entry, outlier positions and tail tokens exact.  This is the
+ * "dequantize before use" read of [TQ] section 4.2 and the scale/zero-point
+ * reconstruction of [KVC3] "Quanto 的量化原理", for callers that want the values
+ * rather than attention over them.  0 <= t0 <= t1 <= length; t0 == t1 is a no-op;
+ * KVQ_EINVAL for a bad range or `which`. */
 kvq_status kvq_dequantize(const kvq_cache *cache, int32_t which, int64_t t0, int64_t t1,
                           float *out, void *stream);
 

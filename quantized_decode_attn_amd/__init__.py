@@ -150,6 +150,19 @@ def kvq_dequantize(cache: KvqCache, which: int, t0: int, t1: int, out, stream=No
 _CFG_FIELDS = [f[0] for f in KvqConfig._fields_]
 
 
+def _check_tensor(t, name: str, shape: tuple, dtype, device) -> None:
+    """A tensor handed to the C ABI must have the layout the library reads: the exact
+    shape, dtype, contiguous storage and the cache's device."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, the cache on %s" % (name, t.device, device))
+
+
 def make_config(cfg: dict) -> KvqConfig:
     d = dict(cfg)
     d.setdefault("capacity", d.get("tokens"))
@@ -193,9 +206,19 @@ class Cache:
     def length(self) -> int:
         return int(self.desc.length)
 
+    @property
+    def device(self):
+        return self.bufs["rope"].device
+
     def append(self, k_new, v_new, stream=None) -> None:
         """k_new, v_new: fp16 tensors [B][Hkv][N][D] on the device (keys pre-RoPE)."""
+        import torch
+        B, H, D = self.cfg["batch"], self.cfg["kv_heads"], self.cfg["head_dim"]
+        if k_new.dim() != 4:
+            raise ValueError("k_new must be [B][Hkv][N][D]")
         n = k_new.shape[2]
+        _check_tensor(k_new, "k_new", (B, H, n, D), torch.float16, self.device)
+        _check_tensor(v_new, "v_new", (B, H, n, D), torch.float16, self.device)
         kvq_quantize_append(self.desc, k_new, v_new, n, stream)
 
     def workspace(self, num_splits: int = 0):
@@ -210,8 +233,11 @@ class Cache:
         import torch
         if q_pos is None:
             q_pos = self.length - 1
+        shape = (self.cfg["batch"], self.cfg["q_heads"], self.cfg["head_dim"])
+        _check_tensor(q, "q", shape, torch.float16, self.device)
         if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            out = torch.empty(shape, dtype=torch.float32, device=q.device)
+        _check_tensor(out, "out", shape, torch.float32, self.device)
         ws = self.workspace(num_splits)
         kvq_decode_attention(self.desc, q, q_pos, out, ws, ws.numel(), num_splits, stream)
         return out

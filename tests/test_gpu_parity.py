@@ -330,3 +330,22 @@ def test_full_size_all_heads(name):
         say("  heads", i0 + len(sel), "of", len(pairs), "bitwise equal; decode max abs err so far", worst)
         del hcs, hl
     assert worst <= TOL
+
+
+def test_binding_rejects_mislaid_tensors():
+    """The binding checks shape, dtype, contiguity and device before calling the C ABI."""
+    import torch
+    cfg = synth.config("c0", tokens=100, capacity=128)
+    k, v = inputs(cfg)
+    cache = build_gpu_cache(cfg, k, v)
+    kd, vd = upload(k), upload(v)
+    for bad in (kd[:, :2], kd.float(), kd.transpose(2, 3).contiguous().transpose(2, 3), kd.cpu()):
+        with pytest.raises(ValueError):
+            cache.append(bad, vd)
+    q = upload(synth.gen_q(cfg))
+    for bad in (q[:, :2], q.float(), q.transpose(1, 2).contiguous().transpose(1, 2)):
+        with pytest.raises(ValueError):
+            cache.decode(bad)
+    with pytest.raises(ValueError):
+        cache.decode(q, out=torch.empty((1, 4, 64), dtype=torch.float16, device="cuda"))
+    assert cache.length == 100
