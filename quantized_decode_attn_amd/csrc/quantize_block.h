@@ -193,6 +193,27 @@ __device__ __forceinline__ float lanes_max(float v) {
   return v;
 }
 
+// Packed fp16 minimum / maximum of two elements per register.  Minimum and maximum of
+// fp16 values are exact in fp16, and in IEEE mode a quiet NaN operand (the outlier mark)
+// yields the other operand, as fminf/fmaxf do.  Written out so that the compiler adds no
+// NaN-quieting operations around the loaded operands (never signaling NaNs here).
+__device__ __forceinline__ uint32_t pk_min_h(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_h(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+constexpr uint32_t kPkPosInf = 0x7C007C00u, kPkNegInf = 0xFC00FC00u;
+
+// Element k (0 or 1) of a packed fp16 pair.
+__device__ __forceinline__ _Float16 half_of(uint32_t w, int k) {
+  return __builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * k)));
+}
+
 // ---------------------------------------------------------------- scalar pieces
 
 // fp16 zero = min rounded down, fp16 scale = (max - zero) / L rounded up; a group
@@ -233,6 +254,20 @@ __device__ __forceinline__ float code_fast(float d, float z, float r, float a, f
   qc = x * r;
   qc = __builtin_amdgcn_fmed3f(qc, a, b);
   if constexpr (OUTL) qc = (d != d) ? 0.0f : qc;
+  const float rr = __builtin_rintf(qc);
+  near = fabsf(qc - rr) > kTieMargin;
+  return rr;
+}
+
+// The same from the element's fp16 bits: d - z is one mixed-precision FMA (d * 1 - z,
+// rounded once: the IEEE fp32 subtraction of the converted value), and an outlier mark
+// (NaN) propagates to the difference.
+template <bool OUTL, bool CLIP>
+__device__ __forceinline__ float code_fast_h(_Float16 h, float z, float r, float a, float b, bool& near, float& qc) {
+  const float x = __builtin_fmaf((float)h, 1.0f, -z);
+  qc = x * r;
+  qc = __builtin_amdgcn_fmed3f(qc, a, b);
+  if constexpr (OUTL) qc = (x != x) ? 0.0f : qc;
   const float rr = __builtin_rintf(qc);
   near = fabsf(qc - rr) > kTieMargin;
   return rr;
@@ -324,11 +359,13 @@ __device__ __forceinline__ void stage_chunks(uint4 (&v)[BK * D / 8 / kThreads], 
 // column stages it in ocol/oval (ascending column order within the row, value read
 // back from the tile it wrote itself); the columns are returned packed a byte each
 // for the marking after the clip.
-template <int D, int BK>
-__device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThreads], const uint16_t* tile, int ko,
+template <int D, int BK, int KO>
+__device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThreads], const uint16_t* tile, int ko_rt,
                                              uint8_t* ocol, uint16_t* oval, uint32_t (&colpk)[BK * D / 8 / kThreads]) {
   using S = Stage<D, BK>;
   constexpr int P = D + 8;
+  constexpr int KMAX = KO > 0 ? KO : 4;  // outlier slots a row can hold
+  const int ko = KO > 0 ? KO : ko_rt;
   constexpr int G = S::NC < 2 ? S::NC : 2;  // rows searched together (register budget)
   const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
 #pragma unroll
@@ -345,7 +382,7 @@ __device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThre
     uint32_t sel[G][4];
 #pragma unroll
     for (int g = 0; g < G; ++g) sel[g][0] = sel[g][1] = sel[g][2] = sel[g][3] = 0u;
-    if (ko <= 2) {
+    if (KO == 1 || KO == 2 || (KO < 0 && ko <= 2)) {
       // the lane's two largest keys by a merge tree, then the row's largest, then the
       // row's largest among the other lanes' first and the owner's second
 #pragma unroll
@@ -391,14 +428,14 @@ __device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThre
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         cols[r] = 255 - (int)(sel[g][r] & 0xffu);
-        colpk[i] |= (uint32_t)(cols[r] & 0xff) << (8 * r);
+        if (r < KMAX) colpk[i] |= (uint32_t)(cols[r] & 0xff) << (8 * r);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < KMAX; ++r) {
         if (r < ko && (cols[r] >> 3) == part) {
           int rank = 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) rank += (q < ko && cols[q] < cols[r]) ? 1 : 0;
+          for (int q = 0; q < KMAX; ++q) rank += (q < ko && cols[q] < cols[r]) ? 1 : 0;
           ocol[j * 4 + rank] = (uint8_t)cols[r];
           oval[j * 4 + rank] = tile[j * P + cols[r]];
         }
@@ -409,9 +446,10 @@ __device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThre
 
 // Writes the block's CSR slice staged in ocol/oval (consecutive threads) and its
 // row pointers (ko entries per token).
-template <int BK>
+template <int BK, int KO>
 __device__ __forceinline__ void write_csr(const uint8_t* ocol, const uint16_t* oval, int32_t* rowptr, uint8_t* col_out,
-                                          uint16_t* val_out, int64_t bh, int64_t T, int64_t t0, int ko) {
+                                          uint16_t* val_out, int64_t bh, int64_t T, int64_t t0, int ko_rt) {
+  const int ko = KO > 0 ? KO : ko_rt;
   for (int idx = threadIdx.x; idx < BK * ko; idx += kThreads) {
     const int j = idx / ko, r = idx % ko;
     col_out[(bh * T + t0) * ko + idx] = ocol[j * 4 + r];
@@ -426,15 +464,17 @@ __device__ __forceinline__ void write_csr(const uint8_t* ocol, const uint16_t* o
 
 // The outlier positions get the quiet NaN in the tile (each by the thread that staged
 // the position).
-template <int D, int BK>
-__device__ __forceinline__ void mark_outliers(uint16_t* tile, const uint32_t (&colpk)[BK * D / 8 / kThreads], int ko) {
+template <int D, int BK, int KO>
+__device__ __forceinline__ void mark_outliers(uint16_t* tile, const uint32_t (&colpk)[BK * D / 8 / kThreads], int ko_rt) {
   using S = Stage<D, BK>;
   constexpr int P = D + 8;
+  constexpr int KMAX = KO > 0 ? KO : 4;
+  const int ko = KO > 0 ? KO : ko_rt;
   const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
 #pragma unroll
   for (int i = 0; i < S::NC; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < KMAX; ++r) {
       const int col = (int)((colpk[i] >> (8 * r)) & 0xffu);
       if (r < ko && (col >> 3) == part) tile[(i * S::RPS + r0) * P + col] = kMarkNaN;
     }
@@ -726,7 +766,7 @@ struct ValueSmem {
 
 // Steps 1, 2 and 2b for one tile; returns the clip threshold (0 without clipping).
 // The tile is written raw; the outliers are marked after the clip (which counts them).
-template <int D, int BK, bool OUTL, bool CLIP>
+template <int D, int BK, int KO, bool CLIP>
 __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uint16_t* oval, ClipSmem& cs, Red& red,
                                               const kvq_cache& c, bool is_key, const uint16_t* src_new,
                                               int64_t bh, int64_t n, int64_t old_len, int64_t n_new) {
@@ -750,17 +790,17 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uin
     fast = clip_candidates<D, BK>(tile, cmax, rank_top, cs, red);
   }
   uint32_t colpk[S::NC];
-  if constexpr (OUTL) row_outliers<D, BK>(v, tile, ko, ocol, oval, colpk);
+  if constexpr (KO != 0) row_outliers<D, BK, KO>(v, tile, ko, ocol, oval, colpk);
   __syncthreads();  // the tile, the staged CSR slice and the candidate lists are complete
-  if constexpr (OUTL)
-    write_csr<BK>(ocol, oval, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
+  if constexpr (KO != 0)
+    write_csr<BK, KO>(ocol, oval, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
                   is_key ? c.k_val : c.v_val, bh, T, t0, ko);
   float thr = 0.0f;
   if constexpr (CLIP)
     thr = fast ? clip_from_candidates<BK * D>(cs, red, c.cfg.clip_quantile)
                : clip_from_tile<D, BK>(tile, cs, red, c.cfg.clip_quantile, gmax);
   // the clip's reads of the tile ended at its closing barrier
-  if constexpr (OUTL) mark_outliers<D, BK>(tile, colpk, ko);
+  if constexpr (KO != 0) mark_outliers<D, BK, KO>(tile, colpk, ko);
   return thr;
 }
 
@@ -783,10 +823,9 @@ __device__ __forceinline__ void key_codes(const uint32_t (&xw)[8][4], const floa
     for (int q = 0; q < 8; ++q) {
       bool near;
       float qc;
-      const float d = xel(xw, u, q);
-      cf[q] = code_fast<OUTL, CLIP>(d, zq[q], rq[q], aq[q], bq[q], near, qc);
+      cf[q] = code_fast_h<OUTL, CLIP>(half_of(xw[u][q >> 1], q & 1), zq[q], rq[q], aq[q], bq[q], near, qc);
       // rare: a quotient this close to a rounding boundary is decided exactly
-      if (near) cf[q] = code_near<OUTL, CLIP>(d, zq[q], sq[q], qc, (float)L, thr);
+      if (near) cf[q] = code_near<OUTL, CLIP>(xel(xw, u, q), zq[q], sq[q], qc, (float)L, thr);
     }
     uint32_t wu = 0;
     if constexpr (KB == 4) {
@@ -815,9 +854,10 @@ __device__ __forceinline__ void key_codes(const uint32_t (&xw)[8][4], const floa
 // the NTG lanes sharing a channel set form one DPP row and read distinct LDS banks.
 // LUTB: 0 for uniform keys (code width from the configuration), else the code width
 // of codebook keys.
-template <int D, int BK, int LUTB, bool OUTL, bool CLIP>
+template <int D, int BK, int LUTB, int KO, bool CLIP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
                                                                  int64_t old_len, int64_t n_new, int64_t n_first) {
+  constexpr bool OUTL = KO != 0;
   constexpr int P = D + 8;
   constexpr int NTG = BK / 8;
   constexpr int NA = D / 8;
@@ -833,15 +873,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const float Lf = (float)L;
 
   const float thr =
-      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
+      prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
   __syncthreads();
 
   const bool active = NA * NTG == kThreads || tid < NA * NTG;
   const int a = tid / NTG, tg = tid % NTG;
   uint32_t xw[8][4];
   float lo[8], hi[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) { lo[q] = __builtin_inff(); hi[q] = -__builtin_inff(); }
+  // per channel min / max over the cell's tokens on packed fp16 pairs (exact)
+  uint32_t plo[4] = {kPkPosInf, kPkPosInf, kPkPosInf, kPkPosInf};
+  uint32_t phi[4] = {kPkNegInf, kPkNegInf, kPkNegInf, kPkNegInf};
 #pragma unroll
   for (int u = 0; u < 8; ++u) xw[u][0] = xw[u][1] = xw[u][2] = xw[u][3] = 0u;
   if (active) {
@@ -852,12 +893,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       const uint2 wh = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + D / 2 + 4 * a]);
       xw[u][0] = wl.x; xw[u][1] = wl.y; xw[u][2] = wh.x; xw[u][3] = wh.y;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float v = xel(xw, u, q);
-        lo[q] = fminf(lo[q], v);
-        hi[q] = fmaxf(hi[q], v);
+      for (int i = 0; i < 4; ++i) {
+        plo[i] = pk_min_h(plo[i], xw[u][i]);
+        phi[i] = pk_max_h(phi[i], xw[u][i]);
       }
     }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    lo[q] = (float)half_of(plo[q >> 1], q & 1);
+    hi[q] = (float)half_of(phi[q >> 1], q & 1);
   }
   __syncthreads();  // the tile is dead from here on; its space holds the outputs
   auto& M = sh.u.out.meta;
@@ -1044,9 +1089,10 @@ __device__ __forceinline__ void vgroup_minmax(float* lo, float* hi, int lpg) {
   }
 }
 
-template <int D, int BK, int VB, bool OUTL, bool CLIP>
+template <int D, int BK, int VB, int KO, bool CLIP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_values_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
                                                                    int64_t old_len, int64_t n_new, int64_t n_first) {
+  constexpr bool OUTL = KO != 0;
   constexpr int P = D + 8;
   constexpr int TPW = 32 / VB;
   constexpr int CW = VB == 4 ? 8 : 4;
@@ -1064,36 +1110,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int lpg = G / CW;
 
   const float thr =
-      prepare_tile<D, BK, OUTL, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
+      prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
   __syncthreads();
 
   const bool active = NCC * NTG == kThreads || tid < NCC * NTG;
   const int tg = tid / NCC, cc = tid % NCC;
   const int ch0 = cc * CW, grp = ch0 / G;
-  float x[TPW][CW];
+  // the cell as fp16 pairs (channel q of token u in half q % 2 of xr[u][q / 2]); row
+  // min / max over the cell's channels on packed pairs (exact), then over the lanes
+  uint32_t xr[TPW][CW / 2];
   float lo[TPW], hi[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    lo[u] = __builtin_inff();
-    hi[u] = -__builtin_inff();
+    uint32_t mn = kPkPosInf, mx = kPkNegInf;
+#pragma unroll
+    for (int i = 0; i < CW / 2; ++i) xr[u][i] = 0u;
     if (active) {
       const int j = TPW * tg + u;
-      uint32_t hw[CW / 2];
       if constexpr (CW == 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(&sh.u.tile[j * P + ch0]);
-        hw[0] = v.x; hw[1] = v.y; hw[2] = v.z; hw[3] = v.w;
+        xr[u][0] = v.x; xr[u][1] = v.y; xr[u][2] = v.z; xr[u][3] = v.w;
       } else {
         const uint2 v = *reinterpret_cast<const uint2*>(&sh.u.tile[j * P + ch0]);
-        hw[0] = v.x; hw[1] = v.y;
+        xr[u][0] = v.x; xr[u][1] = v.y;
       }
-#pragma unroll
-      for (int q = 0; q < CW; ++q) {
-        const float v = h2f((uint16_t)(hw[q >> 1] >> (16 * (q & 1))));
-        x[u][q] = v;
-        lo[u] = fminf(lo[u], v);
-        hi[u] = fmaxf(hi[u], v);
+      if constexpr (CW == 8) {
+        mn = pk_min_h(pk_min_h(xr[u][0], xr[u][1]), pk_min_h(xr[u][2], xr[u][3]));
+        mx = pk_max_h(pk_max_h(xr[u][0], xr[u][1]), pk_max_h(xr[u][2], xr[u][3]));
+      } else {
+        mn = pk_min_h(xr[u][0], xr[u][1]);
+        mx = pk_max_h(xr[u][0], xr[u][1]);
       }
     }
+    lo[u] = fminf((float)half_of(mn, 0), (float)half_of(mn, 1));
+    hi[u] = fmaxf((float)half_of(mx, 0), (float)half_of(mx, 1));
   }
   vgroup_minmax<TPW>(lo, hi, lpg);
 #pragma unroll
@@ -1162,6 +1212,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int k = 0; k < TPW / TPB; ++k) {
       float cf[TPB][CW];
+      bool anynear = false;
 #pragma unroll
       for (int t = 0; t < TPB; ++t)
 #pragma unroll
@@ -1169,10 +1220,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
           const int u = k * TPB + t;
           bool near;
           float qc;
-          cf[t][q] = code_fast<OUTL, CLIP>(x[u][q], zu[u], ru[u], au[u], bu[u], near, qc);
-          // rare: a quotient this close to a rounding boundary is decided exactly
-          if (near) cf[t][q] = code_near<OUTL, CLIP>(x[u][q], zu[u], su[u], qc, (float)L, thr);
+          cf[t][q] = code_fast_h<OUTL, CLIP>(half_of(xr[u][q >> 1], q & 1), zu[u], ru[u], au[u], bu[u], near, qc);
+          anynear = anynear || near;
         }
+      // rare: a quotient this close to a rounding boundary is decided exactly (the fast
+      // quotient is recomputed there, bit for bit the same)
+      if (anynear) {
+#pragma unroll
+        for (int t = 0; t < TPB; ++t)
+#pragma unroll
+          for (int q = 0; q < CW; ++q) {
+            const int u = k * TPB + t;
+            const _Float16 hq = half_of(xr[u][q >> 1], q & 1);
+            bool near;
+            float qc;
+            (void)code_fast_h<OUTL, CLIP>(hq, zu[u], ru[u], au[u], bu[u], near, qc);
+            if (near) cf[t][q] = code_near<OUTL, CLIP>((float)hq, zu[u], su[u], qc, (float)L, thr);
+          }
+      }
 #pragma unroll
       for (int q = 0; q < CW; ++q) {
         float byte = cf[TPB - 1][q];

@@ -9,11 +9,11 @@
 namespace kvq {
 namespace {
 
-template <int D, int BK, int LUTB, bool OUTL, bool CLIP>
+template <int D, int BK, int LUTB, int KO, bool CLIP>
 hipError_t launch_k(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
                     int64_t n_first, int64_t nblocks, hipStream_t s) {
   dim3 grid((unsigned)nblocks, (unsigned)c.cfg.kv_heads, (unsigned)c.cfg.batch);
-  hipLaunchKernelGGL((qb::quantize_keys_kernel<D, BK, LUTB, OUTL, CLIP>), grid, dim3(qb::kThreads), 0, s, c, k_new,
+  hipLaunchKernelGGL((qb::quantize_keys_kernel<D, BK, LUTB, KO, CLIP>), grid, dim3(qb::kThreads), 0, s, c, k_new,
                      old_len, n_new, n_first);
   return hipGetLastError();
 }
@@ -21,11 +21,18 @@ hipError_t launch_k(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, 
 template <int D, int BK, int LUTB>
 hipError_t dispatch_k(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
                       int64_t n_first, int64_t nblocks, hipStream_t s) {
-  const bool outl = kvq::host_kout(c.cfg) > 0, clip = c.cfg.clip_quantile > 0.0f;
-  if (outl && clip) return launch_k<D, BK, LUTB, true, true>(c, k_new, old_len, n_new, n_first, nblocks, s);
-  if (outl) return launch_k<D, BK, LUTB, true, false>(c, k_new, old_len, n_new, n_first, nblocks, s);
-  if (clip) return launch_k<D, BK, LUTB, false, true>(c, k_new, old_len, n_new, n_first, nblocks, s);
-  return launch_k<D, BK, LUTB, false, false>(c, k_new, old_len, n_new, n_first, nblocks, s);
+  // outliers per vector: none, exactly two (the 1% of 128 channels), or any other count
+  // (1..4, read at run time); uniform keys only get the two-outlier specialisation
+  const int ko = kvq::host_kout(c.cfg);
+  const bool clip = c.cfg.clip_quantile > 0.0f;
+#define KVQ_K(KO)                                                                                  \
+  return clip ? launch_k<D, BK, LUTB, KO, true>(c, k_new, old_len, n_new, n_first, nblocks, s)     \
+              : launch_k<D, BK, LUTB, KO, false>(c, k_new, old_len, n_new, n_first, nblocks, s);
+  if (ko == 0) { KVQ_K(0) }
+  if constexpr (LUTB == 0)
+    if (ko == 2) { KVQ_K(2) }
+  KVQ_K(-1)
+#undef KVQ_K
 }
 
 template <int LUTB>

@@ -4,11 +4,11 @@
 namespace kvq {
 namespace {
 
-template <int D, int BK, int VB, bool OUTL, bool CLIP>
+template <int D, int BK, int VB, int KO, bool CLIP>
 hipError_t launch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
                     int64_t n_first, int64_t nblocks, hipStream_t s) {
   dim3 grid((unsigned)nblocks, (unsigned)c.cfg.kv_heads, (unsigned)c.cfg.batch);
-  hipLaunchKernelGGL((qb::quantize_values_kernel<D, BK, VB, OUTL, CLIP>), grid, dim3(qb::kThreads), 0, s, c,
+  hipLaunchKernelGGL((qb::quantize_values_kernel<D, BK, VB, KO, CLIP>), grid, dim3(qb::kThreads), 0, s, c,
                      v_new, old_len, n_new, n_first);
   return hipGetLastError();
 }
@@ -16,11 +16,17 @@ hipError_t launch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, 
 template <int D, int BK, int VB>
 hipError_t dispatch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
                       int64_t n_first, int64_t nblocks, hipStream_t s) {
-  const bool outl = kvq::host_kout(c.cfg) > 0, clip = c.cfg.clip_quantile > 0.0f;
-  if (outl && clip) return launch_v<D, BK, VB, true, true>(c, v_new, old_len, n_new, n_first, nblocks, s);
-  if (outl) return launch_v<D, BK, VB, true, false>(c, v_new, old_len, n_new, n_first, nblocks, s);
-  if (clip) return launch_v<D, BK, VB, false, true>(c, v_new, old_len, n_new, n_first, nblocks, s);
-  return launch_v<D, BK, VB, false, false>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  // outliers per vector: none, exactly two (the 1% of 128 channels), or any other count
+  // (1..4, read at run time)
+  const int ko = kvq::host_kout(c.cfg);
+  const bool clip = c.cfg.clip_quantile > 0.0f;
+#define KVQ_V(KO)                                                                                  \
+  return clip ? launch_v<D, BK, VB, KO, true>(c, v_new, old_len, n_new, n_first, nblocks, s)       \
+              : launch_v<D, BK, VB, KO, false>(c, v_new, old_len, n_new, n_first, nblocks, s);
+  if (ko == 0) { KVQ_V(0) }
+  if (ko == 2) { KVQ_V(2) }
+  KVQ_V(-1)
+#undef KVQ_V
 }
 
 template <int D, int BK>
