@@ -316,6 +316,12 @@ struct Stage {
   static_assert(NC * RPS == BK && NC * kThreads * 8 == BK * D, "tile split");
 };
 
+// Largest and middle of three (v_max3_u32 / v_med3_u32 after instruction selection).
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) { return max(max(a, b), c); }
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
 // Unsigned maximum over aligned groups of N lanes (N = 8 or 16).
 template <int N>
 __device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
@@ -337,16 +343,28 @@ __device__ __forceinline__ void stage_chunks(uint4 (&v)[BK * D / 8 / kThreads], 
   constexpr int P = D + 8;
   const int64_t tail0 = (old_len / BK) * BK;
   const int r0 = threadIdx.x / S::LPR, part = threadIdx.x % S::LPR;
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  if (t0 >= old_len) {
+    // the whole block comes from the new tokens (every block but the first after an
+    // append that left a tail): one block base and 32-bit lane offsets
+    const uint16_t* blk = src_new + (bh * n_new + (t0 - old_len)) * D;
 #pragma unroll
-  for (int i = 0; i < S::NC; ++i) {
-    const int j = i * S::RPS + r0;
-    const int64_t t = t0 + j;
-    const uint16_t* row = t < old_len ? tail + (bh * BK + (t - tail0)) * D
-                                      : src_new + (bh * n_new + (t - old_len)) * D;
-    // the new fp16 tokens are read once: non-temporal loads
-    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-    const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(row + part * 8));
-    v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    for (int i = 0; i < S::NC; ++i) {
+      const uint32_t off = (uint32_t)((i * S::RPS + r0) * D + part * 8) * 2u;
+      // the new fp16 tokens are read once: non-temporal loads
+      const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(reinterpret_cast<const char*>(blk) + off));
+      v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::NC; ++i) {
+      const int j = i * S::RPS + r0;
+      const int64_t t = t0 + j;
+      const uint16_t* row = t < old_len ? tail + (bh * BK + (t - tail0)) * D
+                                        : src_new + (bh * n_new + (t - old_len)) * D;
+      const u4v x = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(row + part * 8));
+      v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
   }
 #pragma unroll
   for (int i = 0; i < S::NC; ++i)
@@ -387,15 +405,18 @@ __device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThre
       // row's largest among the other lanes' first and the owner's second
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) {
-          h[p2] = max(key[g][2 * p2], key[g][2 * p2 + 1]);
-          l[p2] = min(key[g][2 * p2], key[g][2 * p2 + 1]);
-        }
-        const uint32_t hA = max(h[0], h[1]), lA = max(min(h[0], h[1]), max(l[0], l[1]));
-        const uint32_t hB = max(h[2], h[3]), lB = max(min(h[2], h[3]), max(l[2], l[3]));
-        const uint32_t m1 = max(hA, hB), m2 = max(min(hA, hB), max(lA, lB));
+        // groups {0,1,2}, {3,4,5}, {6,7}: top of each by max3 / max, second by med3 / min;
+        // the lane's second is the larger of the middle top and the largest second (a
+        // group's second is below its own top, and every top but the largest is at most
+        // the middle one)
+        const uint32_t* k8 = key[g];
+        const uint32_t t0 = umax3(k8[0], k8[1], k8[2]);
+        const uint32_t s0 = umed3(k8[0], k8[1], k8[2]);
+        const uint32_t t1 = umax3(k8[3], k8[4], k8[5]);
+        const uint32_t s1 = umed3(k8[3], k8[4], k8[5]);
+        const uint32_t t2 = max(k8[6], k8[7]), s2 = min(k8[6], k8[7]);
+        const uint32_t m1 = umax3(t0, t1, t2);
+        const uint32_t m2 = max(umed3(t0, t1, t2), umax3(s0, s1, s2));
         const uint32_t M1 = lanes_max_u32<S::LPR>(m1);
         sel[g][0] = M1;
         if (ko == 2) sel[g][1] = lanes_max_u32<S::LPR>(m1 == M1 ? m2 : m1);
