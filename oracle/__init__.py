@@ -91,6 +91,8 @@ def load(path: str):
         "orc_dequantize_head": (C.c_int, [C.POINTER(Cfg), C.POINTER(_Head), C.c_int, i64, i64, vp]),
         "orc_decode_head": (C.c_int, [C.POINTER(Cfg), C.POINTER(_Head), vp, i64, vp]),
         "orc_decode_many": (C.c_int, [C.POINTER(Cfg), i64, vp, vp, vp, vp]),
+        "orc_chunk_head": (C.c_int, [C.POINTER(Cfg), C.POINTER(_Head), vp, C.c_int32, i64, vp]),
+        "orc_chunk_many": (C.c_int, [C.POINTER(Cfg), i64, vp, vp, C.c_int32, vp, vp]),
         "orc_max_threads": (C.c_int, []),
     }
     for name, (res, args) in sig.items():
@@ -230,6 +232,17 @@ class HeadCache:
             raise RuntimeError("oracle decode failed")
         return out
 
+    def chunk(self, q_bits: np.ndarray, q_pos: int) -> np.ndarray:
+        """fp64 outputs ``[nq][D]`` of ``nq`` consecutive queries (fp16 bits ``[nq][D]``)
+        at positions ``q_pos ..``, each attending causally to the cache."""
+        q = np.ascontiguousarray(q_bits, np.uint16).reshape(-1, self.cfg["head_dim"])
+        out = np.empty(q.shape, np.float64)
+        s = self._struct()
+        if lib().orc_chunk_head(C.byref(self._c), C.byref(s), q.ctypes.data, q.shape[0], int(q_pos),
+                                out.ctypes.data):
+            raise RuntimeError("oracle chunk attention failed")
+        return out
+
 
 def decode_many(cfg: dict, heads: list, qs: np.ndarray, q_pos) -> np.ndarray:
     """fp64 outputs ``[n][D]`` for ``n`` (HeadCache, query) pairs, OpenMP across pairs."""
@@ -243,6 +256,22 @@ def decode_many(cfg: dict, heads: list, qs: np.ndarray, q_pos) -> np.ndarray:
     if lib().orc_decode_many(C.byref(c), n, C.cast(arr, C.c_void_p), qs.ctypes.data,
                              pos.ctypes.data, out.ctypes.data):
         raise RuntimeError("oracle decode failed")
+    return out
+
+
+def chunk_many(cfg: dict, heads: list, qs: np.ndarray, nq: int, q_pos) -> np.ndarray:
+    """fp64 outputs ``[n][nq][D]`` for ``n`` (HeadCache, query chunk) pairs; chunk ``i``
+    is ``qs[i]`` (fp16 bits ``[nq][D]``) at positions ``q_pos[i] ..``.  OpenMP across pairs."""
+    n = len(heads)
+    structs = [h._struct() for h in heads]
+    arr = (C.POINTER(_Head) * n)(*[C.pointer(s) for s in structs])
+    qs = np.ascontiguousarray(qs, np.uint16).reshape(n, nq, -1)
+    pos = np.ascontiguousarray(np.broadcast_to(np.asarray(q_pos, np.int64), (n,)))
+    out = np.empty((n, nq, cfg["head_dim"]), np.float64)
+    c = make_cfg(cfg)
+    if lib().orc_chunk_many(C.byref(c), n, C.cast(arr, C.c_void_p), qs.ctypes.data, int(nq),
+                            pos.ctypes.data, out.ctypes.data):
+        raise RuntimeError("oracle chunk attention failed")
     return out
 
 

@@ -499,13 +499,15 @@ static void orc_rope(const double *x, double *y, int D, double pos, double theta
   }
 }
 
-/* out = softmax(q' K'^T / sqrt(D)) V over the whole cache of one kv head, for one
- * query vector q (fp16 [D], position q_pos).  Sums run in ascending t. */
-int orc_decode_head(const orc_cfg *c, const orc_head *hd, const uint16_t *q, int64_t q_pos,
-                    double *out) {
+/* out = softmax(q' K'^T / sqrt(D)) V over the first T tokens of one kv head's cache,
+ * for one query vector q (fp16 [D], rotated at position q_pos): the attention step of
+ * the decode loop over the dequantized cache ([TQ] section 4.2: the quantized cache is
+ * dequantized before it is used; [KVC3] "Pre-RoPE Key Quantization": keys are rotated
+ * at their own position when read).  Sums run in ascending t. */
+static int orc_attend(const orc_cfg *c, const orc_head *hd, const uint16_t *q, int64_t q_pos,
+                      int64_t T, double *out) {
   const int D = c->head_dim;
-  const int64_t T = hd->length;
-  if (T <= 0) return -1;
+  if (T <= 0 || T > hd->length) return -1;
   double *qx = (double *)malloc(sizeof(double) * D * 4);
   float *row = (float *)malloc(sizeof(float) * D);
   double *s = (double *)malloc(sizeof(double) * (size_t)T);
@@ -539,6 +541,29 @@ int orc_decode_head(const orc_cfg *c, const orc_head *hd, const uint16_t *q, int
   return 0;
 }
 
+/* Single-query decode: the query attends to every token the cache holds. */
+int orc_decode_head(const orc_cfg *c, const orc_head *hd, const uint16_t *q, int64_t q_pos,
+                    double *out) {
+  return orc_attend(c, hd, q, q_pos, hd->length, out);
+}
+
+/* A chunk of nq consecutive query tokens (a prefill chunk, or the draft tokens of a
+ * speculative-verification step; [UQ] section 5.1 counts first-token latency among
+ * the costs to evaluate): query j (fp16 [D] at q + j*D) sits at position q_pos + j
+ * and attends causally, to the cache tokens t <= q_pos + j, i.e. to the first
+ * min(q_pos + j + 1, length) of them.  out is [nq][D]. */
+int orc_chunk_head(const orc_cfg *c, const orc_head *hd, const uint16_t *q, int32_t nq,
+                   int64_t q_pos, double *out) {
+  if (nq <= 0 || q_pos < 0) return -1;
+  for (int32_t j = 0; j < nq; ++j) {
+    int64_t nvis = q_pos + j + 1;
+    if (nvis > hd->length) nvis = hd->length;
+    if (orc_attend(c, hd, q + (int64_t)j * c->head_dim, q_pos + j, nvis, out + (int64_t)j * c->head_dim))
+      return -1;
+  }
+  return 0;
+}
+
 /* Several independent (query, kv head) pairs; results do not depend on the
  * number of threads. */
 int orc_decode_many(const orc_cfg *c, int64_t n, const orc_head *const *hds,
@@ -547,6 +572,18 @@ int orc_decode_many(const orc_cfg *c, int64_t n, const orc_head *const *hds,
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
   for (int64_t i = 0; i < n; ++i)
     err |= orc_decode_head(c, hds[i], qs + i * c->head_dim, q_pos[i], outs + i * c->head_dim) != 0;
+  return err ? -1 : 0;
+}
+
+/* Several independent (query chunk, kv head) pairs: chunk i is nq queries at
+ * qs + i*nq*D, positions q_pos[i] .. q_pos[i] + nq - 1, output outs + i*nq*D. */
+int orc_chunk_many(const orc_cfg *c, int64_t n, const orc_head *const *hds, const uint16_t *qs,
+                   int32_t nq, const int64_t *q_pos, double *outs) {
+  int err = 0;
+  const int64_t stride = (int64_t)nq * c->head_dim;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+  for (int64_t i = 0; i < n; ++i)
+    err |= orc_chunk_head(c, hds[i], qs + i * stride, nq, q_pos[i], outs + i * stride) != 0;
   return err ? -1 : 0;
 }
 

@@ -50,6 +50,13 @@ static int run(orc_cfg c, int64_t T) {
   double out[256];
   const int64_t pos[3] = {T - 1, T + 1000, 3};
   for (int i = 0; i < 3 && !err; ++i) err |= orc_decode_head(&c, &h, q, pos[i], out);
+  /* a chunk of 5 queries in buffers of exactly 5 rows, the last rows past the end */
+  uint16_t *qc = malloc((size_t)(5 * D) * 2);
+  double *oc = malloc((size_t)(5 * D) * sizeof(double));
+  for (int64_t i = 0; i < 5 * D; ++i) qc[i] = f16_of(unif() * 2.0 - 1.0);
+  if (!err) err |= orc_chunk_head(&c, &h, qc, 5, T - 3, oc);
+  if (!err) err |= orc_chunk_head(&c, &h, qc, 5, 0, oc);
+  free(qc); free(oc);
   const int64_t nblk = T / c.k_block;
   if (nblk > 0) (void)orc_clip_threshold(k, (int64_t)c.k_block * D, 0.99f);
   free(deq); free(k); free(v); free(lut);

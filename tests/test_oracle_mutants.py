@@ -33,6 +33,10 @@ MUTANTS = {
     "lut_ties_upper": ("cc += d[i] > mid[k];", "cc += d[i] >= mid[k];"),
     "softmax_uses_key_as_value": ("orc_dequant_row(c, hd, 1, t, row);", "orc_dequant_row(c, hd, 0, t, row);"),
     "f2h_truncates": ("float r = nearbyintf(ldexpf(a, 10 - e));", "float r = truncf(ldexpf(a, 10 - e));"),
+    "chunk_excludes_own_token": ("int64_t nvis = q_pos + j + 1;", "int64_t nvis = q_pos + j;"),
+    "chunk_sees_whole_cache": ("if (nvis > hd->length) nvis = hd->length;", "nvis = hd->length;"),
+    "chunk_rotates_all_rows_at_first_position": ("q_pos + j, nvis,", "q_pos, nvis,"),
+    "chunk_row_offset_ignored": ("out + (int64_t)j * c->head_dim))", "out))"),
 }
 
 

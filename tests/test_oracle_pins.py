@@ -542,3 +542,86 @@ def test_blocks_are_independent_of_later_tokens(orc):
     assert np.array_equal(a.k_tail[:5], k[32:37]) and np.array_equal(a.v_tail[:5], v[32:37])
     assert np.array_equal(a.dequantize(0, 0, 32), b.dequantize(0, 0, 32))
     assert np.array_equal(a.dequantize(0, 32, 37), hval(k[32:37]).astype(np.float32))
+
+
+# --------------------------------------------------------------------------- chunk of queries
+def test_chunk_equals_textbook_causal_attention_on_grid(orc):
+    """Query j of a chunk sits at position q_pos + j and sees the tokens t <= q_pos + j.
+    On an on-grid cache (exact dequantization) every row must equal plain fp64 softmax
+    attention over that prefix, with rotary matrices applied to the raw inputs; rows
+    at or past the last token see the whole cache."""
+    rng = np.random.default_rng(61)
+    D, Bk, T = 16, 16, 48
+    c = tiny(head_dim=D, k_block=Bk, tokens=T + 5, v_group=D, capacity=64)
+    k = np.concatenate([_on_grid(rng, T, D, Bk, 15, True), rng.standard_normal((5, D))])
+    v = np.concatenate([_on_grid(rng, T, D, Bk, 15, False), rng.standard_normal((5, D))])
+    kb, vb = f16(k), f16(v)
+    hc = orc.HeadCache(c).build(kb, vb)
+    kr_all = [hval(kb[t]) for t in range(T + 5)]
+    for q_pos, nq in ((14, 5), (44, 12), (0, 3)):
+        q = f16(rng.standard_normal((nq, D)) * 2)
+        out = hc.chunk(q, q_pos)
+        assert out.shape == (nq, D)
+        for j in range(nq):
+            p = q_pos + j
+            n = min(p + 1, T + 5)
+            qr = _rot_matrix(p, D, 10000.0) @ hval(q[j])
+            kr = np.stack([_rot_matrix(t, D, 10000.0) @ kr_all[t] for t in range(n)])
+            ref = _softmax_attn(qr, kr, hval(vb[:n]), D)
+            assert np.max(np.abs(out[j] - ref)) < 1e-12, (q_pos, j)
+
+
+def test_chunk_zero_queries_average_their_prefix(orc):
+    """q = 0 gives equal weights, so row j is the mean of the first min(q_pos + j + 1, T)
+    dequantized values: the causal boundary is visible in the output."""
+    rng = np.random.default_rng(62)
+    c = tiny(head_dim=32, k_block=16, tokens=72, v_group=16, outlier_pct=4, clip_quantile=0.9)
+    k = _rand_block(rng, 72, 32, heavy=True)
+    v = _rand_block(rng, 72, 32, heavy=True)
+    hc = orc.HeadCache(c).build(k, v)
+    vh = _deq(hc, 1)
+    out = hc.chunk(f16(np.zeros((9, 32))), 62)
+    for j in range(9):
+        n = min(63 + j, 72)
+        assert np.allclose(out[j], vh[:n].mean(0), rtol=0, atol=1e-12), j
+
+
+def test_chunk_rows_equal_decode_over_the_prefix_cache(orc):
+    """Blocks are quantized independently of later tokens, so a cache built from the
+    first n tokens holds the same dequantized values whenever n is a block boundary or
+    lies past the last one (then the difference is only the shorter fp16 tail).  Row j
+    of a chunk must equal single-query decode over such a prefix cache; with nq = 1 at
+    the last position it is the decode over the whole cache."""
+    rng = np.random.default_rng(63)
+    c = tiny(head_dim=16, k_block=16, tokens=75, v_group=8, outlier_pct=7, clip_quantile=0.9)
+    k = _rand_block(rng, 75, 16, heavy=True)
+    v = _rand_block(rng, 75, 16, heavy=True)
+    full = orc.HeadCache(c).build(k, v)
+    q = f16(rng.standard_normal((12, 16)))
+    q_pos = 63                                             # rows see 64 (a boundary) .. 75 tokens
+    out = full.chunk(q, q_pos)
+    for j in range(12):
+        n = min(q_pos + j + 1, 75)
+        pre = orc.HeadCache(c).build(k[:n], v[:n])
+        ref = pre.decode(q[j], q_pos=q_pos + j)
+        assert np.max(np.abs(out[j] - ref)) < 1e-12, j
+    last = full.chunk(q[:1], 74)
+    assert np.array_equal(last[0], full.decode(q[0], q_pos=74))
+
+
+def test_chunk_ignores_tokens_after_each_query(orc):
+    """Changing the newest (fp16 tail) tokens leaves every row that does not see them
+    unchanged and changes the rows that do."""
+    rng = np.random.default_rng(64)
+    c = tiny(head_dim=16, k_block=16, tokens=45, v_group=16)
+    k = _rand_block(rng, 45, 16)
+    v = _rand_block(rng, 45, 16)
+    k2, v2 = k.copy(), v.copy()
+    k2[40:] = f16(rng.standard_normal((5, 16)) * 3)
+    v2[40:] = f16(rng.standard_normal((5, 16)) * 3)
+    a = orc.HeadCache(c).build(k, v)
+    b = orc.HeadCache(c).build(k2, v2)
+    q = f16(rng.standard_normal((8, 16)))
+    oa, ob = a.chunk(q, 35), b.chunk(q, 35)               # rows see 36 .. 43 tokens
+    assert np.array_equal(oa[:5], ob[:5])                  # rows 0..4 see t <= 39
+    assert all(np.max(np.abs(oa[j] - ob[j])) > 1e-6 for j in range(5, 8))
