@@ -207,6 +207,32 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int64_t q
 kvq_status kvq_decode_attention_noalloc(const kvq_cache *cache, const void *q, int64_t q_pos,
                                         float *out, int32_t num_splits, void *stream);
 
+/* Bytes of device workspace kvq_chunk_attention needs for a chunk of nq queries and
+ * `num_splits` splits per (b, kv-head) (0 = the library's choice; at most 4096): one
+ * (max, sum, output) partial of head_dim + 2 floats per (b, q-head, query, split),
+ * B * q_heads * nq * splits * (head_dim + 2) * 4 bytes, in the FlashAttention manner
+ * of [TQ] section 5.2.  Host only; returns 0 for an invalid cache, nq outside
+ * [1, 1024] or a negative split count. */
+size_t kvq_chunk_workspace_bytes(const kvq_cache *cache, int32_t nq, int32_t num_splits);
+
+/* Causal attention of a chunk of nq consecutive query tokens over the cache: a
+ * prefill chunk, or the draft tokens of a speculative-verification step ([UQ]
+ * section 5.1 counts first-token latency among the costs a deployment measures).
+ * Query j sits at position q_pos + j and sees the cache tokens t <= q_pos + j:
+ *   out[b][hq][j] = softmax_{t < n_j}( RoPE(q[b][hq][j], q_pos + j) . RoPE(k_hat[b][h][t], t) / sqrt(D) ) v_hat[b][h][t],
+ *   n_j = min(q_pos + j + 1, length),
+ * with h = hq / (q_heads/kv_heads) and k_hat, v_hat as in kvq_decode_attention.  The
+ * usual call appends the chunk's own keys and values first (kvq_quantize_append) and
+ * passes q_pos = length - nq.  With nq = 1 and q_pos = length - 1 this is the decode
+ * step.  q: *device* fp16 [batch][q_heads][nq][head_dim], pre-RoPE.  out: *device*
+ * fp32 [batch][q_heads][nq][head_dim].  ws: *device* workspace of ws_bytes >=
+ * kvq_chunk_workspace_bytes(cache, nq, num_splits).  The result does not depend on
+ * num_splits beyond fp32 rounding.  KVQ_EINVAL if length == 0, nq outside [1, 1024],
+ * q_pos < 0, or num_splits negative or above 4096. */
+kvq_status kvq_chunk_attention(const kvq_cache *cache, const void *q, int32_t nq, int64_t q_pos,
+                               float *out, void *ws, size_t ws_bytes, int32_t num_splits,
+                               void *stream);
+
 /* Dequantize tokens [t0, t1) of keys (which = 0) or values (which = 1) into *device*
  * fp32 out [batch][kv_heads][t1-t0][head_dim], pre-RoPE: x = fmaf(c, scale, zero) or
  * the codebook entry, outlier positions and tail tokens exact.  This is the

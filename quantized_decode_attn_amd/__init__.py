@@ -8,7 +8,7 @@ every call raises: there is no fallback.
 The functions carry the names of the C ABI in ``include/kvq.h``
 (``kvq_cache_layout``, ``kvq_cache_init``, ``kvq_quantize_append``,
 ``kvq_decode_workspace_bytes``, ``kvq_decode_attention``, ``kvq_decode_attention_noalloc``,
-``kvq_dequantize``,
+``kvq_chunk_workspace_bytes``, ``kvq_chunk_attention``, ``kvq_dequantize``,
 ``kvq_status_string``); ``Cache`` bundles the buffers of one cache.
 """
 from __future__ import annotations
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4, -5
 EXPORTED = ["kvq_status_string", "kvq_cache_layout", "kvq_cache_init", "kvq_quantize_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
-            "kvq_dequantize"]
+            "kvq_chunk_workspace_bytes", "kvq_chunk_attention", "kvq_dequantize"]
 NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -78,6 +78,10 @@ def lib() -> C.CDLL:
         L.kvq_decode_attention.argtypes = [C.POINTER(KvqCache), vp, i64, vp, vp, C.c_size_t, i32, vp]
         L.kvq_decode_attention_noalloc.restype = i32
         L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(KvqCache), vp, i64, vp, i32, vp]
+        L.kvq_chunk_workspace_bytes.restype = C.c_size_t
+        L.kvq_chunk_workspace_bytes.argtypes = [C.POINTER(KvqCache), i32, i32]
+        L.kvq_chunk_attention.restype = i32
+        L.kvq_chunk_attention.argtypes = [C.POINTER(KvqCache), vp, i32, i64, vp, vp, C.c_size_t, i32, vp]
         L.kvq_dequantize.restype = i32
         L.kvq_dequantize.argtypes = [C.POINTER(KvqCache), i32, i64, i64, vp, vp]
         _lib = L
@@ -138,6 +142,18 @@ def kvq_decode_attention_noalloc(cache: KvqCache, q, q_pos: int, out, num_splits
                                             int(num_splits), _stream(stream))
     if st != KVQ_OK:
         raise KvqError(st, "kvq_decode_attention_noalloc")
+
+
+def kvq_chunk_workspace_bytes(cache: KvqCache, nq: int, num_splits: int = 0) -> int:
+    return int(lib().kvq_chunk_workspace_bytes(C.byref(cache), int(nq), int(num_splits)))
+
+
+def kvq_chunk_attention(cache: KvqCache, q, nq: int, q_pos: int, out, ws, ws_bytes: int, num_splits: int = 0,
+                        stream=None) -> None:
+    st = lib().kvq_chunk_attention(C.byref(cache), _ptr(q), int(nq), int(q_pos), _ptr(out), _ptr(ws),
+                                   int(ws_bytes), int(num_splits), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_chunk_attention")
 
 
 def kvq_dequantize(cache: KvqCache, which: int, t0: int, t1: int, out, stream=None) -> None:
@@ -240,6 +256,27 @@ class Cache:
         _check_tensor(out, "out", shape, torch.float32, self.device)
         ws = self.workspace(num_splits)
         kvq_decode_attention(self.desc, q, q_pos, out, ws, ws.numel(), num_splits, stream)
+        return out
+
+    def chunk(self, q, q_pos: int | None = None, num_splits: int = 0, out=None, stream=None):
+        """q: fp16 [B][Hq][nq][D] on the device (pre-RoPE), queries at positions q_pos ..
+        q_pos + nq - 1 (default: the last nq tokens of the cache), each attending
+        causally.  Returns fp32 [B][Hq][nq][D]."""
+        import torch
+        if q.dim() != 4:
+            raise ValueError("q must be [B][Hq][nq][D]")
+        nq = q.shape[2]
+        if q_pos is None:
+            q_pos = self.length - nq
+        shape = (self.cfg["batch"], self.cfg["q_heads"], nq, self.cfg["head_dim"])
+        _check_tensor(q, "q", shape, torch.float16, self.device)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=q.device)
+        _check_tensor(out, "out", shape, torch.float32, self.device)
+        need = kvq_chunk_workspace_bytes(self.desc, nq, num_splits)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 4), dtype=torch.uint8, device=self.device)
+        kvq_chunk_attention(self.desc, q, nq, q_pos, out, self._ws, self._ws.numel(), num_splits, stream)
         return out
 
     def dequantize(self, which: int, t0: int = 0, t1: int | None = None, stream=None):

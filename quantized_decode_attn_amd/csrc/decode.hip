@@ -1,4 +1,6 @@
-// decode.hip -- single-query decode attention computed directly on the packed cache.
+// decode.hip -- decode attention computed directly on the packed cache: the generic
+// split kernel (any supported configuration, one query or a causal chunk of queries)
+// and the kernel that merges the split partials.
 //
 // Pages cited (title, address):
 //   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
@@ -18,12 +20,15 @@
 // ([TQ] sections 5.1 and 6.3; [UQ] section 4.2; the custom kernels of [KVC3]
 // "Q-Norm 与其他细节").
 //
-// Work split (split-K flash decoding): a work item is (b, kv-head, split); a split is
-// a contiguous range of Bk-token blocks (the last split of a sequence also takes the
-// unquantized tail).  Each wave owns whole items and keeps, for every query head of
-// its kv-head, the running max m, the running sum l and the unnormalised output o
-// (online softmax in base 2).  Partials (m, l, o) go to the workspace and a second
-// kernel merges the splits of every (b, q-head) in a fixed order.
+// Work split (split-K flash decoding): a work item is (b, kv-head, row set, split); a
+// split is a contiguous range of Bk-token blocks (the last split of a sequence also
+// takes the unquantized tail).  A row is one query vector: query head g of the kv head
+// and, for a chunk of nq queries, query j, rotated at q_pos + j and seeing the first
+// min(q_pos + j + 1, length) tokens (single-query decode: one query per head, the whole
+// cache).  Each wave owns whole items and keeps, for every row of its set, the running
+// max m, the running sum l and the unnormalised output o (online softmax in base 2).
+// Partials (m, l, o) go to the workspace and a second kernel merges the splits of
+// every row in a fixed order.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -55,17 +60,17 @@ struct WaveLds {  // offsets (in floats) of one wave's scratch area
   int wts, wq, p, ps, vs, vz, state, vc, lut, total;
 };
 
-__host__ __device__ inline WaveLds wave_lds(int D, int Bk, int gq, int ng, int tpi, int kb, int kmode,
+__host__ __device__ inline WaveLds wave_lds(int D, int Bk, int rows, int ng, int tpi, int kb, int kmode,
                                              bool ko) {
   WaveLds w;
   int o = 0;
   w.wts = o; o += (D / 2) * 12;
-  w.wq = o; o += gq * D;
+  w.wq = o; o += rows * D;
   w.p = o; o += Bk;
   w.ps = o; o += Bk * ng;
   w.vs = o; o += Bk * ng;
   w.vz = o; o += Bk * ng;
-  w.state = o; o += gq * (D + 2 + ng);
+  w.state = o; o += rows * (D + 2 + ng);
   w.vc = o; o += ko ? tpi * D : 0;
   w.lut = o; o += kmode == 1 ? D * (1 << kb) : 0;
   w.total = o;
@@ -82,13 +87,12 @@ __device__ __forceinline__ uint32_t get_code(const uint32_t (&w)[KW], int k) {
 
 template <int D, int KB, int KMODE, int VB>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
-                                                                const uint16_t* __restrict__ q,
-                                                                int64_t q_pos, float* __restrict__ ws,
-                                                                int S, int64_t nitems) {
+                                                                const uint16_t* __restrict__ q, RowSpec rs,
+                                                                float* __restrict__ ws, int S, int64_t nitems) {
   using Sh = Shape<D, KB, KMODE, VB>;
   extern __shared__ float lds[];
   const int Bk = c.cfg.k_block;
-  const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, GQ = Hq / H;
+  const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, GQ = Hq / H, R = GQ * rs.nq;
   const int G = c.cfg.v_group, ng = D / G;
   const int ko = kout_of(c.cfg);
   const int64_t T = c.cfg.capacity;
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     table[j * Sh::TPITCH + 2 * i] = c.rope[2 * idx];
     table[j * Sh::TPITCH + 2 * i + 1] = c.rope[2 * idx + 1];
   }
-  const WaveLds L = wave_lds(D, Bk, GQ, ng, Sh::TPI, KB, KMODE, ko > 0);
+  const WaveLds L = wave_lds(D, Bk, rs.rpi, ng, Sh::TPI, KB, KMODE, ko > 0);
   float* wl = lds + Bk * Sh::TPITCH + wave * L.total;
   float* wts = wl + L.wts;
   float* wq = wl + L.wq;
@@ -121,20 +125,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
   const int64_t total_waves = (int64_t)gridDim.x * kWaves;
   for (int64_t item = (int64_t)blockIdx.x * kWaves + wave; item < nitems; item += total_waves) {
     const int split = (int)(item % S);
-    const int64_t bh = item / S;
+    const int64_t rest = item / S;
+    const int set = (int)(rest % rs.nsets);
+    const int64_t bh = rest / rs.nsets;
     const int h = (int)(bh % H);
     const int b = (int)(bh / H);
+    const int row0 = set * rs.rpi;
+    const int nrows = R - row0 < rs.rpi ? R - row0 : rs.rpi;
     const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
     const bool do_tail = split == S - 1 && ntail > 0;
+    // the widest view of the set's rows: no later token is visible to any of them
+    int64_t vmax = 0;
+    for (int g = 0; g < nrows; ++g) {
+      const int64_t v = row_visible(rs, (row0 + g) % rs.nq, c.length);
+      vmax = v > vmax ? v : vmax;
+    }
 
     // ---- per item: query weights Wq = scale * conj(q) * e^{-i f p} (fp64), state reset
-    for (int g = 0; g < GQ; ++g) {
-      const uint16_t* qv = q + ((int64_t)b * Hq + (int64_t)h * GQ + g) * D;
+    for (int g = 0; g < nrows; ++g) {
+      const int row = row0 + g, qj = row % rs.nq;
+      const uint16_t* qv = q + (((int64_t)b * Hq + (int64_t)h * GQ + row / rs.nq) * rs.nq + qj) * D;
+      const int64_t pos = rs.q_pos + qj;
       for (int i = lane; i < Sh::HALF; i += kWave) {
         const double qa = (double)h2f(qv[i]), qb = (double)h2f(qv[i + Sh::HALF]);
         const double f = pow((double)c.cfg.rope_theta, -(2.0 * i) / (double)D);
         double sn, cs;
-        sincos((double)q_pos * f, &sn, &cs);
+        sincos((double)pos * f, &sn, &cs);
         const double sc = (double)kLog2e / sqrt((double)D);
         wq[g * D + 2 * i] = (float)(sc * (qa * cs - qb * sn));
         wq[g * D + 2 * i + 1] = (float)(-sc * (qa * sn + qb * cs));
@@ -156,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       const bool tail = bi == n1 - n0;
       const int64_t n = tail ? nfull : n0 + bi;
       const int64_t tb = n * Bk;                         // absolute first token
+      if (tb >= vmax) break;                             // past every row's view (blocks ascend)
       const int ntok = tail ? ntail : Bk;
       const int iters = (ntok + Sh::TPI - 1) / Sh::TPI;
 
@@ -168,7 +185,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
         }
       }
 
-      for (int g = 0; g < GQ; ++g) {
+      for (int g = 0; g < nrows; ++g) {
+        // tokens of this block the row sees (a causal row may see none or a prefix)
+        const int64_t seen = row_visible(rs, (row0 + g) % rs.nq, c.length) - tb;
+        if (seen <= 0) continue;
+        const int nvis = seen < ntok ? (int)seen : ntok;
         float* st = state + g * (D + 2 + ng);
         // ---- per block and pair: W = Wq * e^{i f n Bk}, folded with the metadata
         for (int i = lane; i < Sh::HALF; i += kWave) {
@@ -265,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
             }
           }
           s = group_sum<Sh::LPT>(s);
-          if (j >= ntok) s = -__builtin_inff();
+          if (j >= nvis) s = -__builtin_inff();
           sc[it] = s;
           mloc = fmaxf(mloc, s);
         }
@@ -279,10 +300,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
         for (int it = 0; it < MAXIT; ++it) {
           if (it >= iters) break;
           const int j = it * Sh::TPI + ts;
-          const float p = j < ntok ? exp2f(sc[it] - mnew) : 0.0f;
+          const float p = j < nvis ? exp2f(sc[it] - mnew) : 0.0f;
           if (r == 0) {
             lsum += p;
-            if (j < ntok) Pl[j] = p;
+            if (j < ntok) Pl[j] = p;  // 0 for the tokens the row does not see
           }
         }
         lsum = wave_sum(lsum);
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
               for (int row = 0; row < Sh::TPI; ++row) acc[k] += VC[row * D + lane + k * kWave];
           }
         } else {
-          for (int j = 0; j < ntok; ++j) {
+          for (int j = 0; j < nvis; ++j) {
             const float p = Pl[j];
 #pragma unroll
             for (int k = 0; k < Sh::CPL; ++k)
@@ -357,10 +378,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       }
     }
 
-    // ---- write the partial of every query head of this kv head
-    for (int g = 0; g < GQ; ++g) {
+    // ---- write the partial of every row of the set
+    for (int g = 0; g < nrows; ++g) {
+      const int row = row0 + g;
       const float* st = state + g * (D + 2 + ng);
-      float* dst = ws + (((int64_t)b * Hq + (int64_t)h * GQ + g) * S + split) * (D + 2);
+      float* dst = ws + ((((int64_t)b * Hq + (int64_t)h * GQ + row / rs.nq) * rs.nq + row % rs.nq) * S + split) *
+                            (D + 2);
       for (int k = lane; k < D; k += kWave) dst[2 + k] = st[2 + k] + st[2 + D + k / G];
       if (lane == 0) {
         dst[0] = st[0];
@@ -371,20 +394,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
   }
 }
 
-// Finish one (b, q-head): optionally attend over the unquantized tail tokens (exact
-// fp16 keys and values, the newest length % k_block tokens), then merge the S split
-// partials and the tail in a fixed order:
+// Finish one row (b, q-head, query j): optionally attend over the unquantized tail
+// tokens the row sees (exact fp16 keys and values, the newest length % k_block tokens),
+// then merge the S split partials and the tail in a fixed order:
 //   M = max m_s,  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const uint16_t* __restrict__ q,
-                                                          int64_t q_pos, const float* __restrict__ ws,
+                                                          RowSpec rs, const float* __restrict__ ws,
                                                           float* __restrict__ out, int S, int with_tail) {
   const int D = c.cfg.head_dim, half = D / 2, Bk = c.cfg.k_block;
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H;
-  const int64_t bq = blockIdx.x;
-  const int b = (int)(bq / Hq), hq = (int)(bq % Hq), h = hq / gq;
+  const int64_t bq = blockIdx.x;  // row index over [B][Hq][nq]
+  const int qj = (int)(bq % rs.nq);
+  const int64_t bhq = bq / rs.nq;
+  const int b = (int)(bhq / Hq), hq = (int)(bhq % Hq), h = hq / gq;
   const int64_t bh = (int64_t)b * H + h;
+  const int64_t q_pos = rs.q_pos + qj;
   const int64_t nfull = c.length / Bk;
-  const int ntail = with_tail ? (int)(c.length - nfull * Bk) : 0;
+  int ntail = with_tail ? (int)(c.length - nfull * Bk) : 0;
+  if (ntail > 0) {  // the tail tokens this row sees
+    const int64_t seen = row_visible(rs, qj, c.length) - nfull * Bk;
+    ntail = seen <= 0 ? 0 : (seen < ntail ? (int)seen : ntail);
+  }
   const int tid = threadIdx.x;
   if (ntail == 0 && S <= kFinishFastSplits) {
     // No tail and few splits: each channel's thread loads every split's (m, l) and its
@@ -526,44 +556,64 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
 }
 
 template <int D, int KB, int KMODE, int VB>
-hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                        hipStream_t s, int cus) {
+hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s,
+                        int cus) {
   using Sh = Shape<D, KB, KMODE, VB>;
-  const int GQ = c.cfg.q_heads / c.cfg.kv_heads, ng = D / c.cfg.v_group;
-  const WaveLds L = wave_lds(D, c.cfg.k_block, GQ, ng, Sh::TPI, KB, KMODE, host_kout(c.cfg) > 0);
-  const size_t bytes = ((size_t)c.cfg.k_block * Sh::TPITCH + (size_t)kWaves * L.total) * sizeof(float);
-  if (bytes > 160 * 1024) return hipErrorInvalidValue;
+  const int R = c.cfg.q_heads / c.cfg.kv_heads * rs.nq, ng = D / c.cfg.v_group;
+  // rows per item: up to 8 (all query heads of a kv head for one query), fewer when
+  // their state does not fit the LDS
+  int rpi = R < 8 ? R : 8;
+  size_t bytes = 0;
+  for (;; --rpi) {
+    if (rpi < 1) return hipErrorInvalidValue;
+    const WaveLds L = wave_lds(D, c.cfg.k_block, rpi, ng, Sh::TPI, KB, KMODE, host_kout(c.cfg) > 0);
+    bytes = ((size_t)c.cfg.k_block * Sh::TPITCH + (size_t)kWaves * L.total) * sizeof(float);
+    if (bytes <= 160 * 1024) break;
+  }
+  rs.rpi = rpi;
+  rs.nsets = (R + rpi - 1) / rpi;
   hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<D, KB, KMODE, VB>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
-  const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
+  const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * rs.nsets * S;
   int64_t grid = (nitems + kWaves - 1) / kWaves;
   const int64_t cap = (int64_t)cus * (bytes <= 80 * 1024 ? 2 : 1);
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL((decode_split_kernel<D, KB, KMODE, VB>), dim3((unsigned)grid), dim3(kThreads), bytes, s,
-                     c, q, q_pos, ws, S, nitems);
+                     c, q, rs, ws, S, nitems);
   return hipGetLastError();
 }
 
 template <int D, int KB, int KMODE>
-hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
-                     int cus) {
-  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, q_pos, ws, S, s, cus);
-  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, q_pos, ws, S, s, cus);
+hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s, int cus) {
+  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, rs, ws, S, s, cus);
+  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, rs, ws, S, s, cus);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
-                    int cus) {
+hipError_t launch_d(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s, int cus) {
   const int kb = c.cfg.k_bits, km = c.cfg.k_mode;
-  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, q_pos, ws, S, s, cus);
-  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, q_pos, ws, S, s, cus);
-  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, q_pos, ws, S, s, cus);
-  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, q_pos, ws, S, s, cus);
-  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, q_pos, ws, S, s, cus);
-  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, q_pos, ws, S, s, cus);
+  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, rs, ws, S, s, cus);
+  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, rs, ws, S, s, cus);
+  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, rs, ws, S, s, cus);
+  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, rs, ws, S, s, cus);
+  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, rs, ws, S, s, cus);
+  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, rs, ws, S, s, cus);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_generic(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s,
+                          int cus) {
+  if (c.cfg.head_dim == 128) return launch_d<128>(c, q, rs, ws, S, s, cus);
+  if (c.cfg.head_dim == 64) return launch_d<64>(c, q, rs, ws, S, s, cus);
+  return hipErrorInvalidValue;
+}
+
+int device_cus() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  return cus;
 }
 
 }  // namespace
@@ -575,20 +625,34 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
 
 hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
                          int splits, hipStream_t s) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cus();
+  const RowSpec rs{q_pos, 1, 0, 1, 1};
   hipError_t e = launch_decode_mha(c, q, q_pos, ws, splits, s, cus);
   if (e == hipErrorNotSupported) e = launch_decode_gqa(c, q, q_pos, ws, splits, s, cus);
   int with_tail = 1;  // the tuned kernels leave the unquantized tail to the finish kernel
   if (e == hipErrorNotSupported) {
     with_tail = 0;
-    if (c.cfg.head_dim == 128) e = launch_d<128>(c, q, q_pos, ws, splits, s, cus);
-    else if (c.cfg.head_dim == 64) e = launch_d<64>(c, q, q_pos, ws, splits, s, cus);
-    else e = hipErrorInvalidValue;
+    e = launch_generic(c, q, rs, ws, splits, s, cus);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(256), 0, s, c,
-                     q, q_pos, ws, out, splits, with_tail);
+                     q, rs, ws, out, splits, with_tail);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk(const kvq_cache& c, const uint16_t* q, int nq, int64_t q_pos, float* out, float* ws,
+                        int splits, hipStream_t s) {
+  const int cus = device_cus();
+  const RowSpec rs{q_pos, nq, 1, 1, 1};
+  hipError_t e = launch_chunk_mfma(c, q, rs, ws, splits, s, cus);
+  int with_tail = 1;  // the matrix-core kernel leaves the unquantized tail to the finish kernel
+  if (e == hipErrorNotSupported) {
+    with_tail = 0;
+    e = launch_generic(c, q, rs, ws, splits, s, cus);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)((int64_t)c.cfg.batch * c.cfg.q_heads * nq)), dim3(256),
+                     0, s, c, q, rs, ws, out, splits, with_tail);
   return hipGetLastError();
 }
 

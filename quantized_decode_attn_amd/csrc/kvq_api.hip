@@ -88,6 +88,23 @@ int auto_splits(const kvq_config& c) {
   return (int)s;
 }
 
+// Splits per (b, kv-head) for a chunk of nq queries: about two work items per SIMD of
+// an MI355X (256 CUs x 4) over the row tiles of 16, in multiples of 4 (the waves of a
+// matrix-core workgroup), without splitting a sequence below one block per split.
+int auto_chunk_splits(const kvq_config& c, int nq) {
+  const int64_t rows = (int64_t)(c.q_heads / c.kv_heads) * nq;
+  const int64_t units = (int64_t)c.batch * c.kv_heads * ((rows + 15) / 16);
+  int64_t s = (2048 + units - 1) / units;
+  s = (s + 3) / 4 * 4;
+  const int64_t nblk = c.capacity / c.k_block;
+  if (s > nblk) s = nblk;
+  if (s > 4096) s = 4096;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+constexpr int32_t kMaxChunk = 1024;
+
 }  // namespace
 
 extern "C" {
@@ -211,6 +228,28 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, i
   st = scratch_of_current_device(&ws);
   if (st != KVQ_OK) return st;
   return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, ws, S, (hipStream_t)stream));
+}
+
+size_t kvq_chunk_workspace_bytes(const kvq_cache* cache, int32_t nq, int32_t num_splits) {
+  if (check_cache(cache) != KVQ_OK || num_splits < 0 || nq < 1 || nq > kMaxChunk) return 0;
+  const kvq_config& c = cache->cfg;
+  const int S = num_splits ? num_splits : auto_chunk_splits(c, nq);
+  return (size_t)c.batch * c.q_heads * nq * S * (c.head_dim + 2) * sizeof(float);
+}
+
+kvq_status kvq_chunk_attention(const kvq_cache* cache, const void* q, int32_t nq, int64_t q_pos, float* out,
+                               void* ws, size_t ws_bytes, int32_t num_splits, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || q_pos < 0 || num_splits < 0 || cache->length == 0) return KVQ_EINVAL;
+  if (nq < 1 || nq > kMaxChunk || q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
+  const kvq_config& c = cache->cfg;
+  const int S = num_splits ? num_splits : auto_chunk_splits(c, nq);
+  if (S > 4096) return KVQ_EINVAL;
+  const size_t need = (size_t)c.batch * c.q_heads * nq * S * (c.head_dim + 2) * sizeof(float);
+  if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
+  return from_hip(kvq::launch_chunk(*cache, (const uint16_t*)q, nq, q_pos, out, (float*)ws, S,
+                                    (hipStream_t)stream));
 }
 
 kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, int64_t t0, int64_t t1, float* out,

@@ -37,6 +37,32 @@ hipError_t launch_tail_copy(const kvq_cache& c, const uint16_t* k_new, const uin
 hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out,
                          float* ws, int splits, hipStream_t s);
 
+// Rows of the split kernels: query vectors (query head g of a kv head, query j of a
+// chunk of nq; q and out are [B][Hq][nq][D]) with their rotation position q_pos + j
+// and the cache tokens they see.
+struct RowSpec {
+  int64_t q_pos;  // position of query 0
+  int nq;         // queries per query head
+  int causal;     // 1: query j sees the tokens t <= q_pos + j; 0: the whole cache
+  int rpi;        // rows per work item (set by the launcher of the generic kernel)
+  int nsets;      // row sets per kv head (idem)
+};
+
+__host__ __device__ inline int64_t row_visible(const RowSpec& rs, int j, int64_t length) {
+  if (!rs.causal) return length;
+  const int64_t n = rs.q_pos + j + 1;
+  return n < length ? n : length;
+}
+
+// Causal attention of a chunk of nq queries (the generic split kernel, or the
+// matrix-core kernel where it applies), partials merged by the finish kernel.
+hipError_t launch_chunk(const kvq_cache& c, const uint16_t* q, int nq, int64_t q_pos, float* out,
+                        float* ws, int splits, hipStream_t s);
+
+// The matrix-core chunk kernel; hipErrorNotSupported for configurations it does not cover.
+hipError_t launch_chunk_mfma(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S,
+                             hipStream_t s, int cus);
+
 hipError_t launch_dequantize(const kvq_cache& c, int which, int64_t t0, int64_t t1, float* out,
                              hipStream_t s);
 

@@ -32,7 +32,7 @@ import multiprocessing as _mp
 import numpy as np
 
 CHUNK = 65536
-TENSOR_K, TENSOR_V, TENSOR_Q, TENSOR_STD, TENSOR_INJECT, TENSOR_CALIB = 0, 1, 2, 3, 4, 5
+TENSOR_K, TENSOR_V, TENSOR_Q, TENSOR_STD, TENSOR_INJECT, TENSOR_CALIB, TENSOR_QCHUNK = 0, 1, 2, 3, 4, 5, 6
 
 # The five workloads.  ``tokens`` is the cache length the decode attends over;
 # ``existing`` (only the prefill-append workload) is the part already in the
@@ -176,6 +176,16 @@ def gen_q(cfg: dict, seed: int = 0) -> np.ndarray:
     out = np.empty((B, Hq, D), np.uint16)
     for b in range(B):
         out[b] = _rng(seed, TENSOR_Q, b).standard_normal((Hq, D)).astype(np.float16).view(np.uint16)
+    return out
+
+
+def gen_q_chunk(cfg: dict, nq: int, seed: int = 0) -> np.ndarray:
+    """Queries of a chunk of ``nq`` tokens, fp16 bits ``uint16 [B][Hq][nq][D]``
+    (pre-RoPE), drawn like the decode queries from N(0, 1)."""
+    B, Hq, D = cfg["batch"], cfg["q_heads"], cfg["head_dim"]
+    out = np.empty((B, Hq, nq, D), np.uint16)
+    for b in range(B):
+        out[b] = _rng(seed, TENSOR_QCHUNK, b, nq).standard_normal((Hq, nq, D)).astype(np.float16).view(np.uint16)
     return out
 
 

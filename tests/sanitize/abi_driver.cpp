@@ -25,6 +25,9 @@ hipError_t launch_decode(const kvq_cache&, const uint16_t*, int64_t, float*, flo
 hipError_t launch_dequantize(const kvq_cache&, int, int64_t, int64_t, float*, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_chunk(const kvq_cache&, const uint16_t*, int, int64_t, float*, float*, int, hipStream_t) {
+  return hipErrorNotSupported;
+}
 }  // namespace kvq
 
 static int failures = 0;
@@ -129,6 +132,20 @@ int main() {
   big.batch = 8; big.q_heads = 32; big.kv_heads = 32;
   kvq_cache kb = fake_cache(big, 100);
   EXPECT(kvq_decode_attention_noalloc(&kb, (void*)0x1000, 99, out, 4096, nullptr) == KVQ_EWORKSPACE);
+  // chunk of queries: workspace sizing and argument checks
+  EXPECT(kvq_chunk_workspace_bytes(&k, 5, 3) == (size_t)2 * 8 * 5 * 3 * 130 * 4);
+  EXPECT(kvq_chunk_workspace_bytes(&k, 0, 3) == 0 && kvq_chunk_workspace_bytes(&k, 1025, 3) == 0);
+  EXPECT(kvq_chunk_workspace_bytes(&k, 5, -1) == 0 && kvq_chunk_workspace_bytes(nullptr, 5, 3) == 0);
+  const size_t cws = kvq_chunk_workspace_bytes(&k, 5, 0);
+  EXPECT(cws > 0 && cws % ((size_t)2 * 8 * 5 * 130 * 4) == 0);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, 295, out, (void*)0x3000, cws, 0, nullptr) == KVQ_EHIP);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, 295, out, (void*)0x3000, cws - 1, 0, nullptr) == KVQ_EWORKSPACE);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 0, 295, out, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 1025, 0, out, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, -1, out, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, 295, out, (void*)0x3000, cws, 4097, nullptr) == KVQ_EINVAL);
+  EXPECT(kvq_chunk_attention(&k, nullptr, 5, 295, out, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
+  EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, 295, nullptr, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
   EXPECT(kvq_dequantize(&k, 0, 0, 300, out, nullptr) == KVQ_EHIP);
   EXPECT(kvq_dequantize(&k, 2, 0, 300, out, nullptr) == KVQ_EINVAL);
   EXPECT(kvq_dequantize(&k, 1, 10, 5, out, nullptr) == KVQ_EINVAL);
