@@ -12,7 +12,11 @@ decode call's average duration, measured with HIP events on the stream the kerne
 run on); the append's tokens/s is reported beside it, as is a read-streaming probe
 (the achievable bandwidth of a plain 1 GiB read on the same device and stream).
 
-    python bench.py [--steps K] [--warmup W] [--workload c4] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload c4] [--gpus 1] [--chunk NQ]
+
+``--chunk NQ`` adds a third timed call to every step: causal attention of a chunk of NQ
+queries per sequence at the newest NQ positions (a prefill chunk or speculative
+verification) over the same cache, reported under "chunk".
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -174,6 +178,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0, help="also time attention of a chunk of this many queries")
+    ap.add_argument("--chunk-splits", type=int, default=0)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -210,10 +216,14 @@ def main():
     n_new = T - existing
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     cache.workspace(args.splits)
+    nq = args.chunk
+    if nq:
+        qc_d = up(synth.gen_q_chunk(cfg, nq))
+        outc = torch.empty((B, Hq, nq, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     # Untimed between the timed regions: a 1 GiB read that evicts the 256 MB Infinity
     # Cache and the L2 (writing back the append's dirty lines), so that neither the append
     # nor the decode starts with the other's data, or dirty lines, in the caches.
@@ -230,6 +240,11 @@ def main():
         if e: e[2].record(stream)
         cache.decode(q_d, q_pos=T - 1, num_splits=args.splits, out=out)
         if e: e[3].record(stream)
+        if nq:
+            scrub_view.sum()
+            if e: e[4].record(stream)
+            cache.chunk(qc_d, q_pos=T - nq, num_splits=args.chunk_splits, out=outc)
+            if e: e[5].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -304,6 +319,23 @@ def main():
         "decode_frac_of_stream": round(dec_gbps / probe_gbps, 4),
         "append_frac_of_stream": round(app_gbps / probe_gbps, 4),
     }
+    if nq:
+        ch_ms = np.array([ev[i][4].elapsed_time(ev[i][5]) for i in range(args.steps)])
+        cbytes = B * H * T * decode_bytes_per_token_head(cfg) + B * Hq * nq * D * (2 + 4)
+        # QK and PV: 2 D flops each per (query, visible token)
+        vis = sum(min(T - nq + j + 1, T) for j in range(nq))
+        cflops = 4.0 * B * Hq * D * vis
+        c_gbps = cbytes / (ch_ms.mean() * 1e-3) / 1e9
+        c_tflops = cflops / (ch_ms.mean() * 1e-3) / 1e12
+        log("chunk   %.1f us  nq %d  %.1f GB/s (%.1f%% of 8 TB/s)  %.1f TFLOP/s"
+            % (ch_ms.mean() * 1e3, nq, c_gbps, c_gbps / 80, c_tflops))
+        rec["chunk"] = {"nq": nq, "q_pos": T - nq, "splits": args.chunk_splits or "auto",
+                        "us": round(float(ch_ms.mean()) * 1e3, 2),
+                        "GBps": round(c_gbps, 2), "frac_hbm_peak": round(c_gbps / HBM_PEAK_GBPS, 4),
+                        "TFLOPs": round(c_tflops, 2), "algorithmic_bytes": int(cbytes),
+                        "algorithmic_flops": cflops,
+                        "query_tokens_per_s": round(B * nq / (ch_ms.mean() * 1e-3), 1),
+                        "kernel": "chunk (split + finish launches)"}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds)

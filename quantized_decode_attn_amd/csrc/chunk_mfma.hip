@@ -56,7 +56,7 @@ namespace {
 
 using namespace dcm;
 
-constexpr int kCW = 4;                      // waves per workgroup
+constexpr int kCW = 8;                      // waves per workgroup
 constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;                 // floats per rotary-table row
 constexpr int kRows = 16;                   // rows per tile
@@ -75,23 +75,16 @@ __device__ __forceinline__ f4 mfma16(u4v a, u4v b, f4 c) {
 }
 
 // Two fp32 values as fp16 (rounded toward zero) in one dword, and their remainders
-// x - hi (exact in fp32, then rounded toward zero) in another.
+// x - hi (exact in fp32, then rounded toward zero) in another.  `neg1` is -1.0 passed
+// in from the host: as a value the compiler cannot see, x + neg1 * hi stays one mixed
+// fp16/fp32 fused multiply-add (v_fma_mix_f32) instead of a conversion and a subtraction.
 __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
-__device__ __forceinline__ float rem_lo(float x, uint32_t hi) {
-  float r;
-  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi), "v"(x));
-  return r;
-}
-__device__ __forceinline__ float rem_hi(float x, uint32_t hi) {
-  float r;
-  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi), "v"(x));
-  return r;
-}
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo, float neg1) {
   hi = pk_rtz(a, b);
-  lo = pk_rtz(rem_lo(a, hi), rem_hi(b, hi));
+  const h2t h = __builtin_bit_cast(h2t, hi);
+  lo = pk_rtz(__builtin_fmaf((float)h.x, neg1, a), __builtin_fmaf((float)h.y, neg1, b));
 }
 
 // The exponent e with bound * 2^e in [2^14, 2^15) (bound > 0).
@@ -145,45 +138,64 @@ struct CRegs {
   uint32_t vs[2], vz[2];  // value scale/zero of tokens lane, 64 + lane (both groups)
 };
 
-template <int VB>
-__device__ __forceinline__ const uint8_t* ck_block(const kvq_cache& c, int64_t bh, int64_t n) {
-  return static_cast<const uint8_t*>(c.k_codes) + (bh * c.cfg.capacity + n * kBK) * (kD / 2);
-}
-template <int VB>
-__device__ __forceinline__ const uint32_t* cv_block(const kvq_cache& c, int64_t bh, int64_t n) {
-  constexpr int TPW = 32 / VB;
-  return static_cast<const uint32_t*>(c.v_codes) + (bh * (c.cfg.capacity / TPW) + n * (kBK / TPW)) * kD;
-}
-template <int VB>
-__device__ __forceinline__ void cload_k(CRegs<VB>& R, int tau, const uint8_t* kblk, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-  const int t = tok_of<VB>(tau, m >> 2, m & 3);
-  R.k[tau] = *reinterpret_cast<const uint4*>(kblk + (uint32_t)(t * (kD / 2) + 16 * g));
-}
-template <int VB>
-__device__ __forceinline__ void cload_v(CRegs<VB>& R, int kp, int h, const uint32_t* vblk, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-  const int word = VB == 4 ? 4 * kp + g : 2 * kp + (g >> 1);
-  R.v[kp][h] = *reinterpret_cast<const uint4*>(vblk + (uint32_t)(word * kD + 64 * h + 4 * m));
+// Buffer resources of one (b, kv-head): the head's slice of each buffer, with its exact
+// size as the record count (a load outside it returns 0 instead of touching other
+// memory).  Loads then take a lane-constant 32-bit offset and a wave-uniform block
+// offset, so block addresses cost no vector registers.
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 family: raw (untyped) buffer access
+struct CRsrc {
+  __amdgpu_buffer_rsrc_t k, v, ks, kz, vs, vz, rope;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
 }
 template <int VB, int NG>
-__device__ __forceinline__ void cload_meta(CRegs<VB>& R, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
-  const int64_t m = (bh * (c.cfg.capacity / kBK) + n) * kD;
-  R.kmeta[0] = c.k_scale[m + lane];
-  R.kmeta[1] = c.k_scale[m + lane + kHalf];
-  R.kmeta[2] = c.k_zero[m + lane];
-  R.kmeta[3] = c.k_zero[m + lane + kHalf];
-  R.eb = reinterpret_cast<const float2*>(c.rope + (int64_t)kBK * kD + n * kD)[lane];
-  const int64_t m0 = (bh * c.cfg.capacity + n * kBK) * NG;
+__device__ __forceinline__ CRsrc head_rsrc(const kvq_cache& c, int64_t bh) {
+  const int64_t T = c.cfg.capacity;
+  CRsrc r;
+  r.k = rsrc(static_cast<const uint8_t*>(c.k_codes) + bh * T * (kD / 2), T * (kD / 2));
+  r.v = rsrc(static_cast<const uint8_t*>(c.v_codes) + bh * T * (kD * VB / 8), T * (kD * VB / 8));
+  r.ks = rsrc(c.k_scale + bh * (T / kBK) * kD, (T / kBK) * kD * 2);
+  r.kz = rsrc(c.k_zero + bh * (T / kBK) * kD, (T / kBK) * kD * 2);
+  r.vs = rsrc(c.v_scale + bh * T * NG, T * NG * 2);
+  r.vz = rsrc(c.v_zero + bh * T * NG, T * NG * 2);
+  r.rope = rsrc(c.rope, ((int64_t)kBK + T / kBK) * kD * 4);
+  return r;
+}
+
+template <int VB>
+__device__ __forceinline__ void cload_k(CRegs<VB>& R, int tau, const CRsrc& rs, int64_t n, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const int t = tok_of<VB>(tau, m >> 2, m & 3);
+  R.k[tau] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs.k, t * (kD / 2) + 16 * g, (int)(n * kBK * (kD / 2)), 0));
+}
+template <int VB>
+__device__ __forceinline__ void cload_v(CRegs<VB>& R, int kp, int h, const CRsrc& rs, int64_t n, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const int word = VB == 4 ? 4 * kp + g : 2 * kp + (g >> 1);
+  R.v[kp][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rs.v, (word * kD + 64 * h + 4 * m) * 4, (int)(n * kBK * kD * VB / 8), 0));
+}
+template <int VB, int NG>
+__device__ __forceinline__ void cload_meta(CRegs<VB>& R, const CRsrc& rs, int64_t n, int lane) {
+  const int kb = (int)(n * kD * 2);
+  R.kmeta[0] = __builtin_amdgcn_raw_buffer_load_b16(rs.ks, 2 * lane, kb, 0);
+  R.kmeta[1] = __builtin_amdgcn_raw_buffer_load_b16(rs.ks, 2 * (lane + kHalf), kb, 0);
+  R.kmeta[2] = __builtin_amdgcn_raw_buffer_load_b16(rs.kz, 2 * lane, kb, 0);
+  R.kmeta[3] = __builtin_amdgcn_raw_buffer_load_b16(rs.kz, 2 * (lane + kHalf), kb, 0);
+  R.eb = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs.rope, 8 * lane,
+                                                                          (int)(((int64_t)kBK + n) * kD * 4), 0));
+  const int vb = (int)(n * kBK * NG * 2);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int t = kWave * k + lane;
     if constexpr (NG == 2) {
-      R.vs[k] = *reinterpret_cast<const uint32_t*>(c.v_scale + m0 + 2 * t);
-      R.vz[k] = *reinterpret_cast<const uint32_t*>(c.v_zero + m0 + 2 * t);
+      R.vs[k] = __builtin_amdgcn_raw_buffer_load_b32(rs.vs, 4 * t, vb, 0);
+      R.vz[k] = __builtin_amdgcn_raw_buffer_load_b32(rs.vz, 4 * t, vb, 0);
     } else {
-      R.vs[k] = c.v_scale[m0 + t];
-      R.vz[k] = c.v_zero[m0 + t];
+      R.vs[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.vs, 2 * t, vb, 0);
+      R.vz[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.vz, 2 * t, vb, 0);
     }
   }
 }
@@ -193,22 +205,21 @@ struct CState {
   float m;        // running max (base 2)
   float l;        // partial sum of p over the lane's tokens
   float z[2];     // partial sum of p * zero over the lane's tokens, per group
-  int e;          // o is held at scale 2^e
+  int e;          // o is held at scale 2^(e - 18) (4-bit) or 2^(e - 16) (2-bit): weights at 2^e
   f4 o[8];        // O^T tiles 4 h + c: element v = channel 64 h + 16 g + 4 v + c of row m
 };
 
 template <int VB, int NG>
-__device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __restrict__ wl, const CLds& L,
+__device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CState& st, float* __restrict__ wl,
+                                            const CLds& L,
                                             const float* __restrict__ table, const float* __restrict__ wq,
                                             int eq, int lane, const kvq_cache& c, int64_t bh, int64_t n,
-                                            int64_t nn, bool more, int64_t vis_row, bool masked) {
+                                            int64_t nn, bool more, int64_t vis_row, bool masked, float neg1) {
   const int m = lane & 15, g = lane >> 4;
   float* Meta = wl + L.meta;
   float* EB = wl + L.eb;
   float* VS = wl + L.vs;
   float* VZ = wl + L.vz;
-  const uint8_t* knext = ck_block<VB>(c, bh, nn);
-  const uint32_t* vnext = cv_block<VB>(c, bh, nn);
 
   // ---- block constants into LDS: key scale/zero at 2^ek (the block's largest rotated
   // key below 2^15), the block rotation, the value metadata in slot order
@@ -239,13 +250,22 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
     }
     vsmax = wave_max_uniform(vmx);
   }
-  if (more) cload_meta<VB, NG>(R, c, bh, nn, lane);
+  if (more) cload_meta<VB, NG>(R, rs, nn, lane);
   wave_lds_sync();
 
   // ---- scores: S[tau] = S^T rows 4 g + v of tile tau, column m (the lane's row)
   f4 S[8];
 #pragma unroll
   for (int tau = 0; tau < 8; ++tau) S[tau] = f4{0.f, 0.f, 0.f, 0.f};
+  // rotary table row of the lane's token, 16-float chunks swapped on rows 16..31 mod 32
+  // (tsw): the 16 tokens a wave reads at once then hit 16 different 4-bank groups
+  const int tsw = ((m >> 3) & 1) << 4;
+  float4 t01, t23;
+  {
+    const float* tr = table + tok_of<VB>(0, m >> 2, m & 3) * kTP;
+    t01 = *reinterpret_cast<const float4*>(tr + ((32 * g) ^ tsw));
+    t23 = *reinterpret_cast<const float4*>(tr + ((32 * g + 4) ^ tsw));
+  }
 #pragma unroll
   for (int kap = 0; kap < 4; ++kap) {
     const int p0 = 16 * g + 4 * kap;  // the chunk's first pair for this lane
@@ -263,7 +283,7 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
         const float wr = qr[u] * ec[u] - qi[u] * es[u];
         const float wi = qr[u] * es[u] + qi[u] * ec[u];
         uint32_t hi, lo;
-        split2(wr, -wi, hi, lo);
+        split2(wr, -wi, hi, lo, neg1);
         Bh[u] = hi;
         Bl[u] = lo;
       }
@@ -273,6 +293,14 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
     for (int u = 0; u < 4; ++u) M[u] = *reinterpret_cast<const float4*>(Meta + 4 * (p0 + u));
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau) {
+      // the next iteration's cos/sin, read ahead of this one's arithmetic
+      float4 tn01 = t01, tn23 = t23;
+      if (tau < 7 || kap < 3) {
+        const int tn = tau < 7 ? tau + 1 : 0, pn = tau < 7 ? p0 : p0 + 4;
+        const float* tr = table + tok_of<VB>(tn, m >> 2, m & 3) * kTP;
+        tn01 = *reinterpret_cast<const float4*>(tr + ((2 * pn) ^ tsw));
+        tn23 = *reinterpret_cast<const float4*>(tr + ((2 * pn + 4) ^ tsw));
+      }
       const uint32_t x = kap == 0 ? R.k[tau].x : kap == 1 ? R.k[tau].y : kap == 2 ? R.k[tau].z : R.k[tau].w;
       // nibbles masked into bits 0-3 / 4-7 of a 16-bit half are exact fp16 subnormals
       // (code * 2^-24, code * 2^-20), read in place by the dequantizing FMAs
@@ -281,9 +309,6 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
       const h2t a13 = __builtin_bit_cast(h2t, t8 & 0x000F000Fu), b13 = __builtin_bit_cast(h2t, t8 & 0x00F000F0u);
       const float ca[4] = {(float)a02.x, (float)a13.x, (float)a02.y, (float)a13.y};
       const float cb[4] = {(float)b02.x, (float)b13.x, (float)b02.y, (float)b13.y};
-      const int j = tok_of<VB>(tau, m >> 2, m & 3);
-      const float4 t01 = *reinterpret_cast<const float4*>(table + j * kTP + 2 * p0);
-      const float4 t23 = *reinterpret_cast<const float4*>(table + j * kTP + 2 * p0 + 4);
       const float cs[4] = {t01.x, t01.z, t23.x, t23.z}, sn[4] = {t01.y, t01.w, t23.y, t23.w};
       u4v Ah, Al;
 #pragma unroll
@@ -293,31 +318,38 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
         const float X = __builtin_fmaf(ka, cs[u], -(kb * sn[u]));
         const float Y = __builtin_fmaf(ka, sn[u], kb * cs[u]);
         uint32_t hi, lo;
-        split2(X, Y, hi, lo);
+        split2(X, Y, hi, lo, neg1);
         Ah[u] = hi;
         Al[u] = lo;
       }
       S[tau] = mfma16(Ah, Bh, S[tau]);
       S[tau] = mfma16(Ah, Bl, S[tau]);
       S[tau] = mfma16(Al, Bh, S[tau]);
-      if (kap == 3 && more) cload_k<VB>(R, tau, knext, lane);
+      if (kap == 3 && more) cload_k<VB>(R, tau, rs, nn, lane);
+      t01 = tn01;
+      t23 = tn23;
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- online softmax of row m (base 2; the query weights carry log2(e) / sqrt(D))
   const float unscale = __builtin_amdgcn_ldexpf(1.0f, -(ek + eq));
+#pragma unroll
+  for (int tau = 0; tau < 8; ++tau) S[tau] *= unscale;
+  if (masked) {  // the block reaches past the view of some row: hide the tokens it does not see
+    const int64_t seen64 = vis_row - n * kBK;
+    const int seen = seen64 < 0 ? 0 : (seen64 > kBK ? kBK : (int)seen64);
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (tok_of<VB>(tau, g, v) >= seen) S[tau][v] = -__builtin_inff();
+  }
   float mloc = -__builtin_inff();
 #pragma unroll
-  for (int tau = 0; tau < 8; ++tau) {
+  for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float s = S[tau][v] * unscale;
-      if (masked && n * kBK + tok_of<VB>(tau, g, v) >= vis_row) s = -__builtin_inff();
-      S[tau][v] = s;
-      mloc = fmaxf(mloc, s);
-    }
-  }
+    for (int v = 0; v < 4; ++v) mloc = fmaxf(mloc, S[tau][v]);
   // the row's 128 tokens sit in lanes m, m + 16, m + 32, m + 48
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
@@ -362,7 +394,7 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
         const float p0 = S[2 * kp][v], p1 = S[2 * kp + 1][v];
         zs = __builtin_fmaf(p0, z0[v], __builtin_fmaf(p1, z1[v], zs));
         uint32_t hi, lo;
-        split2(__builtin_amdgcn_ldexpf(p0 * s0[v], E), __builtin_amdgcn_ldexpf(p1 * s1[v], E), hi, lo);
+        split2(__builtin_amdgcn_ldexpf(p0 * s0[v], E), __builtin_amdgcn_ldexpf(p1 * s1[v], E), hi, lo, neg1);
         Wh[grp][v] = hi;
         Wl[grp][v] = lo;
       }
@@ -375,21 +407,26 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
       for (int cc = 0; cc < 4; ++cc) {
         const uint32_t w = cc == 0 ? R.v[kp][h].x : cc == 1 ? R.v[kp][h].y : cc == 2 ? R.v[kp][h].z : R.v[kp][h].w;
         // dword k holds the codes of the tokens of output elements (tile 2 kp, v = k) and
-        // (tile 2 kp + 1, v = k) as fp16 integers: 1024 + c built in the mantissa, then
-        // 1024 subtracted (exact)
+        // (tile 2 kp + 1, v = k), moved into the top bits of the two halves' mantissas:
+        // exact fp16 subnormals code * 2^-18 (4-bit, bits 6-9) or code * 2^-16 (2-bit,
+        // bits 8-9).  The matrix cores keep fp16 subnormal inputs, but sum products at the
+        // precision of the smallest normal exponent: codes in the low mantissa bits would
+        // lose up to 9 bits there, at the top at most 3.
         u4v A;
+        if constexpr (VB == 4) {
+          A[0] = (w << 6) & 0x03C003C0u;  // nibbles 0, 4
+          A[1] = (w << 2) & 0x03C003C0u;  // nibbles 1, 5
+          A[2] = (w >> 2) & 0x03C003C0u;  // nibbles 2, 6
+          A[3] = (w >> 6) & 0x03C003C0u;  // nibbles 3, 7
+        } else {
+          const uint32_t ws = w >> (8 * (g & 1));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int sh = VB == 4 ? 4 * k : 2 * k + 8 * (g & 1);
-          const uint32_t mask = VB == 4 ? 0x000F000Fu : 0x00030003u;
-          h2t hv = __builtin_bit_cast(h2t, ((w >> sh) & mask) | 0x64006400u);
-          hv = hv - h2t{(_Float16)1024.0f, (_Float16)1024.0f};
-          A[k] = __builtin_bit_cast(uint32_t, hv);
+          for (int k = 0; k < 4; ++k) A[k] = (ws << (8 - 2 * k)) & 0x03000300u;  // fields k, k + 8
         }
         st.o[4 * h + cc] = mfma16(A, Wh[grp], st.o[4 * h + cc]);
         st.o[4 * h + cc] = mfma16(A, Wl[grp], st.o[4 * h + cc]);
       }
-      if (more) cload_v<VB>(R, kp, h, vnext, lane);
+      if (more) cload_v<VB>(R, kp, h, rs, nn, lane);
     }
   }
   if (NG == 1) st.z[1] = 0.0f;
@@ -399,7 +436,7 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, CState& st, float* __r
 template <int VB, int NG>
 __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                               RowSpec rs, float* __restrict__ ws, int S,
-                                                              int ntiles, int64_t nwork) {
+                                                              int ntiles, int64_t nwork, float neg1) {
   constexpr int kNT = kCW * 64;
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H, R = gq * rs.nq;
@@ -415,7 +452,7 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
   float* wl = lds + kBK * kTP + kRows * kWQP + kRows + wave * L.total;
   for (int idx = threadIdx.x; idx < kBK * kHalf; idx += kNT) {
     const int j = idx / kHalf, i = idx % kHalf;
-    *reinterpret_cast<float2*>(table + j * kTP + 2 * i) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
+    *reinterpret_cast<float2*>(table + j * kTP + ((2 * i) ^ (j & 16))) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
   }
 
   const int nsg = (S + kCW - 1) / kCW;  // split groups per unit
@@ -475,21 +512,21 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
 #pragma unroll
       for (int t = 0; t < 8; ++t) st.o[t] = f4{0.f, 0.f, 0.f, 0.f};
       CRegs<VB> Rg;
+      const CRsrc rsr = head_rsrc<VB, NG>(c, bh);
       if (sp < nlimit) {
-        cload_meta<VB, NG>(Rg, c, bh, sp, lane);
-        const uint8_t* kb0 = ck_block<VB>(c, bh, sp);
-        const uint32_t* vb0 = cv_block<VB>(c, bh, sp);
+        cload_meta<VB, NG>(Rg, rsr, sp, lane);
 #pragma unroll
-        for (int tau = 0; tau < 8; ++tau) cload_k<VB>(Rg, tau, kb0, lane);
+        for (int tau = 0; tau < 8; ++tau) cload_k<VB>(Rg, tau, rsr, sp, lane);
 #pragma unroll
         for (int kp = 0; kp < 4; ++kp)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) cload_v<VB>(Rg, kp, hh, vb0, lane);
+          for (int hh = 0; hh < 2; ++hh) cload_v<VB>(Rg, kp, hh, rsr, sp, lane);
       }
       for (int64_t n = sp; n < nlimit; n += S) {
         const bool more = n + S < nlimit;
         const bool masked = (n + 1) * kBK > vmin;
-        chunk_block<VB, NG>(Rg, st, wl, L, table, wq, eq, lane, c, bh, n, more ? n + S : n, more, vis_row, masked);
+        chunk_block<VB, NG>(Rg, rsr, st, wl, L, table, wq, eq, lane, c, bh, n, more ? n + S : n, more, vis_row,
+                            masked, neg1);
       }
       // ---- partial of each row: (m, l, o + z) with l, z summed over the row's 4 lanes
       float l = st.l;
@@ -509,7 +546,8 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
           dst[0] = st.m;
           dst[1] = l;
         }
-        const float us = __builtin_amdgcn_ldexpf(1.0f, -st.e);
+        constexpr int kCodeExp = VB == 4 ? 18 : 16;  // codes enter the value products at 2^-kCodeExp
+        const float us = __builtin_amdgcn_ldexpf(1.0f, kCodeExp - st.e);  // o is at 2^(e - kCodeExp)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const float zz = NG == 2 ? z[hh] : z[0];
@@ -537,7 +575,7 @@ hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float
   const int64_t nwork = (int64_t)c.cfg.batch * c.cfg.kv_heads * ntiles * ((S + kCW - 1) / kCW);
   const int64_t grid = nwork < cus ? nwork : cus;
   hipLaunchKernelGGL((chunk_mfma_kernel<VB, NG>), dim3((unsigned)grid), dim3(kCW * 64), bytes, s, c, q, rs, ws, S,
-                     ntiles, nwork);
+                     ntiles, nwork, -1.0f);
   return hipGetLastError();
 }
 
