@@ -85,9 +85,9 @@ def source_hash(names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind: str, workload: str, src_hash: str):
+def measured_traffic(kind: str, workload: str, src_hash: str, nq: int | None = None):
     """HBM bytes per call from the committed counter summary, if it was taken on this
-    workload and on the current kernel sources; otherwise None."""
+    workload (and chunk size) and on the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         recs = json.load(open(path))["records"]
@@ -95,7 +95,7 @@ def measured_traffic(kind: str, workload: str, src_hash: str):
         return None
     for rec in recs:
         if (rec.get("kind") == kind and rec.get("workload") == workload
-                and rec.get("source_hash") == src_hash):
+                and rec.get("source_hash") == src_hash and rec.get("nq") == nq):
             return rec.get("bytes_per_launch")
     return None
 
@@ -329,13 +329,15 @@ def main():
         c_tflops = cflops / (ch_ms.mean() * 1e-3) / 1e12
         log("chunk   %.1f us  nq %d  %.1f GB/s (%.1f%% of 8 TB/s)  %.1f TFLOP/s"
             % (ch_ms.mean() * 1e3, nq, c_gbps, c_gbps / 80, c_tflops))
+        ch_hash = source_hash(["chunk_mfma.hip", "decode.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h"])
         rec["chunk"] = {"nq": nq, "q_pos": T - nq, "splits": args.chunk_splits or "auto",
                         "us": round(float(ch_ms.mean()) * 1e3, 2),
                         "GBps": round(c_gbps, 2), "frac_hbm_peak": round(c_gbps / HBM_PEAK_GBPS, 4),
                         "TFLOPs": round(c_tflops, 2), "algorithmic_bytes": int(cbytes),
                         "algorithmic_flops": cflops,
                         "query_tokens_per_s": round(B * nq / (ch_ms.mean() * 1e-3), 1),
-                        "kernel": "chunk (split + finish launches)"}
+                        "kernel": "chunk (split + finish launches)",
+                        "traffic": measured_traffic("chunk", cfg["workload"], ch_hash, nq)}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds)
