@@ -1,6 +1,6 @@
 // chunk_mfma.hip -- causal attention of a chunk of query tokens over the packed cache,
 // on the matrix cores of gfx950: uniform 4-bit keys, 2/4-bit values, head_dim 128,
-// 128-token blocks, value groups of 64 or 128, no sparse outliers.
+// 128-token blocks, value groups of 64 or 128, 0 to 2 sparse outliers per vector.
 //
 // Pages cited (title, address):
 //   [KVC3] "【LLM量化技术介绍-3】KV Cache量化技术介绍", developer.horizon.auto/blog/13163
@@ -43,6 +43,15 @@
 // with no exchange between lanes, and the lane's A operand is the codes of channels
 // 64 h + 4 m + c (c < 4) from one 16-byte load.
 //
+// Sparse outliers ([KVC3] "Per-Vector Dense-and-Sparse Quantization": code 0 is stored
+// at an outlier, its exact fp16 value in the CSR):
+//  * keys: per (token, entry) one lane forms the rotated difference
+//    D = (x - zero) e^{i f_i j} e^{i f_i n Bk} (the block rotation moved off the query);
+//    every row then adds Re(Wq D) to its score, Wq read from LDS: 2 FMAs per term;
+//  * values: p * (x - zero) per (row, token, entry), fixed point with one shift per
+//    block (from the block's largest |x - zero|), LDS integer adds into a per-wave
+//    [row][channel] array, merged into the output tiles after the block.
+//
 // Work: a workgroup takes kCW consecutive splits of a unit (b, kv-head, row tile), one
 // per wave (split s takes blocks s, s + S, ... below the tile's last visible block), so
 // its waves share the unit's query weights and stream neighbouring blocks.  The
@@ -56,7 +65,11 @@ namespace {
 
 using namespace dcm;
 
-constexpr int kCW = 8;                      // waves per workgroup
+// waves per workgroup: 8 (two per SIMD, 256 registers each) without outliers; 4 (one per
+// SIMD, 512 registers) with them, whose per-wave LDS (difference and correction arrays)
+// and registers do not fit eight
+template <int KO>
+constexpr int cw_of() { return KO ? 4 : 8; }
 constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;                 // floats per rotary-table row
 constexpr int kRows = 16;                   // rows per tile
@@ -111,21 +124,24 @@ __host__ __device__ inline int slot_of(int t) {
 
 // Per-wave LDS area, in floats.
 struct CLds {
-  int meta, eb, vs, vz, total;
+  int meta, eb, vs, vz, de, vcs, vc, total;
 };
-__host__ __device__ inline CLds chunk_lds(int ng) {
+__host__ __device__ inline CLds chunk_lds(int ng, int ko) {
   CLds m;
   int o = 0;
   m.meta = o; o += 4 * kHalf;   // per pair: scale_a 2^(24+ek), zero_a 2^ek, scale_b 2^(20+ek), zero_b 2^ek
   m.eb = o; o += 2 * kHalf;     // per pair: cos/sin(n Bk f_i)
   m.vs = o; o += ng * kBK;      // value scales, [group][slot]
   m.vz = o; o += ng * kBK;      // value zero-points, [group][slot]
+  m.de = o; o += ko * kBK * 4;  // key outliers: (D_x, D_y, pair, -) per (token, entry)
+  m.vcs = o; o += ko ? 2 * kBK : 0;        // value outliers: (columns, values) per token
+  m.vc = o; o += ko ? kRows * kD : 0;      // value corrections [row][channel], fixed point
   m.total = o;
   return m;
 }
 // Workgroup LDS, in floats: rotary table, query weights, per-row exponents, wave areas.
-__host__ __device__ inline int chunk_lds_total(int ng) {
-  return kBK * kTP + kRows * kWQP + kRows + kCW * chunk_lds(ng).total;
+__host__ __device__ inline int chunk_lds_total(int ng, int ko, int cw) {
+  return kBK * kTP + kRows * kWQP + kRows + cw * chunk_lds(ng, ko).total;
 }
 
 template <int VB>
@@ -136,6 +152,7 @@ struct CRegs {
   uint16_t kmeta[4]; // lane i: scale[i], scale[i + 64], zero[i], zero[i + 64]
   float2 eb;         // lane i: cos/sin(n Bk f_i)
   uint32_t vs[2], vz[2];  // value scale/zero of tokens lane, 64 + lane (both groups)
+  uint32_t kc[2], kv[2], vc[2], vv[2];  // outliers of tokens lane, 64 + lane: columns (byte e), values (half e)
 };
 
 // Buffer resources of one (b, kv-head): the head's slice of each buffer, with its exact
@@ -144,12 +161,12 @@ struct CRegs {
 // offset, so block addresses cost no vector registers.
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 family: raw (untyped) buffer access
 struct CRsrc {
-  __amdgpu_buffer_rsrc_t k, v, ks, kz, vs, vz, rope;
+  __amdgpu_buffer_rsrc_t k, v, ks, kz, vs, vz, rope, kcol, kval, vcol, vval;
 };
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRsrcWord3);
 }
-template <int VB, int NG>
+template <int VB, int NG, int KO>
 __device__ __forceinline__ CRsrc head_rsrc(const kvq_cache& c, int64_t bh) {
   const int64_t T = c.cfg.capacity;
   CRsrc r;
@@ -160,6 +177,12 @@ __device__ __forceinline__ CRsrc head_rsrc(const kvq_cache& c, int64_t bh) {
   r.vs = rsrc(c.v_scale + bh * T * NG, T * NG * 2);
   r.vz = rsrc(c.v_zero + bh * T * NG, T * NG * 2);
   r.rope = rsrc(c.rope, ((int64_t)kBK + T / kBK) * kD * 4);
+  if constexpr (KO > 0) {
+    r.kcol = rsrc(c.k_col + bh * T * KO, T * KO);
+    r.kval = rsrc(c.k_val + bh * T * KO, T * KO * 2);
+    r.vcol = rsrc(c.v_col + bh * T * KO, T * KO);
+    r.vval = rsrc(c.v_val + bh * T * KO, T * KO * 2);
+  }
   return r;
 }
 
@@ -177,7 +200,7 @@ __device__ __forceinline__ void cload_v(CRegs<VB>& R, int kp, int h, const CRsrc
   R.v[kp][h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                              rs.v, (word * kD + 64 * h + 4 * m) * 4, (int)(n * kBK * kD * VB / 8), 0));
 }
-template <int VB, int NG>
+template <int VB, int NG, int KO>
 __device__ __forceinline__ void cload_meta(CRegs<VB>& R, const CRsrc& rs, int64_t n, int lane) {
   const int kb = (int)(n * kD * 2);
   R.kmeta[0] = __builtin_amdgcn_raw_buffer_load_b16(rs.ks, 2 * lane, kb, 0);
@@ -198,6 +221,24 @@ __device__ __forceinline__ void cload_meta(CRegs<VB>& R, const CRsrc& rs, int64_
       R.vz[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.vz, 2 * t, vb, 0);
     }
   }
+  if constexpr (KO > 0) {
+    const int cb = (int)(n * kBK * KO);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = kWave * k + lane;
+      if constexpr (KO == 2) {
+        R.kc[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.kcol, 2 * t, cb, 0);
+        R.vc[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.vcol, 2 * t, cb, 0);
+        R.kv[k] = __builtin_amdgcn_raw_buffer_load_b32(rs.kval, 4 * t, 2 * cb, 0);
+        R.vv[k] = __builtin_amdgcn_raw_buffer_load_b32(rs.vval, 4 * t, 2 * cb, 0);
+      } else {
+        R.kc[k] = __builtin_amdgcn_raw_buffer_load_b8(rs.kcol, t, cb, 0);
+        R.vc[k] = __builtin_amdgcn_raw_buffer_load_b8(rs.vcol, t, cb, 0);
+        R.kv[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.kval, 2 * t, 2 * cb, 0);
+        R.vv[k] = __builtin_amdgcn_raw_buffer_load_b16(rs.vval, 2 * t, 2 * cb, 0);
+      }
+    }
+  }
 }
 
 // Running state of the lane's row m over one split.
@@ -209,7 +250,7 @@ struct CState {
   f4 o[8];        // O^T tiles 4 h + c: element v = channel 64 h + 16 g + 4 v + c of row m
 };
 
-template <int VB, int NG>
+template <int VB, int NG, int KO>
 __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CState& st, float* __restrict__ wl,
                                             const CLds& L,
                                             const float* __restrict__ table, const float* __restrict__ wq,
@@ -250,8 +291,55 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     }
     vsmax = wave_max_uniform(vmx);
   }
-  if (more) cload_meta<VB, NG>(R, rs, nn, lane);
+  // value outliers of the lane's two tokens: staged per token for the lanes that hold
+  // their probabilities, and the block's largest |x - zero| for the fixed-point shift
+  int shv = 0;
+  if constexpr (KO > 0) {
+    uint32_t* VCS = reinterpret_cast<uint32_t*>(wl + L.vcs);
+    float dmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = kWave * k + lane;
+      *reinterpret_cast<uint2*>(VCS + 2 * t) = make_uint2(R.vc[k], R.vv[k]);
+#pragma unroll
+      for (int e = 0; e < KO; ++e) {
+        const int col = (int)((R.vc[k] >> (8 * e)) & 0xffu);
+        const int grp = NG == 2 ? col >> 6 : 0;
+        const float z = h2f((uint16_t)(R.vz[k] >> (16 * grp)));
+        dmax = fmaxf(dmax, fabsf(h2f((uint16_t)(R.vv[k] >> (16 * e))) - z));
+      }
+    }
+    // a channel sums at most 128 terms |p (x - z)| <= dmax < 2^ed: each term below 2^23
+    // after the shift, every channel sum below 2^30
+    shv = 23 - __builtin_amdgcn_frexp_expf(wave_max_uniform(dmax));
+  }
+  const uint32_t kcn[2] = {R.kc[0], R.kc[1]}, kvn[2] = {R.kv[0], R.kv[1]};  // this block's key outliers
+  if (more) cload_meta<VB, NG, KO>(R, rs, nn, lane);
   wave_lds_sync();
+
+  // ---- key outliers: D = (x - zero) e^{i f_i (n Bk + j)} per (token, entry), in the keys'
+  // scale 2^ek; the row's score gains Re(Wq D) (2 FMAs per term after the score MFMAs)
+  if constexpr (KO > 0) {
+    float* DE = wl + L.de;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = kWave * k + lane;
+#pragma unroll
+      for (int e = 0; e < KO; ++e) {
+        const int col = (int)((kcn[k] >> (8 * e)) & 0xffu);
+        const int i = col & (kHalf - 1);
+        const bool isb = col >= kHalf;
+        const float4 M = *reinterpret_cast<const float4*>(Meta + 4 * i);
+        const float d = __builtin_amdgcn_ldexpf(h2f((uint16_t)(kvn[k] >> (16 * e))), ek) - (isb ? M.w : M.y);
+        const float2 cssn = *reinterpret_cast<const float2*>(table + t * kTP + ((2 * i) ^ (t & 16)));
+        const float2 eb = *reinterpret_cast<const float2*>(EB + 2 * i);
+        const float dx = isb ? -d * cssn.y : d * cssn.x, dy = isb ? d * cssn.x : d * cssn.y;
+        *reinterpret_cast<float4*>(DE + 4 * (KO * t + e)) =
+            make_float4(eb.x * dx - eb.y * dy, eb.y * dx + eb.x * dy, __builtin_bit_cast(float, i), 0.0f);
+      }
+    }
+    wave_lds_sync();
+  }
 
   // ---- scores: S[tau] = S^T rows 4 g + v of tile tau, column m (the lane's row)
   f4 S[8];
@@ -332,6 +420,20 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     }
   }
 
+  if constexpr (KO > 0) {
+    const float* DE = wl + L.de;
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < KO; ++e) {
+          const float4 d = *reinterpret_cast<const float4*>(DE + 4 * (KO * tok_of<VB>(tau, g, v) + e));
+          const float2 w = *reinterpret_cast<const float2*>(wq + m * kWQP + 2 * __builtin_bit_cast(int, d.z));
+          S[tau][v] = __builtin_fmaf(w.x, d.x, __builtin_fmaf(-w.y, d.y, S[tau][v]));
+        }
+  }
+
   // ---- online softmax of row m (base 2; the query weights carry log2(e) / sqrt(D))
   const float unscale = __builtin_amdgcn_ldexpf(1.0f, -(ek + eq));
 #pragma unroll
@@ -375,6 +477,28 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
   st.e = E;
 #pragma unroll
   for (int t = 0; t < 8; ++t) st.o[t] *= ao;
+
+  // ---- value outliers: p (x - zero) into the [row][channel] array (fixed point at 2^shv)
+  if constexpr (KO > 0) {
+    const uint32_t* VCS = reinterpret_cast<const uint32_t*>(wl + L.vcs);
+    int* VC = reinterpret_cast<int*>(wl + L.vc);
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = tok_of<VB>(tau, g, v);
+        const uint2 cv = *reinterpret_cast<const uint2*>(VCS + 2 * t);
+        const float ps = __builtin_amdgcn_ldexpf(S[tau][v], shv);
+#pragma unroll
+        for (int e = 0; e < KO; ++e) {
+          const int col = (int)((cv.x >> (8 * e)) & 0xffu);
+          const int grp = NG == 2 ? col >> 6 : 0;
+          const float z = VZ[grp * kBK + 16 * tau + 4 * g + v];
+          const float term = ps * (h2f((uint16_t)(cv.y >> (16 * e))) - z);
+          atomicAdd(VC + m * kD + col, (int)__builtin_rintf(term));
+        }
+      }
+  }
 
   // ---- values: O^T[channel][row] += codes x weights, per 32-token chunk kp
 #pragma unroll
@@ -430,13 +554,32 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     }
   }
   if (NG == 1) st.z[1] = 0.0f;
+  if constexpr (KO > 0) {  // this block's value-outlier sums into the output tiles, then cleared
+    wave_lds_sync();
+    constexpr int kCodeExp = VB == 4 ? 18 : 16;
+    int* VC = reinterpret_cast<int*>(wl + L.vc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        int4* pc = reinterpret_cast<int4*>(VC + m * kD + 64 * h + 16 * g + 4 * v);
+        const int4 x = *pc;
+        const int sc = E - kCodeExp - shv;
+        st.o[4 * h][v] += __builtin_amdgcn_ldexpf((float)x.x, sc);
+        st.o[4 * h + 1][v] += __builtin_amdgcn_ldexpf((float)x.y, sc);
+        st.o[4 * h + 2][v] += __builtin_amdgcn_ldexpf((float)x.z, sc);
+        st.o[4 * h + 3][v] += __builtin_amdgcn_ldexpf((float)x.w, sc);
+        *pc = make_int4(0, 0, 0, 0);
+      }
+  }
   wave_lds_sync();
 }
 
-template <int VB, int NG>
-__global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+template <int VB, int NG, int KO>
+__global__ __launch_bounds__(cw_of<KO>() * 64) void chunk_mfma_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                               RowSpec rs, float* __restrict__ ws, int S,
                                                               int ntiles, int64_t nwork, float neg1) {
+  constexpr int kCW = cw_of<KO>();
   constexpr int kNT = kCW * 64;
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H, R = gq * rs.nq;
@@ -448,8 +591,10 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
   float* table = lds;
   float* wq = lds + kBK * kTP;  // [row][pair] (re, im) at 2^eq_row
   int* eqs = reinterpret_cast<int*>(wq + kRows * kWQP);
-  const CLds L = chunk_lds(NG);
+  const CLds L = chunk_lds(NG, KO);
   float* wl = lds + kBK * kTP + kRows * kWQP + kRows + wave * L.total;
+  if (KO > 0)
+    for (int k = lane; k < kRows * kD; k += kWave) reinterpret_cast<int*>(wl + L.vc)[k] = 0;
   for (int idx = threadIdx.x; idx < kBK * kHalf; idx += kNT) {
     const int j = idx / kHalf, i = idx % kHalf;
     *reinterpret_cast<float2*>(table + j * kTP + ((2 * i) ^ (j & 16))) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
@@ -512,9 +657,9 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
 #pragma unroll
       for (int t = 0; t < 8; ++t) st.o[t] = f4{0.f, 0.f, 0.f, 0.f};
       CRegs<VB> Rg;
-      const CRsrc rsr = head_rsrc<VB, NG>(c, bh);
+      const CRsrc rsr = head_rsrc<VB, NG, KO>(c, bh);
       if (sp < nlimit) {
-        cload_meta<VB, NG>(Rg, rsr, sp, lane);
+        cload_meta<VB, NG, KO>(Rg, rsr, sp, lane);
 #pragma unroll
         for (int tau = 0; tau < 8; ++tau) cload_k<VB>(Rg, tau, rsr, sp, lane);
 #pragma unroll
@@ -525,8 +670,8 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
       for (int64_t n = sp; n < nlimit; n += S) {
         const bool more = n + S < nlimit;
         const bool masked = (n + 1) * kBK > vmin;
-        chunk_block<VB, NG>(Rg, rsr, st, wl, L, table, wq, eq, lane, c, bh, n, more ? n + S : n, more, vis_row,
-                            masked, neg1);
+        chunk_block<VB, NG, KO>(Rg, rsr, st, wl, L, table, wq, eq, lane, c, bh, n, more ? n + S : n, more, vis_row,
+                                masked, neg1);
       }
       // ---- partial of each row: (m, l, o + z) with l, z summed over the row's 4 lanes
       float l = st.l;
@@ -562,19 +707,20 @@ __global__ __launch_bounds__(kCW * 64) void chunk_mfma_kernel(kvq_cache c, const
   }
 }
 
-template <int VB, int NG>
+template <int VB, int NG, int KO>
 hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s,
                         int cus) {
-  const size_t bytes = (size_t)chunk_lds_total(NG) * sizeof(float);
+  constexpr int kCW = cw_of<KO>();
+  const size_t bytes = (size_t)chunk_lds_total(NG, KO, kCW) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
-  hipError_t e = hipFuncSetAttribute((const void*)chunk_mfma_kernel<VB, NG>,
+  hipError_t e = hipFuncSetAttribute((const void*)chunk_mfma_kernel<VB, NG, KO>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int R = c.cfg.q_heads / c.cfg.kv_heads * rs.nq;
   const int ntiles = (R + kRows - 1) / kRows;
   const int64_t nwork = (int64_t)c.cfg.batch * c.cfg.kv_heads * ntiles * ((S + kCW - 1) / kCW);
   const int64_t grid = nwork < cus ? nwork : cus;
-  hipLaunchKernelGGL((chunk_mfma_kernel<VB, NG>), dim3((unsigned)grid), dim3(kCW * 64), bytes, s, c, q, rs, ws, S,
+  hipLaunchKernelGGL((chunk_mfma_kernel<VB, NG, KO>), dim3((unsigned)grid), dim3(kCW * 64), bytes, s, c, q, rs, ws, S,
                      ntiles, nwork, -1.0f);
   return hipGetLastError();
 }
@@ -584,12 +730,23 @@ hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float
 hipError_t launch_chunk_mfma(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s,
                              int cus) {
   const kvq_config& g = c.cfg;
-  const int ng = g.head_dim / g.v_group;
-  if (host_kout(g) != 0 || g.k_mode != 0 || g.k_bits != 4 || g.head_dim != kD || g.k_block != kBK ||
+  const int ng = g.head_dim / g.v_group, ko = host_kout(g);
+  // (at head_dim 128 a whole-percent outlier share gives 0 or at least 2 per vector)
+  if (ko > 2 || g.k_mode != 0 || g.k_bits != 4 || g.head_dim != kD || g.k_block != kBK ||
       (g.v_bits != 4 && g.v_bits != 2) || ng < 1 || ng > 2)
     return hipErrorNotSupported;
-  if (g.v_bits == 4) return ng == 2 ? launch_typed<4, 2>(c, q, rs, ws, S, s, cus) : launch_typed<4, 1>(c, q, rs, ws, S, s, cus);
-  return ng == 2 ? launch_typed<2, 2>(c, q, rs, ws, S, s, cus) : launch_typed<2, 1>(c, q, rs, ws, S, s, cus);
+#define KVQ_CHUNK_NG(vb, ko)                                                                  \
+  return ng == 2 ? launch_typed<vb, 2, ko>(c, q, rs, ws, S, s, cus)                         \
+                 : launch_typed<vb, 1, ko>(c, q, rs, ws, S, s, cus);
+#define KVQ_CHUNK(vb)                                                                         \
+  if (g.v_bits == vb) {                                                                       \
+    if (ko == 2) { KVQ_CHUNK_NG(vb, 2) }                                                      \
+    if (ko == 0) { KVQ_CHUNK_NG(vb, 0) }                                                      \
+  }
+  KVQ_CHUNK(4) KVQ_CHUNK(2)
+#undef KVQ_CHUNK
+#undef KVQ_CHUNK_NG
+  return hipErrorNotSupported;
 }
 
 }  // namespace kvq

@@ -2,13 +2,12 @@
 position q_pos + j seeing the cache tokens t <= q_pos + j) against the CPU oracle's fp64
 chunk attention over the same quantized cache: max abs error <= 2e-3.
 
-Cases cover the matrix-core kernel (uniform 4-bit keys, head_dim 128, 128-token blocks,
-no outliers; one head and four heads per kv head, 2- and 4-bit values, one and two
-value groups) and the generic kernel (outliers, codebook keys, head_dim 64, 64-token
-blocks, clipping); chunks that end at the newest token, that reach back over quantized
-blocks and the fp16 tail, that lie past the end or start at position 0; row tiles of 16
-with a ragged last tile; and several split counts.  The chunk workloads of the
-benchmark are checked at full size on sampled heads.
+Cases cover the matrix-core kernel (uniform 4-bit keys, head_dim 128, 128-token blocks;
+one head and four heads per kv head, 2- and 4-bit values, one and two value groups,
+none or two outliers per vector, clipping) and the generic kernel (codebook keys,
+head_dim 64, 64-token blocks, one outlier per vector); chunks that end at the newest
+token, that reach back over quantized blocks and the fp16 tail, that lie past the end or
+start at position 0; row tiles of 16 with a ragged last tile; and several split counts.
 """
 import numpy as np
 import pytest
@@ -43,14 +42,18 @@ CASES = {
                                         capacity=512), None),
     "mfma_gqa4_v4_g64": (synth.config("c2", batch=1, q_heads=4, kv_heads=1, v_group=64, outlier_pct=0,
                                       inject=False, tokens=6 * 128 + 5, capacity=896), None),
+    "mfma_csr_gqa": (synth.config("c2", batch=1, q_heads=8, kv_heads=2, tokens=3 * 128 + 40,
+                                  capacity=512), None),
+    "mfma_clip_csr": (synth.config("c4", batch=1, q_heads=2, kv_heads=2, tokens=3 * 128 + 57,
+                                   capacity=512), None),
+    "mfma_csr_v2_g64": (synth.config("c2", batch=1, q_heads=4, kv_heads=1, v_bits=2, v_group=64,
+                                     tokens=5 * 128 + 11, capacity=768), [200, 451]),
     # generic kernel
-    "generic_csr_gqa": (synth.config("c2", batch=1, q_heads=8, kv_heads=2, tokens=3 * 128 + 40,
-                                     capacity=512), None),
+    "generic_csr1_d64": (synth.config("c0", batch=2, outlier_pct=1, inject=True, tokens=5 * 64 + 30,
+                                      capacity=384), [64, 286]),
     "generic_lut3": (synth.config("c3", batch=1, q_heads=2, kv_heads=2, tokens=4 * 128 + 3,
                                   capacity=640), None),
     "generic_d64": (synth.config("c0", tokens=293, capacity=320), [37, 256]),
-    "generic_clip_csr": (synth.config("c4", batch=1, q_heads=2, kv_heads=2, tokens=3 * 128 + 57,
-                                      capacity=512), None),
 }
 
 
@@ -94,7 +97,7 @@ def test_chunk_matches_oracle(case):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("case", ["mfma_mha_v4", "mfma_gqa4_v2_g64", "generic_csr_gqa"])
+@pytest.mark.parametrize("case", ["mfma_mha_v4", "mfma_gqa4_v2_g64", "mfma_csr_gqa", "generic_csr1_d64"])
 def test_chunk_split_counts_and_determinism(case):
     cfg, chunks = CASES[case]
     T = cfg["tokens"]
@@ -117,7 +120,7 @@ def test_chunk_split_counts_and_determinism(case):
         assert err <= TOL, S
 
 
-@pytest.mark.parametrize("case", ["mfma_mha_v4", "generic_csr_gqa"])
+@pytest.mark.parametrize("case", ["mfma_mha_v4", "mfma_csr_gqa", "generic_csr1_d64"])
 def test_chunk_of_one_is_the_decode_step(case):
     """nq = 1 at the newest position is single-query decode (both against the oracle,
     and against each other within fp32 rounding)."""
