@@ -74,6 +74,7 @@ constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;                 // floats per rotary-table row
 constexpr int kRows = 16;                   // rows per tile
 constexpr int kWQP = 2 * kHalf + 4;         // floats per row of the query weights
+constexpr int kVCP = kD + 4;                // ints per row of the value-outlier sums (banks)
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -133,9 +134,12 @@ __host__ __device__ inline CLds chunk_lds(int ng, int ko) {
   m.eb = o; o += 2 * kHalf;     // per pair: cos/sin(n Bk f_i)
   m.vs = o; o += ng * kBK;      // value scales, [group][slot]
   m.vz = o; o += ng * kBK;      // value zero-points, [group][slot]
-  m.de = o; o += ko * kBK * 4;  // key outliers: (D_x, D_y, pair, -) per (token, entry)
   m.vcs = o; o += ko ? 2 * kBK : 0;        // value outliers: (columns, values) per token
-  m.vc = o; o += ko ? kRows * kD : 0;      // value corrections [row][channel], fixed point
+  // one area, used in turn: the key-outlier score terms [token][row] (block start to the
+  // scores' correction), then the value-outlier sums [row][channel] in fixed point
+  m.de = o;
+  m.vc = o;
+  o += ko ? (kBK * kRows > kRows * kVCP ? kBK * kRows : kRows * kVCP) : 0;
   m.total = o;
   return m;
 }
@@ -317,13 +321,17 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
   if (more) cload_meta<VB, NG, KO>(R, rs, nn, lane);
   wave_lds_sync();
 
-  // ---- key outliers: D = (x - zero) e^{i f_i (n Bk + j)} per (token, entry), in the keys'
-  // scale 2^ek; the row's score gains Re(Wq D) (2 FMAs per term after the score MFMAs)
+  // ---- key outliers: per (token, entry) the rotated difference D = (x - zero) e^{i f_i
+  // (n Bk + j)} in the keys' scale 2^ek, and its score term Re(Wq D) for all 16 rows,
+  // summed over the token's entries into the [token][row] array (lane: tokens lane and
+  // 64 + lane); the rows add them after the score MFMAs
   if constexpr (KO > 0) {
     float* DE = wl + L.de;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int t = kWave * k + lane;
+      float dx[KO], dy[KO];
+      int ie[KO];
 #pragma unroll
       for (int e = 0; e < KO; ++e) {
         const int col = (int)((kcn[k] >> (8 * e)) & 0xffu);
@@ -333,9 +341,24 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
         const float d = __builtin_amdgcn_ldexpf(h2f((uint16_t)(kvn[k] >> (16 * e))), ek) - (isb ? M.w : M.y);
         const float2 cssn = *reinterpret_cast<const float2*>(table + t * kTP + ((2 * i) ^ (t & 16)));
         const float2 eb = *reinterpret_cast<const float2*>(EB + 2 * i);
-        const float dx = isb ? -d * cssn.y : d * cssn.x, dy = isb ? d * cssn.x : d * cssn.y;
-        *reinterpret_cast<float4*>(DE + 4 * (KO * t + e)) =
-            make_float4(eb.x * dx - eb.y * dy, eb.y * dx + eb.x * dy, __builtin_bit_cast(float, i), 0.0f);
+        const float x = isb ? -d * cssn.y : d * cssn.x, y = isb ? d * cssn.x : d * cssn.y;
+        dx[e] = eb.x * x - eb.y * y;
+        dy[e] = eb.y * x + eb.x * y;
+        ie[e] = i;
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < kRows / 4; ++r4) {
+        float cr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          cr[u] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < KO; ++e) {
+            const float2 w = *reinterpret_cast<const float2*>(wq + (4 * r4 + u) * kWQP + 2 * ie[e]);
+            cr[u] = __builtin_fmaf(w.x, dx[e], __builtin_fmaf(-w.y, dy[e], cr[u]));
+          }
+        }
+        *reinterpret_cast<float4*>(DE + t * kRows + 4 * r4) = make_float4(cr[0], cr[1], cr[2], cr[3]);
       }
     }
     wave_lds_sync();
@@ -420,18 +443,15 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     }
   }
 
-  if constexpr (KO > 0) {
-    const float* DE = wl + L.de;
+  if constexpr (KO > 0) {  // key-outlier terms of the lane's row; the area then holds the value sums
+    float* DE = wl + L.de;
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int e = 0; e < KO; ++e) {
-          const float4 d = *reinterpret_cast<const float4*>(DE + 4 * (KO * tok_of<VB>(tau, g, v) + e));
-          const float2 w = *reinterpret_cast<const float2*>(wq + m * kWQP + 2 * __builtin_bit_cast(int, d.z));
-          S[tau][v] = __builtin_fmaf(w.x, d.x, __builtin_fmaf(-w.y, d.y, S[tau][v]));
-        }
+      for (int v = 0; v < 4; ++v) S[tau][v] += DE[tok_of<VB>(tau, g, v) * kRows + m];
+    wave_lds_sync();
+    for (int k = 4 * lane; k < kRows * kVCP; k += 4 * kWave)
+      *reinterpret_cast<int4*>(DE + k) = make_int4(0, 0, 0, 0);
   }
 
   // ---- online softmax of row m (base 2; the query weights carry log2(e) / sqrt(D))
@@ -495,7 +515,7 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
           const int grp = NG == 2 ? col >> 6 : 0;
           const float z = VZ[grp * kBK + 16 * tau + 4 * g + v];
           const float term = ps * (h2f((uint16_t)(cv.y >> (16 * e))) - z);
-          atomicAdd(VC + m * kD + col, (int)__builtin_rintf(term));
+          atomicAdd(VC + m * kVCP + col, (int)__builtin_rintf(term));
         }
       }
   }
@@ -554,7 +574,7 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     }
   }
   if (NG == 1) st.z[1] = 0.0f;
-  if constexpr (KO > 0) {  // this block's value-outlier sums into the output tiles, then cleared
+  if constexpr (KO > 0) {  // this block's value-outlier sums into the output tiles
     wave_lds_sync();
     constexpr int kCodeExp = VB == 4 ? 18 : 16;
     int* VC = reinterpret_cast<int*>(wl + L.vc);
@@ -562,14 +582,13 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        int4* pc = reinterpret_cast<int4*>(VC + m * kD + 64 * h + 16 * g + 4 * v);
+        int4* pc = reinterpret_cast<int4*>(VC + m * kVCP + 64 * h + 16 * g + 4 * v);
         const int4 x = *pc;
         const int sc = E - kCodeExp - shv;
         st.o[4 * h][v] += __builtin_amdgcn_ldexpf((float)x.x, sc);
         st.o[4 * h + 1][v] += __builtin_amdgcn_ldexpf((float)x.y, sc);
         st.o[4 * h + 2][v] += __builtin_amdgcn_ldexpf((float)x.z, sc);
         st.o[4 * h + 3][v] += __builtin_amdgcn_ldexpf((float)x.w, sc);
-        *pc = make_int4(0, 0, 0, 0);
       }
   }
   wave_lds_sync();
@@ -593,8 +612,6 @@ __global__ __launch_bounds__(cw_of<KO>() * 64) void chunk_mfma_kernel(kvq_cache 
   int* eqs = reinterpret_cast<int*>(wq + kRows * kWQP);
   const CLds L = chunk_lds(NG, KO);
   float* wl = lds + kBK * kTP + kRows * kWQP + kRows + wave * L.total;
-  if (KO > 0)
-    for (int k = lane; k < kRows * kD; k += kWave) reinterpret_cast<int*>(wl + L.vc)[k] = 0;
   for (int idx = threadIdx.x; idx < kBK * kHalf; idx += kNT) {
     const int j = idx / kHalf, i = idx % kHalf;
     *reinterpret_cast<float2*>(table + j * kTP + ((2 * i) ^ (j & 16))) = *reinterpret_cast<const float2*>(c.rope + 2 * idx);
