@@ -490,8 +490,11 @@ __device__ __forceinline__ void chunk_block(CRegs<VB>& R, const CRsrc& rs, CStat
     }
   }
   st.l = __builtin_fmaf(st.l, alpha, lsum);
-  // value weights p * scale at 2^E: the block's largest weight of this row in [2^14, 2^15)
-  const float wbound = pmax * vsmax;
+  // value weights p * scale at 2^E: the block's largest weight of this row in [2^14, 2^15).
+  // pmax counts as at least 2^-24: a block whose weights all lie below 2^-24 of the
+  // running maximum's adds nothing the accumulator can hold, and the cap keeps E from
+  // growing so fast that the rescaled accumulator (o * 2^(E - E_old)) overflows
+  const float wbound = fmaxf(pmax, 0x1p-24f) * vsmax;
   const int E = wbound > 0.0f ? exp_to_2p15(wbound) : st.e;
   const float ao = __builtin_amdgcn_ldexpf(alpha, E - st.e);
   st.e = E;

@@ -153,3 +153,27 @@ def test_chunk_binding_checks():
     with pytest.raises(kvq.KvqError):
         cache.chunk(q, q_pos=-1)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", ["mfma_mha_v4", "mfma_csr_gqa"])
+def test_chunk_one_dominant_token(case):
+    """One early token with a huge key component dominates the softmax of the rows that
+    weigh it positively: every later block's probabilities fall below 2^-100 of it.  The
+    per-block weight scaling must not overflow the accumulator for those rows (and the
+    others, which give that token ~0 weight, must stay exact)."""
+    cfg, chunks = CASES[case]
+    T = cfg["tokens"]
+    k, v = inputs(cfg)
+    k = k.copy()
+    k[:, :, 5, 3] = np.float16(30000.0).view(np.uint16)        # a dense value (c1) or the outlier (c2)
+    lut = _lut(cfg)
+    cache = build_gpu_cache(cfg, k, v, chunks, lut)
+    heads = oracle_heads(cfg, k, v, lut)
+    nq = 16
+    q = synth.gen_q_chunk(cfg, nq)
+    out = cache.chunk(upload(q), q_pos=T - nq).cpu().numpy().astype(np.float64)
+    ref = chunk_ref(cfg, heads, q, T - nq)
+    assert np.isfinite(out).all()
+    err = np.abs(out - ref).max()
+    say("case", case, "dominant token: max abs err", err)
+    assert err <= TOL

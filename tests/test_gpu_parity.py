@@ -284,7 +284,10 @@ def test_full_size_all_heads(name):
     """The workload at its full size, appended as the benchmark appends it (the prefill
     workload: its cached half, then the appended half), decoded in the launch
     configuration the benchmark times; every head's cache compared bitwise with the
-    oracle and every (b, q-head) output within 2e-3 of the oracle's fp64 attention."""
+    oracle and every (b, q-head) output within 2e-3 of the oracle's fp64 attention.
+    The chunk attention the benchmark times with --chunk (16 queries at the newest
+    positions, 4 on the 1M-token cache; automatic splits) is checked on the query heads
+    of the first kv head."""
     import torch
     import oracle
     cfg = synth.config(name)
@@ -307,6 +310,9 @@ def test_full_size_all_heads(name):
         say("  appended tokens", t, "of", T)
     q = synth.gen_q(cfg)
     out = cache.decode(upload(q)).cpu().numpy()
+    nq = 4 if T > 500000 else 16
+    qc = synth.gen_q_chunk(cfg, nq)
+    outc = cache.chunk(upload(qc), q_pos=T - nq).cpu().numpy()
     torch.cuda.synchronize()
     bufs = _host_buffers(cache, cfg)
     ko = oracle.kout(cfg)
@@ -327,6 +333,15 @@ def test_full_size_all_heads(name):
         ref = oracle.decode_many(cfg, hl, ql, T - 1)
         got = np.stack([out[b, h * gq + g] for (b, h) in sel for g in range(gq)]).astype(np.float64)
         worst = max(worst, float(np.abs(got - ref).max()))
+        if i0 == 0:   # chunk attention on the first kv head
+            csel = sel[:1]
+            hlc = [hc for hc in hcs[:1] for _ in range(gq)]
+            qlc = np.stack([qc[b, h * gq + g] for (b, h) in csel for g in range(gq)])
+            refc = oracle.chunk_many(cfg, hlc, qlc, nq, T - nq)
+            gotc = np.stack([outc[b, h * gq + g] for (b, h) in csel for g in range(gq)]).astype(np.float64)
+            errc = float(np.abs(gotc - refc).max())
+            say("  chunk of", nq, "on", len(csel), "kv heads: max abs err", errc)
+            assert errc <= TOL
         say("  heads", i0 + len(sel), "of", len(pairs), "bitwise equal; decode max abs err so far", worst)
         del hcs, hl
     assert worst <= TOL
