@@ -18,6 +18,11 @@ run on); the append's tokens/s is reported beside it, as is a read-streaming pro
 queries per sequence at the newest NQ positions (a prefill chunk or speculative
 verification) over the same cache, reported under "chunk".
 
+``--decode-steps N`` also times token-by-token generation on a second cache holding the
+workload's first T - N tokens: N fused decode steps (kvq_decode_step: the token appended
+and attended in one launch), then the same N tokens as kvq_quantize_append of one token
+followed by kvq_decode_attention; reported per step under "decode_step".
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -168,6 +173,47 @@ def copy_probe():
     log("copy probe: 3 x %d bytes" % n)
 
 
+def time_decode_steps(cfg, k_d, v_d, lut_d, n, dev):
+    """Per-step time of n token-by-token decode steps on a cache of the workload's first
+    T - n tokens: fused (one kvq_decode_step per token) against two calls (append of one
+    token, then decode), each timed over the whole sequence with HIP events."""
+    import torch
+    import quantized_decode_attn_amd as kvq
+    T, B, Hq, D = cfg["tokens"], cfg["batch"], cfg["q_heads"], cfg["head_dim"]
+    T0 = T - n
+    qs = torch.from_numpy(np.ascontiguousarray(synth.gen_q_chunk(cfg, n)).view(np.int16)).to(dev).view(torch.float16)
+    toks_k = [k_d[:, :, t].contiguous() for t in range(T0, T)]
+    toks_v = [v_d[:, :, t].contiguous() for t in range(T0, T)]
+    toks_k1 = [k_d[:, :, t:t + 1].contiguous() for t in range(T0, T)]
+    toks_v1 = [v_d[:, :, t:t + 1].contiguous() for t in range(T0, T)]
+    q1 = [qs[:, :, i].contiguous() for i in range(n)]
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    cache = kvq.Cache(cfg, device=dev, lut=lut_d)
+    cache.workspace(0)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for mode in ("fused", "two_calls", "fused", "two_calls"):   # each twice; the second run is reported
+        cache.desc.length = 0
+        cache.append(k_d[:, :, :T0].contiguous(), v_d[:, :, :T0].contiguous())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            if mode == "fused":
+                cache.step(toks_k[i], toks_v[i], q1[i], out=out)
+            else:
+                cache.append(toks_k1[i], toks_v1[i])
+                cache.decode(q1[i], q_pos=T0 + i, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[mode] = e0.elapsed_time(e1) * 1e3 / n
+    log("decode step  fused %.1f us/token, append + decode %.1f us/token (%d tokens from %d)"
+        % (res["fused"], res["two_calls"], n, T0))
+    return {"tokens": n, "from_length": T0, "fused_us_per_token": round(res["fused"], 2),
+            "append_plus_decode_us_per_token": round(res["two_calls"], 2),
+            "speedup": round(res["two_calls"] / res["fused"], 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +226,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="also time attention of a chunk of this many queries")
     ap.add_argument("--chunk-splits", type=int, default=0)
+    ap.add_argument("--decode-steps", type=int, default=0, help="also time this many token-by-token steps")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -338,6 +385,8 @@ def main():
                         "query_tokens_per_s": round(B * nq / (ch_ms.mean() * 1e-3), 1),
                         "kernel": "chunk (split + finish launches)",
                         "traffic": measured_traffic("chunk", cfg["workload"], ch_hash, nq)}
+    if args.decode_steps:
+        rec["decode_step"] = time_decode_steps(cfg, k_d, v_d, lut_d, args.decode_steps, dev)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds)

@@ -207,6 +207,31 @@ kvq_status kvq_decode_attention(const kvq_cache *cache, const void *q, int64_t q
 kvq_status kvq_decode_attention_noalloc(const kvq_cache *cache, const void *q, int64_t q_pos,
                                         float *out, int32_t num_splits, void *stream);
 
+/* One decode step with its token, fused: append one new token per sequence and attend
+ * with the query at the token's position over the whole cache, the token included:
+ *   the same results as kvq_quantize_append(cache, k_new, v_new, 1) followed by
+ *   kvq_decode_attention(cache, q, length - 1, ...) (up to fp32 rounding).
+ * The pages name per-head launches and the quantize/dequantize round trips as costs of
+ * the quantized cache and fusion as their cure ([TQ] sections 5.1 and 6.3).  The token
+ * never takes a launch of its own: the attention reads it from k_new/v_new and one of
+ * its kernels stores it into the fp16 tail.  When it completes a block, that block is
+ * quantized first (one launch, as by kvq_quantize_append).
+ * num_splits == 0 (the library's choice): a short cache (at most 8 quantized blocks per
+ * sequence) takes ONE launch, one workgroup per (b, kv-head) whose waves split the
+ * cache and merge in LDS, so that launch count, not bandwidth, is what the step costs;
+ * a longer one takes the split kernels of kvq_decode_attention with the library's split
+ * count (two launches).  num_splits > 0: those two launches with that many splits.
+ * ws: device workspace of at least kvq_decode_workspace_bytes(cache, num_splits) bytes
+ * (the same as kvq_decode_attention's; the one-launch path does not touch it).
+ * k_new, v_new: *device* fp16 [batch][kv_heads][head_dim], keys pre-RoPE; q: *device*
+ * fp16 [batch][q_heads][head_dim]; out: *device* fp32 [batch][q_heads][head_dim].
+ * `length` grows by one on the host at enqueue time.  KVQ_ECAPACITY if the cache is
+ * full, KVQ_EWORKSPACE for a workspace that is too small, KVQ_EINVAL for a split count
+ * that is negative or above 4096; on any error the cache is left unchanged. */
+kvq_status kvq_decode_step(kvq_cache *cache, const void *k_new, const void *v_new, const void *q,
+                           float *out, void *ws, size_t ws_bytes, int32_t num_splits,
+                           void *stream);
+
 /* Bytes of device workspace kvq_chunk_attention needs for a chunk of nq queries and
  * `num_splits` splits per (b, kv-head) (0 = the library's choice; at most 4096): one
  * (max, sum, output) partial of head_dim + 2 floats per (b, q-head, query, split),

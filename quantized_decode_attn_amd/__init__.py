@@ -8,7 +8,7 @@ every call raises: there is no fallback.
 The functions carry the names of the C ABI in ``include/kvq.h``
 (``kvq_cache_layout``, ``kvq_cache_init``, ``kvq_quantize_append``,
 ``kvq_decode_workspace_bytes``, ``kvq_decode_attention``, ``kvq_decode_attention_noalloc``,
-``kvq_chunk_workspace_bytes``, ``kvq_chunk_attention``, ``kvq_dequantize``,
+``kvq_chunk_workspace_bytes``, ``kvq_chunk_attention``, ``kvq_decode_step``, ``kvq_dequantize``,
 ``kvq_status_string``); ``Cache`` bundles the buffers of one cache.
 """
 from __future__ import annotations
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4, -5
 EXPORTED = ["kvq_status_string", "kvq_cache_layout", "kvq_cache_init", "kvq_quantize_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
-            "kvq_chunk_workspace_bytes", "kvq_chunk_attention", "kvq_dequantize"]
+            "kvq_chunk_workspace_bytes", "kvq_chunk_attention", "kvq_decode_step", "kvq_dequantize"]
 NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -82,6 +82,8 @@ def lib() -> C.CDLL:
         L.kvq_chunk_workspace_bytes.argtypes = [C.POINTER(KvqCache), i32, i32]
         L.kvq_chunk_attention.restype = i32
         L.kvq_chunk_attention.argtypes = [C.POINTER(KvqCache), vp, i32, i64, vp, vp, C.c_size_t, i32, vp]
+        L.kvq_decode_step.restype = i32
+        L.kvq_decode_step.argtypes = [C.POINTER(KvqCache), vp, vp, vp, vp, vp, C.c_size_t, i32, vp]
         L.kvq_dequantize.restype = i32
         L.kvq_dequantize.argtypes = [C.POINTER(KvqCache), i32, i64, i64, vp, vp]
         _lib = L
@@ -154,6 +156,14 @@ def kvq_chunk_attention(cache: KvqCache, q, nq: int, q_pos: int, out, ws, ws_byt
                                    int(ws_bytes), int(num_splits), _stream(stream))
     if st != KVQ_OK:
         raise KvqError(st, "kvq_chunk_attention")
+
+
+def kvq_decode_step(cache: KvqCache, k_new, v_new, q, out, ws, ws_bytes: int, num_splits: int = 0,
+                    stream=None) -> None:
+    st = lib().kvq_decode_step(C.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(ws), ws_bytes,
+                               num_splits, _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_decode_step")
 
 
 def kvq_dequantize(cache: KvqCache, which: int, t0: int, t1: int, out, stream=None) -> None:
@@ -277,6 +287,22 @@ class Cache:
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 4), dtype=torch.uint8, device=self.device)
         kvq_chunk_attention(self.desc, q, nq, q_pos, out, self._ws, self._ws.numel(), num_splits, stream)
+        return out
+
+    def step(self, k_new, v_new, q, num_splits: int = 0, out=None, stream=None):
+        """One fused decode step: append k_new, v_new (fp16 [B][Hkv][D], keys pre-RoPE) and
+        attend with q (fp16 [B][Hq][D]) at the new token's position (num_splits 0: the
+        library's choice, one launch for a short cache).  Returns fp32 [B][Hq][D]."""
+        import torch
+        B, H, Hq, D = self.cfg["batch"], self.cfg["kv_heads"], self.cfg["q_heads"], self.cfg["head_dim"]
+        _check_tensor(k_new, "k_new", (B, H, D), torch.float16, self.device)
+        _check_tensor(v_new, "v_new", (B, H, D), torch.float16, self.device)
+        _check_tensor(q, "q", (B, Hq, D), torch.float16, self.device)
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        _check_tensor(out, "out", (B, Hq, D), torch.float32, self.device)
+        ws = self.workspace(num_splits)
+        kvq_decode_step(self.desc, k_new, v_new, q, out, ws, ws.numel(), num_splits, stream)
         return out
 
     def dequantize(self, which: int, t0: int = 0, t1: int | None = None, stream=None):

@@ -85,10 +85,25 @@ __device__ __forceinline__ uint32_t get_code(const uint32_t (&w)[KW], int k) {
   return v & ((1u << KB) - 1u);
 }
 
-template <int D, int KB, int KMODE, int VB>
+// The new token of a fused decode step: its keys and values [B][Hkv][D] (fp16, pre-RoPE)
+// stand at tail slot jnew.  Every read of that slot in the step's launches takes the
+// input; one launch also writes it into the tail for the steps that follow.  jnew < 0:
+// no such token (plain decode, or a step whose token completed a block).
+struct StepToken {
+  const uint16_t* k;
+  const uint16_t* v;
+  int jnew;
+};
+
+// STEP = false: split kernel, partials to the workspace.  STEP = true: the one-launch
+// decode step, one workgroup per (b, kv-head) whose kWaves waves take the kWaves splits;
+// the partials are merged in LDS, the output written directly (S must equal kWaves) and
+// the step's token stored into the tail.
+template <int D, int KB, int KMODE, int VB, bool STEP>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
                                                                 const uint16_t* __restrict__ q, RowSpec rs,
-                                                                float* __restrict__ ws, int S, int64_t nitems) {
+                                                                float* __restrict__ ws, int S, int64_t nitems,
+                                                                StepToken nt, float* __restrict__ out) {
   using Sh = Shape<D, KB, KMODE, VB>;
   extern __shared__ float lds[];
   const int Bk = c.cfg.k_block;
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
                 s += col < Sh::HALF ? dlt * (wr * cs - wi * sn) : -dlt * (wi * cs + wr * sn);
               }
             } else {
-              const uint16_t* kr = c.k_tail + (bh * Bk + j) * D;
+              const uint16_t* kr = j == nt.jnew ? nt.k + bh * D : c.k_tail + (bh * Bk + j) * D;
 #pragma unroll
               for (int m = 0; m < Sh::PPL; ++m) {
                 const int i = r * Sh::PPL + m;
@@ -362,7 +377,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
             const float p = Pl[j];
 #pragma unroll
             for (int k = 0; k < Sh::CPL; ++k)
-              acc[k] = __builtin_fmaf(p, h2f(c.v_tail[(bh * Bk + j) * D + lane + k * kWave]), acc[k]);
+              acc[k] = __builtin_fmaf(p, h2f(j == nt.jnew ? nt.v[bh * D + lane + k * kWave]
+                                                               : c.v_tail[(bh * Bk + j) * D + lane + k * kWave]),
+                                      acc[k]);
           }
           if (lane == 0)
             for (int gg = 0; gg < ng; ++gg) st[2 + D + gg] *= alpha;
@@ -378,6 +395,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       }
     }
 
+    if constexpr (STEP) {
+      // the new token into the fp16 tail, for the steps that follow (this launch reads it
+      // from the input)
+      if (wave == 0 && nt.jnew >= 0)
+        for (int k = lane; k < D; k += kWave) {
+          c.k_tail[(bh * Bk + nt.jnew) * D + k] = nt.k[bh * D + k];
+          c.v_tail[(bh * Bk + nt.jnew) * D + k] = nt.v[bh * D + k];
+        }
+      break;  // one item per wave: the workgroup's waves hold the kWaves splits of one unit
+    }
     // ---- write the partial of every row of the set
     for (int g = 0; g < nrows; ++g) {
       const int row = row0 + g;
@@ -392,15 +419,39 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     }
     wave_lds_sync();
   }
+  if constexpr (STEP) {
+    // ---- merge the waves' (m, l, o) of every row in wave order:
+    //   M = max m_w,  out = sum_w o_w 2^(m_w - M) / sum_w l_w 2^(m_w - M)
+    __syncthreads();
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % H), b = (int)(bh / H);
+    const float* st0 = lds + Bk * Sh::TPITCH + L.state;
+    for (int idx = threadIdx.x; idx < R * D; idx += kThreads) {
+      const int g = idx / D, k = idx % D;
+      float M = -__builtin_inff();
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st0[w * L.total + g * (D + 2 + ng)]);
+      float Ls = 0.0f, O = 0.0f;
+      for (int w = 0; w < kWaves; ++w) {
+        const float* st = st0 + w * L.total + g * (D + 2 + ng);
+        const float wt = st[0] == -__builtin_inff() ? 0.0f : exp2f(st[0] - M);  // a wave without blocks: 0
+        Ls = __builtin_fmaf(st[1], wt, Ls);
+        O = __builtin_fmaf(st[2 + k] + st[2 + D + k / G], wt, O);
+      }
+      out[((int64_t)b * Hq + (int64_t)h * GQ + g) * D + k] = O / Ls;
+    }
+  }
 }
 
 // Finish one row (b, q-head, query j): optionally attend over the unquantized tail
 // tokens the row sees (exact fp16 keys and values, the newest length % k_block tokens),
 // then merge the S split partials and the tail in a fixed order:
 //   M = max m_s,  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// In a decode step (nt.jnew >= 0) the tail slot jnew is read from the step's token, and
+// the first row of every kv head stores that token into the tail.
 __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                           RowSpec rs, const float* __restrict__ ws,
-                                                          float* __restrict__ out, int S, int with_tail) {
+                                                          float* __restrict__ out, int S, int with_tail,
+                                                          StepToken nt) {
   const int D = c.cfg.head_dim, half = D / 2, Bk = c.cfg.k_block;
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H;
   const int64_t bq = blockIdx.x;  // row index over [B][Hq][nq]
@@ -416,6 +467,10 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
     ntail = seen <= 0 ? 0 : (seen < ntail ? (int)seen : ntail);
   }
   const int tid = threadIdx.x;
+  if (nt.jnew >= 0 && hq % gq == 0 && qj == 0 && tid < D) {
+    c.k_tail[(bh * Bk + nt.jnew) * D + tid] = nt.k[bh * D + tid];
+    c.v_tail[(bh * Bk + nt.jnew) * D + tid] = nt.v[bh * D + tid];
+  }
   if (ntail == 0 && S <= kFinishFastSplits) {
     // No tail and few splits: each channel's thread loads every split's (m, l) and its
     // own partial output at once (one memory round trip, no barriers) and merges them
@@ -466,7 +521,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
     __syncthreads();
     float s = -__builtin_inff();
     if (tid < ntail) {
-      const uint16_t* kr = c.k_tail + (bh * Bk + tid) * D;
+      const uint16_t* kr = tid == nt.jnew ? nt.k + bh * D : c.k_tail + (bh * Bk + tid) * D;
       const float* tab = c.rope + (int64_t)tid * half * 2;
       s = 0.0f;
       for (int i = 0; i < half; ++i) {
@@ -544,11 +599,12 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
       for (; j + 8 <= ntail; j += 8) {
         float t[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = h2f(vt[(int64_t)(j + u) * D]);
+        for (int u = 0; u < 8; ++u) t[u] = h2f(j + u == nt.jnew ? nt.v[bh * D + d] : vt[(int64_t)(j + u) * D]);
 #pragma unroll
         for (int u = 0; u < 8; ++u) ot = __builtin_fmaf(p_s[j + u], t[u], ot);
       }
-      for (; j < ntail; ++j) ot = __builtin_fmaf(p_s[j], h2f(vt[(int64_t)j * D]), ot);
+      for (; j < ntail; ++j)
+        ot = __builtin_fmaf(p_s[j], h2f(j == nt.jnew ? nt.v[bh * D + d] : vt[(int64_t)j * D]), ot);
       O = __builtin_fmaf(ot, wt, O);
     }
     out[bq * D + d] = O / Lsum;
@@ -557,7 +613,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
 
 template <int D, int KB, int KMODE, int VB>
 hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s,
-                        int cus) {
+                        int cus, StepToken nt, float* fused_out) {
   using Sh = Shape<D, KB, KMODE, VB>;
   const int R = c.cfg.q_heads / c.cfg.kv_heads * rs.nq, ng = D / c.cfg.v_group;
   // rows per item: up to 8 (all query heads of a kv head for one query), fewer when
@@ -572,41 +628,54 @@ hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float
   }
   rs.rpi = rpi;
   rs.nsets = (R + rpi - 1) / rpi;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<D, KB, KMODE, VB>,
+  if (fused_out) {  // one-launch step: every row of a kv head in one workgroup, its waves the splits
+    if (rs.nsets != 1) return hipErrorNotSupported;
+    hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<D, KB, KMODE, VB, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    const int64_t units = (int64_t)c.cfg.batch * c.cfg.kv_heads;
+    hipLaunchKernelGGL((decode_split_kernel<D, KB, KMODE, VB, true>), dim3((unsigned)units), dim3(kThreads), bytes,
+                       s, c, q, rs, ws, kWaves, units * kWaves, nt, fused_out);
+    return hipGetLastError();
+  }
+  hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<D, KB, KMODE, VB, false>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * rs.nsets * S;
   int64_t grid = (nitems + kWaves - 1) / kWaves;
   const int64_t cap = (int64_t)cus * (bytes <= 80 * 1024 ? 2 : 1);
   if (grid > cap) grid = cap;
-  hipLaunchKernelGGL((decode_split_kernel<D, KB, KMODE, VB>), dim3((unsigned)grid), dim3(kThreads), bytes, s,
-                     c, q, rs, ws, S, nitems);
+  hipLaunchKernelGGL((decode_split_kernel<D, KB, KMODE, VB, false>), dim3((unsigned)grid), dim3(kThreads), bytes, s,
+                     c, q, rs, ws, S, nitems, nt, nullptr);
   return hipGetLastError();
 }
 
 template <int D, int KB, int KMODE>
-hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s, int cus) {
-  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, rs, ws, S, s, cus);
-  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, rs, ws, S, s, cus);
+hipError_t launch_vb(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s, int cus,
+                     StepToken nt, float* fused_out) {
+  if (c.cfg.v_bits == 4) return launch_typed<D, KB, KMODE, 4>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (c.cfg.v_bits == 2) return launch_typed<D, KB, KMODE, 2>(c, q, rs, ws, S, s, cus, nt, fused_out);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s, int cus) {
+hipError_t launch_d(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s, int cus,
+                    StepToken nt, float* fused_out) {
   const int kb = c.cfg.k_bits, km = c.cfg.k_mode;
-  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, rs, ws, S, s, cus);
-  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, rs, ws, S, s, cus);
-  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, rs, ws, S, s, cus);
-  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, rs, ws, S, s, cus);
-  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, rs, ws, S, s, cus);
-  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, rs, ws, S, s, cus);
+  if (km == 0 && kb == 4) return launch_vb<D, 4, 0>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (km == 0 && kb == 3) return launch_vb<D, 3, 0>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (km == 0 && kb == 2) return launch_vb<D, 2, 0>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, rs, ws, S, s, cus, nt, fused_out);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_generic(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws, int S, hipStream_t s,
-                          int cus) {
-  if (c.cfg.head_dim == 128) return launch_d<128>(c, q, rs, ws, S, s, cus);
-  if (c.cfg.head_dim == 64) return launch_d<64>(c, q, rs, ws, S, s, cus);
+                          int cus, StepToken nt = StepToken{nullptr, nullptr, -1},
+                          float* fused_out = nullptr) {
+  if (c.cfg.head_dim == 128) return launch_d<128>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  if (c.cfg.head_dim == 64) return launch_d<64>(c, q, rs, ws, S, s, cus, nt, fused_out);
   return hipErrorInvalidValue;
 }
 
@@ -623,8 +692,11 @@ hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_po
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus);
 
-hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
-                         int splits, hipStream_t s) {
+// Split kernel + finish kernel; `nt` is the token of a decode step (jnew < 0: none).
+// The tuned kernels read quantized blocks only, so the token reaches them through the
+// finish kernel, which attends over the tail; the generic kernel reads the tail itself.
+static hipError_t decode_two_launches(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
+                               int splits, hipStream_t s, StepToken nt) {
   const int cus = device_cus();
   const RowSpec rs{q_pos, 1, 0, 1, 1};
   hipError_t e = launch_decode_mha(c, q, q_pos, ws, splits, s, cus);
@@ -632,12 +704,33 @@ hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, f
   int with_tail = 1;  // the tuned kernels leave the unquantized tail to the finish kernel
   if (e == hipErrorNotSupported) {
     with_tail = 0;
-    e = launch_generic(c, q, rs, ws, splits, s, cus);
+    e = launch_generic(c, q, rs, ws, splits, s, cus, nt);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(256), 0, s, c,
-                     q, rs, ws, out, splits, with_tail);
+                     q, rs, ws, out, splits, with_tail, nt);
   return hipGetLastError();
+}
+
+bool decode_step_fits(const kvq_config& c) {
+  const int D = c.head_dim, R = c.q_heads / c.kv_heads;
+  const int ppl = c.k_bits == 3 ? 16 : 8, lpt = D / 2 / ppl, tpi = kWave / lpt;
+  const WaveLds L = wave_lds(D, c.k_block, R, D / c.v_group, tpi, c.k_bits, c.k_mode, host_kout(c) > 0);
+  const size_t bytes = ((size_t)c.k_block * (D + 4) + (size_t)kWaves * L.total) * sizeof(float);
+  return R <= 8 && bytes <= 160 * 1024;
+}
+
+hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
+                         int splits, hipStream_t s) {
+  return decode_two_launches(c, q, q_pos, out, ws, splits, s, StepToken{nullptr, nullptr, -1});
+}
+
+hipError_t launch_decode_step(const kvq_cache& c, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              int jnew, float* out, float* ws, int splits, hipStream_t s) {
+  const StepToken nt{k_new, v_new, jnew};
+  if (splits > 0) return decode_two_launches(c, q, c.length - 1, out, ws, splits, s, nt);
+  const RowSpec rs{c.length - 1, 1, 0, 1, 1};
+  return launch_generic(c, q, rs, nullptr, kWaves, s, device_cus(), nt, out);
 }
 
 hipError_t launch_chunk(const kvq_cache& c, const uint16_t* q, int nq, int64_t q_pos, float* out, float* ws,
@@ -652,7 +745,7 @@ hipError_t launch_chunk(const kvq_cache& c, const uint16_t* q, int nq, int64_t q
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)((int64_t)c.cfg.batch * c.cfg.q_heads * nq)), dim3(256),
-                     0, s, c, q, rs, ws, out, splits, with_tail);
+                     0, s, c, q, rs, ws, out, splits, with_tail, StepToken{nullptr, nullptr, -1});
   return hipGetLastError();
 }
 

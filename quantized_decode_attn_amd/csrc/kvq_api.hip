@@ -105,6 +105,9 @@ int auto_chunk_splits(const kvq_config& c, int nq) {
 
 constexpr int32_t kMaxChunk = 1024;
 
+// Longest cache (in quantized blocks per sequence) that a decode step takes in one launch.
+constexpr int64_t kStepOneLaunchBlocks = 8;
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +231,37 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, i
   st = scratch_of_current_device(&ws);
   if (st != KVQ_OK) return st;
   return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, ws, S, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q, float* out,
+                           void* ws, size_t ws_bytes, int32_t num_splits, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new || !q || !out || num_splits < 0 || num_splits > 4096) return KVQ_EINVAL;
+  const kvq_config& c = cache->cfg;
+  const int64_t L0 = cache->length, L1 = L0 + 1, Bk = c.k_block;
+  if (L1 > c.capacity) return KVQ_ECAPACITY;
+  const int S = num_splits ? num_splits : auto_splits(c);
+  const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
+  if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
+  // one launch while the cache is short enough that launches, not bandwidth, set the cost
+  const bool one_launch = num_splits == 0 && L1 / Bk <= kStepOneLaunchBlocks && kvq::decode_step_fits(c);
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* kn = (const uint16_t*)k_new;
+  const uint16_t* vn = (const uint16_t*)v_new;
+  int jnew = (int)(L0 % Bk);
+  if (L1 % Bk == 0) {  // the token completes a block: quantize it (tail + token) first
+    st = from_hip(kvq::launch_quantize(*cache, kn, vn, L0, 1, L0 / Bk, 1, s));
+    if (st != KVQ_OK) return st;
+    jnew = -1;
+  }
+  kvq_cache next = *cache;
+  next.length = L1;
+  st = from_hip(kvq::launch_decode_step(next, (const uint16_t*)q, kn, vn, jnew, out, (float*)ws,
+                                        one_launch ? 0 : S, s));
+  if (st != KVQ_OK) return st;
+  cache->length = L1;
+  return KVQ_OK;
 }
 
 size_t kvq_chunk_workspace_bytes(const kvq_cache* cache, int32_t nq, int32_t num_splits) {

@@ -54,6 +54,18 @@ __host__ __device__ inline int64_t row_visible(const RowSpec& rs, int j, int64_t
   return n < length ? n : length;
 }
 
+// Fused decode step over a cache whose length already counts the new token; the new
+// token's keys and values [B][Hkv][D] stand at tail slot jnew (read from the input,
+// written to the tail), or jnew < 0 when the token completed a block that is already
+// quantized.  splits == 0: one launch, one workgroup per (b, kv-head) whose waves take
+// the splits, merged in LDS (hipErrorNotSupported when the rows of a kv head do not fit
+// one workgroup; ws unused).  splits > 0: the decode split kernel with that many splits
+// and the finish kernel, partials in ws.
+hipError_t launch_decode_step(const kvq_cache& c, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                              int jnew, float* out, float* ws, int splits, hipStream_t s);
+// Whether every query head of a kv head fits one workgroup of the one-launch step (host only).
+bool decode_step_fits(const kvq_config& c);
+
 // Causal attention of a chunk of nq queries (the generic split kernel, or the
 // matrix-core kernel where it applies), partials merged by the finish kernel.
 hipError_t launch_chunk(const kvq_cache& c, const uint16_t* q, int nq, int64_t q_pos, float* out,

@@ -28,6 +28,11 @@ hipError_t launch_dequantize(const kvq_cache&, int, int64_t, int64_t, float*, hi
 hipError_t launch_chunk(const kvq_cache&, const uint16_t*, int, int64_t, float*, float*, int, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_decode_step(const kvq_cache&, const uint16_t*, const uint16_t*, const uint16_t*, int, float*,
+                              float*, int, hipStream_t) {
+  return hipErrorNotSupported;
+}
+bool decode_step_fits(const kvq_config&) { return true; }
 }  // namespace kvq
 
 static int failures = 0;
@@ -146,6 +151,28 @@ int main() {
   EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, 295, out, (void*)0x3000, cws, 4097, nullptr) == KVQ_EINVAL);
   EXPECT(kvq_chunk_attention(&k, nullptr, 5, 295, out, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
   EXPECT(kvq_chunk_attention(&k, (void*)0x1000, 5, 295, nullptr, (void*)0x3000, cws, 0, nullptr) == KVQ_EINVAL);
+  // fused decode step: argument checks, workspace, capacity, then the (stubbed) launch
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws, 0, nullptr) ==
+         KVQ_EHIP);
+  EXPECT(k.length == 300);
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws, 3, nullptr) ==
+         KVQ_EHIP);
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws - 1, 0, nullptr) ==
+         KVQ_EWORKSPACE);
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, nullptr, ws, 0, nullptr) ==
+         KVQ_EWORKSPACE);
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws, -1, nullptr) ==
+         KVQ_EINVAL);
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws, 4097, nullptr) ==
+         KVQ_EINVAL);
+  EXPECT(kvq_decode_step(&k, nullptr, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws, 0, nullptr) == KVQ_EINVAL);
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, nullptr, (void*)0x3000, ws, 0, nullptr) ==
+         KVQ_EINVAL);
+  EXPECT(k.length == 300);
+  k.length = 1024;
+  EXPECT(kvq_decode_step(&k, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, ws, 0, nullptr) ==
+         KVQ_ECAPACITY);
+  k.length = 300;
   EXPECT(kvq_dequantize(&k, 0, 0, 300, out, nullptr) == KVQ_EHIP);
   EXPECT(kvq_dequantize(&k, 2, 0, 300, out, nullptr) == KVQ_EINVAL);
   EXPECT(kvq_dequantize(&k, 1, 10, 5, out, nullptr) == KVQ_EINVAL);
