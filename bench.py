@@ -175,8 +175,13 @@ def copy_probe():
 
 def time_decode_steps(cfg, k_d, v_d, lut_d, n, dev):
     """Per-step time of n token-by-token decode steps on a cache of the workload's first
-    T - n tokens: fused (one kvq_decode_step per token) against two calls (append of one
-    token, then decode), each timed over the whole sequence with HIP events."""
+    T - n tokens, three ways: kvq_decode_step with the library's choice of kernels (one
+    launch for a short cache), kvq_decode_step on the split kernels, and
+    kvq_quantize_append of one token followed by kvq_decode_attention.  Each is timed with
+    HIP events over the whole run, once issued call by call from Python (host cost
+    included) and once captured as one HIP graph of the n steps and replayed (the cost on
+    the GPU: kernels and the gaps between launches), the cache buffers restored to the
+    starting state before each replay, outside the timed region."""
     import torch
     import quantized_decode_attn_amd as kvq
     T, B, Hq, D = cfg["tokens"], cfg["batch"], cfg["q_heads"], cfg["head_dim"]
@@ -189,29 +194,70 @@ def time_decode_steps(cfg, k_d, v_d, lut_d, n, dev):
     q1 = [qs[:, :, i].contiguous() for i in range(n)]
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     cache = kvq.Cache(cfg, device=dev, lut=lut_d)
-    cache.workspace(0)
-    stream = torch.cuda.current_stream()
-    res = {}
-    for mode in ("fused", "two_calls", "fused", "two_calls"):   # each twice; the second run is reported
+    # the library's split count, read back from its workspace size
+    s_auto = kvq.kvq_decode_workspace_bytes(cache.desc, 0) // (B * Hq * (D + 2) * 4)
+    cache.workspace(s_auto)
+
+    def reset():
         cache.desc.length = 0
         cache.append(k_d[:, :, :T0].contiguous(), v_d[:, :, :T0].contiguous())
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+
+    def run(mode, stream):
         for i in range(n):
             if mode == "fused":
-                cache.step(toks_k[i], toks_v[i], q1[i], out=out)
+                cache.step(toks_k[i], toks_v[i], q1[i], out=out, stream=stream)
+            elif mode == "fused_split":
+                cache.step(toks_k[i], toks_v[i], q1[i], num_splits=s_auto, out=out, stream=stream)
             else:
-                cache.append(toks_k1[i], toks_v1[i])
-                cache.decode(q1[i], q_pos=T0 + i, out=out)
+                cache.append(toks_k1[i], toks_v1[i], stream=stream)
+                cache.decode(q1[i], q_pos=T0 + i, out=out, stream=stream)
+
+    modes = ("fused", "fused_split", "two_calls")
+    eager, graph = {}, {}
+    stream = torch.cuda.current_stream()
+    for mode in modes + modes:   # each twice; the second run is reported
+        reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(mode, stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        res[mode] = e0.elapsed_time(e1) * 1e3 / n
-    log("decode step  fused %.1f us/token, append + decode %.1f us/token (%d tokens from %d)"
-        % (res["fused"], res["two_calls"], n, T0))
-    return {"tokens": n, "from_length": T0, "fused_us_per_token": round(res["fused"], 2),
-            "append_plus_decode_us_per_token": round(res["two_calls"], 2),
-            "speedup": round(res["two_calls"] / res["fused"], 3)}
+        eager[mode] = e0.elapsed_time(e1) * 1e3 / n
+    replays = 5
+    for mode in modes:
+        reset()
+        start = {name: buf.clone() for name, buf in cache.bufs.items() if buf is not None}
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+                run(mode, side)
+        torch.cuda.synchronize()
+        total = 0.0
+        for r in range(replays + 1):        # the first replay warms up
+            for name, buf in start.items():
+                cache.bufs[name].copy_(buf)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if r:
+                total += e0.elapsed_time(e1)
+        graph[mode] = total * 1e3 / (n * replays)
+        del g
+    log("decode step, us/token issued from Python: fused %.1f (split kernels %.1f), append + decode %.1f"
+        % (eager["fused"], eager["fused_split"], eager["two_calls"]))
+    log("decode step, us/token replayed as a graph: fused %.1f (split kernels %.1f), append + decode %.1f "
+        "(%d tokens from %d)" % (graph["fused"], graph["fused_split"], graph["two_calls"], n, T0))
+    r2 = lambda x: round(x, 2)
+    return {"tokens": n, "from_length": T0, "splits": int(s_auto),
+            "graph_us_per_token": {k: r2(v) for k, v in graph.items()},
+            "python_us_per_token": {k: r2(v) for k, v in eager.items()},
+            "graph_speedup_vs_append_plus_decode": round(graph["two_calls"] / graph["fused"], 3)}
 
 
 def main():

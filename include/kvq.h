@@ -216,11 +216,13 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache *cache, const void *q, i
  * never takes a launch of its own: the attention reads it from k_new/v_new and one of
  * its kernels stores it into the fp16 tail.  When it completes a block, that block is
  * quantized first (one launch, as by kvq_quantize_append).
- * num_splits == 0 (the library's choice): a short cache (at most 8 quantized blocks per
- * sequence) takes ONE launch, one workgroup per (b, kv-head) whose waves split the
- * cache and merge in LDS, so that launch count, not bandwidth, is what the step costs;
- * a longer one takes the split kernels of kvq_decode_attention with the library's split
- * count (two launches).  num_splits > 0: those two launches with that many splits.
+ * num_splits == 0 (the library's choice): the split kernels of kvq_decode_attention with
+ * the library's split count (two launches), except for a short cache (at most 4
+ * quantized blocks per sequence) in a configuration that none of the tuned decode kernels
+ * covers: that takes ONE launch, one workgroup per (b, kv-head) whose waves split the
+ * cache and merge in LDS.  (Where a tuned kernel applies, it and the merge launch take
+ * less time than the one generic launch, even at 256 tokens.)  num_splits > 0: the two
+ * launches with that many splits.
  * ws: device workspace of at least kvq_decode_workspace_bytes(cache, num_splits) bytes
  * (the same as kvq_decode_attention's; the one-launch path does not touch it).
  * k_new, v_new: *device* fp16 [batch][kv_heads][head_dim], keys pre-RoPE; q: *device*

@@ -373,14 +373,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
               for (int row = 0; row < Sh::TPI; ++row) acc[k] += VC[row * D + lane + k * kWave];
           }
         } else {
-          for (int j = 0; j < nvis; ++j) {
-            const float p = Pl[j];
+          // fp16 tail values, 16 tokens' loads in flight ahead of their FMAs
+          const uint16_t* vt = c.v_tail + bh * Bk * D + lane;
+          const uint16_t* vn = nt.v + bh * D + lane;
+          int j = 0;
+          for (; j + 16 <= nvis; j += 16) {
+            uint16_t t[16][Sh::CPL];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+              for (int k = 0; k < Sh::CPL; ++k)
+                t[u][k] = j + u == nt.jnew ? vn[k * kWave] : vt[(int64_t)(j + u) * D + k * kWave];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+              for (int k = 0; k < Sh::CPL; ++k) acc[k] = __builtin_fmaf(Pl[j + u], h2f(t[u][k]), acc[k]);
+          }
+          for (; j < nvis; ++j)
 #pragma unroll
             for (int k = 0; k < Sh::CPL; ++k)
-              acc[k] = __builtin_fmaf(p, h2f(j == nt.jnew ? nt.v[bh * D + lane + k * kWave]
-                                                               : c.v_tail[(bh * Bk + j) * D + lane + k * kWave]),
+              acc[k] = __builtin_fmaf(Pl[j], h2f(j == nt.jnew ? vn[k * kWave] : vt[(int64_t)j * D + k * kWave]),
                                       acc[k]);
-          }
           if (lane == 0)
             for (int gg = 0; gg < ng; ++gg) st[2 + D + gg] *= alpha;
         }
@@ -552,7 +565,7 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
   // outputs with independent loads, the splits divided between the two thread halves
   // and the halves added in a fixed order.
   __shared__ float wsh[kFinishMaxSplits];
-  __shared__ float osh[256];
+  __shared__ float osh[256], osh_t[256];
   __shared__ float red2[8];
   const float* base = ws + bq * (int64_t)S * (D + 2);
   float mloc = ntail > 0 ? tail_m : -__builtin_inff();
@@ -588,27 +601,226 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
     for (int u = 0; u < 8; ++u) O = __builtin_fmaf(t[u], wsh[sp + u], O);
   }
   for (; sp < s1; ++sp) O = __builtin_fmaf(base[(int64_t)sp * (D + 2) + 2 + d], wsh[sp], O);
+  // the tail's values: tokens j = part, part + nparts, ... of each channel, 16 loads in
+  // flight ahead of their FMAs
+  float ot = 0.0f;
+  if (ntail > 0) {
+    const uint16_t* vt = c.v_tail + bh * Bk * D + d;
+    const uint16_t* vn = nt.v + bh * D + d;
+    int j = part;
+    for (; j + 15 * nparts < ntail; j += 16 * nparts) {
+      uint16_t t[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int jj = j + u * nparts;
+        t[u] = jj == nt.jnew ? vn[0] : vt[(int64_t)jj * D];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) ot = __builtin_fmaf(p_s[j + u * nparts], h2f(t[u]), ot);
+    }
+    for (; j < ntail; j += nparts) ot = __builtin_fmaf(p_s[j], h2f(j == nt.jnew ? vn[0] : vt[(int64_t)j * D]), ot);
+  }
   osh[tid] = O;
+  osh_t[tid] = ot;
   __syncthreads();
   if (part == 0) {
     for (int pt = 1; pt < nparts; ++pt) O += osh[pt * D + d];
     if (ntail > 0) {
-      float ot = 0.0f;
-      const uint16_t* vt = c.v_tail + bh * Bk * D + d;
-      int j = 0;
-      for (; j + 8 <= ntail; j += 8) {
-        float t[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = h2f(j + u == nt.jnew ? nt.v[bh * D + d] : vt[(int64_t)(j + u) * D]);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ot = __builtin_fmaf(p_s[j + u], t[u], ot);
-      }
-      for (; j < ntail; ++j)
-        ot = __builtin_fmaf(p_s[j], h2f(j == nt.jnew ? nt.v[bh * D + d] : vt[(int64_t)j * D]), ot);
+      for (int pt = 1; pt < nparts; ++pt) ot += osh_t[pt * D + d];
       O = __builtin_fmaf(ot, wt, O);
     }
     out[bq * D + d] = O / Lsum;
   }
+}
+
+// 16-bit element e of a row held as uint4 words (e a compile-time index after unrolling).
+template <int N>
+__device__ __forceinline__ uint16_t row_elem(const uint4 (&w)[N], int e) {
+  const uint4& v = w[e >> 3];
+  const int k = (e >> 1) & 3;
+  const uint32_t x = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+  return (uint16_t)(x >> ((e & 1) * 16));
+}
+
+// The finish of a row whose kv head has an unquantized tail, for at most
+// kFinishFastSplits splits: the same arithmetic as decode_finish_kernel, with every
+// global load the row needs (the query, each tail token's key row and rotary offsets,
+// the tail values, the split partials) issued before the first is used, so that the row
+// costs about one memory round trip instead of one per stage.  Thread tid < ntail scores
+// tail token tid; thread (d, part) sums the values of channel d over the tokens
+// part, part + NP, ...; the partial sums are added in part order.
+template <int D>
+__global__ __launch_bounds__(256) void decode_finish_tail_kernel(kvq_cache c, const uint16_t* __restrict__ q,
+                                                               RowSpec rs, const float* __restrict__ ws,
+                                                               float* __restrict__ out, int S, StepToken nt) {
+  constexpr int HALF = D / 2, NP = 256 / D, MAXV = 128 / NP;  // k_block <= 128
+  const int Bk = c.cfg.k_block;
+  const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H;
+  const int64_t bq = blockIdx.x;  // row index over [B][Hq][nq]
+  const int qj = (int)(bq % rs.nq);
+  const int64_t bhq = bq / rs.nq;
+  const int b = (int)(bhq / Hq), hq = (int)(bhq % Hq), h = hq / gq;
+  const int64_t bh = (int64_t)b * H + h;
+  const int64_t q_pos = rs.q_pos + qj;
+  const int64_t nfull = c.length / Bk;
+  int ntail = (int)(c.length - nfull * Bk);
+  {
+    const int64_t seen = row_visible(rs, qj, c.length) - nfull * Bk;
+    ntail = seen <= 0 ? 0 : (seen < ntail ? (int)seen : ntail);
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = tid % D, part = tid / D;
+  if (nt.jnew >= 0 && hq % gq == 0 && qj == 0 && tid < D) {
+    c.k_tail[(bh * Bk + nt.jnew) * D + tid] = nt.k[bh * D + tid];
+    c.v_tail[(bh * Bk + nt.jnew) * D + tid] = nt.v[bh * D + tid];
+  }
+  __shared__ float wr_s[HALF], wi_s[HALF], p_s[128], red[8], osh_t[256];
+
+  // ---- every load first
+  const float* base = ws + bq * (int64_t)S * (D + 2);
+  float mv[kFinishFastSplits], lv[kFinishFastSplits], ov[kFinishFastSplits];
+#pragma unroll
+  for (int sp = 0; sp < kFinishFastSplits; ++sp) {
+    mv[sp] = -__builtin_inff();
+    lv[sp] = ov[sp] = 0.0f;
+    if (sp < S) {
+      mv[sp] = base[(int64_t)sp * (D + 2)];
+      lv[sp] = base[(int64_t)sp * (D + 2) + 1];
+      if (part == 0) ov[sp] = base[(int64_t)sp * (D + 2) + 2 + d];
+    }
+  }
+  double qa = 0.0, qb = 0.0;
+  float eb0 = 0.0f, eb1 = 0.0f, pc = 0.0f, ps = 0.0f, po0 = 0.0f, po1 = 0.0f;
+  // inside the capacity, e^{i f q_pos} = e^{i f nb Bk} e^{i f jq} from the fp64-built tables
+  const bool qtab = q_pos < c.cfg.capacity;
+  if (tid < HALF) {
+    const uint16_t* qv = q + bq * D;
+    qa = (double)h2f(qv[tid]);
+    qb = (double)h2f(qv[tid + HALF]);
+    const float* eb = c.rope + (int64_t)Bk * D + (nfull * HALF + tid) * 2;
+    eb0 = eb[0];
+    eb1 = eb[1];
+    if (qtab) {
+      const float* pb = c.rope + (int64_t)Bk * D + ((q_pos / Bk) * HALF + tid) * 2;
+      const float* po = c.rope + ((q_pos % Bk) * HALF + tid) * 2;
+      pc = pb[0];
+      ps = pb[1];
+      po0 = po[0];
+      po1 = po[1];
+    }
+  }
+  uint4 kraw[D / 8];
+  float4 tab[D / 4];
+  if (tid < ntail) {
+    if (tid == nt.jnew) {
+      const uint16_t* src = nt.k + bh * D;
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k)
+        kraw[k] = make_uint4(src[8 * k] | (uint32_t)src[8 * k + 1] << 16, src[8 * k + 2] | (uint32_t)src[8 * k + 3] << 16,
+                             src[8 * k + 4] | (uint32_t)src[8 * k + 5] << 16, src[8 * k + 6] | (uint32_t)src[8 * k + 7] << 16);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(c.k_tail + (bh * Bk + tid) * D);
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k) kraw[k] = src[k];
+    }
+    const float4* ts = reinterpret_cast<const float4*>(c.rope + (int64_t)tid * HALF * 2);
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) tab[k] = ts[k];
+  }
+  uint16_t vv[MAXV];
+#pragma unroll
+  for (int u = 0; u < MAXV; ++u) {
+    const int j = part + u * NP;
+    vv[u] = j < ntail ? (j == nt.jnew ? nt.v[bh * D + d] : c.v_tail[(bh * Bk + j) * D + d]) : (uint16_t)0;
+  }
+
+  // ---- query weights: scale * conj(q) e^{-i f q_pos} (fp64 angle), times the tail
+  // block's base rotation e^{i f nfull Bk}
+  if (tid < HALF) {
+    double sn, cs;
+    if (qtab) {
+      cs = (double)(pc * po0 - ps * po1);
+      sn = (double)(ps * po0 + pc * po1);
+    } else {
+      const double f = pow((double)c.cfg.rope_theta, -(2.0 * tid) / (double)D);
+      sincos((double)q_pos * f, &sn, &cs);
+    }
+    const double scl = (double)kLog2e / sqrt((double)D);
+    const float qr = (float)(scl * (qa * cs - qb * sn)), qi = (float)(-scl * (qa * sn + qb * cs));
+    wr_s[tid] = qr * eb0 - qi * eb1;
+    wi_s[tid] = qr * eb1 + qi * eb0;
+  }
+  __syncthreads();
+  // ---- tail scores (base 2) and their softmax
+  float s = -__builtin_inff();
+  if (tid < ntail) {
+    s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+      const float a = h2f(row_elem(kraw, i)), bb = h2f(row_elem(kraw, i + HALF));
+      const float4 t = tab[i >> 1];
+      const float cs = (i & 1) ? t.z : t.x, sn = (i & 1) ? t.w : t.y;
+      const float X = __builtin_fmaf(wr_s[i], a, -wi_s[i] * bb);
+      const float Y = -__builtin_fmaf(wi_s[i], a, wr_s[i] * bb);
+      s = __builtin_fmaf(cs, X, __builtin_fmaf(sn, Y, s));
+    }
+  }
+  const float wm = wave_max(s);
+  if (lane == 0) red[wave] = wm;
+  __syncthreads();
+  const float tm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float p = tid < ntail ? exp2f(s - tm) : 0.0f;
+  if (tid < 128) p_s[tid] = p;
+  const float wl = wave_sum(p);
+  if (lane == 0) red[4 + wave] = wl;
+  __syncthreads();
+  const float tl = (red[4] + red[5]) + (red[6] + red[7]);
+
+  // ---- merge in split order, then the tail:
+  //   M = max(m_s, m_tail),  out = (sum_s o_s 2^(m_s - M) + o_tail 2^(m_tail - M)) / (same for l)
+  float M = tm;
+#pragma unroll
+  for (int sp = 0; sp < kFinishFastSplits; ++sp) M = fmaxf(M, mv[sp]);
+  float Lsum = 0.0f, O = 0.0f;
+#pragma unroll
+  for (int sp = 0; sp < kFinishFastSplits; ++sp) {
+    const float w = mv[sp] == -__builtin_inff() ? 0.0f : exp2f(mv[sp] - M);  // empty split: 0
+    Lsum = __builtin_fmaf(lv[sp], w, Lsum);
+    O = __builtin_fmaf(ov[sp], w, O);
+  }
+  const float wt = ntail > 0 ? exp2f(tm - M) : 0.0f;
+  Lsum = __builtin_fmaf(tl, wt, Lsum);
+  float ot = 0.0f;
+#pragma unroll
+  for (int u = 0; u < MAXV; ++u) {
+    const int j = part + u * NP;
+    if (j < ntail) ot = __builtin_fmaf(p_s[j], h2f(vv[u]), ot);
+  }
+  osh_t[tid] = ot;
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int pt = 1; pt < NP; ++pt) ot += osh_t[pt * D + d];
+    O = __builtin_fmaf(ot, wt, O);
+    out[bq * D + d] = O / Lsum;
+  }
+}
+
+// The finish launch of a decode or chunk: the load-ahead kernel where the rows have an
+// unquantized tail to attend over and few splits, else the general one.
+hipError_t launch_finish(const kvq_cache& c, const uint16_t* q, RowSpec rs, const float* ws, float* out, int S,
+                         int with_tail, StepToken nt, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)c.cfg.batch * c.cfg.q_heads * rs.nq));
+  const bool tail = with_tail && c.length % c.cfg.k_block != 0;
+  if (tail && S <= kFinishFastSplits && c.cfg.k_block <= 128) {
+    if (c.cfg.head_dim == 128)
+      hipLaunchKernelGGL(decode_finish_tail_kernel<128>, grid, dim3(256), 0, s, c, q, rs, ws, out, S, nt);
+    else
+      hipLaunchKernelGGL(decode_finish_tail_kernel<64>, grid, dim3(256), 0, s, c, q, rs, ws, out, S, nt);
+  } else {
+    hipLaunchKernelGGL(decode_finish_kernel, grid, dim3(256), 0, s, c, q, rs, ws, out, S, with_tail, nt);
+  }
+  return hipGetLastError();
 }
 
 template <int D, int KB, int KMODE, int VB>
@@ -688,9 +900,9 @@ int device_cus() {
 }  // namespace
 
 hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                             hipStream_t s, int cus);
+                             hipStream_t s, int cus, bool dry = false);
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                             hipStream_t s, int cus);
+                             hipStream_t s, int cus, bool dry = false);
 
 // Split kernel + finish kernel; `nt` is the token of a decode step (jnew < 0: none).
 // The tuned kernels read quantized blocks only, so the token reaches them through the
@@ -707,22 +919,26 @@ static hipError_t decode_two_launches(const kvq_cache& c, const uint16_t* q, int
     e = launch_generic(c, q, rs, ws, splits, s, cus, nt);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)(c.cfg.batch * c.cfg.q_heads)), dim3(256), 0, s, c,
-                     q, rs, ws, out, splits, with_tail, nt);
-  return hipGetLastError();
-}
-
-bool decode_step_fits(const kvq_config& c) {
-  const int D = c.head_dim, R = c.q_heads / c.kv_heads;
-  const int ppl = c.k_bits == 3 ? 16 : 8, lpt = D / 2 / ppl, tpi = kWave / lpt;
-  const WaveLds L = wave_lds(D, c.k_block, R, D / c.v_group, tpi, c.k_bits, c.k_mode, host_kout(c) > 0);
-  const size_t bytes = ((size_t)c.k_block * (D + 4) + (size_t)kWaves * L.total) * sizeof(float);
-  return R <= 8 && bytes <= 160 * 1024;
+  return launch_finish(c, q, rs, ws, out, splits, with_tail, nt, s);
 }
 
 hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out, float* ws,
                          int splits, hipStream_t s) {
   return decode_two_launches(c, q, q_pos, out, ws, splits, s, StepToken{nullptr, nullptr, -1});
+}
+
+bool decode_step_prefers_one_launch(const kvq_cache& c) {
+  const kvq_config& g = c.cfg;
+  const int D = g.head_dim, R = g.q_heads / g.kv_heads;
+  const int ppl = g.k_bits == 3 ? 16 : 8, lpt = D / 2 / ppl, tpi = kWave / lpt;
+  const WaveLds L = wave_lds(D, g.k_block, R, D / g.v_group, tpi, g.k_bits, g.k_mode, host_kout(g) > 0);
+  const size_t bytes = ((size_t)g.k_block * (D + 4) + (size_t)kWaves * L.total) * sizeof(float);
+  if (R > 8 || bytes > 160 * 1024) return false;
+  // where a tuned split kernel covers the configuration, it and the finish kernel take
+  // less time than the one generic launch
+  if (launch_decode_mha(c, nullptr, 0, nullptr, 1, nullptr, 1, true) == hipSuccess) return false;
+  if (launch_decode_gqa(c, nullptr, 0, nullptr, 1, nullptr, 1, true) == hipSuccess) return false;
+  return true;
 }
 
 hipError_t launch_decode_step(const kvq_cache& c, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
@@ -744,9 +960,7 @@ hipError_t launch_chunk(const kvq_cache& c, const uint16_t* q, int nq, int64_t q
     e = launch_generic(c, q, rs, ws, splits, s, cus);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_finish_kernel, dim3((unsigned)((int64_t)c.cfg.batch * c.cfg.q_heads * nq)), dim3(256),
-                     0, s, c, q, rs, ws, out, splits, with_tail, StepToken{nullptr, nullptr, -1});
-  return hipGetLastError();
+  return launch_finish(c, q, rs, ws, out, splits, with_tail, StepToken{nullptr, nullptr, -1}, s);
 }
 
 }  // namespace kvq

@@ -612,10 +612,11 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
 
 template <int VB, int GW, int KO, int NG>
 hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
-                            int cus) {
+                            int cus, bool dry) {
   const GLds L = gqa_lds(NG, KO > 0);
   const size_t bytes = ((size_t)kBK * kTP + (size_t)kGqaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (dry) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO, NG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
@@ -630,9 +631,10 @@ hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos
 
 }  // namespace
 
-// Returns hipErrorNotSupported when the configuration is not one this kernel covers.
+// Returns hipErrorNotSupported when the configuration is not one this kernel covers; with
+// `dry` it launches nothing and only reports whether it does.
 hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                             hipStream_t s, int cus) {
+                             hipStream_t s, int cus, bool dry) {
   const kvq_config& g = c.cfg;
   const int ko = host_kout(g);
   const int gq = g.q_heads / g.kv_heads;
@@ -642,8 +644,8 @@ hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_po
     return hipErrorNotSupported;
   const bool four = gq % 4 == 0;
 #define KVQ_GQA_NG(vb, gw, ko)                                                                \
-  return ng == 2 ? launch_gqa_typed<vb, gw, ko, 2>(c, q, q_pos, ws, S, s, cus)                \
-                 : launch_gqa_typed<vb, gw, ko, 1>(c, q, q_pos, ws, S, s, cus);
+  return ng == 2 ? launch_gqa_typed<vb, gw, ko, 2>(c, q, q_pos, ws, S, s, cus, dry)                \
+                 : launch_gqa_typed<vb, gw, ko, 1>(c, q, q_pos, ws, S, s, cus, dry);
 #define KVQ_GQA(vb, gw)                                                                       \
   if (g.v_bits == vb && four == (gw == 4)) {                                                  \
     if (ko == 2) { KVQ_GQA_NG(vb, gw, 2) }                                                    \

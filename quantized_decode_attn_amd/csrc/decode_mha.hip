@@ -687,17 +687,19 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
 
 }  // namespace
 
-// Returns hipErrorNotSupported when the configuration is not one this kernel covers.
+// Returns hipErrorNotSupported when the configuration is not one this kernel covers; with
+// `dry` it launches nothing and only reports whether it does.
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                             hipStream_t s, int cus);
+                             hipStream_t s, int cus, bool dry);
 
 template <int D, int BK, int KB, int VB, int KO>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                                   hipStream_t s, int cus) {
+                                   hipStream_t s, int cus, bool dry) {
   using Sh = MShape<D, BK, KB, VB>;
   const MLds L = mha_lds(D, BK, KO > 0, false);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (dry) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
@@ -711,12 +713,13 @@ static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_
 
 template <int D, int BK, int KB, int VB>
 static hipError_t launch_mha_lut_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                                       hipStream_t s, int cus) {
+                                       hipStream_t s, int cus, bool dry) {
   using Sh = MShape<D, BK, KB, VB>;
   const MLds L = mha_lds(D, BK, false, true);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)Sh::HALF * PairTab<KB>::PITCH +
                         (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (dry) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)decode_mha_lut_kernel<D, BK, KB, VB>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
@@ -728,7 +731,7 @@ static hipError_t launch_mha_lut_typed(const kvq_cache& c, const uint16_t* q, in
 }
 
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
-                             hipStream_t s, int cus) {
+                             hipStream_t s, int cus, bool dry) {
   const kvq_config& g = c.cfg;
   const int ko = host_kout(g);
   const int ng = g.head_dim / g.v_group;
@@ -738,7 +741,7 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
     // codebook keys: 2- and 3-bit codes (pair tables of 16 and 64 entries), no outliers
     if (ko != 0 || (KB != 3 && KB != 2)) return hipErrorNotSupported;
 #define KVQ_MHA_LUT(d, bk, kb, vb) \
-  if (D == d && BK == bk && KB == kb && VB == vb) return launch_mha_lut_typed<d, bk, kb, vb>(c, q, q_pos, ws, S, s, cus);
+  if (D == d && BK == bk && KB == kb && VB == vb) return launch_mha_lut_typed<d, bk, kb, vb>(c, q, q_pos, ws, S, s, cus, dry);
     KVQ_MHA_LUT(128, 128, 3, 2) KVQ_MHA_LUT(128, 128, 3, 4) KVQ_MHA_LUT(128, 128, 2, 2) KVQ_MHA_LUT(128, 128, 2, 4)
     KVQ_MHA_LUT(128, 64, 3, 2) KVQ_MHA_LUT(128, 64, 3, 4) KVQ_MHA_LUT(128, 64, 2, 2) KVQ_MHA_LUT(128, 64, 2, 4)
     KVQ_MHA_LUT(64, 128, 3, 2) KVQ_MHA_LUT(64, 128, 3, 4) KVQ_MHA_LUT(64, 128, 2, 2) KVQ_MHA_LUT(64, 128, 2, 4)
@@ -749,9 +752,9 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   if (g.k_mode != 0 || (KB != 4 && KB != 2)) return hipErrorNotSupported;
 #define KVQ_MHA(d, bk, kb, vb)                                                                  \
   if (D == d && BK == bk && KB == kb && VB == vb) {                                             \
-    if (ko == 2) return launch_mha_typed<d, bk, kb, vb, 2>(c, q, q_pos, ws, S, s, cus);         \
-    if (ko == 1) return launch_mha_typed<d, bk, kb, vb, 1>(c, q, q_pos, ws, S, s, cus);         \
-    return launch_mha_typed<d, bk, kb, vb, 0>(c, q, q_pos, ws, S, s, cus);                      \
+    if (ko == 2) return launch_mha_typed<d, bk, kb, vb, 2>(c, q, q_pos, ws, S, s, cus, dry);         \
+    if (ko == 1) return launch_mha_typed<d, bk, kb, vb, 1>(c, q, q_pos, ws, S, s, cus, dry);         \
+    return launch_mha_typed<d, bk, kb, vb, 0>(c, q, q_pos, ws, S, s, cus, dry);                      \
   }
   KVQ_MHA(128, 128, 4, 4) KVQ_MHA(128, 128, 4, 2) KVQ_MHA(128, 128, 2, 4) KVQ_MHA(128, 128, 2, 2)
   KVQ_MHA(128, 64, 4, 4) KVQ_MHA(128, 64, 4, 2) KVQ_MHA(128, 64, 2, 4) KVQ_MHA(128, 64, 2, 2)

@@ -105,8 +105,9 @@ int auto_chunk_splits(const kvq_config& c, int nq) {
 
 constexpr int32_t kMaxChunk = 1024;
 
-// Longest cache (in quantized blocks per sequence) that a decode step takes in one launch.
-constexpr int64_t kStepOneLaunchBlocks = 8;
+// Longest cache (in quantized blocks per sequence) that a decode step takes in one launch:
+// one block per wave of its workgroup.  (With two per wave the split kernels are faster.)
+constexpr int64_t kStepOneLaunchBlocks = 4;
 
 }  // namespace
 
@@ -245,7 +246,8 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_ne
   const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
   if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
   // one launch while the cache is short enough that launches, not bandwidth, set the cost
-  const bool one_launch = num_splits == 0 && L1 / Bk <= kStepOneLaunchBlocks && kvq::decode_step_fits(c);
+  const bool one_launch =
+      num_splits == 0 && L1 / Bk <= kStepOneLaunchBlocks && kvq::decode_step_prefers_one_launch(*cache);
   hipStream_t s = (hipStream_t)stream;
   const uint16_t* kn = (const uint16_t*)k_new;
   const uint16_t* vn = (const uint16_t*)v_new;

@@ -63,8 +63,10 @@ __host__ __device__ inline int64_t row_visible(const RowSpec& rs, int j, int64_t
 // and the finish kernel, partials in ws.
 hipError_t launch_decode_step(const kvq_cache& c, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                               int jnew, float* out, float* ws, int splits, hipStream_t s);
-// Whether every query head of a kv head fits one workgroup of the one-launch step (host only).
-bool decode_step_fits(const kvq_config& c);
+// Whether a decode step on a short cache should take the one-launch kernel: every query
+// head of a kv head fits its workgroup, and no tuned split kernel covers the
+// configuration (host only).
+bool decode_step_prefers_one_launch(const kvq_cache& c);
 
 // Causal attention of a chunk of nq queries (the generic split kernel, or the
 // matrix-core kernel where it applies), partials merged by the finish kernel.

@@ -32,7 +32,7 @@ hipError_t launch_decode_step(const kvq_cache&, const uint16_t*, const uint16_t*
                               float*, int, hipStream_t) {
   return hipErrorNotSupported;
 }
-bool decode_step_fits(const kvq_config&) { return true; }
+bool decode_step_prefers_one_launch(const kvq_cache&) { return true; }
 }  // namespace kvq
 
 static int failures = 0;

@@ -6,9 +6,13 @@ From a cache of T0 tokens, N steps run token by token across a block boundary.  
 step's output must be within 2e-3 of the oracle's fp64 decode over a cache built from the
 first t + 1 tokens (the step's own token included), and after the last step the cache
 buffers must equal the oracle's bit for bit.  The same steps through kvq_quantize_append
-and kvq_decode_attention give the same outputs up to fp32 rounding.  Split count 0 takes
-the one-launch kernel for the short caches and the split kernels (tuned MHA or GQA, or
-generic) with the finish kernel for the long ones; split count 3 forces the latter.
+and kvq_decode_attention give the same outputs up to fp32 rounding.
+
+Split count 0 is the library's choice: the one-launch kernel for a short cache (at most
+four quantized blocks) in a configuration no tuned kernel covers (mha_k3, and gqa_d64
+until its fifth block, where it changes over), else the split kernels (tuned MHA or GQA,
+or the generic one for gqa_d64_long) and the finish kernel.  Split count 3 forces the
+split kernels.
 """
 import numpy as np
 import pytest
@@ -42,6 +46,10 @@ CASES = {
     "mha_long": (synth.config("c1", batch=1, q_heads=2, kv_heads=2, tokens=10 * 128 + 60, capacity=1408), 80),
     "gqa_long": (synth.config("c2", batch=1, q_heads=8, kv_heads=2, tokens=9 * 128 + 20, capacity=1280), 30),
     "d64_long": (synth.config("c0", tokens=9 * 64 + 10, capacity=640), 20),
+    # no tuned kernel: head_dim 64 with grouped queries, 3-bit uniform keys
+    "gqa_d64": (synth.config("c0", q_heads=8, kv_heads=2, tokens=5 * 64 + 30, capacity=384), 40),
+    "mha_k3": (synth.config("c1", batch=1, q_heads=2, kv_heads=2, k_bits=3, tokens=3 * 128 + 20, capacity=512), 30),
+    "gqa_d64_long": (synth.config("c0", q_heads=8, kv_heads=2, tokens=9 * 64 + 10, capacity=640), 20),
 }
 
 
@@ -110,3 +118,56 @@ def test_step_rejects_a_full_cache():
     with pytest.raises(kvq.KvqError):
         cache.step(k1, v1, q)
     assert cache.length == 128
+
+
+@pytest.mark.parametrize("case,splits", [("gqa_d64", 0), ("c0_tiny", 3)])
+def test_steps_replay_as_a_graph(case, splits):
+    """A run of steps captured as one HIP graph (a serving loop's use) and replayed three
+    times, the cache buffers restored to the run's starting state before each replay
+    (the steps overwrite tail slots the first steps read): every replay gives the eager
+    run's outputs bit for bit and leaves the same cache."""
+    import torch
+    cfg = CASES[case][0]
+    n = 80                                             # crosses a block boundary
+    T = cfg["tokens"]
+    T0 = T - n
+    B, H, Hq, D = cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
+    k, v = inputs(cfg)
+    qs = synth.gen_q_chunk(cfg, n)
+    kd, vd, qd = upload(k), upload(v), upload(qs)
+    toks = [(kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), qd[:, :, t - T0].contiguous())
+            for t in range(T0, T)]
+    eager = build_gpu_cache(cfg, k[:, :, :T0], v[:, :, :T0], None, _lut(cfg))
+    ref = torch.stack([eager.step(a, b, c, num_splits=splits) for a, b, c in toks])
+    torch.cuda.synchronize()
+    cache = build_gpu_cache(cfg, k[:, :, :T0], v[:, :, :T0], None, _lut(cfg))
+    cache.workspace(splits)
+    outs = torch.empty((n, B, Hq, D), dtype=torch.float32, device=kd.device)
+    start = {name: buf.clone() for name, buf in cache.bufs.items() if buf is not None}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+            for i, (a, b, c) in enumerate(toks):
+                cache.step(a, b, c, num_splits=splits, out=outs[i], stream=side)
+    assert cache.length == T
+    for r in range(3):
+        outs.fill_(float("nan"))
+        for name, buf in start.items():
+            cache.bufs[name].copy_(buf)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("replay", r, "max abs diff", float((outs - ref).abs().max()))
+        assert torch.equal(outs, ref), r
+        eager.decode(toks[-1][2])                      # eager work between replays
+        torch.cuda.synchronize()
+    import oracle
+    lut = _lut(cfg)
+    ko = oracle.kout(cfg)
+    for b in range(B):
+        for h in range(H):
+            hc = oracle.HeadCache(cfg, lut).build(k[b, h], v[b, h])
+            compare_head(cache, hc, cfg, ko, b, h)
