@@ -122,6 +122,28 @@ typedef struct {
  * Tokens [0, floor(length/Bk)*Bk) are quantized; the rest live in the tails.
  * At a quantized position that holds an outlier the stored code is 0; readers
  * use the CSR value there.
+ *
+ * Every buffer above except the tails, k_lut, rope and the row pointers is an array of
+ * per-block slots: block n of (b, h) is slot g = (b * kv_heads + h) * (T / Bk) + n, and
+ * the slot's part of a buffer is its Bk tokens' rows (k_codes, v_codes, v_scale,
+ * v_zero, k_col/k_val and v_col/v_val, the latter Bk * ko entries) or its D entries
+ * (k_scale, k_zero).
+ *
+ * Paged layout (block_table != NULL), for the continuous batching and paged cache
+ * management that [TQ] sections 5.2 and 5.3 name as the serving context of a quantized
+ * cache.  The quantized blocks of all sequences live in one pool of
+ * num_blocks physical blocks; sequence b's logical block n is physical block
+ * p = block_table[b * (T / Bk) + n], and its slot for kv head h is g = p * kv_heads + h
+ * (the buffers hold num_blocks * kv_heads slots; kvq_paged_layout gives their sizes).
+ * Each sequence has its own length: seq_lens (device, [batch]) is what the kernels read,
+ * seq_lens_host (host, [batch]) what the host sequences the launches by; the library
+ * advances both (the device copy stream-ordered).  `length` is unused.  The row
+ * pointers are per slot, [num_blocks * kv_heads][Bk + 1], local to the slot's Bk tokens.
+ * The tails stay per sequence, [batch][kv_heads][Bk][D].  T = capacity is the most
+ * tokens one sequence may hold (the table's row length is T / Bk).  The caller owns
+ * the table: every block a sequence holds (n < seq_lens[b] / Bk, and the blocks an
+ * append completes) must map to a distinct physical block; the kernels clamp an entry
+ * into [0, num_blocks), so a wrong table gives wrong results but no fault.
  */
 typedef struct {
   kvq_config cfg;
@@ -139,6 +161,11 @@ typedef struct {
   uint8_t *v_col;
   uint16_t *v_val;
   float *rope;
+  /* paged layout (see above); all NULL / 0 for the dense layout */
+  const int32_t *block_table;
+  int32_t num_blocks;
+  int64_t *seq_lens;
+  int64_t *seq_lens_host;
 } kvq_cache;
 
 /* Text for a status code (static storage; never NULL).  No passage of the pages defines
@@ -152,6 +179,12 @@ const char *kvq_status_string(kvq_status s);
  * kernels do not build.  The total follows the cache-size formula of [TQ] section 2.1
  * with the packed widths of [KVC3] "前言" (4 bits instead of 16). */
 kvq_status kvq_cache_layout(const kvq_config *cfg, kvq_layout *out);
+
+/* The buffer sizes of a paged cache whose pool holds num_blocks physical blocks (per
+ * slot as kvq_cache_layout's, times num_blocks * kv_heads slots; row pointers
+ * [slots][Bk + 1]; tails, k_lut and rope as in the dense layout).  Host only.
+ * KVQ_EINVAL also for num_blocks < 1 or num_blocks * kv_heads >= 2^31. */
+kvq_status kvq_paged_layout(const kvq_config *cfg, int32_t num_blocks, kvq_layout *out);
 
 /* Prepare an empty cache: validates the descriptor and its buffer pointers,
  * fills `rope` (angles evaluated in fp64) and sets length = 0.  Enqueued on `stream`.
@@ -168,6 +201,20 @@ kvq_status kvq_cache_init(kvq_cache *cache, void *stream);
  * enqueue time.  n_new == 0 is a no-op.  KVQ_ECAPACITY if length + n_new > capacity. */
 kvq_status kvq_quantize_append(kvq_cache *cache, const void *k_new, const void *v_new,
                                int64_t n_new, void *stream);
+
+/* Append a different number of tokens to each sequence of a cache with per-sequence
+ * lengths (seq_lens set; dense or paged): sequence b takes the first n_new_host[b]
+ * rows of k_new[b], v_new[b] (*device* fp16 [batch][kv_heads][n_max][head_dim], keys
+ * pre-RoPE; rows past a sequence's count are not read).  This is one step of continuous
+ * batching ([TQ] section 5.2): sequences in prefill take many tokens, sequences in
+ * decode one, finished ones none.  n_new_dev: *device* int64 [batch], equal to
+ * n_new_host (the kernels read it; the host copy sizes the launches).  Blocks are
+ * quantized and tails kept per sequence as in kvq_quantize_append; both length copies
+ * advance by the counts.  KVQ_EINVAL for a cache without per-sequence lengths, a count
+ * outside [0, n_max] or null pointers, KVQ_ECAPACITY if a sequence would exceed
+ * capacity (nothing is written then). */
+kvq_status kvq_quantize_append_seqs(kvq_cache *cache, const void *k_new, const void *v_new, int64_t n_max,
+                                    const int64_t *n_new_host, const int64_t *n_new_dev, void *stream);
 
 /* Bytes of device workspace kvq_decode_attention needs for `num_splits` splits of
  * the cache per (b, kv-head) (0 = the library's choice for this cache; at most

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ECAPACITY, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4, -5
 EXPORTED = ["kvq_status_string", "kvq_cache_layout", "kvq_cache_init", "kvq_quantize_append",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
-            "kvq_chunk_workspace_bytes", "kvq_chunk_attention", "kvq_decode_step", "kvq_dequantize"]
+            "kvq_chunk_workspace_bytes", "kvq_chunk_attention", "kvq_decode_step", "kvq_dequantize",
+            "kvq_paged_layout", "kvq_quantize_append_seqs"]
 NOALLOC_SCRATCH_BYTES = 16 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -43,7 +44,9 @@ class KvqLayout(C.Structure):
 
 
 class KvqCache(C.Structure):
-    _fields_ = [("cfg", KvqConfig), ("length", C.c_int64)] + [(n, C.c_void_p) for n in BUFFERS]
+    _fields_ = ([("cfg", KvqConfig), ("length", C.c_int64)] + [(n, C.c_void_p) for n in BUFFERS] +
+                [("block_table", C.c_void_p), ("num_blocks", C.c_int32), ("seq_lens", C.c_void_p),
+                 ("seq_lens_host", C.POINTER(C.c_int64))])
 
 
 class KvqError(RuntimeError):
@@ -68,6 +71,10 @@ def lib() -> C.CDLL:
         L.kvq_status_string.argtypes = [i32]
         L.kvq_cache_layout.restype = i32
         L.kvq_cache_layout.argtypes = [C.POINTER(KvqConfig), C.POINTER(KvqLayout)]
+        L.kvq_paged_layout.restype = i32
+        L.kvq_paged_layout.argtypes = [C.POINTER(KvqConfig), i32, C.POINTER(KvqLayout)]
+        L.kvq_quantize_append_seqs.restype = i32
+        L.kvq_quantize_append_seqs.argtypes = [C.POINTER(KvqCache), vp, vp, i64, C.POINTER(C.c_int64), vp, vp]
         L.kvq_cache_init.restype = i32
         L.kvq_cache_init.argtypes = [C.POINTER(KvqCache), vp]
         L.kvq_quantize_append.restype = i32
@@ -101,6 +108,23 @@ def kvq_cache_layout(cfg: KvqConfig) -> KvqLayout:
     if st != KVQ_OK:
         raise KvqError(st, "kvq_cache_layout")
     return out
+
+
+def kvq_paged_layout(cfg: KvqConfig, num_blocks: int) -> KvqLayout:
+    out = KvqLayout()
+    st = lib().kvq_paged_layout(C.byref(cfg), int(num_blocks), C.byref(out))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_paged_layout")
+    return out
+
+
+def kvq_quantize_append_seqs(cache: KvqCache, k_new, v_new, n_max: int, n_host, n_dev, stream=None) -> None:
+    """n_host: a ctypes int64 array of the per-sequence counts; n_dev: the same on the
+    device (an int64 tensor)."""
+    st = lib().kvq_quantize_append_seqs(C.byref(cache), _ptr(k_new), _ptr(v_new), int(n_max),
+                                        C.cast(n_host, C.POINTER(C.c_int64)), _ptr(n_dev), _stream(stream))
+    if st != KVQ_OK:
+        raise KvqError(st, "kvq_quantize_append_seqs")
 
 
 def _stream(stream) -> int:
@@ -201,13 +225,18 @@ class Cache:
     ``[kv_heads][D][2**k_bits]`` of fp16 bits, or None."""
 
     def __init__(self, cfg: dict, device="cuda", lut=None, stream=None):
-        import torch
         self.cfg = dict(cfg)
         self.cfg.setdefault("capacity", self.cfg["tokens"])
         self.c_cfg = make_config(self.cfg)
-        self.layout = kvq_cache_layout(self.c_cfg)
         self.desc = KvqCache()
         self.desc.cfg = self.c_cfg
+        self._alloc(kvq_cache_layout(self.c_cfg), device, lut)
+        kvq_cache_init(self.desc, stream)
+        self._ws = None
+
+    def _alloc(self, layout, device, lut) -> None:
+        import torch
+        self.layout = layout
         self.bufs = {}
         for name in BUFFERS:
             size = getattr(self.layout, name)
@@ -225,8 +254,6 @@ class Cache:
                 t = torch.zeros(size, dtype=torch.uint8, device=device)
                 self.bufs[name] = t
                 setattr(self.desc, name, t.data_ptr())
-        kvq_cache_init(self.desc, stream)
-        self._ws = None
 
     @property
     def length(self) -> int:
@@ -317,3 +344,81 @@ class Cache:
     def buffer(self, name: str):
         """The raw device buffer (uint8) of one layout entry."""
         return self.bufs.get(name)
+
+
+class PagedCache(Cache):
+    """A cache whose sequences each have their own length.  With ``block_table`` (int32
+    ``[batch][capacity / k_block]`` on the device: the physical block of each logical
+    block) the quantized blocks live in a pool of ``num_blocks`` physical blocks (the
+    paged layout); without it the buffers keep the dense per-sequence slots.  The table
+    is read at every call, so the caller may rewrite it in place between calls (a
+    serving loop's block allocator); every block a sequence holds or an append completes
+    must map to its own physical block."""
+
+    def __init__(self, cfg: dict, num_blocks: int | None = None, block_table=None, device="cuda", lut=None,
+                 stream=None):
+        import torch
+        self.cfg = dict(cfg)
+        self.cfg.setdefault("capacity", self.cfg["tokens"])
+        self.c_cfg = make_config(self.cfg)
+        self.desc = KvqCache()
+        self.desc.cfg = self.c_cfg
+        B = self.cfg["batch"]
+        if block_table is not None:
+            nb = self.cfg["capacity"] // self.cfg["k_block"]
+            _check_tensor(block_table, "block_table", (B, nb), torch.int32, torch.device(device))
+            if num_blocks is None:
+                raise ValueError("a block table needs num_blocks")
+            layout = kvq_paged_layout(self.c_cfg, num_blocks)
+            self.block_table = block_table
+            self.desc.block_table = block_table.data_ptr()
+            self.desc.num_blocks = int(num_blocks)
+        else:
+            layout = kvq_cache_layout(self.c_cfg)
+            self.block_table = None
+        self._alloc(layout, device, lut)
+        self.seq_lens_dev = torch.zeros(B, dtype=torch.int64, device=device)
+        self._seq_lens_host = (C.c_int64 * B)()
+        self.desc.seq_lens = self.seq_lens_dev.data_ptr()
+        self.desc.seq_lens_host = C.cast(self._seq_lens_host, C.POINTER(C.c_int64))
+        kvq_cache_init(self.desc, stream)
+        self._ws = None
+
+    @property
+    def lengths(self) -> list:
+        return [int(x) for x in self._seq_lens_host]
+
+    @property
+    def length(self) -> int:
+        raise AttributeError("a PagedCache has one length per sequence: use .lengths")
+
+    def append_seqs(self, k_new, v_new, counts, stream=None) -> None:
+        """Sequence b takes the first counts[b] rows of k_new[b], v_new[b] (fp16
+        [B][Hkv][n_max][D] on the device, keys pre-RoPE)."""
+        import torch
+        B, H, D = self.cfg["batch"], self.cfg["kv_heads"], self.cfg["head_dim"]
+        if k_new.dim() != 4:
+            raise ValueError("k_new must be [B][Hkv][n_max][D]")
+        n_max = k_new.shape[2]
+        _check_tensor(k_new, "k_new", (B, H, n_max, D), torch.float16, self.device)
+        _check_tensor(v_new, "v_new", (B, H, n_max, D), torch.float16, self.device)
+        counts = [int(x) for x in counts]
+        if len(counts) != B:
+            raise ValueError("one count per sequence")
+        n_host = (C.c_int64 * B)(*counts)
+        n_dev = torch.tensor(counts, dtype=torch.int64, device=self.device)
+        kvq_quantize_append_seqs(self.desc, k_new, v_new, n_max, n_host, n_dev, stream)
+        self._last_counts = n_dev   # kept alive until the stream has read it
+
+    def decode(self, q, num_splits: int = 0, out=None, stream=None):
+        """Every sequence's query (fp16 [B][Hq][D], pre-RoPE) at its own newest token.
+        Returns fp32 [B][Hq][D]."""
+        import torch
+        shape = (self.cfg["batch"], self.cfg["q_heads"], self.cfg["head_dim"])
+        _check_tensor(q, "q", shape, torch.float16, self.device)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=q.device)
+        _check_tensor(out, "out", shape, torch.float32, self.device)
+        ws = self.workspace(num_splits)
+        kvq_decode_attention(self.desc, q, -1, out, ws, ws.numel(), num_splits, stream)
+        return out

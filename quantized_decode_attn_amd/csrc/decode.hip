@@ -110,9 +110,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, GQ = Hq / H, R = GQ * rs.nq;
   const int G = c.cfg.v_group, ng = D / G;
   const int ko = kout_of(c.cfg);
-  const int64_t T = c.cfg.capacity;
-  const int64_t nfull = c.length / Bk;
-  const int ntail = (int)(c.length - nfull * Bk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
 
@@ -145,6 +142,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     const int64_t bh = rest / rs.nsets;
     const int h = (int)(bh % H);
     const int b = (int)(bh / H);
+    // the sequence's length (its own in a cache with per-sequence lengths), and the
+    // position of its first query (q_pos < 0: the newest token)
+    const int64_t len_b = seq_len_of(c, b);
+    const int64_t nfull = len_b / Bk;
+    const int ntail = (int)(len_b - nfull * Bk);
+    const int64_t qbase = rs.q_pos < 0 ? len_b - 1 : rs.q_pos;
     const int row0 = set * rs.rpi;
     const int nrows = R - row0 < rs.rpi ? R - row0 : rs.rpi;
     const int64_t n0 = nfull * split / S, n1 = nfull * (split + 1) / S;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     // the widest view of the set's rows: no later token is visible to any of them
     int64_t vmax = 0;
     for (int g = 0; g < nrows; ++g) {
-      const int64_t v = row_visible(rs, (row0 + g) % rs.nq, c.length);
+      const int64_t v = row_visible(rs, (row0 + g) % rs.nq, len_b);
       vmax = v > vmax ? v : vmax;
     }
 
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     for (int g = 0; g < nrows; ++g) {
       const int row = row0 + g, qj = row % rs.nq;
       const uint16_t* qv = q + (((int64_t)b * Hq + (int64_t)h * GQ + row / rs.nq) * rs.nq + qj) * D;
-      const int64_t pos = rs.q_pos + qj;
+      const int64_t pos = qbase + qj;
       for (int i = lane; i < Sh::HALF; i += kWave) {
         const double qa = (double)h2f(qv[i]), qb = (double)h2f(qv[i + Sh::HALF]);
         const double f = pow((double)c.cfg.rope_theta, -(2.0 * i) / (double)D);
@@ -179,9 +182,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     }
     wave_lds_sync();
 
-    const uint8_t* kcodes = static_cast<const uint8_t*>(c.k_codes) + bh * T * (D * KB / 8);
-    const uint32_t* vwords = static_cast<const uint32_t*>(c.v_codes) + bh * (T / Sh::TPW) * D;
-
     const int64_t nblocks = (n1 - n0) + (do_tail ? 1 : 0);
     for (int64_t bi = 0; bi < nblocks; ++bi) {
       const bool tail = bi == n1 - n0;
@@ -190,11 +190,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       if (tb >= vmax) break;                             // past every row's view (blocks ascend)
       const int ntok = tail ? ntail : Bk;
       const int iters = (ntok + Sh::TPI - 1) / Sh::TPI;
+      // the quantized block's slot (slot_of), its codes and value words
+      const int64_t gs = tail ? 0 : slot_of(c, b, h, n);
+      const uint8_t* kblk = static_cast<const uint8_t*>(c.k_codes) + gs * Bk * (D * KB / 8);
+      const uint32_t* vblk = static_cast<const uint32_t*>(c.v_codes) + gs * (Bk / Sh::TPW) * D;
 
       // value metadata of the block (quantized blocks only)
       if (!tail) {
         for (int k = lane; k < Bk * ng; k += kWave) {
-          const int64_t m = (bh * T + tb) * ng + k;
+          const int64_t m = gs * Bk * ng + k;
           VS[k] = h2f(c.v_scale[m]);
           VZ[k] = h2f(c.v_zero[m]);
         }
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
 
       for (int g = 0; g < nrows; ++g) {
         // tokens of this block the row sees (a causal row may see none or a prefix)
-        const int64_t seen = row_visible(rs, (row0 + g) % rs.nq, c.length) - tb;
+        const int64_t seen = row_visible(rs, (row0 + g) % rs.nq, len_b) - tb;
         if (seen <= 0) continue;
         const int nvis = seen < ntok ? (int)seen : ntok;
         float* st = state + g * (D + 2 + ng);
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
           const float wr = qr * cb - qi * sb, wi = qr * sb + qi * cb;
           float* o = wts + i * Sh::NW;
           if (KMODE == 0 && !tail) {
-            const int64_t m = (bh * (T / Bk) + n) * D;
+            const int64_t m = gs * D;
             const float al = h2f(c.k_scale[m + i]), be = h2f(c.k_scale[m + i + Sh::HALF]);
             const float za = h2f(c.k_zero[m + i]), zb = h2f(c.k_zero[m + i + Sh::HALF]);
             o[0] = wr * al;
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
             if (!tail) {
               uint32_t w[Sh::KW];
               const uint32_t* src = reinterpret_cast<const uint32_t*>(
-                  kcodes + (tb + j) * (D * KB / 8) + r * (Sh::KW * 4));
+                  kblk + j * (D * KB / 8) + r * (Sh::KW * 4));
 #pragma unroll
               for (int k = 0; k < Sh::KW; ++k) w[k] = src[k];
 #pragma unroll
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
               }
               // outlier corrections: code 0 was stored there, the CSR holds the value
               if (r < ko) {
-                const int64_t e = (bh * T + tb + j) * ko + r;
+                const int64_t e = (gs * Bk + j) * ko + r;
                 const int col = c.k_col[e];
                 const float xo = h2f(c.k_val[e]);
                 const int i = col % Sh::HALF;
@@ -339,12 +343,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
             if (lane == 0) st[2 + D + gg] = st[2 + D + gg] * alpha + z;
           }
           wave_lds_sync();
-          const int64_t wbase = tb / Sh::TPW;
           for (int gw = 0; gw < Bk / Sh::TPW; ++gw) {
 #pragma unroll
             for (int k = 0; k < Sh::CPL; ++k) {
               const int ch = lane + k * kWave;
-              const uint32_t word = vwords[(wbase + gw) * D + ch];
+              const uint32_t word = vblk[gw * D + ch];
               const int grp = ch / G;
 #pragma unroll
               for (int u = 0; u < Sh::TPW; ++u) {
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
             for (int it = 0; it < iters; ++it) {
               const int j = it * Sh::TPI + ts;
               if (r < ko) {
-                const int64_t e = (bh * T + tb + j) * ko + r;
+                const int64_t e = (gs * Bk + j) * ko + r;
                 const int col = c.v_col[e];
                 const float dlt = h2f(c.v_val[e]) - VZ[j * ng + col / G];
                 VC[ts * D + col] += Pl[j] * dlt;
@@ -472,11 +475,12 @@ __global__ __launch_bounds__(256) void decode_finish_kernel(kvq_cache c, const u
   const int64_t bhq = bq / rs.nq;
   const int b = (int)(bhq / Hq), hq = (int)(bhq % Hq), h = hq / gq;
   const int64_t bh = (int64_t)b * H + h;
-  const int64_t q_pos = rs.q_pos + qj;
-  const int64_t nfull = c.length / Bk;
-  int ntail = with_tail ? (int)(c.length - nfull * Bk) : 0;
+  const int64_t len_b = seq_len_of(c, b);
+  const int64_t q_pos = (rs.q_pos < 0 ? len_b - 1 : rs.q_pos) + qj;
+  const int64_t nfull = len_b / Bk;
+  int ntail = with_tail ? (int)(len_b - nfull * Bk) : 0;
   if (ntail > 0) {  // the tail tokens this row sees
-    const int64_t seen = row_visible(rs, qj, c.length) - nfull * Bk;
+    const int64_t seen = row_visible(rs, qj, len_b) - nfull * Bk;
     ntail = seen <= 0 ? 0 : (seen < ntail ? (int)seen : ntail);
   }
   const int tid = threadIdx.x;
@@ -661,11 +665,12 @@ __global__ __launch_bounds__(256) void decode_finish_tail_kernel(kvq_cache c, co
   const int64_t bhq = bq / rs.nq;
   const int b = (int)(bhq / Hq), hq = (int)(bhq % Hq), h = hq / gq;
   const int64_t bh = (int64_t)b * H + h;
-  const int64_t q_pos = rs.q_pos + qj;
-  const int64_t nfull = c.length / Bk;
-  int ntail = (int)(c.length - nfull * Bk);
+  const int64_t len_b = seq_len_of(c, b);
+  const int64_t q_pos = (rs.q_pos < 0 ? len_b - 1 : rs.q_pos) + qj;
+  const int64_t nfull = len_b / Bk;
+  int ntail = (int)(len_b - nfull * Bk);
   {
-    const int64_t seen = row_visible(rs, qj, c.length) - nfull * Bk;
+    const int64_t seen = row_visible(rs, qj, len_b) - nfull * Bk;
     ntail = seen <= 0 ? 0 : (seen < ntail ? (int)seen : ntail);
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -693,7 +698,7 @@ __global__ __launch_bounds__(256) void decode_finish_tail_kernel(kvq_cache c, co
   float eb0 = 0.0f, eb1 = 0.0f, pc = 0.0f, ps = 0.0f, po0 = 0.0f, po1 = 0.0f;
   // inside the capacity, e^{i f q_pos} = e^{i f nb Bk} e^{i f jq} from the fp64-built tables
   const bool qtab = q_pos < c.cfg.capacity;
-  if (tid < HALF) {
+  if (tid < HALF && ntail > 0) {  // (nfull < T / Bk when there is a tail)
     const uint16_t* qv = q + bq * D;
     qa = (double)h2f(qv[tid]);
     qb = (double)h2f(qv[tid + HALF]);
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(256) void decode_finish_tail_kernel(kvq_cache c, co
 
   // ---- query weights: scale * conj(q) e^{-i f q_pos} (fp64 angle), times the tail
   // block's base rotation e^{i f nfull Bk}
-  if (tid < HALF) {
+  if (tid < HALF && ntail > 0) {
     double sn, cs;
     if (qtab) {
       cs = (double)(pc * po0 - ps * po1);
@@ -811,7 +816,9 @@ __global__ __launch_bounds__(256) void decode_finish_tail_kernel(kvq_cache c, co
 hipError_t launch_finish(const kvq_cache& c, const uint16_t* q, RowSpec rs, const float* ws, float* out, int S,
                          int with_tail, StepToken nt, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)c.cfg.batch * c.cfg.q_heads * rs.nq));
-  const bool tail = with_tail && c.length % c.cfg.k_block != 0;
+  // with per-sequence lengths any sequence may have a tail (a row without one merges
+  // its splits alone)
+  const bool tail = with_tail && (c.seq_lens || c.length % c.cfg.k_block != 0);
   if (tail && S <= kFinishFastSplits && c.cfg.k_block <= 128) {
     if (c.cfg.head_dim == 128)
       hipLaunchKernelGGL(decode_finish_tail_kernel<128>, grid, dim3(256), 0, s, c, q, rs, ws, out, S, nt);

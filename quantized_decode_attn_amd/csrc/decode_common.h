@@ -100,19 +100,20 @@ struct BlockRegs {
   uint2 kval, vval;       // (bytes lane*8..)
 };
 
-// Loaders of the pieces of block n, each into its own register slot, so that a
+// Loaders of the pieces of one block, each into its own register slot, so that a
 // slot can be refilled with the next block as soon as it has been consumed.  Every
-// address is a wave-uniform block base plus a 32-bit lane offset.
+// address is a wave-uniform block base plus a 32-bit lane offset.  A block is named by
+// its slot g (slot_of: the same in the dense and the paged layout); the rotary block
+// base takes its position n.
 template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ const uint8_t* k_block(const kvq_cache& c, int64_t bh, int64_t n) {
+__device__ __forceinline__ const uint8_t* k_block(const kvq_cache& c, int64_t g) {
   using Sh = MShape<D, BK, KB, VB>;
-  return static_cast<const uint8_t*>(c.k_codes) + (bh * c.cfg.capacity + n * BK) * Sh::RK;
+  return static_cast<const uint8_t*>(c.k_codes) + g * BK * Sh::RK;
 }
 template <int D, int BK, int KB, int VB>
-__device__ __forceinline__ const uint8_t* v_block(const kvq_cache& c, int64_t bh, int64_t n) {
+__device__ __forceinline__ const uint8_t* v_block(const kvq_cache& c, int64_t g) {
   using Sh = MShape<D, BK, KB, VB>;
-  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) +
-                                          (bh * (c.cfg.capacity / Sh::TPW) + n * (BK / Sh::TPW)) * D);
+  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) + g * (BK / Sh::TPW) * D);
 }
 
 // Key codes of iteration `it` of a block into slot `slot`.
@@ -145,12 +146,11 @@ __device__ __forceinline__ void load_v(BlockRegs<D, BK, KB, VB, KS, PPL>& R, int
 }
 
 template <int D, int BK, int KB, int VB, int KS, int PPL>
-__device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R, const kvq_cache& c, int64_t bh, int64_t n,
+__device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R, const kvq_cache& c, int64_t g, int64_t n,
                                            int lane, int ko) {
   using Sh = MShape<D, BK, KB, VB>;
-  const int64_t T = c.cfg.capacity;
   if (lane < Sh::HALF) {
-    const int64_t m = (bh * (T / BK) + n) * D;
+    const int64_t m = g * D;
     const uint16_t* ks = c.k_scale + m;
     const uint16_t* kz = c.k_zero + m;
     R.kmeta[0] = ks[lane];
@@ -163,7 +163,7 @@ __device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R,
   }
   if (ko > 0) {
     const int nb = BK * ko;
-    const int64_t e0 = (bh * T + n * BK) * ko;
+    const int64_t e0 = g * BK * ko;
     if (lane * 4 < nb) {
       R.kcol = reinterpret_cast<const uint32_t*>(c.k_col + e0)[lane];
       R.vcol = reinterpret_cast<const uint32_t*>(c.v_col + e0)[lane];
@@ -176,10 +176,10 @@ __device__ __forceinline__ void load_kmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R,
 // Outlier CSR slice of block n: entries 4*lane .. 4*lane+3 (columns and values of
 // the key and the value outliers); BK * ko <= 256.
 template <int D, int BK, int KB, int VB, int KS, int PPL>
-__device__ __forceinline__ void load_csr(BlockRegs<D, BK, KB, VB, KS, PPL>& R, const kvq_cache& c, int64_t bh,
-                                         int64_t n, int lane, int ko) {
+__device__ __forceinline__ void load_csr(BlockRegs<D, BK, KB, VB, KS, PPL>& R, const kvq_cache& c, int64_t g,
+                                         int lane, int ko) {
   const int nb = BK * ko;
-  const int64_t e0 = (bh * c.cfg.capacity + n * BK) * ko;
+  const int64_t e0 = g * BK * ko;
   if (lane * 4 < nb) {
     R.kcol = reinterpret_cast<const uint32_t*>(c.k_col + e0)[lane];
     R.vcol = reinterpret_cast<const uint32_t*>(c.v_col + e0)[lane];
@@ -189,11 +189,10 @@ __device__ __forceinline__ void load_csr(BlockRegs<D, BK, KB, VB, KS, PPL>& R, c
 }
 
 template <int D, int BK, int KB, int VB, int KS, int PPL>
-__device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R, const kvq_cache& c, int64_t bh, int64_t n,
+__device__ __forceinline__ void load_vmeta(BlockRegs<D, BK, KB, VB, KS, PPL>& R, const kvq_cache& c, int64_t g,
                                            int lane, int ng) {
-  const int64_t T = c.cfg.capacity;
   const int ne = BK * ng;
-  const int64_t m0 = (bh * T + n * BK) * ng;
+  const int64_t m0 = g * BK * ng;
   const uint16_t* vs = c.v_scale + m0;
   const uint16_t* vz = c.v_zero + m0;
   // every load is issued (an element past the block's ne reads element 0, and its
@@ -274,9 +273,9 @@ struct CsrTok {
   uint32_t kc[2], kv[2], vc[2], vv[2];
 };
 template <int BK, int KO>
-__device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
+__device__ __forceinline__ void load_csr_tok(CsrTok& C, const kvq_cache& c, int64_t g, int lane) {
   static_assert(KO == 1 || KO == 2, "one or two outliers per vector");
-  const int64_t e0 = (bh * c.cfg.capacity + n * BK) * KO;
+  const int64_t e0 = g * BK * KO;
 #pragma unroll
   for (int k = 0; k < BK / kWave; ++k) {
     const int t = lane + kWave * k;

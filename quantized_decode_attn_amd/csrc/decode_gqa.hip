@@ -88,14 +88,14 @@ struct GRegs {
   uint16_t vs[4], vz[4];  // value scale/zero of elements lane + 64 k ([group][token])
 };
 
-__device__ __forceinline__ const uint8_t* gk_block(const kvq_cache& c, int64_t bh, int64_t n) {
-  return static_cast<const uint8_t*>(c.k_codes) + (bh * c.cfg.capacity + n * kBK) * (kD / 2);
+// Block pieces by slot g (slot_of); the rotary block base by position n.
+__device__ __forceinline__ const uint8_t* gk_block(const kvq_cache& c, int64_t g) {
+  return static_cast<const uint8_t*>(c.k_codes) + g * kBK * (kD / 2);
 }
 template <int VB>
-__device__ __forceinline__ const uint8_t* gv_block(const kvq_cache& c, int64_t bh, int64_t n) {
+__device__ __forceinline__ const uint8_t* gv_block(const kvq_cache& c, int64_t g) {
   constexpr int TPW = 32 / VB;
-  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) +
-                                          (bh * (c.cfg.capacity / TPW) + n * (kBK / TPW)) * kD);
+  return reinterpret_cast<const uint8_t*>(static_cast<const uint32_t*>(c.v_codes) + g * (kBK / TPW) * kD);
 }
 // Key row slot q (16 bytes) of half hf: token 64 hf + lane.
 template <int VB>
@@ -114,8 +114,8 @@ __device__ __forceinline__ void gload_v(GRegs<VB>& R, int s, const uint8_t* vblk
   R.v[s] = *reinterpret_cast<const uint4*>(vblk + (tg * kD + 64 * hc + 4 * (lane & 15)) * 4u);
 }
 template <int VB>
-__device__ __forceinline__ void gload_kmeta(GRegs<VB>& R, const kvq_cache& c, int64_t bh, int64_t n, int lane) {
-  const int64_t m = (bh * (c.cfg.capacity / kBK) + n) * kD;
+__device__ __forceinline__ void gload_kmeta(GRegs<VB>& R, const kvq_cache& c, int64_t g, int64_t n, int lane) {
+  const int64_t m = g * kD;
   R.kmeta[0] = c.k_scale[m + lane];
   R.kmeta[1] = c.k_scale[m + lane + kHalf];
   R.kmeta[2] = c.k_zero[m + lane];
@@ -125,9 +125,8 @@ __device__ __forceinline__ void gload_kmeta(GRegs<VB>& R, const kvq_cache& c, in
   R.eb_s = eb.y;
 }
 template <int VB>
-__device__ __forceinline__ void gload_vmeta(GRegs<VB>& R, const kvq_cache& c, int64_t bh, int64_t n, int lane,
-                                            int ng) {
-  const int64_t m0 = (bh * c.cfg.capacity + n * kBK) * ng;
+__device__ __forceinline__ void gload_vmeta(GRegs<VB>& R, const kvq_cache& c, int64_t g, int lane, int ng) {
+  const int64_t m0 = g * kBK * ng;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (kWave * k < kBK * ng) {
@@ -171,15 +170,16 @@ __device__ __forceinline__ int tau(int q, int m) {
   return VB == 4 ? 8 * (q >> 1) + (q & 1) + 2 * m : q + 4 * m;
 }
 
-template <int VB, int KO, int NG>
+template <int VB, int KO, int NG, bool PG>
 __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, float* __restrict__ wl, const GLds& L,
                                           const float* __restrict__ table, int lane, int G, int ng,
-                                          const kvq_cache& c, int64_t bh, int64_t n, int nstep, bool more) {
+                                          const kvq_cache& c, int64_t b, int64_t h, int64_t n, int nstep, bool more) {
   constexpr bool OUTL = KO > 0;
   constexpr int TPW = 32 / VB;
   const int64_t nn = more ? n + nstep : n;
-  const uint8_t* knext = gk_block(c, bh, nn);
-  const uint8_t* vnext = gv_block<VB>(c, bh, nn);
+  const int64_t gs = slot_t<PG>(c, b, h, n), gnn = more ? slot_t<PG>(c, b, h, nn) : gs;
+  const uint8_t* knext = gk_block(c, gnn);
+  const uint8_t* vnext = gv_block<VB>(c, gnn);
   float* Meta = wl + L.meta;
   float* WA = wl + L.wa;
   uint32_t* W32 = reinterpret_cast<uint32_t*>(wl + L.w32);  // [group][head][half][lane]
@@ -191,8 +191,8 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   // so they are loaded here rather than a block ahead.  Loads still in flight at the
   // block's end would be drained there (the counter is in order, so waiting for them
   // waits for the next block's code loads too).
-  gload_vmeta(R, c, bh, n, lane, NG);
-  if constexpr (OUTL) load_csr_tok<kBK, KO>(C, c, bh, n, lane);
+  gload_vmeta(R, c, gs, lane, NG);
+  if constexpr (OUTL) load_csr_tok<kBK, KO>(C, c, gs, lane);
 
   // ---- per-pair dequantization constants and block-rotated query weights (pair = lane)
   {
@@ -208,7 +208,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
       *reinterpret_cast<float2*>(WA + g * kWAP + 2 * lane) =
           make_float2(wq_r[g] * R.eb_c - wq_i[g] * R.eb_s, -(wq_r[g] * R.eb_s + wq_i[g] * R.eb_c));  // W_r, -W_i
   }
-  gload_kmeta(R, c, bh, nn, lane);
+  gload_kmeta(R, c, gnn, nn, lane);
   wave_lds_sync();
 
   // ---- scores: lane owns tokens lane and 64 + lane; per key channel and token half
@@ -492,7 +492,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 
 // Item = (b, kv-head, head set, split): the wave serves GW (4 or 2) query heads of the
 // group; with 2 the MFMA rows of heads 2 and 3 carry zero weights.
-template <int VB, int GW, int KO, int NG>
+template <int VB, int GW, int KO, int NG, bool PG>
 __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
                                                                    int64_t nitems) {
@@ -501,7 +501,6 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
   extern __shared__ float lds[];
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, gq = Hq / H, nsets = gq / GW;
   const int G = c.cfg.v_group;
-  const int64_t nfull = c.length / kBK;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -524,6 +523,10 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     const int64_t bh = rest / nsets;
     const int h = (int)(bh % H);
     const int b = (int)(bh / H);
+    // the sequence's own length and newest position in a cache with per-sequence lengths
+    const int64_t len_b = seq_len_t<PG>(c, b);
+    const int64_t nfull = len_b / kBK;
+    const int64_t qp = q_pos < 0 ? len_b - 1 : q_pos;
     // split `split` takes blocks split, split + S, ...: the waves of a workgroup hold
     // consecutive splits, so together they stream neighbouring blocks
     const int64_t n0 = split;
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     {
       const double f = pow((double)c.cfg.rope_theta, -(2.0 * lane) / (double)kD);
       double sn, cs;
-      sincos((double)q_pos * f, &sn, &cs);
+      sincos((double)qp * f, &sn, &cs);
       const double scl = (double)kLog2e / sqrt((double)kD);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -564,9 +567,10 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
     GRegs<VB> R;
     CsrTok C;
     if (n0 < nfull) {
-      gload_kmeta(R, c, bh, n0, lane);
-      const uint8_t* kb0 = gk_block(c, bh, n0);
-      const uint8_t* vb0 = gv_block<VB>(c, bh, n0);
+      const int64_t g0 = slot_t<PG>(c, b, h, n0);
+      gload_kmeta(R, c, g0, n0, lane);
+      const uint8_t* kb0 = gk_block(c, g0);
+      const uint8_t* vb0 = gv_block<VB>(c, g0);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -575,7 +579,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
       for (int s = 0; s < GRegs<VB>::NVI; ++s) gload_v(R, s, vb0, lane);
     }
     for (int64_t n = n0; n < nfull; n += S)
-      gqa_block<VB, KO, NG>(R, C, st, wl, L, table, lane, G, NG, c, bh, n, S, n + S < nfull);
+      gqa_block<VB, KO, NG, PG>(R, C, st, wl, L, table, lane, G, NG, c, b, h, n, S, n + S < nfull);
 
     if (OUTL) {  // the item's last block of value corrections
       merge_vcorr_heads(reinterpret_cast<int*>(wl + L.vcorr), st, lane);
@@ -610,21 +614,21 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
   }
 }
 
-template <int VB, int GW, int KO, int NG>
+template <int VB, int GW, int KO, int NG, bool PG>
 hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S, hipStream_t s,
                             int cus, bool dry) {
   const GLds L = gqa_lds(NG, KO > 0);
   const size_t bytes = ((size_t)kBK * kTP + (size_t)kGqaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
   if (dry) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO, NG>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO, NG, PG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int gq = c.cfg.q_heads / c.cfg.kv_heads;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * (gq / GW) * S;
   int64_t grid = (nitems + kGqaWaves - 1) / kGqaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_gqa_kernel<VB, GW, KO, NG>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes, s, c, q,
+  hipLaunchKernelGGL((decode_gqa_kernel<VB, GW, KO, NG, PG>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes, s, c, q,
                      q_pos, ws, S, nitems);
   return hipGetLastError();
 }
@@ -643,9 +647,13 @@ hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_po
       g.k_block != kBK || (g.v_bits != 4 && g.v_bits != 2))
     return hipErrorNotSupported;
   const bool four = gq % 4 == 0;
-#define KVQ_GQA_NG(vb, gw, ko)                                                                \
-  return ng == 2 ? launch_gqa_typed<vb, gw, ko, 2>(c, q, q_pos, ws, S, s, cus, dry)                \
-                 : launch_gqa_typed<vb, gw, ko, 1>(c, q, q_pos, ws, S, s, cus, dry);
+  // per-sequence lengths (dense or paged slots): a kernel of their own
+#define KVQ_GQA_NG(vb, gw, ko)                                                                     \
+  if (c.seq_lens)                                                                                  \
+    return ng == 2 ? launch_gqa_typed<vb, gw, ko, 2, true>(c, q, q_pos, ws, S, s, cus, dry)         \
+                   : launch_gqa_typed<vb, gw, ko, 1, true>(c, q, q_pos, ws, S, s, cus, dry);        \
+  return ng == 2 ? launch_gqa_typed<vb, gw, ko, 2, false>(c, q, q_pos, ws, S, s, cus, dry)          \
+                 : launch_gqa_typed<vb, gw, ko, 1, false>(c, q, q_pos, ws, S, s, cus, dry);
 #define KVQ_GQA(vb, gw)                                                                       \
   if (g.v_bits == vb && four == (gw == 4)) {                                                  \
     if (ko == 2) { KVQ_GQA_NG(vb, gw, 2) }                                                    \

@@ -141,20 +141,21 @@ __device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, V
   }
 }
 
-template <int D, int BK, int KB, int VB, int KO, bool LUT>
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG>
 __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTok& C, MState& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               const uint32_t* __restrict__ ptab, float wq_r, float wq_i,
                                               float inv_unit, int lane, int ts, int r, uint32_t sh, int G, int ng,
-                                              const kvq_cache& c, int64_t bh, int64_t n, int nstep, bool more,
+                                              const kvq_cache& c, int64_t b, int64_t h, int64_t n, int nstep, bool more,
                                               uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
   constexpr bool OUTL = KO > 0;
   static_assert(!(LUT && OUTL), "codebook keys with outliers take the generic kernel");
   constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
   const int64_t nn = more ? n + nstep : n;
-  const uint8_t* knext = k_block<D, BK, KB, VB>(c, bh, nn);
-  const uint8_t* vnext = v_block<D, BK, KB, VB>(c, bh, nn);
+  const int64_t g = slot_t<PG>(c, b, h, n), gnn = more ? slot_t<PG>(c, b, h, nn) : g;
+  const uint8_t* knext = k_block<D, BK, KB, VB>(c, gnn);
+  const uint8_t* vnext = v_block<D, BK, KB, VB>(c, gnn);
   // this block's weights were written during the previous block (or at the item's start)
   float* wA1 = wl + L.wts;
   float* wB1 = wA1 + Sh::HALF;
@@ -174,12 +175,12 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   // so they are loaded here rather than a block ahead (the loads then never stay in
   // flight across the block loop, which would make the compiler drain every load
   // before the next block)
-  load_vmeta(R, c, bh, n, lane, ng);
-  if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, bh, n, lane);
+  load_vmeta(R, c, g, lane, ng);
+  if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, g, lane);
 
   // ---- the next block's metadata (its weights are written during this block's values)
   if constexpr (LUT) load_eb(R, c, nn, lane);
-  else load_kmeta(R, c, bh, nn, lane, 0);
+  else load_kmeta(R, c, gnn, nn, lane, 0);
   wave_lds_sync();
   float A1[8], B1[8], Z1[8], A2[8], B2[8], Z2[8];
   if constexpr (LUT) {
@@ -527,7 +528,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 
 // One (b, head, split) item on one wave: every full block of the split, then the
 // split's (m, l, o) to the workspace.
-template <int D, int BK, int KB, int VB, int KO, bool LUT>
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG>
 __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __restrict__ q, int64_t q_pos,
                                          float* __restrict__ ws, int S, int64_t bh, int split, float* wl,
                                          const MLds& L, const float* table, const uint32_t* ptab, int lane) {
@@ -535,15 +536,18 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   constexpr bool OUTL = KO > 0;
   const int H = c.cfg.kv_heads;
   const int G = c.cfg.v_group, ng = D / G;
-  const int64_t nfull = c.length / BK;
+  const int h = (int)(bh % H);
+  const int b = (int)(bh / H);
+  // the sequence's own length and newest position in a cache with per-sequence lengths
+  const int64_t len_b = seq_len_t<PG>(c, b);
+  const int64_t nfull = len_b / BK;
+  if (q_pos < 0) q_pos = len_b - 1;
   const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
   // 3-bit rows: the lane's 48 bits start at byte 6 r, loaded from the dword below
   const uint32_t koff = KB == 3 ? (uint32_t)(ts * Sh::RK + ((6 * r) & ~3)) : (uint32_t)(ts * Sh::RK + r * (Sh::KW * 4));
   const uint32_t sh = KB == 3 ? (uint32_t)(((6 * r) & 3) * 8) : 0u;
   const uint32_t* pt = LUT ? ptab + r * 8 * PairTab<KB>::PITCH : nullptr;
   const float inv_unit = 1.0f / cvt_lo(1u).x;  // fp8 value of the byte 1
-  const int h = (int)(bh % H);
-  const int b = (int)(bh / H);
   // split `split` takes blocks split, split + S, split + 2 S, ...: the waves of a
   // workgroup hold consecutive splits of one head, so at any time they stream
   // neighbouring blocks (contiguous runs of HBM rather than S scattered streams)
@@ -570,19 +574,20 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   BlockRegs<D, BK, KB, VB> R;
   CsrTok C;
   if (n0 < nfull) {
+    const int64_t g0 = slot_t<PG>(c, b, h, n0);
     if constexpr (LUT) load_eb(R, c, n0, lane);
-    else load_kmeta(R, c, bh, n0, lane, 0);
+    else load_kmeta(R, c, g0, n0, lane, 0);
     write_block_weights<D, BK, KB, VB, KO, LUT>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
-    const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, bh, n0);
-    const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, bh, n0);
+    const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, g0);
+    const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, g0);
 #pragma unroll
     for (int it = 0; it < Sh::NIT; ++it) load_codes(R, it, kb0, koff);
 #pragma unroll
     for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
   }
   for (int64_t n = n0; n < nfull; n += S)
-    process_block<D, BK, KB, VB, KO, LUT>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
-                                          c, bh, n, S, n + S < nfull, koff);
+    process_block<D, BK, KB, VB, KO, LUT, PG>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
+                                          c, b, h, n, S, n + S < nfull, koff);
   if (OUTL) {
     wave_lds_sync();
     int* vci = reinterpret_cast<int*>(wl + L.vcorr);
@@ -622,8 +627,9 @@ __device__ __forceinline__ void stage_rope(float* table, const kvq_cache& c) {
   }
 }
 
-// Uniform keys: every wave takes items on its own.
-template <int D, int BK, int KB, int VB, int KO>
+// Uniform keys: every wave takes items on its own.  PG: per-sequence lengths (dense or
+// paged slots).
+template <int D, int BK, int KB, int VB, int KO, bool PG>
 __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
                                                                    int64_t nitems) {
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
 
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
   for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves)
-    mha_item<D, BK, KB, VB, KO, false>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table, nullptr, lane);
+    mha_item<D, BK, KB, VB, KO, false, PG>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table, nullptr, lane);
 }
 
 // Codebook keys: the workgroup takes groups of up to 8 splits of one (b, head), so
@@ -681,7 +687,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
       ptab[i * PT::PITCH + pc] = ka | (kb << 16);
     }
     __syncthreads();
-    if (split < S) mha_item<D, BK, KB, VB, 0, true>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
+    if (split < S) mha_item<D, BK, KB, VB, 0, true, false>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
   }
 }
 
@@ -692,7 +698,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus, bool dry);
 
-template <int D, int BK, int KB, int VB, int KO>
+template <int D, int BK, int KB, int VB, int KO, bool PG = false>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                    hipStream_t s, int cus, bool dry) {
   using Sh = MShape<D, BK, KB, VB>;
@@ -700,13 +706,13 @@ static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
   if (dry) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO, PG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
   int64_t grid = (nitems + kMhaWaves - 1) / kMhaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
+  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO, PG>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
                      q, q_pos, ws, S, nitems);
   return hipGetLastError();
 }
@@ -737,6 +743,20 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ng = g.head_dim / g.v_group;
   if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
+  if (c.seq_lens) {
+    // per-sequence lengths (dense or paged slots): uniform 4-bit keys at head_dim 128;
+    // every other configuration takes the generic kernel
+    if (g.k_mode != 0 || KB != 4 || D != 128) return hipErrorNotSupported;
+#define KVQ_MHA_PG(bk, vb)                                                                       \
+  if (BK == bk && VB == vb) {                                                                    \
+    if (ko == 2) return launch_mha_typed<128, bk, 4, vb, 2, true>(c, q, q_pos, ws, S, s, cus, dry); \
+    if (ko == 1) return launch_mha_typed<128, bk, 4, vb, 1, true>(c, q, q_pos, ws, S, s, cus, dry); \
+    return launch_mha_typed<128, bk, 4, vb, 0, true>(c, q, q_pos, ws, S, s, cus, dry);              \
+  }
+    KVQ_MHA_PG(128, 4) KVQ_MHA_PG(128, 2) KVQ_MHA_PG(64, 4) KVQ_MHA_PG(64, 2)
+#undef KVQ_MHA_PG
+    return hipErrorNotSupported;
+  }
   if (g.k_mode == 1) {
     // codebook keys: 2- and 3-bit codes (pair tables of 16 and 64 entries), no outliers
     if (ko != 0 || (KB != 3 && KB != 2)) return hipErrorNotSupported;

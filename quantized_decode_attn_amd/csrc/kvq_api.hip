@@ -48,10 +48,65 @@ kvq_status check_cache(const kvq_cache* cache) {
                                 !cache->v_rowptr || !cache->v_col || !cache->v_val))
     return KVQ_EINVAL;
   if (cache->length < 0 || cache->length > c.capacity) return KVQ_EINVAL;
+  // per-sequence lengths (both copies or neither); a block table needs them
+  if (!cache->seq_lens != !cache->seq_lens_host) return KVQ_EINVAL;
+  if (cache->block_table && !cache->seq_lens) return KVQ_EINVAL;
+  if (cache->block_table && (cache->num_blocks < 1 || (int64_t)cache->num_blocks * c.kv_heads >= ((int64_t)1 << 31)))
+    return KVQ_EINVAL;
+  if (cache->seq_lens_host)
+    for (int b = 0; b < c.batch; ++b)
+      if (cache->seq_lens_host[b] < 0 || cache->seq_lens_host[b] > c.capacity) return KVQ_EINVAL;
+  return KVQ_OK;
+}
+
+bool per_sequence(const kvq_cache* cache) { return cache->seq_lens != nullptr; }
+
+// A decode's query position: a cache with per-sequence lengths takes -1 (every sequence
+// at its own newest token; each must hold one), a dense one a position in [0, 2^40].
+kvq_status check_decode_pos(const kvq_cache* cache, int64_t q_pos) {
+  if (per_sequence(cache)) {
+    if (q_pos != -1) return KVQ_EINVAL;
+    for (int b = 0; b < cache->cfg.batch; ++b)
+      if (cache->seq_lens_host[b] < 1) return KVQ_EINVAL;
+    return KVQ_OK;
+  }
+  if (q_pos < 0 || q_pos > ((int64_t)1 << 40) || cache->length == 0) return KVQ_EINVAL;
   return KVQ_OK;
 }
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+// The append of a cache with per-sequence lengths: sequence b takes count(b) =
+// n_host ? n_host[b] : n_rows tokens, the first of its n_rows input rows.  The kernels
+// read the device lengths (and n_dev), the host copies size the launches; every check
+// comes before the first launch, and the host lengths advance only when every launch
+// was enqueued.
+kvq_status append_per_sequence(kvq_cache* cache, const uint16_t* kn, const uint16_t* vn, int64_t n_rows,
+                               const int64_t* n_host, const int64_t* n_dev, hipStream_t s) {
+  const kvq_config& c = cache->cfg;
+  int64_t most_blocks = 0;
+  bool tail = false;
+  for (int b = 0; b < c.batch; ++b) {
+    const int64_t L0 = cache->seq_lens_host[b], L1 = L0 + (n_host ? n_host[b] : n_rows);
+    if (L1 > c.capacity) return KVQ_ECAPACITY;
+    const int64_t nb = L1 / c.k_block - L0 / c.k_block;
+    most_blocks = nb > most_blocks ? nb : most_blocks;
+    tail = tail || (L1 % c.k_block != 0 && L1 != L0);
+  }
+  kvq_status st = KVQ_OK;
+  if (most_blocks > 0) {
+    st = from_hip(kvq::launch_quantize(*cache, kn, vn, 0, n_rows, 0, most_blocks, s, n_dev));
+    if (st != KVQ_OK) return st;
+  }
+  if (tail) {
+    st = from_hip(kvq::launch_tail_copy(*cache, kn, vn, n_rows, 0, 0, s, n_dev));
+    if (st != KVQ_OK) return st;
+  }
+  st = from_hip(kvq::launch_seq_lens_add(*cache, n_rows, s, n_dev));
+  if (st != KVQ_OK) return st;
+  for (int b = 0; b < c.batch; ++b) cache->seq_lens_host[b] += n_host ? n_host[b] : n_rows;
+  return KVQ_OK;
+}
 
 // Device-side split partials of kvq_decode_attention_noalloc: one array per GPU the
 // library runs on (the code object's copy on that device), held until the process ends.
@@ -157,12 +212,58 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout* out) {
   return KVQ_OK;
 }
 
+kvq_status kvq_paged_layout(const kvq_config* cfg, int32_t num_blocks, kvq_layout* out) {
+  kvq_status st = kvq_cache_layout(cfg, out);
+  if (st != KVQ_OK) return st;
+  if (num_blocks < 1 || (int64_t)num_blocks * cfg->kv_heads >= ((int64_t)1 << 31)) return KVQ_EINVAL;
+  // per slot as in the dense layout, num_blocks * kv_heads slots instead of
+  // batch * kv_heads * (T / Bk); row pointers per slot
+  const size_t dense_slots = (size_t)cfg->batch * cfg->kv_heads * (cfg->capacity / cfg->k_block);
+  const size_t slots = (size_t)num_blocks * cfg->kv_heads;
+  auto per = [&](size_t& x) { x = x / dense_slots * slots; };
+  per(out->k_codes);
+  per(out->k_scale);
+  per(out->k_zero);
+  per(out->v_codes);
+  per(out->v_scale);
+  per(out->v_zero);
+  per(out->k_col);
+  per(out->k_val);
+  per(out->v_col);
+  per(out->v_val);
+  if (out->k_rowptr) {
+    out->k_rowptr = slots * (cfg->k_block + 1) * 4;
+    out->v_rowptr = out->k_rowptr;
+  }
+  return KVQ_OK;
+}
+
 kvq_status kvq_cache_init(kvq_cache* cache, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   st = from_hip(kvq::launch_rope_init(*cache, (hipStream_t)stream));
-  if (st == KVQ_OK) cache->length = 0;
+  if (st == KVQ_OK && per_sequence(cache)) st = from_hip(kvq::launch_seq_lens_set(*cache, 0, (hipStream_t)stream));
+  if (st != KVQ_OK) return st;
+  cache->length = 0;
+  if (per_sequence(cache))
+    for (int b = 0; b < cache->cfg.batch; ++b) cache->seq_lens_host[b] = 0;
   return st;
+}
+
+kvq_status kvq_quantize_append_seqs(kvq_cache* cache, const void* k_new, const void* v_new, int64_t n_max,
+                                    const int64_t* n_new_host, const int64_t* n_new_dev, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (!per_sequence(cache) || !n_new_host || !n_new_dev || n_max < 0) return KVQ_EINVAL;
+  bool any = false;
+  for (int b = 0; b < cache->cfg.batch; ++b) {
+    if (n_new_host[b] < 0 || n_new_host[b] > n_max) return KVQ_EINVAL;
+    any = any || n_new_host[b] > 0;
+  }
+  if (!any) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_EINVAL;
+  return append_per_sequence(cache, (const uint16_t*)k_new, (const uint16_t*)v_new, n_max, n_new_host, n_new_dev,
+                             (hipStream_t)stream);
 }
 
 kvq_status kvq_quantize_append(kvq_cache* cache, const void* k_new, const void* v_new,
@@ -173,12 +274,13 @@ kvq_status kvq_quantize_append(kvq_cache* cache, const void* k_new, const void* 
   if (n_new == 0) return KVQ_OK;
   if (!k_new || !v_new) return KVQ_EINVAL;
   const kvq_config& c = cache->cfg;
-  const int64_t L0 = cache->length, L1 = L0 + n_new, Bk = c.k_block;
-  if (L1 > c.capacity) return KVQ_ECAPACITY;
-  const int64_t nf0 = L0 / Bk, nf1 = L1 / Bk;
   hipStream_t s = (hipStream_t)stream;
   const uint16_t* kn = (const uint16_t*)k_new;
   const uint16_t* vn = (const uint16_t*)v_new;
+  if (per_sequence(cache)) return append_per_sequence(cache, kn, vn, n_new, nullptr, nullptr, s);
+  const int64_t L0 = cache->length, L1 = L0 + n_new, Bk = c.k_block;
+  if (L1 > c.capacity) return KVQ_ECAPACITY;
+  const int64_t nf0 = L0 / Bk, nf1 = L1 / Bk;
   if (nf1 > nf0) {
     st = from_hip(kvq::launch_quantize(*cache, kn, vn, L0, n_new, nf0, nf1 - nf0, s));
     if (st != KVQ_OK) return st;
@@ -206,8 +308,9 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int64_t q
                                 void* ws, size_t ws_bytes, int32_t num_splits, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (!q || !out || q_pos < 0 || num_splits < 0 || cache->length == 0) return KVQ_EINVAL;
-  if (q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
+  if (!q || !out || num_splits < 0) return KVQ_EINVAL;
+  st = check_decode_pos(cache, q_pos);
+  if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
   const int S = num_splits ? num_splits : auto_splits(c);
   if (S > 4096) return KVQ_EINVAL;
@@ -221,8 +324,9 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, i
                                         int32_t num_splits, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (!q || !out || q_pos < 0 || num_splits < 0 || cache->length == 0) return KVQ_EINVAL;
-  if (q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
+  if (!q || !out || num_splits < 0) return KVQ_EINVAL;
+  st = check_decode_pos(cache, q_pos);
+  if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
   const int S = num_splits ? num_splits : auto_splits(c);
   if (S > 4096) return KVQ_EINVAL;
@@ -239,6 +343,7 @@ kvq_status kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_ne
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (!k_new || !v_new || !q || !out || num_splits < 0 || num_splits > 4096) return KVQ_EINVAL;
+  if (per_sequence(cache)) return KVQ_EUNSUPPORTED;
   const kvq_config& c = cache->cfg;
   const int64_t L0 = cache->length, L1 = L0 + 1, Bk = c.k_block;
   if (L1 > c.capacity) return KVQ_ECAPACITY;
@@ -277,6 +382,7 @@ kvq_status kvq_chunk_attention(const kvq_cache* cache, const void* q, int32_t nq
                                void* ws, size_t ws_bytes, int32_t num_splits, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
+  if (per_sequence(cache)) return KVQ_EUNSUPPORTED;
   if (!q || !out || q_pos < 0 || num_splits < 0 || cache->length == 0) return KVQ_EINVAL;
   if (nq < 1 || nq > kMaxChunk || q_pos > (int64_t)1 << 40) return KVQ_EINVAL;
   const kvq_config& c = cache->cfg;
@@ -292,6 +398,7 @@ kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, int64_t t0, int
                           void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
+  if (per_sequence(cache)) return KVQ_EUNSUPPORTED;
   if ((which != 0 && which != 1) || t0 < 0 || t1 < t0 || t1 > cache->length) return KVQ_EINVAL;
   if (t1 == t0) return KVQ_OK;
   if (!out) return KVQ_EINVAL;

@@ -108,4 +108,37 @@ __device__ __forceinline__ int kout_of(const kvq_config& c) {
   return c.outlier_pct > 0 ? (c.outlier_pct * c.head_dim + 99) / 100 : 0;
 }
 
+// Tokens of sequence b: its own length in a paged cache (clamped into [0, capacity]),
+// else the cache's one length.
+__device__ __forceinline__ int64_t seq_len_of(const kvq_cache& c, int64_t b) {
+  if (!c.seq_lens) return c.length;
+  const int64_t L = c.seq_lens[b];
+  return L < 0 ? 0 : (L > c.cfg.capacity ? (int64_t)c.cfg.capacity : L);
+}
+
+// The slot of block n of (b, kv head h): every per-block buffer is an array of slots.
+// Dense layout: (b * kv_heads + h) * (T / Bk) + n.  Paged: the physical block of
+// (b, n) from the table (clamped into the pool) times kv_heads, plus h.
+__device__ __forceinline__ int64_t slot_of(const kvq_cache& c, int64_t b, int64_t h, int64_t n) {
+  const int64_t nb = c.cfg.capacity / c.cfg.k_block;
+  if (!c.block_table) return (b * c.cfg.kv_heads + h) * nb + n;
+  int64_t p = c.block_table[b * nb + n];
+  p = p < 0 ? 0 : (p >= c.num_blocks ? (int64_t)c.num_blocks - 1 : p);
+  return p * c.cfg.kv_heads + h;
+}
+
+// The same with the layout fixed at compile time: PG (per-sequence lengths, dense or
+// paged slots) or the dense layout with one length, whose kernels then carry no
+// paging code at all.
+template <bool PG>
+__device__ __forceinline__ int64_t seq_len_t(const kvq_cache& c, int64_t b) {
+  if constexpr (PG) return seq_len_of(c, b);
+  else return c.length;
+}
+template <bool PG>
+__device__ __forceinline__ int64_t slot_t(const kvq_cache& c, int64_t b, int64_t h, int64_t n) {
+  if constexpr (PG) return slot_of(c, b, h, n);
+  else return (b * c.cfg.kv_heads + h) * (c.cfg.capacity / c.cfg.k_block) + n;
+}
+
 }  // namespace kvq

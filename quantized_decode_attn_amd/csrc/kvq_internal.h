@@ -17,22 +17,34 @@ hipError_t launch_rope_init(const kvq_cache& c, hipStream_t s);
 
 // Quantize the complete blocks [n_first, n_first + nblocks) of every (b, kv-head).
 // Tokens below `old_len` come from the tails, the others from the new input
-// (row t - old_len of `k_new`/`v_new`, each [B][Hkv][n_new][D]).
+// (row t - old_len of `k_new`/`v_new`, each [B][Hkv][n_new][D]).  In a paged cache
+// every sequence uses its own length from the device array instead of old_len and
+// n_first, and nblocks is the most blocks any sequence completes.
+// n_seq (device, per sequence; caches with per-sequence lengths only): each sequence's
+// count of new tokens, n_new then being the input's rows per sequence.
 hipError_t launch_quantize(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
                            int64_t old_len, int64_t n_new, int64_t n_first, int64_t nblocks,
-                           hipStream_t s);
+                           hipStream_t s, const int64_t* n_seq = nullptr);
 
 // The parts of launch_quantize: one kernel per tensor (uniform or codebook keys).
 hipError_t launch_quantize_keys_uniform(const kvq_cache& c, const uint16_t* k_new, int64_t old_len,
-                                        int64_t n_new, int64_t n_first, int64_t nblocks, hipStream_t s);
+                                        int64_t n_new, int64_t n_first, int64_t nblocks, const int64_t* n_seq,
+                                        hipStream_t s);
 hipError_t launch_quantize_keys_lut(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
-                                    int64_t n_first, int64_t nblocks, hipStream_t s);
+                                    int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s);
 hipError_t launch_quantize_values(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
-                                  int64_t n_first, int64_t nblocks, hipStream_t s);
+                                  int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s);
 
-// Copy new rows [src0, n_new) into tail slots [dst0, ...).
+// Copy new rows [src0, n_new) into tail slots [dst0, ...) (a paged cache: per
+// sequence, from its own length).
 hipError_t launch_tail_copy(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
-                            int64_t n_new, int64_t src0, int64_t dst0, hipStream_t s);
+                            int64_t n_new, int64_t src0, int64_t dst0, hipStream_t s,
+                            const int64_t* n_seq = nullptr);
+// A paged cache's device lengths advance by n, or by n_seq[b] (stream-ordered after the
+// append).
+hipError_t launch_seq_lens_add(const kvq_cache& c, int64_t n, hipStream_t s, const int64_t* n_seq = nullptr);
+// ... or are set to n (the cache's initialisation).
+hipError_t launch_seq_lens_set(const kvq_cache& c, int64_t n, hipStream_t s);
 
 hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out,
                          float* ws, int splits, hipStream_t s);

@@ -466,20 +466,23 @@ __device__ __forceinline__ void row_outliers(const uint4 (&v)[BK * D / 8 / kThre
 }
 
 // Writes the block's CSR slice staged in ocol/oval (consecutive threads) and its
-// row pointers (ko entries per token).
+// row pointers (ko entries per token).  col_out / val_out point at the slot's Bk * ko
+// entries, rowptr at the row-pointer array the tokens t_base + j index (the (b, h)
+// row's T + 1 entries with t_base = the block's first token in the dense layout; the
+// slot's own Bk + 1 with t_base = 0 in the paged one).
 template <int BK, int KO>
 __device__ __forceinline__ void write_csr(const uint8_t* ocol, const uint16_t* oval, int32_t* rowptr, uint8_t* col_out,
-                                          uint16_t* val_out, int64_t bh, int64_t T, int64_t t0, int ko_rt) {
+                                          uint16_t* val_out, int64_t t_base, int ko_rt) {
   const int ko = KO > 0 ? KO : ko_rt;
   for (int idx = threadIdx.x; idx < BK * ko; idx += kThreads) {
     const int j = idx / ko, r = idx % ko;
-    col_out[(bh * T + t0) * ko + idx] = ocol[j * 4 + r];
-    val_out[(bh * T + t0) * ko + idx] = oval[j * 4 + r];
+    col_out[idx] = ocol[j * 4 + r];
+    val_out[idx] = oval[j * 4 + r];
   }
   for (int j = threadIdx.x; j < BK; j += kThreads) {
-    const int64_t t = t0 + j;
-    rowptr[bh * (T + 1) + t + 1] = (int32_t)((t + 1) * ko);
-    if (t == 0) rowptr[bh * (T + 1)] = 0;
+    const int64_t t = t_base + j;
+    rowptr[t + 1] = (int32_t)((t + 1) * ko);
+    if (t == 0) rowptr[0] = 0;
   }
 }
 
@@ -790,7 +793,7 @@ struct ValueSmem {
 template <int D, int BK, int KO, bool CLIP>
 __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uint16_t* oval, ClipSmem& cs, Red& red,
                                               const kvq_cache& c, bool is_key, const uint16_t* src_new,
-                                              int64_t bh, int64_t n, int64_t old_len, int64_t n_new) {
+                                              int64_t bh, int64_t n, int64_t g, int64_t old_len, int64_t n_new) {
   using S = Stage<D, BK>;
   const int64_t T = c.cfg.capacity;
   const int64_t t0 = n * BK;
@@ -814,8 +817,12 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uin
   if constexpr (KO != 0) row_outliers<D, BK, KO>(v, tile, ko, ocol, oval, colpk);
   __syncthreads();  // the tile, the staged CSR slice and the candidate lists are complete
   if constexpr (KO != 0)
-    write_csr<BK, KO>(ocol, oval, is_key ? c.k_rowptr : c.v_rowptr, is_key ? c.k_col : c.v_col,
-                  is_key ? c.k_val : c.v_val, bh, T, t0, ko);
+  {
+    const bool paged = c.block_table != nullptr;
+    int32_t* rp = (is_key ? c.k_rowptr : c.v_rowptr) + (paged ? g * (BK + 1) : bh * (T + 1));
+    write_csr<BK, KO>(ocol, oval, rp, (is_key ? c.k_col : c.v_col) + g * BK * ko,
+                      (is_key ? c.k_val : c.v_val) + g * BK * ko, paged ? 0 : t0, ko);
+  }
   float thr = 0.0f;
   if constexpr (CLIP)
     thr = fast ? clip_from_candidates<BK * D>(cs, red, c.cfg.clip_quantile)
@@ -877,15 +884,24 @@ __device__ __forceinline__ void key_codes(const uint32_t (&xw)[8][4], const floa
 // of codebook keys.
 template <int D, int BK, int LUTB, int KO, bool CLIP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
-                                                                 int64_t old_len, int64_t n_new, int64_t n_first) {
+                                                                 int64_t old_len_arg, int64_t n_new, int64_t n_first,
+    const int64_t* __restrict__ n_seq) {
   constexpr bool OUTL = KO != 0;
   constexpr int P = D + 8;
   constexpr int NTG = BK / 8;
   constexpr int NA = D / 8;
   __shared__ KeySmem<D, BK> sh;
   const int tid = threadIdx.x;
-  const int64_t n = n_first + blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
+  // per-sequence lengths: this sequence's own length, its own count of new tokens
+  // (n_seq; n_new is then the input's rows per sequence) and the blocks they complete
+  const int64_t old_len = c.seq_lens ? seq_len_of(c, b) : old_len_arg;
+  // (a device count is clamped to the input's rows, a block to the capacity: a count
+  // that disagrees with the host's gives wrong tokens, never an access out of bounds)
+  const int64_t n_b = n_seq ? min(max(n_seq[b], (int64_t)0), n_new) : n_new;
+  const int64_t n = (c.seq_lens ? old_len / BK : n_first) + blockIdx.x;
+  if (n >= (old_len + n_b) / BK || n >= c.cfg.capacity / BK) return;
+  const int64_t g = slot_of(c, b, h, n);
   const int64_t T = c.cfg.capacity;
   const int64_t bh = (int64_t)b * c.cfg.kv_heads + h;
   constexpr bool lut = LUTB > 0;
@@ -894,7 +910,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const float Lf = (float)L;
 
   const float thr =
-      prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, true, k_new, bh, n, old_len, n_new);
+      prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, true, k_new, bh, n, g, old_len, n_new);
   __syncthreads();
 
   const bool active = NA * NTG == kThreads || tid < NA * NTG;
@@ -950,8 +966,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       uint16_t z16, s16;
       meta_from(l0, h0, L, &z16, &s16);
       const int ch = (tg < 4) ? 4 * a + tg : D / 2 + 4 * a + tg - 4;
-      c.k_scale[(bh * (T / BK) + n) * D + ch] = s16;
-      c.k_zero[(bh * (T / BK) + n) * D + ch] = z16;
+      c.k_scale[g * D + ch] = s16;
+      c.k_zero[g * D + ch] = z16;
       const float z = h2f(z16), s = h2f(s16), r = recip_or_zero(s);
       float qa, qb;
       quotient_bounds<CLIP>(z, r, Lf, thr, &qa, &qb);
@@ -1062,7 +1078,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   }
   __syncthreads();
-  uint8_t* out = static_cast<uint8_t*>(c.k_codes) + (bh * T + n * BK) * rk;
+  uint8_t* out = static_cast<uint8_t*>(c.k_codes) + g * BK * rk;
   if (rk % 16 == 0) {
     const int per_row = rk / 16;
     for (int idx = tid; idx < BK * per_row; idx += kThreads) {
@@ -1112,7 +1128,8 @@ __device__ __forceinline__ void vgroup_minmax(float* lo, float* hi, int lpg) {
 
 template <int D, int BK, int VB, int KO, bool CLIP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_values_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
-                                                                   int64_t old_len, int64_t n_new, int64_t n_first) {
+                                                                   int64_t old_len_arg, int64_t n_new, int64_t n_first,
+    const int64_t* __restrict__ n_seq) {
   constexpr bool OUTL = KO != 0;
   constexpr int P = D + 8;
   constexpr int TPW = 32 / VB;
@@ -1121,9 +1138,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   constexpr int NTG = BK / TPW;
   __shared__ ValueSmem<D, BK> sh;
   const int tid = threadIdx.x;
-  const int64_t n = n_first + blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t T = c.cfg.capacity;
+  // per-sequence lengths: this sequence's own length, its own count of new tokens
+  // (n_seq; n_new is then the input's rows per sequence) and the blocks they complete
+  const int64_t old_len = c.seq_lens ? seq_len_of(c, b) : old_len_arg;
+  // (a device count is clamped to the input's rows, a block to the capacity: a count
+  // that disagrees with the host's gives wrong tokens, never an access out of bounds)
+  const int64_t n_b = n_seq ? min(max(n_seq[b], (int64_t)0), n_new) : n_new;
+  const int64_t n = (c.seq_lens ? old_len / BK : n_first) + blockIdx.x;
+  if (n >= (old_len + n_b) / BK || n >= c.cfg.capacity / BK) return;
+  const int64_t g = slot_of(c, b, h, n);
   const int64_t bh = (int64_t)b * c.cfg.kv_heads + h;
   const int L = (1 << VB) - 1;
   const float Lf = (float)L;
@@ -1131,7 +1155,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int lpg = G / CW;
 
   const float thr =
-      prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, false, v_new, bh, n, old_len, n_new);
+      prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, false, v_new, bh, n, g, old_len, n_new);
   __syncthreads();
 
   const bool active = NCC * NTG == kThreads || tid < NCC * NTG;
@@ -1188,8 +1212,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         uint16_t z16, s16;
         meta_from(l0, h0, L, &z16, &s16);
         const int j = TPW * tg + uu;
-        c.v_scale[(bh * T + n * BK + j) * ng + grp] = s16;
-        c.v_zero[(bh * T + n * BK + j) * ng + grp] = z16;
+        c.v_scale[(g * BK + j) * ng + grp] = s16;
+        c.v_zero[(g * BK + j) * ng + grp] = z16;
         const float z = h2f(z16), s = h2f(s16), r = recip_or_zero(s);
         float qa, qb;
         quotient_bounds<CLIP>(z, r, Lf, thr, &qa, &qb);
@@ -1267,7 +1291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         w[q] = put_byte(byte, k, w[q]);
       }
     }
-    uint32_t* out = static_cast<uint32_t*>(c.v_codes) + (bh * (T / TPW) + n * (BK / TPW) + tg) * D + ch0;
+    uint32_t* out = static_cast<uint32_t*>(c.v_codes) + (g * (BK / TPW) + tg) * D + ch0;
     reinterpret_cast<uint4*>(out)[0] = make_uint4(w[0], w[1], w[2], w[3]);
     if constexpr (CW == 8) reinterpret_cast<uint4*>(out)[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }

@@ -12,11 +12,11 @@
 namespace kvq {
 hipError_t launch_rope_init(const kvq_cache&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quantize(const kvq_cache&, const uint16_t*, const uint16_t*, int64_t, int64_t, int64_t, int64_t,
-                           hipStream_t) {
+                           hipStream_t, const int64_t*) {
   return hipErrorNotSupported;
 }
 hipError_t launch_tail_copy(const kvq_cache&, const uint16_t*, const uint16_t*, int64_t, int64_t, int64_t,
-                            hipStream_t) {
+                            hipStream_t, const int64_t*) {
   return hipErrorNotSupported;
 }
 hipError_t launch_decode(const kvq_cache&, const uint16_t*, int64_t, float*, float*, int, hipStream_t) {
@@ -33,6 +33,8 @@ hipError_t launch_decode_step(const kvq_cache&, const uint16_t*, const uint16_t*
   return hipErrorNotSupported;
 }
 bool decode_step_prefers_one_launch(const kvq_cache&) { return true; }
+hipError_t launch_seq_lens_add(const kvq_cache&, int64_t, hipStream_t, const int64_t*) { return hipErrorNotSupported; }
+hipError_t launch_seq_lens_set(const kvq_cache&, int64_t, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace kvq
 
 static int failures = 0;
@@ -181,6 +183,68 @@ int main() {
   k.v_scale = nullptr;
   EXPECT(kvq_quantize_append(&k, (void*)0x1000, (void*)0x1000, 5, nullptr) == KVQ_EINVAL);
   EXPECT(kvq_decode_attention(&k, (void*)0x1000, 299, out, (void*)0x3000, ws, 0, nullptr) == KVQ_EINVAL);
+  // paged layout and per-sequence lengths: sizes, descriptor checks, what each call
+  // accepts; the host lengths change only when every launch succeeded
+  {
+    kvq_config c = base();
+    kvq_layout dense, paged;
+    EXPECT(kvq_cache_layout(&c, &dense) == KVQ_OK);
+    EXPECT(kvq_paged_layout(&c, 5, &paged) == KVQ_OK);
+    const size_t dslots = (size_t)2 * 2 * 8, pslots = (size_t)5 * 2;  // batch*kv_heads*T/Bk, pool*kv_heads
+    EXPECT(paged.k_codes == dense.k_codes / dslots * pslots && paged.v_scale == dense.v_scale / dslots * pslots);
+    EXPECT(paged.k_col == dense.k_col / dslots * pslots && paged.k_scale == dense.k_scale / dslots * pslots);
+    EXPECT(paged.k_rowptr == pslots * 129 * 4 && paged.k_tail == dense.k_tail && paged.rope == dense.rope);
+    EXPECT(kvq_paged_layout(&c, 0, &paged) == KVQ_EINVAL && kvq_paged_layout(&c, 1 << 30, &paged) == KVQ_EINVAL);
+    kvq_cache p = fake_cache(c, 0);
+    int64_t host[2] = {300, 0};
+    p.seq_lens_host = host;
+    EXPECT(kvq_cache_init(&p, nullptr) == KVQ_EINVAL);           // host lengths without device ones
+    p.seq_lens = (int64_t*)0x5000;
+    p.block_table = (const int32_t*)0x6000;
+    EXPECT(kvq_cache_init(&p, nullptr) == KVQ_EINVAL);           // a table without a pool size
+    p.num_blocks = 5;
+    EXPECT(kvq_cache_init(&p, nullptr) == KVQ_EHIP);
+    EXPECT(host[0] == 300);
+    host[1] = 2000;
+    EXPECT(kvq_quantize_append(&p, (void*)0x1000, (void*)0x1000, 1, nullptr) == KVQ_EINVAL);  // length > T
+    host[1] = 1000;
+    EXPECT(kvq_quantize_append(&p, (void*)0x1000, (void*)0x1000, 30, nullptr) == KVQ_ECAPACITY);
+    EXPECT(kvq_quantize_append(&p, (void*)0x1000, (void*)0x1000, 20, nullptr) == KVQ_EHIP);
+    EXPECT(host[0] == 300 && host[1] == 1000);
+    const size_t pws = kvq_decode_workspace_bytes(&p, 0);
+    EXPECT(kvq_decode_attention(&p, (void*)0x1000, -1, out, (void*)0x3000, pws, 0, nullptr) == KVQ_EHIP);
+    EXPECT(kvq_decode_attention(&p, (void*)0x1000, 299, out, (void*)0x3000, pws, 0, nullptr) == KVQ_EINVAL);
+    EXPECT(kvq_decode_attention_noalloc(&p, (void*)0x1000, -1, out, 0, nullptr) == KVQ_EHIP);
+    host[1] = 0;
+    EXPECT(kvq_decode_attention(&p, (void*)0x1000, -1, out, (void*)0x3000, pws, 0, nullptr) == KVQ_EINVAL);
+    EXPECT(kvq_chunk_attention(&p, (void*)0x1000, 4, 0, out, (void*)0x3000, 1 << 30, 0, nullptr) ==
+           KVQ_EUNSUPPORTED);
+    EXPECT(kvq_decode_step(&p, (void*)0x1000, (void*)0x1000, (void*)0x1000, out, (void*)0x3000, pws, 0, nullptr) ==
+           KVQ_EUNSUPPORTED);
+    EXPECT(kvq_dequantize(&p, 0, 0, 1, out, nullptr) == KVQ_EUNSUPPORTED);
+    // ragged append: counts in [0, n_max], capacity per sequence, nothing to do
+    host[0] = 300; host[1] = 1000;
+    const int64_t cnt_ok[2] = {5, 24}, cnt_cap[2] = {5, 25}, cnt_bad[2] = {-1, 3}, cnt_zero[2] = {0, 0};
+    const int64_t* dev_cnt = (const int64_t*)0x7000;
+    EXPECT(kvq_quantize_append_seqs(&p, (void*)0x1000, (void*)0x1000, 24, cnt_ok, dev_cnt, nullptr) == KVQ_EHIP);
+    EXPECT(kvq_quantize_append_seqs(&p, (void*)0x1000, (void*)0x1000, 30, cnt_cap, dev_cnt, nullptr) ==
+           KVQ_ECAPACITY);
+    EXPECT(kvq_quantize_append_seqs(&p, (void*)0x1000, (void*)0x1000, 23, cnt_ok, dev_cnt, nullptr) == KVQ_EINVAL);
+    EXPECT(kvq_quantize_append_seqs(&p, (void*)0x1000, (void*)0x1000, 24, cnt_bad, dev_cnt, nullptr) == KVQ_EINVAL);
+    EXPECT(kvq_quantize_append_seqs(&p, (void*)0x1000, (void*)0x1000, 24, cnt_ok, nullptr, nullptr) == KVQ_EINVAL);
+    EXPECT(kvq_quantize_append_seqs(&p, nullptr, nullptr, 24, cnt_zero, dev_cnt, nullptr) == KVQ_OK);
+    EXPECT(kvq_quantize_append_seqs(&p, nullptr, (void*)0x1000, 24, cnt_ok, dev_cnt, nullptr) == KVQ_EINVAL);
+    EXPECT(host[0] == 300 && host[1] == 1000);
+    p.block_table = nullptr;  // per-sequence lengths over the dense slots
+    host[1] = 7;
+    EXPECT(kvq_quantize_append(&p, (void*)0x1000, (void*)0x1000, 3, nullptr) == KVQ_EHIP);
+    EXPECT(kvq_decode_attention(&p, (void*)0x1000, -1, out, (void*)0x3000, pws, 0, nullptr) == KVQ_EHIP);
+    p.seq_lens = nullptr;
+    EXPECT(kvq_quantize_append(&p, (void*)0x1000, (void*)0x1000, 3, nullptr) == KVQ_EINVAL);  // one copy only
+    kvq_cache dcache = fake_cache(base(), 100);
+    EXPECT(kvq_quantize_append_seqs(&dcache, (void*)0x1000, (void*)0x1000, 24, cnt_ok, dev_cnt, nullptr) ==
+           KVQ_EINVAL);
+  }
   printf("%s (%d failures)\n", failures ? "FAILED" : "ok", failures);
   return failures ? 1 : 0;
 }
