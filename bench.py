@@ -20,8 +20,13 @@ verification) over the same cache, reported under "chunk".
 
 ``--decode-steps N`` also times token-by-token generation on a second cache holding the
 workload's first T - N tokens: N fused decode steps (kvq_decode_step: the token appended
-and attended in one launch), then the same N tokens as kvq_quantize_append of one token
+inside the attention's own launches), then the same N tokens as kvq_quantize_append of one token
 followed by kvq_decode_attention; reported per step under "decode_step".
+
+``--paged`` also times the workload's shapes as a continuous batch: per-sequence lengths
+in [T/8, T], blocks in a shuffled pool of exactly the blocks they need; the ragged
+prefill (kvq_quantize_append_seqs) and the decode of every sequence at its own newest
+token, paged and in dense slots; reported under "paged".
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -260,6 +265,70 @@ def time_decode_steps(cfg, k_d, v_d, lut_d, n, dev):
             "graph_speedup_vs_append_plus_decode": round(graph["two_calls"] / graph["fused"], 3)}
 
 
+def time_paged(cfg, k_d, v_d, lut_d, dev, reps=10):
+    """The workload's shapes as a continuous batch: per-sequence lengths drawn uniformly
+    from [T/8, T] (seeded), the quantized blocks in a pool of exactly the blocks they
+    need, mapped through a shuffled block table.  Times the ragged prefill (one
+    kvq_quantize_append_seqs of every sequence's tokens) and the decode of every sequence
+    at its own newest token, against the same lengths in the dense slots."""
+    import torch
+    import quantized_decode_attn_amd as kvq
+    T, B, H, Hq, D, Bk = (cfg["tokens"], cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"],
+                          cfg["k_block"])
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(T // 8, T + 1, size=B)
+    need = [-(-int(L) // Bk) for L in lengths]
+    P = int(sum(need))
+    perm = rng.permutation(P)
+    table = np.zeros((B, T // Bk), np.int32)
+    i = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[i:i + n]
+        i += n
+    q = torch.from_numpy(np.ascontiguousarray(synth.gen_q(cfg, seed=4)).view(np.int16)).to(dev).view(torch.float16)
+    kin, vin = k_d[:, :, :T].contiguous(), v_d[:, :, :T].contiguous()
+    tokens = int(lengths.sum())
+    dbytes = tokens * H * decode_bytes_per_token_head(cfg) + B * Hq * D * 6
+    abytes = tokens * H * append_bytes_per_token_head(cfg)
+    res = {"lengths": "uniform in [T/8, T], seed 11", "tokens": tokens, "pool_blocks": P,
+           "pool_fraction_of_dense": round(P / (B * T / Bk), 3)}
+    stream = torch.cuda.current_stream()
+    for name, paged in (("paged", True), ("dense_slots", False)):
+        if paged:
+            cache = kvq.PagedCache(cfg, num_blocks=P, block_table=torch.from_numpy(table).to(dev), device=dev,
+                                   lut=lut_d)
+        else:
+            cache = kvq.PagedCache(cfg, device=dev, lut=lut_d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.append_seqs(kin, vin, lengths)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        app_us = e0.elapsed_time(e1) * 1e3
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        cache.workspace(0)
+        for _ in range(2):
+            cache.decode(q, out=out)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            cache.decode(q, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"decode_us": round(dec_us, 2), "decode_GBps": round(dbytes / dec_us / 1e3, 1),
+                     "decode_frac": round(dbytes / dec_us / 1e3 / HBM_PEAK_GBPS, 4),
+                     "prefill_append_us": round(app_us, 1),
+                     "prefill_append_tokens_per_s": round(tokens / app_us * 1e6, 1),
+                     "prefill_append_GBps": round(abytes / app_us / 1e3, 1)}
+        log("%-11s decode %.1f us %.0f GB/s (%.1f%% of 8 TB/s); ragged prefill append %.1f us %.0f GB/s"
+            % (name, dec_us, dbytes / dec_us / 1e3, 100 * dbytes / dec_us / 1e3 / HBM_PEAK_GBPS, app_us,
+               abytes / app_us / 1e3))
+        del cache
+    res["algorithmic_decode_bytes"] = int(dbytes)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +342,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="also time attention of a chunk of this many queries")
     ap.add_argument("--chunk-splits", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=0, help="also time this many token-by-token steps")
+    ap.add_argument("--paged", action="store_true", help="also time a paged cache with mixed sequence lengths")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -433,6 +503,8 @@ def main():
                         "traffic": measured_traffic("chunk", cfg["workload"], ch_hash, nq)}
     if args.decode_steps:
         rec["decode_step"] = time_decode_steps(cfg, k_d, v_d, lut_d, args.decode_steps, dev)
+    if args.paged:
+        rec["paged"] = time_paged(cfg, k_d, v_d, lut_d, dev)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds)

@@ -221,8 +221,10 @@ kvq_status kvq_quantize_append_seqs(kvq_cache *cache, const void *k_new, const v
  * 4096): one (max, sum, output) partial of head_dim + 2 floats per (b, q-head, split),
  * B * q_heads * splits * (head_dim + 2) * 4 bytes.  The split-K decode reads the
  * packed cache once and keeps only these partials as intermediate state, in the
- * FlashAttention manner [TQ] section 5.2 pairs with the quantized cache.  Host only;
- * returns 0 for an invalid cache or a negative split count. */
+ * FlashAttention manner [TQ] section 5.2 pairs with the quantized cache.  With
+ * per-sequence lengths the library's choice is four times the dense one (more, shorter
+ * work items even out the different lengths).  Host only; returns 0 for an invalid
+ * cache or a negative split count. */
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t num_splits);
 
 /* Single-query decode attention over the whole cache:

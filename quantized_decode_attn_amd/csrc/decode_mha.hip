@@ -654,8 +654,9 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
 }
 
 // Codebook keys: the workgroup takes groups of up to 8 splits of one (b, head), so
-// that its waves share the head's pair table, rebuilt at every group.
-template <int D, int BK, int KB, int VB>
+// that its waves share the head's pair table, rebuilt at every group.  PG: per-sequence
+// lengths (dense or paged slots).
+template <int D, int BK, int KB, int VB, bool PG>
 __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                        int64_t q_pos, float* __restrict__ ws, int S,
                                                                        int64_t ngroups) {
@@ -687,7 +688,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
       ptab[i * PT::PITCH + pc] = ka | (kb << 16);
     }
     __syncthreads();
-    if (split < S) mha_item<D, BK, KB, VB, 0, true, false>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
+    if (split < S) mha_item<D, BK, KB, VB, 0, true, PG>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
   }
 }
 
@@ -717,7 +718,7 @@ static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_
   return hipGetLastError();
 }
 
-template <int D, int BK, int KB, int VB>
+template <int D, int BK, int KB, int VB, bool PG = false>
 static hipError_t launch_mha_lut_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                        hipStream_t s, int cus, bool dry) {
   using Sh = MShape<D, BK, KB, VB>;
@@ -726,12 +727,12 @@ static hipError_t launch_mha_lut_typed(const kvq_cache& c, const uint16_t* q, in
                         (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
   if (dry) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_lut_kernel<D, BK, KB, VB>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_lut_kernel<D, BK, KB, VB, PG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (int64_t)c.cfg.batch * c.cfg.kv_heads * ((S + kMhaWaves - 1) / kMhaWaves);
   const int64_t grid = ngroups < cus ? ngroups : cus;
-  hipLaunchKernelGGL((decode_mha_lut_kernel<D, BK, KB, VB>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s,
+  hipLaunchKernelGGL((decode_mha_lut_kernel<D, BK, KB, VB, PG>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s,
                      c, q, q_pos, ws, S, ngroups);
   return hipGetLastError();
 }
@@ -744,9 +745,19 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
   if (c.seq_lens) {
-    // per-sequence lengths (dense or paged slots): uniform 4-bit keys at head_dim 128;
-    // every other configuration takes the generic kernel
-    if (g.k_mode != 0 || KB != 4 || D != 128) return hipErrorNotSupported;
+    // per-sequence lengths (dense or paged slots): uniform 4-bit keys and 2/3-bit
+    // codebook keys at head_dim 128; every other configuration takes the generic kernel
+    if (D != 128) return hipErrorNotSupported;
+    if (g.k_mode == 1) {
+      if (ko != 0 || (KB != 3 && KB != 2)) return hipErrorNotSupported;
+#define KVQ_MHA_LUT_PG(bk, kb, vb) \
+  if (BK == bk && KB == kb && VB == vb) return launch_mha_lut_typed<128, bk, kb, vb, true>(c, q, q_pos, ws, S, s, cus, dry);
+      KVQ_MHA_LUT_PG(128, 3, 2) KVQ_MHA_LUT_PG(128, 3, 4) KVQ_MHA_LUT_PG(128, 2, 2) KVQ_MHA_LUT_PG(128, 2, 4)
+      KVQ_MHA_LUT_PG(64, 3, 2) KVQ_MHA_LUT_PG(64, 3, 4) KVQ_MHA_LUT_PG(64, 2, 2) KVQ_MHA_LUT_PG(64, 2, 4)
+#undef KVQ_MHA_LUT_PG
+      return hipErrorNotSupported;
+    }
+    if (g.k_mode != 0 || KB != 4) return hipErrorNotSupported;
 #define KVQ_MHA_PG(bk, vb)                                                                       \
   if (BK == bk && VB == vb) {                                                                    \
     if (ko == 2) return launch_mha_typed<128, bk, 4, vb, 2, true>(c, q, q_pos, ws, S, s, cus, dry); \

@@ -143,6 +143,18 @@ int auto_splits(const kvq_config& c) {
   return (int)s;
 }
 
+// The library's split count with per-sequence lengths: four times the dense choice
+// (capped by the blocks of a full sequence and 4096).  Every sequence is split S ways,
+// so a short one has short items; with about four items per wave the persistent grid
+// evens the lengths out better than with one.
+int auto_splits_seq(const kvq_config& c) {
+  int64_t s = (int64_t)auto_splits(c) * 4;
+  const int64_t nblk = c.capacity / c.k_block;
+  if (s > nblk) s = nblk;
+  if (s > 4096) s = 4096;
+  return (int)(s < 1 ? 1 : s);
+}
+
 // Splits per (b, kv-head) for a chunk of nq queries: about two work items per SIMD of
 // an MI355X (256 CUs x 4) over the row tiles of 16, in multiples of 4 (the waves of a
 // matrix-core workgroup), without splitting a sequence below one block per split.
@@ -300,7 +312,7 @@ kvq_status kvq_quantize_append(kvq_cache* cache, const void* k_new, const void* 
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_splits) {
   if (check_cache(cache) != KVQ_OK || num_splits < 0) return 0;
   const kvq_config& c = cache->cfg;
-  const int S = num_splits ? num_splits : auto_splits(c);
+  const int S = num_splits ? num_splits : (per_sequence(cache) ? auto_splits_seq(c) : auto_splits(c));
   return (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
 }
 
@@ -312,7 +324,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int64_t q
   st = check_decode_pos(cache, q_pos);
   if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
-  const int S = num_splits ? num_splits : auto_splits(c);
+  const int S = num_splits ? num_splits : (per_sequence(cache) ? auto_splits_seq(c) : auto_splits(c));
   if (S > 4096) return KVQ_EINVAL;
   const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
   if (!ws || ws_bytes < need) return KVQ_EWORKSPACE;
@@ -328,14 +340,15 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, i
   st = check_decode_pos(cache, q_pos);
   if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
-  const int S = num_splits ? num_splits : auto_splits(c);
+  const int S = num_splits ? num_splits : (per_sequence(cache) ? auto_splits_seq(c) : auto_splits(c));
   if (S > 4096) return KVQ_EINVAL;
   const size_t need = (size_t)c.batch * c.q_heads * S * (c.head_dim + 2) * sizeof(float);
   if (need > kNoallocScratchBytes) return KVQ_EWORKSPACE;
   float* ws = nullptr;
   st = scratch_of_current_device(&ws);
   if (st != KVQ_OK) return st;
-  return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, ws, S, (hipStream_t)stream));
+  return from_hip(kvq::launch_decode(*cache, (const uint16_t*)q, q_pos, out, ws, S,
+                                     (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_step(kvq_cache* cache, const void* k_new, const void* v_new, const void* q, float* out,

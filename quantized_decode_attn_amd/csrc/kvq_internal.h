@@ -46,6 +46,7 @@ hipError_t launch_seq_lens_add(const kvq_cache& c, int64_t n, hipStream_t s, con
 // ... or are set to n (the cache's initialisation).
 hipError_t launch_seq_lens_set(const kvq_cache& c, int64_t n, hipStream_t s);
 
+// q_pos < 0 (caches with per-sequence lengths): every sequence at its own newest token.
 hipError_t launch_decode(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* out,
                          float* ws, int splits, hipStream_t s);
 

@@ -9,11 +9,13 @@ within 2e-3 of the oracle's fp64 decode of a cache built from that sequence's to
 alone, and every quantized block the sequence holds (read from the pool through the
 table) and its fp16 tail equal to the oracle's bit for bit.  The paged cache and the
 dense per-sequence cache give bitwise the same outputs (the same kernels; only the
-block addressing differs), and so does a plain dense cache when all lengths are equal.
+block addressing differs); a plain dense cache at equal lengths gives the same outputs
+within the split-order bound of fp32 (the per-sequence kernels choose each sequence's
+split count by its length, so they may group the blocks differently).
 
-Cases: the tuned one-head kernel (uniform 4-bit keys, 0 and 2 outliers per vector,
-clipping), the tuned grouped-query kernel (with outliers), and the generic kernel
-(codebook keys; head_dim 64 with grouped queries).
+Cases: the tuned one-head kernels (uniform 4-bit keys with 0 and 2 outliers per vector
+and clipping; 3-bit codebook keys with 2-bit values), the tuned grouped-query kernel
+(with outliers), and the generic kernel (head_dim 64 with grouped queries).
 """
 import numpy as np
 import pytest
@@ -45,7 +47,7 @@ CASES = {
                      [[256, 5, 130], [1, 1, 1], [300, 0, 127], [211, 1, 0]]),
     "gqa_csr": (synth.config("c2", batch=2, q_heads=8, kv_heads=2, tokens=896, capacity=896),
                 [[400, 128], [1, 1], [0, 300], [95, 1]]),
-    "generic_lut": (synth.config("c3", batch=2, q_heads=2, kv_heads=2, tokens=640, capacity=640),
+    "lut_v2": (synth.config("c3", batch=2, q_heads=2, kv_heads=2, tokens=640, capacity=640),
                     [[200, 3], [200, 129], [1, 0]]),
     "generic_gqa_d64": (synth.config("c0", batch=3, q_heads=8, kv_heads=2, tokens=512, capacity=512),
                         [[64, 3, 100], [1, 64, 100], [130, 0, 1]]),
@@ -176,8 +178,8 @@ def test_paged_matches_oracle_and_dense(case):
 @pytest.mark.parametrize("case", ["mha_v4", "gqa_csr", "generic_gqa_d64"])
 def test_equal_lengths_match_the_dense_cache(case):
     """All sequences at one length: the paged cache's decode equals the plain dense
-    cache's bit for bit (same split count; configurations where both take the same
-    kernel: codebook keys, for one, take a tuned kernel in the dense cache only)."""
+    cache's within 2e-5, the bound of a change of split grouping (the per-sequence
+    kernels give a sequence ceil(blocks / ceil((T / Bk) / S)) splits)."""
     import torch
     import quantized_decode_attn_amd as kvq
     from _gpu_util import build_gpu_cache
@@ -199,7 +201,7 @@ def test_equal_lengths_match_the_dense_cache(case):
         a = paged.decode(q, num_splits=S).cpu().numpy()
         b = plain.decode(q, q_pos=T - 1, num_splits=S).cpu().numpy()
         say("case", case, "splits", S, "max abs diff", float(np.abs(a - b).max()))
-        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert float(np.abs(a - b).max()) <= 2e-5
 
 
 def test_paged_calls_and_checks():
