@@ -69,12 +69,19 @@ typedef int32_t kvq_status;
  *   no part in the statistics ([KVC3] "Per-Vector Dense-and-Sparse Quantization").
  * rope_theta: base of the rotary embedding applied to keys and the query at read
  *   time (rotate-half pairs (i, i + head_dim/2), angle pos * theta^(-2i/head_dim)).
+ * keep_pct p > 0: in every quantized block the R = ceil(p*k_block/100) key vectors of
+ *   largest squared L2 norm (the fp16 values squared exactly in fp64 and added in
+ *   channel order; ties to the lower token) are kept exactly as fp16 and take no part
+ *   in the block's statistics (code 0 is stored for them): the norm-based importance
+ *   and high-precision retention of [TQ] sections 3.2 and 6.1.  Values are quantized
+ *   as usual.
  *
  * Supported by the kernels: head_dim in {64, 128}; k_bits in {2, 3, 4} (k_mode 0 or
  * 1); v_bits in {2, 4}; v_group in {16, 32, 64, 128} dividing head_dim; k_block in
  * {64, 128}; capacity a positive multiple of k_block below 2^31; q_heads a multiple of
  * kv_heads with q_heads/kv_heads <= 8; clip_quantile in [0, 1); outlier_pct in
- * [0, 100] with ceil(p*head_dim/100) <= 4; rope_theta > 1.
+ * [0, 100] with ceil(p*head_dim/100) <= 4; rope_theta > 1; keep_pct in [0, 100] with
+ * R <= 16, and only with uniform keys (k_mode 0), no outliers and no clipping.
  */
 typedef struct {
   int32_t batch, q_heads, kv_heads, head_dim, capacity;
@@ -83,6 +90,7 @@ typedef struct {
   float clip_quantile;
   int32_t outlier_pct;
   float rope_theta;
+  int32_t keep_pct;
 } kvq_config;
 
 /* Byte size of each buffer of a cache; 0 = buffer not used by this configuration. */
@@ -91,6 +99,7 @@ typedef struct {
   size_t v_codes, v_scale, v_zero, v_tail;
   size_t k_rowptr, k_col, k_val, v_rowptr, v_col, v_val;
   size_t rope;
+  size_t k_keep_idx, k_keep_val;
 } kvq_layout;
 
 /* A cache: caller-owned device buffers plus the host-side token count.
@@ -118,6 +127,9 @@ typedef struct {
  *  v_rowptr, v_col, v_val: the same for values.
  *  rope     f32  [Bk][D/2][2] cos/sin(j * f_i), then [T/Bk][D/2][2] cos/sin(n*Bk*f_i),
  *                 with f_i = theta^(-2i/D); filled by kvq_cache_init.
+ *  k_keep_idx u8   [BH][T/Bk][R]     keep_pct > 0: the kept tokens' offsets in the
+ *                 block, ascending.
+ *  k_keep_val fp16 [BH][T/Bk][R][D]  their key vectors, exact input bits.
  *
  * Tokens [0, floor(length/Bk)*Bk) are quantized; the rest live in the tails.
  * At a quantized position that holds an outlier the stored code is 0; readers
@@ -126,8 +138,8 @@ typedef struct {
  * Every buffer above except the tails, k_lut, rope and the row pointers is an array of
  * per-block slots: block n of (b, h) is slot g = (b * kv_heads + h) * (T / Bk) + n, and
  * the slot's part of a buffer is its Bk tokens' rows (k_codes, v_codes, v_scale,
- * v_zero, k_col/k_val and v_col/v_val, the latter Bk * ko entries) or its D entries
- * (k_scale, k_zero).
+ * v_zero, k_col/k_val and v_col/v_val, the latter Bk * ko entries), its D entries
+ * (k_scale, k_zero) or its R kept keys (k_keep_idx, k_keep_val).
  *
  * Paged layout (block_table != NULL), for the continuous batching and paged cache
  * management that [TQ] sections 5.2 and 5.3 name as the serving context of a quantized
@@ -161,6 +173,8 @@ typedef struct {
   uint8_t *v_col;
   uint16_t *v_val;
   float *rope;
+  uint8_t *k_keep_idx;
+  uint16_t *k_keep_val;
   /* paged layout (see above); all NULL / 0 for the dense layout */
   const int32_t *block_table;
   int32_t num_blocks;

@@ -43,7 +43,7 @@ class Cfg(C.Structure):
                 ("head_dim", C.c_int32), ("capacity", C.c_int32), ("k_bits", C.c_int32),
                 ("k_mode", C.c_int32), ("k_block", C.c_int32), ("v_bits", C.c_int32),
                 ("v_group", C.c_int32), ("clip_quantile", C.c_float), ("outlier_pct", C.c_int32),
-                ("rope_theta", C.c_float)]
+                ("rope_theta", C.c_float), ("keep_pct", C.c_int32)]
 
 
 class _Head(C.Structure):
@@ -52,7 +52,7 @@ class _Head(C.Structure):
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("v_tail", C.c_void_p),
                 ("k_rowptr", C.c_void_p), ("k_col", C.c_void_p), ("k_val", C.c_void_p),
                 ("v_rowptr", C.c_void_p), ("v_col", C.c_void_p), ("v_val", C.c_void_p),
-                ("length", C.c_int64)]
+                ("k_keep_idx", C.c_void_p), ("k_keep_val", C.c_void_p), ("length", C.c_int64)]
 
 
 _lib = None
@@ -83,6 +83,7 @@ def load(path: str):
         "orc_f2h_array": (None, [vp, vp, i64, C.c_int]),
         "orc_kv_bytes": (C.c_double, [i64, i64, i64, i64, i64]),
         "orc_kout": (C.c_int, [C.POINTER(Cfg)]),
+        "orc_keep_count": (C.c_int, [C.POINTER(Cfg)]),
         "orc_layout": (None, [C.POINTER(Cfg), vp]),
         "orc_clip_threshold": (C.c_float, [vp, i64, C.c_float]),
         "orc_quantize_block": (C.c_int, [C.POINTER(Cfg), C.c_int, i64, vp, C.POINTER(_Head)]),
@@ -103,7 +104,8 @@ def load(path: str):
 
 
 LAYOUT_NAMES = ["k_codes", "k_scale", "k_zero", "k_lut", "k_tail", "v_codes", "v_scale",
-                "v_zero", "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val"]
+                "v_zero", "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val",
+                "k_keep_idx", "k_keep_val"]
 
 _CFG_KEYS = [f[0] for f in Cfg._fields_]
 
@@ -113,6 +115,7 @@ def make_cfg(cfg: dict) -> Cfg:
     defaults to ``tokens``."""
     d = dict(cfg)
     d.setdefault("capacity", d.get("tokens"))
+    d.setdefault("keep_pct", 0)
     return Cfg(**{k: d[k] for k in _CFG_KEYS})
 
 
@@ -121,9 +124,15 @@ def kout(cfg: dict) -> int:
     return lib().orc_kout(C.byref(c))
 
 
+def keep_count(cfg: dict) -> int:
+    """Key vectors kept in fp16 per quantized block."""
+    c = make_cfg(cfg)
+    return lib().orc_keep_count(C.byref(c))
+
+
 def layout(cfg: dict) -> dict:
     c = make_cfg(cfg)
-    out = np.zeros(15, np.int64)
+    out = np.zeros(17, np.int64)
     lib().orc_layout(C.byref(c), out.ctypes.data)
     return dict(zip(LAYOUT_NAMES, (int(v) for v in out)))
 
@@ -184,6 +193,9 @@ class HeadCache:
         self.v_col = np.zeros(T * ko, np.uint8)
         self.k_val = np.zeros(T * ko, np.uint16)
         self.v_val = np.zeros(T * ko, np.uint16)
+        R = keep_count(c)
+        self.k_keep_idx = np.zeros(T // Bk * R, np.uint8)
+        self.k_keep_val = np.zeros((T // Bk * R, D), np.uint16)
         self.length = 0
         self._c = make_cfg(self.cfg)
 

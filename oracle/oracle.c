@@ -37,6 +37,7 @@ typedef struct {
   float clip_quantile;
   int32_t outlier_pct;
   float rope_theta;
+  int32_t keep_pct;        /* key vectors kept in fp16 per block, percent (0 = none) */
 } orc_cfg;
 
 /* Buffers of ONE (batch, kv-head) of the cache, laid out exactly as the library's
@@ -57,6 +58,8 @@ typedef struct {
   int32_t *v_rowptr;
   uint8_t *v_col;
   uint16_t *v_val;
+  uint8_t *k_keep_idx;     /* [capacity/k_block][R]    retained token offsets      */
+  uint16_t *k_keep_val;    /* [capacity/k_block][R][D] their keys, fp16           */
   int64_t length;          /* tokens held                                       */
 } orc_head;
 
@@ -143,10 +146,15 @@ int orc_kout(const orc_cfg *c) {
   return c->outlier_pct > 0 ? (c->outlier_pct * c->head_dim + 99) / 100 : 0;
 }
 
+/* Key vectors kept in fp16 per quantized block: ceil(keep_pct * k_block / 100). */
+int orc_keep_count(const orc_cfg *c) {
+  return c->keep_pct > 0 ? (c->keep_pct * c->k_block + 99) / 100 : 0;
+}
+
 /* Byte size of every buffer of the whole cache, in the order
  * k_codes k_scale k_zero k_lut k_tail v_codes v_scale v_zero v_tail
- * k_rowptr k_col k_val v_rowptr v_col v_val (15 entries). */
-void orc_layout(const orc_cfg *c, int64_t out[15]) {
+ * k_rowptr k_col k_val v_rowptr v_col v_val k_keep_idx k_keep_val (17 entries). */
+void orc_layout(const orc_cfg *c, int64_t out[17]) {
   const int64_t BH = (int64_t)c->batch * c->kv_heads, D = c->head_dim, T = c->capacity;
   const int64_t nblk = T / c->k_block, ko = orc_kout(c);
   const int uni = c->k_mode == 0;
@@ -165,6 +173,55 @@ void orc_layout(const orc_cfg *c, int64_t out[15]) {
   out[12] = out[9];
   out[13] = out[10];
   out[14] = out[11];
+  out[15] = BH * nblk * orc_keep_count(c);
+  out[16] = out[15] * D * 2;
+}
+
+/* Importance of a key vector: its squared L2 norm, the squares of the fp16 values
+ * (exact in fp64) added in channel order in fp64 ([TQ] section 3.2: importance from the
+ * vector's own norm; section 6.1: the L2 norm directly). */
+static double orc_key_norm2(const uint16_t *row, int D) {
+  double s = 0.0;
+  for (int d = 0; d < D; ++d) {
+    const double x = (double)orc_h2f(row[d]);
+    s += x * x;
+  }
+  return s;
+}
+
+/* The R key vectors of a block kept in fp16 ([TQ] section 3.2: the few important keys
+ * keep high precision, the rest are quantized): the R largest norms, ties to the lower
+ * token; written in ascending token order; their rows are masked out of the block's
+ * statistics and take code 0. */
+static void orc_keep_rows(const orc_cfg *c, int64_t n, const uint16_t *src, uint8_t *mask,
+                          orc_head *hd) {
+  const int D = c->head_dim, Bk = c->k_block, R = orc_keep_count(c);
+  double norm[256];
+  uint8_t kept[256];
+  int sel[64];
+  for (int j = 0; j < Bk; ++j) {
+    norm[j] = orc_key_norm2(src + (int64_t)j * D, D);
+    kept[j] = 0;
+  }
+  for (int r = 0; r < R; ++r) {
+    int best = -1;
+    for (int j = 0; j < Bk; ++j) {
+      if (kept[j]) continue;
+      if (best < 0 || norm[j] > norm[best]) best = j;
+    }
+    kept[best] = 1;
+    sel[r] = best;
+  }
+  for (int a = 1; a < R; ++a)
+    for (int b = a; b > 0 && sel[b - 1] > sel[b]; --b) {
+      int t = sel[b]; sel[b] = sel[b - 1]; sel[b - 1] = t;
+    }
+  for (int r = 0; r < R; ++r) {
+    const int j = sel[r];
+    hd->k_keep_idx[n * R + r] = (uint8_t)j;
+    memcpy(hd->k_keep_val + (n * R + r) * D, src + (int64_t)j * D, (size_t)D * sizeof(uint16_t));
+    memset(mask + (int64_t)j * D, 1, (size_t)D);
+  }
 }
 
 /* ------------------------------------------------------------------------- */
@@ -312,6 +369,8 @@ int orc_quantize_block(const orc_cfg *c, int is_key, int64_t n, const uint16_t *
       rp[t0 + j + 1] = (int32_t)((t0 + j + 1) * kout);
     }
   }
+  /* 1b. the block's important key vectors, kept in fp16 */
+  if (is_key && orc_keep_count(c) > 0) orc_keep_rows(c, n, src, mask, hd);
   /* 2. clip threshold over the whole block (outliers included), 3. dense values */
   const int clip = c->clip_quantile > 0.0f;
   const float thr = clip ? orc_clip_threshold(src, nel, c->clip_quantile) : 0.0f;
@@ -471,6 +530,13 @@ static void orc_dequant_row(const orc_cfg *c, const orc_head *hd, int which, int
     const uint16_t *val = which ? hd->v_val : hd->k_val;
     const int32_t *rp = which ? hd->v_rowptr : hd->k_rowptr;
     for (int32_t r = rp[t]; r < rp[t + 1]; ++r) out[col[r]] = orc_h2f(val[r]);
+  }
+  const int R = orc_keep_count(c);
+  if (which == 0 && R > 0) {  /* a key kept in fp16 is read exactly */
+    const int64_t n = t / Bk;
+    for (int r = 0; r < R; ++r)
+      if (hd->k_keep_idx[n * R + r] == (uint8_t)(t % Bk))
+        for (int ch = 0; ch < D; ++ch) out[ch] = orc_h2f(hd->k_keep_val[(n * R + r) * D + ch]);
   }
 }
 

@@ -32,11 +32,12 @@ class KvqConfig(C.Structure):
                 ("head_dim", C.c_int32), ("capacity", C.c_int32), ("k_bits", C.c_int32),
                 ("k_mode", C.c_int32), ("k_block", C.c_int32), ("v_bits", C.c_int32),
                 ("v_group", C.c_int32), ("clip_quantile", C.c_float), ("outlier_pct", C.c_int32),
-                ("rope_theta", C.c_float)]
+                ("rope_theta", C.c_float), ("keep_pct", C.c_int32)]
 
 
 BUFFERS = ["k_codes", "k_scale", "k_zero", "k_lut", "k_tail", "v_codes", "v_scale", "v_zero",
-           "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val", "rope"]
+           "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val", "rope",
+           "k_keep_idx", "k_keep_val"]
 
 
 class KvqLayout(C.Structure):
@@ -216,6 +217,7 @@ def _check_tensor(t, name: str, shape: tuple, dtype, device) -> None:
 def make_config(cfg: dict) -> KvqConfig:
     d = dict(cfg)
     d.setdefault("capacity", d.get("tokens"))
+    d.setdefault("keep_pct", 0)
     return KvqConfig(**{k: d[k] for k in _CFG_FIELDS})
 
 

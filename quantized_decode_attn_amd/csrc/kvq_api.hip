@@ -22,6 +22,7 @@ kvq_status check_cfg(const kvq_config* c) {
   if (!(c->clip_quantile >= 0.0f && c->clip_quantile < 1.0f)) return KVQ_EINVAL;
   if (c->outlier_pct < 0 || c->outlier_pct > 100) return KVQ_EINVAL;
   if (!(c->rope_theta > 1.0f) || !isfinite(c->rope_theta)) return KVQ_EINVAL;
+  if (c->keep_pct < 0 || c->keep_pct > 100) return KVQ_EINVAL;
   // what the kernels are built for
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_EUNSUPPORTED;
   if (c->k_bits < 2 || c->k_bits > 4) return KVQ_EUNSUPPORTED;
@@ -31,6 +32,10 @@ kvq_status check_cfg(const kvq_config* c) {
   if (c->k_block != 64 && c->k_block != 128) return KVQ_EUNSUPPORTED;
   if (c->q_heads / c->kv_heads > 8) return KVQ_EUNSUPPORTED;
   if (kvq::host_kout(*c) > 4) return KVQ_EUNSUPPORTED;
+  // kept fp16 keys: up to 16 per block, with uniform keys, no outliers, no clipping
+  if (kvq::keep_count(*c) > 16) return KVQ_EUNSUPPORTED;
+  if (c->keep_pct > 0 && (c->k_mode != 0 || c->outlier_pct > 0 || c->clip_quantile > 0.0f))
+    return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -47,6 +52,7 @@ kvq_status check_cache(const kvq_cache* cache) {
   if (kvq::host_kout(c) > 0 && (!cache->k_rowptr || !cache->k_col || !cache->k_val ||
                                 !cache->v_rowptr || !cache->v_col || !cache->v_val))
     return KVQ_EINVAL;
+  if (kvq::keep_count(c) > 0 && (!cache->k_keep_idx || !cache->k_keep_val)) return KVQ_EINVAL;
   if (cache->length < 0 || cache->length > c.capacity) return KVQ_EINVAL;
   // per-sequence lengths (both copies or neither); a block table needs them
   if (!cache->seq_lens != !cache->seq_lens_host) return KVQ_EINVAL;
@@ -221,6 +227,9 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout* out) {
     out->v_val = out->k_val;
   }
   out->rope = ((size_t)c.k_block + nblk) * (D / 2) * 2 * 4;
+  const size_t R = kvq::keep_count(c);
+  out->k_keep_idx = BH * nblk * R;
+  out->k_keep_val = BH * nblk * R * D * 2;
   return KVQ_OK;
 }
 
@@ -243,6 +252,8 @@ kvq_status kvq_paged_layout(const kvq_config* cfg, int32_t num_blocks, kvq_layou
   per(out->k_val);
   per(out->v_col);
   per(out->v_val);
+  per(out->k_keep_idx);
+  per(out->k_keep_val);
   if (out->k_rowptr) {
     out->k_rowptr = slots * (cfg->k_block + 1) * 4;
     out->v_rowptr = out->k_rowptr;

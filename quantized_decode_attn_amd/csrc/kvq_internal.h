@@ -13,6 +13,11 @@ inline int host_kout(const kvq_config& c) {
   return c.outlier_pct > 0 ? (c.outlier_pct * c.head_dim + 99) / 100 : 0;
 }
 
+// Key vectors kept in fp16 per quantized block (keep_pct > 0).
+__host__ __device__ inline int keep_count(const kvq_config& c) {
+  return c.keep_pct > 0 ? (c.keep_pct * c.k_block + 99) / 100 : 0;
+}
+
 hipError_t launch_rope_init(const kvq_cache& c, hipStream_t s);
 
 // Quantize the complete blocks [n_first, n_first + nblocks) of every (b, kv-head).

@@ -71,6 +71,7 @@ static kvq_cache fake_cache(const kvq_config& c, int64_t length) {
   k.k_rowptr = (int32_t*)p(lay.k_rowptr); k.k_col = (uint8_t*)p(lay.k_col); k.k_val = (uint16_t*)p(lay.k_val);
   k.v_rowptr = (int32_t*)p(lay.v_rowptr); k.v_col = (uint8_t*)p(lay.v_col); k.v_val = (uint16_t*)p(lay.v_val);
   k.rope = (float*)p(lay.rope);
+  k.k_keep_idx = (uint8_t*)p(lay.k_keep_idx); k.k_keep_val = (uint16_t*)p(lay.k_keep_val);
   return k;
 }
 
@@ -109,6 +110,25 @@ int main() {
     EXPECT(kvq_cache_layout(&c, &lay) == b.want);
   }
   EXPECT(kvq_cache_layout(nullptr, &lay) == KVQ_EINVAL);
+  {  // keys kept in fp16: count, sizes, the combinations refused
+    kvq_config c = base();
+    c.keep_pct = 5;  // 6.4 -> 7 per block of 128
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EUNSUPPORTED);  // with outliers and clipping
+    c.outlier_pct = 0; c.clip_quantile = 0.0f;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_OK);
+    EXPECT(lay.k_keep_idx == (size_t)2 * 2 * 8 * 7 && lay.k_keep_val == lay.k_keep_idx * 128 * 2);
+    c.keep_pct = 13;  // 17 per block
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EUNSUPPORTED);
+    c.keep_pct = -1;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EINVAL);
+    c.keep_pct = 5; c.k_mode = 1;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EUNSUPPORTED);
+    c.k_mode = 0;
+    kvq_cache kk = fake_cache(c, 0);
+    EXPECT(kvq_cache_init(&kk, nullptr) == KVQ_EHIP);
+    kk.k_keep_val = nullptr;
+    EXPECT(kvq_cache_init(&kk, nullptr) == KVQ_EINVAL);
+  }
   EXPECT(kvq_cache_layout(nullptr, nullptr) == KVQ_EINVAL);
 
   // init, append, decode, dequantize: checks first, then the (stubbed) launch fails

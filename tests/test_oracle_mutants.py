@@ -37,6 +37,14 @@ MUTANTS = {
     "chunk_sees_whole_cache": ("if (nvis > hd->length) nvis = hd->length;", "nvis = hd->length;"),
     "chunk_rotates_all_rows_at_first_position": ("q_pos + j, nvis,", "q_pos, nvis,"),
     "chunk_row_offset_ignored": ("out + (int64_t)j * c->head_dim))", "out))"),
+    "keep_smallest_norm": ("if (best < 0 || norm[j] > norm[best]) best = j;",
+                           "if (best < 0 || norm[j] < norm[best]) best = j;"),
+    "keep_tie_higher_token": ("if (best < 0 || norm[j] > norm[best]) best = j;",
+                              "if (best < 0 || norm[j] >= norm[best]) best = j;"),
+    "keep_norm_l1": ("    s += x * x;", "    s += fabs(x);"),
+    "kept_rows_in_stats": ("    memset(mask + (int64_t)j * D, 1, (size_t)D);\n", ""),
+    "kept_key_read_quantized": ("out[ch] = orc_h2f(hd->k_keep_val[(n * R + r) * D + ch]);", "out[ch] = out[ch];"),
+    "keep_count_floor": ("(c->keep_pct * c->k_block + 99) / 100", "(c->keep_pct * c->k_block) / 100"),
 }
 
 

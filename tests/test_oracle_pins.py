@@ -625,3 +625,108 @@ def test_chunk_ignores_tokens_after_each_query(orc):
     oa, ob = a.chunk(q, 35), b.chunk(q, 35)               # rows see 36 .. 43 tokens
     assert np.array_equal(oa[:5], ob[:5])                  # rows 0..4 see t <= 39
     assert all(np.max(np.abs(oa[j] - ob[j])) > 1e-6 for j in range(5, 8))
+
+
+# --------------------------------------------------------------------------- keys kept in fp16
+# [TQ] section 3.2: the few key vectors judged important by their own norm keep fp16, the
+# rest are quantized; section 6.1: the L2 norm directly.
+def _exact_norm2(row_bits):
+    return math.fsum(float(x) ** 2 for x in hval(row_bits))
+
+
+def test_keep_selects_largest_l2_norms(orc):
+    """Per block the ceil(p Bk / 100) tokens of largest exact squared L2 norm (ties to
+    the lower token) are kept, in ascending order, with their exact rows.  The block
+    plants a tie among the top norms and a token whose L1 norm is large but whose L2
+    norm is not."""
+    rng = np.random.default_rng(61)
+    D, Bk, T = 16, 16, 48
+    c = tiny(head_dim=D, k_block=Bk, tokens=T, v_group=D, keep_pct=15)    # 2.4 -> 3 per block
+    x = rng.standard_normal((T, D))
+    x[3] = 4.0                   # block 0: tokens 3 and 9 tie at the top
+    x[9] = x[3]
+    for j, a in ((17, 15.0), (22, 15.5), (27, 16.0)):     # block 1: one large element each:
+        x[j] = 0.0                                        # L2^2 225 to 256, L1 15 to 16
+        x[j, 5] = a
+    x[20] = 3.5                  # L1 56 (largest by L1), L2^2 196: not kept
+    k = f16(x)
+    v = f16(rng.standard_normal((T, D)))
+    assert orc.keep_count(c) == 3
+    hc = orc.HeadCache(c).build(k, v)
+    for n in range(T // Bk):
+        norms = [_exact_norm2(k[n * Bk + j]) for j in range(Bk)]
+        order = sorted(range(Bk), key=lambda j: (-norms[j], j))[:3]
+        want = sorted(order)
+        got = list(hc.k_keep_idx[n * 3:(n + 1) * 3])
+        assert got == want, (n, got, want)
+        for r, j in enumerate(want):
+            assert np.array_equal(hc.k_keep_val[n * 3 + r], k[n * Bk + j])
+    assert 3 in hc.k_keep_idx[:3] and 9 in hc.k_keep_idx[:3]           # the tie: both fit
+    assert list(hc.k_keep_idx[3:6]) == [1, 6, 11]                      # offsets in block 1
+
+
+def test_keep_tie_goes_to_the_lower_token(orc):
+    rng = np.random.default_rng(62)
+    D, Bk = 16, 16
+    c = tiny(head_dim=D, k_block=Bk, tokens=Bk, v_group=D, keep_pct=5)     # 0.8 -> 1
+    x = rng.standard_normal((Bk, D)) * 0.1
+    x[6] = 2.0
+    x[11] = 2.0
+    hc = orc.HeadCache(c).build(f16(x), f16(x))
+    assert list(hc.k_keep_idx) == [6]
+
+
+def test_kept_rows_leave_the_statistics(orc):
+    """A kept token takes no part in its block's per-channel statistics: the block's
+    scale, zero and the other tokens' codes equal those of the same block with the kept
+    row replaced by a copy of a neighbour (which changes no minimum or maximum) and
+    nothing kept."""
+    rng = np.random.default_rng(63)
+    D, Bk = 16, 16
+    x = rng.standard_normal((Bk, D))
+    x[5] *= 9.0
+    c = tiny(head_dim=D, k_block=Bk, tokens=Bk, v_group=D, keep_pct=5)
+    a = orc.HeadCache(c).build(f16(x), f16(x))
+    assert list(a.k_keep_idx) == [5]
+    y = x.copy()
+    y[5] = y[4]
+    b = orc.HeadCache(tiny(head_dim=D, k_block=Bk, tokens=Bk, v_group=D)).build(f16(y), f16(x))
+    assert np.array_equal(a.k_scale, b.k_scale) and np.array_equal(a.k_zero, b.k_zero)
+    ka, kb_ = _deq(a, 0), _deq(b, 0)
+    rows = [j for j in range(Bk) if j != 5]
+    assert np.array_equal(ka[rows], kb_[rows])
+    assert np.array_equal(ka[5], hval(f16(x[5])))                        # read exactly
+
+
+def test_kept_keys_are_exact_in_textbook_attention(orc):
+    """On-grid keys plus, in every block, two off-grid keys of much larger norm: with two
+    keys kept per block the cache dequantizes exactly, so the decode equals plain fp64
+    softmax attention with rotary matrices on the raw inputs; without keeping it does
+    not."""
+    rng = np.random.default_rng(64)
+    D, Bk, T = 16, 16, 48
+    L = 15
+    k = _on_grid(rng, T, D, Bk, L, True)
+    for n in range(T // Bk):
+        for j in (n * Bk + 2, n * Bk + 13):
+            k[j] = rng.standard_normal(D) * 8.0 + 20.0
+    v = _on_grid(rng, T, D, Bk, L, False)
+    kb, vb = f16(k), f16(v)
+    c = tiny(head_dim=D, k_block=Bk, tokens=T, v_group=D, keep_pct=10)   # 1.6 -> 2
+    hc = orc.HeadCache(c).build(kb, vb)
+    assert np.array_equal(_deq(hc, 0), hval(kb))
+    q = f16(rng.standard_normal(D))
+    qp = T - 1
+    qr = _rot_matrix(qp, D, 10000.0) @ hval(q)
+    kr = np.stack([_rot_matrix(t, D, 10000.0) @ hval(kb[t]) for t in range(T)])
+    ref = _softmax_attn(qr, kr, hval(vb), D)
+    assert np.max(np.abs(hc.decode(q, q_pos=qp) - ref)) < 1e-12
+    plain = orc.HeadCache(tiny(head_dim=D, k_block=Bk, tokens=T, v_group=D)).build(kb, vb)
+    assert np.max(np.abs(plain.decode(q, q_pos=qp) - ref)) > 1e-6
+
+
+def test_keep_layout_sizes(orc):
+    c = tiny(head_dim=16, k_block=16, tokens=64, v_group=16, keep_pct=15, batch=2, kv_heads=3, q_heads=3)
+    lay = orc.layout(c)
+    assert lay["k_keep_idx"] == 2 * 3 * 4 * 3 and lay["k_keep_val"] == 2 * 3 * 4 * 3 * 16 * 2
+    assert orc.layout(tiny())["k_keep_idx"] == 0
