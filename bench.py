@@ -59,19 +59,26 @@ def kout(cfg):
     return (p * cfg["head_dim"] + 99) // 100 if p > 0 else 0
 
 
+def keep_count(cfg) -> int:
+    p = cfg.get("keep_pct", 0)
+    return (p * cfg["k_block"] + 99) // 100 if p > 0 else 0
+
+
 def decode_bytes_per_token_head(cfg) -> float:
     """Bytes one decode must read per (b, kv-head, token): packed key and value codes,
     key scale/zero amortised over the block, value scale/zero, outlier columns and
-    values.  The CSR row pointers (4 B per token and tensor) are not counted: every
-    quantized token holds exactly ceil(pct * D / 100) entries, so a reader computes
-    the offsets and never loads the pointers."""
+    values, and the keys kept in fp16 (one offset byte and 2 D bytes each, amortised
+    over the block).  The CSR row pointers (4 B per token and tensor) are not counted:
+    every quantized token holds exactly ceil(pct * D / 100) entries, so a reader
+    computes the offsets and never loads the pointers."""
     D, Bk, ko = cfg["head_dim"], cfg["k_block"], kout(cfg)
     rk = D * cfg["k_bits"] / 8
     rv = D * cfg["v_bits"] / 8
     kmeta = 2 * D * 2 / Bk if cfg["k_mode"] == 0 else 0.0
     vmeta = (D // cfg["v_group"]) * 2 * 2
     csr = 2 * ko * 3
-    return rk + rv + kmeta + vmeta + csr
+    kept = keep_count(cfg) * (1 + 2 * D) / Bk
+    return rk + rv + kmeta + vmeta + csr + kept
 
 
 def decode_bytes(cfg, T) -> float:
@@ -343,6 +350,8 @@ def main():
     ap.add_argument("--chunk-splits", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=0, help="also time this many token-by-token steps")
     ap.add_argument("--paged", action="store_true", help="also time a paged cache with mixed sequence lengths")
+    ap.add_argument("--keep-pct", type=int, default=0,
+                    help="the workload with this percentage of each block's keys kept in fp16 by norm")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -354,6 +363,9 @@ def main():
         return
 
     cfg = synth.config(args.workload)
+    if args.keep_pct:
+        cfg["keep_pct"] = args.keep_pct
+        cfg["workload"] += "-keep%dpct" % args.keep_pct
     T, B, H, Hq, D = cfg["tokens"], cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
     existing = cfg["existing"]
     log("workload", args.workload, cfg["workload"])
@@ -463,7 +475,7 @@ def main():
         "config": {"workload": cfg["workload"], "batch": B, "q_heads": Hq, "kv_heads": H,
                    "head_dim": D, "tokens": T, "appended_per_step": n_new, "k_bits": cfg["k_bits"],
                    "v_bits": cfg["v_bits"], "k_block": cfg["k_block"], "v_group": cfg["v_group"],
-                   "splits": args.splits or "auto"},
+                   "splits": args.splits or "auto", "keep_pct": cfg.get("keep_pct", 0)},
         "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "decode_us": round(float(dec_ms.mean()) * 1e3, 2),
         "append_us": round(float(app_ms.mean()) * 1e3, 2),

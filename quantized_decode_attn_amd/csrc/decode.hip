@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
   const int H = c.cfg.kv_heads, Hq = c.cfg.q_heads, GQ = Hq / H, R = GQ * rs.nq;
   const int G = c.cfg.v_group, ng = D / G;
   const int ko = kout_of(c.cfg);
+  const int NK = keep_count(c.cfg);  // keys kept in fp16 per block
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ts = lane / Sh::LPT, r = lane % Sh::LPT;
 
@@ -194,6 +195,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       const int64_t gs = tail ? 0 : slot_of(c, b, h, n);
       const uint8_t* kblk = static_cast<const uint8_t*>(c.k_codes) + gs * Bk * (D * KB / 8);
       const uint32_t* vblk = static_cast<const uint32_t*>(c.v_codes) + gs * (Bk / Sh::TPW) * D;
+      // the block's keys kept in fp16: one bit per token offset (Bk <= 128), and a kept
+      // token's place among them (their rows are stored in ascending token order)
+      uint32_t km[4] = {0u, 0u, 0u, 0u};
+      if (!tail && NK > 0)
+        for (int r2 = 0; r2 < NK; ++r2) {
+          const uint32_t jj = c.k_keep_idx[gs * NK + r2];
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) km[q2] |= (jj >> 5) == (uint32_t)q2 ? 1u << (jj & 31u) : 0u;
+        }
+      auto kept_pos = [&](int j) -> int {
+        const int wsel = j >> 5, bit = j & 31;
+        int pos = 0;
+        uint32_t wd = 0u;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          if (q2 < wsel) pos += __builtin_popcount(km[q2]);
+          if (q2 == wsel) wd = km[q2];
+        }
+        if (!((wd >> bit) & 1u)) return -1;
+        return pos + __builtin_popcount(wd & ((1u << bit) - 1u));
+      };
 
       // value metadata of the block (quantized blocks only)
       if (!tail) {
@@ -253,7 +275,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
           float s = 0.0f;
           if (j < ntok) {
             const float* tab = table + j * Sh::TPITCH + 2 * r * Sh::PPL;
-            if (!tail) {
+            const int kp = tail || NK == 0 ? -1 : kept_pos(j);
+            if (!tail && kp < 0) {
               uint32_t w[Sh::KW];
               const uint32_t* src = reinterpret_cast<const uint32_t*>(
                   kblk + j * (D * KB / 8) + r * (Sh::KW * 4));
@@ -292,7 +315,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
                 s += col < Sh::HALF ? dlt * (wr * cs - wi * sn) : -dlt * (wi * cs + wr * sn);
               }
             } else {
-              const uint16_t* kr = j == nt.jnew ? nt.k + bh * D : c.k_tail + (bh * Bk + j) * D;
+              // an fp16 key: a kept key of a quantized block, or a tail token (the step's
+              // new token read from the input)
+              const uint16_t* kr = !tail ? c.k_keep_val + (gs * NK + kp) * D
+                                         : (j == nt.jnew ? nt.k + bh * D : c.k_tail + (bh * Bk + j) * D);
 #pragma unroll
               for (int m = 0; m < Sh::PPL; ++m) {
                 const int i = r * Sh::PPL + m;

@@ -49,11 +49,11 @@ constexpr float kW32Span = 4294901760.0f;  // 2^32 - 2^16: full scale of the fix
 struct MLds {
   int wts, s, ps, vcorr, total;
 };
-__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut) {
+__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut, bool keep = false) {
   MLds m;
   int o = 0;
-  // uniform keys: A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB]; codebook keys: WR WI; one array per name
-  m.wts = o; o += (lut ? 2 : outl ? 10 : 6) * (D / 2);
+  // uniform keys: A1 B1 Z1 A2 B2 Z2 [WR WI [ZA ZB]]; codebook keys: WR WI; one array per name
+  m.wts = o; o += (lut ? 2 : outl ? 10 : keep ? 8 : 6) * (D / 2);
   m.s = o; o += BK * (D / 16);                // token scores, as every lane of a token holds it;
                                               // then the fixed-point value weights [2][BK] (u32)
   m.ps = o; o += 256;                         // nibble planes of the value weights [2][16][8]
@@ -108,9 +108,10 @@ __device__ __forceinline__ void load_eb(BlockRegs<D, BK, KB, VB>& R, const kvq_c
 }
 
 // Block weights of the block whose metadata R holds, one rotary pair per lane, into the
-// wave's LDS area: codebook keys WR WI; uniform keys A1 B1 Z1 A2 B2 Z2 [WR WI ZA ZB]
-// (W = query weight rotated by the block's first position, folded with scale and zero).
-template <int D, int BK, int KB, int VB, int KO, bool LUT>
+// wave's LDS area: codebook keys WR WI; uniform keys A1 B1 Z1 A2 B2 Z2, then WR WI ZA ZB
+// with outliers, WR WI with kept fp16 keys (W = query weight rotated by the block's
+// first position, folded with scale and zero).
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool KEEP = false>
 __device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, VB>& R, float* wb, float wq_r,
                                                     float wq_i, float inv_unit, int lane) {
   constexpr int HALF = D / 2;
@@ -132,16 +133,18 @@ __device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, V
     wb[3 * HALF + lane] = -wi * al * ua;           // A2
     wb[4 * HALF + lane] = -wr * be * ub;           // B2
     wb[5 * HALF + lane] = -(wi * za + wr * zb);    // Z2
-    if constexpr (KO > 0) {
+    if constexpr (KO > 0 || KEEP) {
       wb[6 * HALF + lane] = wr;                    // WR
       wb[7 * HALF + lane] = wi;                    // WI
+    }
+    if constexpr (KO > 0) {
       wb[8 * HALF + lane] = za;                    // ZA
       wb[9 * HALF + lane] = zb;                    // ZB
     }
   }
 }
 
-template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG>
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG, bool KEEP>
 __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTok& C, MState& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               const uint32_t* __restrict__ ptab, float wq_r, float wq_i,
@@ -177,6 +180,22 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   // before the next block)
   load_vmeta(R, c, g, lane, ng);
   if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, g, lane);
+  // keys of this block kept in fp16 (at most 16 rows, stored in ascending token order):
+  // lane covers rotary pairs 16 (lane & 3) .. +16 of kept row lane >> 2, channels of both
+  // halves; loaded here, used right after the score loop.  Lanes past the last row
+  // reload it.
+  uint4 kpa[2], kpb[2];
+  uint32_t kpj = 0;
+  const int NK = KEEP ? keep_count(c.cfg) : 0;
+  if constexpr (KEEP) {
+    const int64_t row = g * NK + min(lane >> 2, NK - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(c.k_keep_val + row * D + 16 * (lane & 3));
+    kpa[0] = src[0];
+    kpa[1] = src[1];
+    kpb[0] = src[Sh::HALF / 8];
+    kpb[1] = src[Sh::HALF / 8 + 1];
+    kpj = c.k_keep_idx[row];
+  }
 
   // ---- the next block's metadata (its weights are written during this block's values)
   if constexpr (LUT) load_eb(R, c, nn, lane);
@@ -302,6 +321,40 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     }
   }
   wave_lds_sync();
+
+  if constexpr (KEEP) {
+    // exact scores of the kept keys, in place of the ones their stored code 0 gave:
+    // sum_i a_i (wr_i cos - wi_i sin) - b_i (wi_i cos + wr_i sin) at the token's offset
+    const float* wWRk = wl + L.wts + 6 * Sh::HALF;
+    const float* wWIk = wWRk + Sh::HALF;
+    const int i0 = 16 * (lane & 3);
+    const float* tj = table + (int)(kpj & (BK - 1)) * Sh::TPITCH;
+    const uint32_t* ha = reinterpret_cast<const uint32_t*>(kpa);
+    const uint32_t* hb = reinterpret_cast<const uint32_t*>(kpb);
+    float s = 0.0f;
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+      const float4 wr4 = *reinterpret_cast<const float4*>(wWRk + i0 + 4 * m4);
+      const float4 wi4 = *reinterpret_cast<const float4*>(wWIk + i0 + 4 * m4);
+      const float wr[4] = {wr4.x, wr4.y, wr4.z, wr4.w}, wi[4] = {wi4.x, wi4.y, wi4.z, wi4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int m = 4 * m4 + u;
+        const float2 cssn = *reinterpret_cast<const float2*>(tj + Sh::tab_off(i0 + m));
+        const float a = h2f((uint16_t)(ha[m >> 1] >> (16 * (m & 1))));
+        const float bb = h2f((uint16_t)(hb[m >> 1] >> (16 * (m & 1))));
+        s = __builtin_fmaf(a, __builtin_fmaf(wr[u], cssn.x, -wi[u] * cssn.y), s);
+        s = __builtin_fmaf(-bb, __builtin_fmaf(wi[u], cssn.x, wr[u] * cssn.y), s);
+      }
+    }
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+    if ((lane & 3) == 0 && (lane >> 2) < NK) {
+      const int t = (int)(kpj & (BK - 1));
+      Sc[((t / Sh::TPI) >> 2) * (4 * kWave) + (t % Sh::TPI) * (4 * Sh::LPT) + ((t / Sh::TPI) & 3)] = s;
+    }
+    wave_lds_sync();
+  }
 
   // the block's serial part (softmax, value weights, planes, value dot products) runs at
   // a raised wave priority, so that its short dependency chains win issue slots over the
@@ -442,7 +495,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 
   // ---- the next block's weights: this block's were last read by its softmax (key
   // outliers); writing them here lets their LDS round trip overlap the value dot products
-  write_block_weights<D, BK, KB, VB, KO, LUT>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
+  write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
 
   // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
   // sum_t w_t * code_t by 4-bit integer dot products over the eight weight nibbles, in
@@ -528,7 +581,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 
 // One (b, head, split) item on one wave: every full block of the split, then the
 // split's (m, l, o) to the workspace.
-template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG>
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG, bool KEEP>
 __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __restrict__ q, int64_t q_pos,
                                          float* __restrict__ ws, int S, int64_t bh, int split, float* wl,
                                          const MLds& L, const float* table, const uint32_t* ptab, int lane) {
@@ -577,7 +630,7 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
     const int64_t g0 = slot_t<PG>(c, b, h, n0);
     if constexpr (LUT) load_eb(R, c, n0, lane);
     else load_kmeta(R, c, g0, n0, lane, 0);
-    write_block_weights<D, BK, KB, VB, KO, LUT>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
+    write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
     const uint8_t* kb0 = k_block<D, BK, KB, VB>(c, g0);
     const uint8_t* vb0 = v_block<D, BK, KB, VB>(c, g0);
 #pragma unroll
@@ -586,7 +639,7 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
     for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
   }
   for (int64_t n = n0; n < nfull; n += S)
-    process_block<D, BK, KB, VB, KO, LUT, PG>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
+    process_block<D, BK, KB, VB, KO, LUT, PG, KEEP>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
                                           c, b, h, n, S, n + S < nfull, koff);
   if (OUTL) {
     wave_lds_sync();
@@ -628,8 +681,8 @@ __device__ __forceinline__ void stage_rope(float* table, const kvq_cache& c) {
 }
 
 // Uniform keys: every wave takes items on its own.  PG: per-sequence lengths (dense or
-// paged slots).
-template <int D, int BK, int KB, int VB, int KO, bool PG>
+// paged slots); KEEP: keys kept in fp16 by norm.
+template <int D, int BK, int KB, int VB, int KO, bool PG, bool KEEP = false>
 __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
                                                                    int64_t nitems) {
@@ -642,7 +695,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
 
   float* table = lds;
   stage_rope<D, BK, kNT>(table, c);
-  const MLds L = mha_lds(D, BK, OUTL, false);
+  const MLds L = mha_lds(D, BK, OUTL, false, KEEP);
   float* wl = lds + BK * Sh::TPITCH + wave * L.total;
   if (OUTL)
     for (int k = lane; k < D + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
@@ -650,7 +703,8 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
 
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
   for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves)
-    mha_item<D, BK, KB, VB, KO, false, PG>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table, nullptr, lane);
+    mha_item<D, BK, KB, VB, KO, false, PG, KEEP>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table, nullptr,
+                                                 lane);
 }
 
 // Codebook keys: the workgroup takes groups of up to 8 splits of one (b, head), so
@@ -688,7 +742,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
       ptab[i * PT::PITCH + pc] = ka | (kb << 16);
     }
     __syncthreads();
-    if (split < S) mha_item<D, BK, KB, VB, 0, true, PG>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
+    if (split < S) mha_item<D, BK, KB, VB, 0, true, PG, false>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
   }
 }
 
@@ -699,21 +753,21 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus, bool dry);
 
-template <int D, int BK, int KB, int VB, int KO, bool PG = false>
+template <int D, int BK, int KB, int VB, int KO, bool PG = false, bool KEEP = false>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                    hipStream_t s, int cus, bool dry) {
   using Sh = MShape<D, BK, KB, VB>;
-  const MLds L = mha_lds(D, BK, KO > 0, false);
+  const MLds L = mha_lds(D, BK, KO > 0, false, KEEP);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
   if (dry) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO, PG>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
   int64_t grid = (nitems + kMhaWaves - 1) / kMhaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO, PG>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
+  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
                      q, q_pos, ws, S, nitems);
   return hipGetLastError();
 }
@@ -744,6 +798,19 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ng = g.head_dim / g.v_group;
   if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
+  if (g.keep_pct > 0) {
+    // keys kept in fp16 (uniform keys without outliers): 4-bit keys at head_dim 128 and
+    // 128-token blocks, dense or per-sequence; every other configuration takes the
+    // generic kernel
+    if (D != 128 || BK != 128 || KB != 4 || g.k_mode != 0 || ko != 0) return hipErrorNotSupported;
+    if (VB == 4)
+      return c.seq_lens ? launch_mha_typed<128, 128, 4, 4, 0, true, true>(c, q, q_pos, ws, S, s, cus, dry)
+                        : launch_mha_typed<128, 128, 4, 4, 0, false, true>(c, q, q_pos, ws, S, s, cus, dry);
+    if (VB == 2)
+      return c.seq_lens ? launch_mha_typed<128, 128, 4, 2, 0, true, true>(c, q, q_pos, ws, S, s, cus, dry)
+                        : launch_mha_typed<128, 128, 4, 2, 0, false, true>(c, q, q_pos, ws, S, s, cus, dry);
+    return hipErrorNotSupported;
+  }
   if (c.seq_lens) {
     // per-sequence lengths (dense or paged slots): uniform 4-bit keys and 2/3-bit
     // codebook keys at head_dim 128; every other configuration takes the generic kernel

@@ -1,8 +1,8 @@
 // dequantize.hip -- packed cache -> fp32 values (pre-RoPE).
 //
 // x = fmaf(code, scale, zero) with one fp32 rounding, or the codebook entry for
-// codebook keys; outlier positions take their exact fp16 value from the CSR and the
-// tail tokens are exact.  This is the read-side inverse of the per-block scale and
+// codebook keys; outlier positions take their exact fp16 value from the CSR, kept keys
+// their fp16 rows, and the tail tokens are exact.  This is the read-side inverse of the per-block scale and
 // zero-point storage of "【LLM量化技术介绍-3】KV Cache量化技术介绍"
 // (developer.horizon.auto/blog/13163), section "Quanto 的量化原理".
 #include "kvq_device.h"
@@ -55,6 +55,12 @@ __global__ void dequantize_kernel(kvq_cache c, int which, int64_t t0, int64_t t1
       const uint16_t* val = which ? c.v_val : c.k_val;
       for (int r = 0; r < ko; ++r)
         if (col[(bh * T + t) * ko + r] == ch) x = h2f(val[(bh * T + t) * ko + r]);
+    }
+    const int R = keep_count(c.cfg);
+    if (t < nfull && which == 0 && R > 0) {  // a key kept in fp16 reads back exactly
+      const int64_t slot = bh * (T / Bk) + t / Bk;
+      for (int r = 0; r < R; ++r)
+        if (c.k_keep_idx[slot * R + r] == (uint8_t)(t % Bk)) x = h2f(c.k_keep_val[(slot * R + r) * D + ch]);
     }
     out[bh * (t1 - t0) * D + i] = x;
   }

@@ -512,7 +512,7 @@ constexpr int kCandCap = 256;  // clip candidates per wave
 struct ClipSmem {
   uint32_t hist[256];
   uint32_t ncand[kThreads / kWave];
-  uint16_t cand[kThreads / kWave][kCandCap];
+  alignas(8) uint16_t cand[kThreads / kWave][kCandCap];  // (kept-key norms when not clipping)
 };
 
 // The largest 15-bit magnitude of each of the thread's staged chunks.
@@ -832,6 +832,59 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uin
   return thr;
 }
 
+// ---------------------------------------------------------------- keys kept in fp16
+// The R key vectors of the block with the largest squared L2 norm ([TQ] sections 3.2
+// and 6.1: importance from the vector's own norm, the important few kept in high
+// precision): thread j < BK squares its token's fp16 values exactly in fp64 and adds
+// them in channel order; a token is kept when fewer than R tokens come before it in
+// (norm descending, token ascending).  The kept rows are copied out in ascending token
+// order and then marked with the outlier mark in the tile, which takes them out of the
+// per-channel statistics and gives them code 0.  norm: BK doubles, flag: BK ints.
+template <int D, int BK>
+__device__ __forceinline__ void keep_rows(uint16_t* tile, double* norm, int* flag, const kvq_cache& c, int64_t g) {
+  constexpr int P = D + 8;
+  const int R = keep_count(c.cfg);
+  const int tid = threadIdx.x;
+  if (tid < BK) {
+    double s = 0.0;
+    for (int d = 0; d < D; d += 8) {
+      const uint4 w = *reinterpret_cast<const uint4*>(&tile[tid * P + d]);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const double x = (double)h2f((uint16_t)(ws[k >> 1] >> (16 * (k & 1))));
+        s += x * x;  // the square is exact; one rounding per addition, in channel order
+      }
+    }
+    norm[tid] = s;
+  }
+  __syncthreads();
+  if (tid < BK) {
+    const double m = norm[tid];
+    int before = 0;
+    for (int k = 0; k < BK; ++k) {
+      const double o = norm[k];
+      before += (o > m || (o == m && k < tid)) ? 1 : 0;
+    }
+    flag[tid] = before < R ? 1 : 0;
+  }
+  __syncthreads();
+  if (tid < BK && flag[tid]) {
+    int pos = 0;
+    for (int k = 0; k < tid; ++k) pos += flag[k];
+    c.k_keep_idx[g * R + pos] = (uint8_t)tid;
+    uint16_t* dst = c.k_keep_val + (g * R + pos) * D;
+    for (int d = 0; d < D; d += 8)
+      *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(&tile[tid * P + d]);
+  }
+  __syncthreads();  // every kept row is read before the rows are marked
+  for (int idx = tid; idx < BK * D; idx += kThreads) {
+    const int j = idx / D;
+    if (flag[j]) tile[j * P + idx % D] = kMarkNaN;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- keys
 // A key cell is held as its fp16 bits, two elements per register (element q of token
 // u in half q % 2 of xw[u][q / 2]), and converted where it is used.
@@ -881,12 +934,13 @@ __device__ __forceinline__ void key_codes(const uint32_t (&xw)[8][4], const floa
 // e/2 + (e%2) D/2).  Thread tid = a * NTG + tg; the cell's tokens are tg + NTG u, so
 // the NTG lanes sharing a channel set form one DPP row and read distinct LDS banks.
 // LUTB: 0 for uniform keys (code width from the configuration), else the code width
-// of codebook keys.
-template <int D, int BK, int LUTB, int KO, bool CLIP>
+// of codebook keys.  RET: keys kept in fp16 (uniform keys without outliers or clipping).
+template <int D, int BK, int LUTB, int KO, bool CLIP, bool RET>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_keys_kernel(kvq_cache c, const uint16_t* __restrict__ k_new,
                                                                  int64_t old_len_arg, int64_t n_new, int64_t n_first,
     const int64_t* __restrict__ n_seq) {
-  constexpr bool OUTL = KO != 0;
+  static_assert(!RET || (LUTB == 0 && KO == 0 && !CLIP), "kept keys: uniform keys without outliers or clip");
+  constexpr bool OUTL = KO != 0 || RET;  // kept rows carry the outlier mark
   constexpr int P = D + 8;
   constexpr int NTG = BK / 8;
   constexpr int NA = D / 8;
@@ -912,6 +966,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const float thr =
       prepare_tile<D, BK, KO, CLIP>(sh.u.tile, sh.ocol, sh.oval, sh.clip, sh.red, c, true, k_new, bh, n, g, old_len, n_new);
   __syncthreads();
+  if constexpr (RET)  // the clip's candidate lists are free (no clipping here)
+    keep_rows<D, BK>(sh.u.tile, reinterpret_cast<double*>(sh.clip.cand),
+                     reinterpret_cast<int*>(reinterpret_cast<double*>(sh.clip.cand) + BK), c, g);
 
   const bool active = NA * NTG == kThreads || tid < NA * NTG;
   const int a = tid / NTG, tg = tid % NTG;

@@ -9,11 +9,11 @@
 namespace kvq {
 namespace {
 
-template <int D, int BK, int LUTB, int KO, bool CLIP>
+template <int D, int BK, int LUTB, int KO, bool CLIP, bool RET = false>
 hipError_t launch_k(const kvq_cache& c, const uint16_t* k_new, int64_t old_len, int64_t n_new,
                     int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s) {
   dim3 grid((unsigned)nblocks, (unsigned)c.cfg.kv_heads, (unsigned)c.cfg.batch);
-  hipLaunchKernelGGL((qb::quantize_keys_kernel<D, BK, LUTB, KO, CLIP>), grid, dim3(qb::kThreads), 0, s, c, k_new,
+  hipLaunchKernelGGL((qb::quantize_keys_kernel<D, BK, LUTB, KO, CLIP, RET>), grid, dim3(qb::kThreads), 0, s, c, k_new,
                      old_len, n_new, n_first, n_seq);
   return hipGetLastError();
 }
@@ -25,6 +25,8 @@ hipError_t dispatch_k(const kvq_cache& c, const uint16_t* k_new, int64_t old_len
   // (1..4, read at run time); uniform keys only get the two-outlier specialisation
   const int ko = kvq::host_kout(c.cfg);
   const bool clip = c.cfg.clip_quantile > 0.0f;
+  if constexpr (LUTB == 0)  // keys kept in fp16 (no outliers, no clipping)
+    if (c.cfg.keep_pct > 0) return launch_k<D, BK, 0, 0, false, true>(c, k_new, old_len, n_new, n_first, nblocks, n_seq, s);
 #define KVQ_K(KO)                                                                                  \
   return clip ? launch_k<D, BK, LUTB, KO, true>(c, k_new, old_len, n_new, n_first, nblocks, n_seq, s)     \
               : launch_k<D, BK, LUTB, KO, false>(c, k_new, old_len, n_new, n_first, nblocks, n_seq, s);

@@ -20,11 +20,19 @@ def torch_dev():
     return torch, torch.device("cuda:0")
 
 
+def keep_count(cfg: dict) -> int:
+    p = cfg.get("keep_pct", 0)
+    return (p * cfg["k_block"] + 99) // 100 if p > 0 else 0
+
+
 def per_head_bytes(cfg: dict, ko: int) -> dict:
     D, T, Bk = cfg["head_dim"], cfg["capacity"], cfg["k_block"]
     ng = D // cfg["v_group"]
     uni = cfg["k_mode"] == 0
+    R = keep_count(cfg)
     return {
+        "k_keep_idx": (T // Bk) * R,
+        "k_keep_val": (T // Bk) * R * D * 2,
         "k_codes": T * D * cfg["k_bits"] // 8,
         "k_scale": (T // Bk) * D * 2 if uni else 0,
         "k_zero": (T // Bk) * D * 2 if uni else 0,
@@ -50,7 +58,10 @@ def defined_bytes(cfg: dict, ko: int, length: int) -> dict:
     nt = length - nq
     ng = D // cfg["v_group"]
     uni = cfg["k_mode"] == 0
+    R = keep_count(cfg)
     return {
+        "k_keep_idx": (nq // Bk) * R,
+        "k_keep_val": (nq // Bk) * R * D * 2,
         "k_codes": nq * D * cfg["k_bits"] // 8,
         "k_scale": (nq // Bk) * D * 2 if uni else 0,
         "k_zero": (nq // Bk) * D * 2 if uni else 0,

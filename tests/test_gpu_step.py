@@ -11,7 +11,7 @@ and kvq_decode_attention give the same outputs up to fp32 rounding.
 Split count 0 is the library's choice: the one-launch kernel for a short cache (at most
 four quantized blocks) in a configuration no tuned kernel covers (mha_k3, and gqa_d64
 until its fifth block, where it changes over), else the split kernels (tuned MHA or GQA,
-or the generic one for gqa_d64_long) and the finish kernel.  Split count 3 forces the
+or the generic one for gqa_d64_long and the kept-key cases) and the finish kernel.  Split count 3 forces the
 split kernels.
 """
 import numpy as np
@@ -50,6 +50,11 @@ CASES = {
     "gqa_d64": (synth.config("c0", q_heads=8, kv_heads=2, tokens=5 * 64 + 30, capacity=384), 40),
     "mha_k3": (synth.config("c1", batch=1, q_heads=2, kv_heads=2, k_bits=3, tokens=3 * 128 + 20, capacity=512), 30),
     "gqa_d64_long": (synth.config("c0", q_heads=8, kv_heads=2, tokens=9 * 64 + 10, capacity=640), 20),
+    # keys kept in fp16 by norm: the quantize of a completed block picks them
+    "mha_keep": (synth.config("c1", batch=1, q_heads=2, kv_heads=2, tokens=3 * 128 + 20, capacity=512,
+                              keep_pct=5), 40),
+    "gqa_d64_keep": (synth.config("c0", q_heads=8, kv_heads=2, tokens=5 * 64 + 30, capacity=384,
+                                  keep_pct=12), 40),
 }
 
 
