@@ -512,7 +512,7 @@ constexpr int kCandCap = 256;  // clip candidates per wave
 struct ClipSmem {
   uint32_t hist[256];
   uint32_t ncand[kThreads / kWave];
-  alignas(8) uint16_t cand[kThreads / kWave][kCandCap];  // (kept-key norms when not clipping)
+  alignas(16) uint16_t cand[kThreads / kWave][kCandCap];  // (kept-key norms when not clipping)
 };
 
 // The largest 15-bit magnitude of each of the thread's staged chunks.
@@ -835,52 +835,116 @@ __device__ __forceinline__ float prepare_tile(uint16_t* tile, uint8_t* ocol, uin
 // ---------------------------------------------------------------- keys kept in fp16
 // The R key vectors of the block with the largest squared L2 norm ([TQ] sections 3.2
 // and 6.1: importance from the vector's own norm, the important few kept in high
-// precision): thread j < BK squares its token's fp16 values exactly in fp64 and adds
-// them in channel order; a token is kept when fewer than R tokens come before it in
-// (norm descending, token ascending).  The kept rows are copied out in ascending token
-// order and then marked with the outlier mark in the tile, which takes them out of the
-// per-channel statistics and gives them code 0.  norm: BK doubles, flag: BK ints.
+// precision), the norm being the fp64 sum of the exact squares in channel order.  A
+// token is kept when fewer than R tokens come before it in (norm descending, token
+// ascending).  The kept rows are copied out in ascending token order and marked with
+// the outlier mark in the tile, which takes them out of the per-channel statistics and
+// gives them code 0.
+//
+// The sum is taken in parallel (kThreads / BK threads per token, four chains each).
+// Every square of a row is an integer multiple of 2^m, m set by the row's smallest
+// nonzero exponent, so every partial sum, in any order, is too; while the total stays
+// below 2^(m + 53) each of them is an fp64 number, every addition is exact and the
+// parallel sum equals the channel-order one bit for bit.  A row past that bound (a
+// range of magnitudes beyond 2^26, or a non-finite value) is summed again in channel
+// order by one thread.  norm: BK doubles; flag: 256 ints (the waves' kept-token masks,
+// the kept tokens in order, the rows summed exactly).
 template <int D, int BK>
 __device__ __forceinline__ void keep_rows(uint16_t* tile, double* norm, int* flag, const kvq_cache& c, int64_t g) {
+  static_assert(BK % kWave == 0 && BK <= 128 && kThreads % BK == 0, "whole waves of tokens, offsets in a byte");
   constexpr int P = D + 8;
+  constexpr int TPT = kThreads / BK;  // threads per token
+  constexpr int CH = D / TPT;         // channels per thread
+  static_assert(CH % 8 == 0 && TPT <= kWave, "16-byte row pieces");
+  constexpr int NW = kThreads / kWave;
   const int R = keep_count(c.cfg);
   const int tid = threadIdx.x;
-  if (tid < BK) {
-    double s = 0.0;
-    for (int d = 0; d < D; d += 8) {
-      const uint4 w = *reinterpret_cast<const uint4*>(&tile[tid * P + d]);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int j = tid / TPT, part = tid % TPT;
+  uint32_t* masks = reinterpret_cast<uint32_t*>(flag);  // [NW][2]
+  int* order = flag + 2 * NW;                            // [R <= 16]: kept tokens, ascending
+  int* exact = flag + 64;                                // [BK]
+  {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    uint32_t emin = 31u;  // smallest biased exponent (subnormals as 1) of a nonzero value
+    const uint16_t* row = &tile[j * P + part * CH];
+#pragma unroll
+    for (int d = 0; d < CH; d += 8) {
+      const uint4 w = *reinterpret_cast<const uint4*>(row + d);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const double x = (double)h2f((uint16_t)(ws[k >> 1] >> (16 * (k & 1))));
-        s += x * x;  // the square is exact; one rounding per addition, in channel order
+        const uint16_t hv = (uint16_t)(ws[k >> 1] >> (16 * (k & 1)));
+        const double x = (double)h2f(hv);
+        acc[k & 3] = __builtin_fma(x, x, acc[k & 3]);
+        const uint32_t mag = hv & 0x7fffu;
+        emin = min(emin, mag ? max(mag >> 10, 1u) : 31u);
       }
     }
-    norm[tid] = s;
-  }
-  __syncthreads();
-  if (tid < BK) {
-    const double m = norm[tid];
-    int before = 0;
-    for (int k = 0; k < BK; ++k) {
-      const double o = norm[k];
-      before += (o > m || (o == m && k < tid)) ? 1 : 0;
+    double sm = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+#pragma unroll
+    for (int o = 1; o < TPT; o <<= 1) {
+      sm += __shfl_xor(sm, o, kWave);
+      emin = min(emin, (uint32_t)__shfl_xor((int)emin, o, kWave));
     }
-    flag[tid] = before < R ? 1 : 0;
+    // squares are multiples of 2^(2 e - 50) (e the biased exponent, 1 for subnormals)
+    const bool ok = sm < __builtin_ldexp(1.0, 2 * (int)emin - 50 + 53);
+    if (part == 0) {
+      norm[j] = sm;
+      exact[j] = ok ? 1 : 0;
+    }
   }
   __syncthreads();
-  if (tid < BK && flag[tid]) {
-    int pos = 0;
-    for (int k = 0; k < tid; ++k) pos += flag[k];
-    c.k_keep_idx[g * R + pos] = (uint8_t)tid;
-    uint16_t* dst = c.k_keep_val + (g * R + pos) * D;
-    for (int d = 0; d < D; d += 8)
-      *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(&tile[tid * P + d]);
+  if (tid < BK && !exact[tid]) {
+    double sm = 0.0;
+    for (int d = 0; d < D; ++d) {
+      const double x = (double)h2f(tile[tid * P + d]);
+      sm = __builtin_fma(x, x, sm);  // the square is exact: one rounding per addition
+    }
+    norm[tid] = sm;
   }
-  __syncthreads();  // every kept row is read before the rows are marked
-  for (int idx = tid; idx < BK * D; idx += kThreads) {
-    const int j = idx / D;
-    if (flag[j]) tile[j * P + idx % D] = kMarkNaN;
+  __syncthreads();
+  bool kept;
+  {
+    const double m = norm[j];
+    int before = 0;
+    const int k0 = part * (BK / TPT);
+#pragma unroll 8
+    for (int k = k0; k < k0 + BK / TPT; k += 2) {
+      const double2 o = *reinterpret_cast<const double2*>(norm + k);
+      before += (o.x > m || (o.x == m && k < j)) ? 1 : 0;
+      before += (o.y > m || (o.y == m && k + 1 < j)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 1; o < TPT; o <<= 1) before += __shfl_xor(before, o, kWave);
+    kept = part == 0 && before < R;
+    const uint64_t bal = __ballot(kept);
+    if (lane == 0) {
+      masks[2 * wave] = (uint32_t)bal;
+      masks[2 * wave + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  __syncthreads();
+  if (kept) {
+    int pos = 0;
+    for (int w = 0; w < wave; ++w) pos += __builtin_popcount(masks[2 * w]) + __builtin_popcount(masks[2 * w + 1]);
+    const uint64_t mine = (uint64_t)masks[2 * wave] | ((uint64_t)masks[2 * wave + 1] << 32);
+    pos += __builtin_popcountll(mine & ((1ull << lane) - 1ull));
+    // (finite norms keep exactly R tokens; NaN norms compare false and could claim more)
+    if (pos < R) {
+      order[pos] = j;
+      c.k_keep_idx[g * R + pos] = (uint8_t)j;
+    }
+  }
+  __syncthreads();
+  // rows out, 16 bytes a thread, each chunk then marked by the thread that read it
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const uint4 mark = make_uint4(kMarkNaN * 0x10001u, kMarkNaN * 0x10001u, kMarkNaN * 0x10001u, kMarkNaN * 0x10001u);
+  for (int e = tid; e < R * CPR; e += kThreads) {
+    const int row = e / CPR, ch = e % CPR;
+    uint4* src = reinterpret_cast<uint4*>(&tile[order[row] * P + 8 * ch]);
+    *reinterpret_cast<uint4*>(c.k_keep_val + (g * R + row) * D + 8 * ch) = *src;
+    *src = mark;
   }
   __syncthreads();
 }

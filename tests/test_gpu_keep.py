@@ -129,3 +129,31 @@ def test_kept_keys_in_a_paged_cache():
         err = float(np.abs(out[b] - ref).max())
         say("  sequence", b, "length", L, "max abs err", err)
         assert err <= TOL
+
+
+def test_norm_rounding_decides_the_kept_key():
+    """Row A: 2048 in channel 0, then 63 channels of 2^-16; in channel order every
+    tiny square (a quarter ulp of 2^22) rounds away and the norm is exactly 2^22.  Row
+    B: 2048 and 2^-15, norm 2^22 + 2^-30 exactly.  With one key kept per block the
+    oracle keeps B; a sum in another order (the tiny squares first) would make A the
+    larger.  The kernel's parallel sum must fall back to channel order here."""
+    import oracle
+    cfg = synth.config("c0", batch=1, q_heads=2, kv_heads=2, k_block=64, tokens=3 * 64 + 5, capacity=256,
+                       keep_pct=1)
+    assert oracle.keep_count(cfg) == 1
+    k, v = inputs(cfg)
+    k = k.copy()
+    for n in range(3):
+        for h in range(2):
+            a = np.full(64, 0x0100, np.uint16)      # 2^-16 (subnormal)
+            a[0] = 0x6800                          # 2048
+            bb = np.zeros(64, np.uint16)
+            bb[0], bb[1] = 0x6800, 0x0200          # 2048, 2^-15
+            ja, jb = (5, 40) if n != 1 else (40, 5)
+            k[0, h, n * 64 + ja] = a
+            k[0, h, n * 64 + jb] = bb
+    cache = build_gpu_cache(cfg, k, v, [70, 127])
+    heads = oracle_heads(cfg, k, v)
+    for (b, h), hc in heads.items():
+        assert list(hc.k_keep_idx[:3].reshape(-1)) == [40, 5, 40]
+        compare_head(cache, hc, cfg, oracle.kout(cfg), b, h)
