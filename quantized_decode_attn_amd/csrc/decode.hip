@@ -143,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     const int64_t bh = rest / rs.nsets;
     const int h = (int)(bh % H);
     const int b = (int)(bh / H);
+    const SlotRow sr = slot_row(c, b, h);
     // the sequence's length (its own in a cache with per-sequence lengths), and the
     // position of its first query (q_pos < 0: the newest token)
     const int64_t len_b = seq_len_of(c, b);
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       const int ntok = tail ? ntail : Bk;
       const int iters = (ntok + Sh::TPI - 1) / Sh::TPI;
       // the quantized block's slot (slot_of), its codes and value words
-      const int64_t gs = tail ? 0 : slot_of(c, b, h, n);
+      const int64_t gs = tail ? 0 : slot_at<true>(sr, n);
       const uint8_t* kblk = static_cast<const uint8_t*>(c.k_codes) + gs * Bk * (D * KB / 8);
       const uint32_t* vblk = static_cast<const uint32_t*>(c.v_codes) + gs * (Bk / Sh::TPW) * D;
       // the block's keys kept in fp16: one bit per token offset (Bk <= 128), and a kept

@@ -173,11 +173,11 @@ __device__ __forceinline__ int tau(int q, int m) {
 template <int VB, int KO, int NG, bool PG>
 __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, float* __restrict__ wl, const GLds& L,
                                           const float* __restrict__ table, int lane, int G, int ng,
-                                          const kvq_cache& c, int64_t b, int64_t h, int64_t n, int nstep, bool more) {
+                                          const kvq_cache& c, const SlotRow& sr, int64_t n, int nstep, bool more) {
   constexpr bool OUTL = KO > 0;
   constexpr int TPW = 32 / VB;
   const int64_t nn = more ? n + nstep : n;
-  const int64_t gs = slot_t<PG>(c, b, h, n), gnn = more ? slot_t<PG>(c, b, h, nn) : gs;
+  const int64_t gs = slot_at<PG>(sr, n), gnn = more ? slot_at<PG>(sr, nn) : gs;
   const uint8_t* knext = gk_block(c, gnn);
   const uint8_t* vnext = gv_block<VB>(c, gnn);
   float* Meta = wl + L.meta;
@@ -566,8 +566,9 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
 
     GRegs<VB> R;
     CsrTok C;
+    const SlotRow sr = slot_row(c, b, h);
     if (n0 < nfull) {
-      const int64_t g0 = slot_t<PG>(c, b, h, n0);
+      const int64_t g0 = slot_at<PG>(sr, n0);
       gload_kmeta(R, c, g0, n0, lane);
       const uint8_t* kb0 = gk_block(c, g0);
       const uint8_t* vb0 = gv_block<VB>(c, g0);
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
       for (int s = 0; s < GRegs<VB>::NVI; ++s) gload_v(R, s, vb0, lane);
     }
     for (int64_t n = n0; n < nfull; n += S)
-      gqa_block<VB, KO, NG, PG>(R, C, st, wl, L, table, lane, G, NG, c, b, h, n, S, n + S < nfull);
+      gqa_block<VB, KO, NG, PG>(R, C, st, wl, L, table, lane, G, NG, c, sr, n, S, n + S < nfull);
 
     if (OUTL) {  // the item's last block of value corrections
       merge_vcorr_heads(reinterpret_cast<int*>(wl + L.vcorr), st, lane);

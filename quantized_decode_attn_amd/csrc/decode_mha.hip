@@ -43,7 +43,7 @@ namespace {
 using namespace dcm;
 
 constexpr int kMhaWaves = 8;  // two waves per SIMD
-constexpr float kW32Span = 4294901760.0f;  // 2^32 - 2^16: full scale of the fixed-point value weights
+constexpr float kW24Span = 16776960.0f;  // 2^24 - 2^8: full scale of the fixed-point value weights
 
 // Per-wave LDS area, in floats.
 struct MLds {
@@ -149,14 +149,14 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               const uint32_t* __restrict__ ptab, float wq_r, float wq_i,
                                               float inv_unit, int lane, int ts, int r, uint32_t sh, int G, int ng,
-                                              const kvq_cache& c, int64_t b, int64_t h, int64_t n, int nstep, bool more,
+                                              const kvq_cache& c, const SlotRow& sr, int64_t n, int nstep, bool more,
                                               uint32_t koff) {
   using Sh = MShape<D, BK, KB, VB>;
   constexpr bool OUTL = KO > 0;
   static_assert(!(LUT && OUTL), "codebook keys with outliers take the generic kernel");
   constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
   const int64_t nn = more ? n + nstep : n;
-  const int64_t g = slot_t<PG>(c, b, h, n), gnn = more ? slot_t<PG>(c, b, h, nn) : g;
+  const int64_t g = slot_at<PG>(sr, n), gnn = more ? slot_at<PG>(sr, nn) : g;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, gnn);
   const uint8_t* vnext = v_block<D, BK, KB, VB>(c, gnn);
   // this block's weights were written during the previous block (or at the item's start)
@@ -405,10 +405,12 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   }
 
   // ---- value weights w_t = p_t * scale_t per [group][token], quantized per block to
-  // 32-bit fixed point for the integer dot products: W = rint(w K) with
-  // K = (2^32 - 2^16) / (the block's largest weight), so W < 2^32 and each weight is
-  // exact up to half a unit (2^-33 of the block maximum) plus the fp32 rounding of w K
-  // (2^-24 of w itself): fp32-class accuracy for every weight, however small next to
+  // 24-bit fixed point for the integer dot products: W = rint(w K) with
+  // K = (2^24 - 2^8) / (the block's largest weight), so W < 2^24 and each weight is
+  // exact up to half a unit (2^-25 of the block maximum) plus the fp32 rounding of w K
+  // (2^-24 of w itself).  Summed over a block the first part is at most
+  // BK L 2^-25 max(scale) = 2^-25 BK max|v - z|, below the worst case of a plain fp32
+  // sum of the BK products (BK 2^-24 of the largest), however small a weight is next to
   // the block maximum.  The zero-point part p_t * zero_t is summed in fp32.  Element
   // lane + 64 k is token (64 k) % BK + lane of group (64 k) / BK, so its probability is
   // p[((64 k) % BK) / 64].
@@ -438,9 +440,9 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   wmax0 = wave_max_uniform(wmax0);
   if (ng > 1) wmax1 = wave_max_uniform(wmax1);
   // fixed-point scale and its inverse; they need only agree with each other (to fp32
-  // rounding).  wmax * K <= (2^32 - 2^16)(1 + 2^-23) stays below 2^32.
-  const float kq0 = wmax0 > 0.0f ? kW32Span * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
-  const float kq1 = wmax1 > 0.0f ? kW32Span * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
+  // rounding).  wmax * K <= (2^24 - 2^8)(1 + 2^-22) stays below 2^24.
+  const float kq0 = wmax0 > 0.0f ? kW24Span * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
+  const float kq1 = wmax1 > 0.0f ? kW24Span * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
   wave_lds_sync();  // every lane has read its scores before the weights overwrite them
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -498,15 +500,16 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
 
   // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
-  // sum_t w_t * code_t by 4-bit integer dot products over the eight weight nibbles, in
-  // two passes (bits 16..31, then 0..15) that share the accumulator registers.  A plane
+  // sum_t w_t * code_t by 4-bit integer dot products over the six weight nibbles, in
+  // two passes (bits 16..23, then 0..15) that share the accumulator registers.  A plane
   // sum is at most BK * 15 * 15 = 28,800, so four planes combine exactly in 32 bits.
   const int ch0 = (4 * lane) % D;
   const int grp0 = ch0 / G;
-  const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / kW32Span);
+  const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / kW24Span);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int poff = pass == 0 ? 4 : 0;  // plane offset within a token group's eight
+    const int npl = pass == 0 ? 2 : 4;   // planes 4 and 5 hold bits 16..23; 6 and 7 are zero
     uint32_t ia[4][4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -522,8 +525,10 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
         for (int k = 0; k < 4; ++k) {
           ia[k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[k][0], false);
           ia[k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[k][1], false);
-          ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
-          ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
+          if (npl == 4) {
+            ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
+            ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
+          }
         }
       } else {
         const uint4 pe = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + poff);
@@ -533,12 +538,14 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
           const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
           ia[k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[k][0], false);
           ia[k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[k][1], false);
-          ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
-          ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
           ia[k][0] = __builtin_amdgcn_udot8(po.x, od, ia[k][0], false);
           ia[k][1] = __builtin_amdgcn_udot8(po.y, od, ia[k][1], false);
-          ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
-          ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
+          if (npl == 4) {
+            ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
+            ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
+            ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
+            ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
+          }
         }
       }
     }
@@ -626,8 +633,9 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
 
   BlockRegs<D, BK, KB, VB> R;
   CsrTok C;
+  const SlotRow sr = slot_row(c, b, h);
   if (n0 < nfull) {
-    const int64_t g0 = slot_t<PG>(c, b, h, n0);
+    const int64_t g0 = slot_at<PG>(sr, n0);
     if constexpr (LUT) load_eb(R, c, n0, lane);
     else load_kmeta(R, c, g0, n0, lane, 0);
     write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
@@ -640,7 +648,7 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   }
   for (int64_t n = n0; n < nfull; n += S)
     process_block<D, BK, KB, VB, KO, LUT, PG, KEEP>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
-                                          c, b, h, n, S, n + S < nfull, koff);
+                                          c, sr, n, S, n + S < nfull, koff);
   if (OUTL) {
     wave_lds_sync();
     int* vci = reinterpret_cast<int*>(wl + L.vcorr);

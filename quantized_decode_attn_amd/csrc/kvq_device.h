@@ -127,6 +127,37 @@ __device__ __forceinline__ int64_t slot_of(const kvq_cache& c, int64_t b, int64_
   return p * c.cfg.kv_heads + h;
 }
 
+// The slots of one (b, kv head), with the division by the block size done once: the
+// slot of block 0 in the dense layout, or the sequence's row of the block table.
+struct SlotRow {
+  int64_t base;
+  const int32_t* row;
+  int64_t last;  // num_blocks - 1
+  int64_t H, h;
+};
+__device__ __forceinline__ SlotRow slot_row(const kvq_cache& c, int64_t b, int64_t h) {
+  const int64_t nb = c.cfg.capacity / c.cfg.k_block;
+  SlotRow s;
+  s.base = (b * c.cfg.kv_heads + h) * nb;
+  s.row = c.block_table ? c.block_table + b * nb : nullptr;
+  s.last = (int64_t)c.num_blocks - 1;
+  s.H = c.cfg.kv_heads;
+  s.h = h;
+  return s;
+}
+// Block n's slot (slot_of); PG false: the dense layout, known at compile time.
+template <bool PG>
+__device__ __forceinline__ int64_t slot_at(const SlotRow& s, int64_t n) {
+  if constexpr (PG) {
+    if (s.row) {
+      int64_t p = s.row[n];
+      p = p < 0 ? 0 : (p > s.last ? s.last : p);
+      return p * s.H + s.h;
+    }
+  }
+  return s.base + n;
+}
+
 // The same with the layout fixed at compile time: PG (per-sequence lengths, dense or
 // paged slots) or the dense layout with one length, whose kernels then carry no
 // paging code at all.
