@@ -58,8 +58,15 @@ typedef int32_t kvq_status;
  *             block of k_block tokens ([KVC3] "Per-Channel Key Quantization").
  *   k_mode 1: per-channel non-uniform codebook of 2^k_bits sorted fp16 entries,
  *             supplied by the caller ([KVC3] "Non-Uniform KV Cache Quantization").
- * Values: uniform asymmetric per token over groups of v_group channels, one fp16
- *   scale and zero-point per group ([KVC3] "Quanto 的量化原理").
+ * Values:
+ *   v_mode 0: uniform asymmetric per token over groups of v_group channels, one fp16
+ *             scale and zero-point per group ([KVC3] "Quanto 的量化原理").
+ *   v_mode 1: per-channel non-uniform codebook of 2^v_bits sorted fp16 entries per
+ *             (kv head, channel), supplied by the caller: the page applies the
+ *             non-uniform format to the Value cache first ([KVC3] "Non-Uniform KV Cache
+ *             Quantization"); a codebook of log-spaced levels is the log quantization of
+ *             [TQ] section 3.3.  The code is the nearest entry, decided at the fp32
+ *             midpoints, ties to the lower code (as for codebook keys).
  * clip_quantile q > 0: before the statistics, every dense value of a block is
  *   clipped to [-t, t], t = the q-quantile of |x| over that block's k_block x
  *   head_dim elements of the same tensor (exact order statistics, linear
@@ -81,7 +88,8 @@ typedef int32_t kvq_status;
  * {64, 128}; capacity a positive multiple of k_block below 2^31; q_heads a multiple of
  * kv_heads with q_heads/kv_heads <= 8; clip_quantile in [0, 1); outlier_pct in
  * [0, 100] with ceil(p*head_dim/100) <= 4; rope_theta > 1; keep_pct in [0, 100] with
- * R <= 16, and only with uniform keys (k_mode 0), no outliers and no clipping.
+ * R <= 16, and only with uniform keys (k_mode 0), no outliers and no clipping; v_mode in
+ * {0, 1}, 1 only without outliers and clipping.
  */
 typedef struct {
   int32_t batch, q_heads, kv_heads, head_dim, capacity;
@@ -91,6 +99,7 @@ typedef struct {
   int32_t outlier_pct;
   float rope_theta;
   int32_t keep_pct;
+  int32_t v_mode;
 } kvq_config;
 
 /* Byte size of each buffer of a cache; 0 = buffer not used by this configuration. */
@@ -100,6 +109,7 @@ typedef struct {
   size_t k_rowptr, k_col, k_val, v_rowptr, v_col, v_val;
   size_t rope;
   size_t k_keep_idx, k_keep_val;
+  size_t v_lut;
 } kvq_layout;
 
 /* A cache: caller-owned device buffers plus the host-side token count.
@@ -117,8 +127,9 @@ typedef struct {
  *  v_codes  u32  [BH][T/(32/v_bits)][D] words: word (t / tpw, d), tpw = 32/v_bits,
  *                 holds the codes of channel d for tpw consecutive tokens; token t
  *                 at bits [(t % tpw)*v_bits, ...).
- *  v_scale  fp16 [BH][T][D/v_group]
- *  v_zero   fp16 [BH][T][D/v_group]
+ *  v_scale  fp16 [BH][T][D/v_group]   uniform values only.
+ *  v_zero   fp16 [BH][T][D/v_group]   uniform values only.
+ *  v_lut    fp16 [kv_heads][D][2^v_bits] codebook values: input, sorted ascending.
  *  v_tail   fp16 [BH][Bk][D]
  *  k_rowptr i32  [BH][T+1]            CSR row pointers of key outliers; for every
  *                 quantized token rowptr[t+1] - rowptr[t] == ko and rowptr[0] == 0.
@@ -175,6 +186,7 @@ typedef struct {
   float *rope;
   uint8_t *k_keep_idx;
   uint16_t *k_keep_val;
+  const uint16_t *v_lut;
   /* paged layout (see above); all NULL / 0 for the dense layout */
   const int32_t *block_table;
   int32_t num_blocks;

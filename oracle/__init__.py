@@ -43,7 +43,7 @@ class Cfg(C.Structure):
                 ("head_dim", C.c_int32), ("capacity", C.c_int32), ("k_bits", C.c_int32),
                 ("k_mode", C.c_int32), ("k_block", C.c_int32), ("v_bits", C.c_int32),
                 ("v_group", C.c_int32), ("clip_quantile", C.c_float), ("outlier_pct", C.c_int32),
-                ("rope_theta", C.c_float), ("keep_pct", C.c_int32)]
+                ("rope_theta", C.c_float), ("keep_pct", C.c_int32), ("v_mode", C.c_int32)]
 
 
 class _Head(C.Structure):
@@ -52,7 +52,8 @@ class _Head(C.Structure):
                 ("v_scale", C.c_void_p), ("v_zero", C.c_void_p), ("v_tail", C.c_void_p),
                 ("k_rowptr", C.c_void_p), ("k_col", C.c_void_p), ("k_val", C.c_void_p),
                 ("v_rowptr", C.c_void_p), ("v_col", C.c_void_p), ("v_val", C.c_void_p),
-                ("k_keep_idx", C.c_void_p), ("k_keep_val", C.c_void_p), ("length", C.c_int64)]
+                ("k_keep_idx", C.c_void_p), ("k_keep_val", C.c_void_p), ("v_lut", C.c_void_p),
+                ("length", C.c_int64)]
 
 
 _lib = None
@@ -105,7 +106,7 @@ def load(path: str):
 
 LAYOUT_NAMES = ["k_codes", "k_scale", "k_zero", "k_lut", "k_tail", "v_codes", "v_scale",
                 "v_zero", "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val",
-                "k_keep_idx", "k_keep_val"]
+                "k_keep_idx", "k_keep_val", "v_lut"]
 
 _CFG_KEYS = [f[0] for f in Cfg._fields_]
 
@@ -116,6 +117,7 @@ def make_cfg(cfg: dict) -> Cfg:
     d = dict(cfg)
     d.setdefault("capacity", d.get("tokens"))
     d.setdefault("keep_pct", 0)
+    d.setdefault("v_mode", 0)
     return Cfg(**{k: d[k] for k in _CFG_KEYS})
 
 
@@ -132,7 +134,7 @@ def keep_count(cfg: dict) -> int:
 
 def layout(cfg: dict) -> dict:
     c = make_cfg(cfg)
-    out = np.zeros(17, np.int64)
+    out = np.zeros(18, np.int64)
     lib().orc_layout(C.byref(c), out.ctypes.data)
     return dict(zip(LAYOUT_NAMES, (int(v) for v in out)))
 
@@ -164,7 +166,7 @@ class HeadCache:
     """Host buffers of one (batch, kv-head) of the quantized cache, in the library's
     per-(b, h) layout."""
 
-    def __init__(self, cfg: dict, lut_head: np.ndarray | None = None):
+    def __init__(self, cfg: dict, lut_head: np.ndarray | None = None, vlut_head: np.ndarray | None = None):
         self.cfg = dict(cfg)
         self.cfg.setdefault("capacity", self.cfg["tokens"])
         c = self.cfg
@@ -183,8 +185,14 @@ class HeadCache:
         self.k_tail = np.zeros((Bk, D), np.uint16)
         self.v_codes = np.zeros(T * D * c["v_bits"] // 8, np.uint8)
         ng = D // c["v_group"]
-        self.v_scale = np.zeros((T, ng), np.uint16)
-        self.v_zero = np.zeros((T, ng), np.uint16)
+        vuni = c.get("v_mode", 0) == 0
+        self.v_scale = np.zeros((T, ng) if vuni else (0,), np.uint16)
+        self.v_zero = np.zeros((T, ng) if vuni else (0,), np.uint16)
+        if not vuni:
+            assert vlut_head is not None and vlut_head.shape == (D, 1 << c["v_bits"])
+            self.v_lut = np.ascontiguousarray(vlut_head, np.uint16)
+        else:
+            self.v_lut = np.zeros(0, np.uint16)
         self.v_tail = np.zeros((Bk, D), np.uint16)
         n = T + 1 if ko else 0
         self.k_rowptr = np.zeros(n, np.int32)
@@ -287,13 +295,15 @@ def chunk_many(cfg: dict, heads: list, qs: np.ndarray, nq: int, q_pos) -> np.nda
     return out
 
 
-def build_heads(cfg: dict, k_src: np.ndarray, v_src: np.ndarray, luts=None) -> list:
+def build_heads(cfg: dict, k_src: np.ndarray, v_src: np.ndarray, luts=None, vluts=None) -> list:
     """Quantize ``n`` heads at once (fp16 bits ``[n][T][D]`` each), OpenMP across heads;
-    ``luts`` gives each head's codebook (codebook keys only).  Returns the HeadCaches."""
+    ``luts`` / ``vluts`` give each head's key / value codebook (codebook modes only).
+    Returns the HeadCaches."""
     k = np.ascontiguousarray(k_src, np.uint16)
     v = np.ascontiguousarray(v_src, np.uint16)
     n, T = k.shape[0], k.shape[1]
-    heads = [HeadCache(cfg, None if luts is None else luts[i]) for i in range(n)]
+    heads = [HeadCache(cfg, None if luts is None else luts[i], None if vluts is None else vluts[i])
+             for i in range(n)]
     arr = (_Head * n)(*[h._struct() for h in heads])
     c = make_cfg(cfg)
     if lib().orc_build_heads(C.byref(c), n, C.cast(arr, C.c_void_p), k.ctypes.data, v.ctypes.data, T):
@@ -307,14 +317,15 @@ def max_threads() -> int:
     return int(lib().orc_max_threads())
 
 
-def build_cache(cfg: dict, k_src: np.ndarray, v_src: np.ndarray, lut: np.ndarray | None = None) -> list:
+def build_cache(cfg: dict, k_src: np.ndarray, v_src: np.ndarray, lut: np.ndarray | None = None,
+                vlut: np.ndarray | None = None) -> list:
     """Quantize whole ``[B][Hkv][T][D]`` sources; returns ``[B][Hkv]`` nested lists of HeadCache."""
     B, H = cfg["batch"], cfg["kv_heads"]
     out = []
     for b in range(B):
         row = []
         for h in range(H):
-            hc = HeadCache(cfg, None if lut is None else lut[h])
+            hc = HeadCache(cfg, None if lut is None else lut[h], None if vlut is None else vlut[h])
             hc.build(k_src[b, h], v_src[b, h])
             row.append(hc)
         out.append(row)

@@ -38,6 +38,7 @@ typedef struct {
   int32_t outlier_pct;
   float rope_theta;
   int32_t keep_pct;        /* key vectors kept in fp16 per block, percent (0 = none) */
+  int32_t v_mode;          /* 0: uniform per-token values; 1: per-channel codebook      */
 } orc_cfg;
 
 /* Buffers of ONE (batch, kv-head) of the cache, laid out exactly as the library's
@@ -60,6 +61,7 @@ typedef struct {
   uint16_t *v_val;
   uint8_t *k_keep_idx;     /* [capacity/k_block][R]    retained token offsets      */
   uint16_t *k_keep_val;    /* [capacity/k_block][R][D] their keys, fp16           */
+  const uint16_t *v_lut;   /* [D][2^v_bits]          fp16 (codebook values)    */
   int64_t length;          /* tokens held                                       */
 } orc_head;
 
@@ -153,8 +155,8 @@ int orc_keep_count(const orc_cfg *c) {
 
 /* Byte size of every buffer of the whole cache, in the order
  * k_codes k_scale k_zero k_lut k_tail v_codes v_scale v_zero v_tail
- * k_rowptr k_col k_val v_rowptr v_col v_val k_keep_idx k_keep_val (17 entries). */
-void orc_layout(const orc_cfg *c, int64_t out[17]) {
+ * k_rowptr k_col k_val v_rowptr v_col v_val k_keep_idx k_keep_val v_lut (18 entries). */
+void orc_layout(const orc_cfg *c, int64_t out[18]) {
   const int64_t BH = (int64_t)c->batch * c->kv_heads, D = c->head_dim, T = c->capacity;
   const int64_t nblk = T / c->k_block, ko = orc_kout(c);
   const int uni = c->k_mode == 0;
@@ -164,7 +166,7 @@ void orc_layout(const orc_cfg *c, int64_t out[17]) {
   out[3] = uni ? 0 : (int64_t)c->kv_heads * D * (1 << c->k_bits) * 2;
   out[4] = BH * c->k_block * D * 2;
   out[5] = BH * T * D * c->v_bits / 8;
-  out[6] = BH * T * (D / c->v_group) * 2;
+  out[6] = c->v_mode == 1 ? 0 : BH * T * (D / c->v_group) * 2;
   out[7] = out[6];
   out[8] = out[4];
   out[9] = ko ? BH * (T + 1) * 4 : 0;
@@ -175,6 +177,7 @@ void orc_layout(const orc_cfg *c, int64_t out[17]) {
   out[14] = out[11];
   out[15] = BH * nblk * orc_keep_count(c);
   out[16] = out[15] * D * 2;
+  out[17] = c->v_mode == 1 ? (int64_t)c->kv_heads * D * (1 << c->v_bits) * 2 : 0;
 }
 
 /* Importance of a key vector: its squared L2 norm, the squares of the fp16 values
@@ -346,6 +349,26 @@ static int64_t orc_v_bitpos(const orc_cfg *c, int64_t t, int d) {
   return ((t / tpw) * (int64_t)c->head_dim + d) * 32 + (t % tpw) * c->v_bits;
 }
 
+/* Per-channel non-uniform codebook ([KVC3] "Non-Uniform KV Cache Quantization"): the
+ * code of x is its nearest entry among the channel's sorted fp16 centroids, decided
+ * at the fp32 midpoints, ties to the lower code; marked (outlier or kept) positions
+ * get code 0.  lut: [D][L + 1]; d, mask, code: the block, [Bk][D]. */
+static void orc_codebook_codes(const uint16_t *lut, int D, int L, int Bk, const float *d,
+                               const uint8_t *mask, uint8_t *code) {
+  for (int ch = 0; ch < D; ++ch) {
+    const uint16_t *C = lut + (int64_t)ch * (L + 1);
+    float mid[255];
+    for (int k = 0; k < L; ++k) mid[k] = (orc_h2f(C[k]) + orc_h2f(C[k + 1])) * 0.5f;
+    for (int j = 0; j < Bk; ++j) {
+      const int64_t i = (int64_t)j * D + ch;
+      int cc = 0;
+      if (!mask[i])
+        for (int k = 0; k < L; ++k) cc += d[i] > mid[k];
+      code[i] = (uint8_t)cc;
+    }
+  }
+}
+
 int orc_quantize_block(const orc_cfg *c, int is_key, int64_t n, const uint16_t *src,
                        orc_head *hd) {
   const int D = c->head_dim, Bk = c->k_block, kout = orc_kout(c);
@@ -380,20 +403,12 @@ int orc_quantize_block(const orc_cfg *c, int is_key, int64_t n, const uint16_t *
   }
   /* 4-5. statistics, metadata, codes */
   if (is_key && c->k_mode == 1) {
-    /* Per-channel non-uniform codebook ([KVC3] "Non-Uniform KV Cache Quantization"):
-     * nearest of the sorted centroids, decided at fp32 midpoints, ties to the lower code. */
-    for (int ch = 0; ch < D; ++ch) {
-      const uint16_t *C = hd->k_lut + (int64_t)ch * (L + 1);
-      float mid[255];
-      for (int k = 0; k < L; ++k) mid[k] = (orc_h2f(C[k]) + orc_h2f(C[k + 1])) * 0.5f;
-      for (int j = 0; j < Bk; ++j) {
-        const int64_t i = (int64_t)j * D + ch;
-        int cc = 0;
-        if (!mask[i])
-          for (int k = 0; k < L; ++k) cc += d[i] > mid[k];
-        code[i] = (uint8_t)cc;
-      }
-    }
+    orc_codebook_codes(hd->k_lut, D, L, Bk, d, mask, code);
+  } else if (!is_key && c->v_mode == 1) {
+    /* The same for values: the page names the Value cache first among the tensors a
+     * uniform grid fits badly; [TQ] section 3.3 names log quantization as one such
+     * non-uniform grid (a codebook whose levels are spaced by powers of two). */
+    orc_codebook_codes(hd->v_lut, D, L, Bk, d, mask, code);
   } else if (is_key) {
     /* Per-channel keys over the token block ([KVC3] "Per-Channel Key Quantization",
      * quantized before RoPE per "Pre-RoPE Key Quantization"). */
@@ -521,8 +536,11 @@ static void orc_dequant_row(const orc_cfg *c, const orc_head *hd, int which, int
     const int G = c->v_group, ng = D / G;
     for (int ch = 0; ch < D; ++ch) {
       const uint32_t cc = orc_get_bits(hd->v_codes, orc_v_bitpos(c, t, ch), c->v_bits);
-      out[ch] = fmaf((float)cc, orc_h2f(hd->v_scale[t * ng + ch / G]),
-                     orc_h2f(hd->v_zero[t * ng + ch / G]));
+      if (c->v_mode == 1)
+        out[ch] = orc_h2f(hd->v_lut[(int64_t)ch * (1 << c->v_bits) + cc]);
+      else
+        out[ch] = fmaf((float)cc, orc_h2f(hd->v_scale[t * ng + ch / G]),
+                       orc_h2f(hd->v_zero[t * ng + ch / G]));
     }
   }
   if (kout > 0) {

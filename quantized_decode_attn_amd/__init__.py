@@ -32,12 +32,12 @@ class KvqConfig(C.Structure):
                 ("head_dim", C.c_int32), ("capacity", C.c_int32), ("k_bits", C.c_int32),
                 ("k_mode", C.c_int32), ("k_block", C.c_int32), ("v_bits", C.c_int32),
                 ("v_group", C.c_int32), ("clip_quantile", C.c_float), ("outlier_pct", C.c_int32),
-                ("rope_theta", C.c_float), ("keep_pct", C.c_int32)]
+                ("rope_theta", C.c_float), ("keep_pct", C.c_int32), ("v_mode", C.c_int32)]
 
 
 BUFFERS = ["k_codes", "k_scale", "k_zero", "k_lut", "k_tail", "v_codes", "v_scale", "v_zero",
            "v_tail", "k_rowptr", "k_col", "k_val", "v_rowptr", "v_col", "v_val", "rope",
-           "k_keep_idx", "k_keep_val"]
+           "k_keep_idx", "k_keep_val", "v_lut"]
 
 
 class KvqLayout(C.Structure):
@@ -218,35 +218,38 @@ def make_config(cfg: dict) -> KvqConfig:
     d = dict(cfg)
     d.setdefault("capacity", d.get("tokens"))
     d.setdefault("keep_pct", 0)
+    d.setdefault("v_mode", 0)
     return KvqConfig(**{k: d[k] for k in _CFG_FIELDS})
 
 
 class Cache:
     """Device buffers of one cache (torch uint8 tensors sized by kvq_cache_layout) and the
     C descriptor pointing at them.  ``lut`` (codebook keys) is a uint16 tensor
-    ``[kv_heads][D][2**k_bits]`` of fp16 bits, or None."""
+    ``[kv_heads][D][2**k_bits]`` of fp16 bits, or None; ``vlut`` (codebook values,
+    v_mode 1) the same ``[kv_heads][D][2**v_bits]``."""
 
-    def __init__(self, cfg: dict, device="cuda", lut=None, stream=None):
+    def __init__(self, cfg: dict, device="cuda", lut=None, stream=None, vlut=None):
         self.cfg = dict(cfg)
         self.cfg.setdefault("capacity", self.cfg["tokens"])
         self.c_cfg = make_config(self.cfg)
         self.desc = KvqCache()
         self.desc.cfg = self.c_cfg
-        self._alloc(kvq_cache_layout(self.c_cfg), device, lut)
+        self._alloc(kvq_cache_layout(self.c_cfg), device, lut, vlut)
         kvq_cache_init(self.desc, stream)
         self._ws = None
 
-    def _alloc(self, layout, device, lut) -> None:
+    def _alloc(self, layout, device, lut, vlut=None) -> None:
         import torch
         self.layout = layout
         self.bufs = {}
         for name in BUFFERS:
             size = getattr(self.layout, name)
-            if name == "k_lut":
+            if name in ("k_lut", "v_lut"):
+                book = lut if name == "k_lut" else vlut
                 if size:
-                    if lut is None:
-                        raise ValueError("a codebook is required for k_mode 1")
-                    t = lut.to(device=device).contiguous().view(torch.uint8).reshape(-1)
+                    if book is None:
+                        raise ValueError("a codebook is required for %s" % ("k_mode 1" if name == "k_lut" else "v_mode 1"))
+                    t = book.to(device=device).contiguous().view(torch.uint8).reshape(-1)
                     if t.numel() != size:
                         raise ValueError("codebook has %d bytes, expected %d" % (t.numel(), size))
                     self.bufs[name] = t
@@ -358,7 +361,7 @@ class PagedCache(Cache):
     must map to its own physical block."""
 
     def __init__(self, cfg: dict, num_blocks: int | None = None, block_table=None, device="cuda", lut=None,
-                 stream=None):
+                 stream=None, vlut=None):
         import torch
         self.cfg = dict(cfg)
         self.cfg.setdefault("capacity", self.cfg["tokens"])
@@ -378,7 +381,7 @@ class PagedCache(Cache):
         else:
             layout = kvq_cache_layout(self.c_cfg)
             self.block_table = None
-        self._alloc(layout, device, lut)
+        self._alloc(layout, device, lut, vlut)
         self.seq_lens_dev = torch.zeros(B, dtype=torch.int64, device=device)
         self._seq_lens_host = (C.c_int64 * B)()
         self.desc.seq_lens = self.seq_lens_dev.data_ptr()

@@ -23,6 +23,7 @@ kvq_status check_cfg(const kvq_config* c) {
   if (c->outlier_pct < 0 || c->outlier_pct > 100) return KVQ_EINVAL;
   if (!(c->rope_theta > 1.0f) || !isfinite(c->rope_theta)) return KVQ_EINVAL;
   if (c->keep_pct < 0 || c->keep_pct > 100) return KVQ_EINVAL;
+  if (c->v_mode != 0 && c->v_mode != 1) return KVQ_EINVAL;
   // what the kernels are built for
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_EUNSUPPORTED;
   if (c->k_bits < 2 || c->k_bits > 4) return KVQ_EUNSUPPORTED;
@@ -36,6 +37,8 @@ kvq_status check_cfg(const kvq_config* c) {
   if (kvq::keep_count(*c) > 16) return KVQ_EUNSUPPORTED;
   if (c->keep_pct > 0 && (c->k_mode != 0 || c->outlier_pct > 0 || c->clip_quantile > 0.0f))
     return KVQ_EUNSUPPORTED;
+  // codebook values: no outliers, no clipping (both belong to the uniform value range)
+  if (c->v_mode == 1 && (c->outlier_pct > 0 || c->clip_quantile > 0.0f)) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -44,9 +47,11 @@ kvq_status check_cache(const kvq_cache* cache) {
   kvq_status st = check_cfg(&cache->cfg);
   if (st != KVQ_OK) return st;
   const kvq_config& c = cache->cfg;
-  if (!cache->k_codes || !cache->k_tail || !cache->v_codes || !cache->v_scale || !cache->v_zero ||
-      !cache->v_tail || !cache->rope)
+  if (!cache->k_codes || !cache->k_tail || !cache->v_codes || !cache->v_tail || !cache->rope)
     return KVQ_EINVAL;
+  if (c.v_mode == 0 && (!cache->v_scale || !cache->v_zero)) return KVQ_EINVAL;
+  if (c.v_mode == 1 && !cache->v_lut) return KVQ_EINVAL;
+  if (c.v_mode == 1) return KVQ_EUNSUPPORTED;  // codebook values: layout only, no kernels yet
   if (c.k_mode == 0 && (!cache->k_scale || !cache->k_zero)) return KVQ_EINVAL;
   if (c.k_mode == 1 && !cache->k_lut) return KVQ_EINVAL;
   if (kvq::host_kout(c) > 0 && (!cache->k_rowptr || !cache->k_col || !cache->k_val ||
@@ -215,8 +220,12 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout* out) {
   }
   out->k_tail = BH * c.k_block * D * 2;
   out->v_codes = BH * T * D * c.v_bits / 8;
-  out->v_scale = BH * T * (D / c.v_group) * 2;
-  out->v_zero = out->v_scale;
+  if (c.v_mode == 0) {
+    out->v_scale = BH * T * (D / c.v_group) * 2;
+    out->v_zero = out->v_scale;
+  } else {
+    out->v_lut = (size_t)c.kv_heads * D * ((size_t)1 << c.v_bits) * 2;
+  }
   out->v_tail = out->k_tail;
   if (ko) {
     out->k_rowptr = BH * (T + 1) * 4;

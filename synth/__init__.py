@@ -33,6 +33,7 @@ import numpy as np
 
 CHUNK = 65536
 TENSOR_K, TENSOR_V, TENSOR_Q, TENSOR_STD, TENSOR_INJECT, TENSOR_CALIB, TENSOR_QCHUNK = 0, 1, 2, 3, 4, 5, 6
+TENSOR_VCALIB = 7
 
 # The five workloads.  ``tokens`` is the cache length the decode attends over;
 # ``existing`` (only the prefill-append workload) is the part already in the
@@ -224,3 +225,41 @@ def calib_lut(cfg: dict, seed: int = 1, ntok: int = 4096) -> np.ndarray:
             c16 = np.sort(_lloyd_1d(x[:, d], K).astype(np.float16))
             out[h, d] = c16.view(np.uint16)
     return out
+
+
+def _value_calib_sample(cfg: dict, h: int, seed: int, ntok: int) -> np.ndarray:
+    """A seeded calibration sample of one kv head's values, float64 ``[ntok][D]``, drawn
+    like the workload's values (N(0, 1) per element)."""
+    return _rng(seed, TENSOR_VCALIB, h).standard_normal((ntok, cfg["head_dim"]))
+
+
+def calib_vlut(cfg: dict, seed: int = 2, ntok: int = 4096) -> np.ndarray:
+    """Per-(kv-head, channel) non-uniform value codebook, fp16 bits
+    ``uint16 [Hkv][D][2**v_bits]``, sorted ascending: 1-D Lloyd k-means per channel on a
+    calibration sample, as the offline calibration of the key codebook."""
+    H, D, K = cfg["kv_heads"], cfg["head_dim"], 1 << cfg["v_bits"]
+    out = np.empty((H, D, K), np.uint16)
+    for h in range(H):
+        x = _value_calib_sample(cfg, h, seed, ntok)
+        for d in range(D):
+            out[h, d] = np.sort(_lloyd_1d(x[:, d], K).astype(np.float16)).view(np.uint16)
+    return out
+
+
+def log_vlut(cfg: dict, absmax: np.ndarray) -> np.ndarray:
+    """Log-spaced value codebook, fp16 bits ``uint16 [Hkv][D][2**v_bits]``, sorted
+    ascending: the levels +-s 2^-k for k < 2^(v_bits - 1), with s = absmax[h][d] rounded
+    to fp16 (so every level is an fp16 number unless it falls below the normal range)."""
+    H, D, K = cfg["kv_heads"], cfg["head_dim"], 1 << cfg["v_bits"]
+    half = K // 2
+    s = np.asarray(absmax, np.float64).reshape(H, D).astype(np.float16).astype(np.float64)
+    pos = s[:, :, None] * 2.0 ** -np.arange(half)[::-1]                 # ascending
+    lv = np.concatenate([-pos[:, :, ::-1], pos], axis=2)
+    return lv.astype(np.float16).view(np.uint16)
+
+
+def calib_log_vlut(cfg: dict, seed: int = 2, ntok: int = 4096, q: float = 0.999) -> np.ndarray:
+    """log_vlut with s the q-quantile of |x| per channel of the calibration sample."""
+    H = cfg["kv_heads"]
+    absmax = np.stack([np.quantile(np.abs(_value_calib_sample(cfg, h, seed, ntok)), q, axis=0) for h in range(H)])
+    return log_vlut(cfg, absmax)

@@ -2,7 +2,8 @@
  * caches whose buffers are allocated to their exact layout sizes, so that any read or
  * write past a buffer, any signed overflow or any misaligned access in the oracle is
  * reported.  Covers uniform and codebook keys, 2/3/4-bit codes, head sizes 64 and 128,
- * clipping, outliers, keys kept in fp16, ragged tails, dequantization and decode.  Exit
+ * clipping, outliers, keys kept in fp16, codebook values, ragged tails, dequantization
+ * and decode.  Exit
  * status 0 = clean. */
 #include "../../oracle/oracle.c"
 
@@ -18,7 +19,7 @@ static uint16_t f16_of(double x) { return orc_f2h_rn((float)x); }
 static void *xalloc(int64_t n) { return n > 0 ? malloc((size_t)n) : NULL; }
 
 static int run(orc_cfg c, int64_t T) {
-  int64_t lay[17];
+  int64_t lay[18];
   orc_layout(&c, lay);
   const int D = c.head_dim;
   orc_head h;
@@ -38,6 +39,13 @@ static int run(orc_cfg c, int64_t T) {
   h.k_rowptr = xalloc(lay[9] / bh); h.k_col = xalloc(lay[10] / bh); h.k_val = xalloc(lay[11] / bh);
   h.v_rowptr = xalloc(lay[12] / bh); h.v_col = xalloc(lay[13] / bh); h.v_val = xalloc(lay[14] / bh);
   h.k_keep_idx = xalloc(lay[15] / bh); h.k_keep_val = xalloc(lay[16] / bh);
+  uint16_t *vlut = xalloc(lay[17] / c.kv_heads);
+  if (vlut) {
+    const int nl = 1 << c.v_bits;
+    for (int d = 0; d < D; ++d)
+      for (int k = 0; k < nl; ++k) vlut[d * nl + k] = f16_of(-1.5 + 3.0 * (k + 0.5) / nl);
+  }
+  h.v_lut = vlut;
   uint16_t *k = malloc((size_t)(T * D) * 2), *v = malloc((size_t)(T * D) * 2);
   for (int64_t i = 0; i < T * D; ++i) {
     const double heavy = unif() < 0.02 ? 40.0 : 1.0;
@@ -61,7 +69,7 @@ static int run(orc_cfg c, int64_t T) {
   free(qc); free(oc);
   const int64_t nblk = T / c.k_block;
   if (nblk > 0) (void)orc_clip_threshold(k, (int64_t)c.k_block * D, 0.99f);
-  free(deq); free(k); free(v); free(lut);
+  free(deq); free(k); free(v); free(lut); free(vlut);
   free(h.k_codes); free(h.k_scale); free(h.k_zero); free(h.k_tail); free(h.v_codes); free(h.v_scale);
   free(h.v_zero); free(h.v_tail); free(h.k_rowptr); free(h.k_col); free(h.k_val); free(h.v_rowptr);
   free(h.v_col); free(h.v_val); free(h.k_keep_idx); free(h.k_keep_val);
@@ -70,7 +78,7 @@ static int run(orc_cfg c, int64_t T) {
 
 int main(void) {
   /* batch, q_heads, kv_heads, D, capacity, k_bits, k_mode, k_block, v_bits, v_group, clip, pct, theta,
-   * keep */
+   * keep, v_mode */
   const orc_cfg cfgs[] = {
       {1, 4, 4, 64, 320, 4, 0, 64, 4, 64, 0.0f, 0, 10000.0f},
       {1, 2, 2, 128, 768, 4, 0, 128, 4, 128, 0.99f, 1, 10000.0f},
@@ -81,8 +89,10 @@ int main(void) {
       {1, 4, 4, 64, 256, 2, 0, 64, 2, 16, 0.5f, 0, 10000.0f},
       {1, 2, 2, 128, 512, 4, 0, 128, 4, 128, 0.0f, 0, 10000.0f, 12},
       {1, 8, 2, 64, 320, 3, 0, 64, 2, 32, 0.0f, 0, 10000.0f, 25},
+      {1, 2, 2, 128, 512, 4, 0, 128, 4, 128, 0.0f, 0, 10000.0f, 0, 1},
+      {1, 8, 2, 64, 320, 3, 1, 64, 2, 32, 0.0f, 0, 10000.0f, 0, 1},
   };
-  const int64_t lens[] = {293, 697, 589, 643, 333, 300, 200, 450, 301};
+  const int64_t lens[] = {293, 697, 589, 643, 333, 300, 200, 450, 301, 400, 250};
   int err = 0;
   for (size_t i = 0; i < sizeof cfgs / sizeof cfgs[0]; ++i) {
     const int e = run(cfgs[i], lens[i]);

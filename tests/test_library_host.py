@@ -40,9 +40,16 @@ def test_status_strings(L):
     assert kvq.kvq_status_string(-99) == "unknown status"
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
+VARIANTS = {
+    "c1_keep5": dict(keep_pct=5),
+    "c3_vlut": dict(v_mode=1),
+    "c0_vlut2": dict(v_mode=1, v_bits=2, v_group=32),
+}
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4", "c1_keep5", "c3_vlut", "c0_vlut2"])
 def test_layout_matches_oracle_layout(L, orc, name):
-    cfg = synth.config(name)
+    cfg = synth.config(name[:2], **VARIANTS.get(name, {}))
     lay = kvq.kvq_cache_layout(kvq.make_config(cfg))
     ref = orc.layout(cfg)
     for k, v in ref.items():
@@ -68,11 +75,21 @@ def L_layout(c):
     ("k_block", 32, kvq.KVQ_EUNSUPPORTED), ("q_heads", 6, kvq.KVQ_EINVAL), ("clip_quantile", 1.0, kvq.KVQ_EINVAL),
     ("clip_quantile", -0.1, kvq.KVQ_EINVAL), ("outlier_pct", 101, kvq.KVQ_EINVAL), ("outlier_pct", 4, kvq.KVQ_EUNSUPPORTED),
     ("rope_theta", 0.5, kvq.KVQ_EINVAL), ("k_mode", 2, kvq.KVQ_EINVAL), ("capacity", 0, kvq.KVQ_EINVAL),
+    ("v_mode", 2, kvq.KVQ_EINVAL), ("v_mode", -1, kvq.KVQ_EINVAL),
 ])
 def test_layout_rejects(L, field, value, want):
     cfg = synth.config("c1", q_heads=32, kv_heads=8)
     cfg[field] = value
     assert _status(cfg) == want
+
+
+def test_value_codebook_excludes_outliers_and_clipping(L):
+    """Codebook values replace the uniform value range that outliers and clipping act
+    on: either with v_mode 1 is refused; keys kept in fp16 combine with it."""
+    assert _status(synth.config("c1", v_mode=1)) == kvq.KVQ_OK
+    assert _status(synth.config("c2", v_mode=1)) == kvq.KVQ_EUNSUPPORTED          # 1% outliers
+    assert _status(synth.config("c4", v_mode=1)) == kvq.KVQ_EUNSUPPORTED          # clip + outliers
+    assert _status(synth.config("c1", v_mode=1, keep_pct=5)) == kvq.KVQ_OK
 
 
 def _fake_cache(cfg, length=0):

@@ -25,7 +25,7 @@ MUTANTS = {
     "clip_no_interpolation": ("const double f = pos - (double)k;", "const double f = 0.0;"),
     "clip_one_sided": ("d[i] = clip ? fminf(fmaxf(x, -thr), thr) : x;", "d[i] = clip ? fminf(x, thr) : x;"),
     "round_half_up": ("float r = nearbyintf(q);", "float r = floorf(q + 0.5f);"),
-    "dequant_drops_zero": ("out[ch] = fmaf((float)cc, orc_h2f(hd->v_scale[t * ng + ch / G]),\n                     orc_h2f(hd->v_zero[t * ng + ch / G]));",
+    "dequant_drops_zero": ("out[ch] = fmaf((float)cc, orc_h2f(hd->v_scale[t * ng + ch / G]),\n                       orc_h2f(hd->v_zero[t * ng + ch / G]));",
                            "out[ch] = (float)cc * orc_h2f(hd->v_scale[t * ng + ch / G]);"),
     "key_natural_order": ("return (e >> 1) + (e & 1) * (D / 2);", "return e;"),
     "value_word_transposed": ("return ((t / tpw) * (int64_t)c->head_dim + d) * 32 + (t % tpw) * c->v_bits;",
@@ -45,6 +45,12 @@ MUTANTS = {
     "kept_rows_in_stats": ("    memset(mask + (int64_t)j * D, 1, (size_t)D);\n", ""),
     "kept_key_read_quantized": ("out[ch] = orc_h2f(hd->k_keep_val[(n * R + r) * D + ch]);", "out[ch] = out[ch];"),
     "keep_count_floor": ("(c->keep_pct * c->k_block + 99) / 100", "(c->keep_pct * c->k_block) / 100"),
+    # (mistakes that stay inside the buffers: the mutated oracle runs in this process)
+    "vlut_row_stride_halved": ("orc_h2f(hd->v_lut[(int64_t)ch * (1 << c->v_bits) + cc])",
+                               "orc_h2f(hd->v_lut[(int64_t)ch * (1 << (c->v_bits - 1)) + cc])"),
+    "vlut_channel_ignored": ("orc_h2f(hd->v_lut[(int64_t)ch * (1 << c->v_bits) + cc])", "orc_h2f(hd->v_lut[cc])"),
+    "vlut_not_in_layout": ("out[17] = c->v_mode == 1 ? (int64_t)c->kv_heads * D * (1 << c->v_bits) * 2 : 0;",
+                           "out[17] = 0;"),
 }
 
 

@@ -730,3 +730,95 @@ def test_keep_layout_sizes(orc):
     lay = orc.layout(c)
     assert lay["k_keep_idx"] == 2 * 3 * 4 * 3 and lay["k_keep_val"] == 2 * 3 * 4 * 3 * 16 * 2
     assert orc.layout(tiny())["k_keep_idx"] == 0
+
+
+# --------------------------------------------------------------------------- codebook values
+def _vlut_cfg(D=16, vb=2, Bk=16, T=48, **kw):
+    return tiny(head_dim=D, k_block=Bk, tokens=T, k_bits=4, v_bits=vb, v_group=D, v_mode=1, **kw)
+
+
+def test_value_codebook_codes_are_nearest_centroid(orc):
+    """Values quantized by a per-channel sorted codebook: every dequantized value is
+    the nearest entry of its channel (brute force over the entries), whatever the key
+    width (keys 4-bit, values 2-bit here)."""
+    rng = np.random.default_rng(71)
+    c = _vlut_cfg()
+    vlut = np.sort(rng.standard_normal((16, 4)) * 1.2, axis=1).astype(np.float16).view(np.uint16)
+    k = _rand_block(rng, 48, 16)
+    v = _rand_block(rng, 48, 16)
+    hc = orc.HeadCache(c, None, vlut).build(k, v)
+    x = hval(v)
+    xh = _deq(hc, 1)
+    C = hval(vlut)                                              # [D][4]
+    best = np.argmin(np.abs(x[:, :, None] - C[None]), axis=2)
+    got = np.argmax(xh[:, :, None] == C[None], axis=2)
+    mids = (C[:, :-1] + C[:, 1:]) / 2
+    near = np.min(np.abs(x[:, :, None] - mids[None]), axis=2) < 1e-6 * (1 + np.abs(x))
+    assert np.array_equal(best[~near], got[~near])
+    assert np.all(np.isin(xh, C))
+    # keys are still uniform and their codes unaffected by the value codebook
+    ref = orc.HeadCache(tiny(head_dim=16, k_block=16, tokens=48, v_group=16)).build(k, v)
+    assert np.array_equal(_deq(hc, 0), _deq(ref, 0))
+
+
+def test_value_codebook_ties_go_to_the_lower_entry(orc):
+    rng = np.random.default_rng(72)
+    c = _vlut_cfg(vb=4)
+    z, s = -1.0, 0.125
+    vlut = np.tile(f16(z + s * np.arange(16)), (16, 1))
+    v = _rand_block(rng, 48, 16, scale=0.5)
+    v[5] = f16(z + s * (np.arange(16) % 15 + 0.5))              # exact midpoints
+    hc = orc.HeadCache(c, None, vlut).build(v, v)
+    u = (hval(v) - z) / s
+    want = np.clip(np.floor(u + 0.5 - 1e-12), 0, 15)
+    got = (_deq(hc, 1) - z) / s
+    assert np.array_equal(got, want)
+
+
+def test_log_spaced_codebook_keeps_its_levels_and_is_finer_near_zero(orc):
+    """Log quantization as a codebook: levels +-s 2^-k.  Values on a level come back
+    exactly; the step between neighbouring levels halves towards zero."""
+    import synth
+    rng = np.random.default_rng(73)
+    c = _vlut_cfg(vb=4)
+    lut = synth.log_vlut(dict(c, kv_heads=1), np.full((1, 16), 3.0))[0]      # [D][16]
+    C = hval(lut)
+    assert np.all(np.diff(C, axis=1) > 0)
+    pos = C[0][C[0] > 0]
+    assert np.allclose(pos / pos.max(), 2.0 ** -np.arange(len(pos))[::-1])
+    steps = np.diff(pos)
+    assert np.allclose(steps[1:] / steps[:-1], 2.0)
+    idx = rng.integers(0, 16, (48, 16))
+    v = np.take_along_axis(np.broadcast_to(lut, (48, 16, 16)), idx[:, :, None], axis=2)[:, :, 0]
+    hc = orc.HeadCache(c, None, lut).build(_rand_block(rng, 48, 16), v)
+    assert np.array_equal(_deq(hc, 1), hval(v))
+
+
+def test_codebook_values_are_exact_in_textbook_attention(orc):
+    """Keys on their block grid and values on their channel's codebook: the cache
+    dequantizes exactly, so the decode equals plain fp64 softmax attention with rotary
+    matrices on the raw inputs."""
+    rng = np.random.default_rng(74)
+    D, Bk, T = 16, 16, 48
+    k = f16(_on_grid(rng, T, D, Bk, 15, True))
+    vlut = np.sort(rng.standard_normal((D, 4)) * 2.0, axis=1).astype(np.float16).view(np.uint16)
+    idx = rng.integers(0, 4, (T, D))
+    v = np.take_along_axis(np.broadcast_to(vlut, (T, D, 4)), idx[:, :, None], axis=2)[:, :, 0]
+    c = _vlut_cfg(D=D, Bk=Bk, T=T)
+    hc = orc.HeadCache(c, None, vlut).build(k, v)
+    assert np.array_equal(_deq(hc, 1), hval(v))
+    q = f16(rng.standard_normal(D))
+    for qp in (T - 1, 5):
+        qr = _rot_matrix(qp, D, 10000.0) @ hval(q)
+        kr = np.stack([_rot_matrix(t, D, 10000.0) @ hval(k[t]) for t in range(T)])
+        ref = _softmax_attn(qr, kr, hval(v), D)
+        assert np.max(np.abs(hc.decode(q, q_pos=qp) - ref)) < 1e-12
+
+
+def test_value_codebook_layout_sizes(orc):
+    c = _vlut_cfg(D=16, vb=2, T=64, batch=2, kv_heads=3, q_heads=3)
+    lay = orc.layout(c)
+    assert lay["v_scale"] == 0 and lay["v_zero"] == 0
+    assert lay["v_lut"] == 3 * 16 * 4 * 2
+    assert lay["v_codes"] == 2 * 3 * 64 * 16 * 2 // 8
+    assert orc.layout(tiny())["v_lut"] == 0

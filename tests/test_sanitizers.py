@@ -36,7 +36,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", OMP_NUM_THREADS="2")
     rc, log = _run([exe], env=env)
     assert rc == 0 and "runtime error" not in log and "AddressSanitizer" not in log, log
-    assert log.count(": ok") == 9, log
+    assert log.count(": ok") == 11, log
 
 
 def test_abi_host_paths_under_asan_ubsan(tmp_path):
