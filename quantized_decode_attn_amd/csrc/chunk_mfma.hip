@@ -752,7 +752,7 @@ hipError_t launch_chunk_mfma(const kvq_cache& c, const uint16_t* q, RowSpec rs, 
   const kvq_config& g = c.cfg;
   const int ng = g.head_dim / g.v_group, ko = host_kout(g);
   // (at head_dim 128 a whole-percent outlier share gives 0 or at least 2 per vector)
-  if (ko > 2 || g.k_mode != 0 || g.k_bits != 4 || g.head_dim != kD || g.k_block != kBK || g.keep_pct > 0 ||
+  if (ko > 2 || g.k_mode != 0 || g.k_bits != 4 || g.head_dim != kD || g.k_block != kBK || g.keep_pct > 0 || g.v_mode != 0 ||
       (g.v_bits != 4 && g.v_bits != 2) || ng < 1 || ng > 2)
     return hipErrorNotSupported;
 #define KVQ_CHUNK_NG(vb, ko)                                                                  \

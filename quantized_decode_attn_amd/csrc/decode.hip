@@ -57,11 +57,12 @@ struct Shape {
 };
 
 struct WaveLds {  // offsets (in floats) of one wave's scratch area
-  int wts, wq, p, ps, vs, vz, state, vc, lut, total;
+  int wts, wq, p, ps, vs, vz, state, vc, lut, vlut, total;
 };
 
+// nvlut: entries of the value codebook (D * 2^v_bits with codebook values, else 0)
 __host__ __device__ inline WaveLds wave_lds(int D, int Bk, int rows, int ng, int tpi, int kb, int kmode,
-                                             bool ko) {
+                                             bool ko, int nvlut) {
   WaveLds w;
   int o = 0;
   w.wts = o; o += (D / 2) * 12;
@@ -73,6 +74,7 @@ __host__ __device__ inline WaveLds wave_lds(int D, int Bk, int rows, int ng, int
   w.state = o; o += rows * (D + 2 + ng);
   w.vc = o; o += ko ? tpi * D : 0;
   w.lut = o; o += kmode == 1 ? D * (1 << kb) : 0;
+  w.vlut = o; o += nvlut;
   w.total = o;
   return w;
 }
@@ -121,7 +123,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     table[j * Sh::TPITCH + 2 * i] = c.rope[2 * idx];
     table[j * Sh::TPITCH + 2 * i + 1] = c.rope[2 * idx + 1];
   }
-  const WaveLds L = wave_lds(D, Bk, rs.rpi, ng, Sh::TPI, KB, KMODE, ko > 0);
+  const bool vcb = c.cfg.v_mode == 1;  // codebook values
+  constexpr int NLV = 1 << VB;
+  const WaveLds L = wave_lds(D, Bk, rs.rpi, ng, Sh::TPI, KB, KMODE, ko > 0, vcb ? D * NLV : 0);
   float* wl = lds + Bk * Sh::TPITCH + wave * L.total;
   float* wts = wl + L.wts;
   float* wq = wl + L.wq;
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
   float* state = wl + L.state;
   float* VC = wl + L.vc;
   float* lutl = wl + L.lut;
+  float* vlutl = wl + L.vlut;
   const float* rope_blk = c.rope + (int64_t)Bk * D;  // [T/Bk][HALF][2]
   __syncthreads();
 
@@ -182,6 +187,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       for (int k = lane; k < D * (1 << KB); k += kWave)
         lutl[k] = h2f(c.k_lut[(int64_t)h * D * (1 << KB) + k]);
     }
+    if (vcb)
+      for (int k = lane; k < D * NLV; k += kWave) vlutl[k] = h2f(c.v_lut[(int64_t)h * D * NLV + k]);
     wave_lds_sync();
 
     const int64_t nblocks = (n1 - n0) + (do_tail ? 1 : 0);
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       };
 
       // value metadata of the block (quantized blocks only)
-      if (!tail) {
+      if (!tail && !vcb) {
         for (int k = lane; k < Bk * ng; k += kWave) {
           const int64_t m = gs * Bk * ng + k;
           VS[k] = h2f(c.v_scale[m]);
@@ -359,7 +366,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
         float acc[Sh::CPL];
 #pragma unroll
         for (int k = 0; k < Sh::CPL; ++k) acc[k] = st[2 + lane + k * kWave] * alpha;
-        if (!tail) {
+        if (!tail && vcb) {
+          // codebook values: each code reads its channel's entry
+          for (int gw = 0; gw < Bk / Sh::TPW; ++gw) {
+#pragma unroll
+            for (int k = 0; k < Sh::CPL; ++k) {
+              const int ch = lane + k * kWave;
+              const uint32_t word = vblk[gw * D + ch];
+              const float* cb = vlutl + ch * NLV;
+#pragma unroll
+              for (int u = 0; u < Sh::TPW; ++u)
+                acc[k] = __builtin_fmaf(Pl[gw * Sh::TPW + u], cb[(word >> (u * VB)) & (NLV - 1u)], acc[k]);
+            }
+          }
+          if (lane == 0)
+            for (int gg = 0; gg < ng; ++gg) st[2 + D + gg] *= alpha;
+        } else if (!tail) {
           for (int k = lane; k < Bk * ng; k += kWave) PS[k] = Pl[k / ng] * VS[k];
           float zp[8];
           for (int gg = 0; gg < ng; ++gg) zp[gg] = 0.0f;
@@ -868,7 +890,8 @@ hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float
   size_t bytes = 0;
   for (;; --rpi) {
     if (rpi < 1) return hipErrorInvalidValue;
-    const WaveLds L = wave_lds(D, c.cfg.k_block, rpi, ng, Sh::TPI, KB, KMODE, host_kout(c.cfg) > 0);
+    const WaveLds L = wave_lds(D, c.cfg.k_block, rpi, ng, Sh::TPI, KB, KMODE, host_kout(c.cfg) > 0,
+                               c.cfg.v_mode == 1 ? D << VB : 0);
     bytes = ((size_t)c.cfg.k_block * Sh::TPITCH + (size_t)kWaves * L.total) * sizeof(float);
     if (bytes <= 160 * 1024) break;
   }
@@ -965,7 +988,8 @@ bool decode_step_prefers_one_launch(const kvq_cache& c) {
   const kvq_config& g = c.cfg;
   const int D = g.head_dim, R = g.q_heads / g.kv_heads;
   const int ppl = g.k_bits == 3 ? 16 : 8, lpt = D / 2 / ppl, tpi = kWave / lpt;
-  const WaveLds L = wave_lds(D, g.k_block, R, D / g.v_group, tpi, g.k_bits, g.k_mode, host_kout(g) > 0);
+  const WaveLds L = wave_lds(D, g.k_block, R, D / g.v_group, tpi, g.k_bits, g.k_mode, host_kout(g) > 0,
+                             g.v_mode == 1 ? D << g.v_bits : 0);
   const size_t bytes = ((size_t)g.k_block * (D + 4) + (size_t)kWaves * L.total) * sizeof(float);
   if (R > 8 || bytes > 160 * 1024) return false;
   // where a tuned split kernel covers the configuration, it and the finish kernel take

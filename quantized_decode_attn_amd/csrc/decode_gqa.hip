@@ -645,7 +645,7 @@ hipError_t launch_decode_gqa(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int gq = g.q_heads / g.kv_heads;
   const int ng = g.head_dim / g.v_group;
   if (gq < 2 || gq % 2 || g.k_mode != 0 || g.k_bits != 4 || ko > 2 || ng < 1 || ng > 2 || g.head_dim != kD ||
-      g.k_block != kBK || (g.v_bits != 4 && g.v_bits != 2) || g.keep_pct > 0)
+      g.k_block != kBK || (g.v_bits != 4 && g.v_bits != 2) || g.keep_pct > 0 || g.v_mode != 0)
     return hipErrorNotSupported;
   const bool four = gq % 4 == 0;
   // per-sequence lengths (dense or paged slots): a kernel of their own

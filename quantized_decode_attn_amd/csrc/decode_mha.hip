@@ -805,6 +805,7 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ko = host_kout(g);
   const int ng = g.head_dim / g.v_group;
   if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
+  if (g.v_mode != 0) return hipErrorNotSupported;  // codebook values: the generic kernel
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
   if (g.keep_pct > 0) {
     // keys kept in fp16 (uniform keys without outliers): 4-bit keys at head_dim 128 and

@@ -47,8 +47,12 @@ __global__ void dequantize_kernel(kvq_cache c, int which, int64_t t0, int64_t t1
       const int vb = c.cfg.v_bits, tpw = 32 / vb, G = c.cfg.v_group;
       const uint32_t* words = static_cast<const uint32_t*>(c.v_codes) + bh * (T / tpw) * D;
       const uint32_t code = (words[(t / tpw) * D + ch] >> ((t % tpw) * vb)) & ((1u << vb) - 1u);
-      const int64_t m = (bh * T + t) * (D / G) + ch / G;
-      x = __builtin_fmaf((float)code, h2f(c.v_scale[m]), h2f(c.v_zero[m]));
+      if (c.cfg.v_mode == 1) {
+        x = h2f(c.v_lut[((int64_t)h * D + ch) * (1 << vb) + code]);
+      } else {
+        const int64_t m = (bh * T + t) * (D / G) + ch / G;
+        x = __builtin_fmaf((float)code, h2f(c.v_scale[m]), h2f(c.v_zero[m]));
+      }
     }
     if (t < nfull && ko > 0) {
       const uint8_t* col = which ? c.v_col : c.k_col;

@@ -51,7 +51,6 @@ kvq_status check_cache(const kvq_cache* cache) {
     return KVQ_EINVAL;
   if (c.v_mode == 0 && (!cache->v_scale || !cache->v_zero)) return KVQ_EINVAL;
   if (c.v_mode == 1 && !cache->v_lut) return KVQ_EINVAL;
-  if (c.v_mode == 1) return KVQ_EUNSUPPORTED;  // codebook values: layout only, no kernels yet
   if (c.k_mode == 0 && (!cache->k_scale || !cache->k_zero)) return KVQ_EINVAL;
   if (c.k_mode == 1 && !cache->k_lut) return KVQ_EINVAL;
   if (kvq::host_kout(c) > 0 && (!cache->k_rowptr || !cache->k_col || !cache->k_val ||

@@ -4,6 +4,64 @@
 namespace kvq {
 namespace {
 
+// Codebook values (v_mode 1): the code of x is its nearest entry among the channel's
+// sorted fp16 centroids, decided at the fp32 midpoints (C[k] + C[k+1]) / 2 with ties to
+// the lower code ([KVC3] "Non-Uniform KV Cache Quantization", which names the Value
+// cache first; a log-spaced codebook is the log quantization of [TQ] section 3.3).
+// Elementwise: no statistics, outliers or clipping.  A thread packs whole words (one
+// channel, 32 / VB consecutive tokens, as the uniform kernel stores them), reading each
+// token from the tail or from the new rows.
+template <int D, int BK, int VB>
+__global__ __launch_bounds__(qb::kThreads) void quantize_values_lut_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
+                                                                           int64_t old_len_arg, int64_t n_new,
+                                                                           int64_t n_first, const int64_t* __restrict__ n_seq) {
+  constexpr int NL = 1 << VB, L = NL - 1;
+  constexpr int TPW = 32 / VB;
+  constexpr int NWORD = (BK / TPW) * D;  // words of the block
+  __shared__ float mid[D * L];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t old_len = c.seq_lens ? seq_len_of(c, b) : old_len_arg;
+  const int64_t n_b = n_seq ? min(max(n_seq[b], (int64_t)0), n_new) : n_new;
+  const int64_t n = (c.seq_lens ? old_len / BK : n_first) + blockIdx.x;
+  if (n >= (old_len + n_b) / BK || n >= c.cfg.capacity / BK) return;
+  const int64_t g = slot_of(c, b, h, n);
+  const int64_t bh = (int64_t)b * c.cfg.kv_heads + h;
+  const uint16_t* lut = c.v_lut + (int64_t)h * D * NL;
+  for (int k = threadIdx.x; k < D * L; k += qb::kThreads) {
+    const int ch = k / L, e = k % L;
+    mid[k] = (h2f(lut[ch * NL + e]) + h2f(lut[ch * NL + e + 1])) * 0.5f;
+  }
+  __syncthreads();
+  const int64_t t0 = n * BK, tail0 = (old_len / BK) * BK;
+  uint32_t* words = static_cast<uint32_t*>(c.v_codes) + g * NWORD;
+  for (int w = threadIdx.x; w < NWORD; w += qb::kThreads) {
+    const int tg = w / D, ch = w % D;
+    const float* m = mid + ch * L;
+    uint32_t word = 0u;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int64_t t = t0 + tg * TPW + u;
+      const uint16_t* row = t < old_len ? c.v_tail + (bh * BK + (t - tail0)) * D
+                                        : v_new + (bh * n_new + (t - old_len)) * D;
+      const float x = h2f(row[ch]);
+      uint32_t code = 0u;
+#pragma unroll
+      for (int k = 0; k < L; ++k) code += x > m[k] ? 1u : 0u;
+      word |= code << (u * VB);
+    }
+    words[w] = word;
+  }
+}
+
+template <int D, int BK, int VB>
+hipError_t launch_v_lut(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
+                        int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s) {
+  dim3 grid((unsigned)nblocks, (unsigned)c.cfg.kv_heads, (unsigned)c.cfg.batch);
+  hipLaunchKernelGGL((quantize_values_lut_kernel<D, BK, VB>), grid, dim3(qb::kThreads), 0, s, c, v_new, old_len,
+                     n_new, n_first, n_seq);
+  return hipGetLastError();
+}
+
 template <int D, int BK, int VB, int KO, bool CLIP>
 hipError_t launch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
                     int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s) {
@@ -16,6 +74,7 @@ hipError_t launch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, 
 template <int D, int BK, int VB>
 hipError_t dispatch_v(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
                       int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s) {
+  if (c.cfg.v_mode == 1) return launch_v_lut<D, BK, VB>(c, v_new, old_len, n_new, n_first, nblocks, n_seq, s);
   // outliers per vector: none, exactly two (the 1% of 128 channels), or any other count
   // (1..4, read at run time)
   const int ko = kvq::host_kout(c.cfg);

@@ -29,6 +29,7 @@ def per_head_bytes(cfg: dict, ko: int) -> dict:
     D, T, Bk = cfg["head_dim"], cfg["capacity"], cfg["k_block"]
     ng = D // cfg["v_group"]
     uni = cfg["k_mode"] == 0
+    vuni = cfg.get("v_mode", 0) == 0
     R = keep_count(cfg)
     return {
         "k_keep_idx": (T // Bk) * R,
@@ -38,8 +39,8 @@ def per_head_bytes(cfg: dict, ko: int) -> dict:
         "k_zero": (T // Bk) * D * 2 if uni else 0,
         "k_tail": Bk * D * 2,
         "v_codes": T * D * cfg["v_bits"] // 8,
-        "v_scale": T * ng * 2,
-        "v_zero": T * ng * 2,
+        "v_scale": T * ng * 2 if vuni else 0,
+        "v_zero": T * ng * 2 if vuni else 0,
         "v_tail": Bk * D * 2,
         "k_rowptr": (T + 1) * 4 if ko else 0,
         "k_col": T * ko,
@@ -58,6 +59,7 @@ def defined_bytes(cfg: dict, ko: int, length: int) -> dict:
     nt = length - nq
     ng = D // cfg["v_group"]
     uni = cfg["k_mode"] == 0
+    vuni = cfg.get("v_mode", 0) == 0
     R = keep_count(cfg)
     return {
         "k_keep_idx": (nq // Bk) * R,
@@ -67,8 +69,8 @@ def defined_bytes(cfg: dict, ko: int, length: int) -> dict:
         "k_zero": (nq // Bk) * D * 2 if uni else 0,
         "k_tail": nt * D * 2,
         "v_codes": nq * D * cfg["v_bits"] // 8,
-        "v_scale": nq * ng * 2,
-        "v_zero": nq * ng * 2,
+        "v_scale": nq * ng * 2 if vuni else 0,
+        "v_zero": nq * ng * 2 if vuni else 0,
         "v_tail": nt * D * 2,
         "k_rowptr": (nq + 1) * 4 if ko and nq else 0,
         "k_col": nq * ko,
@@ -108,13 +110,14 @@ def upload(x: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.float16)
 
 
-def build_gpu_cache(cfg: dict, k: np.ndarray, v: np.ndarray, chunks=None, lut=None):
+def build_gpu_cache(cfg: dict, k: np.ndarray, v: np.ndarray, chunks=None, lut=None, vlut=None):
     """A library cache filled with ``k``/``v`` (fp16 bits [B][Hkv][T][D]) through
     kvq_quantize_append, in one call or in the given chunk sizes."""
     import quantized_decode_attn_amd as kvq
     torch, dev = torch_dev()
     lut_t = None if lut is None else torch.from_numpy(lut.view(np.int16)).to(dev)
-    cache = kvq.Cache(cfg, device=dev, lut=lut_t)
+    vlut_t = None if vlut is None else torch.from_numpy(vlut.view(np.int16)).to(dev)
+    cache = kvq.Cache(cfg, device=dev, lut=lut_t, vlut=vlut_t)
     T = k.shape[2]
     chunks = chunks or [T]
     assert sum(chunks) == T
@@ -127,7 +130,7 @@ def build_gpu_cache(cfg: dict, k: np.ndarray, v: np.ndarray, chunks=None, lut=No
     return cache
 
 
-def oracle_heads(cfg: dict, k: np.ndarray, v: np.ndarray, lut=None, heads=None) -> dict:
+def oracle_heads(cfg: dict, k: np.ndarray, v: np.ndarray, lut=None, heads=None, vlut=None) -> dict:
     import oracle
     out = {}
     B, H = k.shape[0], k.shape[1]
@@ -135,7 +138,7 @@ def oracle_heads(cfg: dict, k: np.ndarray, v: np.ndarray, lut=None, heads=None) 
         for h in range(H):
             if heads is not None and (b, h) not in heads:
                 continue
-            hc = oracle.HeadCache(cfg, None if lut is None else lut[h])
+            hc = oracle.HeadCache(cfg, None if lut is None else lut[h], None if vlut is None else vlut[h])
             hc.build(k[b, h], v[b, h])
             out[(b, h)] = hc
     return out
