@@ -75,7 +75,7 @@ def decode_bytes_per_token_head(cfg) -> float:
     rk = D * cfg["k_bits"] / 8
     rv = D * cfg["v_bits"] / 8
     kmeta = 2 * D * 2 / Bk if cfg["k_mode"] == 0 else 0.0
-    vmeta = (D // cfg["v_group"]) * 2 * 2
+    vmeta = (D // cfg["v_group"]) * 2 * 2 if cfg.get("v_mode", 0) == 0 else 0.0
     csr = 2 * ko * 3
     kept = keep_count(cfg) * (1 + 2 * D) / Bk
     return rk + rv + kmeta + vmeta + csr + kept
@@ -84,6 +84,7 @@ def decode_bytes_per_token_head(cfg) -> float:
 def decode_bytes(cfg, T) -> float:
     B, H, Hq, D = cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
     lut = H * D * (1 << cfg["k_bits"]) * 2 if cfg["k_mode"] == 1 else 0
+    lut += H * D * (1 << cfg["v_bits"]) * 2 if cfg.get("v_mode", 0) == 1 else 0
     return B * H * T * decode_bytes_per_token_head(cfg) + B * Hq * D * (2 + 4) + lut
 
 
@@ -127,7 +128,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(cfg, k, v, q, lut, seconds: float):
+def cpu_baseline(cfg, k, v, q, lut, seconds: float, vlut=None):
     """The oracle as it stands, on a bounded sample of the same workload: quantize a
     sample of heads (OpenMP across heads), then time fp64 decode over them; each leg
     is sized to about ``seconds`` of wall time."""
@@ -138,7 +139,7 @@ def cpu_baseline(cfg, k, v, q, lut, seconds: float):
     gq = Hq // H
     threads = oracle.max_threads()
     t0 = time.perf_counter()
-    hc = oracle.HeadCache(cfg, None if lut is None else lut[0]).build(k[0, 0], v[0, 0])
+    hc = oracle.HeadCache(cfg, None if lut is None else lut[0], None if vlut is None else vlut[0]).build(k[0, 0], v[0, 0])
     t_build1 = time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.decode_many(cfg, [hc], q[0, :1], T - 1)
@@ -149,8 +150,9 @@ def cpu_baseline(cfg, k, v, q, lut, seconds: float):
     ks = np.stack([k[b, h] for (b, h) in sample])
     vs = np.stack([v[b, h] for (b, h) in sample])
     luts = None if lut is None else [lut[h] for (_, h) in sample]
+    vluts = None if vlut is None else [vlut[h] for (_, h) in sample]
     t0 = time.perf_counter()
-    heads = oracle.build_heads(cfg, ks, vs, luts)
+    heads = oracle.build_heads(cfg, ks, vs, luts, vluts)
     t_build = time.perf_counter() - t0
     del ks, vs
     hl = [heads[i] for i in range(nheads) for _ in range(gq)]
@@ -352,6 +354,8 @@ def main():
     ap.add_argument("--paged", action="store_true", help="also time a paged cache with mixed sequence lengths")
     ap.add_argument("--keep-pct", type=int, default=0,
                     help="the workload with this percentage of each block's keys kept in fp16 by norm")
+    ap.add_argument("--v-codebook", choices=["none", "kmeans", "log"], default="none",
+                    help="the workload with values quantized by a per-channel codebook (calibrated or log-spaced)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -366,6 +370,9 @@ def main():
     if args.keep_pct:
         cfg["keep_pct"] = args.keep_pct
         cfg["workload"] += "-keep%dpct" % args.keep_pct
+    if args.v_codebook != "none":
+        cfg["v_mode"] = 1
+        cfg["workload"] += "-v%s" % args.v_codebook
     T, B, H, Hq, D = cfg["tokens"], cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
     existing = cfg["existing"]
     log("workload", args.workload, cfg["workload"])
@@ -374,6 +381,9 @@ def main():
     v = synth.gen_tensor(cfg, synth.TENSOR_V)
     q = synth.gen_q(cfg)
     lut = synth.calib_lut(cfg) if cfg["k_mode"] == 1 else None
+    vlut = None
+    if args.v_codebook != "none":
+        vlut = synth.calib_log_vlut(cfg) if args.v_codebook == "log" else synth.calib_vlut(cfg)
     log("inputs drawn in %.1f s" % (time.time() - t0))
 
     import torch
@@ -383,7 +393,8 @@ def main():
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.float16)
     k_d, v_d, q_d = up(k), up(v), up(q)
     lut_d = None if lut is None else torch.from_numpy(lut.view(np.int16)).to(dev)
-    cache = kvq.Cache(cfg, device=dev, lut=lut_d)
+    vlut_d = None if vlut is None else torch.from_numpy(vlut.view(np.int16)).to(dev)
+    cache = kvq.Cache(cfg, device=dev, lut=lut_d, vlut=vlut_d)
     if existing:
         cache.append(k_d[:, :, :existing].contiguous(), v_d[:, :, :existing].contiguous())
     k_new = k_d[:, :, existing:].contiguous()
@@ -475,7 +486,8 @@ def main():
         "config": {"workload": cfg["workload"], "batch": B, "q_heads": Hq, "kv_heads": H,
                    "head_dim": D, "tokens": T, "appended_per_step": n_new, "k_bits": cfg["k_bits"],
                    "v_bits": cfg["v_bits"], "k_block": cfg["k_block"], "v_group": cfg["v_group"],
-                   "splits": args.splits or "auto", "keep_pct": cfg.get("keep_pct", 0)},
+                   "splits": args.splits or "auto", "keep_pct": cfg.get("keep_pct", 0),
+                   "v_mode": cfg.get("v_mode", 0)},
         "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "decode_us": round(float(dec_ms.mean()) * 1e3, 2),
         "append_us": round(float(app_ms.mean()) * 1e3, 2),
@@ -519,7 +531,7 @@ def main():
         rec["paged"] = time_paged(cfg, k_d, v_d, lut_d, dev)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
-        rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(cfg, k, v, q, lut, args.cpu_seconds, vlut)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -8,17 +8,21 @@ namespace {
 // sorted fp16 centroids, decided at the fp32 midpoints (C[k] + C[k+1]) / 2 with ties to
 // the lower code ([KVC3] "Non-Uniform KV Cache Quantization", which names the Value
 // cache first; a log-spaced codebook is the log quantization of [TQ] section 3.3).
-// Elementwise: no statistics, outliers or clipping.  A thread packs whole words (one
-// channel, 32 / VB consecutive tokens, as the uniform kernel stores them), reading each
-// token from the tail or from the new rows.
+// Elementwise: no statistics, outliers or clipping.  The code is the number of
+// midpoints below x, found by a binary search over the channel's midpoints in LDS
+// (they never decrease, so the search and the count agree; NaN compares false and gets
+// code 0).  A thread takes one token group (32 / VB tokens) of 8 channels: a 16-byte
+// load per token row (from the tail or from the new rows), 8 words out (one channel,
+// the group's tokens, as the uniform kernel stores them).  The midpoints are stored
+// index-major, [k][D], so that a wave's lookups spread over the banks by channel.
 template <int D, int BK, int VB>
 __global__ __launch_bounds__(qb::kThreads) void quantize_values_lut_kernel(kvq_cache c, const uint16_t* __restrict__ v_new,
                                                                            int64_t old_len_arg, int64_t n_new,
                                                                            int64_t n_first, const int64_t* __restrict__ n_seq) {
   constexpr int NL = 1 << VB, L = NL - 1;
   constexpr int TPW = 32 / VB;
-  constexpr int NWORD = (BK / TPW) * D;  // words of the block
-  __shared__ float mid[D * L];
+  constexpr int NTASK = (BK / TPW) * (D / 8);  // (token group, channel octet) pairs
+  __shared__ float mid[L * D];
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t old_len = c.seq_lens ? seq_len_of(c, b) : old_len_arg;
   const int64_t n_b = n_seq ? min(max(n_seq[b], (int64_t)0), n_new) : n_new;
@@ -29,27 +33,34 @@ __global__ __launch_bounds__(qb::kThreads) void quantize_values_lut_kernel(kvq_c
   const uint16_t* lut = c.v_lut + (int64_t)h * D * NL;
   for (int k = threadIdx.x; k < D * L; k += qb::kThreads) {
     const int ch = k / L, e = k % L;
-    mid[k] = (h2f(lut[ch * NL + e]) + h2f(lut[ch * NL + e + 1])) * 0.5f;
+    mid[e * D + ch] = (h2f(lut[ch * NL + e]) + h2f(lut[ch * NL + e + 1])) * 0.5f;
   }
   __syncthreads();
   const int64_t t0 = n * BK, tail0 = (old_len / BK) * BK;
-  uint32_t* words = static_cast<uint32_t*>(c.v_codes) + g * NWORD;
-  for (int w = threadIdx.x; w < NWORD; w += qb::kThreads) {
-    const int tg = w / D, ch = w % D;
-    const float* m = mid + ch * L;
-    uint32_t word = 0u;
+  uint32_t* words = static_cast<uint32_t*>(c.v_codes) + g * (BK / TPW) * D;
+  for (int task = threadIdx.x; task < NTASK; task += qb::kThreads) {
+    const int tg = task / (D / 8), c0 = 8 * (task % (D / 8));
+    uint32_t wd[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int64_t t = t0 + tg * TPW + u;
       const uint16_t* row = t < old_len ? c.v_tail + (bh * BK + (t - tail0)) * D
                                         : v_new + (bh * n_new + (t - old_len)) * D;
-      const float x = h2f(row[ch]);
-      uint32_t code = 0u;
+      const uint4 x4 = *reinterpret_cast<const uint4*>(row + c0);
+      const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-      for (int k = 0; k < L; ++k) code += x > m[k] ? 1u : 0u;
-      word |= code << (u * VB);
+      for (int e = 0; e < 8; ++e) {
+        const float x = h2f((uint16_t)(xw[e >> 1] >> (16 * (e & 1))));
+        const float* m = mid + c0 + e;
+        uint32_t code = 0u;
+#pragma unroll
+        for (int step = NL / 2; step >= 1; step >>= 1)
+          code += x > m[(code + step - 1) * D] ? (uint32_t)step : 0u;
+        wd[e] |= code << (u * VB);
+      }
     }
-    words[w] = word;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) words[tg * D + c0 + e] = wd[e];
   }
 }
 
