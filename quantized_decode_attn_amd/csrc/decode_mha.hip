@@ -47,9 +47,10 @@ constexpr float kW24Span = 16776960.0f;  // 2^24 - 2^8: full scale of the fixed-
 
 // Per-wave LDS area, in floats.
 struct MLds {
-  int wts, s, ps, vcorr, total;
+  int wts, s, ps, vcorr, vlut, total;
 };
-__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut, bool keep = false) {
+// nvl: entries per channel of the value codebook (codebook values), else 0
+__host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut, bool keep = false, int nvl = 0) {
   MLds m;
   int o = 0;
   // uniform keys: A1 B1 Z1 A2 B2 Z2 [WR WI [ZA ZB]]; codebook keys: WR WI; one array per name
@@ -58,6 +59,10 @@ __host__ __device__ inline MLds mha_lds(int D, int BK, bool outl, bool lut, bool
                                               // then the fixed-point value weights [2][BK] (u32)
   m.ps = o; o += 256;                         // nibble planes of the value weights [2][16][8]
   m.vcorr = o; o += outl ? D + 4 : 0;         // value outlier corrections [D] (int), then the scale shift
+  // value codebook [nvl][D] (fp16): codebook values use no nibble planes and have no
+  // outliers, so it starts at the planes' area and runs on past it
+  m.vlut = m.ps;
+  if (nvl && D * nvl / 2 > 256) o += D * nvl / 2 - 256;
   m.total = o;
   return m;
 }
@@ -144,7 +149,7 @@ __device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, V
   }
 }
 
-template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG, bool KEEP>
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG, bool KEEP, bool VCB>
 __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTok& C, MState& st,
                                               float* __restrict__ wl, const MLds& L, const float* __restrict__ table,
                                               const uint32_t* __restrict__ ptab, float wq_r, float wq_i,
@@ -178,7 +183,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   // so they are loaded here rather than a block ahead (the loads then never stay in
   // flight across the block loop, which would make the compiler drain every load
   // before the next block)
-  load_vmeta(R, c, g, lane, ng);
+  if constexpr (!VCB) load_vmeta(R, c, g, lane, ng);
   if constexpr (OUTL) load_csr_tok<BK, KO>(C, c, g, lane);
   // keys of this block kept in fp16 (at most 16 rows, stored in ascending token order):
   // lane covers rotary pairs 16 (lane & 3) .. +16 of kept row lane >> 2, channels of both
@@ -404,159 +409,194 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     st.zpart[1] *= alpha;
   }
 
-  // ---- value weights w_t = p_t * scale_t per [group][token], quantized per block to
-  // 24-bit fixed point for the integer dot products: W = rint(w K) with
-  // K = (2^24 - 2^8) / (the block's largest weight), so W < 2^24 and each weight is
-  // exact up to half a unit (2^-25 of the block maximum) plus the fp32 rounding of w K
-  // (2^-24 of w itself).  Summed over a block the first part is at most
-  // BK L 2^-25 max(scale) = 2^-25 BK max|v - z|, below the worst case of a plain fp32
-  // sum of the BK products (BK 2^-24 of the largest), however small a weight is next to
-  // the block maximum.  The zero-point part p_t * zero_t is summed in fp32.  Element
-  // lane + 64 k is token (64 k) % BK + lane of group (64 k) / BK, so its probability is
-  // p[((64 k) % BK) / 64].
-  uint32_t* W32 = reinterpret_cast<uint32_t*>(Sc);                        // [2][BK], over the scores
-  uint32_t* PLN = reinterpret_cast<uint32_t*>(PS);                        // [2][16][8] nibble planes
-  float wv[4], vzc[4];
-  float wmax0 = 0.0f, wmax1 = 0.0f;
+  float vzc[4];  // value zero-points of elements lane + 64 k (uniform values)
+  if constexpr (VCB) {
+    // ---- codebook values: every token's probability to LDS (over the scores), then
+    // acc += p_t * codebook[channel][code] for each code of the lane's value words (the
+    // head's fp16 codebook sits in the wave's LDS area); no fixed point, no zero-point
+    float* PT = Sc;
+    wave_lds_sync();  // every lane has read its scores
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int grp = (kWave * k) / BK, kt = ((kWave * k) % BK) / kWave;
-    wv[k] = 0.0f;
-    vzc[k] = 0.0f;
-    if (kWave * k < BK * ng) {
-      const float pp = p[kt];
-      wv[k] = pp * h2f(R.vs[k]);
-      const float z = h2f(R.vz[k]);
-      vzc[k] = z;
-      if (grp == 0) {
-        st.zpart[0] = __builtin_fmaf(pp, z, st.zpart[0]);
-        wmax0 = fmaxf(wmax0, wv[k]);
-      } else {
-        st.zpart[1] = __builtin_fmaf(pp, z, st.zpart[1]);
-        wmax1 = fmaxf(wmax1, wv[k]);
-      }
-    }
-  }
-  wmax0 = wave_max_uniform(wmax0);
-  if (ng > 1) wmax1 = wave_max_uniform(wmax1);
-  // fixed-point scale and its inverse; they need only agree with each other (to fp32
-  // rounding).  wmax * K <= (2^24 - 2^8)(1 + 2^-22) stays below 2^24.
-  const float kq0 = wmax0 > 0.0f ? kW24Span * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
-  const float kq1 = wmax1 > 0.0f ? kW24Span * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
-  wave_lds_sync();  // every lane has read its scores before the weights overwrite them
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = lane + 64 * k;
-    if (kWave * k < BK * ng) {
-      const float kq = (kWave * k) / BK == 0 ? kq0 : kq1;
-      W32[e] = (uint32_t)__builtin_rintf(wv[k] * kq);
-    }
-  }
-  wave_lds_sync();
-  // nibble planes: plane n of a token group holds nibble n of each token's weight,
-  // token u of the group at bits [4u, 4u+4) (the bit position of its code in a word);
-  // a lane builds planes kk and kk + 4 of one token group
-  for (int grp = 0; grp < ng; ++grp) {
-    const uint32_t* wg = W32 + grp * BK;
-    uint32_t plo = 0, phi = 0;
-    if constexpr (VB == 4) {
-      const int tg = lane >> 2, kk = lane & 3;           // 16 groups of 8 tokens
-      if (tg < BK / 8) {
-        const uint4 w0 = *reinterpret_cast<const uint4*>(wg + 8 * tg);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(wg + 8 * tg + 4);
-        const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          plo |= __builtin_amdgcn_ubfe(d[u], 4 * kk, 4) << (4 * u);
-          phi |= __builtin_amdgcn_ubfe(d[u], 4 * kk + 16, 4) << (4 * u);
-        }
-        PLN[grp * 128 + 8 * tg + kk] = plo;
-        PLN[grp * 128 + 8 * tg + 4 + kk] = phi;
-      }
-    } else {
-      const int tg = lane >> 3, par = (lane >> 2) & 1, kk = lane & 3;   // 8 groups of 16 tokens
-      if (tg < BK / 16) {
-        uint32_t d[8];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {  // tokens 2u + par of the group
-          const uint4 w = *reinterpret_cast<const uint4*>(wg + 16 * tg + 4 * h);
-          d[2 * h] = par ? w.y : w.x;
-          d[2 * h + 1] = par ? w.w : w.z;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          plo |= __builtin_amdgcn_ubfe(d[u], 4 * kk, 4) << (4 * u);
-          phi |= __builtin_amdgcn_ubfe(d[u], 4 * kk + 16, 4) << (4 * u);
-        }
-        PLN[grp * 128 + 16 * tg + 8 * par + kk] = plo;
-        PLN[grp * 128 + 16 * tg + 8 * par + 4 + kk] = phi;
-      }
-    }
-  }
-  wave_lds_sync();
-
-  // ---- the next block's weights: this block's were last read by its softmax (key
-  // outliers); writing them here lets their LDS round trip overlap the value dot products
-  write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
-
-  // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
-  // sum_t w_t * code_t by 4-bit integer dot products over the six weight nibbles, in
-  // two passes (bits 16..23, then 0..15) that share the accumulator registers.  A plane
-  // sum is at most BK * 15 * 15 = 28,800, so four planes combine exactly in 32 bits.
-  const int ch0 = (4 * lane) % D;
-  const int grp0 = ch0 / G;
-  const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / kW24Span);
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int poff = pass == 0 ? 4 : 0;  // plane offset within a token group's eight
-    const int npl = pass == 0 ? 2 : 4;   // planes 4 and 5 hold bits 16..23; 6 and 7 are zero
-    uint32_t ia[4][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int pl = 0; pl < 4; ++pl) ia[k][pl] = 0;
+    for (int k = 0; k < TPL; ++k) PT[lane + kWave * k] = p[k];
+    wave_lds_sync();
+    write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
+    constexpr int NLV = 1 << VB;
+    // [NLV][D], read as fp16 so that the products are mixed-precision FMAs
+    const _Float16* book = reinterpret_cast<const _Float16*>(wl + L.vlut);
+    const int ch0 = (4 * lane) % D;
 #pragma unroll
     for (int i = 0; i < Sh::NVI; ++i) {
-      const int g = i * (256 / D) + (4 * lane) / D;
+      const int g = i * (256 / D) + (4 * lane) / D;  // the load's token group
       const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
-      if constexpr (VB == 4) {
-        const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 8 * g + poff);
+      float pp[Sh::TPW];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          ia[k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[k][0], false);
-          ia[k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[k][1], false);
-          if (npl == 4) {
-            ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
-            ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
-          }
-        }
-      } else {
-        const uint4 pe = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + poff);
-        const uint4 po = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + 8 + poff);
+      for (int q4 = 0; q4 < Sh::TPW / 4; ++q4) {
+        const float4 f = *reinterpret_cast<const float4*>(PT + g * Sh::TPW + 4 * q4);
+        pp[4 * q4] = f.x; pp[4 * q4 + 1] = f.y; pp[4 * q4 + 2] = f.z; pp[4 * q4 + 3] = f.w;
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
-          ia[k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[k][0], false);
-          ia[k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[k][1], false);
-          ia[k][0] = __builtin_amdgcn_udot8(po.x, od, ia[k][0], false);
-          ia[k][1] = __builtin_amdgcn_udot8(po.y, od, ia[k][1], false);
-          if (npl == 4) {
-            ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
-            ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
-            ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
-            ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
-          }
+      for (int k = 0; k < 4; ++k) {
+        const _Float16* cb = book + ch0 + k;
+#pragma unroll
+        for (int u = 0; u < Sh::TPW; ++u)
+          st.acc[k] = __builtin_fmaf(pp[u], (float)cb[((words[k] >> (u * VB)) & (NLV - 1u)) * D], st.acc[k]);
+      }
+    }
+  } else {
+    // ---- value weights w_t = p_t * scale_t per [group][token], quantized per block to
+    // 24-bit fixed point for the integer dot products: W = rint(w K) with
+    // K = (2^24 - 2^8) / (the block's largest weight), so W < 2^24 and each weight is
+    // exact up to half a unit (2^-25 of the block maximum) plus the fp32 rounding of w K
+    // (2^-24 of w itself).  Summed over a block the first part is at most
+    // BK L 2^-25 max(scale) = 2^-25 BK max|v - z|, below the worst case of a plain fp32
+    // sum of the BK products (BK 2^-24 of the largest), however small a weight is next to
+    // the block maximum.  The zero-point part p_t * zero_t is summed in fp32.  Element
+    // lane + 64 k is token (64 k) % BK + lane of group (64 k) / BK, so its probability is
+    // p[((64 k) % BK) / 64].
+    uint32_t* W32 = reinterpret_cast<uint32_t*>(Sc);                        // [2][BK], over the scores
+    uint32_t* PLN = reinterpret_cast<uint32_t*>(PS);                        // [2][16][8] nibble planes
+    float wv[4];
+    float wmax0 = 0.0f, wmax1 = 0.0f;
+  #pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int grp = (kWave * k) / BK, kt = ((kWave * k) % BK) / kWave;
+      wv[k] = 0.0f;
+      vzc[k] = 0.0f;
+      if (kWave * k < BK * ng) {
+        const float pp = p[kt];
+        wv[k] = pp * h2f(R.vs[k]);
+        const float z = h2f(R.vz[k]);
+        vzc[k] = z;
+        if (grp == 0) {
+          st.zpart[0] = __builtin_fmaf(pp, z, st.zpart[0]);
+          wmax0 = fmaxf(wmax0, wv[k]);
+        } else {
+          st.zpart[1] = __builtin_fmaf(pp, z, st.zpart[1]);
+          wmax1 = fmaxf(wmax1, wv[k]);
         }
       }
     }
-    const float unit = pass == 0 ? inv * 65536.0f : inv;
-#pragma unroll
+    wmax0 = wave_max_uniform(wmax0);
+    if (ng > 1) wmax1 = wave_max_uniform(wmax1);
+    // fixed-point scale and its inverse; they need only agree with each other (to fp32
+    // rounding).  wmax * K <= (2^24 - 2^8)(1 + 2^-22) stays below 2^24.
+    const float kq0 = wmax0 > 0.0f ? kW24Span * __builtin_amdgcn_rcpf(wmax0) : 0.0f;
+    const float kq1 = wmax1 > 0.0f ? kW24Span * __builtin_amdgcn_rcpf(wmax1) : 0.0f;
+    wave_lds_sync();  // every lane has read its scores before the weights overwrite them
+  #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t tot = ia[k][0] + (ia[k][1] << 4) + (ia[k][2] << 8) + (ia[k][3] << 12);
-      st.acc[k] = __builtin_fmaf((float)tot, unit, st.acc[k]);
+      const int e = lane + 64 * k;
+      if (kWave * k < BK * ng) {
+        const float kq = (kWave * k) / BK == 0 ? kq0 : kq1;
+        W32[e] = (uint32_t)__builtin_rintf(wv[k] * kq);
+      }
     }
-  }
+    wave_lds_sync();
+    // nibble planes: plane n of a token group holds nibble n of each token's weight,
+    // token u of the group at bits [4u, 4u+4) (the bit position of its code in a word);
+    // a lane builds planes kk and kk + 4 of one token group
+    for (int grp = 0; grp < ng; ++grp) {
+      const uint32_t* wg = W32 + grp * BK;
+      uint32_t plo = 0, phi = 0;
+      if constexpr (VB == 4) {
+        const int tg = lane >> 2, kk = lane & 3;           // 16 groups of 8 tokens
+        if (tg < BK / 8) {
+          const uint4 w0 = *reinterpret_cast<const uint4*>(wg + 8 * tg);
+          const uint4 w1 = *reinterpret_cast<const uint4*>(wg + 8 * tg + 4);
+          const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  #pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            plo |= __builtin_amdgcn_ubfe(d[u], 4 * kk, 4) << (4 * u);
+            phi |= __builtin_amdgcn_ubfe(d[u], 4 * kk + 16, 4) << (4 * u);
+          }
+          PLN[grp * 128 + 8 * tg + kk] = plo;
+          PLN[grp * 128 + 8 * tg + 4 + kk] = phi;
+        }
+      } else {
+        const int tg = lane >> 3, par = (lane >> 2) & 1, kk = lane & 3;   // 8 groups of 16 tokens
+        if (tg < BK / 16) {
+          uint32_t d[8];
+  #pragma unroll
+          for (int h = 0; h < 4; ++h) {  // tokens 2u + par of the group
+            const uint4 w = *reinterpret_cast<const uint4*>(wg + 16 * tg + 4 * h);
+            d[2 * h] = par ? w.y : w.x;
+            d[2 * h + 1] = par ? w.w : w.z;
+          }
+  #pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            plo |= __builtin_amdgcn_ubfe(d[u], 4 * kk, 4) << (4 * u);
+            phi |= __builtin_amdgcn_ubfe(d[u], 4 * kk + 16, 4) << (4 * u);
+          }
+          PLN[grp * 128 + 16 * tg + 8 * par + kk] = plo;
+          PLN[grp * 128 + 16 * tg + 8 * par + 4 + kk] = phi;
+        }
+      }
+    }
+    wave_lds_sync();
 
+    // ---- the next block's weights: this block's were last read by its softmax (key
+    // outliers); writing them here lets their LDS round trip overlap the value dot products
+    write_block_weights<D, BK, KB, VB, KO, LUT, KEEP>(R, wl + L.wts, wq_r, wq_i, inv_unit, lane);
+
+    // ---- values: lane owns channels ch0..ch0+3, the token group changes with the load;
+    // sum_t w_t * code_t by 4-bit integer dot products over the six weight nibbles, in
+    // two passes (bits 16..23, then 0..15) that share the accumulator registers.  A plane
+    // sum is at most BK * 15 * 15 = 28,800, so four planes combine exactly in 32 bits.
+    const int ch0 = (4 * lane) % D;
+    const int grp0 = ch0 / G;
+    const float inv = (grp0 == 0 ? wmax0 : wmax1) * (1.0f / kW24Span);
+  #pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int poff = pass == 0 ? 4 : 0;  // plane offset within a token group's eight
+      const int npl = pass == 0 ? 2 : 4;   // planes 4 and 5 hold bits 16..23; 6 and 7 are zero
+      uint32_t ia[4][4];
+  #pragma unroll
+      for (int k = 0; k < 4; ++k)
+  #pragma unroll
+        for (int pl = 0; pl < 4; ++pl) ia[k][pl] = 0;
+  #pragma unroll
+      for (int i = 0; i < Sh::NVI; ++i) {
+        const int g = i * (256 / D) + (4 * lane) / D;
+        const uint32_t words[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+        if constexpr (VB == 4) {
+          const uint4 pl = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 8 * g + poff);
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ia[k][0] = __builtin_amdgcn_udot8(pl.x, words[k], ia[k][0], false);
+            ia[k][1] = __builtin_amdgcn_udot8(pl.y, words[k], ia[k][1], false);
+            if (npl == 4) {
+              ia[k][2] = __builtin_amdgcn_udot8(pl.z, words[k], ia[k][2], false);
+              ia[k][3] = __builtin_amdgcn_udot8(pl.w, words[k], ia[k][3], false);
+            }
+          }
+        } else {
+          const uint4 pe = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + poff);
+          const uint4 po = *reinterpret_cast<const uint4*>(PLN + grp0 * 128 + 16 * g + 8 + poff);
+  #pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t ev = words[k] & 0x33333333u, od = (words[k] >> 2) & 0x33333333u;
+            ia[k][0] = __builtin_amdgcn_udot8(pe.x, ev, ia[k][0], false);
+            ia[k][1] = __builtin_amdgcn_udot8(pe.y, ev, ia[k][1], false);
+            ia[k][0] = __builtin_amdgcn_udot8(po.x, od, ia[k][0], false);
+            ia[k][1] = __builtin_amdgcn_udot8(po.y, od, ia[k][1], false);
+            if (npl == 4) {
+              ia[k][2] = __builtin_amdgcn_udot8(pe.z, ev, ia[k][2], false);
+              ia[k][3] = __builtin_amdgcn_udot8(pe.w, ev, ia[k][3], false);
+              ia[k][2] = __builtin_amdgcn_udot8(po.z, od, ia[k][2], false);
+              ia[k][3] = __builtin_amdgcn_udot8(po.w, od, ia[k][3], false);
+            }
+          }
+        }
+      }
+      const float unit = pass == 0 ? inv * 65536.0f : inv;
+  #pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t tot = ia[k][0] + (ia[k][1] << 4) + (ia[k][2] << 8) + (ia[k][3] << 12);
+        st.acc[k] = __builtin_fmaf((float)tot, unit, st.acc[k]);
+      }
+    }
+
+  }
   // ---- value outliers: p * (x - zero) scattered into the channel array, merged into
   // the accumulators at the next block's softmax (or the item's end), so that the
   // atomics complete in the shadow of the next block's scores
@@ -588,7 +628,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
 
 // One (b, head, split) item on one wave: every full block of the split, then the
 // split's (m, l, o) to the workspace.
-template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG, bool KEEP>
+template <int D, int BK, int KB, int VB, int KO, bool LUT, bool PG, bool KEEP, bool VCB>
 __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __restrict__ q, int64_t q_pos,
                                          float* __restrict__ ws, int S, int64_t bh, int split, float* wl,
                                          const MLds& L, const float* table, const uint32_t* ptab, int lane) {
@@ -634,6 +674,15 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
   BlockRegs<D, BK, KB, VB> R;
   CsrTok C;
   const SlotRow sr = slot_row(c, b, h);
+  if constexpr (VCB) {
+    // the head's value codebook into the wave's LDS area, code-major ([code][channel]):
+    // a wave's lookups then spread over the banks by channel
+    constexpr int NLV = 1 << VB;
+    const uint16_t* src = c.v_lut + (int64_t)h * D * NLV;  // [channel][code]
+    uint16_t* dst = reinterpret_cast<uint16_t*>(wl + L.vlut);
+    for (int k = lane; k < D * NLV; k += kWave) dst[(k % NLV) * D + k / NLV] = src[k];
+    wave_lds_sync();
+  }
   if (n0 < nfull) {
     const int64_t g0 = slot_at<PG>(sr, n0);
     if constexpr (LUT) load_eb(R, c, n0, lane);
@@ -647,7 +696,7 @@ __device__ __forceinline__ void mha_item(const kvq_cache& c, const uint16_t* __r
     for (int i = 0; i < Sh::NVI; ++i) load_v(R, i, vb0, lane);
   }
   for (int64_t n = n0; n < nfull; n += S)
-    process_block<D, BK, KB, VB, KO, LUT, PG, KEEP>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
+    process_block<D, BK, KB, VB, KO, LUT, PG, KEEP, VCB>(R, C, st, wl, L, table, pt, wq_r, wq_i, inv_unit, lane, ts, r, sh, G, ng,
                                           c, sr, n, S, n + S < nfull, koff);
   if (OUTL) {
     wave_lds_sync();
@@ -690,7 +739,7 @@ __device__ __forceinline__ void stage_rope(float* table, const kvq_cache& c) {
 
 // Uniform keys: every wave takes items on its own.  PG: per-sequence lengths (dense or
 // paged slots); KEEP: keys kept in fp16 by norm.
-template <int D, int BK, int KB, int VB, int KO, bool PG, bool KEEP = false>
+template <int D, int BK, int KB, int VB, int KO, bool PG, bool KEEP = false, bool VCB = false>
 __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
                                                                    int64_t nitems) {
@@ -703,7 +752,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
 
   float* table = lds;
   stage_rope<D, BK, kNT>(table, c);
-  const MLds L = mha_lds(D, BK, OUTL, false, KEEP);
+  const MLds L = mha_lds(D, BK, OUTL, false, KEEP, VCB ? 1 << VB : 0);
   float* wl = lds + BK * Sh::TPITCH + wave * L.total;
   if (OUTL)
     for (int k = lane; k < D + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
@@ -711,8 +760,8 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
 
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
   for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves)
-    mha_item<D, BK, KB, VB, KO, false, PG, KEEP>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table, nullptr,
-                                                 lane);
+    mha_item<D, BK, KB, VB, KO, false, PG, KEEP, VCB>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table,
+                                                      nullptr, lane);
 }
 
 // Codebook keys: the workgroup takes groups of up to 8 splits of one (b, head), so
@@ -750,7 +799,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
       ptab[i * PT::PITCH + pc] = ka | (kb << 16);
     }
     __syncthreads();
-    if (split < S) mha_item<D, BK, KB, VB, 0, true, PG, false>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
+    if (split < S) mha_item<D, BK, KB, VB, 0, true, PG, false, false>(c, q, q_pos, ws, S, bh, split, wl, L, table, ptab, lane);
   }
 }
 
@@ -761,21 +810,21 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
 hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                              hipStream_t s, int cus, bool dry);
 
-template <int D, int BK, int KB, int VB, int KO, bool PG = false, bool KEEP = false>
+template <int D, int BK, int KB, int VB, int KO, bool PG = false, bool KEEP = false, bool VCB = false>
 static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos, float* ws, int S,
                                    hipStream_t s, int cus, bool dry) {
   using Sh = MShape<D, BK, KB, VB>;
-  const MLds L = mha_lds(D, BK, KO > 0, false, KEEP);
+  const MLds L = mha_lds(D, BK, KO > 0, false, KEEP, VCB ? 1 << VB : 0);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
   if (bytes > 160 * 1024) return hipErrorNotSupported;
   if (dry) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP>,
+  hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP, VCB>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
   const int64_t nitems = (int64_t)c.cfg.batch * c.cfg.kv_heads * S;
   int64_t grid = (nitems + kMhaWaves - 1) / kMhaWaves;
   if (grid > cus) grid = cus;
-  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
+  hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP, VCB>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
                      q, q_pos, ws, S, nitems);
   return hipGetLastError();
 }
@@ -805,7 +854,20 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ko = host_kout(g);
   const int ng = g.head_dim / g.v_group;
   if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
-  if (g.v_mode != 0) return hipErrorNotSupported;  // codebook values: the generic kernel
+  if (g.v_mode != 0) {
+    // codebook values (no outliers by construction): uniform 4-bit keys at head_dim 128
+    // and 128-token blocks, 2- or 4-bit values, dense or per-sequence, no kept keys;
+    // everything else takes the generic kernel
+    if (g.head_dim != 128 || g.k_block != 128 || g.k_bits != 4 || g.k_mode != 0 || ko != 0 || g.keep_pct > 0)
+      return hipErrorNotSupported;
+    if (g.v_bits == 4)
+      return c.seq_lens ? launch_mha_typed<128, 128, 4, 4, 0, true, false, true>(c, q, q_pos, ws, S, s, cus, dry)
+                        : launch_mha_typed<128, 128, 4, 4, 0, false, false, true>(c, q, q_pos, ws, S, s, cus, dry);
+    if (g.v_bits == 2)
+      return c.seq_lens ? launch_mha_typed<128, 128, 4, 2, 0, true, false, true>(c, q, q_pos, ws, S, s, cus, dry)
+                        : launch_mha_typed<128, 128, 4, 2, 0, false, false, true>(c, q, q_pos, ws, S, s, cus, dry);
+    return hipErrorNotSupported;
+  }
   const int D = g.head_dim, BK = g.k_block, KB = g.k_bits, VB = g.v_bits;
   if (g.keep_pct > 0) {
     // keys kept in fp16 (uniform keys without outliers): 4-bit keys at head_dim 128 and

@@ -3,8 +3,9 @@
 pages list among the non-uniform schemes).
 
 Against the CPU oracle: the packed cache bit for bit after ragged appends; decode and
-chunk attention within 2e-3 of the oracle's fp64 attention (the generic kernel, which
-reads each code's entry from its channel's codebook); dequantized keys and values bit
+chunk attention within 2e-3 of the oracle's fp64 attention (the tuned one-head kernel
+for 4-bit keys at head_dim 128, the generic kernel otherwise; both read each code's
+entry from its channel's codebook); dequantized keys and values bit
 for bit; a paged pool with ragged lengths; fused decode steps across a block boundary.
 """
 import numpy as np
@@ -35,6 +36,8 @@ CASES = {
                                      v_mode=1), "log", [200, 1, 300, 189]),
     "gqa_d64_v2_kmeans": (synth.config("c0", q_heads=8, kv_heads=2, v_bits=2, v_group=32, tokens=5 * 64 + 17,
                                        capacity=384, v_mode=1), "kmeans", [64, 100, 173]),
+    "mha_d128_v2_kmeans": (synth.config("c1", batch=1, q_heads=3, kv_heads=3, v_bits=2, v_group=64,
+                                        tokens=4 * 128 + 99, capacity=640, v_mode=1), "kmeans", [128, 300, 183]),
     "k3lut_v2_kmeans": (synth.config("c3", batch=1, q_heads=4, kv_heads=4, tokens=3 * 128 + 9, capacity=512,
                                      v_mode=1), "kmeans", None),
     "keep_and_v4_log": (synth.config("c1", batch=1, q_heads=2, kv_heads=2, tokens=4 * 128 + 77, capacity=640,
