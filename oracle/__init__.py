@@ -84,6 +84,8 @@ def load(path: str):
         "orc_f2h_array": (None, [vp, vp, i64, C.c_int]),
         "orc_kv_bytes": (C.c_double, [i64, i64, i64, i64, i64]),
         "orc_kout": (C.c_int, [C.POINTER(Cfg)]),
+        "orc_f_to_e4m3": (C.c_uint8, [C.c_uint16]),
+        "orc_e4m3_to_f": (C.c_float, [C.c_uint8]),
         "orc_keep_count": (C.c_int, [C.POINTER(Cfg)]),
         "orc_layout": (None, [C.POINTER(Cfg), vp]),
         "orc_clip_threshold": (C.c_float, [vp, i64, C.c_float]),
@@ -139,6 +141,19 @@ def layout(cfg: dict) -> dict:
     return dict(zip(LAYOUT_NAMES, (int(v) for v in out)))
 
 
+def e4m3_from_f16(bits) -> np.ndarray:
+    """fp16 bits -> OCP E4M3 bytes (nearest, ties to even, saturating to +-448)."""
+    b = np.asarray(bits, np.uint16).reshape(-1)
+    L = lib()
+    return np.array([L.orc_f_to_e4m3(int(x)) for x in b], np.uint8).reshape(np.shape(bits))
+
+
+def e4m3_to_f(codes) -> np.ndarray:
+    c = np.asarray(codes, np.uint8).reshape(-1)
+    L = lib()
+    return np.array([L.orc_e4m3_to_f(int(x)) for x in c], np.float32).reshape(np.shape(codes))
+
+
 def h2f(h: np.ndarray) -> np.ndarray:
     h = np.ascontiguousarray(h, np.uint16)
     f = np.empty(h.shape, np.float32)
@@ -188,7 +203,7 @@ class HeadCache:
         vuni = c.get("v_mode", 0) == 0
         self.v_scale = np.zeros((T, ng) if vuni else (0,), np.uint16)
         self.v_zero = np.zeros((T, ng) if vuni else (0,), np.uint16)
-        if not vuni:
+        if c.get("v_mode", 0) == 1:
             assert vlut_head is not None and vlut_head.shape == (D, 1 << c["v_bits"])
             self.v_lut = np.ascontiguousarray(vlut_head, np.uint16)
         else:

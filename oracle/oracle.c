@@ -38,7 +38,8 @@ typedef struct {
   int32_t outlier_pct;
   float rope_theta;
   int32_t keep_pct;        /* key vectors kept in fp16 per block, percent (0 = none) */
-  int32_t v_mode;          /* 0: uniform per-token values; 1: per-channel codebook      */
+  int32_t v_mode;          /* 0: uniform per-token values; 1: per-channel codebook;    */
+                           /* 2: fp8 e4m3 (with k_mode 2)                             */
 } orc_cfg;
 
 /* Buffers of ONE (batch, kv-head) of the cache, laid out exactly as the library's
@@ -84,6 +85,44 @@ float orc_h2f(uint16_t h) {
 }
 
 /* round to nearest, ties to even */
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN, so the largest finite value is 1.75 * 2^8 = 448; the
+ * smallest normal 2^-6, subnormals m * 2^-9.  Written from that definition. */
+float orc_e4m3_to_f(uint8_t b) {
+  const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  float v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexpf((float)m, -9);
+  else
+    v = ldexpf((float)(8 + m), e - 10);           /* (8 + m) * 2^(e-7-3) */
+  return sign ? -v : v;
+}
+
+/* fp16 -> E4M3, round to nearest, ties to even; magnitudes beyond the largest finite
+ * value (infinities included) saturate to +-448; NaN gives S.1111.111.  The fp16
+ * value is exact in float; the grid step at |x| is 2^(floor(log2|x|) - 3) for normal
+ * results and 2^-9 below 2^-6, and nearbyintf rounds ties to even. */
+uint8_t orc_f_to_e4m3(uint16_t h) {
+  const float x = orc_h2f(h);
+  const uint8_t sign = (uint8_t)((h >> 15) << 7);
+  if (x != x) return (uint8_t)(sign | 0x7F);
+  float a = fabsf(x);
+  if (a == 0.0f) return sign;
+  if (isinf(a)) return (uint8_t)(sign | 0x7E);      /* saturate */
+  int e;
+  (void)frexpf(a, &e);                              /* a = f * 2^e, f in [0.5, 1) */
+  int ex = e - 1;                                   /* floor(log2 a) */
+  if (ex < -6) ex = -6;                             /* subnormal step 2^-9 */
+  float q = nearbyintf(ldexpf(a, 3 - ex));          /* units of 2^(ex-3) */
+  if (q >= 16.0f) { q = 8.0f; ex += 1; }            /* rounded up to the next binade */
+  const float r = ldexpf(q, ex - 3);
+  if (r > 448.0f) return (uint8_t)(sign | 0x7E);    /* saturate */
+  if (ex == -6 && q < 8.0f) return (uint8_t)(sign | (uint8_t)q);              /* subnormal */
+  return (uint8_t)(sign | (uint8_t)((ex + 7) << 3) | (uint8_t)((int)q - 8));  /* normal */
+}
+
 uint16_t orc_f2h_rn(float f) {
   const uint16_t sign = signbit(f) ? 0x8000 : 0;
   const float a = fabsf(f);
@@ -163,10 +202,10 @@ void orc_layout(const orc_cfg *c, int64_t out[18]) {
   out[0] = BH * T * D * c->k_bits / 8;
   out[1] = uni ? BH * nblk * D * 2 : 0;
   out[2] = out[1];
-  out[3] = uni ? 0 : (int64_t)c->kv_heads * D * (1 << c->k_bits) * 2;
+  out[3] = c->k_mode == 1 ? (int64_t)c->kv_heads * D * (1 << c->k_bits) * 2 : 0;
   out[4] = BH * c->k_block * D * 2;
   out[5] = BH * T * D * c->v_bits / 8;
-  out[6] = c->v_mode == 1 ? 0 : BH * T * (D / c->v_group) * 2;
+  out[6] = c->v_mode != 0 ? 0 : BH * T * (D / c->v_group) * 2;
   out[7] = out[6];
   out[8] = out[4];
   out[9] = ko ? BH * (T + 1) * 4 : 0;
@@ -402,7 +441,10 @@ int orc_quantize_block(const orc_cfg *c, int is_key, int64_t n, const uint16_t *
     d[i] = clip ? fminf(fmaxf(x, -thr), thr) : x;
   }
   /* 4-5. statistics, metadata, codes */
-  if (is_key && c->k_mode == 1) {
+  if ((is_key && c->k_mode == 2) || (!is_key && c->v_mode == 2)) {
+    /* FP8 cache ([UQ] section 2.1): every element cast to E4M3, no statistics */
+    for (int64_t i = 0; i < nel; ++i) code[i] = orc_f_to_e4m3(src[i]);
+  } else if (is_key && c->k_mode == 1) {
     orc_codebook_codes(hd->k_lut, D, L, Bk, d, mask, code);
   } else if (!is_key && c->v_mode == 1) {
     /* The same for values: the page names the Value cache first among the tensors a
@@ -526,7 +568,9 @@ static void orc_dequant_row(const orc_cfg *c, const orc_head *hd, int which, int
     for (int e = 0; e < D; ++e) {
       const int ch = orc_k_channel_of_element(e, D);
       const uint32_t cc = orc_get_bits(hd->k_codes, orc_k_bitpos(c, t, e), kb);
-      if (c->k_mode == 1)
+      if (c->k_mode == 2)
+        out[ch] = orc_e4m3_to_f((uint8_t)cc);
+      else if (c->k_mode == 1)
         out[ch] = orc_h2f(hd->k_lut[(int64_t)ch * (1 << kb) + cc]);
       else
         out[ch] = fmaf((float)cc, orc_h2f(hd->k_scale[(t / Bk) * D + ch]),
@@ -536,7 +580,9 @@ static void orc_dequant_row(const orc_cfg *c, const orc_head *hd, int which, int
     const int G = c->v_group, ng = D / G;
     for (int ch = 0; ch < D; ++ch) {
       const uint32_t cc = orc_get_bits(hd->v_codes, orc_v_bitpos(c, t, ch), c->v_bits);
-      if (c->v_mode == 1)
+      if (c->v_mode == 2)
+        out[ch] = orc_e4m3_to_f((uint8_t)cc);
+      else if (c->v_mode == 1)
         out[ch] = orc_h2f(hd->v_lut[(int64_t)ch * (1 << c->v_bits) + cc]);
       else
         out[ch] = fmaf((float)cc, orc_h2f(hd->v_scale[t * ng + ch / G]),

@@ -49,6 +49,11 @@ MUTANTS = {
     "vlut_row_stride_halved": ("orc_h2f(hd->v_lut[(int64_t)ch * (1 << c->v_bits) + cc])",
                                "orc_h2f(hd->v_lut[(int64_t)ch * (1 << (c->v_bits - 1)) + cc])"),
     "vlut_channel_ignored": ("orc_h2f(hd->v_lut[(int64_t)ch * (1 << c->v_bits) + cc])", "orc_h2f(hd->v_lut[cc])"),
+    "e4m3_ties_away": ("float q = nearbyintf(ldexpf(a, 3 - ex));", "float q = roundf(ldexpf(a, 3 - ex));"),
+    "e4m3_overflow_to_nan": ("if (r > 448.0f) return (uint8_t)(sign | 0x7E);", "if (r > 448.0f) return (uint8_t)(sign | 0x7F);"),
+    "e4m3_bias_8": ("return (uint8_t)(sign | (uint8_t)((ex + 7) << 3) | (uint8_t)((int)q - 8));",
+                    "return (uint8_t)(sign | (uint8_t)((ex + 8) << 3) | (uint8_t)((int)q - 8));"),
+    "e4m3_decode_bias_off_by_one": ("v = ldexpf((float)(8 + m), e - 10);", "v = ldexpf((float)(8 + m), e - 11);"),
     "vlut_not_in_layout": ("out[17] = c->v_mode == 1 ? (int64_t)c->kv_heads * D * (1 << c->v_bits) * 2 : 0;",
                            "out[17] = 0;"),
 }

@@ -822,3 +822,78 @@ def test_value_codebook_layout_sizes(orc):
     assert lay["v_lut"] == 3 * 16 * 4 * 2
     assert lay["v_codes"] == 2 * 3 * 64 * 16 * 2 // 8
     assert orc.layout(tiny())["v_lut"] == 0
+
+
+# --------------------------------------------------------------------------- FP8 cache
+def _fp8_cfg(D=16, Bk=16, T=48, **kw):
+    return tiny(head_dim=D, k_block=Bk, tokens=T, k_bits=8, k_mode=2, v_bits=8, v_mode=2, v_group=D, **kw)
+
+
+def test_e4m3_conversion_matches_torch_cast(orc):
+    """Every fp16 value: the oracle's E4M3 cast (nearest, ties to even) equals torch's
+    float8_e4m3fn cast, which overflows to NaN where the oracle saturates: compared on
+    the value clamped to +-448.  Infinities saturate, NaN stays NaN."""
+    import torch
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = orc.e4m3_from_f16(h)
+    f = torch.from_numpy(h.view(np.int16)).view(torch.float16).to(torch.float32)
+    ref = f.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    fin = torch.isfinite(f).numpy()
+    assert np.array_equal(mine[fin], ref[fin])
+    assert orc.e4m3_from_f16(np.uint16(0x7C00)) == 0x7E and orc.e4m3_from_f16(np.uint16(0xFC00)) == 0xFE
+    assert (orc.e4m3_from_f16(np.uint16(0x7E00)) & 0x7F) == 0x7F
+    assert orc.e4m3_from_f16(f16(464.0)) == 0x7E and orc.e4m3_from_f16(f16(1.0625)) == 0x38    # ties to even
+
+
+def test_e4m3_decode_matches_torch(orc):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    back = orc.e4m3_to_f(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    same = (back == ref) | (np.isnan(back) & np.isnan(ref))
+    assert same.all()
+    assert np.nanmax(np.abs(back)) == 448.0 and np.isnan(back[0x7F]) and back[1] == 2.0 ** -9
+
+
+def test_fp8_cache_dequantizes_to_the_cast(orc):
+    """Keys and values of an FP8 cache read back as the E4M3 cast of their input, in
+    quantized blocks and (exactly) in the fp16 tail."""
+    import torch
+    rng = np.random.default_rng(81)
+    c = _fp8_cfg(T=53)
+    k = f16(rng.standard_normal((53, 16)) * 40.0)
+    v = f16(rng.standard_normal((53, 16)) * 3.0)
+    hc = orc.HeadCache(c).build(k, v)
+    nq = 48
+    for which, x in ((0, k), (1, v)):
+        cast = torch.from_numpy(x[:nq].view(np.int16)).view(torch.float16).to(torch.float32).clamp(-448, 448)
+        want = cast.to(torch.float8_e4m3fn).to(torch.float32).numpy()
+        got = _deq(hc, which)
+        assert np.array_equal(got[:nq], want)
+        assert np.array_equal(got[nq:], hval(x[nq:]))
+
+
+def test_fp8_cache_is_exact_in_textbook_attention(orc):
+    """Keys and values that are E4M3 numbers come back exactly, so the decode equals
+    plain fp64 softmax attention with rotary matrices on the raw inputs."""
+    rng = np.random.default_rng(82)
+    D, Bk, T = 16, 16, 48
+    codes = rng.integers(0, 256, (2, T, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                        # no NaN
+    kv = orc.e4m3_to_f(codes)
+    k, v = f16(kv[0]), f16(kv[1])
+    hc = orc.HeadCache(_fp8_cfg(D=D, Bk=Bk, T=T)).build(k, v)
+    assert np.array_equal(_deq(hc, 0), hval(k)) and np.array_equal(_deq(hc, 1), hval(v))
+    q = f16(rng.standard_normal(D) * 0.02)
+    for qp in (T - 1, 3):
+        qr = _rot_matrix(qp, D, 10000.0) @ hval(q)
+        kr = np.stack([_rot_matrix(t, D, 10000.0) @ hval(k[t]) for t in range(T)])
+        ref = _softmax_attn(qr, kr, hval(v), D)
+        assert np.max(np.abs(hc.decode(q, q_pos=qp) - ref)) < 1e-9 * max(1.0, np.abs(ref).max())
+
+
+def test_fp8_layout_sizes(orc):
+    lay = orc.layout(_fp8_cfg(T=64, batch=2, kv_heads=3, q_heads=3))
+    assert lay["k_codes"] == lay["v_codes"] == 2 * 3 * 64 * 16          # one byte per element
+    assert lay["k_scale"] == lay["k_zero"] == lay["v_scale"] == lay["v_zero"] == 0
+    assert lay["k_lut"] == lay["v_lut"] == 0
