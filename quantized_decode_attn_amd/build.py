@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.hip", "quantize.hip", "quantize_keys.hip", "quantize_keys_lut.hip", "quantize_values.hip", "dequantize.hip", "decode.hip", "decode_mha.hip", "decode_gqa.hip", "chunk_mfma.hip"]
+SOURCES = ["kvq_api.hip", "quantize.hip", "quantize_keys.hip", "quantize_keys_lut.hip", "quantize_values.hip", "dequantize.hip", "decode.hip", "decode_mha.hip", "decode_gqa.hip", "chunk_mfma.hip", "quantize_fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
     table[j * Sh::TPITCH + 2 * i + 1] = c.rope[2 * idx + 1];
   }
   const bool vcb = c.cfg.v_mode == 1;  // codebook values
+  const bool vf8 = c.cfg.v_mode == 2;  // FP8 values
   constexpr int NLV = 1 << VB;
   const WaveLds L = wave_lds(D, Bk, rs.rpi, ng, Sh::TPI, KB, KMODE, ko > 0, vcb ? D * NLV : 0);
   float* wl = lds + Bk * Sh::TPITCH + wave * L.total;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
       };
 
       // value metadata of the block (quantized blocks only)
-      if (!tail && !vcb) {
+      if (!tail && !vcb && !vf8) {
         for (int k = lane; k < Bk * ng; k += kWave) {
           const int64_t m = gs * Bk * ng + k;
           VS[k] = h2f(c.v_scale[m]);
@@ -299,9 +300,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
                   X = __builtin_fmaf(B1[m], (float)cb, __builtin_fmaf(A1[m], (float)ca, Z1[m]));
                   Y = __builtin_fmaf(B2[m], (float)cb, __builtin_fmaf(A2[m], (float)ca, Z2[m]));
                 } else {
+                  // codebook keys: the channel's entries; FP8 keys: the E4M3 values
                   const int ch = r * Sh::PPL + m;
-                  const float a = lutl[ch * (1 << KB) + ca];
-                  const float bb = lutl[(ch + Sh::HALF) * (1 << KB) + cb];
+                  const float a = KMODE == 2 ? e4m3_to_f32(ca) : lutl[ch * (1 << KB) + ca];
+                  const float bb = KMODE == 2 ? e4m3_to_f32(cb) : lutl[(ch + Sh::HALF) * (1 << KB) + cb];
                   X = __builtin_fmaf(WR[m], a, -WI[m] * bb);
                   Y = -__builtin_fmaf(WI[m], a, WR[m] * bb);
                 }
@@ -366,7 +368,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
         float acc[Sh::CPL];
 #pragma unroll
         for (int k = 0; k < Sh::CPL; ++k) acc[k] = st[2 + lane + k * kWave] * alpha;
-        if (!tail && vcb) {
+        if (!tail && vf8) {
+          // FP8 values: each code is an E4M3 value
+          for (int gw = 0; gw < Bk / Sh::TPW; ++gw) {
+#pragma unroll
+            for (int k = 0; k < Sh::CPL; ++k) {
+              const uint32_t word = vblk[gw * D + lane + k * kWave];
+#pragma unroll
+              for (int u = 0; u < Sh::TPW; ++u)
+                acc[k] = __builtin_fmaf(Pl[gw * Sh::TPW + u], e4m3_to_f32((word >> (u * VB)) & ((1u << VB) - 1u)),
+                                        acc[k]);
+            }
+          }
+          if (lane == 0)
+            for (int gg = 0; gg < ng; ++gg) st[2 + D + gg] *= alpha;
+        } else if (!tail && vcb) {
           // codebook values: each code reads its channel's entry
           for (int gw = 0; gw < Bk / Sh::TPW; ++gw) {
 #pragma unroll
@@ -937,6 +953,9 @@ hipError_t launch_d(const kvq_cache& c, const uint16_t* q, RowSpec rs, float* ws
   if (km == 1 && kb == 4) return launch_vb<D, 4, 1>(c, q, rs, ws, S, s, cus, nt, fused_out);
   if (km == 1 && kb == 3) return launch_vb<D, 3, 1>(c, q, rs, ws, S, s, cus, nt, fused_out);
   if (km == 1 && kb == 2) return launch_vb<D, 2, 1>(c, q, rs, ws, S, s, cus, nt, fused_out);
+  // FP8 keys come with FP8 values
+  if (km == 2 && kb == 8 && c.cfg.v_bits == 8)
+    return launch_typed<D, 8, 2, 8>(c, q, rs, ws, S, s, cus, nt, fused_out);
   return hipErrorInvalidValue;
 }
 

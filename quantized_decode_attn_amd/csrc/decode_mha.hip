@@ -854,6 +854,7 @@ hipError_t launch_decode_mha(const kvq_cache& c, const uint16_t* q, int64_t q_po
   const int ko = host_kout(g);
   const int ng = g.head_dim / g.v_group;
   if (g.q_heads != g.kv_heads || ko > 2 || ng > 2 || g.k_block * ng > 256) return hipErrorNotSupported;
+  if (g.v_mode == 2 || g.k_mode == 2) return hipErrorNotSupported;  // FP8: the generic kernel
   if (g.v_mode != 0) {
     // codebook values (no outliers by construction): uniform 4-bit keys at head_dim 128
     // and 128-token blocks, 2- or 4-bit values, dense or per-sequence, no kept keys;

@@ -37,7 +37,9 @@ __global__ void dequantize_kernel(kvq_cache c, int which, int64_t t0, int64_t t1
       uint32_t w = row[pos >> 3];
       if ((pos & 7) + kb > 8) w |= (uint32_t)row[(pos >> 3) + 1] << 8;
       const uint32_t code = (w >> (pos & 7)) & ((1u << kb) - 1u);
-      if (c.cfg.k_mode == 1) {
+      if (c.cfg.k_mode == 2) {
+        x = e4m3_to_f32(code);
+      } else if (c.cfg.k_mode == 1) {
         x = h2f(c.k_lut[((int64_t)h * D + ch) * (1 << kb) + code]);
       } else {
         const int64_t m = (bh * (T / Bk) + t / Bk) * D + ch;
@@ -47,7 +49,9 @@ __global__ void dequantize_kernel(kvq_cache c, int which, int64_t t0, int64_t t1
       const int vb = c.cfg.v_bits, tpw = 32 / vb, G = c.cfg.v_group;
       const uint32_t* words = static_cast<const uint32_t*>(c.v_codes) + bh * (T / tpw) * D;
       const uint32_t code = (words[(t / tpw) * D + ch] >> ((t % tpw) * vb)) & ((1u << vb) - 1u);
-      if (c.cfg.v_mode == 1) {
+      if (c.cfg.v_mode == 2) {
+        x = e4m3_to_f32(code);
+      } else if (c.cfg.v_mode == 1) {
         x = h2f(c.v_lut[((int64_t)h * D + ch) * (1 << vb) + code]);
       } else {
         const int64_t m = (bh * T + t) * (D / G) + ch / G;

@@ -16,18 +16,21 @@ kvq_status check_cfg(const kvq_config* c) {
     return KVQ_EINVAL;
   if (c->head_dim % 2 || c->q_heads % c->kv_heads) return KVQ_EINVAL;
   if (c->k_bits < 1 || c->k_bits > 8 || c->v_bits < 1 || c->v_bits > 8) return KVQ_EINVAL;
-  if (c->k_mode != 0 && c->k_mode != 1) return KVQ_EINVAL;
+  if (c->k_mode < 0 || c->k_mode > 2) return KVQ_EINVAL;
   if (c->k_block <= 0 || c->capacity % c->k_block) return KVQ_EINVAL;
   if (c->v_group <= 0 || c->head_dim % c->v_group) return KVQ_EINVAL;
   if (!(c->clip_quantile >= 0.0f && c->clip_quantile < 1.0f)) return KVQ_EINVAL;
   if (c->outlier_pct < 0 || c->outlier_pct > 100) return KVQ_EINVAL;
   if (!(c->rope_theta > 1.0f) || !isfinite(c->rope_theta)) return KVQ_EINVAL;
   if (c->keep_pct < 0 || c->keep_pct > 100) return KVQ_EINVAL;
-  if (c->v_mode != 0 && c->v_mode != 1) return KVQ_EINVAL;
+  if (c->v_mode < 0 || c->v_mode > 2) return KVQ_EINVAL;
+  // FP8: keys and values together, one byte per element
+  if ((c->k_mode == 2) != (c->v_mode == 2)) return KVQ_EINVAL;
+  if (c->k_mode == 2 && (c->k_bits != 8 || c->v_bits != 8)) return KVQ_EINVAL;
   // what the kernels are built for
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_EUNSUPPORTED;
-  if (c->k_bits < 2 || c->k_bits > 4) return KVQ_EUNSUPPORTED;
-  if (c->v_bits != 2 && c->v_bits != 4) return KVQ_EUNSUPPORTED;
+  if (c->k_mode != 2 && (c->k_bits < 2 || c->k_bits > 4)) return KVQ_EUNSUPPORTED;
+  if (c->v_mode != 2 && c->v_bits != 2 && c->v_bits != 4) return KVQ_EUNSUPPORTED;
   if (c->v_group != 16 && c->v_group != 32 && c->v_group != 64 && c->v_group != 128)
     return KVQ_EUNSUPPORTED;
   if (c->k_block != 64 && c->k_block != 128) return KVQ_EUNSUPPORTED;
@@ -37,8 +40,9 @@ kvq_status check_cfg(const kvq_config* c) {
   if (kvq::keep_count(*c) > 16) return KVQ_EUNSUPPORTED;
   if (c->keep_pct > 0 && (c->k_mode != 0 || c->outlier_pct > 0 || c->clip_quantile > 0.0f))
     return KVQ_EUNSUPPORTED;
-  // codebook values: no outliers, no clipping (both belong to the uniform value range)
-  if (c->v_mode == 1 && (c->outlier_pct > 0 || c->clip_quantile > 0.0f)) return KVQ_EUNSUPPORTED;
+  // codebook or FP8 values: no outliers, no clipping (both belong to the uniform range)
+  if (c->v_mode != 0 && (c->outlier_pct > 0 || c->clip_quantile > 0.0f)) return KVQ_EUNSUPPORTED;
+  if (c->k_mode == 2 && c->keep_pct > 0) return KVQ_EUNSUPPORTED;
   return KVQ_OK;
 }
 
@@ -214,7 +218,7 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout* out) {
   if (c.k_mode == 0) {
     out->k_scale = BH * nblk * D * 2;
     out->k_zero = out->k_scale;
-  } else {
+  } else if (c.k_mode == 1) {
     out->k_lut = (size_t)c.kv_heads * D * ((size_t)1 << c.k_bits) * 2;
   }
   out->k_tail = BH * c.k_block * D * 2;
@@ -222,7 +226,7 @@ kvq_status kvq_cache_layout(const kvq_config* cfg, kvq_layout* out) {
   if (c.v_mode == 0) {
     out->v_scale = BH * T * (D / c.v_group) * 2;
     out->v_zero = out->v_scale;
-  } else {
+  } else if (c.v_mode == 1) {
     out->v_lut = (size_t)c.kv_heads * D * ((size_t)1 << c.v_bits) * 2;
   }
   out->v_tail = out->k_tail;

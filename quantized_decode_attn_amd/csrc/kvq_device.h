@@ -108,6 +108,44 @@ __device__ __forceinline__ int kout_of(const kvq_config& c) {
   return c.outlier_pct > 0 ? (c.outlier_pct * c.head_dim + 99) / 100 : 0;
 }
 
+// OCP FP8 E4M3 ("e4m3fn": 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+// S.1111.111 = NaN, largest finite 448), the element format of an FP8 cache ([UQ]
+// section 2.1).  fp16 -> E4M3 rounds to nearest, ties to even, in integer arithmetic on
+// the fp16 fields: the significand (1024 + m, or m for a subnormal) is shifted right to
+// the E4M3 unit of the value's binade (2^(E-3), at least 2^-9); magnitudes past 448
+// (infinities included) saturate to +-448, NaN stays NaN.
+__host__ __device__ __forceinline__ uint32_t f16_to_e4m3(uint32_t h) {
+  const uint32_t sign = (h >> 8) & 0x80u;
+  const uint32_t mag = h & 0x7FFFu;
+  if (mag > 0x7C00u) return sign | 0x7Fu;
+  if (mag == 0x7C00u) return sign | 0x7Eu;
+  const int e16 = (int)(mag >> 10);
+  const uint32_t sig = e16 ? (0x400u | (mag & 0x3FFu)) : (mag & 0x3FFu);  // value = sig 2^(max(e16,1)-25)
+  int ex = (e16 ? e16 : 1) - 15;                                          // binade of a normal fp16
+  if (ex < -6) ex = -6;
+  const int sh = ex + 22 - (e16 ? e16 : 1);                               // >= 7
+  uint32_t q = 0u;
+  if (sh < 32) {
+    const uint32_t keep = sig >> sh, rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    q = keep + ((rem > half || (rem == half && (keep & 1u))) ? 1u : 0u);
+  }
+  if (q >= 16u) {  // rounded up into the next binade
+    q >>= 1;
+    ex += 1;
+  }
+  if (ex > 8 || (ex == 8 && q > 14u)) return sign | 0x7Eu;  // above 448
+  if (ex == -6 && q < 8u) return sign | q;                   // subnormal (or zero)
+  return sign | ((uint32_t)(ex + 7) << 3) | (q - 8u);
+}
+__host__ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v;
+  if (e == 0u) v = (float)m * 0x1p-9f;
+  else v = __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20));  // 2^(e-7) (1 + m/8)
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  return (b & 0x80u) ? -v : v;
+}
+
 // Tokens of sequence b: its own length in a paged cache (clamped into [0, capacity]),
 // else the cache's one length.
 __device__ __forceinline__ int64_t seq_len_of(const kvq_cache& c, int64_t b) {

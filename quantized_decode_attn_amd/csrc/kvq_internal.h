@@ -39,6 +39,10 @@ hipError_t launch_quantize_keys_lut(const kvq_cache& c, const uint16_t* k_new, i
                                     int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s);
 hipError_t launch_quantize_values(const kvq_cache& c, const uint16_t* v_new, int64_t old_len, int64_t n_new,
                                   int64_t n_first, int64_t nblocks, const int64_t* n_seq, hipStream_t s);
+// FP8 cache (k_mode 2 with v_mode 2): both tensors of each completed block in one kernel.
+hipError_t launch_quantize_fp8(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new, int64_t old_len,
+                               int64_t n_new, int64_t n_first, int64_t nblocks, const int64_t* n_seq,
+                               hipStream_t s);
 
 // Copy new rows [src0, n_new) into tail slots [dst0, ...) (a paged cache: per
 // sequence, from its own length).

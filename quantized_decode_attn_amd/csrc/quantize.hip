@@ -91,6 +91,7 @@ hipError_t launch_quantize(const kvq_cache& c, const uint16_t* k_new, const uint
                            int64_t old_len, int64_t n_new, int64_t n_first, int64_t nblocks,
                            hipStream_t s, const int64_t* n_seq) {
   if (nblocks <= 0 || nblocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (c.cfg.k_mode == 2) return launch_quantize_fp8(c, k_new, v_new, old_len, n_new, n_first, nblocks, n_seq, s);
   hipError_t e = c.cfg.k_mode == 1
                      ? launch_quantize_keys_lut(c, k_new, old_len, n_new, n_first, nblocks, n_seq, s)
                      : launch_quantize_keys_uniform(c, k_new, old_len, n_new, n_first, nblocks, n_seq, s);

@@ -44,10 +44,11 @@ VARIANTS = {
     "c1_keep5": dict(keep_pct=5),
     "c3_vlut": dict(v_mode=1),
     "c0_vlut2": dict(v_mode=1, v_bits=2, v_group=32),
+    "c1_fp8": dict(k_mode=2, k_bits=8, v_mode=2, v_bits=8),
 }
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4", "c1_keep5", "c3_vlut", "c0_vlut2"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4", "c1_keep5", "c3_vlut", "c0_vlut2", "c1_fp8"])
 def test_layout_matches_oracle_layout(L, orc, name):
     cfg = synth.config(name[:2], **VARIANTS.get(name, {}))
     lay = kvq.kvq_cache_layout(kvq.make_config(cfg))
@@ -74,8 +75,9 @@ def L_layout(c):
     ("v_group", 48, kvq.KVQ_EINVAL), ("v_group", 8, kvq.KVQ_EUNSUPPORTED), ("k_block", 100, kvq.KVQ_EINVAL),
     ("k_block", 32, kvq.KVQ_EUNSUPPORTED), ("q_heads", 6, kvq.KVQ_EINVAL), ("clip_quantile", 1.0, kvq.KVQ_EINVAL),
     ("clip_quantile", -0.1, kvq.KVQ_EINVAL), ("outlier_pct", 101, kvq.KVQ_EINVAL), ("outlier_pct", 4, kvq.KVQ_EUNSUPPORTED),
-    ("rope_theta", 0.5, kvq.KVQ_EINVAL), ("k_mode", 2, kvq.KVQ_EINVAL), ("capacity", 0, kvq.KVQ_EINVAL),
-    ("v_mode", 2, kvq.KVQ_EINVAL), ("v_mode", -1, kvq.KVQ_EINVAL),
+    ("rope_theta", 0.5, kvq.KVQ_EINVAL), ("k_mode", 3, kvq.KVQ_EINVAL), ("capacity", 0, kvq.KVQ_EINVAL),
+    ("v_mode", 3, kvq.KVQ_EINVAL), ("v_mode", -1, kvq.KVQ_EINVAL),
+    ("k_mode", 2, kvq.KVQ_EINVAL), ("v_mode", 2, kvq.KVQ_EINVAL),              # FP8 needs both, 8 bits
 ])
 def test_layout_rejects(L, field, value, want):
     cfg = synth.config("c1", q_heads=32, kv_heads=8)
