@@ -354,6 +354,7 @@ def main():
     ap.add_argument("--paged", action="store_true", help="also time a paged cache with mixed sequence lengths")
     ap.add_argument("--keep-pct", type=int, default=0,
                     help="the workload with this percentage of each block's keys kept in fp16 by norm")
+    ap.add_argument("--fp8", action="store_true", help="the workload as an FP8 (E4M3) cache")
     ap.add_argument("--v-codebook", choices=["none", "kmeans", "log"], default="none",
                     help="the workload with values quantized by a per-channel codebook (calibrated or log-spaced)")
     args = ap.parse_args()
@@ -373,6 +374,9 @@ def main():
     if args.v_codebook != "none":
         cfg["v_mode"] = 1
         cfg["workload"] += "-v%s" % args.v_codebook
+    if args.fp8:
+        cfg.update(k_mode=2, k_bits=8, v_mode=2, v_bits=8, outlier_pct=0, clip_quantile=0.0, inject=False)
+        cfg["workload"] += "-fp8"
     T, B, H, Hq, D = cfg["tokens"], cfg["batch"], cfg["kv_heads"], cfg["q_heads"], cfg["head_dim"]
     existing = cfg["existing"]
     log("workload", args.workload, cfg["workload"])
@@ -381,7 +385,7 @@ def main():
     v = synth.gen_tensor(cfg, synth.TENSOR_V)
     q = synth.gen_q(cfg)
     lut = synth.calib_lut(cfg) if cfg["k_mode"] == 1 else None
-    vlut = None
+    vlut = None  # (an FP8 cache has no codebook)
     if args.v_codebook != "none":
         vlut = synth.calib_log_vlut(cfg) if args.v_codebook == "log" else synth.calib_vlut(cfg)
     log("inputs drawn in %.1f s" % (time.time() - t0))

@@ -58,6 +58,10 @@ typedef int32_t kvq_status;
  *             block of k_block tokens ([KVC3] "Per-Channel Key Quantization").
  *   k_mode 1: per-channel non-uniform codebook of 2^k_bits sorted fp16 entries,
  *             supplied by the caller ([KVC3] "Non-Uniform KV Cache Quantization").
+ *   k_mode 2: FP8 cache ([UQ] section 2.1): every key element cast to OCP E4M3 (4
+ *             exponent bits, bias 7, 3 mantissa bits, largest finite 448), nearest with
+ *             ties to even, saturating at +-448; requires v_mode 2 and k_bits = v_bits
+ *             = 8.  The byte is the code; no metadata.
  * Values:
  *   v_mode 0: uniform asymmetric per token over groups of v_group channels, one fp16
  *             scale and zero-point per group ([KVC3] "Quanto 的量化原理").
@@ -67,6 +71,7 @@ typedef int32_t kvq_status;
  *             Quantization"); a codebook of log-spaced levels is the log quantization of
  *             [TQ] section 3.3.  The code is the nearest entry, decided at the fp32
  *             midpoints, ties to the lower code (as for codebook keys).
+ *   v_mode 2: FP8 values, cast to E4M3 like the keys of k_mode 2 (the two go together).
  * clip_quantile q > 0: before the statistics, every dense value of a block is
  *   clipped to [-t, t], t = the q-quantile of |x| over that block's k_block x
  *   head_dim elements of the same tensor (exact order statistics, linear
@@ -89,7 +94,8 @@ typedef int32_t kvq_status;
  * kv_heads with q_heads/kv_heads <= 8; clip_quantile in [0, 1); outlier_pct in
  * [0, 100] with ceil(p*head_dim/100) <= 4; rope_theta > 1; keep_pct in [0, 100] with
  * R <= 16, and only with uniform keys (k_mode 0), no outliers and no clipping; v_mode in
- * {0, 1}, 1 only without outliers and clipping.
+ * {0, 1, 2}, 1 and 2 only without outliers and clipping; the FP8 cache (k_mode 2, v_mode
+ * 2, 8 bits) without kept keys.
  */
 typedef struct {
   int32_t batch, q_heads, kv_heads, head_dim, capacity;
