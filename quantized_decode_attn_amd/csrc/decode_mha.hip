@@ -113,8 +113,8 @@ __device__ __forceinline__ void load_eb(BlockRegs<D, BK, KB, VB>& R, const kvq_c
 }
 
 // Block weights of the block whose metadata R holds, one rotary pair per lane, into the
-// wave's LDS area: codebook keys WR WI; uniform keys A1 B1 Z1 A2 B2 Z2, then WR WI ZA ZB
-// with outliers, WR WI with kept fp16 keys (W = query weight rotated by the block's
+// wave's LDS area: codebook keys WR WI; uniform keys A1 B1 Z1 A2 B2 Z2, then (WR, WI, ZA,
+// ZB) per pair with outliers, WR WI with kept fp16 keys (W = query weight rotated by the block's
 // first position, folded with scale and zero).
 template <int D, int BK, int KB, int VB, int KO, bool LUT, bool KEEP = false>
 __device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, VB>& R, float* wb, float wq_r,
@@ -138,13 +138,12 @@ __device__ __forceinline__ void write_block_weights(const BlockRegs<D, BK, KB, V
     wb[3 * HALF + lane] = -wi * al * ua;           // A2
     wb[4 * HALF + lane] = -wr * be * ub;           // B2
     wb[5 * HALF + lane] = -(wi * za + wr * zb);    // Z2
-    if constexpr (KO > 0 || KEEP) {
+    if constexpr (KO > 0) {
+      // (WR, WI, ZA, ZB) of the pair side by side: one read per outlier correction
+      *reinterpret_cast<float4*>(wb + 6 * HALF + 4 * lane) = make_float4(wr, wi, za, zb);
+    } else if constexpr (KEEP) {
       wb[6 * HALF + lane] = wr;                    // WR
       wb[7 * HALF + lane] = wi;                    // WI
-    }
-    if constexpr (KO > 0) {
-      wb[8 * HALF + lane] = za;                    // ZA
-      wb[9 * HALF + lane] = zb;                    // ZB
     }
   }
 }
@@ -171,10 +170,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   float* wA2 = wZ1 + Sh::HALF;
   float* wB2 = wA2 + Sh::HALF;
   float* wZ2 = wB2 + Sh::HALF;
-  float* wWR = wZ2 + Sh::HALF;
-  float* wWI = wWR + Sh::HALF;
-  float* wZA = wWI + Sh::HALF;
-  float* wZB = wZA + Sh::HALF;
+  const float* wOut = wZ2 + Sh::HALF;  // outliers: (WR, WI, ZA, ZB) per pair
   float* Sc = wl + L.s;
   float* PS = wl + L.ps;
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);
@@ -383,9 +379,10 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
         const float val = h2f((uint16_t)(C.kv[k] >> (16 * q)));
         const int i = col % Sh::HALF;
         const bool a = col < Sh::HALF;
-        const float dl = val - (a ? wZA[i] : wZB[i]);
+        const float4 w4 = *reinterpret_cast<const float4*>(wOut + 4 * i);
+        const float dl = val - (a ? w4.z : w4.w);
         const float2 cssn = *reinterpret_cast<const float2*>(table + t * Sh::TPITCH + Sh::tab_off(i));
-        const float wr = wWR[i], wi = wWI[i];
+        const float wr = w4.x, wi = w4.y;
         p[k] += a ? dl * (wr * cssn.x - wi * cssn.y) : -dl * (wi * cssn.x + wr * cssn.y);
       }
     }
