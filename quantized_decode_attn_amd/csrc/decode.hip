@@ -56,6 +56,8 @@ struct Shape {
   static constexpr int NW = 12;                       // floats of per-pair weights
 };
 
+typedef float f2v __attribute__((ext_vector_type(2)));
+
 struct WaveLds {  // offsets (in floats) of one wave's scratch area
   int wts, wq, p, ps, vs, vz, state, vc, lut, vlut, total;
 };
@@ -300,10 +302,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
                   X = __builtin_fmaf(B1[m], (float)cb, __builtin_fmaf(A1[m], (float)ca, Z1[m]));
                   Y = __builtin_fmaf(B2[m], (float)cb, __builtin_fmaf(A2[m], (float)ca, Z2[m]));
                 } else {
-                  // codebook keys: the channel's entries; FP8 keys: the E4M3 values
+                  // codebook keys: the channel's entries; FP8 keys: the pair's two bytes
+                  // (adjacent in the row) converted together, the hardware conversion
+                  // reading OCP E4M3
                   const int ch = r * Sh::PPL + m;
-                  const float a = KMODE == 2 ? e4m3_to_f32(ca) : lutl[ch * (1 << KB) + ca];
-                  const float bb = KMODE == 2 ? e4m3_to_f32(cb) : lutl[(ch + Sh::HALF) * (1 << KB) + cb];
+                  float a, bb;
+                  if constexpr (KMODE == 2) {
+                    const f2v ab = (m & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w[m >> 1], true)
+                                           : __builtin_amdgcn_cvt_pk_f32_fp8(w[m >> 1], false);
+                    a = ab.x;
+                    bb = ab.y;
+                  } else {
+                    a = lutl[ch * (1 << KB) + ca];
+                    bb = lutl[(ch + Sh::HALF) * (1 << KB) + cb];
+                  }
                   X = __builtin_fmaf(WR[m], a, -WI[m] * bb);
                   Y = -__builtin_fmaf(WI[m], a, WR[m] * bb);
                 }
@@ -369,15 +381,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(kvq_cache c,
 #pragma unroll
         for (int k = 0; k < Sh::CPL; ++k) acc[k] = st[2 + lane + k * kWave] * alpha;
         if (!tail && vf8) {
-          // FP8 values: each code is an E4M3 value
+          // FP8 values (8-bit value words only): each code is an E4M3 value
+          if constexpr (VB == 8)
           for (int gw = 0; gw < Bk / Sh::TPW; ++gw) {
 #pragma unroll
             for (int k = 0; k < Sh::CPL; ++k) {
-              const uint32_t word = vblk[gw * D + lane + k * kWave];
+              const uint32_t word = vblk[gw * D + lane + k * kWave];  // 4 tokens' bytes
+              const f2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+              const f2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+              const float vv[4] = {v01.x, v01.y, v23.x, v23.y};
 #pragma unroll
-              for (int u = 0; u < Sh::TPW; ++u)
-                acc[k] = __builtin_fmaf(Pl[gw * Sh::TPW + u], e4m3_to_f32((word >> (u * VB)) & ((1u << VB) - 1u)),
-                                        acc[k]);
+              for (int u = 0; u < 4; ++u) acc[k] = __builtin_fmaf(Pl[gw * 4 + u], vv[u], acc[k]);
             }
           }
           if (lane == 0)

@@ -151,3 +151,23 @@ def test_fp8_cache_in_fused_steps():
     assert worst <= TOL
     for (b, h), hc in _heads(cfg, k, v).items():
         compare_head(cache, hc, cfg, 0, b, h)
+
+
+def test_fp8_nonfinite_inputs_cast_like_the_oracle():
+    """NaN inputs stay NaN (S.1111.111, the cast's rare slow path) and infinities
+    saturate to +-448, in keys and values: the bytes equal the oracle's and so do the
+    dequantized bits."""
+    import oracle
+    cfg = synth.config("c0", tokens=3 * 64 + 5, capacity=256, **FP8)
+    k, v = inputs(cfg)
+    k = k.copy(); v = v.copy()
+    k[0, 0, 3, 5] = 0x7E00; k[0, 1, 70, 0] = 0xFE01; k[0, 2, 130, 63] = 0x7C00; k[0, 3, 10, 9] = 0xFC00
+    v[0, 0, 64, 1] = 0x7C00; v[0, 1, 65, 2] = 0xFE00; v[0, 3, 150, 40] = 0xFC00; v[0, 2, 5, 6] = 0x7E10
+    cache = build_gpu_cache(cfg, k, v, [100, 97])
+    heads = _heads(cfg, k, v)
+    for (b, h), hc in heads.items():
+        compare_head(cache, hc, cfg, 0, b, h)
+    for which in (0, 1):
+        g = cache.dequantize(which).cpu().numpy()
+        for (b, h), hc in heads.items():
+            assert np.array_equal(g[b, h].view(np.uint32), hc.dequantize(which).view(np.uint32)), (which, b, h)
