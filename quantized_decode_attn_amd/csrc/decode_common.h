@@ -11,6 +11,45 @@ namespace dcm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Work items of a cache with per-sequence lengths: every item of sequence b costs about
+// len_b / S blocks.  The host sorts the sequences by their host lengths, longest first,
+// and the waves take the items in that order in a snake: wave p takes item
+// r * nw + p in even rounds r and r * nw + nw - 1 - p in odd ones, so that a wave with a
+// long item in one round gets a short one in the next.  n == 0: natural order.
+constexpr int kOrderMax = 1024;
+struct SeqOrder {
+  int32_t n;
+  uint16_t b[kOrderMax];
+};
+inline SeqOrder seq_order(const kvq_cache& c) {
+  SeqOrder o;
+  o.n = 0;
+  const int B = c.cfg.batch;
+  if (!c.seq_lens_host || B > kOrderMax) return o;
+  for (int b = 0; b < B; ++b) o.b[b] = (uint16_t)b;
+  // insertion sort, longest first, ties in sequence order (B is small)
+  for (int i = 1; i < B; ++i) {
+    const uint16_t x = o.b[i];
+    const int64_t lx = c.seq_lens_host[x];
+    int j = i - 1;
+    while (j >= 0 && c.seq_lens_host[o.b[j]] < lx) {
+      o.b[j + 1] = o.b[j];
+      --j;
+    }
+    o.b[j + 1] = x;
+  }
+  o.n = B;
+  return o;
+}
+__device__ __forceinline__ int64_t snake_item(int64_t r, int64_t p, int64_t nw) {
+  return r * nw + ((r & 1) ? nw - 1 - p : p);
+}
+// The natural index of the k-th item in length order (per_seq items per sequence).
+__device__ __forceinline__ int64_t ordered_item(const SeqOrder& ord, int64_t k, int64_t per_seq) {
+  const int64_t qs = k / per_seq, rest = k - qs * per_seq;
+  return (ord.n ? (int64_t)ord.b[qs] : qs) * per_seq + rest;
+}
+
 template <int D, int BK, int KB, int VB, int PPL_ = 8>
 struct MShape {
   static constexpr int HALF = D / 2;

@@ -495,7 +495,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 template <int VB, int GW, int KO, int NG, bool PG>
 __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
-                                                                   int64_t nitems) {
+                                                                   int64_t nitems, const SeqOrder ord) {
   constexpr int kNT = kGqaWaves * 64;
   constexpr bool OUTL = KO > 0;
   extern __shared__ float lds[];
@@ -516,7 +516,14 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
   __syncthreads();
 
   const int64_t total_waves = (int64_t)gridDim.x * kGqaWaves;
-  for (int64_t item = (int64_t)blockIdx.x * kGqaWaves + wave; item < nitems; item += total_waves) {
+  const int64_t p = (int64_t)blockIdx.x * kGqaWaves + wave;
+  const int64_t per_seq = (int64_t)H * nsets * S;
+  // per-sequence lengths: items in length order, dealt in a snake (every wave exits once
+  // k passes nitems); dense: item p, p + total_waves, ...
+  for (int64_t r = 0;; ++r) {
+    const int64_t k = PG ? snake_item(r, p, total_waves) : p + r * total_waves;
+    if (k >= nitems) break;
+    const int64_t item = PG ? ordered_item(ord, k, per_seq) : k;
     const int split = (int)(item % S);
     const int64_t rest = item / S;
     const int set = (int)(rest % nsets);
@@ -630,7 +637,7 @@ hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos
   int64_t grid = (nitems + kGqaWaves - 1) / kGqaWaves;
   if (grid > cus) grid = cus;
   hipLaunchKernelGGL((decode_gqa_kernel<VB, GW, KO, NG, PG>), dim3((unsigned)grid), dim3(kGqaWaves * 64), bytes, s, c, q,
-                     q_pos, ws, S, nitems);
+                     q_pos, ws, S, nitems, PG ? seq_order(c) : SeqOrder{0, {}});
   return hipGetLastError();
 }
 

@@ -739,7 +739,7 @@ __device__ __forceinline__ void stage_rope(float* table, const kvq_cache& c) {
 template <int D, int BK, int KB, int VB, int KO, bool PG, bool KEEP = false, bool VCB = false>
 __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c, const uint16_t* __restrict__ q,
                                                                    int64_t q_pos, float* __restrict__ ws, int S,
-                                                                   int64_t nitems) {
+                                                                   int64_t nitems, const SeqOrder ord) {
   using Sh = MShape<D, BK, KB, VB>;
   constexpr int kNT = kMhaWaves * 64;
   constexpr bool OUTL = KO > 0;
@@ -756,9 +756,21 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
   __syncthreads();
 
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
-  for (int64_t item = (int64_t)blockIdx.x * kMhaWaves + wave; item < nitems; item += total_waves)
-    mha_item<D, BK, KB, VB, KO, false, PG, KEEP, VCB>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table,
-                                                      nullptr, lane);
+  const int64_t p = (int64_t)blockIdx.x * kMhaWaves + wave;
+  if constexpr (PG) {  // items in length order, dealt in a snake (every wave exits once k passes nitems)
+    const int64_t per_seq = (int64_t)c.cfg.kv_heads * S;
+    for (int64_t r = 0;; ++r) {
+      const int64_t k = snake_item(r, p, total_waves);
+      if (k >= nitems) break;
+      const int64_t item = ordered_item(ord, k, per_seq);
+      mha_item<D, BK, KB, VB, KO, false, PG, KEEP, VCB>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table,
+                                                        nullptr, lane);
+    }
+  } else {
+    for (int64_t item = p; item < nitems; item += total_waves)
+      mha_item<D, BK, KB, VB, KO, false, PG, KEEP, VCB>(c, q, q_pos, ws, S, item / S, (int)(item % S), wl, L, table,
+                                                        nullptr, lane);
+  }
 }
 
 // Codebook keys: the workgroup takes groups of up to 8 splits of one (b, head), so
@@ -822,7 +834,7 @@ static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_
   int64_t grid = (nitems + kMhaWaves - 1) / kMhaWaves;
   if (grid > cus) grid = cus;
   hipLaunchKernelGGL((decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP, VCB>), dim3((unsigned)grid), dim3(kMhaWaves * 64), bytes, s, c,
-                     q, q_pos, ws, S, nitems);
+                     q, q_pos, ws, S, nitems, PG ? seq_order(c) : SeqOrder{0, {}});
   return hipGetLastError();
 }
 
