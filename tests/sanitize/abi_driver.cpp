@@ -72,6 +72,7 @@ static kvq_cache fake_cache(const kvq_config& c, int64_t length) {
   k.v_rowptr = (int32_t*)p(lay.v_rowptr); k.v_col = (uint8_t*)p(lay.v_col); k.v_val = (uint16_t*)p(lay.v_val);
   k.rope = (float*)p(lay.rope);
   k.k_keep_idx = (uint8_t*)p(lay.k_keep_idx); k.k_keep_val = (uint16_t*)p(lay.k_keep_val);
+  k.v_lut = (const uint16_t*)p(lay.v_lut);
   return k;
 }
 
@@ -128,6 +129,32 @@ int main() {
     EXPECT(kvq_cache_init(&kk, nullptr) == KVQ_EHIP);
     kk.k_keep_val = nullptr;
     EXPECT(kvq_cache_init(&kk, nullptr) == KVQ_EINVAL);
+  }
+  {  // codebook values and the FP8 cache: sizes, the combinations refused, the buffers required
+    kvq_config c = base();
+    c.v_mode = 1;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EUNSUPPORTED);  // with outliers and clipping
+    c.outlier_pct = 0; c.clip_quantile = 0.0f;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_OK);
+    EXPECT(lay.v_scale == 0 && lay.v_zero == 0 && lay.v_lut == (size_t)2 * 128 * 16 * 2);
+    kvq_cache kv = fake_cache(c, 0);
+    EXPECT(kvq_cache_init(&kv, nullptr) == KVQ_EHIP);
+    kv.v_lut = nullptr;
+    EXPECT(kvq_cache_init(&kv, nullptr) == KVQ_EINVAL);
+    c.v_mode = 3;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EINVAL);
+    c.v_mode = 2;  // FP8 values need FP8 keys, 8 bits each
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EINVAL);
+    c.k_mode = 2;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EINVAL);
+    c.k_bits = 8; c.v_bits = 8;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_OK);
+    EXPECT(lay.k_codes == (size_t)2 * 2 * 1024 * 128 && lay.v_codes == lay.k_codes);
+    EXPECT(lay.k_scale == 0 && lay.k_lut == 0 && lay.v_scale == 0 && lay.v_lut == 0);
+    kvq_cache kf = fake_cache(c, 0);
+    EXPECT(kvq_cache_init(&kf, nullptr) == KVQ_EHIP);
+    c.keep_pct = 5;
+    EXPECT(kvq_cache_layout(&c, &lay) == KVQ_EUNSUPPORTED);
   }
   EXPECT(kvq_cache_layout(nullptr, nullptr) == KVQ_EINVAL);
 
