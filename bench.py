@@ -95,6 +95,17 @@ def append_bytes_per_token_head(cfg) -> float:
     return 2 * D * 2 + decode_bytes_per_token_head(cfg) - 2 * ko * 3 + csr
 
 
+def dtype_of(cfg) -> str:
+    """The arithmetic the decode computes in, for the JSON line."""
+    if cfg.get("v_mode", 0) == 2:
+        return "f32 scores/softmax over E4M3 keys and values (exact conversions); fp32 accumulation"
+    if cfg.get("v_mode", 0) == 1:
+        return "f32 scores/softmax; fp16 codebook values times f32 probabilities; fp32 accumulation"
+    w = "30-bit digit" if cfg["q_heads"] > cfg["kv_heads"] else "24-bit"
+    return ("f32 scores/softmax; value weights as %s fixed point x u%d codes, exact integer sums; "
+            "fp32 accumulation" % (w, cfg["v_bits"]))
+
+
 def source_hash(names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -484,8 +495,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("f32 scores/softmax; value weights as %s fixed point x u%d codes, exact integer "
-                  "sums; fp32 accumulation" % ("30-bit digit" if Hq > H else "32-bit", cfg["v_bits"])),
+        "dtype": dtype_of(cfg),
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": cfg["workload"], "batch": B, "q_heads": Hq, "kv_heads": H,
                    "head_dim": D, "tokens": T, "appended_per_step": n_new, "k_bits": cfg["k_bits"],

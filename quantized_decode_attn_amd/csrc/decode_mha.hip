@@ -28,9 +28,10 @@
 //    and the value weights;
 //  * values are stored as words of consecutive tokens of one channel, so a 16-byte
 //    load gives each lane 4 channels x (32 / v_bits) tokens; the per-token weights
-//    p*scale are quantized per block to 32-bit fixed point and split into eight
+//    p*scale are quantized per block to 24-bit fixed point and split into six
 //    nibble planes, and the value update is v_dot8_u32_u4 on the packed codes
-//    (no unpacking, 8 codes per instruction and plane).
+//    (no unpacking, 8 codes per instruction and plane); codebook values instead add
+//    p * entry per code from an LDS copy of the head's codebook.
 // The pages' fusion advice ([TQ] sections 5.1 and 6.3) is the design: no dequantized
 // value is ever written to memory.
 #include <math.h>
