@@ -85,6 +85,18 @@ SMALL = {
     # one head per kv head with one outlier per vector (head_dim 64: ceil(0.64) = 1)
     "mha_csr1_d64": (synth.config("c0", batch=2, outlier_pct=1, inject=True, tokens=5 * 64 + 30,
                                   capacity=384), [64, 286]),
+    # the clip at the ends of its candidate path on a 128 x 128 tile: between the two
+    # largest magnitudes (rank 1 from the top, the highest quantile below 1), the deepest
+    # rank the candidate lists serve (255), and one rank deeper (256: the whole-tile
+    # selection)
+    "clip_rank1": (synth.config("c4", batch=1, q_heads=2, kv_heads=2, tokens=2 * 128 + 57, capacity=384,
+                                existing=0, clip_quantile=(16383 - 1 + 0.5) / 16383), [128, 185]),
+    "clip_rank255": (synth.config("c4", batch=1, q_heads=2, kv_heads=2, tokens=2 * 128 + 57,
+                                  capacity=384, existing=0, clip_quantile=(16383 - 255 + 0.5) / 16383),
+                     [128, 185]),
+    "clip_rank256": (synth.config("c4", batch=1, q_heads=2, kv_heads=2, tokens=2 * 128 + 57,
+                                  capacity=384, existing=0, clip_quantile=(16383 - 256 + 0.5) / 16383),
+                     [128, 185]),
 }
 
 
