@@ -41,6 +41,12 @@ namespace {
 using namespace dcm;
 
 constexpr int kGqaWaves = 8;
+
+// Blocks each wave of the workgroup has started (waves w and w + 4 share a SIMD).  As in
+// the one-head kernel, the wave that has started fewer blocks than its SIMD partner runs
+// one priority level higher, which keeps the older wave from finishing first and
+// leaving the younger one alone on the SIMD.
+__shared__ int gqa_progress[kGqaWaves];
 constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;  // floats per rotary-table row: 64 (cos, sin) pairs + 4 (banks)
 constexpr int kWAP = 2 * kHalf + 4;  // floats per head of the query weights (distinct banks per head)
@@ -185,8 +191,18 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   uint32_t* W32 = reinterpret_cast<uint32_t*>(wl + L.w32);  // [group][head][half][lane]
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
   const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
+  bool behind;  // wave-uniform: this wave has started fewer blocks than its SIMD partner
+  {
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (lane == 0) __hip_atomic_fetch_add(&gqa_progress[wv], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int mine = __hip_atomic_load(&gqa_progress[wv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int theirs =
+        __hip_atomic_load(&gqa_progress[wv ^ (kGqaWaves / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    behind = __builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0) != 0;
+  }
 
-  __builtin_amdgcn_s_setprio(0);
+  if (behind) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
   // value scale/zero and outlier entries of this block: needed only after the scores,
   // so they are loaded here rather than a block ahead.  Loads still in flight at the
   // block's end would be drained there (the counter is in order, so waiting for them
@@ -300,7 +316,8 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
 
   // the block's serial part (softmax, value weights, value MFMAs, outliers) runs at a
   // raised wave priority, the score loop at the base one
-  __builtin_amdgcn_s_setprio(1);
+  if (behind) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(1);
 
   // ---- online softmax per head; lane owns tokens lane and 64 + lane
   float p[2][4];
@@ -513,6 +530,7 @@ __global__ __launch_bounds__(kGqaWaves * 64) void decode_gqa_kernel(kvq_cache c,
   float* wl = lds + kBK * kTP + wave * L.total;
   if (OUTL)
     for (int k = lane; k < 4 * kD + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
+  if (threadIdx.x < kGqaWaves) gqa_progress[threadIdx.x] = 0;
   __syncthreads();
 
   const int64_t total_waves = (int64_t)gridDim.x * kGqaWaves;

@@ -44,6 +44,15 @@ namespace {
 using namespace dcm;
 
 constexpr int kMhaWaves = 8;  // two waves per SIMD
+
+// Blocks each wave of the workgroup has started.  Waves w and w + 4 share a SIMD, and
+// when both are ready the older one wins the issue slot: left alone, waves 0-3 finish
+// their items about 1.4 times sooner than waves 4-7, and the later waves then run
+// without a partner to hide their latency.  A wave that has started fewer blocks than
+// its partner runs one priority level higher until it has caught up, so both stream
+// to the end together.  (The counts steer the issue order only: every wave still
+// computes exactly its own blocks.)
+__shared__ int mha_progress[kMhaWaves];
 constexpr float kW24Span = 16776960.0f;  // 2^24 - 2^8: full scale of the fixed-point value weights
 
 // Per-wave LDS area, in floats.
@@ -160,6 +169,15 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   constexpr bool OUTL = KO > 0;
   static_assert(!(LUT && OUTL), "codebook keys with outliers take the generic kernel");
   constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
+  bool behind;  // wave-uniform: this wave has started fewer blocks than its SIMD partner
+  {
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (lane == 0) __hip_atomic_fetch_add(&mha_progress[wv], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int mine = __hip_atomic_load(&mha_progress[wv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int theirs =
+        __hip_atomic_load(&mha_progress[wv ^ (kMhaWaves / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    behind = __builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0) != 0;
+  }
   const int64_t nn = more ? n + nstep : n;
   const int64_t g = slot_at<PG>(sr, n), gnn = more ? slot_at<PG>(sr, nn) : g;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, gnn);
@@ -232,7 +250,8 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
     }
   }
 
-  __builtin_amdgcn_s_setprio(0);
+  if (behind) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
   // ---- scores, summed over a token's lanes and written to LDS by its first lane
   // rotary-table rows in registers one iteration ahead, so the LDS latency of the
   // next token's cos/sin overlaps this token's arithmetic
@@ -361,7 +380,8 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   // the block's serial part (softmax, value weights, planes, value dot products) runs at
   // a raised wave priority, so that its short dependency chains win issue slots over the
   // other wave's score loop; the priority drops back at the next block's score loop
-  __builtin_amdgcn_s_setprio(1);
+  if (behind) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(1);
 
   // ---- online softmax in base 2; lane owns tokens lane + 64 k
   float p[TPL];
@@ -754,6 +774,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_kernel(kvq_cache c,
   float* wl = lds + BK * Sh::TPITCH + wave * L.total;
   if (OUTL)
     for (int k = lane; k < D + 4; k += kWave) reinterpret_cast<int*>(wl + L.vcorr)[k] = 0;
+  if (threadIdx.x < kMhaWaves) mha_progress[threadIdx.x] = 0;
   __syncthreads();
 
   const int64_t total_waves = (int64_t)gridDim.x * kMhaWaves;
@@ -797,6 +818,7 @@ __global__ __launch_bounds__(kMhaWaves * 64) void decode_mha_lut_kernel(kvq_cach
   float* wl = reinterpret_cast<float*>(ptab + Sh::HALF * PT::PITCH) + wave * L.total;
 
   const int gps = (S + kMhaWaves - 1) / kMhaWaves;  // groups per (b, head)
+  if (threadIdx.x < kMhaWaves) mha_progress[threadIdx.x] = 0;  // published by the loop's first barrier
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
     const int64_t bh = g / gps;
     const int split = (int)(g % gps) * kMhaWaves + wave;
