@@ -70,6 +70,12 @@ using namespace dcm;
 // and registers do not fit eight
 template <int KO>
 constexpr int cw_of() { return KO ? 4 : 8; }
+
+// Blocks each wave of an 8-wave workgroup has started (waves w and w + 4 share a SIMD):
+// the wave behind its partner runs at a raised priority, so that the older wave of a
+// SIMD does not finish its split long before the younger one (the next unit's barrier
+// would wait for it).
+__shared__ int chunk_progress[8];
 constexpr int kD = 128, kBK = 128, kHalf = 64;
 constexpr int kTP = kD + 4;                 // floats per rotary-table row
 constexpr int kRows = 16;                   // rows per tile
@@ -621,6 +627,7 @@ __global__ __launch_bounds__(cw_of<KO>() * 64) void chunk_mfma_kernel(kvq_cache 
   }
 
   const int nsg = (S + kCW - 1) / kCW;  // split groups per unit
+  if (threadIdx.x < 8) chunk_progress[threadIdx.x] = 0;  // published by the loop's first barrier
   for (int64_t work = blockIdx.x; work < nwork; work += gridDim.x) {
     const int sg = (int)(work % nsg);
     const int64_t unit = work / nsg;
@@ -688,6 +695,13 @@ __global__ __launch_bounds__(cw_of<KO>() * 64) void chunk_mfma_kernel(kvq_cache 
           for (int hh = 0; hh < 2; ++hh) cload_v<VB>(Rg, kp, hh, rsr, sp, lane);
       }
       for (int64_t n = sp; n < nlimit; n += S) {
+        if constexpr (kCW == 8) {
+          if (lane == 0) __hip_atomic_fetch_add(&chunk_progress[wave], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          const int mine = __hip_atomic_load(&chunk_progress[wave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          const int theirs = __hip_atomic_load(&chunk_progress[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (__builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0)) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
+        }
         const bool more = n + S < nlimit;
         const bool masked = (n + 1) * kBK > vmin;
         chunk_block<VB, NG, KO>(Rg, rsr, st, wl, L, table, wq, eq, lane, c, bh, n, more ? n + S : n, more, vis_row,
