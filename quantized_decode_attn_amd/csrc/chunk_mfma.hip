@@ -746,7 +746,7 @@ hipError_t launch_typed(const kvq_cache& c, const uint16_t* q, RowSpec rs, float
                         int cus) {
   constexpr int kCW = cw_of<KO>();
   const size_t bytes = (size_t)chunk_lds_total(NG, KO, kCW) * sizeof(float);
-  if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (bytes + 8 * sizeof(int) > 160 * 1024) return hipErrorNotSupported;  // with the static progress counts
   hipError_t e = hipFuncSetAttribute((const void*)chunk_mfma_kernel<VB, NG, KO>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;

@@ -645,7 +645,7 @@ hipError_t launch_gqa_typed(const kvq_cache& c, const uint16_t* q, int64_t q_pos
                             int cus, bool dry) {
   const GLds L = gqa_lds(NG, KO > 0);
   const size_t bytes = ((size_t)kBK * kTP + (size_t)kGqaWaves * L.total) * sizeof(float);
-  if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (bytes + kGqaWaves * sizeof(int) > 160 * 1024) return hipErrorNotSupported;  // with the static progress counts
   if (dry) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)decode_gqa_kernel<VB, GW, KO, NG, PG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);

@@ -848,7 +848,7 @@ static hipError_t launch_mha_typed(const kvq_cache& c, const uint16_t* q, int64_
   using Sh = MShape<D, BK, KB, VB>;
   const MLds L = mha_lds(D, BK, KO > 0, false, KEEP, VCB ? 1 << VB : 0);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)kMhaWaves * L.total) * sizeof(float);
-  if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (bytes + kMhaWaves * sizeof(int) > 160 * 1024) return hipErrorNotSupported;  // with the static progress counts
   if (dry) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)decode_mha_kernel<D, BK, KB, VB, KO, PG, KEEP, VCB>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -868,7 +868,7 @@ static hipError_t launch_mha_lut_typed(const kvq_cache& c, const uint16_t* q, in
   const MLds L = mha_lds(D, BK, false, true);
   const size_t bytes = ((size_t)BK * Sh::TPITCH + (size_t)Sh::HALF * PairTab<KB>::PITCH +
                         (size_t)kMhaWaves * L.total) * sizeof(float);
-  if (bytes > 160 * 1024) return hipErrorNotSupported;
+  if (bytes + kMhaWaves * sizeof(int) > 160 * 1024) return hipErrorNotSupported;  // with the static progress counts
   if (dry) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)decode_mha_lut_kernel<D, BK, KB, VB, PG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
