@@ -696,10 +696,7 @@ __global__ __launch_bounds__(cw_of<KO>() * 64) void chunk_mfma_kernel(kvq_cache 
       }
       for (int64_t n = sp; n < nlimit; n += S) {
         if constexpr (kCW == 8) {
-          if (lane == 0) __hip_atomic_fetch_add(&chunk_progress[wave], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          const int mine = __hip_atomic_load(&chunk_progress[wave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          const int theirs = __hip_atomic_load(&chunk_progress[wave ^ 4], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (__builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0)) __builtin_amdgcn_s_setprio(1);
+          if (behind_partner<kCW>(chunk_progress, lane)) __builtin_amdgcn_s_setprio(1);
           else __builtin_amdgcn_s_setprio(0);
         }
         const bool more = n + S < nlimit;

@@ -362,5 +362,21 @@ __device__ __forceinline__ void merge_vcorr(int* VCI, int sh, float (&acc)[4], i
   }
 }
 
+// Issue balance between the two waves of a SIMD in an 8-wave workgroup (waves w and
+// w + 4): at equal priority the older wave wins the issue slot, finishes its work long
+// before the younger one and leaves it streaming alone.  Each wave counts the blocks it
+// has started in `progress` (kWaves ints of workgroup memory, zeroed before the first
+// call); the result is true, uniform over the wave, while this wave has started fewer
+// blocks than its partner, and the caller then raises its priority one level.
+template <int kWaves>
+__device__ __forceinline__ bool behind_partner(int* progress, int lane) {
+  static_assert(kWaves == 8, "partners w and w + 4");
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (lane == 0) __hip_atomic_fetch_add(&progress[wv], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const int mine = __hip_atomic_load(&progress[wv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const int theirs = __hip_atomic_load(&progress[wv ^ (kWaves / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0) != 0;
+}
+
 }  // namespace dcm
 }  // namespace kvq

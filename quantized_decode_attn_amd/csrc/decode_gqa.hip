@@ -191,15 +191,7 @@ __device__ __forceinline__ void gqa_block(GRegs<VB>& R, CsrTok& C, GState& st, f
   uint32_t* W32 = reinterpret_cast<uint32_t*>(wl + L.w32);  // [group][head][half][lane]
   int* VCI = reinterpret_cast<int*>(wl + L.vcorr);  // [4][D], then the 4 scale shifts
   const int hl = lane & 3;  // the head this lane feeds into the MFMA A operand
-  bool behind;  // wave-uniform: this wave has started fewer blocks than its SIMD partner
-  {
-    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (lane == 0) __hip_atomic_fetch_add(&gqa_progress[wv], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const int mine = __hip_atomic_load(&gqa_progress[wv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const int theirs =
-        __hip_atomic_load(&gqa_progress[wv ^ (kGqaWaves / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    behind = __builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0) != 0;
-  }
+  const bool behind = behind_partner<kGqaWaves>(gqa_progress, lane);  // wave-uniform
 
   if (behind) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);

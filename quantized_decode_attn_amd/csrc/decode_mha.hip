@@ -169,15 +169,7 @@ __device__ __forceinline__ void process_block(BlockRegs<D, BK, KB, VB>& R, CsrTo
   constexpr bool OUTL = KO > 0;
   static_assert(!(LUT && OUTL), "codebook keys with outliers take the generic kernel");
   constexpr int TPL = BK / kWave;  // tokens per lane in the softmax
-  bool behind;  // wave-uniform: this wave has started fewer blocks than its SIMD partner
-  {
-    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (lane == 0) __hip_atomic_fetch_add(&mha_progress[wv], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const int mine = __hip_atomic_load(&mha_progress[wv], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    const int theirs =
-        __hip_atomic_load(&mha_progress[wv ^ (kMhaWaves / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    behind = __builtin_amdgcn_readfirstlane(mine < theirs ? 1 : 0) != 0;
-  }
+  const bool behind = behind_partner<kMhaWaves>(mha_progress, lane);  // wave-uniform
   const int64_t nn = more ? n + nstep : n;
   const int64_t g = slot_at<PG>(sr, n), gnn = more ? slot_at<PG>(sr, nn) : g;
   const uint8_t* knext = k_block<D, BK, KB, VB>(c, gnn);
